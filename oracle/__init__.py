@@ -1,0 +1,133 @@
+"""fp64 CPU oracle for paged-KV attention (GQA/MHA and absorbed MLA).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg import this package.  It shares no code with the HIP
+library and never imports it.
+
+`paged_oracle.c` holds the arithmetic (plain double-precision loops written
+from the definition: boostr 0.2.0-beta.2 `standard_attention_fwd` /
+`build_attention_mask` / `expand_kv`, with the paged layout and absolute
+positions of ruDNN 0.1.107 `DevicePlan::attention` and `DevicePlan::mla`).
+This module only builds it with gcc and marshals numpy arrays into it.
+`brute.py` is an independent pure-Python brute force for tiny inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "paged_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "libpaged_oracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+                           "-o", tmp, _SRC, "-lm", "-lpthread"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        for name, extra in (("po_attention", [P, P, P]), ("po_mla", [P, P, P, P])):
+            fn = getattr(lib, name)
+            fn.restype = I
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except Exception:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+_DT = {"f32": 0, "bf16": 1}
+
+
+def _storage(a: np.ndarray, dtype: str) -> np.ndarray:
+    want = np.float32 if dtype == "f32" else np.uint16
+    return np.ascontiguousarray(a, dtype=want)
+
+
+_ERR = {-1: "query outside every sequence", -2: "block-table entry outside the pool",
+        -3: "out of memory", -4: "bad geometry"}
+
+
+def attention(b, rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """Paged GQA/MHA attention of batch `b` (fields as in synth.PagedBatch).
+
+    rows: optional flat indices query*hq + head to evaluate; returns
+    (out [n, dv], lse [n]).  Without rows returns (out [Q, hq, dv], lse [Q, hq]).
+    """
+    lib = _load()
+    Q = int(b.cu_q[-1])
+    n = Q * b.hq if rows is None else int(len(rows))
+    out = np.empty((n, b.dv), dtype=np.float64)
+    lse = np.empty(n, dtype=np.float64)
+    q, k, v = (_storage(x, b.dtype) for x in (b.q, b.k, b.v))
+    sl, cu, qp, bt = _i32(b.seq_lens), _i32(b.cu_q), _i32(b.q_pos), _i32(b.block_table)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    rc = lib.po_attention(
+        ctypes.c_int(_DT[b.dtype]), _ptr(q), _ptr(k), _ptr(v),
+        ctypes.c_int(len(sl)), _ptr(sl), _ptr(cu), _ptr(qp), _ptr(bt), ctypes.c_int(bt.shape[1]),
+        ctypes.c_int(b.page_size), ctypes.c_int(b.num_pages), ctypes.c_int(b.hq), ctypes.c_int(b.hkv),
+        ctypes.c_int(b.d), ctypes.c_int(b.dv), ctypes.c_double(b.scale), ctypes.c_int(int(b.causal)),
+        ctypes.c_int(int(b.window)), _ptr(r), ctypes.c_int64(0 if r is None else len(r)),
+        _ptr(out), _ptr(lse), ctypes.c_int(nthreads or default_threads()))
+    if rc:
+        raise RuntimeError(f"oracle: {_ERR.get(rc, rc)}")
+    if rows is None:
+        return out.reshape(Q, b.hq, b.dv), lse.reshape(Q, b.hq)
+    return out, lse
+
+
+def mla(b, rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None
+        ) -> Tuple[np.ndarray, np.ndarray]:
+    """Absorbed MLA of batch `b` (fields as in synth.MlaBatch); same return
+    convention as `attention` with dv = R."""
+    lib = _load()
+    Q = int(b.cu_q[-1])
+    n = Q * b.heads if rows is None else int(len(rows))
+    out = np.empty((n, b.r), dtype=np.float64)
+    lse = np.empty(n, dtype=np.float64)
+    qa, qr, lat, kp = (_storage(x, b.dtype) for x in (b.q_abs, b.q_rope, b.latent, b.kpos))
+    sl, cu, qp, bt = _i32(b.seq_lens), _i32(b.cu_q), _i32(b.q_pos), _i32(b.block_table)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    rc = lib.po_mla(
+        ctypes.c_int(_DT[b.dtype]), _ptr(qa), _ptr(qr), _ptr(lat), _ptr(kp),
+        ctypes.c_int(len(sl)), _ptr(sl), _ptr(cu), _ptr(qp), _ptr(bt), ctypes.c_int(bt.shape[1]),
+        ctypes.c_int(b.page_size), ctypes.c_int(b.num_pages), ctypes.c_int(b.heads), ctypes.c_int(b.r),
+        ctypes.c_int(b.p), ctypes.c_double(b.scale), ctypes.c_int(int(b.causal)), ctypes.c_int(int(b.window)),
+        _ptr(r), ctypes.c_int64(0 if r is None else len(r)), _ptr(out), _ptr(lse),
+        ctypes.c_int(nthreads or default_threads()))
+    if rc:
+        raise RuntimeError(f"oracle: {_ERR.get(rc, rc)}")
+    if rows is None:
+        return out.reshape(Q, b.heads, b.r), lse.reshape(Q, b.heads)
+    return out, lse

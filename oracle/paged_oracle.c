@@ -1,0 +1,260 @@
+/*
+ * paged_oracle.c -- plain fp64 CPU oracle for attention over a paged KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes (the plain definition, no blocking, no fusion, no
+ * reordering beyond the definition):
+ *
+ *   boostr 0.2.0-beta.2, attention/flash_standard.rs, `standard_attention_fwd`:
+ *     out = softmax(scale * Q K^T + mask) V, and the natural-log logsumexp of
+ *     the masked, scaled scores per query row.
+ *   ...with the mask of `build_attention_mask` (same page): a key is hidden
+ *     when causal and it lies after the query, or when a window W > 0 is set and
+ *     key + W <= query; W = 0 means unlimited.
+ *   ...with GQA as in `expand_kv` (same page): query head h reads KV head
+ *     floor(h / (Hq / Hkv)).
+ *   ruDNN 0.1.107, paged_attention/mod.rs, `DevicePlan::attention`: Q packed
+ *     [queries, Hq, D]; K [pages, page_size, Hkv, D]; V [pages, page_size,
+ *     Hkv, Dv]; causal masking compares absolute positions taken from the plan,
+ *     prefill chunks included.  The logical key index t of a sequence IS its
+ *     absolute position; it lives in page block_table[s][t / page_size], slot
+ *     t % page_size.
+ *   ruDNN, `DevicePlan::mla`: absorbed Q [queries, H, R], position Q
+ *     [queries, H, P], latent [pages, page_size, 1, R] used as both key and
+ *     value, rotated position cache [pages, page_size, 1, P]; the score adds
+ *     the latent dot product and the position dot product before scaling.
+ *
+ * Keys that are not visible to a query row are never read.  Inputs are f32 or
+ * bf16 (raw 16-bit patterns) and are widened exactly to double.  All
+ * arithmetic is double precision with libm exp/log.
+ *
+ * Rows run in parallel on POSIX threads; each (query, head) row is computed by
+ * one thread in one fixed order, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { PO_F32 = 0, PO_BF16 = 1 };
+
+/* Exact widening of one stored element to double. */
+static double po_load(int dtype, const void *base, int64_t idx)
+{
+    if (dtype == PO_F32)
+        return (double)((const float *)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    /* geometry */
+    int dtype;
+    int num_seqs, table_width, page_size, num_pages;
+    const int32_t *seq_lens, *cu_q, *q_pos, *block_table;
+    int num_queries;
+    int hq, hkv, d, dv;          /* MLA: hkv = 1, d = R (latent rank), dv = R */
+    int p;                       /* MLA position width; 0 for plain attention */
+    double scale;
+    int causal, window;
+    /* tensors */
+    const void *q, *k, *v;       /* MLA: k = v = latent */
+    const void *qp, *kp;         /* MLA only */
+    /* rows to evaluate: NULL = every (query, head) in order */
+    const int64_t *rows;
+    int64_t num_rows;
+    double *out, *lse;
+    /* work distribution */
+    int nthreads;
+    int status;
+} po_job;
+
+typedef struct { po_job *job; int tid; } po_thread_arg;
+
+/* Sequence that owns packed query i: cu_q[s] <= i < cu_q[s + 1]. */
+static int po_seq_of(const po_job *j, int i)
+{
+    for (int s = 0; s < j->num_seqs; ++s)
+        if (j->cu_q[s] <= i && i < j->cu_q[s + 1])
+            return s;
+    return -1;
+}
+
+/* Visibility of key t for a query at absolute position pos in a sequence of
+ * length len (the mask predicate above, on absolute positions). */
+static int po_visible(const po_job *j, int t, int pos, int len)
+{
+    if (t < 0 || t >= len) return 0;
+    if (j->causal && t > pos) return 0;
+    if (j->window > 0 && (int64_t)t + j->window <= pos) return 0;
+    return 1;
+}
+
+/* Element offset of (key t, kv head kvh, component c) in a pool whose rows are
+ * `width` wide and that has `heads` heads per slot. */
+static int64_t po_pool_offset(const po_job *j, int s, int t, int kvh, int heads, int width, int c,
+                              int *bad)
+{
+    int page = j->block_table[(int64_t)s * j->table_width + t / j->page_size];
+    if (page < 0 || page >= j->num_pages) { *bad = 1; return 0; }
+    int slot = t % j->page_size;
+    return (((int64_t)page * j->page_size + slot) * heads + kvh) * width + c;
+}
+
+/* One (query i, head h) row: out_row[0..dv), *lse_row. */
+static int po_row(const po_job *j, int i, int h, double *sc, double *out_row, double *lse_row)
+{
+    int s = po_seq_of(j, i);
+    if (s < 0) return -1;
+    int len = j->seq_lens[s];
+    int pos = j->q_pos[i];
+    int group = j->hq / j->hkv;
+    int kvh = h / group;
+    int bad = 0;
+
+    /* scores of the visible keys; invisible keys are skipped, never read */
+    double m = -INFINITY;
+    int count = 0;
+    for (int t = 0; t < len; ++t) {
+        if (!po_visible(j, t, pos, len)) { sc[t] = -INFINITY; continue; }
+        double dot = 0.0;
+        for (int c = 0; c < j->d; ++c) {
+            double qv = po_load(j->dtype, j->q, ((int64_t)i * j->hq + h) * j->d + c);
+            double kv = po_load(j->dtype, j->k, po_pool_offset(j, s, t, kvh, j->hkv, j->d, c, &bad));
+            dot += qv * kv;
+        }
+        for (int c = 0; c < j->p; ++c) {
+            double qv = po_load(j->dtype, j->qp, ((int64_t)i * j->hq + h) * j->p + c);
+            double kv = po_load(j->dtype, j->kp, po_pool_offset(j, s, t, 0, 1, j->p, c, &bad));
+            dot += qv * kv;
+        }
+        if (bad) return -2;
+        sc[t] = j->scale * dot;
+        if (sc[t] > m) m = sc[t];
+        ++count;
+    }
+    if (count == 0) {
+        /* softmax over an empty set is undefined */
+        for (int c = 0; c < j->dv; ++c) out_row[c] = NAN;
+        *lse_row = -INFINITY;
+        return 0;
+    }
+
+    /* softmax weights and their sum */
+    double l = 0.0;
+    for (int t = 0; t < len; ++t) {
+        if (sc[t] == -INFINITY) continue;
+        sc[t] = exp(sc[t] - m);
+        l += sc[t];
+    }
+    /* weighted sum of the visible value rows, keys in increasing order */
+    for (int c = 0; c < j->dv; ++c) out_row[c] = 0.0;
+    for (int t = 0; t < len; ++t) {
+        if (!po_visible(j, t, pos, len)) continue;
+        for (int c = 0; c < j->dv; ++c)
+            out_row[c] += sc[t] * po_load(j->dtype, j->v, po_pool_offset(j, s, t, kvh, j->hkv, j->dv, c, &bad));
+    }
+    for (int c = 0; c < j->dv; ++c) out_row[c] /= l;
+    if (bad) return -2;
+    *lse_row = m + log(l);
+    return 0;
+}
+
+static void *po_worker(void *arg)
+{
+    po_thread_arg *a = (po_thread_arg *)arg;
+    po_job *j = a->job;
+    int max_len = 1;
+    for (int s = 0; s < j->num_seqs; ++s)
+        if (j->seq_lens[s] > max_len) max_len = j->seq_lens[s];
+    double *sc = (double *)malloc(sizeof(double) * (size_t)max_len);
+    if (!sc) { j->status = -3; return NULL; }
+    int64_t total = j->rows ? j->num_rows : (int64_t)j->num_queries * j->hq;
+    for (int64_t r = a->tid; r < total; r += j->nthreads) {
+        int64_t flat = j->rows ? j->rows[r] : r;
+        int i = (int)(flat / j->hq), h = (int)(flat % j->hq);
+        int rc = po_row(j, i, h, sc, j->out + r * j->dv, j->lse + r);
+        if (rc) j->status = rc;
+    }
+    free(sc);
+    return NULL;
+}
+
+static int po_run(po_job *j)
+{
+    if (j->hq <= 0 || j->hkv <= 0 || j->hq % j->hkv != 0 || j->page_size <= 0) return -4;
+    if (j->rows) {
+        for (int64_t r = 0; r < j->num_rows; ++r)
+            if (j->rows[r] < 0 || j->rows[r] >= (int64_t)j->num_queries * j->hq) return -4;
+    }
+    int n = j->nthreads > 0 ? j->nthreads : 1;
+    j->nthreads = n;
+    j->status = 0;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n);
+    po_thread_arg *args = (po_thread_arg *)malloc(sizeof(po_thread_arg) * (size_t)n);
+    if (!th || !args) { free(th); free(args); return -3; }
+    for (int t = 0; t < n; ++t) {
+        args[t].job = j;
+        args[t].tid = t;
+        pthread_create(&th[t], NULL, po_worker, &args[t]);
+    }
+    for (int t = 0; t < n; ++t) pthread_join(th[t], NULL);
+    free(th);
+    free(args);
+    return j->status;
+}
+
+/*
+ * Paged GQA/MHA attention.  Returns 0, or a negative code: -1 query outside
+ * every sequence, -2 block-table entry outside the pool, -3 out of memory,
+ * -4 bad geometry.  out is [rows, dv] (all rows: [queries, hq, dv]) and lse
+ * is [rows] natural-log logsumexp of the scaled, masked scores.
+ */
+int po_attention(int dtype, const void *q, const void *k, const void *v,
+                 int num_seqs, const int32_t *seq_lens, const int32_t *cu_q, const int32_t *q_pos,
+                 const int32_t *block_table, int table_width, int page_size, int num_pages,
+                 int hq, int hkv, int d, int dv, double scale, int causal, int window,
+                 const int64_t *rows, int64_t num_rows, double *out, double *lse, int nthreads)
+{
+    po_job j;
+    memset(&j, 0, sizeof j);
+    j.dtype = dtype;
+    j.num_seqs = num_seqs; j.table_width = table_width; j.page_size = page_size; j.num_pages = num_pages;
+    j.seq_lens = seq_lens; j.cu_q = cu_q; j.q_pos = q_pos; j.block_table = block_table;
+    j.num_queries = num_seqs > 0 ? cu_q[num_seqs] : 0;
+    j.hq = hq; j.hkv = hkv; j.d = d; j.dv = dv; j.p = 0;
+    j.scale = scale; j.causal = causal; j.window = window;
+    j.q = q; j.k = k; j.v = v;
+    j.rows = rows; j.num_rows = num_rows; j.out = out; j.lse = lse; j.nthreads = nthreads;
+    return po_run(&j);
+}
+
+/*
+ * Absorbed MLA: one shared latent head used as key and value, plus a rotated
+ * position cache that only enters the score.  Same return codes and output
+ * layout as po_attention, with dv = r.
+ */
+int po_mla(int dtype, const void *q_abs, const void *q_rope, const void *latent, const void *kpos,
+           int num_seqs, const int32_t *seq_lens, const int32_t *cu_q, const int32_t *q_pos,
+           const int32_t *block_table, int table_width, int page_size, int num_pages,
+           int heads, int r, int p, double scale, int causal, int window,
+           const int64_t *rows, int64_t num_rows, double *out, double *lse, int nthreads)
+{
+    po_job j;
+    memset(&j, 0, sizeof j);
+    j.dtype = dtype;
+    j.num_seqs = num_seqs; j.table_width = table_width; j.page_size = page_size; j.num_pages = num_pages;
+    j.seq_lens = seq_lens; j.cu_q = cu_q; j.q_pos = q_pos; j.block_table = block_table;
+    j.num_queries = num_seqs > 0 ? cu_q[num_seqs] : 0;
+    j.hq = heads; j.hkv = 1; j.d = r; j.dv = r; j.p = p;
+    j.scale = scale; j.causal = causal; j.window = window;
+    j.q = q_abs; j.k = latent; j.v = latent; j.qp = q_rope; j.kp = kpos;
+    j.rows = rows; j.num_rows = num_rows; j.out = out; j.lse = lse; j.nthreads = nthreads;
+    return po_run(&j);
+}
