@@ -1,0 +1,219 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged-KV attention library.
+ *
+ * The library computes attention forward over a paged KV cache:
+ *
+ *   out[i, h, :] = sum_t softmax_t(scale * q[i, h, :] . k[t, kvh, :] + mask(i, t)) v[t, kvh, :]
+ *
+ * as defined by boostr 0.2.0-beta.2, attention/flash_standard.rs
+ * (`standard_attention_fwd`: softmax(Q K^T * scale + mask) V, natural-log
+ * logsumexp per query row in f32; `build_attention_mask`: causal and
+ * sliding-window masking; `expand_kv`: query head h uses KV head
+ * h / (Hq / Hkv)), over the paged layout and absolute positions of ruDNN
+ * 0.1.107, paged_attention/mod.rs (`DevicePlan::attention`: packed Q
+ * [queries, Hq, D], K [pages, page_size, Hkv, D], V [pages, page_size, Hkv,
+ * Dv]; causal masking compares absolute positions from the plan, prefill
+ * chunks included, so packed decode queries and chunked-prefill queries run
+ * in one launch).
+ *
+ * Masking, for a query at absolute position p of a sequence holding L keys:
+ * key position t is visible iff t < L, (causal == 0 or t <= p) and
+ * (window == 0 or t > p - window).  Logical key t of sequence s lives in pool
+ * page block_table[s * table_width + t / page_size], slot t % page_size.
+ *
+ * Conventions for every entry point:
+ *   - Return value: PA_OK (0) or a negative pa_status.  On failure nothing
+ *     was launched, allocated or written (ruDNN `execute_attention_into` and
+ *     `execute_backward_into` validate everything before any launch or
+ *     allocation); pa_last_error() then gives a detail message for the
+ *     calling thread.
+ *   - Device pointers are HIP device addresses on the plan's device; tensors
+ *     are dense row-major with the shapes stated.  The caller owns every
+ *     tensor, the workspace included; the library owns only the plan.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  The forward calls
+ *     only enqueue kernels: no host synchronisation, no device-to-host
+ *     readback (ruDNN `attention_into_split`).
+ *   - Calls that share an output or a workspace must be ordered by the
+ *     caller (same stream, or events); concurrent calls on them race.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  The error strings of ruDNN's `PagedAttentionError` map onto
+ * these classes; pa_status_string() names them. */
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* null pointer, unknown dtype, flag out of range */
+  PA_ERR_SHAPE = -2,       /* incompatible head/cache/output shape or scale */
+  PA_ERR_PLAN = -3,        /* malformed schedule: offsets, positions, block table */
+  PA_ERR_UNSUPPORTED = -4, /* valid request with no kernel specialisation in this build */
+  PA_ERR_WORKSPACE = -5,   /* split workspace missing or too small */
+  PA_ERR_OVERLAP = -6,     /* an output overlaps an input or another output */
+  PA_ERR_RANGE = -7,       /* a size exceeds the 32-bit index range */
+  PA_ERR_HIP = -8,         /* HIP runtime failure (allocation, copy or launch) */
+  PA_ERR_DEVICE = -9       /* plan used on a device other than the one it was made on */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0, /* IEEE binary32 */
+  PA_BF16 = 1 /* bfloat16, raw 16-bit patterns; outputs rounded to nearest even */
+} pa_dtype;
+
+/*
+ * Schedule of one batch (host memory; copied, not retained).
+ *
+ * ruDNN `DevicePlan` (its doc comment sits, garbled, above the backward
+ * structs): immutable metadata uploaded once and reusable for every call while
+ * the schedule is unchanged; cache data are supplied separately.  The query
+ * packing follows alice-llm 2.0.0, sparse_attention/llama3_bridge.rs
+ * (`CuSeqlensQ` offsets and per-sequence `BlockTables`).
+ *
+ *   num_seqs         S >= 0
+ *   seq_lens[S]      L_s >= 0 keys held by sequence s (its new tokens included)
+ *   cu_q[S+1]        packed query offsets: queries of s are cu_q[s] .. cu_q[s+1]-1;
+ *                    cu_q[0] == 0, non-decreasing
+ *   q_pos[Q]         absolute position of each packed query, 0 <= q_pos < L_s
+ *                    (Q = cu_q[S]); a query's own key is in the cache
+ *   block_table[S*W] pool page of logical page j of sequence s at [s * W + j];
+ *                    entries j < ceil(L_s / page_size) must be in [0, num_pages);
+ *                    later entries are ignored
+ *   table_width      W >= 1
+ *   page_size        keys per page; a power of two in [1, 1024]
+ *   num_pages        pages in the K/V pools
+ *   num_q_heads      Hq (MLA: H)
+ *   num_kv_heads     Hkv, divides Hq (MLA: must be 1)
+ *   causal           0 or 1
+ *   window           0 = unlimited, else the number of visible keys ending at the
+ *                    query position (boostr `StandardAttnConfig::window_size`)
+ *   max_splits       1..64: cap on the key ranges one decode query row is split
+ *                    into (1 = never split; no workspace needed)
+ *   mla              0 = GQA/MHA plan (pa_attention_fwd); 1 = absorbed-MLA plan
+ *                    (pa_mla_fwd)
+ *   split_tokens     0 = library default; else target keys per decode split
+ *                    (rounded to a multiple of 64)
+ */
+typedef struct pa_plan_desc {
+  int32_t num_seqs;
+  const int32_t* seq_lens;
+  const int32_t* cu_q;
+  const int32_t* q_pos;
+  const int32_t* block_table;
+  int32_t table_width;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t causal;
+  int32_t window;
+  int32_t max_splits;
+  int32_t mla;
+  int32_t split_tokens;
+} pa_plan_desc;
+
+typedef struct pa_plan pa_plan;
+
+/* Counts of the work a plan schedules (host-side, no synchronisation). */
+typedef struct pa_plan_info {
+  int32_t num_queries;   /* Q */
+  int32_t decode_items;  /* (query, KV head, key range) workgroups */
+  int32_t prefill_items; /* (query tile, KV head) workgroups */
+  int32_t split_rows;    /* (query, KV head) rows split into >1 ranges */
+  int32_t split_slots;   /* partial-statistics slots those rows use */
+  int32_t launches;      /* kernels one forward call enqueues (0, 1 or 2) */
+} pa_plan_info;
+
+/*
+ * Validate a schedule, build the work list on the host and upload it with one
+ * asynchronous host-to-device copy on `stream` (on the current HIP device).
+ * The plan keeps its host copy and is bound to that device.  Errors:
+ * PA_ERR_INVALID, PA_ERR_PLAN, PA_ERR_UNSUPPORTED (e.g. page_size not a power of
+ * two), PA_ERR_RANGE, PA_ERR_HIP.  *out_plan is set only on success.
+ */
+int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan);
+
+/* Free a plan (NULL is allowed).  Waits for the device to finish using it. */
+int pa_plan_destroy(pa_plan* plan);
+
+/* Fill *info with the plan's work counts. */
+int pa_plan_get_info(const pa_plan* plan, pa_plan_info* info);
+
+/*
+ * Bytes of f32 split workspace a forward call with value width `v_head_dim`
+ * needs (0 when no query row is split).  The workspace holds, per split slot
+ * and query head of the group, the unnormalised output sums and (max, sum)
+ * statistics (ruDNN `SplitWorkspace`: f32 partials matched to queries, heads,
+ * value width and splits).
+ */
+int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* bytes);
+
+/*
+ * Paged GQA/MHA attention forward (ruDNN `DevicePlan::attention_into` /
+ * `attention_into_split`).
+ *
+ *   dtype        PA_F32 or PA_BF16, the type of q, k_pool, v_pool and out
+ *   q            [Q, Hq, head_dim]
+ *   k_pool       [num_pages, page_size, Hkv, head_dim]
+ *   v_pool       [num_pages, page_size, Hkv, v_head_dim]
+ *   out          [Q, Hq, v_head_dim], written (must not overlap any input)
+ *   lse          NULL or f32 [Q, Hq]: natural-log logsumexp of the scaled,
+ *                masked scores of each row
+ *   head_dim     D, 1..1024; v_head_dim Dv, 1..1024 (this build runs
+ *                D = Dv in {64, 128, 256}; others give PA_ERR_UNSUPPORTED)
+ *   scale        finite and > 0 (e.g. 1/sqrt(D))
+ *   workspace    f32 scratch of >= pa_plan_workspace_bytes(plan, v_head_dim)
+ *                bytes, 256-byte aligned; may be NULL when that is 0
+ *   event_after_main  NULL, or a hipEvent_t recorded on `stream` right after
+ *                the main attention kernel and before the split merge (lets a
+ *                caller time the two kernels separately)
+ *
+ * The plan must be a GQA plan (mla == 0) made on the current device.
+ * Q == 0 returns PA_OK without launching anything.
+ */
+int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool,
+                     const void* v_pool, void* out, float* lse, int32_t head_dim,
+                     int32_t v_head_dim, float scale, void* workspace, size_t workspace_bytes,
+                     void* event_after_main, void* stream);
+
+/*
+ * Absorbed multi-head latent attention forward (ruDNN `DevicePlan::mla`): one
+ * shared latent head serves as both key and value; a rotated position cache
+ * adds a second dot product to every score:
+ *
+ *   score(i, h, t) = scale * (q_abs[i, h, :] . latent[t, :] + q_rope[i, h, :] . kpos[t, :])
+ *   out[i, h, :]   = sum_t softmax_t(score + mask) latent[t, :]
+ *
+ *   q_abs   [Q, H, rank]        q_rope [Q, H, rope_dim]
+ *   latent  [num_pages, page_size, 1, rank]
+ *   kpos    [num_pages, page_size, 1, rope_dim]
+ *   out     [Q, H, rank]        lse NULL or f32 [Q, H]
+ *   rank    1..1024, rope_dim 1..256 (this build runs bf16 with H = 16,
+ *           rank = 512, rope_dim = 64)
+ *   scale   from the model's original query/key head size, not the latent
+ *           rank (e.g. 1/sqrt(rank + rope_dim))
+ *
+ * The plan must be an MLA plan (mla == 1, num_kv_heads == 1).  The remaining
+ * arguments are as for pa_attention_fwd.
+ */
+int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void* q_rope,
+               const void* latent, const void* kpos, void* out, float* lse, int32_t rank,
+               int32_t rope_dim, float scale, void* workspace, size_t workspace_bytes,
+               void* event_after_main, void* stream);
+
+/* Static name of a status code. */
+const char* pa_status_string(int status);
+
+/* Detail message of the calling thread's last failure ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,548 @@
+// Host side of the C ABI declared in include/paged_attn.h: schedule
+// validation, work-list planning, plan upload, argument checks and kernel
+// dispatch.  Nothing here synchronises with the device or reads device memory
+// back on the forward path.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/paged_attn.h"
+#include "pa_launch.h"
+
+using pa::MergeItem;
+using pa::WorkItem;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+// Sequences with at most this many queries run as per-query decode items;
+// longer runs of queries become prefill tiles of kPrefillRows query rows.
+constexpr int kDecodeMaxQueries = 4;
+constexpr int kPrefillRows = 128;
+constexpr int kDefaultSplitTokens = 512;
+constexpr int kDefaultMlaSplitTokens = 1024;
+constexpr int kSplitAlign = 64;
+constexpr int kMaxSplitsLimit = 64;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct pa_plan {
+  int device = -1;
+  hipStream_t created_on = nullptr;
+  hipEvent_t ready = nullptr;
+  // schedule, host copy
+  int32_t S = 0, Q = 0, W = 0, ps = 1, page_shift = 0, num_pages = 0;
+  int32_t hq = 0, hkv = 0, causal = 0, window = 0, max_splits = 1, mla = 0, split_tokens = 0;
+  std::vector<int32_t> seq_lens, cu_q, q_pos, bt;
+  // work lists, host copy
+  std::vector<WorkItem> items;  // launch order
+  std::vector<MergeItem> merges;
+  int32_t n_decode = 0, n_prefill = 0, n_slots = 0;
+  // device copy: one allocation
+  std::vector<char> blob;
+  char* dev = nullptr;
+  const int32_t* d_bt = nullptr;
+  const int32_t* d_qpos = nullptr;
+  const int32_t* d_lens = nullptr;
+  const WorkItem* d_items = nullptr;
+  const MergeItem* d_merges = nullptr;
+
+  int group() const { return hq / hkv; }
+};
+
+namespace {
+
+// Keys visible to a query at position p in a sequence of L keys form one
+// contiguous range [lo, hi] (boostr `build_attention_mask` on absolute
+// positions); p < L guarantees it holds p itself.
+void visible_range(int p, int L, int causal, int window, int* lo, int* hi) {
+  *hi = causal ? p : L - 1;
+  *lo = window > 0 ? std::max(0, p - window + 1) : 0;
+}
+
+int validate_desc(const pa_plan_desc* d) {
+  if (!d) return fail(PA_ERR_INVALID, "plan descriptor is NULL");
+  if (d->num_seqs < 0) return fail(PA_ERR_PLAN, "num_seqs %d < 0", d->num_seqs);
+  if (d->num_seqs > 0 && (!d->seq_lens || !d->cu_q || !d->block_table))
+    return fail(PA_ERR_INVALID, "seq_lens, cu_q and block_table are required when num_seqs > 0");
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "head counts Hq=%d Hkv=%d: need Hkv > 0 dividing Hq", d->num_q_heads,
+                d->num_kv_heads);
+  if (d->mla != 0 && d->mla != 1) return fail(PA_ERR_INVALID, "mla must be 0 or 1");
+  if (d->mla && d->num_kv_heads != 1) return fail(PA_ERR_SHAPE, "MLA latent cache must have one shared head");
+  if (d->causal != 0 && d->causal != 1) return fail(PA_ERR_INVALID, "causal must be 0 or 1");
+  if (d->window < 0) return fail(PA_ERR_INVALID, "window %d < 0", d->window);
+  if (d->max_splits < 1 || d->max_splits > kMaxSplitsLimit)
+    return fail(PA_ERR_INVALID, "max_splits %d outside [1, %d]", d->max_splits, kMaxSplitsLimit);
+  if (d->split_tokens < 0) return fail(PA_ERR_INVALID, "split_tokens %d < 0", d->split_tokens);
+  if (d->page_size <= 0) return fail(PA_ERR_PLAN, "page_size %d <= 0", d->page_size);
+  if ((d->page_size & (d->page_size - 1)) != 0 || d->page_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "page_size %d: kernels need a power of two <= 1024", d->page_size);
+  if (d->num_pages <= 0) return fail(PA_ERR_PLAN, "num_pages %d <= 0", d->num_pages);
+  if (d->num_seqs > 0 && d->table_width <= 0) return fail(PA_ERR_PLAN, "table_width %d <= 0", d->table_width);
+  if ((int64_t)d->num_seqs * std::max(d->table_width, 1) > INT32_MAX)
+    return fail(PA_ERR_RANGE, "block table exceeds 32-bit indexing");
+  if ((int64_t)d->num_pages * d->page_size > INT32_MAX)
+    return fail(PA_ERR_RANGE, "pool slots exceed 32-bit indexing");
+  if (d->num_seqs == 0) return PA_OK;
+  if (d->cu_q[0] != 0) return fail(PA_ERR_PLAN, "cu_q[0] = %d, expected 0", d->cu_q[0]);
+  for (int s = 0; s < d->num_seqs; ++s)
+    if (d->cu_q[s + 1] < d->cu_q[s]) return fail(PA_ERR_PLAN, "cu_q decreases at sequence %d", s);
+  const int64_t Q = d->cu_q[d->num_seqs];
+  if (Q * d->num_q_heads > INT32_MAX) return fail(PA_ERR_RANGE, "queries x heads exceed 32-bit indexing");
+  if (Q > 0 && !d->q_pos) return fail(PA_ERR_INVALID, "q_pos is required when there are queries");
+  for (int s = 0; s < d->num_seqs; ++s) {
+    const int L = d->seq_lens[s];
+    if (L < 0) return fail(PA_ERR_PLAN, "seq_lens[%d] = %d < 0", s, L);
+    if ((int64_t)L > (int64_t)d->table_width * d->page_size)
+      return fail(PA_ERR_PLAN, "seq_lens[%d] = %d exceeds table_width x page_size", s, L);
+    for (int i = d->cu_q[s]; i < d->cu_q[s + 1]; ++i)
+      if (d->q_pos[i] < 0 || d->q_pos[i] >= L)
+        return fail(PA_ERR_PLAN, "q_pos[%d] = %d outside [0, seq_lens[%d] = %d)", i, d->q_pos[i], s, L);
+    const int pages = (L + d->page_size - 1) / d->page_size;
+    for (int j = 0; j < pages; ++j) {
+      const int pg = d->block_table[(int64_t)s * d->table_width + j];
+      if (pg < 0 || pg >= d->num_pages)
+        return fail(PA_ERR_PLAN, "block_table[%d][%d] = %d outside [0, %d)", s, j, pg, d->num_pages);
+    }
+  }
+  return PA_OK;
+}
+
+// Split one decode query row's visible range into page-friendly key ranges.
+void plan_decode_row(pa_plan* p, int s, int i, int kvh, int split_tokens, std::vector<WorkItem>& out) {
+  int lo, hi;
+  visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &lo, &hi);
+  const int n = hi - lo + 1;
+  int nsplit = std::min(p->max_splits, (n + split_tokens - 1) / split_tokens);
+  nsplit = std::max(nsplit, 1);
+  if (nsplit == 1) {
+    out.push_back(WorkItem{pa::kDecode, s, kvh, i, 1, lo, hi + 1, -1});
+    return;
+  }
+  int chunk = (n + nsplit - 1) / nsplit;
+  chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+  nsplit = (n + chunk - 1) / chunk;
+  if (nsplit == 1) {
+    out.push_back(WorkItem{pa::kDecode, s, kvh, i, 1, lo, hi + 1, -1});
+    return;
+  }
+  const int base = p->n_slots;
+  for (int j = 0; j < nsplit; ++j) {
+    const int b = lo + j * chunk, e = std::min(hi + 1, b + chunk);
+    out.push_back(WorkItem{pa::kDecode, s, kvh, i, 1, b, e, base + j});
+  }
+  p->merges.push_back(MergeItem{i, kvh, base, nsplit});
+  p->n_slots += nsplit;
+}
+
+void build_work(pa_plan* p) {
+  std::vector<WorkItem> dec, pre;
+  const int G = p->group();
+  const int split_tokens = p->split_tokens > 0
+                               ? std::max(kSplitAlign, (p->split_tokens + kSplitAlign - 1) / kSplitAlign * kSplitAlign)
+                               : (p->mla ? kDefaultMlaSplitTokens : kDefaultSplitTokens);
+  for (int s = 0; s < p->S; ++s) {
+    const int q0 = p->cu_q[s], q1 = p->cu_q[s + 1];
+    const int nq = q1 - q0;
+    if (nq == 0) continue;
+    if (p->mla || nq <= kDecodeMaxQueries) {
+      for (int i = q0; i < q1; ++i)
+        for (int kvh = 0; kvh < p->hkv; ++kvh) plan_decode_row(p, s, i, kvh, split_tokens, dec);
+    } else {
+      const int tile_q = std::max(1, kPrefillRows / G);
+      for (int t0 = q0; t0 < q1; t0 += tile_q) {
+        const int t1 = std::min(q1, t0 + tile_q);
+        int lo = INT32_MAX, hi = -1;
+        for (int i = t0; i < t1; ++i) {
+          int a, b;
+          visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &a, &b);
+          lo = std::min(lo, a);
+          hi = std::max(hi, b);
+        }
+        for (int kvh = 0; kvh < p->hkv; ++kvh) pre.push_back(WorkItem{pa::kPrefill, s, kvh, t0, t1 - t0, lo, hi + 1, -1});
+      }
+    }
+  }
+  // longest first, so the tail of the launch is made of short items
+  auto longer = [](const WorkItem& a, const WorkItem& b) {
+    const int64_t wa = (int64_t)(a.tok_end - a.tok_begin) * a.q_count, wb = (int64_t)(b.tok_end - b.tok_begin) * b.q_count;
+    return wa > wb;
+  };
+  std::stable_sort(pre.begin(), pre.end(), longer);
+  std::stable_sort(dec.begin(), dec.end(), longer);
+  p->n_prefill = (int32_t)pre.size();
+  p->n_decode = (int32_t)dec.size();
+  p->items = std::move(pre);
+  p->items.insert(p->items.end(), dec.begin(), dec.end());
+}
+
+size_t workspace_bytes_for(const pa_plan* p, int dv) {
+  if (p->n_slots == 0) return 0;
+  const size_t G = p->group();
+  return align_up((size_t)p->n_slots * G * dv * sizeof(float), kAlign) +
+         align_up((size_t)p->n_slots * G * 2 * sizeof(float), kAlign);
+}
+
+struct Extent {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+
+bool overlaps(const Extent& a, const Extent& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
+  return x < y + b.n && y < x + a.n;
+}
+
+int check_disjoint(const std::vector<Extent>& outs, const std::vector<Extent>& ins) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Extent& in : ins)
+      if (overlaps(outs[i], in)) return fail(PA_ERR_OVERLAP, "%s overlaps %s", outs[i].name, in.name);
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlaps(outs[i], outs[j])) return fail(PA_ERR_OVERLAP, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  return PA_OK;
+}
+
+int check_device(const pa_plan* p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  if (dev != p->device) return fail(PA_ERR_DEVICE, "metadata belongs to device %d, current device is %d", p->device, dev);
+  return PA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Common forward path once the kernel family is chosen.
+struct FwdCall {
+  const pa_plan* plan;
+  int dtype, d, dv;
+  pa::KernelArgs args;
+  void* event_after_main;
+  hipStream_t stream;
+};
+
+}  // namespace
+
+extern "C" {
+
+int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
+  if (!out_plan) return fail(PA_ERR_INVALID, "out_plan is NULL");
+  int rc = validate_desc(desc);
+  if (rc != PA_OK) return rc;
+
+  pa_plan* p = new (std::nothrow) pa_plan();
+  if (!p) return fail(PA_ERR_HIP, "host allocation failed");
+  p->S = desc->num_seqs;
+  p->W = std::max(desc->table_width, 1);
+  p->ps = desc->page_size;
+  while ((1 << p->page_shift) < p->ps) ++p->page_shift;
+  p->num_pages = desc->num_pages;
+  p->hq = desc->num_q_heads;
+  p->hkv = desc->num_kv_heads;
+  p->causal = desc->causal;
+  p->window = desc->window;
+  p->max_splits = desc->max_splits;
+  p->mla = desc->mla;
+  p->split_tokens = desc->split_tokens;
+  p->cu_q.assign(1, 0);
+  if (p->S > 0) {
+    p->seq_lens.assign(desc->seq_lens, desc->seq_lens + p->S);
+    p->cu_q.assign(desc->cu_q, desc->cu_q + p->S + 1);
+    p->bt.assign(desc->block_table, desc->block_table + (size_t)p->S * p->W);
+  }
+  p->Q = p->cu_q.back();
+  if (p->Q > 0) p->q_pos.assign(desc->q_pos, desc->q_pos + p->Q);
+  build_work(p);
+
+  // one blob: block table | q_pos | seq_lens | items | merges
+  size_t off_bt = 0;
+  size_t off_qpos = align_up(off_bt + p->bt.size() * 4, kAlign);
+  size_t off_lens = align_up(off_qpos + p->q_pos.size() * 4, kAlign);
+  size_t off_items = align_up(off_lens + p->seq_lens.size() * 4, kAlign);
+  size_t off_merges = align_up(off_items + p->items.size() * sizeof(WorkItem), kAlign);
+  size_t total = align_up(off_merges + p->merges.size() * sizeof(MergeItem), kAlign);
+  total = std::max(total, kAlign);
+  p->blob.assign(total, 0);
+  if (!p->bt.empty()) memcpy(p->blob.data() + off_bt, p->bt.data(), p->bt.size() * 4);
+  if (!p->q_pos.empty()) memcpy(p->blob.data() + off_qpos, p->q_pos.data(), p->q_pos.size() * 4);
+  if (!p->seq_lens.empty()) memcpy(p->blob.data() + off_lens, p->seq_lens.data(), p->seq_lens.size() * 4);
+  if (!p->items.empty()) memcpy(p->blob.data() + off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+  if (!p->merges.empty())
+    memcpy(p->blob.data() + off_merges, p->merges.data(), p->merges.size() * sizeof(MergeItem));
+
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetDevice");
+  }
+  e = hipMalloc(reinterpret_cast<void**>(&p->dev), total);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipMalloc(plan)");
+  }
+  p->created_on = reinterpret_cast<hipStream_t>(stream);
+  e = hipMemcpyAsync(p->dev, p->blob.data(), total, hipMemcpyHostToDevice, p->created_on);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(p->ready, p->created_on);
+  if (e != hipSuccess) {
+    (void)hipStreamSynchronize(p->created_on);
+    (void)hipFree(p->dev);
+    if (p->ready) (void)hipEventDestroy(p->ready);
+    delete p;
+    return hip_fail(e, "plan upload");
+  }
+  p->d_bt = reinterpret_cast<const int32_t*>(p->dev + off_bt);
+  p->d_qpos = reinterpret_cast<const int32_t*>(p->dev + off_qpos);
+  p->d_lens = reinterpret_cast<const int32_t*>(p->dev + off_lens);
+  p->d_items = reinterpret_cast<const WorkItem*>(p->dev + off_items);
+  p->d_merges = reinterpret_cast<const MergeItem*>(p->dev + off_merges);
+  *out_plan = p;
+  return ok();
+}
+
+int pa_plan_destroy(pa_plan* plan) {
+  if (!plan) return ok();
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  if (prev != plan->device) (void)hipSetDevice(plan->device);
+  if (plan->ready) (void)hipEventSynchronize(plan->ready);
+  // kernels that read the plan may still be queued on other streams
+  (void)hipDeviceSynchronize();
+  if (plan->dev) (void)hipFree(plan->dev);
+  if (plan->ready) (void)hipEventDestroy(plan->ready);
+  if (prev >= 0 && prev != plan->device) (void)hipSetDevice(prev);
+  delete plan;
+  return ok();
+}
+
+int pa_plan_get_info(const pa_plan* plan, pa_plan_info* info) {
+  if (!plan || !info) return fail(PA_ERR_INVALID, "plan or info is NULL");
+  info->num_queries = plan->Q;
+  info->decode_items = plan->n_decode;
+  info->prefill_items = plan->n_prefill;
+  info->split_rows = (int32_t)plan->merges.size();
+  info->split_slots = plan->n_slots;
+  info->launches = plan->items.empty() ? 0 : (plan->merges.empty() ? 1 : 2);
+  return ok();
+}
+
+int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* bytes) {
+  if (!plan || !bytes) return fail(PA_ERR_INVALID, "plan or bytes is NULL");
+  if (v_head_dim <= 0 || v_head_dim > 1024) return fail(PA_ERR_SHAPE, "v_head_dim %d outside [1, 1024]", v_head_dim);
+  *bytes = workspace_bytes_for(plan, v_head_dim);
+  return ok();
+}
+
+static int launch_common(FwdCall& c, bool is_mla) {
+  const pa_plan* p = c.plan;
+  if (p->Q == 0 || p->items.empty()) return ok();
+  if (c.stream != p->created_on) {
+    hipError_t e = hipStreamWaitEvent(c.stream, p->ready, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(plan)");
+  }
+  hipError_t e;
+  if (is_mla) {
+    e = pa::launch_mla_main(c.dtype, c.args, c.stream);
+  } else {
+    e = pa::launch_gqa_main(c.dtype, c.d, p->group(), p->n_decode, p->n_prefill, c.args, c.stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (c.event_after_main) {
+    e = hipEventRecord(reinterpret_cast<hipEvent_t>(c.event_after_main), c.stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(event_after_main)");
+  }
+  if (!p->merges.empty()) {
+    if (is_mla)
+      e = pa::launch_mla_merge(c.dtype, c.args, p->d_merges, (int)p->merges.size(), c.stream);
+    else
+      e = pa::launch_gqa_merge(c.dtype, c.d, p->group(), c.args, p->d_merges, (int)p->merges.size(), c.stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return ok();
+}
+
+static int check_workspace(const pa_plan* p, int dv, void* workspace, size_t workspace_bytes, float** ws_o,
+                           float** ws_ml, size_t* need_out) {
+  const size_t need = workspace_bytes_for(p, dv);
+  *need_out = need;
+  *ws_o = *ws_ml = nullptr;
+  if (need == 0) return PA_OK;
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "plan splits %d query rows: a %zu-byte workspace is required",
+                              (int)p->merges.size(), need);
+  if (workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "split workspace has %zu bytes, plan needs %zu", workspace_bytes, need);
+  if ((uintptr_t)workspace % kAlign) return fail(PA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  *ws_o = reinterpret_cast<float*>(workspace);
+  *ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                    align_up((size_t)p->n_slots * p->group() * dv * sizeof(float), kAlign));
+  return PA_OK;
+}
+
+int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool, const void* v_pool,
+                     void* out, float* lse, int32_t head_dim, int32_t v_head_dim, float scale, void* workspace,
+                     size_t workspace_bytes, void* event_after_main, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
+  if (plan->mla) return fail(PA_ERR_INVALID, "plan was made for MLA (use pa_mla_fwd)");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!q || !k_pool || !v_pool || !out) return fail(PA_ERR_INVALID, "q, k_pool, v_pool and out are required");
+  if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
+    return fail(PA_ERR_SHAPE, "head sizes D=%d Dv=%d outside [1, 1024]", head_dim, v_head_dim);
+  if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
+  int rc = check_device(plan);
+  if (rc != PA_OK) return rc;
+  float *ws_o, *ws_ml;
+  size_t need;
+  rc = check_workspace(plan, v_head_dim, workspace, workspace_bytes, &ws_o, &ws_ml, &need);
+  if (rc != PA_OK) return rc;
+  const int G = plan->group();
+  if (head_dim != v_head_dim) return fail(PA_ERR_UNSUPPORTED, "this build needs D == Dv (got %d, %d)", head_dim, v_head_dim);
+  if (plan->n_decode > 0 && !pa::gqa_supported(dtype, head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "no decode kernel for dtype %d, D=%d, G=%d", dtype, head_dim, G);
+  if (plan->n_prefill > 0 && !pa::prefill_supported(dtype, head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, D=%d, G=%d", dtype, head_dim, G);
+  const size_t es = dtype == PA_F32 ? 4 : 2;
+  const size_t slots = (size_t)plan->num_pages * plan->ps * plan->hkv;
+  std::vector<Extent> outs = {{out, (size_t)plan->Q * plan->hq * v_head_dim * es, "out"},
+                              {lse, lse ? (size_t)plan->Q * plan->hq * 4 : 0, "lse"},
+                              {workspace, need, "workspace"}};
+  std::vector<Extent> ins = {{q, (size_t)plan->Q * plan->hq * head_dim * es, "q"},
+                             {k_pool, slots * head_dim * es, "k_pool"},
+                             {v_pool, slots * v_head_dim * es, "v_pool"}};
+  rc = check_disjoint(outs, ins);
+  if (rc != PA_OK) return rc;
+
+  FwdCall c{plan, dtype, head_dim, v_head_dim, {}, event_after_main, reinterpret_cast<hipStream_t>(stream)};
+  pa::KernelArgs& a = c.args;
+  a.q = q;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = ws_o;
+  a.ws_ml = ws_ml;
+  a.block_table = plan->d_bt;
+  a.q_pos = plan->d_qpos;
+  a.seq_lens = plan->d_lens;
+  a.items = plan->d_items;
+  a.n_items = (int32_t)plan->items.size();
+  a.table_width = plan->W;
+  a.page_shift = plan->page_shift;
+  a.hq = plan->hq;
+  a.hkv = plan->hkv;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.causal = plan->causal;
+  a.window = plan->window;
+  return launch_common(c, false);
+}
+
+int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void* q_rope, const void* latent,
+               const void* kpos, void* out, float* lse, int32_t rank, int32_t rope_dim, float scale,
+               void* workspace, size_t workspace_bytes, void* event_after_main, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
+  if (!plan->mla) return fail(PA_ERR_INVALID, "plan was made for GQA (use pa_attention_fwd)");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!q_abs || !q_rope || !latent || !kpos || !out)
+    return fail(PA_ERR_INVALID, "q_abs, q_rope, latent, kpos and out are required");
+  if (rank <= 0 || rank > 1024) return fail(PA_ERR_SHAPE, "latent rank %d outside [1, 1024]", rank);
+  if (rope_dim <= 0 || rope_dim > 256)
+    return fail(PA_ERR_SHAPE, "incompatible MLA positional dimensions: rope_dim %d outside [1, 256]", rope_dim);
+  if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
+  int rc = check_device(plan);
+  if (rc != PA_OK) return rc;
+  float *ws_o, *ws_ml;
+  size_t need;
+  rc = check_workspace(plan, rank, workspace, workspace_bytes, &ws_o, &ws_ml, &need);
+  if (rc != PA_OK) return rc;
+  if (!pa::mla_supported(dtype, plan->hq, rank, rope_dim))
+    return fail(PA_ERR_UNSUPPORTED, "no MLA kernel for dtype %d, H=%d, rank=%d, rope_dim=%d", dtype, plan->hq, rank,
+                rope_dim);
+  const size_t es = dtype == PA_F32 ? 4 : 2;
+  const size_t slots = (size_t)plan->num_pages * plan->ps;
+  std::vector<Extent> outs = {{out, (size_t)plan->Q * plan->hq * rank * es, "out"},
+                              {lse, lse ? (size_t)plan->Q * plan->hq * 4 : 0, "lse"},
+                              {workspace, need, "workspace"}};
+  std::vector<Extent> ins = {{q_abs, (size_t)plan->Q * plan->hq * rank * es, "q_abs"},
+                             {q_rope, (size_t)plan->Q * plan->hq * rope_dim * es, "q_rope"},
+                             {latent, slots * rank * es, "latent"},
+                             {kpos, slots * rope_dim * es, "kpos"}};
+  rc = check_disjoint(outs, ins);
+  if (rc != PA_OK) return rc;
+
+  FwdCall c{plan, dtype, rank, rank, {}, event_after_main, reinterpret_cast<hipStream_t>(stream)};
+  pa::KernelArgs& a = c.args;
+  a.q = q_abs;
+  a.k = latent;
+  a.v = latent;
+  a.qr = q_rope;
+  a.kr = kpos;
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = ws_o;
+  a.ws_ml = ws_ml;
+  a.block_table = plan->d_bt;
+  a.q_pos = plan->d_qpos;
+  a.seq_lens = plan->d_lens;
+  a.items = plan->d_items;
+  a.n_items = (int32_t)plan->items.size();
+  a.table_width = plan->W;
+  a.page_shift = plan->page_shift;
+  a.hq = plan->hq;
+  a.hkv = 1;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.causal = plan->causal;
+  a.window = plan->window;
+  return launch_common(c, true);
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_SHAPE: return "incompatible paged head/cache/output shape or scale";
+    case PA_ERR_PLAN: return "malformed schedule metadata";
+    case PA_ERR_UNSUPPORTED: return "no kernel specialisation for this request";
+    case PA_ERR_WORKSPACE: return "split workspace shape mismatch";
+    case PA_ERR_OVERLAP: return "output overlaps an input";
+    case PA_ERR_RANGE: return "paged dimension exceeds 32-bit indexing";
+    case PA_ERR_HIP: return "HIP runtime failure";
+    case PA_ERR_DEVICE: return "metadata belongs to another device";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+// Device-side building blocks shared by the paged-attention kernels (gfx950).
+//
+// Work is described by a flat list of WorkItem records built on the host from
+// the schedule (sequence lengths, packed query offsets, absolute query
+// positions, block tables) and uploaded once per plan.  One workgroup runs
+// one item.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+
+// One unit of work.  Decode items cover one query, one KV head and one
+// contiguous range of that query's visible keys; prefill items cover up to a
+// tile of consecutive queries of one sequence and one KV head.
+struct WorkItem {
+  int32_t kind;       // kDecode / kPrefill
+  int32_t seq;        // sequence index (row of the block table)
+  int32_t kvh;        // KV head
+  int32_t q_begin;    // first packed query
+  int32_t q_count;    // number of queries (decode: 1)
+  int32_t tok_begin;  // first logical key position visited (inclusive)
+  int32_t tok_end;    // last logical key position visited (exclusive)
+  int32_t slot;       // decode: split-partial slot, or -1 to write the output directly
+};
+constexpr int32_t kDecode = 0;
+constexpr int32_t kPrefill = 1;
+
+// One split query row to combine: partials slot .. slot + nsplit - 1 hold the
+// per-split statistics of (query q, KV head kvh).
+struct MergeItem {
+  int32_t q, kvh, slot, nsplit;
+};
+
+struct KernelArgs {
+  const void* q;          // [Q, Hq, D]            (MLA: absorbed query [Q, H, R])
+  const void* k;          // [pages, ps, Hkv, D]   (MLA: latent [pages, ps, 1, R])
+  const void* v;          // [pages, ps, Hkv, Dv]  (MLA: latent)
+  const void* qr;         // MLA only: position query [Q, H, P]
+  const void* kr;         // MLA only: rotated position cache [pages, ps, 1, P]
+  void* out;              // [Q, Hq, Dv]
+  float* lse;             // [Q, Hq] or null
+  float* ws_o;            // split partials: [slots, G, Dv] unnormalised sums
+  float* ws_ml;           // split partials: [slots, G, 2] = (running max in log2 units, sum)
+  const int32_t* block_table;  // [S, W]
+  const int32_t* q_pos;        // [Q]
+  const int32_t* seq_lens;     // [S]
+  const WorkItem* items;
+  int32_t n_items;
+  int32_t table_width;
+  int32_t page_shift;     // log2(page_size)
+  int32_t hq, hkv;
+  float scale;            // softmax scale
+  float scale_log2;       // scale * log2(e)
+  int32_t causal, window;
+};
+
+// ---------------------------------------------------------------------------
+// Lane exchange.  DPP row operations stay inside a 16-lane row; crossing rows
+// goes through ds_swizzle/bpermute (__shfl_xor).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // reverse within each 8-lane half row
+constexpr int kDppMirror = 0x140;      // reverse within each 16-lane row
+
+// Sum over aligned groups of N consecutive lanes (N = 1..64, power of two);
+// every lane of the group receives the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Combine across lanes whose index differs by a multiple of STRIDE (the
+// other lanes of the same column), STRIDE * COUNT = 64.
+template <int STRIDE>
+__device__ __forceinline__ float column_max(float x) {
+  for (int s = STRIDE; s < kWave; s <<= 1) x = fmaxf(x, __shfl_xor(x, s));
+  return x;
+}
+template <int STRIDE>
+__device__ __forceinline__ float column_sum(float x) {
+  for (int s = STRIDE; s < kWave; s <<= 1) x += __shfl_xor(x, s);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 helpers (storage is raw 16-bit patterns).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  float2_t f = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs and an fp32 accumulator.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// (lo16(a), lo16(b)) and (hi16(a), hi16(b)): the same dimension of two keys.
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Map a dispatch index to an item index so that consecutive items land on the
+// same XCD: the hardware deals workgroups round-robin over the 8 XCDs.
+__device__ __forceinline__ int xcd_item(int b, int n) {
+  constexpr int kXcd = 8;
+  const int per = n / kXcd, rem = n % kXcd;
+  const int x = b % kXcd, j = b / kXcd;
+  // XCD x owns a contiguous run of per (+1 for the first rem XCDs) items
+  const int start = x * per + (x < rem ? x : rem);
+  return start + j;
+}
+
+}  // namespace pa

@@ -1,0 +1,112 @@
+// Kernel entry points and their launchers.  Host code reaches the kernels
+// only through the launch_* functions declared in pa_launch.h.
+#include "pa_decode.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+// Decode launch shape: 4 waves share one item, 8 key loads per lane per block.
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeUnroll = 8;
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(KernelArgs a) {
+  __shared__ float smem[kDecodeWaves * G * (D + 2)];
+  const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
+  decode_item<T, D, G, kDecodeWaves, kDecodeUnroll>(a, it, smem);
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void merge_kernel(KernelArgs a, const MergeItem* merges) {
+  const MergeItem mi = merges[blockIdx.x];
+  merge_row<T, D, G>(a, mi);
+}
+
+namespace {
+
+using LaunchFn = hipError_t (*)(const KernelArgs&, int, const MergeItem*, int, hipStream_t);
+
+template <typename T, int D, int G>
+hipError_t launch_decode_t(const KernelArgs& a, int n_items, const MergeItem* merges, int n_merges,
+                           hipStream_t stream) {
+  if (n_items > 0) {
+    hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(n_items), dim3(kDecodeWaves * kWave), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int D, int G>
+hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, hipStream_t stream) {
+  if (n_merges > 0) {
+    hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3(n_merges), dim3(256), 0, stream, a, merges);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <template <typename, int, int> class Sel, typename T, int D>
+LaunchFn pick_g(int g) {
+  switch (g) {
+    case 1: return Sel<T, D, 1>::fn;
+    case 2: return Sel<T, D, 2>::fn;
+    case 4: return Sel<T, D, 4>::fn;
+    case 8: return Sel<T, D, 8>::fn;
+    case 16: return Sel<T, D, 16>::fn;
+    default: return nullptr;
+  }
+}
+
+template <template <typename, int, int> class Sel, typename T>
+LaunchFn pick_d(int d, int g) {
+  switch (d) {
+    case 64: return pick_g<Sel, T, 64>(g);
+    case 128: return pick_g<Sel, T, 128>(g);
+    case 256: return pick_g<Sel, T, 256>(g);
+    default: return nullptr;
+  }
+}
+
+template <template <typename, int, int> class Sel>
+LaunchFn pick(int dtype, int d, int g) {
+  if (dtype == 0) return pick_d<Sel, float>(d, g);
+  if (dtype == 1) return pick_d<Sel, uint16_t>(d, g);
+  return nullptr;
+}
+
+template <typename T, int D, int G>
+struct DecodeSel {
+  static constexpr LaunchFn fn = launch_decode_t<T, D, G>;
+};
+template <typename T, int D, int G>
+struct MergeSel {
+  static constexpr LaunchFn fn = launch_merge_t<T, D, G>;
+};
+
+}  // namespace
+
+bool gqa_supported(int dtype, int d, int g) { return pick<DecodeSel>(dtype, d, g) != nullptr; }
+
+bool prefill_supported(int, int, int) { return false; }
+
+hipError_t launch_gqa_main(int dtype, int d, int g, int n_decode, int n_prefill, const KernelArgs& a,
+                           hipStream_t stream) {
+  if (n_prefill > 0) return hipErrorInvalidValue;
+  LaunchFn f = pick<DecodeSel>(dtype, d, g);
+  return f ? f(a, n_decode, nullptr, 0, stream) : hipErrorInvalidValue;
+}
+
+bool mla_supported(int, int, int, int) { return false; }
+hipError_t launch_mla_main(int, const KernelArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_mla_merge(int, const KernelArgs&, const MergeItem*, int, hipStream_t) {
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,
+                            hipStream_t stream) {
+  LaunchFn f = pick<MergeSel>(dtype, d, g);
+  return f ? f(a, 0, merges, n_merges, stream) : hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,26 @@
+// Host-visible launchers of the paged-attention kernels (internal to the
+// library; the public boundary is include/paged_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "pa_device.h"
+
+namespace pa {
+
+// dtype: 0 = f32, 1 = bf16.  d: head size.  g: query heads per KV head.
+bool gqa_supported(int dtype, int d, int g);
+bool prefill_supported(int dtype, int d, int g);
+// Main GQA launch over a.items: decode-only, prefill-only or one mixed launch.
+hipError_t launch_gqa_main(int dtype, int d, int g, int n_decode, int n_prefill, const KernelArgs& a,
+                           hipStream_t stream);
+hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,
+                            hipStream_t stream);
+
+// Absorbed MLA: h query heads, latent rank r, position width p.
+bool mla_supported(int dtype, int h, int r, int p);
+hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream);
+hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
+                            hipStream_t stream);
+
+}  // namespace pa
