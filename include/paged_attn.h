@@ -149,7 +149,7 @@ int pa_plan_get_info(const pa_plan* plan, pa_plan_info* info);
  * needs (0 when no query row is split).  The workspace holds, per split slot
  * and query head of the group, the unnormalised output sums and (max, sum)
  * statistics (ruDNN `SplitWorkspace`: f32 partials matched to queries, heads,
- * value width and splits).
+ * value width and splits); a second, small kernel merges them.
  */
 int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* bytes);
 
@@ -168,7 +168,7 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
  *                D = Dv in {64, 128, 256}; others give PA_ERR_UNSUPPORTED)
  *   scale        finite and > 0 (e.g. 1/sqrt(D))
  *   workspace    f32 scratch of >= pa_plan_workspace_bytes(plan, v_head_dim)
- *                bytes, 256-byte aligned; may be NULL when that is 0
+ *                bytes, 256-byte aligned; may be NULL when that size is 0
  *   event_after_main  NULL, or a hipEvent_t recorded on `stream` right after
  *                the main attention kernel and before the split merge (lets a
  *                caller time the two kernels separately)

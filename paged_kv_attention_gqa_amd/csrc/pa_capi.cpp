@@ -143,20 +143,20 @@ void plan_decode_row(pa_plan* p, int s, int i, int kvh, int split_tokens, std::v
   int nsplit = std::min(p->max_splits, (n + split_tokens - 1) / split_tokens);
   nsplit = std::max(nsplit, 1);
   if (nsplit == 1) {
-    out.push_back(WorkItem{pa::kDecode, s, kvh, i, 1, lo, hi + 1, -1});
+    out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, lo, hi + 1, -1});
     return;
   }
   int chunk = (n + nsplit - 1) / nsplit;
   chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
   nsplit = (n + chunk - 1) / chunk;
   if (nsplit == 1) {
-    out.push_back(WorkItem{pa::kDecode, s, kvh, i, 1, lo, hi + 1, -1});
+    out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, lo, hi + 1, -1});
     return;
   }
   const int base = p->n_slots;
   for (int j = 0; j < nsplit; ++j) {
     const int b = lo + j * chunk, e = std::min(hi + 1, b + chunk);
-    out.push_back(WorkItem{pa::kDecode, s, kvh, i, 1, b, e, base + j});
+    out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, b, e, base + j});
   }
   p->merges.push_back(MergeItem{i, kvh, base, nsplit});
   p->n_slots += nsplit;
@@ -173,8 +173,15 @@ void build_work(pa_plan* p) {
     const int nq = q1 - q0;
     if (nq == 0) continue;
     if (p->mla || nq <= kDecodeMaxQueries) {
-      for (int i = q0; i < q1; ++i)
-        for (int kvh = 0; kvh < p->hkv; ++kvh) plan_decode_row(p, s, i, kvh, split_tokens, dec);
+      for (int i = q0; i < q1; ++i) {
+        // KV heads innermost: the heads of one key range run side by side and
+        // together read whole [Hkv, D] slot rows of each page
+        std::vector<WorkItem> row;
+        for (int kvh = 0; kvh < p->hkv; ++kvh) plan_decode_row(p, s, i, kvh, split_tokens, row);
+        const size_t per = row.size() / p->hkv;
+        for (size_t j = 0; j < per; ++j)
+          for (int kvh = 0; kvh < p->hkv; ++kvh) dec.push_back(row[kvh * per + j]);
+      }
     } else {
       const int tile_q = std::max(1, kPrefillRows / G);
       for (int t0 = q0; t0 < q1; t0 += tile_q) {
@@ -186,7 +193,7 @@ void build_work(pa_plan* p) {
           lo = std::min(lo, a);
           hi = std::max(hi, b);
         }
-        for (int kvh = 0; kvh < p->hkv; ++kvh) pre.push_back(WorkItem{pa::kPrefill, s, kvh, t0, t1 - t0, lo, hi + 1, -1});
+        for (int kvh = 0; kvh < p->hkv; ++kvh) pre.push_back(WorkItem{pa::kPrefill, kvh, s, t0, t1 - t0, lo, hi + 1, -1});
       }
     }
   }
@@ -203,11 +210,13 @@ void build_work(pa_plan* p) {
   p->items.insert(p->items.end(), dec.begin(), dec.end());
 }
 
+// Workspace: partial sums [slots, G, Dv] | (max, sum) [slots, G, 2].
+size_t ws_o_bytes(const pa_plan* p, int dv) { return align_up((size_t)p->n_slots * p->group() * dv * 4, kAlign); }
+size_t ws_ml_bytes(const pa_plan* p) { return align_up((size_t)p->n_slots * p->group() * 2 * 4, kAlign); }
+
 size_t workspace_bytes_for(const pa_plan* p, int dv) {
   if (p->n_slots == 0) return 0;
-  const size_t G = p->group();
-  return align_up((size_t)p->n_slots * G * dv * sizeof(float), kAlign) +
-         align_up((size_t)p->n_slots * G * 2 * sizeof(float), kAlign);
+  return ws_o_bytes(p, dv) + ws_ml_bytes(p);
 }
 
 struct Extent {
@@ -383,10 +392,9 @@ static int launch_common(FwdCall& c, bool is_mla) {
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(event_after_main)");
   }
   if (!p->merges.empty()) {
-    if (is_mla)
-      e = pa::launch_mla_merge(c.dtype, c.args, p->d_merges, (int)p->merges.size(), c.stream);
-    else
-      e = pa::launch_gqa_merge(c.dtype, c.d, p->group(), c.args, p->d_merges, (int)p->merges.size(), c.stream);
+    e = is_mla ? pa::launch_mla_merge(c.dtype, c.args, p->d_merges, (int)p->merges.size(), c.stream)
+               : pa::launch_gqa_merge(c.dtype, c.d, p->group(), c.args, p->d_merges, (int)p->merges.size(),
+                                      c.stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return ok();
@@ -403,9 +411,9 @@ static int check_workspace(const pa_plan* p, int dv, void* workspace, size_t wor
   if (workspace_bytes < need)
     return fail(PA_ERR_WORKSPACE, "split workspace has %zu bytes, plan needs %zu", workspace_bytes, need);
   if ((uintptr_t)workspace % kAlign) return fail(PA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
-  *ws_o = reinterpret_cast<float*>(workspace);
-  *ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                    align_up((size_t)p->n_slots * p->group() * dv * sizeof(float), kAlign));
+  char* base = reinterpret_cast<char*>(workspace);
+  *ws_o = reinterpret_cast<float*>(base);
+  *ws_ml = reinterpret_cast<float*>(base + ws_o_bytes(p, dv));
   return PA_OK;
 }
 

@@ -36,6 +36,15 @@ __device__ __forceinline__ uint4 load16(const void* base, uint64_t elem_off, int
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + elem_off * esize);
 }
 
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, uint64_t idx, float v) {
+  if constexpr (sizeof(T) == 2) {
+    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)(pack_bf16(v, 0.f) & 0xFFFFu);
+  } else {
+    reinterpret_cast<float*>(out)[idx] = v;
+  }
+}
+
 // Scores of G heads against one key chunk held by this lane.
 template <typename T, int G>
 __device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& kv, float (&s)[G]) {
@@ -63,7 +72,7 @@ __device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& 
 
 // Decode body.  NW waves share one item: wave w takes key blocks w, w+NW, ...
 // and the waves' statistics are combined through LDS at the end.
-// smem must hold NW * G * (EPV * LPT + 2) floats.
+// smem must hold NW * G * (D + 2) floats.
 template <typename T, int D, int G, int NW, int U>
 __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem& it, float* smem) {
   constexpr int EPV = Vec16<T>::kElems;  // elements per 16-byte chunk
@@ -72,6 +81,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   constexpr int BLK = U * TPW;           // keys per wave per block
   static_assert(D % EPV == 0 && LPT <= kWave && kWave % LPT == 0, "unsupported head size");
   static_assert(U % 2 == 0, "keys are processed in pairs");
+  static_assert(NW > 1, "waves combine through LDS");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -101,33 +111,38 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 
   const int t0 = tb & ~1;  // pairs start on even positions
   for (int B = t0 + wave * BLK; B < te; B += NW * BLK) {
-    uint4 kr[U], vr[U];
+    // Keys outside [tb, te) are clamped onto an in-range key: every load stays
+    // inside the sequence's referenced pages and the loads need no branches;
+    // the scores of those slots are masked to -inf below.
+    int pg[U];
     bool valid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = B + 2 * ((u >> 1) * TPW + r) + (u & 1);
       valid[u] = (t >= tb) && (t < te);
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (valid[u]) {
-        const int page = bt[t >> a.page_shift];
-        const uint64_t off = ((uint64_t)page * ps + (t & (ps - 1))) * row_stride + (uint64_t)kvh * D + c * EPV;
-        kr[u] = load16(a.k, off, sizeof(T));
-        vr[u] = load16(a.v, off, sizeof(T));
-      }
+      const int tc = min(max(t, tb), te - 1);
+      pg[u] = bt[tc >> a.page_shift];
     }
-
-    // scores, reduced over the LPT lanes of each row
-    float s[U][G];
+    uint4 kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      chunk_scores<T, G>(qv, kr[u], s[u]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        s[u][g] = group_sum<LPT>(s[u][g]);
-        s[u][g] = valid[u] ? s[u][g] : -INFINITY;
-      }
+      const int t = B + 2 * ((u >> 1) * TPW + r) + (u & 1);
+      const int tc = min(max(t, tb), te - 1);
+      const uint64_t off = ((uint64_t)pg[u] * ps + (tc & (ps - 1))) * row_stride + (uint64_t)kvh * D + c * EPV;
+      kr[u] = load16(a.k, off, sizeof(T));
+      vr[u] = load16(a.v, off, sizeof(T));
     }
+
+    // scores, reduced over the LPT lanes of each row (step-major so that
+    // independent DPP operations fill each other's hazard slots)
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) chunk_scores<T, G>(qv, kr[u], s[u]);
+    group_sum_all<LPT, U * G>(&s[0][0]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[u][g] = valid[u] ? s[u][g] : -INFINITY;
 
     // online softmax per row and head, one rescale per block
 #pragma unroll
@@ -136,13 +151,13 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 #pragma unroll
       for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][g]);
       const float mu = (mx == -INFINITY) ? 0.f : mx;
-      const float alpha = exp2f((m[g] - mu) * a.scale_log2);
+      const float alpha = fast_exp2((m[g] - mu) * a.scale_log2);
       m[g] = mx;
       l[g] *= alpha;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) o[g][e] *= alpha;
 #pragma unroll
-      for (int u = 0; u < U; ++u) s[u][g] = exp2f((s[u][g] - mu) * a.scale_log2);
+      for (int u = 0; u < U; ++u) s[u][g] = fast_exp2((s[u][g] - mu) * a.scale_log2);
     }
 
     // P.V
@@ -185,7 +200,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   for (int g = 0; g < G; ++g) {
     const float M = column_max<LPT>(m[g]);
     const float mu = (M == -INFINITY) ? 0.f : M;
-    const float f = exp2f((m[g] - mu) * a.scale_log2);
+    const float f = fast_exp2((m[g] - mu) * a.scale_log2);
     m[g] = M;
     l[g] = column_sum<LPT>(l[g] * f);
 #pragma unroll
@@ -195,89 +210,42 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   // combine the NW waves through LDS: [wave][g][D] sums, then [wave][g] (m, l)
   float* so = smem;
   float* sml = smem + NW * G * D;
-  if (NW > 1) {
-    if (r == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) so[(wave * G + g) * D + c * EPV + e] = o[g][e];
-        if (c == 0) {
-          sml[(wave * G + g) * 2 + 0] = m[g];
-          sml[(wave * G + g) * 2 + 1] = l[g];
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // final: thread x handles (g, d) outputs x, x + blockDim, ...
-  const int nthreads = NW * kWave;
-  for (int idx = threadIdx.x; idx < G * D; idx += nthreads) {
-    const int g = idx / D, d = idx % D;
-    float M, L, O;
-    if (NW > 1) {
-      M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sml[(w * G + g) * 2]);
-      const float mu = (M == -INFINITY) ? 0.f : M;
-      L = 0.f;
-      O = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = exp2f((sml[(w * G + g) * 2] - mu) * a.scale_log2);
-        L += sml[(w * G + g) * 2 + 1] * f;
-        O += so[(w * G + g) * D + d] * f;
-      }
-    } else {
-      // single wave: lane (0, c) holds dims c*EPV .. c*EPV+EPV-1 of every head
-      M = 0.f; L = 0.f; O = 0.f;  // filled below
-    }
-    if (NW > 1) {
-      const int h = kvh * G + g;
-      if (it.slot < 0) {
-        const float val = O / L;
-        if constexpr (sizeof(T) == 2) {
-          reinterpret_cast<uint16_t*>(a.out)[((uint64_t)qi * a.hq + h) * D + d] =
-              (uint16_t)(pack_bf16(val, 0.f) & 0xFFFFu);
-        } else {
-          reinterpret_cast<float*>(a.out)[((uint64_t)qi * a.hq + h) * D + d] = val;
-        }
-        if (a.lse && d == 0) a.lse[(uint64_t)qi * a.hq + h] = M * a.scale + logf(L);
-      } else {
-        a.ws_o[((uint64_t)it.slot * G + g) * D + d] = O;
-        if (d == 0) {
-          a.ws_ml[((uint64_t)it.slot * G + g) * 2 + 0] = M * a.scale_log2;
-          a.ws_ml[((uint64_t)it.slot * G + g) * 2 + 1] = L;
-        }
-      }
-    }
-  }
-  if (NW == 1 && r == 0) {
+  if (r == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int h = kvh * G + g;
-      if (it.slot < 0) {
-        const float inv = 1.f / l[g];
-        if constexpr (sizeof(T) == 2) {
-          uint4 w;
-          w.x = pack_bf16(o[g][0] * inv, o[g][1] * inv);
-          w.y = pack_bf16(o[g][2] * inv, o[g][3] * inv);
-          w.z = pack_bf16(o[g][4] * inv, o[g][5] * inv);
-          w.w = pack_bf16(o[g][6] * inv, o[g][7] * inv);
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * a.hq + h) * D + c * EPV) = w;
-        } else {
-          float4 w = make_float4(o[g][0] * inv, o[g][1] * inv, o[g][2] * inv, o[g][3] * inv);
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + ((uint64_t)qi * a.hq + h) * D + c * EPV) = w;
-        }
-        if (a.lse && c == 0) a.lse[(uint64_t)qi * a.hq + h] = m[g] * a.scale + logf(l[g]);
-      } else {
-        float* dst = a.ws_o + ((uint64_t)it.slot * G + g) * D + c * EPV;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) dst[e] = o[g][e];
-        if (c == 0) {
-          a.ws_ml[((uint64_t)it.slot * G + g) * 2 + 0] = m[g] * a.scale_log2;
-          a.ws_ml[((uint64_t)it.slot * G + g) * 2 + 1] = l[g];
-        }
+      for (int e = 0; e < EPV; ++e) so[(wave * G + g) * D + c * EPV + e] = o[g][e];
+      if (c == 0) {
+        sml[(wave * G + g) * 2 + 0] = m[g];
+        sml[(wave * G + g) * 2 + 1] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+
+  // thread x finalises outputs (g, d) = x, x + blockDim, ...
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+    const int g = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sml[(w * G + g) * 2]);
+    const float mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2((sml[(w * G + g) * 2] - mu) * a.scale_log2);
+      L += sml[(w * G + g) * 2 + 1] * f;
+      O += so[(w * G + g) * D + d] * f;
+    }
+    const int h = kvh * G + g;
+    if (it.slot < 0) {
+      store_out<T>(a.out, ((uint64_t)qi * a.hq + h) * D + d, O / L);
+      if (a.lse && d == 0) a.lse[(uint64_t)qi * a.hq + h] = M * a.scale + logf(L);
+    } else {
+      a.ws_o[((uint64_t)it.slot * G + g) * D + d] = O;
+      if (d == 0) {
+        a.ws_ml[((uint64_t)it.slot * G + g) * 2 + 0] = M * a.scale_log2;
+        a.ws_ml[((uint64_t)it.slot * G + g) * 2 + 1] = L;
       }
     }
   }
@@ -286,28 +254,42 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 // Log-sum-exp merge of split partials (ruDNN `attention_into_split`: merge the
 // fp32 statistics; the weights are alice-llm `lse_combine`'s): for each head
 // of the group, M = max_j m_j, w_j = 2^(m_j - M), out = sum_j w_j o_j / sum_j
-// w_j l_j, lse = ln 2 * (M + log2 sum_j w_j l_j).
+// w_j l_j, lse = ln 2 * (M + log2 sum_j w_j l_j).  All loads of a row are
+// issued before any arithmetic (up to kMergeUnroll splits at a time).
+constexpr int kMergeUnroll = 16;
+
 template <typename T, int D, int G>
 __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& mi) {
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
     const int g = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int j = 0; j < mi.nsplit; ++j) M = fmaxf(M, a.ws_ml[((uint64_t)(mi.slot + j) * G + g) * 2]);
-    const float mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, O = 0.f;
-    for (int j = 0; j < mi.nsplit; ++j) {
-      const uint64_t sl = (uint64_t)(mi.slot + j) * G + g;
-      const float w = exp2f(a.ws_ml[sl * 2] - mu);
-      L += a.ws_ml[sl * 2 + 1] * w;
-      O += a.ws_o[sl * D + d] * w;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int j0 = 0; j0 < mi.nsplit; j0 += kMergeUnroll) {
+      float mj[kMergeUnroll], lj[kMergeUnroll], oj[kMergeUnroll];
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int j = j0 + u;
+        const uint64_t sl = (uint64_t)(mi.slot + min(j, mi.nsplit - 1)) * G + g;
+        mj[u] = a.ws_ml[sl * 2];
+        lj[u] = a.ws_ml[sl * 2 + 1];
+        oj[u] = a.ws_o[sl * D + d];
+        if (j >= mi.nsplit) mj[u] = -INFINITY;
+      }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) Mn = fmaxf(Mn, mj[u]);
+      const float f = fast_exp2(M - Mn);  // M = -inf on the first pass: f = 0 and L = O = 0
+      L *= f;
+      O *= f;
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const float w = fast_exp2(mj[u] - Mn);
+        L += lj[u] * w;
+        O += oj[u] * w;
+      }
+      M = Mn;
     }
     const int h = mi.kvh * G + g;
-    const float val = O / L;
-    if constexpr (sizeof(T) == 2) {
-      reinterpret_cast<uint16_t*>(a.out)[((uint64_t)mi.q * a.hq + h) * D + d] = (uint16_t)(pack_bf16(val, 0.f) & 0xFFFFu);
-    } else {
-      reinterpret_cast<float*>(a.out)[((uint64_t)mi.q * a.hq + h) * D + d] = val;
-    }
+    store_out<T>(a.out, ((uint64_t)mi.q * a.hq + h) * D + d, O / L);
     if (a.lse && d == 0) a.lse[(uint64_t)mi.q * a.hq + h] = (M + log2f(L)) * 0.69314718055994530942f;
   }
 }

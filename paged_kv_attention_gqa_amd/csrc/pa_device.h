@@ -18,8 +18,8 @@ constexpr int kWave = 64;
 // tile of consecutive queries of one sequence and one KV head.
 struct WorkItem {
   int32_t kind;       // kDecode / kPrefill
-  int32_t seq;        // sequence index (row of the block table)
   int32_t kvh;        // KV head
+  int32_t seq;        // sequence index (row of the block table)
   int32_t q_begin;    // first packed query
   int32_t q_count;    // number of queries (decode: 1)
   int32_t tok_begin;  // first logical key position visited (inclusive)
@@ -83,6 +83,40 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 64) x += __shfl_xor(x, 32);
   return x;
 }
+
+// group_sum over N values at once, one reduction step at a time across all
+// values (independent DPP operations back to back).
+template <int N, int COUNT>
+__device__ __forceinline__ void group_sum_all(float* x) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i) x[i] += dpp<kDppXor1>(x[i]);
+  }
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i) x[i] += dpp<kDppXor2>(x[i]);
+  }
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i) x[i] += dpp<kDppHalfMirror>(x[i]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i) x[i] += dpp<kDppMirror>(x[i]);
+  }
+  if constexpr (N >= 32) {
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i) x[i] += __shfl_xor(x[i], 16);
+  }
+  if constexpr (N >= 64) {
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i) x[i] += __shfl_xor(x[i], 32);
+  }
+}
+
+// 2^x on the transcendental unit (v_exp_f32).  Results below the normal range
+// flush to zero, which only affects softmax weights under 2^-126.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Combine across lanes whose index differs by a multiple of STRIDE (the
 // other lanes of the same column), STRIDE * COUNT = 64.

@@ -16,6 +16,7 @@ __global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(KernelArgs 
   decode_item<T, D, G, kDecodeWaves, kDecodeUnroll>(a, it, smem);
 }
 
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(KernelArgs a, const MergeItem* merges) {
   const MergeItem mi = merges[blockIdx.x];
@@ -36,6 +37,7 @@ hipError_t launch_decode_t(const KernelArgs& a, int n_items, const MergeItem* me
   }
   return hipSuccess;
 }
+
 
 template <typename T, int D, int G>
 hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, hipStream_t stream) {
@@ -79,6 +81,7 @@ template <typename T, int D, int G>
 struct DecodeSel {
   static constexpr LaunchFn fn = launch_decode_t<T, D, G>;
 };
+
 template <typename T, int D, int G>
 struct MergeSel {
   static constexpr LaunchFn fn = launch_merge_t<T, D, G>;
@@ -97,16 +100,17 @@ hipError_t launch_gqa_main(int dtype, int d, int g, int n_decode, int n_prefill,
   return f ? f(a, n_decode, nullptr, 0, stream) : hipErrorInvalidValue;
 }
 
-bool mla_supported(int, int, int, int) { return false; }
-hipError_t launch_mla_main(int, const KernelArgs&, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_mla_merge(int, const KernelArgs&, const MergeItem*, int, hipStream_t) {
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream) {
   LaunchFn f = pick<MergeSel>(dtype, d, g);
   return f ? f(a, 0, merges, n_merges, stream) : hipErrorInvalidValue;
 }
+
+bool mla_supported(int, int, int, int) { return false; }
+hipError_t launch_mla_merge(int, const KernelArgs&, const MergeItem*, int, hipStream_t) {
+  return hipErrorInvalidValue;
+}
+hipError_t launch_mla_main(int, const KernelArgs&, hipStream_t) { return hipErrorInvalidValue; }
+
 
 }  // namespace pa

@@ -14,6 +14,7 @@ bool prefill_supported(int dtype, int d, int g);
 // Main GQA launch over a.items: decode-only, prefill-only or one mixed launch.
 hipError_t launch_gqa_main(int dtype, int d, int g, int n_decode, int n_prefill, const KernelArgs& a,
                            hipStream_t stream);
+// Log-sum-exp merge of split rows into the output.
 hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream);
 
@@ -22,5 +23,6 @@ bool mla_supported(int dtype, int h, int r, int p);
 hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream);
 hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream);
+
 
 }  // namespace pa

@@ -45,7 +45,7 @@ class GqaRun:
         self.out = torch.empty((b.num_queries, b.hq, b.dv), dtype=tdt, device="cuda")
         self.lse = torch.empty((b.num_queries, b.hq), dtype=torch.float32, device="cuda") if with_lse else None
         nbytes = pa.pa_plan_workspace_bytes(self.plan, b.dv)
-        self.workspace = torch.empty(max(nbytes, 1) // 4 + 64, dtype=torch.float32, device="cuda") if nbytes else None
+        self.workspace = torch.zeros(max(nbytes, 1) // 4 + 64, dtype=torch.float32, device="cuda") if nbytes else None
         self.info = pa.pa_plan_get_info(self.plan)
 
     def __call__(self, event_after_main=None):
@@ -73,7 +73,7 @@ class MlaRun:
         self.out = torch.empty((m.num_queries, m.heads, m.r), dtype=torch.bfloat16, device="cuda")
         self.lse = torch.empty((m.num_queries, m.heads), dtype=torch.float32, device="cuda") if with_lse else None
         nbytes = pa.pa_plan_workspace_bytes(self.plan, m.r)
-        self.workspace = torch.empty(max(nbytes, 1) // 4 + 64, dtype=torch.float32, device="cuda") if nbytes else None
+        self.workspace = torch.zeros(max(nbytes, 1) // 4 + 64, dtype=torch.float32, device="cuda") if nbytes else None
         self.info = pa.pa_plan_get_info(self.plan)
 
     def __call__(self, event_after_main=None):
