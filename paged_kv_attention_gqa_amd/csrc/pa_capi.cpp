@@ -210,9 +210,9 @@ void build_work(pa_plan* p) {
   p->items.insert(p->items.end(), dec.begin(), dec.end());
 }
 
-// Workspace: partial sums [slots, G, Dv] | (max, sum) [slots, G, 2].
+// Workspace: partial sums [slots, G, Dv] | (max, sum, unrounded sum) [slots, G, 3].
 size_t ws_o_bytes(const pa_plan* p, int dv) { return align_up((size_t)p->n_slots * p->group() * dv * 4, kAlign); }
-size_t ws_ml_bytes(const pa_plan* p) { return align_up((size_t)p->n_slots * p->group() * 2 * 4, kAlign); }
+size_t ws_ml_bytes(const pa_plan* p) { return align_up((size_t)p->n_slots * p->group() * 3 * 4, kAlign); }
 
 size_t workspace_bytes_for(const pa_plan* p, int dv) {
   if (p->n_slots == 0) return 0;

@@ -72,7 +72,7 @@ __device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& 
 
 // Decode body.  NW waves share one item: wave w takes key blocks w, w+NW, ...
 // and the waves' statistics are combined through LDS at the end.
-// smem must hold NW * G * (D + 2) floats.
+// smem must hold NW * G * (D + 3) floats.
 template <typename T, int D, int G, int NW, int U>
 __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem& it, float* smem) {
   constexpr int EPV = Vec16<T>::kElems;  // elements per 16-byte chunk
@@ -100,11 +100,15 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   for (int g = 0; g < G; ++g)
     qv[g] = load16(a.q, ((uint64_t)qi * a.hq + (uint64_t)kvh * G + g) * D + c * EPV, sizeof(T));
 
-  float m[G], l[G], o[G][EPV];
+  // l sums the weights as the P.V products used them (bf16-rounded for bf16
+  // data) and normalises the output; lx sums the unrounded weights for the
+  // logsumexp.
+  float m[G], l[G], lx[G], o[G][EPV];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
+    lx[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) o[g][e] = 0.f;
   }
@@ -154,6 +158,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
       const float alpha = fast_exp2((m[g] - mu) * a.scale_log2);
       m[g] = mx;
       l[g] *= alpha;
+      lx[g] *= alpha;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) o[g][e] *= alpha;
 #pragma unroll
@@ -176,6 +181,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
         for (int g = 0; g < G; ++g) {
           const uint32_t pp = pack_bf16(s[u][g], s[u + 1][g]);
           l[g] += bf16_lo(pp) + bf16_hi(pp);
+          lx[g] += s[u][g] + s[u + 1][g];
 #pragma unroll
           for (int e = 0; e < EPV; ++e) o[g][e] = dot2_bf16(vp[e], pp, o[g][e]);
         }
@@ -188,6 +194,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           l[g] += s[u][g];
+          lx[g] += s[u][g];
 #pragma unroll
           for (int e = 0; e < EPV; ++e) o[g][e] = fmaf(s[u][g], vf[e], o[g][e]);
         }
@@ -203,11 +210,12 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
     const float f = fast_exp2((m[g] - mu) * a.scale_log2);
     m[g] = M;
     l[g] = column_sum<LPT>(l[g] * f);
+    lx[g] = column_sum<LPT>(lx[g] * f);
 #pragma unroll
     for (int e = 0; e < EPV; ++e) o[g][e] = column_sum<LPT>(o[g][e] * f);
   }
 
-  // combine the NW waves through LDS: [wave][g][D] sums, then [wave][g] (m, l)
+  // combine the NW waves through LDS: [wave][g][D] sums, then [wave][g] (m, l, lx)
   float* so = smem;
   float* sml = smem + NW * G * D;
   if (r == 0) {
@@ -216,8 +224,9 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 #pragma unroll
       for (int e = 0; e < EPV; ++e) so[(wave * G + g) * D + c * EPV + e] = o[g][e];
       if (c == 0) {
-        sml[(wave * G + g) * 2 + 0] = m[g];
-        sml[(wave * G + g) * 2 + 1] = l[g];
+        sml[(wave * G + g) * 3 + 0] = m[g];
+        sml[(wave * G + g) * 3 + 1] = l[g];
+        sml[(wave * G + g) * 3 + 2] = lx[g];
       }
     }
   }
@@ -228,24 +237,26 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
     const int g = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sml[(w * G + g) * 2]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sml[(w * G + g) * 3]);
     const float mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, O = 0.f;
+    float L = 0.f, LX = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2((sml[(w * G + g) * 2] - mu) * a.scale_log2);
-      L += sml[(w * G + g) * 2 + 1] * f;
+      const float f = fast_exp2((sml[(w * G + g) * 3] - mu) * a.scale_log2);
+      L += sml[(w * G + g) * 3 + 1] * f;
+      LX += sml[(w * G + g) * 3 + 2] * f;
       O += so[(w * G + g) * D + d] * f;
     }
     const int h = kvh * G + g;
     if (it.slot < 0) {
       store_out<T>(a.out, ((uint64_t)qi * a.hq + h) * D + d, O / L);
-      if (a.lse && d == 0) a.lse[(uint64_t)qi * a.hq + h] = M * a.scale + logf(L);
+      if (a.lse && d == 0) a.lse[(uint64_t)qi * a.hq + h] = M * a.scale + logf(LX);
     } else {
       a.ws_o[((uint64_t)it.slot * G + g) * D + d] = O;
       if (d == 0) {
-        a.ws_ml[((uint64_t)it.slot * G + g) * 2 + 0] = M * a.scale_log2;
-        a.ws_ml[((uint64_t)it.slot * G + g) * 2 + 1] = L;
+        a.ws_ml[((uint64_t)it.slot * G + g) * 3 + 0] = M * a.scale_log2;
+        a.ws_ml[((uint64_t)it.slot * G + g) * 3 + 1] = L;
+        a.ws_ml[((uint64_t)it.slot * G + g) * 3 + 2] = LX;
       }
     }
   }
@@ -262,15 +273,16 @@ template <typename T, int D, int G>
 __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& mi) {
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
     const int g = idx / D, d = idx % D;
-    float M = -INFINITY, L = 0.f, O = 0.f;
+    float M = -INFINITY, L = 0.f, LX = 0.f, O = 0.f;
     for (int j0 = 0; j0 < mi.nsplit; j0 += kMergeUnroll) {
-      float mj[kMergeUnroll], lj[kMergeUnroll], oj[kMergeUnroll];
+      float mj[kMergeUnroll], lj[kMergeUnroll], lxj[kMergeUnroll], oj[kMergeUnroll];
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
         const int j = j0 + u;
         const uint64_t sl = (uint64_t)(mi.slot + min(j, mi.nsplit - 1)) * G + g;
-        mj[u] = a.ws_ml[sl * 2];
-        lj[u] = a.ws_ml[sl * 2 + 1];
+        mj[u] = a.ws_ml[sl * 3];
+        lj[u] = a.ws_ml[sl * 3 + 1];
+        lxj[u] = a.ws_ml[sl * 3 + 2];
         oj[u] = a.ws_o[sl * D + d];
         if (j >= mi.nsplit) mj[u] = -INFINITY;
       }
@@ -279,18 +291,20 @@ __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& 
       for (int u = 0; u < kMergeUnroll; ++u) Mn = fmaxf(Mn, mj[u]);
       const float f = fast_exp2(M - Mn);  // M = -inf on the first pass: f = 0 and L = O = 0
       L *= f;
+      LX *= f;
       O *= f;
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
         const float w = fast_exp2(mj[u] - Mn);
         L += lj[u] * w;
+        LX += lxj[u] * w;
         O += oj[u] * w;
       }
       M = Mn;
     }
     const int h = mi.kvh * G + g;
     store_out<T>(a.out, ((uint64_t)mi.q * a.hq + h) * D + d, O / L);
-    if (a.lse && d == 0) a.lse[(uint64_t)mi.q * a.hq + h] = (M + log2f(L)) * 0.69314718055994530942f;
+    if (a.lse && d == 0) a.lse[(uint64_t)mi.q * a.hq + h] = (M + log2f(LX)) * 0.69314718055994530942f;
   }
 }
 

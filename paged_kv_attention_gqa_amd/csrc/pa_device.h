@@ -44,7 +44,7 @@ struct KernelArgs {
   void* out;              // [Q, Hq, Dv]
   float* lse;             // [Q, Hq] or null
   float* ws_o;            // split partials: [slots, G, Dv] unnormalised sums
-  float* ws_ml;           // split partials: [slots, G, 2] = (running max in log2 units, sum)
+  float* ws_ml;           // split partials: [slots, G, 3] = (max in log2 units, sum, unrounded sum)
   const int32_t* block_table;  // [S, W]
   const int32_t* q_pos;        // [Q]
   const int32_t* seq_lens;     // [S]

@@ -2,6 +2,7 @@
 // only through the launch_* functions declared in pa_launch.h.
 #include "pa_decode.h"
 #include "pa_launch.h"
+#include "pa_prefill.h"
 
 namespace pa {
 
@@ -11,11 +12,36 @@ constexpr int kDecodeUnroll = 8;
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(KernelArgs a) {
-  __shared__ float smem[kDecodeWaves * G * (D + 2)];
+  __shared__ float smem[kDecodeWaves * G * (D + 3)];
   const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
   decode_item<T, D, G, kDecodeWaves, kDecodeUnroll>(a, it, smem);
 }
 
+
+// One launch for plans with prefill tiles: decode items and prefill tiles
+// share the grid (packed decode + chunked prefill in one dispatch).
+template <typename T, int D, int G>
+struct MixedShape {
+  static constexpr bool kMfma = sizeof(T) == 2 && (D == 64 || D == 128) && G <= 128;
+  static constexpr int kDecodeBytes = kDecodeWaves * G * (D + 3) * 4;
+  static constexpr int kPrefillBytes = kMfma ? PrefillSmem<(D <= 128 ? D : 128)>::kBytes : 0;
+  static constexpr int kBytes = kDecodeBytes > kPrefillBytes ? kDecodeBytes : kPrefillBytes;
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecodeWaves* kWave) void mixed_kernel(KernelArgs a) {
+  static_assert(kDecodeWaves == kPrefillWaves, "decode and prefill share the workgroup shape");
+  __shared__ __attribute__((aligned(16))) char smem[MixedShape<T, D, G>::kBytes];
+  const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
+  if (it.kind == kPrefill) {
+    if constexpr (MixedShape<T, D, G>::kMfma)
+      prefill_item<D, G>(a, it, smem);
+    else
+      prefill_item_by_queries<T, D, G, kDecodeWaves, kDecodeUnroll>(a, it, reinterpret_cast<float*>(smem));
+  } else {
+    decode_item<T, D, G, kDecodeWaves, kDecodeUnroll>(a, it, reinterpret_cast<float*>(smem));
+  }
+}
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(KernelArgs a, const MergeItem* merges) {
@@ -38,6 +64,15 @@ hipError_t launch_decode_t(const KernelArgs& a, int n_items, const MergeItem* me
   return hipSuccess;
 }
 
+
+template <typename T, int D, int G>
+hipError_t launch_mixed_t(const KernelArgs& a, int n_items, const MergeItem*, int, hipStream_t stream) {
+  if (n_items > 0) {
+    hipLaunchKernelGGL((mixed_kernel<T, D, G>), dim3(n_items), dim3(kDecodeWaves * kWave), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
 
 template <typename T, int D, int G>
 hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, hipStream_t stream) {
@@ -83,6 +118,10 @@ struct DecodeSel {
 };
 
 template <typename T, int D, int G>
+struct MixedSel {
+  static constexpr LaunchFn fn = launch_mixed_t<T, D, G>;
+};
+template <typename T, int D, int G>
 struct MergeSel {
   static constexpr LaunchFn fn = launch_merge_t<T, D, G>;
 };
@@ -91,13 +130,12 @@ struct MergeSel {
 
 bool gqa_supported(int dtype, int d, int g) { return pick<DecodeSel>(dtype, d, g) != nullptr; }
 
-bool prefill_supported(int, int, int) { return false; }
+bool prefill_supported(int dtype, int d, int g) { return pick<MixedSel>(dtype, d, g) != nullptr; }
 
 hipError_t launch_gqa_main(int dtype, int d, int g, int n_decode, int n_prefill, const KernelArgs& a,
                            hipStream_t stream) {
-  if (n_prefill > 0) return hipErrorInvalidValue;
-  LaunchFn f = pick<DecodeSel>(dtype, d, g);
-  return f ? f(a, n_decode, nullptr, 0, stream) : hipErrorInvalidValue;
+  LaunchFn f = n_prefill > 0 ? pick<MixedSel>(dtype, d, g) : pick<DecodeSel>(dtype, d, g);
+  return f ? f(a, n_decode + n_prefill, nullptr, 0, stream) : hipErrorInvalidValue;
 }
 
 hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,

@@ -18,8 +18,10 @@ logical order; values are N(0, 1) float32 rounded to the storage type.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Callable, Dict, Optional
 
 import numpy as np
@@ -28,14 +30,20 @@ BF16_NAN = np.uint16(0x7FC0)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bit patterns, round to nearest even; NaN -> quiet NaN."""
+    """float32 -> bf16 bit patterns, round to nearest even; NaN -> quiet NaN.
+    (For every non-NaN input the 32-bit sum below cannot overflow.)"""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r[nan] = BF16_NAN
-    return r
+        out[nan] = BF16_NAN
+    return out
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -43,15 +51,46 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _normal(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 24) -> np.ndarray:
-    """N(0,1) float32 draws in the storage type, generated in chunks so large
-    pools do not need a full float32 temporary."""
+_CHUNK = 1 << 22
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _chunked(rng: np.random.Generator, n: int, fill):
+    """Run fill(child_generator, start, end) over fixed 4M-element chunks.
+    Each chunk draws from its own child stream spawned from one seed taken
+    from `rng`, so the values do not depend on the thread count."""
+    seed = int(rng.integers(0, 2 ** 63 - 1))
+    starts = list(range(0, n, _CHUNK))
+    children = np.random.SeedSequence(seed).spawn(len(starts))
+
+    def work(k):
+        fill(np.random.default_rng(children[k]), starts[k], min(n, starts[k] + _CHUNK))
+
+    if len(starts) <= 1:
+        for k in range(len(starts)):
+            work(k)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(len(starts))))
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """N(0,1) float32 draws rounded to the storage type."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        x = rng.standard_normal(e - s, dtype=np.float32)
+
+    def fill(g, s, e):
+        x = g.standard_normal(e - s, dtype=np.float32)
         out[s:e] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    _chunked(rng, n, fill)
     return out.reshape(shape)
 
 
@@ -248,17 +287,20 @@ def config_bf16_mixed_batch(seed: int = 4) -> PagedBatch:
                       bt, ps, pool, hq, hkv, d, d, 1.0 / math.sqrt(128.0), True, 4096, q, k, v, seed, 16)
 
 
-def _unit_rms_bf16(rng: np.random.Generator, shape, chunk_rows: int = 1 << 15) -> np.ndarray:
+def _unit_rms_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     """N(0,1) rows rescaled in float32 to unit RMS (no epsilon, no weight),
     then rounded to bf16."""
-    rows = int(np.prod(shape[:-1]))
     width = shape[-1]
-    out = np.empty((rows, width), dtype=np.uint16)
-    for s in range(0, rows, chunk_rows):
-        e = min(rows, s + chunk_rows)
-        x = rng.standard_normal((e - s, width), dtype=np.float32)
+    rows = int(np.prod(shape[:-1]))
+    out = np.empty(rows * width, dtype=np.uint16)
+    assert _CHUNK % width == 0
+
+    def fill(g, s, e):
+        x = g.standard_normal(e - s, dtype=np.float32).reshape(-1, width)
         rms = np.sqrt(np.mean(x * x, axis=1, dtype=np.float32), dtype=np.float32)
-        out[s:e] = f32_to_bf16_bits(x / rms[:, None])
+        out[s:e] = f32_to_bf16_bits(x / rms[:, None]).reshape(-1)
+
+    _chunked(rng, rows * width, fill)
     return out.reshape(shape)
 
 
