@@ -88,32 +88,63 @@ def _traffic(kernel_key):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(b, mla, unit_bytes):
+def cpu_baseline(b, mla, work, hbm):
+    """The fp64 oracle on the host cores, over the whole workload (decode)
+    or over a bounded sample of query rows (prefill), in the GPU's unit."""
     import oracle
     n = oracle.default_threads()
+    rows = None
+    frac = 1.0
+    if not hbm:
+        total = b.num_queries * b.hq
+        rows = np.random.default_rng(0).choice(total, size=min(total, 8192), replace=False)
+        frac = len(rows) / total
     t0 = time.perf_counter()
     if mla:
-        oracle.mla(b, nthreads=n)
+        oracle.mla(b, rows=rows, nthreads=n)
     else:
-        oracle.attention(b, nthreads=n)
+        oracle.attention(b, rows=rows, nthreads=n)
     dt = time.perf_counter() - t0
-    return {"value": round(unit_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
-            "sample": f"the full workload, one pass ({dt:.2f} s)"}
+    scaled = work * frac / dt
+    if hbm:
+        return {"value": round(scaled / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+                "sample": f"the full workload, one pass ({dt:.2f} s)"}
+    return {"value": round(scaled / 1e12, 6), "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+            "sample": f"{len(rows)} random (query, head) rows of the workload ({dt:.2f} s), "
+                      "flops scaled by the sampled fraction"}
 
 
-def run(args):
+def _is_mla(b):
+    return hasattr(b, "latent")
+
+
+def split_work(b):
+    """Algorithmic work split by role: (decode K/V bytes, prefill flops) for
+    GQA batches, where decode queries are sequences with at most 4 queries."""
+    vis = visible_counts(b)
+    counts = np.diff(b.cu_q)
+    es = 4 if b.dtype == "f32" else 2
+    dec_b, pre_f = 0, 0
+    for s in range(b.num_seqs):
+        v = int(vis[b.cu_q[s]:b.cu_q[s + 1]].sum())
+        if counts[s] <= 4:
+            dec_b += v * b.hkv * (b.d + b.dv) * es
+        else:
+            pre_f += v * b.hq * 2 * (b.d + b.dv)
+    return dec_b, pre_f
+
+
+def measure(name, steps, warmup, split_tokens=0):
+    """Time `steps` forward passes of workload `name` (after `warmup`) with HIP
+    events around the main kernel and the wall clock around the whole loop."""
     import torch
-    import paged_kv_attention_gqa_amd as pa  # noqa: F401  (fails loudly if the library is missing)
     from synth import CONFIGS
-    from tests.gpu_harness import GqaRun, MlaRun, to_torch
+    from tests.gpu_harness import GqaRun, MlaRun
 
-    pa.load_library()
-    torch.cuda.set_device(0)
-    b = CONFIGS[args.workload]()
-    mla = hasattr(b, "latent")
-    run_ = MlaRun(b, split_tokens=args.split_tokens) if mla else GqaRun(b, split_tokens=args.split_tokens,
-                                                                          with_lse=False)
-    bytes_alg, flops_alg = algorithmic_work(b, mla)
+    b = CONFIGS[name]()
+    mla = _is_mla(b)
+    run_ = MlaRun(b, split_tokens=split_tokens, with_lse=False) if mla else \
+        GqaRun(b, split_tokens=split_tokens, with_lse=False)
 
     # Rotate between pool copies so consecutive steps do not re-read a
     # cache-resident pool: the copies together exceed the 256 MB MALL twice over.
@@ -125,63 +156,125 @@ def run(args):
         pools.append(tuple(t.clone() for t in pools[0]))
 
     def step(j, ev_mid=None):
-        a, c = pools[j % len(pools)]
+        x, y = pools[j % len(pools)]
         if mla:
-            run_.latent, run_.kpos = a, c
+            run_.latent, run_.kpos = x, y
         else:
-            run_.k, run_.v = a, c
+            run_.k, run_.v = x, y
         run_(event_after_main=ev_mid)
 
-    for j in range(args.warmup):
+    for j in range(warmup):
         step(j)
     torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for e in mids:  # torch creates the HIP event on first record; the library records it again
         e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for j in range(args.steps):
+    for j in range(steps):
         starts[j].record(stream)
         step(j, mids[j])
         ends[j].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    main_ms = float(np.mean([s.elapsed_time(m) for s, m in zip(starts, mids)]))
-    merge_ms = float(np.mean([m.elapsed_time(e) for m, e in zip(mids, ends)]))
-    ms_per_step = wall * 1e3 / args.steps
+    res = {
+        "b": b, "mla": mla, "info": run_.info, "copies": len(pools),
+        "ms_per_step": wall * 1e3 / steps,
+        "main_ms": float(np.mean([x.elapsed_time(y) for x, y in zip(starts, mids)])),
+        "merge_ms": float(np.mean([x.elapsed_time(y) for x, y in zip(mids, ends)])),
+    }
+    del pools, run_
+    torch.cuda.empty_cache()
+    return res
 
-    info = run_.info
-    kernel_key = f"{args.workload}:main"
-    achieved = bytes_alg / (main_ms * 1e-3) / 1e9
+
+def summarize(name, r):
+    """Per-workload rates against the roofline of what bounds it."""
+    b = r["b"]
+    kv_bytes, flops = algorithmic_work(b, r["mla"])
+    main_s = r["main_ms"] * 1e-3
+    step_s = r["ms_per_step"] * 1e-3
+    out = {"workload": name, "ms_per_step": round(r["ms_per_step"], 5), "main_kernel_ms": round(r["main_ms"], 5),
+           "merge_kernel_ms": round(r["merge_ms"], 5), "kv_bytes": kv_bytes, "flops": flops}
+    if r["mla"] or r["info"]["prefill_items"] == 0:
+        out.update(bound="hbm", step_gbs=round(kv_bytes / step_s / 1e9, 2),
+                   kernel_gbs=round(kv_bytes / main_s / 1e9, 2),
+                   frac=round(kv_bytes / main_s / 1e9 / HBM_PEAK_GBS, 4),
+                   step_tflops=round(flops / step_s / 1e12, 3))
+    elif r["info"]["decode_items"] == 0:
+        out.update(bound="mfma", step_tflops=round(flops / step_s / 1e12, 2),
+                   kernel_tflops=round(flops / main_s / 1e12, 2),
+                   frac=round(flops / main_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4))
+    else:
+        dec_b, pre_f = split_work(b)
+        t_bw, t_mf = dec_b / (HBM_PEAK_GBS * 1e9), pre_f / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        out.update(bound="hbm+mfma", decode_kv_bytes=dec_b, prefill_flops=pre_f,
+                   decode_gbs_at_step=round(dec_b / step_s / 1e9, 2),
+                   prefill_tflops_at_step=round(pre_f / step_s / 1e12, 2),
+                   frac=round(max(t_bw, t_mf) / main_s, 4),
+                   frac_sum=round((t_bw + t_mf) / main_s, 4))
+    return out
+
+
+PRIMARY = "bf16_decode_batch"
+SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode")
+
+
+def run(args):
+    import torch
+    import paged_kv_attention_gqa_amd as pa
+
+    pa.load_library()  # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    name = args.workload
+    r = measure(name, args.steps, args.warmup, args.split_tokens)
+    b = r["b"]
+    mla = r["mla"]
+    bytes_alg, flops_alg = algorithmic_work(b, mla)
+    summ = summarize(name, r)
+    hbm = summ["bound"] == "hbm"
+    main_s = r["main_ms"] * 1e-3
+    if hbm:
+        achieved, peak, unit = bytes_alg / main_s / 1e9, HBM_PEAK_GBS, "GB/s"
+        value, vunit = bytes_alg / (r["ms_per_step"] * 1e-3) / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = flops_alg / main_s / 1e12, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+        value, vunit = flops_alg / (r["ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
     result = {
         "metric": METRIC,
-        "value": round(bytes_alg / (ms_per_step * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
+        "value": round(value, 2),
+        "unit": vunit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if b.dtype == "bf16" else "f32",
+        "dtype": b.dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "seed": b.seed, "sequences": b.num_seqs,
+        "config": {"workload": name, "seed": b.seed, "sequences": b.num_seqs,
                    "queries": b.num_queries, "page_size": b.page_size, "max_splits": b.max_splits,
                    **({"heads": b.heads, "rank": b.r, "rope_dim": b.p} if mla else
                       {"hq": b.hq, "hkv": b.hkv, "head_dim": b.d}),
                    "causal": b.causal, "window": b.window, "kv_bytes": bytes_alg, "flops": flops_alg,
-                   "pool_copies_rotated": len(pools)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(kernel_key)},
-        "kernels": {"main_ms": round(main_ms, 5), "merge_ms": round(merge_ms, 5), "plan": info},
+                   "pool_copies_rotated": r["copies"]},
+        "roofline": {"bound": "hbm" if hbm else "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": _traffic(f"{name}:main")},
+        "kernels": {"main_ms": round(r["main_ms"], 5), "merge_ms": round(r["merge_ms"], 5), "plan": r["info"]},
     }
+    if not args.no_secondary and name == PRIMARY:
+        result["secondary"] = []
+        for n in SECONDARY:
+            try:
+                result["secondary"].append(summarize(n, measure(n, args.steps, args.warmup)))
+            except pa.PaError as e:  # a workload this build cannot run is reported, not hidden
+                result["secondary"].append({"workload": n, "error": str(e)})
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(b, mla, bytes_alg)
+        result["cpu_baseline"] = cpu_baseline(b, mla, bytes_alg if hbm else flops_alg, hbm)
     return result
 
 
@@ -193,6 +286,7 @@ def main():
     ap.add_argument("--workload", default="bf16_decode_batch")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "

@@ -13,7 +13,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/paged_attn.h"
+#include "paged_attn.h"
 #include "pa_launch.h"
 
 using pa::MergeItem;

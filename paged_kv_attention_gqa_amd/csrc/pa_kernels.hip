@@ -6,15 +6,31 @@
 
 namespace pa {
 
-// Decode launch shape: 4 waves share one item, 8 key loads per lane per block.
+// Decode launch shape: 4 waves share one item; U key loads per lane per block
+// (fewer for large groups, whose per-key state grows with G).
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeUnroll = 8;
+template <int G>
+struct DecodeUnroll {
+  static constexpr int kValue = G <= 8 ? 4 : 2;
+};
+
+// Occupancy targets (waves per SIMD) the register allocator must meet.
+// Decode streams HBM and wants several workgroups per CU in flight; its
+// registers grow with the group size G (G query rows per lane), so the target
+// drops for large groups rather than spill.  A mixed / prefill workgroup holds
+// 64 KB of LDS, so two fit a CU.
+template <int G>
+struct Occupancy {
+  static constexpr int kDecode = G <= 4 ? 4 : (G <= 8 ? 2 : 1);
+  static constexpr int kMixed = G <= 8 ? 2 : 1;
+};
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves* kWave) void decode_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kDecodeWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kDecode)))
+void decode_kernel(KernelArgs a) {
   __shared__ float smem[kDecodeWaves * G * (D + 3)];
   const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
-  decode_item<T, D, G, kDecodeWaves, kDecodeUnroll>(a, it, smem);
+  decode_item<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, smem);
 }
 
 
@@ -29,7 +45,8 @@ struct MixedShape {
 };
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves* kWave) void mixed_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kDecodeWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kMixed)))
+void mixed_kernel(KernelArgs a) {
   static_assert(kDecodeWaves == kPrefillWaves, "decode and prefill share the workgroup shape");
   __shared__ __attribute__((aligned(16))) char smem[MixedShape<T, D, G>::kBytes];
   const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
@@ -37,9 +54,9 @@ __global__ __launch_bounds__(kDecodeWaves* kWave) void mixed_kernel(KernelArgs a
     if constexpr (MixedShape<T, D, G>::kMfma)
       prefill_item<D, G>(a, it, smem);
     else
-      prefill_item_by_queries<T, D, G, kDecodeWaves, kDecodeUnroll>(a, it, reinterpret_cast<float*>(smem));
+      prefill_item_by_queries<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
   } else {
-    decode_item<T, D, G, kDecodeWaves, kDecodeUnroll>(a, it, reinterpret_cast<float*>(smem));
+    decode_item<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
   }
 }
 

@@ -11,13 +11,13 @@
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation; softmax statistics are
 // fp32 and kept per query row in registers (online softmax across key tiles).
 //
-// Data flow per 64-key tile:
-//   HBM --(16-byte loads, page-gathered)--> registers --> LDS:
-//     K  row-major   [64 keys][D]     (rows padded by 16 bytes)
-//     V^T            [D][64 keys]     (keys permuted to the MFMA k order,
-//                                      16-byte groups XOR-swizzled by dim)
+// Data flow per 64-key tile (two LDS stages, one barrier per tile):
+//   HBM --global_load_lds_dwordx4 (page-gathered, no registers)--> LDS
+//     K, V row-major [64 keys][D], the 16-byte pieces of key row t stored at
+//     piece ^ (t & 7) so that column reads of 8 rows hit 8 bank groups
 //   each wave (32 rows):  S^T[64 x 32] = K . Q^T      (Q^T held in registers)
-//                         O^T[D x 32] += V^T . P^T    (P^T straight from S^T)
+//                         O^T[D x 32] += V^T . P^T    (V^T read with
+//                         ds_read_b64_tr_b16, P^T straight from S^T)
 // In the S^T / O^T accumulator layout every lane owns one query row, so the
 // row max, the rescale and the row sum need at most one cross-lane step.
 #pragma once
@@ -28,6 +28,7 @@
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kPrefillTileKeys = 64;
@@ -36,38 +37,50 @@ constexpr int kPrefillRowsPerWave = 32;
 
 template <int D>
 struct PrefillSmem {
-  static constexpr int kRow = D * 2 + 16;                   // bytes per K row
-  static constexpr int kVRow = kPrefillTileKeys * 2 + 16;  // bytes per V^T row
-  static constexpr int kBytes = kPrefillTileKeys * kRow + D * kVRow;
+  static constexpr int kTile = kPrefillTileKeys * D * 2;  // bytes of one K or V tile
+  static constexpr int kStage = 2 * kTile;
+  static constexpr int kBytes = 2 * kStage;               // two stages
 };
 
 __device__ __forceinline__ floatx16_t mfma_32x32x16(const bf16x8_t& a, const bf16x8_t& b, const floatx16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Position of key t inside the V^T tile: swap bits 2 and 3 so that the eight
-// keys one lane feeds to a P.V k-step are contiguous.
-__device__ __forceinline__ int vt_col(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-// Byte offset of 16-byte group `grp` (8 keys) of V^T row `d`.
-__device__ __forceinline__ int vt_off(int d, int grp, int vrow) { return d * vrow + ((grp ^ ((d >> 3) & 7)) << 4); }
+// 16 bytes from global memory to LDS at (wave-uniform base) + 16 * lane.
+__device__ __forceinline__ void load_to_lds(const void* src, char* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_base), 16, 0, 0);
+}
+
+// Transposed read: in each 16-lane group, lane 4r + j supplies the address of
+// 4 halfwords of row r; lane i receives halfword i % 4 of lane 4r + i / 4's
+// chunk for r = 0..3.
+__device__ __forceinline__ short4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p));
+}
+
+// Byte offset of 16-byte piece `piece` of key row `key` inside a tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int key, int piece) {
+  return key * (D * 2) + ((piece ^ (key & 7)) << 4);
+}
 
 template <int D, int G>
 __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem& it, char* smem) {
   constexpr int NT = kPrefillTileKeys;
-  constexpr int KS = D / 16;      // MFMA k-steps of S^T (over head dims)
-  constexpr int DB = D / 32;      // 32-dim blocks of O^T
-  constexpr int PIECES = D / 8;   // 16-byte pieces per key row
-  constexpr int KROW = PrefillSmem<D>::kRow;
-  constexpr int VROW = PrefillSmem<D>::kVRow;
-  constexpr int NTHR = kPrefillWaves * kWave;
-  constexpr int KCH = NT * PIECES / NTHR;        // K pieces per thread per tile
-  constexpr int VCH = (NT / 2) * PIECES / NTHR;  // V key-pair pieces per thread per tile
-  static_assert(KCH >= 1 && VCH >= 1 && (NT * PIECES) % NTHR == 0, "tile does not divide over the workgroup");
-  static_assert(kPrefillWaves * kPrefillRowsPerWave % G == 0 || G > 128, "rows per tile must hold whole queries");
+  constexpr int KS = D / 16;                         // MFMA k-steps of S^T (over head dims)
+  constexpr int DB = D / 32;                         // 32-dim blocks of O^T
+  constexpr int PIECES = D / 8;                      // 16-byte pieces per key row
+  constexpr int TILE = PrefillSmem<D>::kTile;
+  constexpr int STAGE = PrefillSmem<D>::kStage;
+  constexpr int KEYS_PER_LOAD = kWave / PIECES;      // key rows one wave-wide load covers
+  constexpr int LOADS_PER_TILE = NT / KEYS_PER_LOAD; // per K (or V) tile
+  constexpr int LOADS_PER_WAVE = 2 * LOADS_PER_TILE / kPrefillWaves;
+  static_assert(PIECES >= 8 && kWave % PIECES == 0, "head size must be a multiple of 64");
+  static_assert((2 * LOADS_PER_TILE) % kPrefillWaves == 0, "tile loads must split over the waves");
 
-  char* ks = smem;
-  char* vs = smem + NT * KROW;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -82,8 +95,6 @@ __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem
   const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
   const uint64_t row_stride = (uint64_t)a.hkv * D;
   const uint64_t head_off = (uint64_t)it.kvh * D;
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(a.k);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(a.v);
 
   // Q^T operand: lane (n, h) holds dims 16 ks + 8 h .. +7 of row n
   bf16x8_t qf[KS];
@@ -108,75 +119,66 @@ __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem
     for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
   float m = -INFINITY, l = 0.f, lx = 0.f;  // lx: unrounded weights, for the logsumexp
 
-  // global -> register staging of one tile
-  uint4 kreg[KCH], vreg[VCH][2];
-  auto slot_offset = [&](int t) -> uint64_t {
-    const int tc = min(max(t, tb), te - 1);  // out-of-range keys read an in-range key, masked below
-    const int page = bt[tc >> a.page_shift];
-    return ((uint64_t)page * ps + (tc & (ps - 1))) * row_stride + head_off;
+  // This wave issues loads wave * LOADS_PER_WAVE .. +LOADS_PER_WAVE of each
+  // tile; load i covers K (i < LOADS_PER_TILE) or V rows KEYS_PER_LOAD *
+  // (i % LOADS_PER_TILE) + lane / PIECES at stored piece lane % PIECES.  Page
+  // numbers run one tile ahead of the data.
+  const int my_key_in_load = lane / PIECES;
+  const int my_stored_piece = lane % PIECES;
+  int pg[LOADS_PER_WAVE];
+  auto clamp_key = [&](int t) { return min(max(t, tb), te - 1); };  // out-of-range keys read an in-range key
+  auto load_key = [&](int i) { return KEYS_PER_LOAD * (i % LOADS_PER_TILE) + my_key_in_load; };
+  auto fetch_pages = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < LOADS_PER_WAVE; ++j)
+      pg[j] = bt[clamp_key(t0 + load_key(wave * LOADS_PER_WAVE + j)) >> a.page_shift];
   };
-  auto load_tile = [&](int t0) {
+  auto issue_tile = [&](int t0, char* stage) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = i * NTHR + tid;
-      const int key = c / PIECES, piece = c % PIECES;
-      kreg[i] = *reinterpret_cast<const uint4*>(kpool + slot_offset(t0 + key) + piece * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = i * NTHR + tid;
-      const int pair = c / PIECES, piece = c % PIECES;
-      vreg[i][0] = *reinterpret_cast<const uint4*>(vpool + slot_offset(t0 + 2 * pair) + piece * 8);
-      vreg[i][1] = *reinterpret_cast<const uint4*>(vpool + slot_offset(t0 + 2 * pair + 1) + piece * 8);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = i * NTHR + tid;
-      const int key = c / PIECES, piece = c % PIECES;
-      *reinterpret_cast<uint4*>(ks + key * KROW + piece * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = i * NTHR + tid;
-      const int pair = c / PIECES, piece = c % PIECES;
-      const int col = vt_col(2 * pair);  // even; its odd partner lands next to it
-      const uint32_t w0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-      const uint32_t w1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = piece * 8 + 2 * j;
-        *reinterpret_cast<uint32_t*>(vs + vt_off(d0, col >> 3, VROW) + (col & 7) * 2) = interleave_lo(w0[j], w1[j]);
-        *reinterpret_cast<uint32_t*>(vs + vt_off(d0 + 1, col >> 3, VROW) + (col & 7) * 2) =
-            interleave_hi(w0[j], w1[j]);
-      }
+    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
+      const int i = wave * LOADS_PER_WAVE + j;
+      const int key = load_key(i);
+      const int t = clamp_key(t0 + key);
+      const int piece = my_stored_piece ^ (key & 7);
+      const uint16_t* pool = reinterpret_cast<const uint16_t*>(i < LOADS_PER_TILE ? a.k : a.v);
+      const uint16_t* src = pool + ((uint64_t)pg[j] * ps + (t & (ps - 1))) * row_stride + head_off + piece * 8;
+      load_to_lds(src, stage + (i < LOADS_PER_TILE ? 0 : TILE) + (i % LOADS_PER_TILE) * 1024);
     }
   };
 
   const int t_first = tb & ~(NT - 1);
-  if (t_first < te) load_tile(t_first);
-  for (int t0 = t_first; t0 < te; t0 += NT) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (t0 + NT < te) load_tile(t0 + NT);  // in flight while this tile is computed
+  int stage = 0;
+  if (t_first < te) {
+    fetch_pages(t_first);
+    issue_tile(t_first, smem);
+    fetch_pages(t_first + NT);
+  }
+  for (int t0 = t_first; t0 < te; t0 += NT, stage ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed in LDS
+    __syncthreads();                // ... and every other wave's; the other stage is free
+    if (t0 + NT < te) {             // next tile streams in while this one is computed
+      issue_tile(t0 + NT, smem + (stage ^ 1) * STAGE);
+      fetch_pages(t0 + 2 * NT);
+    }
+    const char* ks = smem + stage * STAGE;
+    const char* vs = ks + TILE;
 
     // tile entirely hidden from every row of this wave?
     const bool hidden = pmax < 0 || (a.causal && t0 > pmax) || (a.window > 0 && t0 + NT - 1 <= pmin - a.window);
     if (hidden) continue;
     const bool full = t0 >= tb && t0 + NT <= te && (!a.causal || t0 + NT - 1 <= pmin) &&
-                      (a.window == 0 || t0 > pmax - a.window) && pmax >= 0;
+                      (a.window == 0 || t0 > pmax - a.window);
 
-    // S^T = K . Q^T : two 32-key blocks
+    // S^T = K . Q^T : two 32-key blocks; lane (n, h) reads dims 16 k + 8 h of key row n
     floatx16_t s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
+      const int key = mb * 32 + n;
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + (mb * 32 + n) * KROW + 32 * k + 16 * h);
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + tile_off<D>(key, 2 * k + h));
         s[mb] = mfma_32x32x16(kf, qf[k], s[mb]);
       }
     }
@@ -206,12 +208,20 @@ __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem
     m = mx;
     l *= alpha;
     lx *= alpha;
+    if (__any(alpha != 1.f)) {  // no row of the wave raised its max: nothing to rescale
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[b][e] *= alpha;
+        for (int e = 0; e < 16; ++e) o[b][e] *= alpha;
+    }
 
-    // P^T operand for k-step kk: elements 8 (kk % 2) .. +7 of block kk / 2
+    // O^T += V^T . P^T.  k-step kk covers keys 16 kk .. +15; lane (n, h) feeds
+    // keys 16 kk + 8 (e/4) + 4 h + e%4 (e = 0..7): elements 8 (kk % 2) + e of
+    // S^T block kk / 2, and the V^T rows of the same keys by two transposed
+    // reads (4 keys each) of dims 32 b + 16 (lane/16 % 2) + lane % 16.
+    const int grp = lane >> 4, gi = lane & 15;
+    const int hh = grp >> 1, d16 = grp & 1;
+    const int rr = gi >> 2, jj = gi & 3;
 #pragma unroll
     for (int kk = 0; kk < NT / 16; ++kk) {
       const int mb = kk >> 1, e0 = 8 * (kk & 1);
@@ -225,10 +235,18 @@ __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem
         lx += p0 + p1;
       }
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      const int key0 = 16 * kk + 4 * hh + rr;  // rows r of the first read; +8 for the second
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        const int d = 32 * b + n;
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vs + vt_off(d, 2 * kk + h, VROW));
+        const int dim = 32 * b + 16 * d16 + 4 * jj;
+        const int piece = dim >> 3, half = (dim & 7) * 2;
+        const short4_t v0 = lds_read_tr16(vs + tile_off<D>(key0, piece) + half);
+        const short4_t v1 = lds_read_tr16(vs + tile_off<D>(key0 + 8, piece) + half);
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
+                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
+                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
+                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
         o[b] = mfma_32x32x16(vf, pf, o[b]);
       }
     }
