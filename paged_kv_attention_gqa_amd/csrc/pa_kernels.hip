@@ -2,6 +2,7 @@
 // only through the launch_* functions declared in pa_launch.h.
 #include "pa_decode.h"
 #include "pa_launch.h"
+#include "pa_mla.h"
 #include "pa_prefill.h"
 
 namespace pa {
@@ -58,6 +59,15 @@ void mixed_kernel(KernelArgs a) {
   } else {
     decode_item<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
   }
+}
+
+// Absorbed-MLA decode: one (query, key range) item per workgroup, 144 KB of
+// LDS (a private two-stage tile ring per wave), one workgroup per CU.
+template <typename T>
+__global__ __launch_bounds__(kMlaWaves* kWave) void mla_kernel(KernelArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[MlaSmem::kBytes];
+  const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
+  mla_item<T>(a, it, smem);
 }
 
 template <typename T, int D, int G>
@@ -161,11 +171,24 @@ hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const 
   return f ? f(a, 0, merges, n_merges, stream) : hipErrorInvalidValue;
 }
 
-bool mla_supported(int, int, int, int) { return false; }
-hipError_t launch_mla_merge(int, const KernelArgs&, const MergeItem*, int, hipStream_t) {
-  return hipErrorInvalidValue;
+bool mla_supported(int dtype, int h, int r, int p) {
+  return dtype == 1 && h == kMlaHeads && r == kMlaRank && p == kMlaRope;
 }
-hipError_t launch_mla_main(int, const KernelArgs&, hipStream_t) { return hipErrorInvalidValue; }
+
+hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream) {
+  if (dtype != 1) return hipErrorInvalidValue;
+  if (a.n_items > 0) {
+    hipLaunchKernelGGL((mla_kernel<uint16_t>), dim3(a.n_items), dim3(kMlaWaves * kWave), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
+                            hipStream_t stream) {
+  if (dtype != 1) return hipErrorInvalidValue;
+  return launch_merge_t<uint16_t, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, stream);
+}
 
 
 }  // namespace pa
