@@ -269,9 +269,11 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 // issued before any arithmetic (up to kMergeUnroll splits at a time).
 constexpr int kMergeUnroll = 16;
 
+// The (g, d) outputs of a row are spread over `chunks` workgroups; this one
+// takes outputs chunk, chunk + chunks, ... in units of blockDim.
 template <typename T, int D, int G>
-__device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& mi) {
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+__device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& mi, int chunk, int chunks) {
+  for (int idx = chunk * blockDim.x + threadIdx.x; idx < G * D; idx += chunks * blockDim.x) {
     const int g = idx / D, d = idx % D;
     float M = -INFINITY, L = 0.f, LX = 0.f, O = 0.f;
     for (int j0 = 0; j0 < mi.nsplit; j0 += kMergeUnroll) {

@@ -161,6 +161,13 @@ __device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// Wave-uniform read of plan metadata through the constant address space.
+// The plan's device buffer is written only by its upload, never by a kernel,
+// so the load may go through the scalar cache (s_load) and count against the
+// scalar counter instead of the vector-memory counter.
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+__device__ __forceinline__ int load_uniform(const int32_t* p, int idx) { return ((const_i32_t*)p)[idx]; }
+
 // Map a dispatch index to an item index so that consecutive items land on the
 // same XCD: the hardware deals workgroups round-robin over the 8 XCDs.
 __device__ __forceinline__ int xcd_item(int b, int n) {

@@ -61,19 +61,21 @@ void mixed_kernel(KernelArgs a) {
   }
 }
 
-// Absorbed-MLA decode: one (query, key range) item per workgroup, 144 KB of
-// LDS (a private two-stage tile ring per wave), one workgroup per CU.
+// Absorbed-MLA decode: one (query, key range) item per workgroup, a 72 KB
+// LDS tile ring, two workgroups per CU.
 template <typename T>
-__global__ __launch_bounds__(kMlaWaves* kWave) void mla_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_eu(2))) void mla_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[MlaSmem::kBytes];
   const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
   mla_item<T>(a, it, smem);
 }
 
+// grid: (split rows, chunks of 256 outputs per row)
+constexpr int kMergeThreads = 256;
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void merge_kernel(KernelArgs a, const MergeItem* merges) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelArgs a, const MergeItem* merges) {
   const MergeItem mi = merges[blockIdx.x];
-  merge_row<T, D, G>(a, mi);
+  merge_row<T, D, G>(a, mi, blockIdx.y, gridDim.y);
 }
 
 namespace {
@@ -104,7 +106,8 @@ hipError_t launch_mixed_t(const KernelArgs& a, int n_items, const MergeItem*, in
 template <typename T, int D, int G>
 hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, hipStream_t stream) {
   if (n_merges > 0) {
-    hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3(n_merges), dim3(256), 0, stream, a, merges);
+    const int chunks = (G * D + kMergeThreads - 1) / kMergeThreads;
+    hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3(n_merges, chunks), dim3(kMergeThreads), 0, stream, a, merges);
     return hipGetLastError();
   }
   return hipSuccess;

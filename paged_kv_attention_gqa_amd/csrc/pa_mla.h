@@ -14,11 +14,15 @@
 // N dimension:
 //   S^T[16 keys x 16 heads] = latent . q_abs^T + kpos . q_rope^T   (16x16x32)
 //   O^T[R x 16 heads]      += latent^T . P^T                      (16x16x16)
-// Each wave streams its own 16-key tiles (wave w takes tiles w, w+4, ...)
-// into a private two-stage LDS ring with global_load_lds_dwordx4 (16-byte
-// pieces of key row t stored at piece ^ (t & 7)); latent^T fragments come from
-// ds_read_b64_tr_b16.  Every lane owns one head's column, so softmax needs two
-// cross-lane steps per tile.  The four waves merge through LDS at the end.
+// The four waves of a workgroup share a four-stage LDS ring of 16-key tiles
+// (three in flight while one is used, one barrier per tile), loaded with
+// global_load_lds_dwordx4 (16-byte pieces of key row t stored at piece ^ (t &
+// 7)); block-table entries are wave-uniform scalar loads, so the
+// vector-memory counter counts tile loads only.  Every wave computes the
+// small score tile (so softmax statistics agree across waves without any
+// exchange) and owns R / 4 = 128 output dims; latent^T fragments come from
+// ds_read_b64_tr_b16.  Every lane owns one head's column, so softmax needs
+// two cross-lane steps per tile.
 #pragma once
 
 #include "pa_decode.h"
@@ -27,7 +31,6 @@
 
 namespace pa {
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMlaHeads = 16;
@@ -35,16 +38,13 @@ constexpr int kMlaRank = 512;
 constexpr int kMlaRope = 64;
 constexpr int kMlaTileKeys = 16;
 constexpr int kMlaWaves = 4;
+constexpr int kMlaStages = 4;  // tiles in the ring: three in flight while one is used
 
 struct MlaSmem {
   static constexpr int kLatTile = kMlaTileKeys * kMlaRank * 2;   // 16 KB
   static constexpr int kPosTile = kMlaTileKeys * kMlaRope * 2;   // 2 KB
   static constexpr int kStage = kLatTile + kPosTile;
-  static constexpr int kWaveRing = 2 * kStage;
-  static constexpr int kRing = kMlaWaves * kWaveRing;           // 144 KB
-  // end-of-item combine: O [wave][head][R] f32 + (m, l, lx) [wave][head]
-  static constexpr int kCombine = kMlaWaves * kMlaHeads * (kMlaRank + 3) * 4;
-  static constexpr int kBytes = kRing > kCombine ? kRing : kCombine;
+  static constexpr int kBytes = kMlaStages * kStage;             // 72 KB
 };
 
 __device__ __forceinline__ floatx4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b, const floatx4_t& c) {
@@ -54,7 +54,15 @@ __device__ __forceinline__ floatx4_t mfma_16x16x16(const short4_t& a, const shor
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Byte offset of 16-byte piece `piece` of key row `key` in a tile of `width`
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Byte offset of 16-byte piece `piece` of key row `key` in a tile of WIDTH
 // bf16 per row.
 template <int WIDTH>
 __device__ __forceinline__ int mla_off(int key, int piece) {
@@ -65,8 +73,15 @@ template <typename T>
 __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it, char* smem) {
   constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = kMlaTileKeys;
   constexpr int KS_LAT = R / 32, KS_POS = P / 32;  // 16x16x32 k-steps
-  constexpr int DB = R / 16;                        // 16-dim blocks of O^T
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int DW = R / kMlaWaves;                 // output dims per wave
+  constexpr int DB = DW / 16;                       // 16-dim blocks of O^T per wave
+  constexpr int ROWS_PER_WAVE = NT / kMlaWaves;     // latent rows each wave loads per tile
+  constexpr int LOADS_PER_TILE = ROWS_PER_WAVE + 1; // + a quarter of the rotary tile
+  static_assert(NT % kMlaWaves == 0 && DW % 16 == 0, "tile must split over the waves");
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (readfirstlane): keeps the tile schedule and its block-table
+  // lookups in scalar registers and scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, c = lane >> 4;           // MFMA column (head / key row) and k-group
   const int qi = it.q_begin;
   const int tb = it.tok_begin, te = it.tok_end;
@@ -91,49 +106,68 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   for (int b = 0; b < DB; ++b) o[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f, lx = 0.f;
 
-  char* ring = smem + wave * MlaSmem::kWaveRing;
   auto clamp_key = [&](int t) { return min(max(t, tb), te - 1); };
-  // One tile: 16 latent rows (one 1 KB load each; the row's page number is
-  // wave-uniform) and 16 rotary rows (two loads of 8 rows x 128 bytes).
+  // This wave's share of a tile: latent rows ROWS_PER_WAVE * wave + r (one
+  // 1 KB load each) and rotary rows 4 wave .. 4 wave + 3 (half a load: lanes
+  // 0..31, 8 lanes of 16 bytes per 128-byte row).
   auto issue_tile = [&](int t0, char* stage) {
+    int pg[ROWS_PER_WAVE];  // wave-uniform: scalar loads
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {  // latent row r: lane loads piece lane ^ (r & 7)
-      const int t = clamp_key(t0 + r);
-      const int page = bt[t >> a.page_shift];
-      const uint16_t* src = lat + ((uint64_t)page * ps + (t & (ps - 1))) * R + ((lane ^ (r & 7)) * 8);
-      load_to_lds(src, stage + r * (R * 2));
+    for (int r = 0; r < ROWS_PER_WAVE; ++r)
+      pg[r] = load_uniform(bt, clamp_key(t0 + ROWS_PER_WAVE * wave + r) >> a.page_shift);
+#pragma unroll
+    for (int r = 0; r < ROWS_PER_WAVE; ++r) {
+      const int row = ROWS_PER_WAVE * wave + r;
+      const int t = clamp_key(t0 + row);
+      const uint16_t* src = lat + ((uint64_t)pg[r] * ps + (t & (ps - 1))) * R + ((lane ^ (row & 7)) * 8);
+      load_to_lds(src, stage + row * (R * 2));
     }
+    if (lane < 32) {
+      const int rl = lane >> 3;  // 0..3
+      int page = pg[0];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // rotary rows 8 i .. 8 i + 7: lane covers row 8 i + lane / 8
-      const int r = 8 * i + (lane >> 3);
-      const int t = clamp_key(t0 + r);
-      const int page = bt[t >> a.page_shift];
-      const uint16_t* src = kpos + ((uint64_t)page * ps + (t & (ps - 1))) * P + (((lane & 7) ^ (r & 7)) * 8);
-      load_to_lds(src, stage + MlaSmem::kLatTile + i * 1024);
+      for (int q = 1; q < ROWS_PER_WAVE; ++q) page = rl == q ? pg[q] : page;
+      const int row = ROWS_PER_WAVE * wave + rl;
+      const int t = clamp_key(t0 + row);
+      const uint16_t* src = kpos + ((uint64_t)page * ps + (t & (ps - 1))) * P + (((lane & 7) ^ (row & 7)) * 8);
+      load_to_lds(src, stage + MlaSmem::kLatTile + wave * 512);
     }
   };
 
-  const int first = tb + wave * NT;
-  int stage = 0;
-  if (first < te) issue_tile(first, ring);
-  for (int t0 = first; t0 < te; t0 += kMlaWaves * NT, stage ^= 1) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's tile has landed (the ring is private to the wave)
-    if (t0 + kMlaWaves * NT < te) issue_tile(t0 + kMlaWaves * NT, ring + (stage ^ 1) * MlaSmem::kStage);
-    const char* ls = ring + stage * MlaSmem::kStage;
+  // tiles start on multiples of 16 keys; keys outside [tb, te) are masked
+  const int first = tb & ~(NT - 1);
+  const int ntiles = (te - first + NT - 1) / NT;
+#pragma unroll
+  for (int j = 0; j < kMlaStages - 1; ++j)
+    if (j < ntiles) issue_tile(first + j * NT, smem + j * MlaSmem::kStage);
+  for (int j = 0; j < ntiles; ++j) {
+    // tiles j+1 .. j+2 may stay in flight; this wave's share of tile j has landed
+    const int ahead = min(ntiles - 1 - j, kMlaStages - 2);
+    if (ahead >= 2)
+      wait_vmcnt<2 * LOADS_PER_TILE>();
+    else if (ahead == 1)
+      wait_vmcnt<LOADS_PER_TILE>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // ... every wave's share has; tile j-1's stage is free for reuse
+    if (j + kMlaStages - 1 < ntiles)
+      issue_tile(first + (j + kMlaStages - 1) * NT, smem + ((j + kMlaStages - 1) % kMlaStages) * MlaSmem::kStage);
+    const int t0 = first + j * NT;
+    const char* ls = smem + (j % kMlaStages) * MlaSmem::kStage;
     const char* kps = ls + MlaSmem::kLatTile;
 
     // S^T: lane (n, c) holds keys 4 c + r (r = 0..3) of head n
+    bf16x8_t kf[KS_LAT + KS_POS];
+#pragma unroll
+    for (int k = 0; k < KS_LAT; ++k) kf[k] = *reinterpret_cast<const bf16x8_t*>(ls + mla_off<R>(n, 4 * k + c));
+#pragma unroll
+    for (int k = 0; k < KS_POS; ++k)
+      kf[KS_LAT + k] = *reinterpret_cast<const bf16x8_t*>(kps + mla_off<P>(n, 4 * k + c));
     floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < KS_LAT; ++k) {
-      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ls + mla_off<R>(n, 4 * k + c));
-      s = mfma_16x16x32(kf, qa[k], s);
-    }
+    for (int k = 0; k < KS_LAT; ++k) s = mfma_16x16x32(kf[k], qa[k], s);
 #pragma unroll
-    for (int k = 0; k < KS_POS; ++k) {
-      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kps + mla_off<P>(n, 4 * k + c));
-      s = mfma_16x16x32(kf, qp[k], s);
-    }
+    for (int k = 0; k < KS_POS; ++k) s = mfma_16x16x32(kf[KS_LAT + k], qp[k], s);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 4 * c + r;
@@ -161,62 +195,46 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
     lx += (p[0] + p[1]) + (p[2] + p[3]);
     const short4_t pf = __builtin_bit_cast(short4_t, make_uint2(w0, w1));
 
-    // O^T block b: lane (i = lane % 16, c) needs latent[4 c + r][16 b + i]:
-    // one transposed read, lane 4 r + j giving the address of dims 16 b + 4 j
-    // of key row 4 c + r.
-    const int rr = n >> 2, jj = n & 3;
-    const int key = 4 * c + rr;
+    // O^T block b (dims DW wave + 16 b ..): lane (i = lane % 16, c) needs
+    // latent[4 c + r][DW wave + 16 b + i]: one transposed read, lane 4 r + j
+    // giving the address of dims DW wave + 16 b + 4 j of key row 4 c + r.
+    const int key = 4 * c + (n >> 2);
+    short4_t vf[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      const int dim = 16 * b + 4 * jj;
-      const short4_t vf = lds_read_tr16(ls + mla_off<R>(key, dim >> 3) + (dim & 7) * 2);
-      o[b] = mfma_16x16x16(vf, pf, o[b]);
+      const int dim = DW * wave + 16 * b + 4 * (n & 3);
+      vf[b] = lds_read_tr16(ls + mla_off<R>(key, dim >> 3) + (dim & 7) * 2);
     }
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[b] = mfma_16x16x16(vf[b], pf, o[b]);
   }
 
-  // full row sums of this wave: the four k-groups hold different keys
+  // full row sums: the four k-groups of lanes hold different keys
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   lx += __shfl_xor(lx, 16);
   lx += __shfl_xor(lx, 32);
 
-  // combine the waves: O^T lane (n, c) element r is dim 16 b + 4 c + r of head n
-  __syncthreads();  // every wave is done with its ring; reuse it for the combine
-  float* so = reinterpret_cast<float*>(smem);                   // [wave][head][R]
-  float* sml = so + kMlaWaves * H * R;                          // [wave][head][3]
+  // O^T lane (n, c) element r is dim DW wave + 16 b + 4 c + r of head n
+  if (it.slot < 0) {
+    const float inv = 1.f / l;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * H + n) * R + DW * wave;
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
-    *reinterpret_cast<floatx4_t*>(so + ((size_t)wave * H + n) * R + 16 * b + 4 * c) = o[b];
-  if (c == 0) {
-    sml[(wave * H + n) * 3 + 0] = m;
-    sml[(wave * H + n) * 3 + 1] = l;
-    sml[(wave * H + n) * 3 + 2] = lx;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < H * R; idx += kMlaWaves * kWave) {
-    const int hd = idx / R, d = idx % R;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMlaWaves; ++w) M = fmaxf(M, sml[(w * H + hd) * 3]);
-    const float mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, LX = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kMlaWaves; ++w) {
-      const float f = fast_exp2((sml[(w * H + hd) * 3] - mu) * a.scale_log2);
-      L += sml[(w * H + hd) * 3 + 1] * f;
-      LX += sml[(w * H + hd) * 3 + 2] * f;
-      O += so[((size_t)w * H + hd) * R + d] * f;
+    for (int b = 0; b < DB; ++b) {
+      uint2 w;
+      w.x = pack_bf16(o[b][0] * inv, o[b][1] * inv);
+      w.y = pack_bf16(o[b][2] * inv, o[b][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * b + 4 * c) = w;
     }
-    if (it.slot < 0) {
-      store_out<T>(a.out, ((uint64_t)qi * H + hd) * R + d, O / L);
-      if (a.lse && d == 0) a.lse[(uint64_t)qi * H + hd] = M * a.scale + logf(LX);
-    } else {
-      a.ws_o[((uint64_t)it.slot * H + hd) * R + d] = O;
-      if (d == 0) {
-        a.ws_ml[((uint64_t)it.slot * H + hd) * 3 + 0] = M * a.scale_log2;
-        a.ws_ml[((uint64_t)it.slot * H + hd) * 3 + 1] = L;
-        a.ws_ml[((uint64_t)it.slot * H + hd) * 3 + 2] = LX;
-      }
+    if (a.lse && wave == 0 && c == 0) a.lse[(uint64_t)qi * H + n] = m * a.scale + logf(lx);
+  } else {
+    float* dst = a.ws_o + ((uint64_t)it.slot * H + n) * R + DW * wave;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) *reinterpret_cast<floatx4_t*>(dst + 16 * b + 4 * c) = o[b];
+    if (wave == 0 && c == 0) {
+      a.ws_ml[((uint64_t)it.slot * H + n) * 3 + 0] = m * a.scale_log2;
+      a.ws_ml[((uint64_t)it.slot * H + n) * 3 + 1] = l;
+      a.ws_ml[((uint64_t)it.slot * H + n) * 3 + 2] = lx;
     }
   }
 }
