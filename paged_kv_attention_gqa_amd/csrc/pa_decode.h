@@ -84,7 +84,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   static_assert(NW > 1, "waves combine through LDS");
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r = lane / LPT;
   const int c = lane % LPT;
   const int qi = it.q_begin;
@@ -113,30 +113,22 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
     for (int e = 0; e < EPV; ++e) o[g][e] = 0.f;
   }
 
-  const int t0 = tb & ~1;  // pairs start on even positions
-  for (int B = t0 + wave * BLK; B < te; B += NW * BLK) {
-    // Keys outside [tb, te) are clamped onto an in-range key: every load stays
-    // inside the sequence's referenced pages and the loads need no branches;
-    // the scores of those slots are masked to -inf below.
-    int pg[U];
+  // Key slot u of a block starting at B: rows take consecutive key pairs.
+  auto key_of = [&](int B, int u) { return B + 2 * ((u >> 1) * TPW + r) + (u & 1); };
+  auto slot_offset = [&](int page, int tc) -> uint64_t {
+    return ((uint64_t)page * ps + (tc & (ps - 1))) * row_stride + (uint64_t)kvh * D + c * EPV;
+  };
+
+  // Scores, online softmax and P.V of one block held in kr / vr.  Keys
+  // outside [tb, te) were loaded from a clamped in-range key (every load stays
+  // inside the sequence's referenced pages, no branches) and are masked here.
+  auto compute_block = [&](int B, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
     bool valid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = B + 2 * ((u >> 1) * TPW + r) + (u & 1);
+      const int t = key_of(B, u);
       valid[u] = (t >= tb) && (t < te);
-      const int tc = min(max(t, tb), te - 1);
-      pg[u] = bt[tc >> a.page_shift];
     }
-    uint4 kr[U], vr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = B + 2 * ((u >> 1) * TPW + r) + (u & 1);
-      const int tc = min(max(t, tb), te - 1);
-      const uint64_t off = ((uint64_t)pg[u] * ps + (tc & (ps - 1))) * row_stride + (uint64_t)kvh * D + c * EPV;
-      kr[u] = load16(a.k, off, sizeof(T));
-      vr[u] = load16(a.v, off, sizeof(T));
-    }
-
     // scores, reduced over the LPT lanes of each row (step-major so that
     // independent DPP operations fill each other's hazard slots)
     float s[U][G];
@@ -199,6 +191,59 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
           for (int e = 0; e < EPV; ++e) o[g][e] = fmaf(s[u][g], vf[e], o[g][e]);
         }
       }
+    }
+  };
+
+  // Blocks start on multiples of BLK.  When a page holds whole blocks, a
+  // block's page number is one wave-uniform scalar load and the next block's
+  // keys stream in while this one is computed; smaller pages look pages up
+  // per lane.
+  const int tstart = tb & ~(BLK - 1);
+  const int step = NW * BLK;
+  if (ps >= BLK) {
+    int B = tstart + wave * BLK;
+    if (B < te) {
+      auto load_block = [&](int blk, int page, uint4 (&kr)[U], uint4 (&vr)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint64_t off = slot_offset(page, min(max(key_of(blk, u), tb), te - 1));
+          kr[u] = load16(a.k, off, sizeof(T));
+          vr[u] = load16(a.v, off, sizeof(T));
+        }
+      };
+      uint4 ka[U], va[U], kb[U], vb[U];
+      load_block(B, load_uniform(bt, B >> a.page_shift), ka, va);
+      int pg_next = B + step < te ? load_uniform(bt, (B + step) >> a.page_shift) : 0;
+      while (true) {
+        if (B + step < te) {
+          load_block(B + step, pg_next, kb, vb);
+          pg_next = B + 2 * step < te ? load_uniform(bt, (B + 2 * step) >> a.page_shift) : 0;
+        }
+        compute_block(B, ka, va);
+        B += step;
+        if (B >= te) break;
+        if (B + step < te) {
+          load_block(B + step, pg_next, ka, va);
+          pg_next = B + 2 * step < te ? load_uniform(bt, (B + 2 * step) >> a.page_shift) : 0;
+        }
+        compute_block(B, kb, vb);
+        B += step;
+        if (B >= te) break;
+      }
+    }
+  } else {
+    for (int B = tstart + wave * BLK; B < te; B += step) {
+      int pg[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) pg[u] = bt[min(max(key_of(B, u), tb), te - 1) >> a.page_shift];
+      uint4 kr[U], vr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t off = slot_offset(pg[u], min(max(key_of(B, u), tb), te - 1));
+        kr[u] = load16(a.k, off, sizeof(T));
+        vr[u] = load16(a.v, off, sizeof(T));
+      }
+      compute_block(B, kr, vr);
     }
   }
 

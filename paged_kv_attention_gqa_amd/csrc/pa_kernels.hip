@@ -22,7 +22,7 @@ struct DecodeUnroll {
 // 64 KB of LDS, so two fit a CU.
 template <int G>
 struct Occupancy {
-  static constexpr int kDecode = G <= 4 ? 4 : (G <= 8 ? 2 : 1);
+  static constexpr int kDecode = G <= 4 ? 3 : (G <= 8 ? 2 : 1);
   static constexpr int kMixed = G <= 8 ? 2 : 1;
 };
 
