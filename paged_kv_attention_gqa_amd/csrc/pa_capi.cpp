@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <map>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -15,6 +16,7 @@
 
 #include "paged_attn.h"
 #include "pa_launch.h"
+#include "pa_prefill.h"
 
 using pa::MergeItem;
 using pa::WorkItem;
@@ -41,8 +43,11 @@ int ok() {
 // Sequences with at most this many queries run as per-query decode items;
 // longer runs of queries become prefill tiles of kPrefillRows query rows.
 constexpr int kDecodeMaxQueries = 4;
-constexpr int kPrefillRows = 128;
+constexpr int kPrefillRows = pa::kPrefillRows;
 constexpr int kDefaultSplitTokens = 512;
+// In a launch that also runs prefill tiles, a decode item is worked by the
+// prefill workgroup's eight waves: give it proportionally more keys.
+constexpr int kMixedSplitTokens = 2048;
 constexpr int kDefaultMlaSplitTokens = 1024;
 constexpr int kSplitAlign = 64;
 constexpr int kMaxSplitsLimit = 64;
@@ -165,9 +170,11 @@ void plan_decode_row(pa_plan* p, int s, int i, int kvh, int split_tokens, std::v
 void build_work(pa_plan* p) {
   std::vector<WorkItem> dec, pre;
   const int G = p->group();
-  const int split_tokens = p->split_tokens > 0
-                               ? std::max(kSplitAlign, (p->split_tokens + kSplitAlign - 1) / kSplitAlign * kSplitAlign)
-                               : (p->mla ? kDefaultMlaSplitTokens : kDefaultSplitTokens);
+  bool has_prefill = false;
+  for (int s = 0; s < p->S && !p->mla; ++s) has_prefill |= (p->cu_q[s + 1] - p->cu_q[s]) > kDecodeMaxQueries;
+  const int split_tokens =
+      p->split_tokens > 0 ? std::max(kSplitAlign, (p->split_tokens + kSplitAlign - 1) / kSplitAlign * kSplitAlign)
+                          : (p->mla ? kDefaultMlaSplitTokens : (has_prefill ? kMixedSplitTokens : kDefaultSplitTokens));
   for (int s = 0; s < p->S; ++s) {
     const int q0 = p->cu_q[s], q1 = p->cu_q[s + 1];
     const int nq = q1 - q0;
@@ -184,26 +191,35 @@ void build_work(pa_plan* p) {
       }
     } else {
       const int tile_q = std::max(1, kPrefillRows / G);
-      for (int t0 = q0; t0 < q1; t0 += tile_q) {
-        const int t1 = std::min(q1, t0 + tile_q);
-        int lo = INT32_MAX, hi = -1;
-        for (int i = t0; i < t1; ++i) {
-          int a, b;
-          visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &a, &b);
-          lo = std::min(lo, a);
-          hi = std::max(hi, b);
+      for (int kvh = 0; kvh < p->hkv; ++kvh)
+        for (int t0 = q0; t0 < q1; t0 += tile_q) {
+          const int t1 = std::min(q1, t0 + tile_q);
+          int lo = INT32_MAX, hi = -1;
+          for (int i = t0; i < t1; ++i) {
+            int a, b;
+            visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &a, &b);
+            lo = std::min(lo, a);
+            hi = std::max(hi, b);
+          }
+          pre.push_back(WorkItem{pa::kPrefill, kvh, s, t0, t1 - t0, lo, hi + 1, -1});
         }
-        for (int kvh = 0; kvh < p->hkv; ++kvh) pre.push_back(WorkItem{pa::kPrefill, kvh, s, t0, t1 - t0, lo, hi + 1, -1});
-      }
     }
   }
-  // longest first, so the tail of the launch is made of short items
-  auto longer = [](const WorkItem& a, const WorkItem& b) {
-    const int64_t wa = (int64_t)(a.tok_end - a.tok_begin) * a.q_count, wb = (int64_t)(b.tok_end - b.tok_begin) * b.q_count;
-    return wa > wb;
-  };
-  std::stable_sort(pre.begin(), pre.end(), longer);
-  std::stable_sort(dec.begin(), dec.end(), longer);
+  auto work = [](const WorkItem& w) { return (int64_t)(w.tok_end - w.tok_begin) * w.q_count; };
+  // Prefill tiles of one (sequence, KV head) read the same keys: keep them
+  // adjacent (consecutive items share an XCD and its L2), groups and tiles
+  // within a group longest first.
+  std::map<std::pair<int, int>, int64_t> group_work;
+  for (const WorkItem& w : pre) group_work[{w.seq, w.kvh}] += work(w);
+  std::stable_sort(pre.begin(), pre.end(), [&](const WorkItem& a, const WorkItem& b) {
+    const int64_t ga = group_work[{a.seq, a.kvh}], gb = group_work[{b.seq, b.kvh}];
+    if (ga != gb) return ga > gb;
+    if (a.seq != b.seq) return a.seq < b.seq;
+    if (a.kvh != b.kvh) return a.kvh < b.kvh;
+    return work(a) > work(b);
+  });
+  // decode items longest first, so the tail of the launch is made of short items
+  std::stable_sort(dec.begin(), dec.end(), [&](const WorkItem& a, const WorkItem& b) { return work(a) > work(b); });
   p->n_prefill = (int32_t)pre.size();
   p->n_decode = (int32_t)dec.size();
   p->items = std::move(pre);

@@ -168,6 +168,14 @@ __device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
 typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 __device__ __forceinline__ int load_uniform(const int32_t* p, int idx) { return ((const_i32_t*)p)[idx]; }
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Map a dispatch index to an item index so that consecutive items land on the
 // same XCD: the hardware deals workgroups round-robin over the 8 XCDs.
 __device__ __forceinline__ int xcd_item(int b, int n) {

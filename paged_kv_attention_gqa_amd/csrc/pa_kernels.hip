@@ -19,7 +19,7 @@ struct DecodeUnroll {
 // Decode streams HBM and wants several workgroups per CU in flight; its
 // registers grow with the group size G (G query rows per lane), so the target
 // drops for large groups rather than spill.  A mixed / prefill workgroup holds
-// 64 KB of LDS, so two fit a CU.
+// 96 KB of LDS and 8 waves, so one fits a CU at 2 waves per SIMD.
 template <int G>
 struct Occupancy {
   static constexpr int kDecode = G <= 4 ? 3 : (G <= 8 ? 2 : 1);
@@ -39,25 +39,24 @@ void decode_kernel(KernelArgs a) {
 // share the grid (packed decode + chunked prefill in one dispatch).
 template <typename T, int D, int G>
 struct MixedShape {
-  static constexpr bool kMfma = sizeof(T) == 2 && (D == 64 || D == 128) && G <= 128;
-  static constexpr int kDecodeBytes = kDecodeWaves * G * (D + 3) * 4;
+  static constexpr bool kMfma = sizeof(T) == 2 && (D == 64 || D == 128) && G <= kPrefillRows;
+  static constexpr int kDecodeBytes = kPrefillWaves * G * (D + 3) * 4;
   static constexpr int kPrefillBytes = kMfma ? PrefillSmem<(D <= 128 ? D : 128)>::kBytes : 0;
   static constexpr int kBytes = kDecodeBytes > kPrefillBytes ? kDecodeBytes : kPrefillBytes;
 };
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kMixed)))
+__global__ __launch_bounds__(kPrefillWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kMixed)))
 void mixed_kernel(KernelArgs a) {
-  static_assert(kDecodeWaves == kPrefillWaves, "decode and prefill share the workgroup shape");
   __shared__ __attribute__((aligned(16))) char smem[MixedShape<T, D, G>::kBytes];
   const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
   if (it.kind == kPrefill) {
     if constexpr (MixedShape<T, D, G>::kMfma)
       prefill_item<D, G>(a, it, smem);
     else
-      prefill_item_by_queries<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
+      prefill_item_by_queries<T, D, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
   } else {
-    decode_item<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
+    decode_item<T, D, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
   }
 }
 
@@ -97,7 +96,7 @@ hipError_t launch_decode_t(const KernelArgs& a, int n_items, const MergeItem* me
 template <typename T, int D, int G>
 hipError_t launch_mixed_t(const KernelArgs& a, int n_items, const MergeItem*, int, hipStream_t stream) {
   if (n_items > 0) {
-    hipLaunchKernelGGL((mixed_kernel<T, D, G>), dim3(n_items), dim3(kDecodeWaves * kWave), 0, stream, a);
+    hipLaunchKernelGGL((mixed_kernel<T, D, G>), dim3(n_items), dim3(kPrefillWaves * kWave), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;

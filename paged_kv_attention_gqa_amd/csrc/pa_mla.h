@@ -16,8 +16,8 @@
 //   O^T[R x 16 heads]      += latent^T . P^T                      (16x16x16)
 // The four waves of a workgroup share a four-stage LDS ring of 16-key tiles
 // (three in flight while one is used, one barrier per tile), loaded with
-// global_load_lds_dwordx4 (16-byte pieces of key row t stored at piece ^ (t &
-// 7)); block-table entries are wave-uniform scalar loads, so the
+// global_load_lds_dwordx4 (16-byte pieces of key row t stored at piece ^
+// swz(t)); block-table entries are wave-uniform scalar loads, so the
 // vector-memory counter counts tile loads only.  Every wave computes the
 // small score tile (so softmax statistics agree across waves without any
 // exchange) and owns R / 4 = 128 output dims; latent^T fragments come from
@@ -54,19 +54,11 @@ __device__ __forceinline__ floatx4_t mfma_16x16x16(const short4_t& a, const shor
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 // Byte offset of 16-byte piece `piece` of key row `key` in a tile of WIDTH
 // bf16 per row.
 template <int WIDTH>
 __device__ __forceinline__ int mla_off(int key, int piece) {
-  return key * (WIDTH * 2) + ((piece ^ (key & 7)) << 4);
+  return key * (WIDTH * 2) + ((piece ^ swz<WIDTH / 8>(key)) << 4);
 }
 
 template <typename T>
@@ -119,7 +111,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
     for (int r = 0; r < ROWS_PER_WAVE; ++r) {
       const int row = ROWS_PER_WAVE * wave + r;
       const int t = clamp_key(t0 + row);
-      const uint16_t* src = lat + ((uint64_t)pg[r] * ps + (t & (ps - 1))) * R + ((lane ^ (row & 7)) * 8);
+      const uint16_t* src = lat + ((uint64_t)pg[r] * ps + (t & (ps - 1))) * R + ((lane ^ swz<R / 8>(row)) * 8);
       load_to_lds(src, stage + row * (R * 2));
     }
     if (lane < 32) {
@@ -129,7 +121,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       for (int q = 1; q < ROWS_PER_WAVE; ++q) page = rl == q ? pg[q] : page;
       const int row = ROWS_PER_WAVE * wave + rl;
       const int t = clamp_key(t0 + row);
-      const uint16_t* src = kpos + ((uint64_t)page * ps + (t & (ps - 1))) * P + (((lane & 7) ^ (row & 7)) * 8);
+      const uint16_t* src = kpos + ((uint64_t)page * ps + (t & (ps - 1))) * P + (((lane & 7) ^ swz<P / 8>(row)) * 8);
       load_to_lds(src, stage + MlaSmem::kLatTile + wave * 512);
     }
   };

@@ -1,4 +1,4 @@
-// Chunked-prefill body (bf16 MFMA): up to 128 query rows -- 128/G consecutive
+// Chunked-prefill body (bf16 MFMA): up to 256 query rows -- 256/G consecutive
 // queries of one sequence times the G query heads of one KV head -- against
 // the keys the plan assigns to the tile, gathered page by page through the
 // block table.
@@ -11,10 +11,11 @@
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation; softmax statistics are
 // fp32 and kept per query row in registers (online softmax across key tiles).
 //
-// Data flow per 64-key tile (two LDS stages, one barrier per tile):
+// Data flow per 64-key tile (three LDS stages, two tiles in flight, one
+// barrier per tile):
 //   HBM --global_load_lds_dwordx4 (page-gathered, no registers)--> LDS
 //     K, V row-major [64 keys][D], the 16-byte pieces of key row t stored at
-//     piece ^ (t & 7) so that column reads of 8 rows hit 8 bank groups
+//     piece ^ swz(t) so that column reads hit distinct bank groups
 //   each wave (32 rows):  S^T[64 x 32] = K . Q^T      (Q^T held in registers)
 //                         O^T[D x 32] += V^T . P^T    (V^T read with
 //                         ds_read_b64_tr_b16, P^T straight from S^T)
@@ -32,14 +33,16 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kPrefillTileKeys = 64;
-constexpr int kPrefillWaves = 4;
+constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRowsPerWave = 32;
+constexpr int kPrefillRows = kPrefillWaves * kPrefillRowsPerWave;
+constexpr int kPrefillStages = 3;
 
 template <int D>
 struct PrefillSmem {
   static constexpr int kTile = kPrefillTileKeys * D * 2;  // bytes of one K or V tile
   static constexpr int kStage = 2 * kTile;
-  static constexpr int kBytes = 2 * kStage;               // two stages
+  static constexpr int kBytes = kPrefillStages * kStage;
 };
 
 __device__ __forceinline__ floatx16_t mfma_32x32x16(const bf16x8_t& a, const bf16x8_t& b, const floatx16_t& c) {
@@ -61,14 +64,30 @@ __device__ __forceinline__ short4_t lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p));
 }
 
+// Where piece `piece` of key row `key` is stored: piece ^ swz(key), a
+// bit-rotated copy of the low key bits.  Sixteen consecutive keys reading the
+// same piece (16-byte operand reads) and four consecutive keys reading four
+// neighbouring pieces (transpose reads) then hit distinct 16-byte bank groups.
+template <int PIECES>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (PIECES >= 16)
+    return ((key & 3) << 2) | ((key >> 2) & 3);
+  else
+    return ((key & 3) << 1) | ((key >> 2) & 1);
+}
+
 // Byte offset of 16-byte piece `piece` of key row `key` inside a tile.
 template <int D>
 __device__ __forceinline__ int tile_off(int key, int piece) {
-  return key * (D * 2) + ((piece ^ (key & 7)) << 4);
+  return key * (D * 2) + ((piece ^ swz<D / 8>(key)) << 4);
 }
 
-template <int D, int G>
-__device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem& it, char* smem) {
+// UNIFORM: pages hold >= 16 keys, so a tile's page numbers are scalar loads
+// and the loop body issues no other vector-memory loads (a single per-lane
+// lookup would make the compiler drain the vector-memory counter before
+// every tile issue).
+template <int D, int G, bool UNIFORM>
+__device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const WorkItem& it, char* smem) {
   constexpr int NT = kPrefillTileKeys;
   constexpr int KS = D / 16;                         // MFMA k-steps of S^T (over head dims)
   constexpr int DB = D / 32;                         // 32-dim blocks of O^T
@@ -82,7 +101,8 @@ __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem
   static_assert((2 * LOADS_PER_TILE) % kPrefillWaves == 0, "tile loads must split over the waves");
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
   const int row = wave * kPrefillRowsPerWave + n;
   const int qloc = row / G, g = row % G;
@@ -121,46 +141,74 @@ __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem
 
   // This wave issues loads wave * LOADS_PER_WAVE .. +LOADS_PER_WAVE of each
   // tile; load i covers K (i < LOADS_PER_TILE) or V rows KEYS_PER_LOAD *
-  // (i % LOADS_PER_TILE) + lane / PIECES at stored piece lane % PIECES.  Page
-  // numbers run one tile ahead of the data.
+  // (i % LOADS_PER_TILE) + lane / PIECES at stored piece lane % PIECES.
+  // Keys outside [tb, te) read a clamped in-range key of the same tile.
+  // With pages of >= 16 keys a tile spans at most NT / 16 pages, whose numbers
+  // are wave-uniform scalar loads: the vector-memory counter then counts tile
+  // loads only and the wait below keeps the next tile in flight.  Smaller
+  // pages are looked up per lane and the wait drains everything.
   const int my_key_in_load = lane / PIECES;
   const int my_stored_piece = lane % PIECES;
-  int pg[LOADS_PER_WAVE];
-  auto clamp_key = [&](int t) { return min(max(t, tb), te - 1); };  // out-of-range keys read an in-range key
+  constexpr int MAXP = NT / 16;
+  const int last_page = (te - 1) >> a.page_shift;
+  auto clamp_key = [&](int t) { return min(max(t, tb), te - 1); };
   auto load_key = [&](int i) { return KEYS_PER_LOAD * (i % LOADS_PER_TILE) + my_key_in_load; };
-  auto fetch_pages = [&](int t0) {
+  // wave-uniform page numbers of the (at most MAXP) pages tile t0 spans
+  auto fetch_pages = [&](int t0, int (&tp)[MAXP]) {
+    if constexpr (UNIFORM) {
+      const int p0 = t0 >> a.page_shift;
 #pragma unroll
-    for (int j = 0; j < LOADS_PER_WAVE; ++j)
-      pg[j] = bt[clamp_key(t0 + load_key(wave * LOADS_PER_WAVE + j)) >> a.page_shift];
+      for (int q = 0; q < MAXP; ++q) tp[q] = load_uniform(bt, min(p0 + q, last_page));
+    }
   };
-  auto issue_tile = [&](int t0, char* stage) {
+  auto issue_tile = [&](int t0, char* stage, const int (&tp)[MAXP]) {
+    const int p0 = t0 >> a.page_shift;
 #pragma unroll
     for (int j = 0; j < LOADS_PER_WAVE; ++j) {
       const int i = wave * LOADS_PER_WAVE + j;
       const int key = load_key(i);
       const int t = clamp_key(t0 + key);
-      const int piece = my_stored_piece ^ (key & 7);
+      int page;
+      if constexpr (UNIFORM) {
+        const int q = (t >> a.page_shift) - p0;  // 0 .. MAXP-1: t lies in this tile
+        page = tp[0];
+#pragma unroll
+        for (int k = 1; k < MAXP; ++k) page = q == k ? tp[k] : page;
+      } else {
+        page = bt[t >> a.page_shift];
+      }
+      const int piece = my_stored_piece ^ swz<PIECES>(key);
       const uint16_t* pool = reinterpret_cast<const uint16_t*>(i < LOADS_PER_TILE ? a.k : a.v);
-      const uint16_t* src = pool + ((uint64_t)pg[j] * ps + (t & (ps - 1))) * row_stride + head_off + piece * 8;
+      const uint16_t* src = pool + ((uint64_t)page * ps + (t & (ps - 1))) * row_stride + head_off + piece * 8;
       load_to_lds(src, stage + (i < LOADS_PER_TILE ? 0 : TILE) + (i % LOADS_PER_TILE) * 1024);
     }
   };
 
+  // Page numbers run one tile ahead of the loads that use them.
   const int t_first = tb & ~(NT - 1);
-  int stage = 0;
-  if (t_first < te) {
-    fetch_pages(t_first);
-    issue_tile(t_first, smem);
-    fetch_pages(t_first + NT);
-  }
-  for (int t0 = t_first; t0 < te; t0 += NT, stage ^= 1) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed in LDS
-    __syncthreads();                // ... and every other wave's; the other stage is free
-    if (t0 + NT < te) {             // next tile streams in while this one is computed
-      issue_tile(t0 + NT, smem + (stage ^ 1) * STAGE);
-      fetch_pages(t0 + 2 * NT);
+  const int ntiles = (te - t_first + NT - 1) / NT;
+  int tp_next[MAXP];
+#pragma unroll
+  for (int j = 0; j < kPrefillStages - 1; ++j) {
+    if (j < ntiles) {
+      fetch_pages(t_first + j * NT, tp_next);
+      issue_tile(t_first + j * NT, smem + j * STAGE, tp_next);
     }
-    const char* ks = smem + stage * STAGE;
+  }
+  fetch_pages(t_first + (kPrefillStages - 1) * NT, tp_next);
+  for (int j = 0; j < ntiles; ++j) {
+    if (UNIFORM && j + 1 < ntiles)
+      wait_vmcnt<LOADS_PER_WAVE>();  // tile j has landed, tile j+1 may still be in flight
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // every wave's share of tile j has landed; tile j-1's stage is free
+    if (j + kPrefillStages - 1 < ntiles) {
+      issue_tile(t_first + (j + kPrefillStages - 1) * NT, smem + ((j + kPrefillStages - 1) % kPrefillStages) * STAGE,
+                 tp_next);
+      fetch_pages(t_first + (j + kPrefillStages) * NT, tp_next);
+    }
+    const int t0 = t_first + j * NT;
+    const char* ks = smem + (j % kPrefillStages) * STAGE;
     const char* vs = ks + TILE;
 
     // tile entirely hidden from every row of this wave?
@@ -268,6 +316,14 @@ __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem
       *reinterpret_cast<uint2*>(orow + 32 * b + 8 * k + 4 * h) = w;
     }
   if (a.lse && h == 0) a.lse[(uint64_t)qi * a.hq + head] = m * a.scale + logf(lx);
+}
+
+template <int D, int G>
+__device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem& it, char* smem) {
+  if (a.page_shift >= 4)
+    prefill_item_impl<D, G, true>(a, it, smem);
+  else
+    prefill_item_impl<D, G, false>(a, it, smem);
 }
 
 // A prefill tile handled one query at a time by the decode body (f32 data and
