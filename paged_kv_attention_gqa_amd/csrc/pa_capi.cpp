@@ -167,6 +167,70 @@ void plan_decode_row(pa_plan* p, int s, int i, int kvh, int split_tokens, std::v
   p->n_slots += nsplit;
 }
 
+// Estimated run time of an item, in units of one decode key: a decode item
+// streams its keys once; a prefill tile of kPrefillTileKeys keys times up to
+// kPrefillRows query rows costs about kPrefillKeyCost decode keys per key;
+// every item pays a fixed start-up cost.
+constexpr int64_t kPrefillKeyCost = 2;
+constexpr int64_t kItemStartCost = 64;
+int64_t item_cost(const WorkItem& w) {
+  if (w.kind == pa::kPrefill) {
+    constexpr int NT = pa::kPrefillTileKeys;
+    const int64_t tiles = (w.tok_end - (w.tok_begin & ~(NT - 1)) + NT - 1) / NT;
+    return tiles * NT * kPrefillKeyCost + kItemStartCost;
+  }
+  return (int64_t)(w.tok_end - w.tok_begin) + kItemStartCost;
+}
+
+// Dispatch order of the work list.  Workgroup b of a launch goes to XCD b % 8
+// and each XCD starts its workgroups in order as CUs free up, so the list is
+// built per XCD and interleaved.  Units of work are dealt, largest first, to
+// the XCD with the least estimated work so far; a unit is one decode item or
+// all prefill tiles of one (sequence, KV head), which read the same keys and
+// so share one L2.  Each XCD then runs its items longest first; XCDs with
+// fewer items are padded with empty items.
+constexpr int kXcds = 8;
+void order_items(pa_plan* p, const std::vector<WorkItem>& pre, const std::vector<WorkItem>& dec) {
+  std::vector<std::vector<WorkItem>> units;
+  std::vector<int64_t> unit_cost;
+  std::map<std::pair<int, int>, size_t> group_of;
+  for (const WorkItem& w : pre) {
+    auto g = group_of.find({w.seq, w.kvh});
+    if (g == group_of.end()) {
+      g = group_of.emplace(std::make_pair(w.seq, w.kvh), units.size()).first;
+      units.emplace_back();
+      unit_cost.push_back(0);
+    }
+    units[g->second].push_back(w);
+    unit_cost[g->second] += item_cost(w);
+  }
+  for (const WorkItem& w : dec) {
+    units.push_back({w});
+    unit_cost.push_back(item_cost(w));
+  }
+  std::vector<size_t> order(units.size());
+  for (size_t u = 0; u < order.size(); ++u) order[u] = u;
+  std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) { return unit_cost[a] > unit_cost[b]; });
+  std::vector<std::vector<WorkItem>> bins(kXcds);
+  int64_t load[kXcds] = {};
+  for (size_t u : order) {
+    const int x = (int)(std::min_element(load, load + kXcds) - load);
+    bins[x].insert(bins[x].end(), units[u].begin(), units[u].end());
+    load[x] += unit_cost[u];
+  }
+  size_t rows = 0;
+  for (auto& b : bins) {
+    std::stable_sort(b.begin(), b.end(), [](const WorkItem& a, const WorkItem& c) { return item_cost(a) > item_cost(c); });
+    rows = std::max(rows, b.size());
+  }
+  p->items.clear();
+  p->items.reserve(rows * kXcds);
+  for (size_t j = 0; j < rows; ++j)
+    for (int x = 0; x < kXcds; ++x)
+      p->items.push_back(j < bins[x].size() ? bins[x][j] : WorkItem{pa::kEmpty, 0, 0, 0, 0, 0, 0, -1});
+  while (!p->items.empty() && p->items.back().kind == pa::kEmpty) p->items.pop_back();
+}
+
 void build_work(pa_plan* p) {
   std::vector<WorkItem> dec, pre;
   const int G = p->group();
@@ -205,25 +269,9 @@ void build_work(pa_plan* p) {
         }
     }
   }
-  auto work = [](const WorkItem& w) { return (int64_t)(w.tok_end - w.tok_begin) * w.q_count; };
-  // Prefill tiles of one (sequence, KV head) read the same keys: keep them
-  // adjacent (consecutive items share an XCD and its L2), groups and tiles
-  // within a group longest first.
-  std::map<std::pair<int, int>, int64_t> group_work;
-  for (const WorkItem& w : pre) group_work[{w.seq, w.kvh}] += work(w);
-  std::stable_sort(pre.begin(), pre.end(), [&](const WorkItem& a, const WorkItem& b) {
-    const int64_t ga = group_work[{a.seq, a.kvh}], gb = group_work[{b.seq, b.kvh}];
-    if (ga != gb) return ga > gb;
-    if (a.seq != b.seq) return a.seq < b.seq;
-    if (a.kvh != b.kvh) return a.kvh < b.kvh;
-    return work(a) > work(b);
-  });
-  // decode items longest first, so the tail of the launch is made of short items
-  std::stable_sort(dec.begin(), dec.end(), [&](const WorkItem& a, const WorkItem& b) { return work(a) > work(b); });
   p->n_prefill = (int32_t)pre.size();
   p->n_decode = (int32_t)dec.size();
-  p->items = std::move(pre);
-  p->items.insert(p->items.end(), dec.begin(), dec.end());
+  order_items(p, pre, dec);
 }
 
 // Workspace: partial sums [slots, G, Dv] | (max, sum, unrounded sum) [slots, G, 3].
@@ -400,7 +448,7 @@ static int launch_common(FwdCall& c, bool is_mla) {
   if (is_mla) {
     e = pa::launch_mla_main(c.dtype, c.args, c.stream);
   } else {
-    e = pa::launch_gqa_main(c.dtype, c.d, p->group(), p->n_decode, p->n_prefill, c.args, c.stream);
+    e = pa::launch_gqa_main(c.dtype, c.d, p->group(), p->n_prefill > 0, c.args, c.stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (c.event_after_main) {

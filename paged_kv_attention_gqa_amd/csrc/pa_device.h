@@ -17,7 +17,7 @@ constexpr int kWave = 64;
 // contiguous range of that query's visible keys; prefill items cover up to a
 // tile of consecutive queries of one sequence and one KV head.
 struct WorkItem {
-  int32_t kind;       // kDecode / kPrefill
+  int32_t kind;       // kDecode / kPrefill / kEmpty
   int32_t kvh;        // KV head
   int32_t seq;        // sequence index (row of the block table)
   int32_t q_begin;    // first packed query
@@ -28,6 +28,7 @@ struct WorkItem {
 };
 constexpr int32_t kDecode = 0;
 constexpr int32_t kPrefill = 1;
+constexpr int32_t kEmpty = 2;  // padding in the dispatch order: the workgroup exits at once
 
 // One split query row to combine: partials slot .. slot + nsplit - 1 hold the
 // per-split statistics of (query q, KV head kvh).
@@ -114,6 +115,17 @@ __device__ __forceinline__ void group_sum_all(float* x) {
   }
 }
 
+// Max / sum of x over lanes i and i ^ 32 (v_permlane32_swap: a VALU lane
+// exchange, no LDS round trip).  Both lanes of a pair get the same result.
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 2^x on the transcendental unit (v_exp_f32).  Results below the normal range
 // flush to zero, which only affects softmax weights under 2^-126.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -174,17 +186,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Map a dispatch index to an item index so that consecutive items land on the
-// same XCD: the hardware deals workgroups round-robin over the 8 XCDs.
-__device__ __forceinline__ int xcd_item(int b, int n) {
-  constexpr int kXcd = 8;
-  const int per = n / kXcd, rem = n % kXcd;
-  const int x = b % kXcd, j = b / kXcd;
-  // XCD x owns a contiguous run of per (+1 for the first rem XCDs) items
-  const int start = x * per + (x < rem ? x : rem);
-  return start + j;
 }
 
 }  // namespace pa

@@ -30,7 +30,8 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecodeWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kDecode)))
 void decode_kernel(KernelArgs a) {
   __shared__ float smem[kDecodeWaves * G * (D + 3)];
-  const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
+  const WorkItem it = a.items[blockIdx.x];
+  if (it.kind == kEmpty) return;
   decode_item<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, smem);
 }
 
@@ -49,7 +50,8 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(kPrefillWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kMixed)))
 void mixed_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[MixedShape<T, D, G>::kBytes];
-  const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
+  const WorkItem it = a.items[blockIdx.x];
+  if (it.kind == kEmpty) return;
   if (it.kind == kPrefill) {
     if constexpr (MixedShape<T, D, G>::kMfma)
       prefill_item<D, G>(a, it, smem);
@@ -65,7 +67,8 @@ void mixed_kernel(KernelArgs a) {
 template <typename T>
 __global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_eu(2))) void mla_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[MlaSmem::kBytes];
-  const WorkItem it = a.items[xcd_item(blockIdx.x, gridDim.x)];
+  const WorkItem it = a.items[blockIdx.x];
+  if (it.kind == kEmpty) return;
   mla_item<T>(a, it, smem);
 }
 
@@ -161,10 +164,9 @@ bool gqa_supported(int dtype, int d, int g) { return pick<DecodeSel>(dtype, d, g
 
 bool prefill_supported(int dtype, int d, int g) { return pick<MixedSel>(dtype, d, g) != nullptr; }
 
-hipError_t launch_gqa_main(int dtype, int d, int g, int n_decode, int n_prefill, const KernelArgs& a,
-                           hipStream_t stream) {
-  LaunchFn f = n_prefill > 0 ? pick<MixedSel>(dtype, d, g) : pick<DecodeSel>(dtype, d, g);
-  return f ? f(a, n_decode + n_prefill, nullptr, 0, stream) : hipErrorInvalidValue;
+hipError_t launch_gqa_main(int dtype, int d, int g, bool has_prefill, const KernelArgs& a, hipStream_t stream) {
+  LaunchFn f = has_prefill ? pick<MixedSel>(dtype, d, g) : pick<DecodeSel>(dtype, d, g);
+  return f ? f(a, a.n_items, nullptr, 0, stream) : hipErrorInvalidValue;
 }
 
 hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,

@@ -36,7 +36,7 @@ constexpr int kPrefillTileKeys = 64;
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillRows = kPrefillWaves * kPrefillRowsPerWave;
-constexpr int kPrefillStages = 3;
+constexpr int kPrefillStages = 4;  // K/V tiles in the LDS ring
 
 template <int D>
 struct PrefillSmem {
@@ -52,9 +52,18 @@ __device__ __forceinline__ floatx16_t mfma_32x32x16(const bf16x8_t& a, const bf1
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-// 16 bytes from global memory to LDS at (wave-uniform base) + 16 * lane.
+// 16 bytes from global memory to LDS at (wave-uniform base) + 16 * lane
+// (global_load_lds_dwordx4; M0 holds the LDS base).
+//
+// Written as inline assembly on purpose: the compiler's wait-count insertion
+// treats every transposed LDS read (ds_read_b64_tr_b16) as possibly aliasing
+// any LDS DMA still in flight and drains the vector-memory counter before it,
+// which would wait for the tiles being prefetched.  Hidden from that pass,
+// the DMA is ordered by the callers' own s_waitcnt vmcnt + barrier pairs.  The
+// instruction writes no VGPR, so there is no in-flight register to track.
 __device__ __forceinline__ void load_to_lds(const void* src, char* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_base), 16, 0, 0);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
 }
 
 // Transposed read: in each 16-lane group, lane 4r + j supplies the address of
@@ -94,11 +103,13 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   constexpr int PIECES = D / 8;                      // 16-byte pieces per key row
   constexpr int TILE = PrefillSmem<D>::kTile;
   constexpr int STAGE = PrefillSmem<D>::kStage;
+  constexpr int NS = kPrefillStages;
   constexpr int KEYS_PER_LOAD = kWave / PIECES;      // key rows one wave-wide load covers
   constexpr int LOADS_PER_TILE = NT / KEYS_PER_LOAD; // per K (or V) tile
   constexpr int LOADS_PER_WAVE = 2 * LOADS_PER_TILE / kPrefillWaves;
   static_assert(PIECES >= 8 && kWave % PIECES == 0, "head size must be a multiple of 64");
   static_assert((2 * LOADS_PER_TILE) % kPrefillWaves == 0, "tile loads must split over the waves");
+  static_assert(KEYS_PER_LOAD <= 16, "one load must stay inside a page of 16 keys");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -113,8 +124,8 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   const int tb = it.tok_begin, te = it.tok_end;
   const int ps = 1 << a.page_shift;
   const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
-  const uint64_t row_stride = (uint64_t)a.hkv * D;
-  const uint64_t head_off = (uint64_t)it.kvh * D;
+  const uint32_t row_stride = (uint32_t)a.hkv * D;
+  const float c2 = a.scale_log2;
 
   // Q^T operand: lane (n, h) holds dims 16 ks + 8 h .. +7 of row n
   bf16x8_t qf[KS];
@@ -137,22 +148,19 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
-  float m = -INFINITY, l = 0.f, lx = 0.f;  // lx: unrounded weights, for the logsumexp
+  float m = -INFINITY, l = 0.f;
 
   // This wave issues loads wave * LOADS_PER_WAVE .. +LOADS_PER_WAVE of each
   // tile; load i covers K (i < LOADS_PER_TILE) or V rows KEYS_PER_LOAD *
-  // (i % LOADS_PER_TILE) + lane / PIECES at stored piece lane % PIECES.
-  // Keys outside [tb, te) read a clamped in-range key of the same tile.
-  // With pages of >= 16 keys a tile spans at most NT / 16 pages, whose numbers
-  // are wave-uniform scalar loads: the vector-memory counter then counts tile
-  // loads only and the wait below keeps the next tile in flight.  Smaller
-  // pages are looked up per lane and the wait drains everything.
+  // (i % LOADS_PER_TILE) + lane / PIECES at stored piece lane % PIECES.  The
+  // KEYS_PER_LOAD keys of one load share a page; a load starting past the
+  // last key is pulled back to the last group and keys past tok_end read the
+  // last key (so every row in LDS is finite sequence data).
   const int my_key_in_load = lane / PIECES;
   const int my_stored_piece = lane % PIECES;
   constexpr int MAXP = NT / 16;
   const int last_page = (te - 1) >> a.page_shift;
-  auto clamp_key = [&](int t) { return min(max(t, tb), te - 1); };
-  auto load_key = [&](int i) { return KEYS_PER_LOAD * (i % LOADS_PER_TILE) + my_key_in_load; };
+  const int last_grp = (te - 1) & ~(KEYS_PER_LOAD - 1);
   // wave-uniform page numbers of the (at most MAXP) pages tile t0 spans
   auto fetch_pages = [&](int t0, int (&tp)[MAXP]) {
     if constexpr (UNIFORM) {
@@ -166,72 +174,59 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
 #pragma unroll
     for (int j = 0; j < LOADS_PER_WAVE; ++j) {
       const int i = wave * LOADS_PER_WAVE + j;
-      const int key = load_key(i);
-      const int t = clamp_key(t0 + key);
+      const int kl = KEYS_PER_LOAD * (i % LOADS_PER_TILE);  // first key of the load within the tile
+      const int grp = min(t0 + kl, last_grp);              // wave-uniform
+      const int t = min(grp + my_key_in_load, te - 1);
       int page;
       if constexpr (UNIFORM) {
-        const int q = (t >> a.page_shift) - p0;  // 0 .. MAXP-1: t lies in this tile
+        const int q = (grp >> a.page_shift) - p0;  // 0 .. MAXP-1
         page = tp[0];
 #pragma unroll
         for (int k = 1; k < MAXP; ++k) page = q == k ? tp[k] : page;
       } else {
         page = bt[t >> a.page_shift];
       }
-      const int piece = my_stored_piece ^ swz<PIECES>(key);
-      const uint16_t* pool = reinterpret_cast<const uint16_t*>(i < LOADS_PER_TILE ? a.k : a.v);
-      const uint16_t* src = pool + ((uint64_t)page * ps + (t & (ps - 1))) * row_stride + head_off + piece * 8;
-      load_to_lds(src, stage + (i < LOADS_PER_TILE ? 0 : TILE) + (i % LOADS_PER_TILE) * 1024);
+      const int piece = my_stored_piece ^ swz<PIECES>(kl + my_key_in_load);
+      const uint16_t* pool = reinterpret_cast<const uint16_t*>(i < LOADS_PER_TILE ? a.k : a.v) +
+                             (uint64_t)page * ps * row_stride + (uint64_t)it.kvh * D;
+      const uint32_t off = (uint32_t)(t & (ps - 1)) * row_stride + piece * 8;
+      load_to_lds(pool + off, stage + (i < LOADS_PER_TILE ? 0 : TILE) + (i % LOADS_PER_TILE) * 1024);
     }
   };
-
-  // Page numbers run one tile ahead of the loads that use them.
-  const int t_first = tb & ~(NT - 1);
-  const int ntiles = (te - t_first + NT - 1) / NT;
-  int tp_next[MAXP];
-#pragma unroll
-  for (int j = 0; j < kPrefillStages - 1; ++j) {
-    if (j < ntiles) {
-      fetch_pages(t_first + j * NT, tp_next);
-      issue_tile(t_first + j * NT, smem + j * STAGE, tp_next);
-    }
-  }
-  fetch_pages(t_first + (kPrefillStages - 1) * NT, tp_next);
-  for (int j = 0; j < ntiles; ++j) {
-    if (UNIFORM && j + 1 < ntiles)
-      wait_vmcnt<LOADS_PER_WAVE>();  // tile j has landed, tile j+1 may still be in flight
-    else
+  // wait until at most `ahead` tiles of this wave's loads are still in flight
+  auto wait_tiles = [&](int ahead) {
+    if (!UNIFORM || ahead <= 0)
       wait_vmcnt<0>();
-    __syncthreads();  // every wave's share of tile j has landed; tile j-1's stage is free
-    if (j + kPrefillStages - 1 < ntiles) {
-      issue_tile(t_first + (j + kPrefillStages - 1) * NT, smem + ((j + kPrefillStages - 1) % kPrefillStages) * STAGE,
-                 tp_next);
-      fetch_pages(t_first + (j + kPrefillStages) * NT, tp_next);
-    }
-    const int t0 = t_first + j * NT;
-    const char* ks = smem + (j % kPrefillStages) * STAGE;
-    const char* vs = ks + TILE;
+    else if (ahead == 1)
+      wait_vmcnt<LOADS_PER_WAVE>();
+    else
+      wait_vmcnt<2 * LOADS_PER_WAVE>();
+  };
 
-    // tile entirely hidden from every row of this wave?
-    const bool hidden = pmax < 0 || (a.causal && t0 > pmax) || (a.window > 0 && t0 + NT - 1 <= pmin - a.window);
-    if (hidden) continue;
-    const bool full = t0 >= tb && t0 + NT <= te && (!a.causal || t0 + NT - 1 <= pmin) &&
-                      (a.window == 0 || t0 > pmax - a.window);
-
-    // S^T = K . Q^T : two 32-key blocks; lane (n, h) reads dims 16 k + 8 h of key row n
-    floatx16_t s[2];
+  // tile entirely hidden from every row of this wave?
+  auto hidden = [&](int t0) {
+    return pmax < 0 || (a.causal && t0 > pmax) || (a.window > 0 && t0 + NT - 1 <= pmin - a.window);
+  };
+  // S^T = K . Q^T : two 32-key blocks; lane (n, h) reads dims 16 k + 8 h of key row n
+  auto scores = [&](const char* ks, floatx16_t (&s)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
-      const int key = mb * 32 + n;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + tile_off<D>(key, 2 * k + h));
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + tile_off<D>(mb * 32 + n, 2 * k + h));
         s[mb] = mfma_32x32x16(kf, qf[k], s[mb]);
       }
-    }
-
-    // mask: accumulator element e of block mb holds key t0 + 32 mb + 8 (e/4) + 4 h + e%4
+  };
+  // mask, new running max and rescale of the accumulators; returns the
+  // subtrahend of the exponent (max in log2 units)
+  auto row_max = [&](int t0, floatx16_t (&s)[2]) {
+    const bool full = t0 >= tb && t0 + NT <= te && (!a.causal || t0 + NT - 1 <= pmin) &&
+                      (a.window == 0 || t0 > pmax - a.window);
+    // accumulator element e of block mb holds key t0 + 32 mb + 8 (e/4) + 4 h + e%4
     if (!full) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -243,44 +238,43 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
           s[mb][e] = vis ? s[mb][e] : -INFINITY;
         }
     }
-
-    // online softmax for this lane's row (both lane halves hold the same row)
     float mx = m;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair32_max(mx);  // both lane halves hold the same row
     const float mu = (mx == -INFINITY) ? 0.f : mx;
-    const float alpha = fast_exp2((m - mu) * a.scale_log2);
+    const float alpha = fast_exp2((m - mu) * c2);
     m = mx;
     l *= alpha;
-    lx *= alpha;
     if (__any(alpha != 1.f)) {  // no row of the wave raised its max: nothing to rescale
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[b][e] *= alpha;
     }
-
-    // O^T += V^T . P^T.  k-step kk covers keys 16 kk .. +15; lane (n, h) feeds
-    // keys 16 kk + 8 (e/4) + 4 h + e%4 (e = 0..7): elements 8 (kk % 2) + e of
-    // S^T block kk / 2, and the V^T rows of the same keys by two transposed
-    // reads (4 keys each) of dims 32 b + 16 (lane/16 % 2) + lane % 16.
-    const int grp = lane >> 4, gi = lane & 15;
-    const int hh = grp >> 1, d16 = grp & 1;
-    const int rr = gi >> 2, jj = gi & 3;
+    return mu * c2;
+  };
+  // P^T = 2^(S^T c - max) rounded to bf16 and O^T += V^T . P^T.  k-step kk
+  // covers keys 16 kk .. +15; lane (n, h) feeds keys 16 kk + 8 (e/4) + 4 h +
+  // e%4 (e = 0..7): elements 8 (kk % 2) + e of S^T block kk / 2, and the V^T
+  // rows of the same keys by two transposed reads (4 keys each) of dims 32 b
+  // + 16 (lane/16 % 2) + lane % 16.
+  const int grp16 = lane >> 4, gi = lane & 15;
+  const int hh = grp16 >> 1, d16 = grp16 & 1;
+  const int rr = gi >> 2, jj = gi & 3;
+  auto weights_pv = [&](const char* vs, const floatx16_t (&s)[2], float sub) {
 #pragma unroll
     for (int kk = 0; kk < NT / 16; ++kk) {
       const int mb = kk >> 1, e0 = 8 * (kk & 1);
       uint32_t pw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p0 = fast_exp2((s[mb][e0 + 2 * j] - mu) * a.scale_log2);
-        const float p1 = fast_exp2((s[mb][e0 + 2 * j + 1] - mu) * a.scale_log2);
+        const float p0 = fast_exp2(__builtin_fmaf(s[mb][e0 + 2 * j], c2, -sub));
+        const float p1 = fast_exp2(__builtin_fmaf(s[mb][e0 + 2 * j + 1], c2, -sub));
         pw[j] = pack_bf16(p0, p1);
-        l += bf16_lo(pw[j]) + bf16_hi(pw[j]);
-        lx += p0 + p1;
+        l += p0 + p1;
       }
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
       const int key0 = 16 * kk + 4 * hh + rr;  // rows r of the first read; +8 for the second
@@ -298,10 +292,63 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
         o[b] = mfma_32x32x16(vf, pf, o[b]);
       }
     }
+  };
+
+  // Software pipeline over the key tiles: iteration j computes the scores of
+  // tile j + 1 on MFMA while the vector units turn the scores of tile j into
+  // weights, then accumulates tile j.  The ring holds tile j (V being read),
+  // j + 1 (K being read), j + 2 (in flight) and j + 3 (issued at the top of
+  // iteration j into the stage tile j - 1 used).  Page numbers run one tile
+  // ahead of the loads that use them.
+  const int t_first = tb & ~(NT - 1);
+  const int ntiles = (te - t_first + NT - 1) / NT;
+  int tp_next[MAXP];
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j) {
+    if (j < ntiles) {
+      fetch_pages(t_first + j * NT, tp_next);
+      issue_tile(t_first + j * NT, smem + j * STAGE, tp_next);
+    }
+  }
+  fetch_pages(t_first + (NS - 1) * NT, tp_next);
+
+  floatx16_t s_cur[2];
+  wait_tiles(min(ntiles - 1, NS - 2));
+  __syncthreads();  // tile 0 has landed everywhere
+  if (!hidden(t_first)) scores(smem, s_cur);
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int t0 = t_first + j * NT;
+    const bool has_next = j + 1 < ntiles;
+    if (has_next) {
+      wait_tiles(min(ntiles - 2 - j, 1));  // tile j + 1 has landed, j + 2 may be in flight
+      __syncthreads();  // ... for every wave; every wave is done with tile j - 1
+      if (j + NS - 1 < ntiles) {
+        issue_tile(t_first + (j + NS - 1) * NT, smem + ((j + NS - 1) % NS) * STAGE, tp_next);
+        fetch_pages(t_first + (j + NS) * NT, tp_next);
+      }
+    }
+    const char* vs = smem + (j % NS) * STAGE + TILE;
+    const char* ks_next = smem + ((j + 1) % NS) * STAGE;
+    const bool cur = !hidden(t0);
+    const bool nxt = has_next && !hidden(t0 + NT);
+    floatx16_t s_next[2];
+    if (cur) {
+      const float sub = row_max(t0, s_cur);
+      if (nxt) {
+        scores(ks_next, s_next);
+        weights_pv(vs, s_cur, sub);
+      } else {
+        weights_pv(vs, s_cur, sub);
+      }
+    } else if (nxt) {
+      scores(ks_next, s_next);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) s_cur[mb] = s_next[mb];
   }
 
-  l += __shfl_xor(l, 32);
-  lx += __shfl_xor(lx, 32);
+  l = pair32_sum(l);
   if (!row_valid) return;
   const float inv = 1.f / l;
   uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * a.hq + head) * D;
@@ -315,7 +362,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
       w.y = pack_bf16(o[b][4 * k + 2] * inv, o[b][4 * k + 3] * inv);
       *reinterpret_cast<uint2*>(orow + 32 * b + 8 * k + 4 * h) = w;
     }
-  if (a.lse && h == 0) a.lse[(uint64_t)qi * a.hq + head] = m * a.scale + logf(lx);
+  if (a.lse && h == 0) a.lse[(uint64_t)qi * a.hq + head] = m * a.scale + logf(l);
 }
 
 template <int D, int G>
