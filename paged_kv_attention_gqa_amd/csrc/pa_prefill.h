@@ -37,6 +37,7 @@ constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillRows = kPrefillWaves * kPrefillRowsPerWave;
 constexpr int kPrefillStages = 4;  // K/V tiles in the LDS ring
+constexpr float kLazyRescaleLog2 = 8.f;  // weights may reach 2^8 before the reference max moves
 
 template <int D>
 struct PrefillSmem {
@@ -64,6 +65,12 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 __device__ __forceinline__ void load_to_lds(const void* src, char* lds_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds_base);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
+}
+// The same load from (wave-uniform base) + 32-bit per-lane byte offset
+// (global_load_lds_dwordx4 with a scalar base address).
+__device__ __forceinline__ void load_to_lds_sv(const char* base, uint32_t off, char* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds) : "m0");
 }
 
 // Transposed read: in each 16-lane group, lane 4r + j supplies the address of
@@ -107,9 +114,10 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   constexpr int KEYS_PER_LOAD = kWave / PIECES;      // key rows one wave-wide load covers
   constexpr int LOADS_PER_TILE = NT / KEYS_PER_LOAD; // per K (or V) tile
   constexpr int LOADS_PER_WAVE = 2 * LOADS_PER_TILE / kPrefillWaves;
+  constexpr int KEYS_PER_WAVE = KEYS_PER_LOAD * LOADS_PER_WAVE;
   static_assert(PIECES >= 8 && kWave % PIECES == 0, "head size must be a multiple of 64");
-  static_assert((2 * LOADS_PER_TILE) % kPrefillWaves == 0, "tile loads must split over the waves");
-  static_assert(KEYS_PER_LOAD <= 16, "one load must stay inside a page of 16 keys");
+  static_assert(KEYS_PER_WAVE == 16 && LOADS_PER_TILE == 4 * LOADS_PER_WAVE,
+                "each wave loads 16 consecutive key rows of K (waves 0-3) or V (waves 4-7)");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,7 +132,6 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   const int tb = it.tok_begin, te = it.tok_end;
   const int ps = 1 << a.page_shift;
   const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
-  const uint32_t row_stride = (uint32_t)a.hkv * D;
   const float c2 = a.scale_log2;
 
   // Q^T operand: lane (n, h) holds dims 16 ks + 8 h .. +7 of row n
@@ -148,49 +155,62 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
+  // m: reference max of the row (raised lazily, see row_max); l: sum of the
+  // (unrounded) weights relative to it
   float m = -INFINITY, l = 0.f;
 
-  // This wave issues loads wave * LOADS_PER_WAVE .. +LOADS_PER_WAVE of each
-  // tile; load i covers K (i < LOADS_PER_TILE) or V rows KEYS_PER_LOAD *
-  // (i % LOADS_PER_TILE) + lane / PIECES at stored piece lane % PIECES.  The
-  // KEYS_PER_LOAD keys of one load share a page; a load starting past the
-  // last key is pulled back to the last group and keys past tok_end read the
-  // last key (so every row in LDS is finite sequence data).
-  const int my_key_in_load = lane / PIECES;
-  const int my_stored_piece = lane % PIECES;
-  constexpr int MAXP = NT / 16;
-  const int last_page = (te - 1) >> a.page_shift;
-  const int last_grp = (te - 1) & ~(KEYS_PER_LOAD - 1);
-  // wave-uniform page numbers of the (at most MAXP) pages tile t0 spans
-  auto fetch_pages = [&](int t0, int (&tp)[MAXP]) {
-    if constexpr (UNIFORM) {
-      const int p0 = t0 >> a.page_shift;
-#pragma unroll
-      for (int q = 0; q < MAXP; ++q) tp[q] = load_uniform(bt, min(p0 + q, last_page));
-    }
+  // Tile loads.  Wave w fills key rows 16 (w % 4) .. +15 of the K tile (w < 4)
+  // or the V tile (w >= 4) with LOADS_PER_WAVE loads of KEYS_PER_LOAD rows;
+  // lane l carries stored piece l % PIECES of row l / PIECES of its load.
+  // Sixteen aligned keys never straddle a page of >= 16 keys, so one page
+  // number per wave and tile is enough: it is a scalar load issued a tile
+  // ahead.  Keys past tok_end read the last key instead (every row in LDS is
+  // finite sequence data; such keys are masked); keys before tok_begin are
+  // sequence keys and are masked as well.
+  const int wq = wave & 3;
+  const bool loads_v = wave >= 4;
+  const uint32_t rs2 = (uint32_t)a.hkv * D * 2;  // bytes between consecutive key rows
+  const char* pool_kvh = reinterpret_cast<const char*>(loads_v ? a.v : a.k) + (uint64_t)it.kvh * D * 2;
+  // Byte offset of this lane's source for load j: (KEYS_PER_LOAD j + my_key)
+  // rows plus its stored piece.  swz permutes the low key bits, so for row
+  // 16 (w % 4) + KEYS_PER_LOAD j + my_key it equals swz(my_key) ^
+  // swz(KEYS_PER_LOAD j); rows are >= 128 bytes apart, so the XOR stays in
+  // the piece bits: lane_off(j) = (lane_off0 ^ (swz(KEYS_PER_LOAD j) << 4)) +
+  // KEYS_PER_LOAD j rows.
+  const int my_key = lane / PIECES;
+  const uint32_t lane_piece0 = (uint32_t)(((lane % PIECES) ^ swz<PIECES>(my_key)) << 4);
+  const uint32_t lane_off0 = (uint32_t)my_key * rs2 + lane_piece0;
+  auto lane_piece = [&](int j) { return lane_piece0 ^ (uint32_t)(swz<PIECES>(KEYS_PER_LOAD * j) << 4); };
+  auto lane_off = [&](int j) {
+    return (lane_off0 ^ (uint32_t)(swz<PIECES>(KEYS_PER_LOAD * j) << 4)) + (uint32_t)(KEYS_PER_LOAD * j) * rs2;
   };
-  auto issue_tile = [&](int t0, char* stage, const int (&tp)[MAXP]) {
-    const int p0 = t0 >> a.page_shift;
+  auto page_of = [&](int t0) {
+    if constexpr (UNIFORM)
+      return load_uniform(bt, min(t0 + KEYS_PER_WAVE * wq, te - 1) >> a.page_shift);
+    else
+      return 0;
+  };
+  auto issue_tile = [&](int t0, char* stage, int page) {
+    char* dst = stage + (loads_v ? TILE : 0) + KEYS_PER_WAVE * wq * (D * 2);
+    const int k0 = t0 + KEYS_PER_WAVE * wq;  // first key of this wave's rows
+    if (UNIFORM && k0 + KEYS_PER_WAVE <= te) {
+      // whole group in range: one scalar base, fixed lane offsets
+      const char* base = pool_kvh + ((uint64_t)page * ps + (k0 & (ps - 1))) * rs2;
 #pragma unroll
-    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
-      const int i = wave * LOADS_PER_WAVE + j;
-      const int kl = KEYS_PER_LOAD * (i % LOADS_PER_TILE);  // first key of the load within the tile
-      const int grp = min(t0 + kl, last_grp);              // wave-uniform
-      const int t = min(grp + my_key_in_load, te - 1);
-      int page;
-      if constexpr (UNIFORM) {
-        const int q = (grp >> a.page_shift) - p0;  // 0 .. MAXP-1
-        page = tp[0];
+      for (int j = 0; j < LOADS_PER_WAVE; ++j)
+        load_to_lds_sv(base, lane_off(j), dst + j * 1024);
+    } else {
 #pragma unroll
-        for (int k = 1; k < MAXP; ++k) page = q == k ? tp[k] : page;
-      } else {
-        page = bt[t >> a.page_shift];
+      for (int j = 0; j < LOADS_PER_WAVE; ++j) {
+        const int t = min(k0 + KEYS_PER_LOAD * j + my_key, te - 1);
+        const uint32_t off = (uint32_t)(t & (ps - 1)) * rs2 + lane_piece(j);
+        if constexpr (UNIFORM) {
+          load_to_lds_sv(pool_kvh + (uint64_t)page * ps * rs2, off, dst + j * 1024);
+        } else {
+          const char* src = pool_kvh + (uint64_t)bt[t >> a.page_shift] * ps * rs2 + off;  // per-lane page
+          load_to_lds(src, dst + j * 1024);
+        }
       }
-      const int piece = my_stored_piece ^ swz<PIECES>(kl + my_key_in_load);
-      const uint16_t* pool = reinterpret_cast<const uint16_t*>(i < LOADS_PER_TILE ? a.k : a.v) +
-                             (uint64_t)page * ps * row_stride + (uint64_t)it.kvh * D;
-      const uint32_t off = (uint32_t)(t & (ps - 1)) * row_stride + piece * 8;
-      load_to_lds(pool + off, stage + (i < LOADS_PER_TILE ? 0 : TILE) + (i % LOADS_PER_TILE) * 1024);
     }
   };
   // wait until at most `ahead` tiles of this wave's loads are still in flight
@@ -221,8 +241,12 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
         s[mb] = mfma_32x32x16(kf, qf[k], s[mb]);
       }
   };
-  // mask, new running max and rescale of the accumulators; returns the
-  // subtrahend of the exponent (max in log2 units)
+  // Mask the tile and update the reference max; returns the exponent offset
+  // (reference max in log2 units).  The reference is raised only when a row's
+  // tile max exceeds it by more than 2^kLazyRescaleLog2 in weight, so weights
+  // stay <= 2^kLazyRescaleLog2 and the accumulators are rescaled only on the
+  // few tiles that raise some row's max that far.  Numerator and denominator
+  // share the reference, so the result does not depend on when it moves.
   auto row_max = [&](int t0, floatx16_t (&s)[2]) {
     const bool full = t0 >= tb && t0 + NT <= te && (!a.causal || t0 + NT - 1 <= pmin) &&
                       (a.window == 0 || t0 > pmax - a.window);
@@ -238,25 +262,25 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
           s[mb][e] = vis ? s[mb][e] : -INFINITY;
         }
     }
-    float mx = m;
+    float mx = s[0][0];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
     mx = pair32_max(mx);  // both lane halves hold the same row
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    const float alpha = fast_exp2((m - mu) * c2);
-    m = mx;
-    l *= alpha;
-    if (__any(alpha != 1.f)) {  // no row of the wave raised its max: nothing to rescale
+    if (__any(mx * c2 > m * c2 + kLazyRescaleLog2)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2((m - (mn == -INFINITY ? 0.f : mn)) * c2);
+      m = mn;
+      l *= alpha;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[b][e] *= alpha;
     }
-    return mu * c2;
+    return (m == -INFINITY ? 0.f : m) * c2;
   };
-  // P^T = 2^(S^T c - max) rounded to bf16 and O^T += V^T . P^T.  k-step kk
+  // P^T = 2^(S^T c - ref) rounded to bf16 and O^T += V^T . P^T.  k-step kk
   // covers keys 16 kk .. +15; lane (n, h) feeds keys 16 kk + 8 (e/4) + 4 h +
   // e%4 (e = 0..7): elements 8 (kk % 2) + e of S^T block kk / 2, and the V^T
   // rows of the same keys by two transposed reads (4 keys each) of dims 32 b
@@ -294,45 +318,44 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     }
   };
 
-  // Software pipeline over the key tiles: iteration j computes the scores of
-  // tile j + 1 on MFMA while the vector units turn the scores of tile j into
+  // Software pipeline over the key tiles: step j computes the scores of tile
+  // j + 1 on MFMA while the vector units turn the scores of tile j into
   // weights, then accumulates tile j.  The ring holds tile j (V being read),
   // j + 1 (K being read), j + 2 (in flight) and j + 3 (issued at the top of
-  // iteration j into the stage tile j - 1 used).  Page numbers run one tile
-  // ahead of the loads that use them.
+  // step j into the stage tile j - 1 used).  Page numbers run one tile ahead
+  // of the loads that use them.  Steps alternate between two score buffers.
   const int t_first = tb & ~(NT - 1);
   const int ntiles = (te - t_first + NT - 1) / NT;
-  int tp_next[MAXP];
+  int page_next = 0;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j) {
     if (j < ntiles) {
-      fetch_pages(t_first + j * NT, tp_next);
-      issue_tile(t_first + j * NT, smem + j * STAGE, tp_next);
+      page_next = page_of(t_first + j * NT);
+      issue_tile(t_first + j * NT, smem + j * STAGE, page_next);
     }
   }
-  fetch_pages(t_first + (NS - 1) * NT, tp_next);
+  page_next = page_of(t_first + (NS - 1) * NT);
 
-  floatx16_t s_cur[2];
+  floatx16_t sa[2], sb[2];
   wait_tiles(min(ntiles - 1, NS - 2));
   __syncthreads();  // tile 0 has landed everywhere
-  if (!hidden(t_first)) scores(smem, s_cur);
+  if (!hidden(t_first)) scores(smem, sa);
 
-  for (int j = 0; j < ntiles; ++j) {
+  auto step = [&](int j, floatx16_t (&s_cur)[2], floatx16_t (&s_next)[2]) __attribute__((always_inline)) {
     const int t0 = t_first + j * NT;
     const bool has_next = j + 1 < ntiles;
     if (has_next) {
       wait_tiles(min(ntiles - 2 - j, 1));  // tile j + 1 has landed, j + 2 may be in flight
       __syncthreads();  // ... for every wave; every wave is done with tile j - 1
       if (j + NS - 1 < ntiles) {
-        issue_tile(t_first + (j + NS - 1) * NT, smem + ((j + NS - 1) % NS) * STAGE, tp_next);
-        fetch_pages(t_first + (j + NS) * NT, tp_next);
+        issue_tile(t_first + (j + NS - 1) * NT, smem + ((j + NS - 1) % NS) * STAGE, page_next);
+        page_next = page_of(t_first + (j + NS) * NT);
       }
     }
     const char* vs = smem + (j % NS) * STAGE + TILE;
     const char* ks_next = smem + ((j + 1) % NS) * STAGE;
     const bool cur = !hidden(t0);
     const bool nxt = has_next && !hidden(t0 + NT);
-    floatx16_t s_next[2];
     if (cur) {
       const float sub = row_max(t0, s_cur);
       if (nxt) {
@@ -344,8 +367,11 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     } else if (nxt) {
       scores(ks_next, s_next);
     }
+  };
+  for (int j = 0; j < ntiles; ++j) {
+    step(j, sa, sb);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) s_cur[mb] = s_next[mb];
+    for (int mb = 0; mb < 2; ++mb) sa[mb] = sb[mb];
   }
 
   l = pair32_sum(l);
