@@ -318,60 +318,52 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     }
   };
 
-  // Software pipeline over the key tiles: step j computes the scores of tile
-  // j + 1 on MFMA while the vector units turn the scores of tile j into
-  // weights, then accumulates tile j.  The ring holds tile j (V being read),
-  // j + 1 (K being read), j + 2 (in flight) and j + 3 (issued at the top of
-  // step j into the stage tile j - 1 used).  Page numbers run one tile ahead
-  // of the loads that use them.  Steps alternate between two score buffers.
+  // Two wave groups in opposite phase.  Between the barriers that publish
+  // tiles j and j + 1, the leading waves (0-3) compute the scores of tile j,
+  // its weights and its accumulation; the trailing waves (4-7) first turn the
+  // scores of tile j - 1 into weights and accumulate them, then compute the
+  // scores of tile j.  Each SIMD holds one wave of each group, so one wave's
+  // MFMA work overlaps the other's vector work.  Tiles land two barriers
+  // after their loads are issued; the ring holds tile j - 1 (V, trailing
+  // waves), j (being read), j + 1 (in flight) and j + 2 (issued after the
+  // barrier of tile j into the stage tile j - 2 used).  Page numbers run one
+  // tile ahead of the loads that use them.
   const int t_first = tb & ~(NT - 1);
   const int ntiles = (te - t_first + NT - 1) / NT;
+  const bool lead = wave < kPrefillWaves / 2;
   int page_next = 0;
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j) {
+  for (int j = 0; j < NS - 2; ++j) {
     if (j < ntiles) {
       page_next = page_of(t_first + j * NT);
       issue_tile(t_first + j * NT, smem + j * STAGE, page_next);
     }
   }
-  page_next = page_of(t_first + (NS - 1) * NT);
+  page_next = page_of(t_first + (NS - 2) * NT);
 
-  floatx16_t sa[2], sb[2];
-  wait_tiles(min(ntiles - 1, NS - 2));
-  __syncthreads();  // tile 0 has landed everywhere
-  if (!hidden(t_first)) scores(smem, sa);
-
-  auto step = [&](int j, floatx16_t (&s_cur)[2], floatx16_t (&s_next)[2]) __attribute__((always_inline)) {
-    const int t0 = t_first + j * NT;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) {
-      wait_tiles(min(ntiles - 2 - j, 1));  // tile j + 1 has landed, j + 2 may be in flight
-      __syncthreads();  // ... for every wave; every wave is done with tile j - 1
-      if (j + NS - 1 < ntiles) {
-        issue_tile(t_first + (j + NS - 1) * NT, smem + ((j + NS - 1) % NS) * STAGE, page_next);
-        page_next = page_of(t_first + (j + NS) * NT);
-      }
-    }
-    const char* vs = smem + (j % NS) * STAGE + TILE;
-    const char* ks_next = smem + ((j + 1) % NS) * STAGE;
-    const bool cur = !hidden(t0);
-    const bool nxt = has_next && !hidden(t0 + NT);
-    if (cur) {
-      const float sub = row_max(t0, s_cur);
-      if (nxt) {
-        scores(ks_next, s_next);
-        weights_pv(vs, s_cur, sub);
-      } else {
-        weights_pv(vs, s_cur, sub);
-      }
-    } else if (nxt) {
-      scores(ks_next, s_next);
+  // One loop body for both groups: weights of tile j - 1, then scores of
+  // tile j; only the barrier (and the loads issued after it) sits before the
+  // weights in the trailing waves and after them in the leading ones.
+  floatx16_t s[2];
+  float sub = 0.f;
+  auto sync = [&](int j) {
+    wait_tiles(min(ntiles - 1 - j, 1));  // tile j has landed, j + 1 may be in flight
+    __syncthreads();                     // ... for every wave; tile j - 2 is no longer read
+    if (j + NS - 2 < ntiles) {
+      issue_tile(t_first + (j + NS - 2) * NT, smem + ((j + NS - 2) % NS) * STAGE, page_next);
+      page_next = page_of(t_first + (j + NS - 1) * NT);
     }
   };
-  for (int j = 0; j < ntiles; ++j) {
-    step(j, sa, sb);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) sa[mb] = sb[mb];
+  for (int j = 0; j <= ntiles; ++j) {
+    const int t0 = t_first + j * NT;
+    const bool more = j < ntiles;
+    if (!lead && more) sync(j);
+    if (j > 0 && !hidden(t0 - NT)) weights_pv(smem + ((j - 1) % NS) * STAGE + TILE, s, sub);
+    if (lead && more) sync(j);
+    if (more && !hidden(t0)) {
+      scores(smem + (j % NS) * STAGE, s);
+      sub = row_max(t0, s);
+    }
   }
 
   l = pair32_sum(l);
