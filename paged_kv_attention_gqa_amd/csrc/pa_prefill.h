@@ -233,13 +233,22 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
+    // K fragments run kAhead MFMAs ahead of their use (a small register ring)
+    constexpr int kSteps = 2 * KS, kAhead = 4;
+    auto frag = [&](int i) {
+      return *reinterpret_cast<const bf16x8_t*>(ks + tile_off<D>((i & 1) * 32 + n, 2 * (i >> 1) + h));
+    };
+    bf16x8_t ring[kAhead];
 #pragma unroll
-    for (int k = 0; k < KS; ++k)
+    for (int i = 0; i < kAhead; ++i) ring[i] = frag(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + tile_off<D>(mb * 32 + n, 2 * k + h));
-        s[mb] = mfma_32x32x16(kf, qf[k], s[mb]);
-      }
+    for (int i = 0; i < kSteps; ++i) {
+      const bf16x8_t kf = ring[i % kAhead];
+      if (i + kAhead < kSteps) ring[i % kAhead] = frag(i + kAhead);
+      s[i & 1] = mfma_32x32x16(kf, qf[i >> 1], s[i & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the read distance (the scheduler would shorten it)
+    }
   };
   // Mask the tile and update the reference max; returns the exponent offset
   // (reference max in log2 units).  The reference is raised only when a row's
