@@ -227,6 +227,25 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   auto hidden = [&](int t0) {
     return pmax < 0 || (a.causal && t0 > pmax) || (a.window > 0 && t0 + NT - 1 <= pmin - a.window);
   };
+  // LDS byte offsets of this lane's operand reads within a tile, computed once:
+  // K fragment k (key row n, piece 2k + h; +32 rows for the second block) and
+  // V^T half-fragments (b, r) of k-step 0 (later k-steps add 16 rows).
+  uint32_t koff[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) koff[k] = (uint32_t)tile_off<D>(n, 2 * k + h);
+  uint32_t voff[DB][2];
+  {
+    const int grp16 = lane >> 4, gi = lane & 15;
+    const int key0 = 4 * (grp16 >> 1) + (gi >> 2);
+    const int dim0 = 16 * (grp16 & 1) + 4 * (gi & 3);
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int dim = 32 * b + dim0;
+        voff[b][r] = (uint32_t)(tile_off<D>(key0 + 8 * r, dim >> 3) + (dim & 7) * 2);
+      }
+  }
   // S^T = K . Q^T : two 32-key blocks; lane (n, h) reads dims 16 k + 8 h of key row n
   auto scores = [&](const char* ks, floatx16_t (&s)[2]) {
 #pragma unroll
@@ -236,7 +255,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     // K fragments run kAhead MFMAs ahead of their use (a small register ring)
     constexpr int kSteps = 2 * KS, kAhead = 4;
     auto frag = [&](int i) {
-      return *reinterpret_cast<const bf16x8_t*>(ks + tile_off<D>((i & 1) * 32 + n, 2 * (i >> 1) + h));
+      return *reinterpret_cast<const bf16x8_t*>(ks + koff[i >> 1] + (i & 1) * 32 * (D * 2));
     };
     bf16x8_t ring[kAhead];
 #pragma unroll
@@ -293,10 +312,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // covers keys 16 kk .. +15; lane (n, h) feeds keys 16 kk + 8 (e/4) + 4 h +
   // e%4 (e = 0..7): elements 8 (kk % 2) + e of S^T block kk / 2, and the V^T
   // rows of the same keys by two transposed reads (4 keys each) of dims 32 b
-  // + 16 (lane/16 % 2) + lane % 16.
-  const int grp16 = lane >> 4, gi = lane & 15;
-  const int hh = grp16 >> 1, d16 = grp16 & 1;
-  const int rr = gi >> 2, jj = gi & 3;
+  // + 16 (lane/16 % 2) + lane % 16 (offsets voff, plus 16 rows per k-step).
   auto weights_pv = [&](const char* vs, const floatx16_t (&s)[2], float sub) {
 #pragma unroll
     for (int kk = 0; kk < NT / 16; ++kk) {
@@ -310,13 +326,10 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
         l += p0 + p1;
       }
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      const int key0 = 16 * kk + 4 * hh + rr;  // rows r of the first read; +8 for the second
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        const int dim = 32 * b + 16 * d16 + 4 * jj;
-        const int piece = dim >> 3, half = (dim & 7) * 2;
-        const short4_t v0 = lds_read_tr16(vs + tile_off<D>(key0, piece) + half);
-        const short4_t v1 = lds_read_tr16(vs + tile_off<D>(key0 + 8, piece) + half);
+        const short4_t v0 = lds_read_tr16(vs + voff[b][0] + kk * 16 * (D * 2));
+        const short4_t v1 = lds_read_tr16(vs + voff[b][1] + kk * 16 * (D * 2));
         const bf16x8_t vf = __builtin_bit_cast(
             bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
