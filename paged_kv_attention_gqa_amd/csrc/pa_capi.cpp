@@ -50,6 +50,11 @@ constexpr int kDefaultSplitTokens = 512;
 constexpr int kMixedSplitTokens = 2048;
 constexpr int kDefaultMlaSplitTokens = 1024;
 constexpr int kSplitAlign = 64;
+// Shortest piece of a split decode row in a balanced plan: a piece's partial
+// results (G x Dv floats for GQA, 16 x 512 for MLA) should stay small next to
+// the keys it reads.
+constexpr int kMinPieceKeys = 128;
+constexpr int kMlaMinPieceKeys = 256;
 constexpr int kMaxSplitsLimit = 64;
 constexpr size_t kAlign = 256;
 
@@ -66,9 +71,11 @@ struct pa_plan {
   int32_t hq = 0, hkv = 0, causal = 0, window = 0, max_splits = 1, mla = 0, split_tokens = 0;
   std::vector<int32_t> seq_lens, cu_q, q_pos, bt;
   // work lists, host copy
-  std::vector<WorkItem> items;  // launch order
+  std::vector<WorkItem> items;    // grouped by workgroup, launch order
+  std::vector<int32_t> wg_first;  // workgroup b runs items wg_first[b] .. wg_first[b + 1] - 1
   std::vector<MergeItem> merges;
   int32_t n_decode = 0, n_prefill = 0, n_slots = 0;
+  int32_t n_cu = 0;               // compute units of the plan's device
   // device copy: one allocation
   std::vector<char> blob;
   char* dev = nullptr;
@@ -76,6 +83,7 @@ struct pa_plan {
   const int32_t* d_qpos = nullptr;
   const int32_t* d_lens = nullptr;
   const WorkItem* d_items = nullptr;
+  const int32_t* d_wg_first = nullptr;
   const MergeItem* d_merges = nullptr;
 
   int group() const { return hq / hkv; }
@@ -229,6 +237,105 @@ void order_items(pa_plan* p, const std::vector<WorkItem>& pre, const std::vector
     for (int x = 0; x < kXcds; ++x)
       p->items.push_back(j < bins[x].size() ? bins[x][j] : WorkItem{pa::kEmpty, 0, 0, 0, 0, 0, 0, -1});
   while (!p->items.empty() && p->items.back().kind == pa::kEmpty) p->items.pop_back();
+  p->wg_first.resize(p->items.size() + 1);
+  for (size_t i = 0; i < p->wg_first.size(); ++i) p->wg_first[i] = (int32_t)i;
+}
+
+// Decode rows balanced over the workgroups resident at once (`slots` = CUs x
+// workgroups per CU).  The key range of every query is cut into pieces and
+// the pieces are dealt to groups of Hkv workgroups, one workgroup per KV
+// head, so that every workgroup gets about the same number of keys and the
+// Hkv workgroups of a group (consecutive, so dispatched together) read the
+// same page slots at the same time; the launch has no tail of lone
+// workgroups.  Cuts fall on multiples of kSplitAlign keys; pieces are at
+// least `min_piece` keys (each split piece costs a partial write and a merge
+// read); a row is cut into at most max_splits pieces, earlier pieces growing
+// when the rest of the row would not fit the remaining pieces at about one
+// target each; a row cut into several pieces gets one partial slot per piece
+// and a merge.  The target of each group is recomputed from the keys
+// still unassigned, and the last group takes whatever remains.
+void plan_balanced(pa_plan* p, int slots, int min_piece) {
+  struct Row {
+    int s, q, lo, hi;  // keys [lo, hi)
+  };
+  std::vector<Row> rows;
+  int64_t left = 0;
+  for (int s = 0; s < p->S; ++s)
+    for (int i = p->cu_q[s]; i < p->cu_q[s + 1]; ++i) {
+      int lo, hi;
+      visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &lo, &hi);
+      rows.push_back(Row{s, i, lo, hi + 1});
+      left += hi + 1 - lo;
+    }
+  const int groups = std::max(1, slots / p->hkv);
+  auto align_up = [](int64_t x) { return (x + kSplitAlign - 1) / kSplitAlign * kSplitAlign; };
+  auto align_down = [](int64_t x) { return x / kSplitAlign * kSplitAlign; };
+  struct Piece {
+    int row, b, e, part;
+  };
+  std::vector<std::vector<Piece>> grp(1);
+  std::vector<int> nparts(rows.size(), 0);
+  int64_t fill = 0, target = (left + groups - 1) / groups;
+  auto close_group = [&]() {
+    if ((int)grp.size() >= groups) return;
+    grp.emplace_back();
+    fill = 0;
+    const int64_t rest = groups - (int64_t)grp.size() + 1;
+    target = (left + rest - 1) / rest;
+  };
+  for (size_t ri = 0; ri < rows.size(); ++ri) {
+    const Row& r = rows[ri];
+    int b = r.lo;
+    while (b < r.hi) {
+      const int64_t rem = r.hi - b, room = target - fill;
+      // this piece must be long enough for the rest of the row to fit in the
+      // pieces max_splits still allows, at about one target each
+      const int64_t pieces_left = p->max_splits - nparts[ri];
+      const int64_t min_len = std::max<int64_t>(min_piece, rem - (pieces_left - 1) * target);
+      int64_t take = rem;
+      if ((int)grp.size() < groups && rem > room && pieces_left > 1) {
+        if (fill > 0 && room < min_len) {  // too little room left: start the piece in the next group
+          close_group();
+          continue;
+        }
+        take = std::min(align_up(b + std::max<int64_t>(room, min_len)) - b, rem);
+        if (rem - take < min_piece) {
+          // the tail would be too short: either take it too, or leave a
+          // min_piece tail, whichever lands nearer the target
+          const int64_t shorter = align_down(r.hi - min_piece) - b;
+          take = (shorter >= min_len && room - shorter < rem - room) ? shorter : rem;
+        }
+      }
+      grp.back().push_back(Piece{(int)ri, b, (int)(b + take), nparts[ri]++});
+      fill += take;
+      left -= take;
+      b += (int)take;
+      if (fill >= target) close_group();
+    }
+  }
+  while (!grp.empty() && grp.back().empty()) grp.pop_back();
+  // partial slots: row r, KV head h, piece j -> first[r] + h * nparts[r] + j
+  std::vector<int> first(rows.size(), -1);
+  for (size_t ri = 0; ri < rows.size(); ++ri) {
+    if (nparts[ri] < 2) continue;
+    first[ri] = p->n_slots;
+    for (int h = 0; h < p->hkv; ++h)
+      p->merges.push_back(MergeItem{rows[ri].q, h, p->n_slots + h * nparts[ri], nparts[ri]});
+    p->n_slots += p->hkv * nparts[ri];
+  }
+  p->items.clear();
+  p->wg_first.assign(1, 0);
+  for (const auto& g : grp)
+    for (int h = 0; h < p->hkv; ++h) {
+      for (const Piece& pc : g) {
+        const Row& r = rows[pc.row];
+        const int slot = first[pc.row] < 0 ? -1 : first[pc.row] + h * nparts[pc.row] + pc.part;
+        p->items.push_back(WorkItem{pa::kDecode, h, r.s, r.q, 1, pc.b, pc.e, slot});
+      }
+      p->wg_first.push_back((int32_t)p->items.size());
+    }
+  p->n_decode = (int32_t)p->items.size();
+  p->n_prefill = 0;
 }
 
 void build_work(pa_plan* p) {
@@ -236,6 +343,11 @@ void build_work(pa_plan* p) {
   const int G = p->group();
   bool has_prefill = false;
   for (int s = 0; s < p->S && !p->mla; ++s) has_prefill |= (p->cu_q[s + 1] - p->cu_q[s]) > kDecodeMaxQueries;
+  if (!has_prefill && p->split_tokens == 0 && p->max_splits > 1 && p->n_cu > 0) {
+    const int per_cu = p->mla ? pa::mla_wgs_per_cu() : pa::decode_wgs_per_cu(G);
+    plan_balanced(p, std::max(1, p->n_cu * per_cu), p->mla ? kMlaMinPieceKeys : kMinPieceKeys);
+    return;
+  }
   const int split_tokens =
       p->split_tokens > 0 ? std::max(kSplitAlign, (p->split_tokens + kSplitAlign - 1) / kSplitAlign * kSplitAlign)
                           : (p->mla ? kDefaultMlaSplitTokens : (has_prefill ? kMixedSplitTokens : kDefaultSplitTokens));
@@ -356,14 +468,21 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   }
   p->Q = p->cu_q.back();
   if (p->Q > 0) p->q_pos.assign(desc->q_pos, desc->q_pos + p->Q);
+  hipError_t e = hipGetDevice(&p->device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&p->n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "device query");
+  }
   build_work(p);
 
-  // one blob: block table | q_pos | seq_lens | items | merges
+  // one blob: block table | q_pos | seq_lens | items | workgroup ranges | merges
   size_t off_bt = 0;
   size_t off_qpos = align_up(off_bt + p->bt.size() * 4, kAlign);
   size_t off_lens = align_up(off_qpos + p->q_pos.size() * 4, kAlign);
   size_t off_items = align_up(off_lens + p->seq_lens.size() * 4, kAlign);
-  size_t off_merges = align_up(off_items + p->items.size() * sizeof(WorkItem), kAlign);
+  size_t off_wg = align_up(off_items + p->items.size() * sizeof(WorkItem), kAlign);
+  size_t off_merges = align_up(off_wg + p->wg_first.size() * 4, kAlign);
   size_t total = align_up(off_merges + p->merges.size() * sizeof(MergeItem), kAlign);
   total = std::max(total, kAlign);
   p->blob.assign(total, 0);
@@ -371,14 +490,10 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   if (!p->q_pos.empty()) memcpy(p->blob.data() + off_qpos, p->q_pos.data(), p->q_pos.size() * 4);
   if (!p->seq_lens.empty()) memcpy(p->blob.data() + off_lens, p->seq_lens.data(), p->seq_lens.size() * 4);
   if (!p->items.empty()) memcpy(p->blob.data() + off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+  memcpy(p->blob.data() + off_wg, p->wg_first.data(), p->wg_first.size() * 4);
   if (!p->merges.empty())
     memcpy(p->blob.data() + off_merges, p->merges.data(), p->merges.size() * sizeof(MergeItem));
 
-  hipError_t e = hipGetDevice(&p->device);
-  if (e != hipSuccess) {
-    delete p;
-    return hip_fail(e, "hipGetDevice");
-  }
   e = hipMalloc(reinterpret_cast<void**>(&p->dev), total);
   if (e != hipSuccess) {
     delete p;
@@ -399,6 +514,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   p->d_qpos = reinterpret_cast<const int32_t*>(p->dev + off_qpos);
   p->d_lens = reinterpret_cast<const int32_t*>(p->dev + off_lens);
   p->d_items = reinterpret_cast<const WorkItem*>(p->dev + off_items);
+  p->d_wg_first = reinterpret_cast<const int32_t*>(p->dev + off_wg);
   p->d_merges = reinterpret_cast<const MergeItem*>(p->dev + off_merges);
   *out_plan = p;
   return ok();
@@ -528,6 +644,8 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   a.seq_lens = plan->d_lens;
   a.items = plan->d_items;
   a.n_items = (int32_t)plan->items.size();
+  a.wg_first = plan->d_wg_first;
+  a.n_wg = (int32_t)plan->wg_first.size() - 1;
   a.table_width = plan->W;
   a.page_shift = plan->page_shift;
   a.hq = plan->hq;
@@ -588,6 +706,8 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   a.seq_lens = plan->d_lens;
   a.items = plan->d_items;
   a.n_items = (int32_t)plan->items.size();
+  a.wg_first = plan->d_wg_first;
+  a.n_wg = (int32_t)plan->wg_first.size() - 1;
   a.table_width = plan->W;
   a.page_shift = plan->page_shift;
   a.hq = plan->hq;

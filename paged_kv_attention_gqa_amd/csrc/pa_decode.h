@@ -73,8 +73,12 @@ __device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& 
 // Decode body.  NW waves share one item: wave w takes key blocks w, w+NW, ...
 // and the waves' statistics are combined through LDS at the end.
 // smem must hold NW * G * (D + 3) floats.
+// tid: the thread index (threadIdx.x); callers that run several items in a
+// loop pass a copy the compiler cannot see through, so that per-lane values
+// are recomputed per item instead of being kept live across the loop.
 template <typename T, int D, int G, int NW, int U>
-__device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem& it, float* smem) {
+__device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem& it, float* smem,
+                                            int tid = threadIdx.x) {
   constexpr int EPV = Vec16<T>::kElems;  // elements per 16-byte chunk
   constexpr int LPT = D / EPV;           // lanes per key row
   constexpr int TPW = kWave / LPT;       // keys per wave-wide load
@@ -83,8 +87,8 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   static_assert(U % 2 == 0, "keys are processed in pairs");
   static_assert(NW > 1, "waves combine through LDS");
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int r = lane / LPT;
   const int c = lane % LPT;
   const int qi = it.q_begin;
@@ -278,7 +282,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   __syncthreads();
 
   // thread x finalises outputs (g, d) = x, x + blockDim, ...
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+  for (int idx = tid; idx < G * D; idx += NW * kWave) {
     const int g = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll

@@ -51,6 +51,8 @@ struct KernelArgs {
   const int32_t* seq_lens;     // [S]
   const WorkItem* items;
   int32_t n_items;
+  const int32_t* wg_first;  // workgroup b runs items wg_first[b] .. wg_first[b + 1] - 1
+  int32_t n_wg;             // workgroups of the main launch
   int32_t table_width;
   int32_t page_shift;     // log2(page_size)
   int32_t hq, hkv;

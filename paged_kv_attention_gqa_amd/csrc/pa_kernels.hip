@@ -30,9 +30,15 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecodeWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kDecode)))
 void decode_kernel(KernelArgs a) {
   __shared__ float smem[kDecodeWaves * G * (D + 3)];
-  const WorkItem it = a.items[blockIdx.x];
-  if (it.kind == kEmpty) return;
-  decode_item<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, smem);
+  const int first = a.wg_first[blockIdx.x], last = a.wg_first[blockIdx.x + 1];
+  int tid = threadIdx.x;
+  for (int i = first; i < last; ++i) {
+    const WorkItem it = a.items[i];
+    if (it.kind == kEmpty) continue;
+    if (i > first) __syncthreads();  // the previous item's waves are done with the LDS
+    asm volatile("" : "+v"(tid));    // per-lane values are recomputed per item, not kept live
+    decode_item<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, smem, tid);
+  }
 }
 
 
@@ -50,6 +56,7 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(kPrefillWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kMixed)))
 void mixed_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[MixedShape<T, D, G>::kBytes];
+  // plans with prefill tiles run one item per workgroup (wg_first[b] = b)
   const WorkItem it = a.items[blockIdx.x];
   if (it.kind == kEmpty) return;
   if (it.kind == kPrefill) {
@@ -67,9 +74,15 @@ void mixed_kernel(KernelArgs a) {
 template <typename T>
 __global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_eu(2))) void mla_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[MlaSmem::kBytes];
-  const WorkItem it = a.items[blockIdx.x];
-  if (it.kind == kEmpty) return;
-  mla_item<T>(a, it, smem);
+  const int first = a.wg_first[blockIdx.x], last = a.wg_first[blockIdx.x + 1];
+  int tid = threadIdx.x;
+  for (int i = first; i < last; ++i) {
+    const WorkItem it = a.items[i];
+    if (it.kind == kEmpty) continue;
+    if (i > first) __syncthreads();  // the previous item's waves are done with the LDS ring
+    asm volatile("" : "+v"(tid));    // per-lane values are recomputed per item, not kept live
+    mla_item<T>(a, it, smem, tid);
+  }
 }
 
 // grid: (split rows, chunks of 256 outputs per row)
@@ -85,10 +98,10 @@ namespace {
 using LaunchFn = hipError_t (*)(const KernelArgs&, int, const MergeItem*, int, hipStream_t);
 
 template <typename T, int D, int G>
-hipError_t launch_decode_t(const KernelArgs& a, int n_items, const MergeItem* merges, int n_merges,
+hipError_t launch_decode_t(const KernelArgs& a, int n_wg, const MergeItem* merges, int n_merges,
                            hipStream_t stream) {
-  if (n_items > 0) {
-    hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(n_items), dim3(kDecodeWaves * kWave), 0, stream, a);
+  if (n_wg > 0) {
+    hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(n_wg), dim3(kDecodeWaves * kWave), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -97,9 +110,9 @@ hipError_t launch_decode_t(const KernelArgs& a, int n_items, const MergeItem* me
 
 
 template <typename T, int D, int G>
-hipError_t launch_mixed_t(const KernelArgs& a, int n_items, const MergeItem*, int, hipStream_t stream) {
-  if (n_items > 0) {
-    hipLaunchKernelGGL((mixed_kernel<T, D, G>), dim3(n_items), dim3(kPrefillWaves * kWave), 0, stream, a);
+hipError_t launch_mixed_t(const KernelArgs& a, int n_wg, const MergeItem*, int, hipStream_t stream) {
+  if (n_wg > 0) {
+    hipLaunchKernelGGL((mixed_kernel<T, D, G>), dim3(n_wg), dim3(kPrefillWaves * kWave), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -166,7 +179,7 @@ bool prefill_supported(int dtype, int d, int g) { return pick<MixedSel>(dtype, d
 
 hipError_t launch_gqa_main(int dtype, int d, int g, bool has_prefill, const KernelArgs& a, hipStream_t stream) {
   LaunchFn f = has_prefill ? pick<MixedSel>(dtype, d, g) : pick<DecodeSel>(dtype, d, g);
-  return f ? f(a, a.n_items, nullptr, 0, stream) : hipErrorInvalidValue;
+  return f ? f(a, a.n_wg, nullptr, 0, stream) : hipErrorInvalidValue;
 }
 
 hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,
@@ -175,14 +188,28 @@ hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const 
   return f ? f(a, 0, merges, n_merges, stream) : hipErrorInvalidValue;
 }
 
+int decode_wgs_per_cu(int g) {
+  switch (g) {
+    case 1: return Occupancy<1>::kDecode;
+    case 2: return Occupancy<2>::kDecode;
+    case 4: return Occupancy<4>::kDecode;
+    case 8: return Occupancy<8>::kDecode;
+    case 16: return Occupancy<16>::kDecode;
+    default: return 1;
+  }
+}
+
+// two 4-wave workgroups per CU (72 KB of LDS each, waves_per_eu(2))
+int mla_wgs_per_cu() { return 2; }
+
 bool mla_supported(int dtype, int h, int r, int p) {
   return dtype == 1 && h == kMlaHeads && r == kMlaRank && p == kMlaRope;
 }
 
 hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream) {
   if (dtype != 1) return hipErrorInvalidValue;
-  if (a.n_items > 0) {
-    hipLaunchKernelGGL((mla_kernel<uint16_t>), dim3(a.n_items), dim3(kMlaWaves * kWave), 0, stream, a);
+  if (a.n_wg > 0) {
+    hipLaunchKernelGGL((mla_kernel<uint16_t>), dim3(a.n_wg), dim3(kMlaWaves * kWave), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;

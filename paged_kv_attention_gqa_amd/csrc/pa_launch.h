@@ -18,6 +18,11 @@ hipError_t launch_gqa_main(int dtype, int d, int g, bool has_prefill, const Kern
 hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream);
 
+// Workgroups of the decode-only (group size g) and MLA kernels that one CU
+// holds at once; the planner balances decode work over CUs x this many.
+int decode_wgs_per_cu(int g);
+int mla_wgs_per_cu();
+
 // Absorbed MLA: h query heads, latent rank r, position width p.
 bool mla_supported(int dtype, int h, int r, int p);
 hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream);

@@ -61,8 +61,9 @@ __device__ __forceinline__ int mla_off(int key, int piece) {
   return key * (WIDTH * 2) + ((piece ^ swz<WIDTH / 8>(key)) << 4);
 }
 
+// tid: the thread index, as for decode_item.
 template <typename T>
-__device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it, char* smem) {
+__device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it, char* smem, int tid = threadIdx.x) {
   constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = kMlaTileKeys;
   constexpr int KS_LAT = R / 32, KS_POS = P / 32;  // 16x16x32 k-steps
   constexpr int DW = R / kMlaWaves;                 // output dims per wave
@@ -70,10 +71,10 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   constexpr int ROWS_PER_WAVE = NT / kMlaWaves;     // latent rows each wave loads per tile
   constexpr int LOADS_PER_TILE = ROWS_PER_WAVE + 1; // + a quarter of the rotary tile
   static_assert(NT % kMlaWaves == 0 && DW % 16 == 0, "tile must split over the waves");
-  const int lane = threadIdx.x & 63;
+  const int lane = tid & 63;
   // wave-uniform (readfirstlane): keeps the tile schedule and its block-table
   // lookups in scalar registers and scalar loads
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, c = lane >> 4;           // MFMA column (head / key row) and k-group
   const int qi = it.q_begin;
   const int tb = it.tok_begin, te = it.tok_end;
