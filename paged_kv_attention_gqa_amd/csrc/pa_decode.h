@@ -45,6 +45,12 @@ __device__ __forceinline__ void store_out(void* out, uint64_t idx, float v) {
   }
 }
 
+// Raw buffer resource over `base` for 16-byte loads at byte offsets below
+// 2^31 (stride 0, 32-bit data format; offsets past the range read zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
 // Scores of G heads against one key chunk held by this lane.
 template <typename T, int G>
 __device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& kv, float (&s)[G]) {
@@ -198,41 +204,74 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
     }
   };
 
-  // Blocks start on multiples of BLK.  When a page holds whole blocks, a
-  // block's page number is one wave-uniform scalar load and the next block's
-  // keys stream in while this one is computed; smaller pages look pages up
-  // per lane.
+  // Blocks start on multiples of BLK; wave w takes blocks B0 + k * step,
+  // B0 = tstart + w * BLK.  When a page holds whole blocks:
+  //  - the page numbers of 64 consecutive blocks of the wave are one vector
+  //    load, lane k holding block k's (v_readlane hands them out);
+  //  - a full block (every key < te) loads from one scalar base per block
+  //    plus fixed per-lane offsets, and the next full block is always loaded
+  //    before the current one is computed (the last one reloads itself), so
+  //    every compute follows the same number of newer loads and the
+  //    compiler's wait counts keep one block in flight;
+  //  - the wave's last block, if it reaches past te, loads clamped keys
+  //    (every load inside the sequence's referenced pages) on its own path.
+  // Smaller pages look pages up per lane.
   const int tstart = tb & ~(BLK - 1);
   const int step = NW * BLK;
   if (ps >= BLK) {
-    int B = tstart + wave * BLK;
-    if (B < te) {
-      auto load_block = [&](int blk, int page, uint4 (&kr)[U], uint4 (&vr)[U]) {
+    const int B0 = tstart + wave * BLK;
+    const int nb = B0 < te ? (te - 1 - B0) / step + 1 : 0;           // blocks with B < te
+    const int nfull = B0 + BLK <= te ? (te - BLK - B0) / step + 1 : 0;  // blocks with B + BLK <= te
+    const uint32_t rs2 = (uint32_t)(row_stride * sizeof(T));  // bytes between consecutive slots
+    const char* kbase = reinterpret_cast<const char*>(a.k) + (uint64_t)kvh * D * sizeof(T);
+    const char* vbase = reinterpret_cast<const char*>(a.v) + (uint64_t)kvh * D * sizeof(T);
+    uint32_t lane_off[U];  // byte offset of this lane's chunk of key u, from the block's first slot
+#pragma unroll
+    for (int u = 0; u < U; ++u) lane_off[u] = (uint32_t)(key_of(0, u) * rs2 + c * 16);
+    const int last_page = (te - 1) >> a.page_shift;
+    for (int w0 = 0; w0 < nb; w0 += kWave) {
+      const int pv = bt[min((B0 + (w0 + lane) * step) >> a.page_shift, last_page)];
+      // buffer loads: the page base in a scalar resource, the slot row as a
+      // scalar offset, this lane's chunk as a fixed vector offset (no per-load
+      // address arithmetic, no address registers next to in-flight loads)
+      auto load_full = [&](int k, uint4 (&kr)[U], uint4 (&vr)[U]) {
+        const int B = B0 + k * step;
+        const uint64_t pg = (uint64_t)__builtin_amdgcn_readlane(pv, k - w0) * ps * rs2;
+        const uint32_t soff = (uint32_t)(B & (ps - 1)) * rs2;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + pg), rv = make_rsrc(vbase + pg);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const uint64_t off = slot_offset(page, min(max(key_of(blk, u), tb), te - 1));
+          kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off[u], soff, 0));
+          vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off[u], soff, 0));
+        }
+      };
+      const int kend = min(nfull, w0 + kWave);  // full blocks of this window: w0 .. kend - 1
+      if (w0 < kend) {
+        uint4 ka[U], va[U], kb[U], vb[U];
+        load_full(w0, ka, va);
+        int k = w0;
+        while (true) {
+          load_full(min(k + 1, kend - 1), kb, vb);
+          __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the block they overlap
+          compute_block(B0 + k * step, ka, va);
+          if (++k >= kend) break;
+          load_full(min(k + 1, kend - 1), ka, va);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_block(B0 + k * step, kb, vb);
+          if (++k >= kend) break;
+        }
+      }
+      if (nfull < nb && nfull < w0 + kWave) {  // the wave's partial last block (k = nfull) is in this window
+        const int B = B0 + nfull * step;
+        const int page = __builtin_amdgcn_readlane(pv, nfull - w0);  // B and te - 1 share this page
+        uint4 kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint64_t off = slot_offset(page, min(key_of(B, u), te - 1));
           kr[u] = load16(a.k, off, sizeof(T));
           vr[u] = load16(a.v, off, sizeof(T));
         }
-      };
-      uint4 ka[U], va[U], kb[U], vb[U];
-      load_block(B, load_uniform(bt, B >> a.page_shift), ka, va);
-      int pg_next = B + step < te ? load_uniform(bt, (B + step) >> a.page_shift) : 0;
-      while (true) {
-        if (B + step < te) {
-          load_block(B + step, pg_next, kb, vb);
-          pg_next = B + 2 * step < te ? load_uniform(bt, (B + 2 * step) >> a.page_shift) : 0;
-        }
-        compute_block(B, ka, va);
-        B += step;
-        if (B >= te) break;
-        if (B + step < te) {
-          load_block(B + step, pg_next, ka, va);
-          pg_next = B + 2 * step < te ? load_uniform(bt, (B + 2 * step) >> a.page_shift) : 0;
-        }
-        compute_block(B, kb, vb);
-        B += step;
-        if (B >= te) break;
+        compute_block(B, kr, vr);
       }
     }
   } else {
