@@ -113,7 +113,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       const int row = ROWS_PER_WAVE * wave + r;
       const int t = clamp_key(t0 + row);
       const uint16_t* src = lat + ((uint64_t)pg[r] * ps + (t & (ps - 1))) * R + ((lane ^ swz<R / 8>(row)) * 8);
-      load_to_lds(src, stage + row * (R * 2));
+      load_to_lds_stream(src, stage + row * (R * 2));
     }
     if (lane < 32) {
       const int rl = lane >> 3;  // 0..3
@@ -123,7 +123,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       const int row = ROWS_PER_WAVE * wave + rl;
       const int t = clamp_key(t0 + row);
       const uint16_t* src = kpos + ((uint64_t)page * ps + (t & (ps - 1))) * P + (((lane & 7) ^ swz<P / 8>(row)) * 8);
-      load_to_lds(src, stage + MlaSmem::kLatTile + wave * 512);
+      load_to_lds_stream(src, stage + MlaSmem::kLatTile + wave * 512);
     }
   };
 

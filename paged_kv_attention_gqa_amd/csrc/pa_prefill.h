@@ -66,6 +66,13 @@ __device__ __forceinline__ void load_to_lds(const void* src, char* lds_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds_base);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
 }
+// The same with the non-temporal hint, for data read once (MLA latent and
+// rotary rows); prefill tiles are shared by the query tiles of a sequence
+// through L2 and keep the default policy (nt measured 1-6% slower there).
+__device__ __forceinline__ void load_to_lds_stream(const void* src, char* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(lds) : "m0");
+}
 // The same load from (wave-uniform base) + 32-bit per-lane byte offset
 // (global_load_lds_dwordx4 with a scalar base address).
 __device__ __forceinline__ void load_to_lds_sv(const char* base, uint32_t off, char* lds_base) {
