@@ -39,6 +39,8 @@ __device__ __forceinline__ uint4 load16(const void* base, uint64_t elem_off, int
 // K/V rows a decode item reads once: non-temporal ("nt") loads.  Measured on
 // MI355X: streaming reads reach ~7.0 TB/s with nt against ~6.2 TB/s without,
 // and the decode kernel gained 11%.
+constexpr float kDecodeLazyLog2 = 8.f;  // weights may reach 2^8 before the reference max moves
+
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load16_stream(const void* base, uint64_t elem_off, int esize) {
   return __builtin_bit_cast(
@@ -160,21 +162,37 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 #pragma unroll
       for (int g = 0; g < G; ++g) s[u][g] = valid[u] ? s[u][g] : -INFINITY;
 
-    // online softmax per row and head, one rescale per block
+    // Online softmax per row and head against a lazily raised reference max:
+    // the reference moves (and the sums are rescaled) only when a block's max
+    // exceeds it by more than 2^kDecodeLazyLog2 in weight, which after the
+    // first blocks is rare; weights stay <= 2^kDecodeLazyLog2.  Numerator and
+    // denominators share the reference, so the result does not depend on it.
+    float mx[G];
+    bool raise = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mx = m[g];
+      mx[g] = s[0][g];
 #pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][g]);
-      const float mu = (mx == -INFINITY) ? 0.f : mx;
-      const float alpha = fast_exp2((m[g] - mu) * a.scale_log2);
-      m[g] = mx;
-      l[g] *= alpha;
-      lx[g] *= alpha;
+      for (int u = 1; u < U; ++u) mx[g] = fmaxf(mx[g], s[u][g]);
+      raise |= mx[g] * a.scale_log2 > m[g] * a.scale_log2 + kDecodeLazyLog2;
+    }
+    if (__any(raise)) {
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) o[g][e] *= alpha;
+      for (int g = 0; g < G; ++g) {
+        const float mn = fmaxf(m[g], mx[g]);
+        const float alpha = fast_exp2((m[g] - (mn == -INFINITY ? 0.f : mn)) * a.scale_log2);
+        m[g] = mn;
+        l[g] *= alpha;
+        lx[g] *= alpha;
 #pragma unroll
-      for (int u = 0; u < U; ++u) s[u][g] = fast_exp2((s[u][g] - mu) * a.scale_log2);
+        for (int e = 0; e < EPV; ++e) o[g][e] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sub = (m[g] == -INFINITY ? 0.f : m[g]) * a.scale_log2;
+#pragma unroll
+      for (int u = 0; u < U; ++u) s[u][g] = fast_exp2(__builtin_fmaf(s[u][g], a.scale_log2, -sub));
     }
 
     // P.V
