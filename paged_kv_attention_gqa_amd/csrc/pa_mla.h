@@ -102,12 +102,17 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   auto clamp_key = [&](int t) { return min(max(t, tb), te - 1); };
   // This wave's share of a tile: latent rows ROWS_PER_WAVE * wave + r (one
   // 1 KB load each) and rotary rows 4 wave .. 4 wave + 3 (half a load: lanes
-  // 0..31, 8 lanes of 16 bytes per 128-byte row).
-  auto issue_tile = [&](int t0, char* stage) {
-    int pg[ROWS_PER_WAVE];  // wave-uniform: scalar loads
+  // 0..31, 8 lanes of 16 bytes per 128-byte row).  With pages of >= 16 keys
+  // the 16 keys of a tile (clamped ones included) share one page, whose
+  // number is a scalar load issued a tile ahead; smaller pages look each row
+  // up.
+  const bool uniform = ps >= NT;
+  auto tile_page = [&](int t0) { return uniform ? load_uniform(bt, clamp_key(t0) >> a.page_shift) : 0; };
+  auto issue_tile = [&](int t0, char* stage, int tpage) {
+    int pg[ROWS_PER_WAVE];
 #pragma unroll
     for (int r = 0; r < ROWS_PER_WAVE; ++r)
-      pg[r] = load_uniform(bt, clamp_key(t0 + ROWS_PER_WAVE * wave + r) >> a.page_shift);
+      pg[r] = uniform ? tpage : load_uniform(bt, clamp_key(t0 + ROWS_PER_WAVE * wave + r) >> a.page_shift);
 #pragma unroll
     for (int r = 0; r < ROWS_PER_WAVE; ++r) {
       const int row = ROWS_PER_WAVE * wave + r;
@@ -130,9 +135,14 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   // tiles start on multiples of 16 keys; keys outside [tb, te) are masked
   const int first = tb & ~(NT - 1);
   const int ntiles = (te - first + NT - 1) / NT;
+  int page_next = 0;
 #pragma unroll
   for (int j = 0; j < kMlaStages - 1; ++j)
-    if (j < ntiles) issue_tile(first + j * NT, smem + j * MlaSmem::kStage);
+    if (j < ntiles) {
+      page_next = tile_page(first + j * NT);
+      issue_tile(first + j * NT, smem + j * MlaSmem::kStage, page_next);
+    }
+  page_next = tile_page(first + (kMlaStages - 1) * NT);
   for (int j = 0; j < ntiles; ++j) {
     // tiles j+1 .. j+2 may stay in flight; this wave's share of tile j has landed
     const int ahead = min(ntiles - 1 - j, kMlaStages - 2);
@@ -143,46 +153,53 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
     else
       wait_vmcnt<0>();
     __syncthreads();  // ... every wave's share has; tile j-1's stage is free for reuse
-    if (j + kMlaStages - 1 < ntiles)
-      issue_tile(first + (j + kMlaStages - 1) * NT, smem + ((j + kMlaStages - 1) % kMlaStages) * MlaSmem::kStage);
+    if (j + kMlaStages - 1 < ntiles) {
+      issue_tile(first + (j + kMlaStages - 1) * NT, smem + ((j + kMlaStages - 1) % kMlaStages) * MlaSmem::kStage,
+                 page_next);
+      page_next = tile_page(first + (j + kMlaStages) * NT);
+    }
     const int t0 = first + j * NT;
     const char* ls = smem + (j % kMlaStages) * MlaSmem::kStage;
     const char* kps = ls + MlaSmem::kLatTile;
 
-    // S^T: lane (n, c) holds keys 4 c + r (r = 0..3) of head n
+    // S^T: lane (n, c) holds keys 4 c + r (r = 0..3) of head n; two
+    // accumulator chains halve the dependent MFMA latency
     bf16x8_t kf[KS_LAT + KS_POS];
 #pragma unroll
     for (int k = 0; k < KS_LAT; ++k) kf[k] = *reinterpret_cast<const bf16x8_t*>(ls + mla_off<R>(n, 4 * k + c));
 #pragma unroll
     for (int k = 0; k < KS_POS; ++k)
       kf[KS_LAT + k] = *reinterpret_cast<const bf16x8_t*>(kps + mla_off<P>(n, 4 * k + c));
-    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+    floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int k = 0; k < KS_LAT; ++k) s = mfma_16x16x32(kf[k], qa[k], s);
+    for (int k = 0; k < KS_LAT; ++k) sc[k & 1] = mfma_16x16x32(kf[k], qa[k], sc[k & 1]);
 #pragma unroll
-    for (int k = 0; k < KS_POS; ++k) s = mfma_16x16x32(kf[KS_LAT + k], qp[k], s);
+    for (int k = 0; k < KS_POS; ++k) sc[k & 1] = mfma_16x16x32(kf[KS_LAT + k], qp[k], sc[k & 1]);
+    floatx4_t s = sc[0] + sc[1];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 4 * c + r;
       s[r] = (t >= tb && t < te) ? s[r] : -INFINITY;
     }
 
+    // Online softmax against a lazily raised reference max (weights stay
+    // <= 2^kLazyRescaleLog2; the accumulators are rescaled only when a tile
+    // raises some head's max past that).
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mx = fmaxf(mx, m);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    const float alpha = fast_exp2((m - mu) * a.scale_log2);
-    m = mx;
-    l *= alpha;
-    lx *= alpha;
-    if (__any(alpha != 1.f)) {
+    mx = pair32_max(pair16_max(mx));  // over the four k-groups of lanes
+    if (__any(mx * a.scale_log2 > m * a.scale_log2 + kLazyRescaleLog2)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2((m - (mn == -INFINITY ? 0.f : mn)) * a.scale_log2);
+      m = mn;
+      l *= alpha;
+      lx *= alpha;
 #pragma unroll
       for (int b = 0; b < DB; ++b) o[b] *= alpha;
     }
+    const float sub = (m == -INFINITY ? 0.f : m) * a.scale_log2;
     float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2((s[r] - mu) * a.scale_log2);
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -sub));
     const uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);
     l += bf16_lo(w0) + bf16_hi(w0) + bf16_lo(w1) + bf16_hi(w1);
     lx += (p[0] + p[1]) + (p[2] + p[3]);
@@ -203,10 +220,8 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   }
 
   // full row sums: the four k-groups of lanes hold different keys
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  lx += __shfl_xor(lx, 16);
-  lx += __shfl_xor(lx, 32);
+  l = pair32_sum(pair16_sum(l));
+  lx = pair32_sum(pair16_sum(lx));
 
   // O^T lane (n, c) element r is dim DW wave + 16 b + 4 c + r of head n
   if (it.slot < 0) {
