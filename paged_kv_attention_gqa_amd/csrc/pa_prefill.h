@@ -37,6 +37,7 @@ constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillRows = kPrefillWaves * kPrefillRowsPerWave;
 constexpr int kPrefillStages = 4;  // K/V tiles in the LDS ring
+constexpr bool kPrefillPingPong = true;  // two wave groups in opposite phase (see prefill_item_impl)
 constexpr float kLazyRescaleLog2 = 8.f;  // weights may reach 2^8 before the reference max moves
 
 template <int D>
@@ -123,8 +124,10 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   constexpr int LOADS_PER_WAVE = 2 * LOADS_PER_TILE / kPrefillWaves;
   constexpr int KEYS_PER_WAVE = KEYS_PER_LOAD * LOADS_PER_WAVE;
   static_assert(PIECES >= 8 && kWave % PIECES == 0, "head size must be a multiple of 64");
-  static_assert(KEYS_PER_WAVE == 16 && LOADS_PER_TILE == 4 * LOADS_PER_WAVE,
-                "each wave loads 16 consecutive key rows of K (waves 0-3) or V (waves 4-7)");
+  constexpr int MB = NT / 32;                        // 32-key MFMA blocks per tile
+  constexpr int HALF = kPrefillWaves / 2;            // waves loading K (the others load V)
+  static_assert(KEYS_PER_WAVE == 16 && LOADS_PER_TILE == HALF * LOADS_PER_WAVE && NT % 32 == 0,
+                "each wave loads 16 consecutive key rows of K (first half of the waves) or V");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -174,8 +177,8 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // ahead.  Keys past tok_end read the last key instead (every row in LDS is
   // finite sequence data; such keys are masked); keys before tok_begin are
   // sequence keys and are masked as well.
-  const int wq = wave & 3;
-  const bool loads_v = wave >= 4;
+  const int wq = wave % HALF;
+  const bool loads_v = wave >= HALF;
   const uint32_t rs2 = (uint32_t)a.hkv * D * 2;  // bytes between consecutive key rows
   const char* pool_kvh = reinterpret_cast<const char*>(loads_v ? a.v : a.k) + (uint64_t)it.kvh * D * 2;
   // Byte offset of this lane's source for load j: (KEYS_PER_LOAD j + my_key)
@@ -254,15 +257,15 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
       }
   }
   // S^T = K . Q^T : two 32-key blocks; lane (n, h) reads dims 16 k + 8 h of key row n
-  auto scores = [&](const char* ks, floatx16_t (&s)[2]) {
+  auto scores = [&](const char* ks, floatx16_t (&s)[MB]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
     // K fragments run kAhead MFMAs ahead of their use (a small register ring)
-    constexpr int kSteps = 2 * KS, kAhead = 4;
+    constexpr int kSteps = MB * KS, kAhead = 4;
     auto frag = [&](int i) {
-      return *reinterpret_cast<const bf16x8_t*>(ks + koff[i >> 1] + (i & 1) * 32 * (D * 2));
+      return *reinterpret_cast<const bf16x8_t*>(ks + koff[i / MB] + (i % MB) * 32 * (D * 2));
     };
     bf16x8_t ring[kAhead];
 #pragma unroll
@@ -272,7 +275,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     for (int i = 0; i < kSteps; ++i) {
       const bf16x8_t kf = ring[i % kAhead];
       if (i + kAhead < kSteps) ring[i % kAhead] = frag(i + kAhead);
-      s[i & 1] = mfma_32x32x16(kf, qf[i >> 1], s[i & 1]);
+      s[i % MB] = mfma_32x32x16(kf, qf[i / MB], s[i % MB]);
       __builtin_amdgcn_sched_barrier(0);  // keep the read distance (the scheduler would shorten it)
     }
   };
@@ -282,13 +285,13 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // stay <= 2^kLazyRescaleLog2 and the accumulators are rescaled only on the
   // few tiles that raise some row's max that far.  Numerator and denominator
   // share the reference, so the result does not depend on when it moves.
-  auto row_max = [&](int t0, floatx16_t (&s)[2]) {
+  auto row_max = [&](int t0, floatx16_t (&s)[MB]) {
     const bool full = t0 >= tb && t0 + NT <= te && (!a.causal || t0 + NT - 1 <= pmin) &&
                       (a.window == 0 || t0 > pmax - a.window);
     // accumulator element e of block mb holds key t0 + 32 mb + 8 (e/4) + 4 h + e%4
     if (!full) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int t = t0 + 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -299,7 +302,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     }
     float mx = s[0][0];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
     mx = pair32_max(mx);  // both lane halves hold the same row
@@ -320,7 +323,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // e%4 (e = 0..7): elements 8 (kk % 2) + e of S^T block kk / 2, and the V^T
   // rows of the same keys by two transposed reads (4 keys each) of dims 32 b
   // + 16 (lane/16 % 2) + lane % 16 (offsets voff, plus 16 rows per k-step).
-  auto weights_pv = [&](const char* vs, const floatx16_t (&s)[2], float sub) {
+  auto weights_pv = [&](const char* vs, const floatx16_t (&s)[MB], float sub) {
 #pragma unroll
     for (int kk = 0; kk < NT / 16; ++kk) {
       const int mb = kk >> 1, e0 = 8 * (kk & 1);
@@ -359,7 +362,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // tile ahead of the loads that use them.
   const int t_first = tb & ~(NT - 1);
   const int ntiles = (te - t_first + NT - 1) / NT;
-  const bool lead = wave < kPrefillWaves / 2;
+  const bool lead = !kPrefillPingPong || wave < kPrefillWaves / 2;
   int page_next = 0;
 #pragma unroll
   for (int j = 0; j < NS - 2; ++j) {
@@ -373,7 +376,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // One loop body for both groups: weights of tile j - 1, then scores of
   // tile j; only the barrier (and the loads issued after it) sits before the
   // weights in the trailing waves and after them in the leading ones.
-  floatx16_t s[2];
+  floatx16_t s[MB];
   float sub = 0.f;
   auto sync = [&](int j) {
     wait_tiles(min(ntiles - 1 - j, 1));  // tile j has landed, j + 1 may be in flight

@@ -107,3 +107,23 @@ def test_constant_values_give_that_constant():
     run()
     out, _ = run.result()
     assert np.abs(out - 0.625).max() <= 2e-2 + 1e-2 * 0.625
+
+
+@pytest.mark.parametrize("max_splits,page_size", [(1, 16), (1, 64), (16, 16)])
+def test_long_rows_span_several_page_windows(max_splits, page_size):
+    """Rows of ~20k keys: unsplit, each wave of the workgroup walks > 64
+    blocks (several windows of preloaded page numbers) and ends on a partial
+    block; split, the pieces start and end inside pages."""
+    b = random_batch(41, dtype="bf16", hq=8, hkv=2, d=128, page_size=page_size, q_counts=(1, 1, 1),
+                     histories=[20000, 16385, 4095], max_splits=max_splits)
+    run = _parity(b)
+    if max_splits == 1:
+        assert run.info["split_rows"] == 0
+
+
+def test_windowed_long_row_starts_mid_page():
+    """A sliding window makes each row start at an arbitrary key: the first
+    block of every piece straddles the window start."""
+    b = random_batch(42, dtype="bf16", hq=16, hkv=4, d=128, page_size=16, q_counts=(1, 2),
+                     histories=[12345, 9999], window=7001)
+    _parity(b)
