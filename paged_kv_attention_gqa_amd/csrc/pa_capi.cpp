@@ -55,6 +55,11 @@ constexpr int kSplitAlign = 64;
 // the keys it reads.
 constexpr int kMinPieceKeys = 128;
 constexpr int kMlaMinPieceKeys = 256;
+// Waves that share one KV head of a balanced decode item.  Fewer waves per
+// head (more heads per workgroup) means shorter pieces for the same number
+// of workgroups, so more splits per row; four keeps the piece count of a
+// one-head workgroup of four waves.
+constexpr int kDecodeWavesPerHead = 4;
 constexpr int kMaxSplitsLimit = 64;
 constexpr size_t kAlign = 256;
 
@@ -75,6 +80,8 @@ struct pa_plan {
   std::vector<int32_t> wg_first;  // workgroup b runs items wg_first[b] .. wg_first[b + 1] - 1
   std::vector<MergeItem> merges;
   int32_t n_decode = 0, n_prefill = 0, n_slots = 0;
+  int32_t heads_shift = 0;        // decode items cover 2^heads_shift consecutive KV heads
+  int32_t n_wg = 0;               // workgroups of the main launch
   int32_t n_cu = 0;               // compute units of the plan's device
   // device copy: one allocation
   std::vector<char> blob;
@@ -148,31 +155,36 @@ int validate_desc(const pa_plan_desc* d) {
   return PA_OK;
 }
 
-// Split one decode query row's visible range into page-friendly key ranges.
-void plan_decode_row(pa_plan* p, int s, int i, int kvh, int split_tokens, std::vector<WorkItem>& out) {
+// Split one decode query row's visible range into page-friendly key ranges,
+// one item per (range, group of 2^heads_shift KV heads), KV heads innermost:
+// the heads of one key range run side by side and together read whole
+// [Hkv, D] slot rows of each page.  Partial slots of a split row are laid out
+// [range][KV head]; an item's slot is its first head's.
+void plan_decode_row(pa_plan* p, int s, int i, int split_tokens, std::vector<WorkItem>& out) {
+  const int hw = 1 << p->heads_shift;
   int lo, hi;
   visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &lo, &hi);
   const int n = hi - lo + 1;
   int nsplit = std::min(p->max_splits, (n + split_tokens - 1) / split_tokens);
   nsplit = std::max(nsplit, 1);
-  if (nsplit == 1) {
-    out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, lo, hi + 1, -1});
-    return;
+  int chunk = n;
+  if (nsplit > 1) {
+    chunk = (n + nsplit - 1) / nsplit;
+    chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    nsplit = (n + chunk - 1) / chunk;
   }
-  int chunk = (n + nsplit - 1) / nsplit;
-  chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
-  nsplit = (n + chunk - 1) / chunk;
   if (nsplit == 1) {
-    out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, lo, hi + 1, -1});
+    for (int kvh = 0; kvh < p->hkv; kvh += hw) out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, lo, hi + 1, -1});
     return;
   }
   const int base = p->n_slots;
   for (int j = 0; j < nsplit; ++j) {
     const int b = lo + j * chunk, e = std::min(hi + 1, b + chunk);
-    out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, b, e, base + j});
+    for (int kvh = 0; kvh < p->hkv; kvh += hw)
+      out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, b, e, base + j * p->hkv + kvh});
   }
-  p->merges.push_back(MergeItem{i, kvh, base, nsplit});
-  p->n_slots += nsplit;
+  for (int kvh = 0; kvh < p->hkv; ++kvh) p->merges.push_back(MergeItem{i, kvh, base + kvh, nsplit, p->hkv});
+  p->n_slots += nsplit * p->hkv;
 }
 
 // Estimated run time of an item, in units of one decode key: a decode item
@@ -243,13 +255,14 @@ void order_items(pa_plan* p, const std::vector<WorkItem>& pre, const std::vector
 
 // Decode rows balanced over the workgroups resident at once (`slots` = CUs x
 // workgroups per CU).  The key range of every query is cut into pieces and
-// the pieces are dealt to groups of Hkv workgroups, one workgroup per KV
-// head, so that every workgroup gets about the same number of keys and the
-// Hkv workgroups of a group (consecutive, so dispatched together) read the
-// same page slots at the same time; the launch has no tail of lone
-// workgroups.  Cuts fall on multiples of kSplitAlign keys; pieces are at
-// least `min_piece` keys (each split piece costs a partial write and a merge
-// read); a row is cut into at most max_splits pieces, earlier pieces growing
+// the pieces are dealt to groups of Hkv / 2^heads_shift workgroups, each
+// workgroup taking 2^heads_shift consecutive KV heads, so that every
+// workgroup gets about the same number of keys and the workgroups of a group
+// (consecutive, so dispatched together) read the same page slots at the same
+// time; the launch has no tail of lone workgroups.  Cuts fall on multiples
+// of kSplitAlign keys; pieces are at least `min_piece` keys (each split piece
+// costs a partial write and a merge read); a row is cut into at most
+// max_splits pieces, earlier pieces growing
 // when the rest of the row would not fit the remaining pieces at about one
 // target each; a row cut into several pieces gets one partial slot per piece
 // and a merge.  The target of each group is recomputed from the keys
@@ -267,7 +280,8 @@ void plan_balanced(pa_plan* p, int slots, int min_piece) {
       rows.push_back(Row{s, i, lo, hi + 1});
       left += hi + 1 - lo;
     }
-  const int groups = std::max(1, slots / p->hkv);
+  const int hw = 1 << p->heads_shift;
+  const int groups = std::max(1, slots / (p->hkv / hw));
   auto align_up = [](int64_t x) { return (x + kSplitAlign - 1) / kSplitAlign * kSplitAlign; };
   auto align_down = [](int64_t x) { return x / kSplitAlign * kSplitAlign; };
   struct Piece {
@@ -314,22 +328,22 @@ void plan_balanced(pa_plan* p, int slots, int min_piece) {
     }
   }
   while (!grp.empty() && grp.back().empty()) grp.pop_back();
-  // partial slots: row r, KV head h, piece j -> first[r] + h * nparts[r] + j
+  // partial slots: row r, piece j, KV head h -> first[r] + j * Hkv + h
   std::vector<int> first(rows.size(), -1);
   for (size_t ri = 0; ri < rows.size(); ++ri) {
     if (nparts[ri] < 2) continue;
     first[ri] = p->n_slots;
     for (int h = 0; h < p->hkv; ++h)
-      p->merges.push_back(MergeItem{rows[ri].q, h, p->n_slots + h * nparts[ri], nparts[ri]});
+      p->merges.push_back(MergeItem{rows[ri].q, h, p->n_slots + h, nparts[ri], p->hkv});
     p->n_slots += p->hkv * nparts[ri];
   }
   p->items.clear();
   p->wg_first.assign(1, 0);
   for (const auto& g : grp)
-    for (int h = 0; h < p->hkv; ++h) {
+    for (int h = 0; h < p->hkv; h += hw) {
       for (const Piece& pc : g) {
         const Row& r = rows[pc.row];
-        const int slot = first[pc.row] < 0 ? -1 : first[pc.row] + h * nparts[pc.row] + pc.part;
+        const int slot = first[pc.row] < 0 ? -1 : first[pc.row] + pc.part * p->hkv + h;
         p->items.push_back(WorkItem{pa::kDecode, h, r.s, r.q, 1, pc.b, pc.e, slot});
       }
       p->wg_first.push_back((int32_t)p->items.size());
@@ -344,8 +358,17 @@ void build_work(pa_plan* p) {
   bool has_prefill = false;
   for (int s = 0; s < p->S && !p->mla; ++s) has_prefill |= (p->cu_q[s + 1] - p->cu_q[s]) > kDecodeMaxQueries;
   if (!has_prefill && p->split_tokens == 0 && p->max_splits > 1 && p->n_cu > 0) {
-    const int per_cu = p->mla ? pa::mla_wgs_per_cu() : pa::decode_wgs_per_cu(G);
-    plan_balanced(p, std::max(1, p->n_cu * per_cu), p->mla ? kMlaMinPieceKeys : kMinPieceKeys);
+    int per_cu = pa::mla_wgs_per_cu();
+    if (!p->mla) {
+      per_cu = pa::decode_wgs_per_cu(G);
+      // heads per item: the largest power of two dividing Hkv that leaves
+      // kDecodeWavesPerHead waves to each head
+      while ((p->hkv % (2 << p->heads_shift)) == 0 &&
+             (2 << p->heads_shift) * kDecodeWavesPerHead <= pa::decode_waves(G))
+        ++p->heads_shift;
+    }
+    plan_balanced(p, p->n_cu * per_cu, p->mla ? kMlaMinPieceKeys : kMinPieceKeys);
+    p->n_wg = (int32_t)p->wg_first.size() - 1;
     return;
   }
   const int split_tokens =
@@ -356,15 +379,7 @@ void build_work(pa_plan* p) {
     const int nq = q1 - q0;
     if (nq == 0) continue;
     if (p->mla || nq <= kDecodeMaxQueries) {
-      for (int i = q0; i < q1; ++i) {
-        // KV heads innermost: the heads of one key range run side by side and
-        // together read whole [Hkv, D] slot rows of each page
-        std::vector<WorkItem> row;
-        for (int kvh = 0; kvh < p->hkv; ++kvh) plan_decode_row(p, s, i, kvh, split_tokens, row);
-        const size_t per = row.size() / p->hkv;
-        for (size_t j = 0; j < per; ++j)
-          for (int kvh = 0; kvh < p->hkv; ++kvh) dec.push_back(row[kvh * per + j]);
-      }
+      for (int i = q0; i < q1; ++i) plan_decode_row(p, s, i, split_tokens, dec);
     } else {
       const int tile_q = std::max(1, kPrefillRows / G);
       for (int kvh = 0; kvh < p->hkv; ++kvh)
@@ -384,6 +399,7 @@ void build_work(pa_plan* p) {
   p->n_prefill = (int32_t)pre.size();
   p->n_decode = (int32_t)dec.size();
   order_items(p, pre, dec);
+  p->n_wg = (int32_t)p->wg_first.size() - 1;
 }
 
 // Workspace: partial sums [slots, G, Dv] | (max, sum, unrounded sum) [slots, G, 3].
@@ -645,7 +661,8 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   a.items = plan->d_items;
   a.n_items = (int32_t)plan->items.size();
   a.wg_first = plan->d_wg_first;
-  a.n_wg = (int32_t)plan->wg_first.size() - 1;
+  a.n_wg = plan->n_wg;
+  a.heads_shift = plan->heads_shift;
   a.table_width = plan->W;
   a.page_shift = plan->page_shift;
   a.hq = plan->hq;
@@ -707,7 +724,8 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   a.items = plan->d_items;
   a.n_items = (int32_t)plan->items.size();
   a.wg_first = plan->d_wg_first;
-  a.n_wg = (int32_t)plan->wg_first.size() - 1;
+  a.n_wg = plan->n_wg;
+  a.heads_shift = plan->heads_shift;
   a.table_width = plan->W;
   a.page_shift = plan->page_shift;
   a.hq = plan->hq;

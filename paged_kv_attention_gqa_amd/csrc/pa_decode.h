@@ -88,15 +88,19 @@ __device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& 
   }
 }
 
-// Decode body.  NW waves share one item: wave w takes key blocks w, w+NW, ...
-// and the waves' statistics are combined through LDS at the end.
+// Decode body.  NW waves share one item of HW = 2^hw_shift KV heads (HW
+// divides NW): wave w works head it.kvh + w % HW and takes that head's key
+// blocks w / HW, w / HW + NW / HW, ...; the statistics of the waves of one
+// head are combined through LDS at the end.  With HW = NW every wave walks the
+// item's whole key range for its own head, and the waves together read whole
+// [Hkv, D] slot rows of each page at the same time.
 // smem must hold NW * G * (D + 3) floats.
 // tid: the thread index (threadIdx.x); callers that run several items in a
 // loop pass a copy the compiler cannot see through, so that per-lane values
 // are recomputed per item instead of being kept live across the loop.
 template <typename T, int D, int G, int NW, int U>
 __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem& it, float* smem,
-                                            int tid = threadIdx.x) {
+                                            int tid = threadIdx.x, int hw_shift = 0) {
   constexpr int EPV = Vec16<T>::kElems;  // elements per 16-byte chunk
   constexpr int LPT = D / EPV;           // lanes per key row
   constexpr int TPW = kWave / LPT;       // keys per wave-wide load
@@ -107,10 +111,13 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hsub = wave & ((1 << hw_shift) - 1);  // this wave's head within the item
+  const int kpart = wave >> hw_shift;              // this wave's share of the head's blocks
+  const int nparts = NW >> hw_shift;               // waves per head
   const int r = lane / LPT;
   const int c = lane % LPT;
   const int qi = it.q_begin;
-  const int kvh = it.kvh;
+  const int kvh = it.kvh + hsub;
   const int tb = it.tok_begin, te = it.tok_end;
   const int ps = 1 << a.page_shift;
   const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
@@ -245,9 +252,9 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   //    (every load inside the sequence's referenced pages) on its own path.
   // Smaller pages look pages up per lane.
   const int tstart = tb & ~(BLK - 1);
-  const int step = NW * BLK;
+  const int step = nparts * BLK;
   if (ps >= BLK) {
-    const int B0 = tstart + wave * BLK;
+    const int B0 = tstart + kpart * BLK;
     const int nb = B0 < te ? (te - 1 - B0) / step + 1 : 0;           // blocks with B < te
     const int nfull = B0 + BLK <= te ? (te - BLK - B0) / step + 1 : 0;  // blocks with B + BLK <= te
     const uint32_t rs2 = (uint32_t)(row_stride * sizeof(T));  // bytes between consecutive slots
@@ -303,7 +310,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
       }
     }
   } else {
-    for (int B = tstart + wave * BLK; B < te; B += step) {
+    for (int B = tstart + kpart * BLK; B < te; B += step) {
       int pg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) pg[u] = bt[min(max(key_of(B, u), tb), te - 1) >> a.page_shift];
@@ -348,31 +355,31 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   }
   __syncthreads();
 
-  // thread x finalises outputs (g, d) = x, x + blockDim, ...
-  for (int idx = tid; idx < G * D; idx += NW * kWave) {
-    const int g = idx / D, d = idx % D;
+  // thread x finalises outputs (head, g, d) = x, x + blockDim, ... of the
+  // item's HW heads, combining the waves w = head + j * HW
+  for (int idx = tid; idx < (G * D << hw_shift); idx += NW * kWave) {
+    const int hs = idx / (G * D), g = idx / D % G, d = idx % D;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sml[(w * G + g) * 3]);
+    for (int w = hs; w < NW; w += 1 << hw_shift) M = fmaxf(M, sml[(w * G + g) * 3]);
     const float mu = (M == -INFINITY) ? 0.f : M;
     float L = 0.f, LX = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = hs; w < NW; w += 1 << hw_shift) {
       const float f = fast_exp2((sml[(w * G + g) * 3] - mu) * a.scale_log2);
       L += sml[(w * G + g) * 3 + 1] * f;
       LX += sml[(w * G + g) * 3 + 2] * f;
       O += so[(w * G + g) * D + d] * f;
     }
-    const int h = kvh * G + g;
+    const int h = (it.kvh + hs) * G + g;
     if (it.slot < 0) {
       store_out<T>(a.out, ((uint64_t)qi * a.hq + h) * D + d, O / L);
       if (a.lse && d == 0) a.lse[(uint64_t)qi * a.hq + h] = M * a.scale + logf(LX);
     } else {
-      a.ws_o[((uint64_t)it.slot * G + g) * D + d] = O;
+      const uint64_t sl = (uint64_t)(it.slot + hs) * G + g;
+      a.ws_o[sl * D + d] = O;
       if (d == 0) {
-        a.ws_ml[((uint64_t)it.slot * G + g) * 3 + 0] = M * a.scale_log2;
-        a.ws_ml[((uint64_t)it.slot * G + g) * 3 + 1] = L;
-        a.ws_ml[((uint64_t)it.slot * G + g) * 3 + 2] = LX;
+        a.ws_ml[sl * 3 + 0] = M * a.scale_log2;
+        a.ws_ml[sl * 3 + 1] = L;
+        a.ws_ml[sl * 3 + 2] = LX;
       }
     }
   }
@@ -397,7 +404,7 @@ __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& 
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
         const int j = j0 + u;
-        const uint64_t sl = (uint64_t)(mi.slot + min(j, mi.nsplit - 1)) * G + g;
+        const uint64_t sl = (uint64_t)(mi.slot + min(j, mi.nsplit - 1) * mi.stride) * G + g;
         mj[u] = a.ws_ml[sl * 3];
         lj[u] = a.ws_ml[sl * 3 + 1];
         lxj[u] = a.ws_ml[sl * 3 + 2];

@@ -13,27 +13,29 @@ namespace pa {
 
 constexpr int kWave = 64;
 
-// One unit of work.  Decode items cover one query, one KV head and one
-// contiguous range of that query's visible keys; prefill items cover up to a
-// tile of consecutive queries of one sequence and one KV head.
+// One unit of work.  Decode items cover one query, 2^KernelArgs::heads_shift
+// consecutive KV heads and one contiguous range of that query's visible keys;
+// prefill items cover up to a tile of consecutive queries of one sequence and
+// one KV head.
 struct WorkItem {
   int32_t kind;       // kDecode / kPrefill / kEmpty
-  int32_t kvh;        // KV head
+  int32_t kvh;        // (first) KV head
   int32_t seq;        // sequence index (row of the block table)
   int32_t q_begin;    // first packed query
   int32_t q_count;    // number of queries (decode: 1)
   int32_t tok_begin;  // first logical key position visited (inclusive)
   int32_t tok_end;    // last logical key position visited (exclusive)
-  int32_t slot;       // decode: split-partial slot, or -1 to write the output directly
+  int32_t slot;       // decode: split-partial slot of the first head (head kvh + i uses slot + i), or -1
+                      // to write the output directly
 };
 constexpr int32_t kDecode = 0;
 constexpr int32_t kPrefill = 1;
 constexpr int32_t kEmpty = 2;  // padding in the dispatch order: the workgroup exits at once
 
-// One split query row to combine: partials slot .. slot + nsplit - 1 hold the
-// per-split statistics of (query q, KV head kvh).
+// One split query row to combine: partials slot + j * stride, j < nsplit,
+// hold the per-split statistics of (query q, KV head kvh).
 struct MergeItem {
-  int32_t q, kvh, slot, nsplit;
+  int32_t q, kvh, slot, nsplit, stride;
 };
 
 struct KernelArgs {
@@ -53,6 +55,7 @@ struct KernelArgs {
   int32_t n_items;
   const int32_t* wg_first;  // workgroup b runs items wg_first[b] .. wg_first[b + 1] - 1
   int32_t n_wg;             // workgroups of the main launch
+  int32_t heads_shift;      // decode items of the decode launch cover 2^heads_shift KV heads
   int32_t table_width;
   int32_t page_shift;     // log2(page_size)
   int32_t hq, hkv;

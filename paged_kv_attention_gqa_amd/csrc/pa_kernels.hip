@@ -7,11 +7,10 @@
 
 namespace pa {
 
-// Decode launch shape: 4 waves share one item; U key loads per lane per block.
-// Small groups (G <= 4) take U = 2 so that a wave fits in 128 VGPRs and four
-// waves share a SIMD (measured 2% faster than U = 4 at three waves); large
-// groups, whose per-key state grows with G, take U = 4 (G = 8) and 2 (G = 16).
-constexpr int kDecodeWaves = 4;
+// U key loads per lane per block.  Small groups (G <= 4) take U = 2 so that
+// a wave fits in 128 VGPRs and four waves share a SIMD (measured 2% faster
+// than U = 4 at three waves); large groups, whose per-key state grows with G,
+// take U = 4 (G = 8) and 2 (G = 16).
 template <int G>
 struct DecodeUnroll {
   static constexpr int kValue = G <= 4 ? 2 : (G <= 8 ? 4 : 2);
@@ -28,10 +27,22 @@ struct Occupancy {
   static constexpr int kMixed = G <= 8 ? 2 : 1;
 };
 
+// Decode launch shape: NW waves share one item.  Eight waves let one item
+// cover up to eight KV heads, one wave each, so that a workgroup reads whole
+// slot rows of every page (measured on MI355X: 6.9 TB/s for whole 32 KB pages
+// against 6.5 TB/s when eight workgroups each read one head's 256-byte
+// chunks).  G = 16 runs one wave per SIMD and so takes four waves.
+template <int G>
+struct DecodeShape {
+  static constexpr int kWaves = G <= 8 ? 8 : 4;
+  static constexpr int kWgsPerCu = Occupancy<G>::kDecode * 4 / kWaves;
+};
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kDecode)))
+__global__ __launch_bounds__(DecodeShape<G>::kWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kDecode)))
 void decode_kernel(KernelArgs a) {
-  __shared__ float smem[kDecodeWaves * G * (D + 3)];
+  constexpr int NW = DecodeShape<G>::kWaves;
+  __shared__ float smem[NW * G * (D + 3)];
   const int first = a.wg_first[blockIdx.x], last = a.wg_first[blockIdx.x + 1];
   int tid = threadIdx.x;
   for (int i = first; i < last; ++i) {
@@ -39,10 +50,9 @@ void decode_kernel(KernelArgs a) {
     if (it.kind == kEmpty) continue;
     if (i > first) __syncthreads();  // the previous item's waves are done with the LDS
     asm volatile("" : "+v"(tid));    // per-lane values are recomputed per item, not kept live
-    decode_item<T, D, G, kDecodeWaves, DecodeUnroll<G>::kValue>(a, it, smem, tid);
+    decode_item<T, D, G, NW, DecodeUnroll<G>::kValue>(a, it, smem, tid, a.heads_shift);
   }
 }
-
 
 // One launch for plans with prefill tiles: decode items and prefill tiles
 // share the grid (packed decode + chunked prefill in one dispatch).
@@ -103,7 +113,7 @@ template <typename T, int D, int G>
 hipError_t launch_decode_t(const KernelArgs& a, int n_wg, const MergeItem* merges, int n_merges,
                            hipStream_t stream) {
   if (n_wg > 0) {
-    hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(n_wg), dim3(kDecodeWaves * kWave), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(n_wg), dim3(DecodeShape<G>::kWaves * kWave), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -192,11 +202,22 @@ hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const 
 
 int decode_wgs_per_cu(int g) {
   switch (g) {
-    case 1: return Occupancy<1>::kDecode;
-    case 2: return Occupancy<2>::kDecode;
-    case 4: return Occupancy<4>::kDecode;
-    case 8: return Occupancy<8>::kDecode;
-    case 16: return Occupancy<16>::kDecode;
+    case 1: return DecodeShape<1>::kWgsPerCu;
+    case 2: return DecodeShape<2>::kWgsPerCu;
+    case 4: return DecodeShape<4>::kWgsPerCu;
+    case 8: return DecodeShape<8>::kWgsPerCu;
+    case 16: return DecodeShape<16>::kWgsPerCu;
+    default: return 1;
+  }
+}
+
+int decode_waves(int g) {
+  switch (g) {
+    case 1: return DecodeShape<1>::kWaves;
+    case 2: return DecodeShape<2>::kWaves;
+    case 4: return DecodeShape<4>::kWaves;
+    case 8: return DecodeShape<8>::kWaves;
+    case 16: return DecodeShape<16>::kWaves;
     default: return 1;
   }
 }

@@ -21,6 +21,9 @@ hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const 
 // Workgroups of the decode-only (group size g) and MLA kernels that one CU
 // holds at once; the planner balances decode work over CUs x this many.
 int decode_wgs_per_cu(int g);
+// Waves of one decode-only workgroup (group size g): an item may cover up to
+// this many KV heads.
+int decode_waves(int g);
 int mla_wgs_per_cu();
 
 // Absorbed MLA: h query heads, latent rank r, position width p.

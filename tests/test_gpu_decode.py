@@ -42,6 +42,10 @@ DECODE_CASES = [
     dict(dtype="f32", hq=2, hkv=1, d=256, page_size=16, q_counts=(2,), max_len=700),
     dict(dtype="bf16", hq=4, hkv=2, d=128, page_size=1, q_counts=(1, 1), max_len=300),
     dict(dtype="bf16", hq=8, hkv=2, d=128, page_size=16, q_counts=(1, 1, 1), histories=[0, 1, 2]),
+    # KV head counts that are not powers of two: items of two heads (Hkv = 6)
+    # and of one head (Hkv = 3)
+    dict(dtype="bf16", hq=12, hkv=6, d=128, page_size=16, q_counts=(1, 1, 1), max_len=2500),
+    dict(dtype="bf16", hq=24, hkv=3, d=64, page_size=32, q_counts=(1, 2), max_len=1800),
 ]
 
 
