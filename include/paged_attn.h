@@ -58,7 +58,7 @@ typedef enum pa_status {
   PA_ERR_OVERLAP = -6,     /* an output overlaps an input or another output */
   PA_ERR_RANGE = -7,       /* a size exceeds the 32-bit index range */
   PA_ERR_HIP = -8,         /* HIP runtime failure (allocation, copy or launch) */
-  PA_ERR_DEVICE = -9       /* plan used on a device other than the one it was made on */
+  PA_ERR_DEVICE = -9       /* plan used on a device other than the one it was made on, or built on the host only */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -127,6 +127,8 @@ typedef struct pa_plan_info {
   int32_t split_rows;    /* (query, KV head) rows split into >1 ranges */
   int32_t split_slots;   /* partial-statistics slots those rows use */
   int32_t launches;      /* kernels one forward call enqueues (0, 1 or 2) */
+  int32_t workgroups;    /* workgroups of the main launch */
+  int32_t heads_per_item; /* KV heads one decode item covers (decode-only plans: a power of two) */
 } pa_plan_info;
 
 /*
@@ -143,6 +145,34 @@ int pa_plan_destroy(pa_plan* plan);
 
 /* Fill *info with the plan's work counts. */
 int pa_plan_get_info(const pa_plan* plan, pa_plan_info* info);
+
+/*
+ * Build the work lists pa_plan_create would build on a device with `num_cus`
+ * compute units, on the host only: no HIP call, no device memory.  For
+ * inspecting and testing the planner (pa_plan_get_info, pa_plan_get_work);
+ * forward calls reject such a plan with PA_ERR_DEVICE.  Release it with
+ * pa_plan_destroy.  Errors: as pa_plan_create, PA_ERR_INVALID for num_cus
+ * outside [1, 65536].
+ */
+int pa_plan_create_host(const pa_plan_desc* desc, int32_t num_cus, pa_plan** out_plan);
+
+/*
+ * Copy a plan's work lists (host copy; any plan).  *n_items, *n_wg and
+ * *n_merges receive the counts; each array may be NULL to skip it, else it
+ * must hold:
+ *   items     8 * n_items int32: per work item (kind: 0 decode, 1 prefill,
+ *             2 empty; first KV head; sequence; first packed query; query
+ *             count; first key; end key (exclusive); partial slot of the
+ *             first head, -1 when the row is not split).  A decode item of a
+ *             decode-only plan covers 2^s consecutive KV heads
+ *             (pa_plan_info.heads_per_item), head kvh + i using slot + i.
+ *   wg_first  n_wg + 1 int32: workgroup b of the main launch runs items
+ *             wg_first[b] .. wg_first[b + 1] - 1.
+ *   merges    5 * n_merges int32: per split (query, KV head) row (query; KV
+ *             head; first slot; number of pieces; slot stride).
+ */
+int pa_plan_get_work(const pa_plan* plan, int32_t* items, int32_t* n_items, int32_t* wg_first, int32_t* n_wg,
+                     int32_t* merges, int32_t* n_merges);
 
 /*
  * Bytes of f32 split workspace a forward call with value width `v_head_dim`

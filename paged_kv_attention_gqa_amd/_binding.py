@@ -21,8 +21,8 @@ PA_BF16 = 1
 STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_INVALID", -2: "PA_ERR_SHAPE", -3: "PA_ERR_PLAN", -4: "PA_ERR_UNSUPPORTED",
                 -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_OVERLAP", -7: "PA_ERR_RANGE", -8: "PA_ERR_HIP",
                 -9: "PA_ERR_DEVICE"}
-EXPORTED = ("pa_plan_create", "pa_plan_destroy", "pa_plan_get_info", "pa_plan_workspace_bytes",
-            "pa_attention_fwd", "pa_mla_fwd", "pa_status_string", "pa_last_error")
+EXPORTED = ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
+            "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_status_string", "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -45,7 +45,8 @@ class _PlanDesc(ctypes.Structure):
 class _PlanInfo(ctypes.Structure):
     _fields_ = [("num_queries", ctypes.c_int32), ("decode_items", ctypes.c_int32),
                 ("prefill_items", ctypes.c_int32), ("split_rows", ctypes.c_int32),
-                ("split_slots", ctypes.c_int32), ("launches", ctypes.c_int32)]
+                ("split_slots", ctypes.c_int32), ("launches", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+                ("heads_per_item", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,6 +62,9 @@ def load_library():
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     lib.pa_plan_create.argtypes = [ctypes.POINTER(_PlanDesc), P, ctypes.POINTER(P)]
+    lib.pa_plan_create_host.argtypes = [ctypes.POINTER(_PlanDesc), I, ctypes.POINTER(P)]
+    IP = ctypes.POINTER(ctypes.c_int32)
+    lib.pa_plan_get_work.argtypes = [P, P, IP, P, IP, P, IP]
     lib.pa_plan_destroy.argtypes = [P]
     lib.pa_plan_get_info.argtypes = [P, ctypes.POINTER(_PlanInfo)]
     lib.pa_plan_workspace_bytes.argtypes = [P, I, ctypes.POINTER(S)]
@@ -70,8 +74,8 @@ def load_library():
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
-    for n in ("pa_plan_create", "pa_plan_destroy", "pa_plan_get_info", "pa_plan_workspace_bytes",
-              "pa_attention_fwd", "pa_mla_fwd"):
+    for n in ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
+              "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd"):
         getattr(lib, n).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -128,11 +132,9 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def pa_plan_create(seq_lens, cu_q, q_pos, block_table, *, page_size: int, num_pages: int, num_q_heads: int,
-                   num_kv_heads: int, causal: bool = True, window: int = 0, max_splits: int = 16, mla: bool = False,
-                   split_tokens: int = 0, stream=None) -> Plan:
-    """Validate and upload a schedule (host arrays); see pa_plan_create in paged_attn.h."""
-    lib = load_library()
+def _plan_desc(seq_lens, cu_q, q_pos, block_table, page_size, num_pages, num_q_heads, num_kv_heads, causal, window,
+               max_splits, mla, split_tokens):
+    """(descriptor, host arrays it points into, Plan.desc dict)."""
     sl, cu, qp = _host_i32(seq_lens), _host_i32(cu_q), _host_i32(q_pos)
     bt = _host_i32(block_table)
     if bt.ndim != 2:
@@ -145,12 +147,53 @@ def pa_plan_create(seq_lens, cu_q, q_pos, block_table, *, page_size: int, num_pa
                      bt.ctypes.data, int(bt.shape[1]), int(page_size), int(num_pages), int(num_q_heads),
                      int(num_kv_heads), int(bool(causal)), int(window), int(max_splits), int(bool(mla)),
                      int(split_tokens))
+    info = dict(num_seqs=int(sl.shape[0]), num_queries=int(cu[-1]), table_width=int(bt.shape[1]),
+                page_size=int(page_size), num_pages=int(num_pages), num_q_heads=int(num_q_heads),
+                num_kv_heads=int(num_kv_heads), causal=bool(causal), window=int(window),
+                max_splits=int(max_splits), mla=bool(mla))
+    return desc, (sl, cu, qp, bt), info
+
+
+def pa_plan_create(seq_lens, cu_q, q_pos, block_table, *, page_size: int, num_pages: int, num_q_heads: int,
+                   num_kv_heads: int, causal: bool = True, window: int = 0, max_splits: int = 16, mla: bool = False,
+                   split_tokens: int = 0, stream=None) -> Plan:
+    """Validate and upload a schedule (host arrays); see pa_plan_create in paged_attn.h."""
+    lib = load_library()
+    desc, keep, info = _plan_desc(seq_lens, cu_q, q_pos, block_table, page_size, num_pages, num_q_heads,
+                                  num_kv_heads, causal, window, max_splits, mla, split_tokens)
     h = ctypes.c_void_p()
     _check(lib.pa_plan_create(ctypes.byref(desc), _stream_handle(stream), ctypes.byref(h)), "pa_plan_create")
-    return Plan(h, dict(num_seqs=int(sl.shape[0]), num_queries=int(cu[-1]), table_width=int(bt.shape[1]),
-                        page_size=int(page_size), num_pages=int(num_pages), num_q_heads=int(num_q_heads),
-                        num_kv_heads=int(num_kv_heads), causal=bool(causal), window=int(window),
-                        max_splits=int(max_splits), mla=bool(mla)))
+    del keep
+    return Plan(h, info)
+
+
+def pa_plan_create_host(seq_lens, cu_q, q_pos, block_table, *, num_cus: int, page_size: int, num_pages: int,
+                        num_q_heads: int, num_kv_heads: int, causal: bool = True, window: int = 0,
+                        max_splits: int = 16, mla: bool = False, split_tokens: int = 0) -> Plan:
+    """Work lists for a device of `num_cus` CUs, built on the host only (no
+    device access); see pa_plan_create_host in paged_attn.h."""
+    lib = load_library()
+    desc, keep, info = _plan_desc(seq_lens, cu_q, q_pos, block_table, page_size, num_pages, num_q_heads,
+                                  num_kv_heads, causal, window, max_splits, mla, split_tokens)
+    h = ctypes.c_void_p()
+    _check(lib.pa_plan_create_host(ctypes.byref(desc), int(num_cus), ctypes.byref(h)), "pa_plan_create_host")
+    del keep
+    return Plan(h, info)
+
+
+def pa_plan_get_work(plan: Plan):
+    """(items [n, 8], wg_first [n_wg + 1], merges [m, 5]) int32 arrays; see
+    pa_plan_get_work in paged_attn.h for the columns."""
+    lib = load_library()
+    ni, nw, nm = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.pa_plan_get_work(plan.handle, None, ctypes.byref(ni), None, ctypes.byref(nw), None, ctypes.byref(nm)),
+           "pa_plan_get_work")
+    items = np.zeros((ni.value, 8), np.int32)
+    wg = np.zeros(nw.value + 1, np.int32)
+    merges = np.zeros((nm.value, 5), np.int32)
+    _check(lib.pa_plan_get_work(plan.handle, items.ctypes.data, ctypes.byref(ni), wg.ctypes.data, ctypes.byref(nw),
+                                merges.ctypes.data, ctypes.byref(nm)), "pa_plan_get_work")
+    return items, wg, merges
 
 
 def pa_plan_destroy(plan: Plan) -> None:

@@ -434,6 +434,7 @@ int check_disjoint(const std::vector<Extent>& outs, const std::vector<Extent>& i
 }
 
 int check_device(const pa_plan* p) {
+  if (!p->dev) return fail(PA_ERR_DEVICE, "plan was built on the host only (pa_plan_create_host)");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
   if (dev != p->device) return fail(PA_ERR_DEVICE, "metadata belongs to device %d, current device is %d", p->device, dev);
@@ -457,13 +458,14 @@ struct FwdCall {
 
 extern "C" {
 
-int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
-  if (!out_plan) return fail(PA_ERR_INVALID, "out_plan is NULL");
-  int rc = validate_desc(desc);
-  if (rc != PA_OK) return rc;
+}  // extern "C"
 
+namespace {
+
+// Host copy of a validated schedule (no device access).
+pa_plan* new_plan(const pa_plan_desc* desc) {
   pa_plan* p = new (std::nothrow) pa_plan();
-  if (!p) return fail(PA_ERR_HIP, "host allocation failed");
+  if (!p) return nullptr;
   p->S = desc->num_seqs;
   p->W = std::max(desc->table_width, 1);
   p->ps = desc->page_size;
@@ -484,6 +486,20 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   }
   p->Q = p->cu_q.back();
   if (p->Q > 0) p->q_pos.assign(desc->q_pos, desc->q_pos + p->Q);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
+  if (!out_plan) return fail(PA_ERR_INVALID, "out_plan is NULL");
+  int rc = validate_desc(desc);
+  if (rc != PA_OK) return rc;
+
+  pa_plan* p = new_plan(desc);
+  if (!p) return fail(PA_ERR_HIP, "host allocation failed");
   hipError_t e = hipGetDevice(&p->device);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&p->n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e != hipSuccess) {
@@ -536,8 +552,39 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   return ok();
 }
 
+int pa_plan_create_host(const pa_plan_desc* desc, int32_t num_cus, pa_plan** out_plan) {
+  if (!out_plan) return fail(PA_ERR_INVALID, "out_plan is NULL");
+  if (num_cus <= 0 || num_cus > 65536) return fail(PA_ERR_INVALID, "num_cus %d outside [1, 65536]", num_cus);
+  int rc = validate_desc(desc);
+  if (rc != PA_OK) return rc;
+  pa_plan* p = new_plan(desc);
+  if (!p) return fail(PA_ERR_HIP, "host allocation failed");
+  p->n_cu = num_cus;
+  build_work(p);
+  *out_plan = p;
+  return ok();
+}
+
+int pa_plan_get_work(const pa_plan* plan, int32_t* items, int32_t* n_items, int32_t* wg_first, int32_t* n_wg,
+                     int32_t* merges, int32_t* n_merges) {
+  if (!plan || !n_items || !n_wg || !n_merges) return fail(PA_ERR_INVALID, "plan and the count pointers are required");
+  static_assert(sizeof(WorkItem) == 8 * sizeof(int32_t) && sizeof(MergeItem) == 5 * sizeof(int32_t),
+                "work records are exported as plain int32 rows");
+  *n_items = (int32_t)plan->items.size();
+  *n_wg = plan->n_wg;
+  *n_merges = (int32_t)plan->merges.size();
+  if (items && !plan->items.empty()) memcpy(items, plan->items.data(), plan->items.size() * sizeof(WorkItem));
+  if (wg_first) memcpy(wg_first, plan->wg_first.data(), (size_t)(plan->n_wg + 1) * sizeof(int32_t));
+  if (merges && !plan->merges.empty()) memcpy(merges, plan->merges.data(), plan->merges.size() * sizeof(MergeItem));
+  return ok();
+}
+
 int pa_plan_destroy(pa_plan* plan) {
   if (!plan) return ok();
+  if (!plan->dev) {  // built on the host only (pa_plan_create_host)
+    delete plan;
+    return ok();
+  }
   int prev = -1;
   (void)hipGetDevice(&prev);
   if (prev != plan->device) (void)hipSetDevice(plan->device);
@@ -559,6 +606,8 @@ int pa_plan_get_info(const pa_plan* plan, pa_plan_info* info) {
   info->split_rows = (int32_t)plan->merges.size();
   info->split_slots = plan->n_slots;
   info->launches = plan->items.empty() ? 0 : (plan->merges.empty() ? 1 : 2);
+  info->workgroups = plan->n_wg;
+  info->heads_per_item = 1 << plan->heads_shift;
   return ok();
 }
 
