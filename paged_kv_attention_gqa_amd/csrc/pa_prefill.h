@@ -318,12 +318,10 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     }
     return (m == -INFINITY ? 0.f : m) * c2;
   };
-  // P^T = 2^(S^T c - ref) rounded to bf16 and O^T += V^T . P^T.  k-step kk
+  // P^T = 2^(S^T c - ref) rounded to bf16 (vector work only).  k-step kk
   // covers keys 16 kk .. +15; lane (n, h) feeds keys 16 kk + 8 (e/4) + 4 h +
-  // e%4 (e = 0..7): elements 8 (kk % 2) + e of S^T block kk / 2, and the V^T
-  // rows of the same keys by two transposed reads (4 keys each) of dims 32 b
-  // + 16 (lane/16 % 2) + lane % 16 (offsets voff, plus 16 rows per k-step).
-  auto weights_pv = [&](const char* vs, const floatx16_t (&s)[MB], float sub) {
+  // e%4 (e = 0..7): elements 8 (kk % 2) + e of S^T block kk / 2.
+  auto weights = [&](const floatx16_t (&s)[MB], float sub, bf16x8_t (&pf)[NT / 16]) {
 #pragma unroll
     for (int kk = 0; kk < NT / 16; ++kk) {
       const int mb = kk >> 1, e0 = 8 * (kk & 1);
@@ -335,7 +333,15 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
         pw[j] = pack_bf16(p0, p1);
         l += p0 + p1;
       }
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      pf[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    }
+  };
+  // O^T += V^T . P^T (matrix work only): the V^T rows of k-step kk's keys by
+  // two transposed reads (4 keys each) of dims 32 b + 16 (lane/16 % 2) +
+  // lane % 16 (offsets voff, plus 16 rows per k-step).
+  auto pv = [&](const char* vs, const bf16x8_t (&pf)[NT / 16]) {
+#pragma unroll
+    for (int kk = 0; kk < NT / 16; ++kk) {
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
         const short4_t v0 = lds_read_tr16(vs + voff[b][0] + kk * 16 * (D * 2));
@@ -345,21 +351,24 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
-        o[b] = mfma_32x32x16(vf, pf, o[b]);
+        o[b] = mfma_32x32x16(vf, pf[kk], o[b]);
       }
     }
   };
 
-  // Two wave groups in opposite phase.  Between the barriers that publish
-  // tiles j and j + 1, the leading waves (0-3) compute the scores of tile j,
-  // its weights and its accumulation; the trailing waves (4-7) first turn the
-  // scores of tile j - 1 into weights and accumulate them, then compute the
-  // scores of tile j.  Each SIMD holds one wave of each group, so one wave's
-  // MFMA work overlaps the other's vector work.  Tiles land two barriers
-  // after their loads are issued; the ring holds tile j - 1 (V, trailing
-  // waves), j (being read), j + 1 (in flight) and j + 2 (issued after the
-  // barrier of tile j into the stage tile j - 2 used).  Page numbers run one
-  // tile ahead of the loads that use them.
+  // Two wave groups in opposite phase, each alternating a matrix phase M(j)
+  // (P.V of tile j - 1, then the scores of tile j) with a vector phase V(j)
+  // (mask, reference max and weights of tile j).  Between the barriers that
+  // publish tiles j and j + 1 the leading waves (0-3) run M(j) then V(j) and
+  // the trailing waves (4-7) V(j - 1) then M(j).  Each SIMD holds one wave of
+  // each group, so while one runs its matrix phase the other runs its vector
+  // phase: the two never wait on each other for the MFMA pipe, and a wave's
+  // in-order issue never holds its vector work behind its own MFMAs.  Tiles
+  // land two barriers after their loads are issued; the ring holds tile
+  // j - 1 (V, read in M(j)), j (being read), j + 1 (in flight) and j + 2
+  // (issued after the barrier of tile j into the stage of tile j - 2, whose
+  // last reader was M(j - 1)).  Page numbers run one tile ahead of the loads
+  // that use them.
   const int t_first = tb & ~(NT - 1);
   const int ntiles = (te - t_first + NT - 1) / NT;
   const bool lead = !kPrefillPingPong || wave < kPrefillWaves / 2;
@@ -373,11 +382,8 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   }
   page_next = page_of(t_first + (NS - 2) * NT);
 
-  // One loop body for both groups: weights of tile j - 1, then scores of
-  // tile j; only the barrier (and the loads issued after it) sits before the
-  // weights in the trailing waves and after them in the leading ones.
   floatx16_t s[MB];
-  float sub = 0.f;
+  bf16x8_t pf[NT / 16];
   auto sync = [&](int j) {
     wait_tiles(min(ntiles - 1 - j, 1));  // tile j has landed, j + 1 may be in flight
     __syncthreads();                     // ... for every wave; tile j - 2 is no longer read
@@ -386,16 +392,22 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
       page_next = page_of(t_first + (j + NS - 1) * NT);
     }
   };
+  auto vector_phase = [&](int jj) {  // tile jj's scores -> weights
+    if (jj >= 0 && jj < ntiles && !hidden(t_first + jj * NT)) weights(s, row_max(t_first + jj * NT, s), pf);
+  };
+  auto matrix_phase = [&](int jj) {  // P.V of tile jj - 1, scores of tile jj
+    if (jj > 0 && !hidden(t_first + (jj - 1) * NT)) pv(smem + ((jj - 1) % NS) * STAGE + TILE, pf);
+    if (jj < ntiles && !hidden(t_first + jj * NT)) scores(smem + (jj % NS) * STAGE, s);
+  };
+  // One loop body for both groups, V(j - 1) then M(j); only the barrier
+  // (and the loads issued after it) sits before V(j - 1) in the trailing
+  // waves and after it in the leading ones.
   for (int j = 0; j <= ntiles; ++j) {
-    const int t0 = t_first + j * NT;
     const bool more = j < ntiles;
     if (!lead && more) sync(j);
-    if (j > 0 && !hidden(t0 - NT)) weights_pv(smem + ((j - 1) % NS) * STAGE + TILE, s, sub);
+    vector_phase(j - 1);
     if (lead && more) sync(j);
-    if (more && !hidden(t0)) {
-      scores(smem + (j % NS) * STAGE, s);
-      sub = row_max(t0, s);
-    }
+    matrix_phase(j);
   }
 
   l = pair32_sum(l);
