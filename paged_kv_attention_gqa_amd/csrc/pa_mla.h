@@ -93,6 +93,11 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
 #pragma unroll
     for (int k = 0; k < KS_POS; ++k) qp[k] = *reinterpret_cast<const bf16x8_t*>(prow + 32 * k + 8 * c);
   }
+  // The tile loads below are inline assembly that the compiler's wait-count
+  // pass does not see; it would count only these query loads as outstanding
+  // and, at every use of a query register in the tile loop, wait until that
+  // few loads remain, i.e. for the tile loads still in flight.  Finishing the
+  // query loads here leaves it nothing to wait for in the loop.
 
   floatx4_t o[DB];
 #pragma unroll
@@ -103,11 +108,33 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   // This wave's share of a tile: latent rows ROWS_PER_WAVE * wave + r (one
   // 1 KB load each) and rotary rows 4 wave .. 4 wave + 3 (half a load: lanes
   // 0..31, 8 lanes of 16 bytes per 128-byte row).  With pages of >= 16 keys
-  // the 16 keys of a tile (clamped ones included) share one page, whose
-  // number is a scalar load issued a tile ahead; smaller pages look each row
-  // up.
+  // the 16 keys of a tile (clamped ones included) share one page, and the
+  // page numbers of 64 consecutive tiles are one vector load (lane k holding
+  // tile win + k's, handed out with v_readlane), reloaded every 64 tiles: a
+  // scalar load per tile would make the first LDS-read wait after it
+  // (lgkmcnt(0)) also wait for that load's trip to memory.  Smaller pages
+  // look each row up.
   const bool uniform = ps >= NT;
-  auto tile_page = [&](int t0) { return uniform ? load_uniform(bt, clamp_key(t0) >> a.page_shift) : 0; };
+  const int first = tb & ~(NT - 1);
+  int win = 0, win_pages = 0;
+  auto load_window = [&](int w) {
+    return bt[clamp_key(first + (w + lane) * NT) >> a.page_shift];
+  };
+  if (uniform) win_pages = load_window(0);
+  wait_vmcnt<0>();  // query loads and the first window (see above)
+  auto tile_page = [&](int t0) {
+    if (!uniform) return 0;
+    const int jt = (t0 - first) / NT;
+    if (jt - win >= kWave) {
+      win += kWave;
+      win_pages = load_window(win);
+      // wait here, once per 64 tiles: left pending, the load would make the
+      // compiler wait for all memory operations where the paths merge, on
+      // every tile
+      wait_vmcnt<0>();
+    }
+    return __builtin_amdgcn_readlane(win_pages, jt - win);
+  };
   auto issue_tile = [&](int t0, char* stage, int tpage) {
     int pg[ROWS_PER_WAVE];
 #pragma unroll
@@ -133,7 +160,6 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   };
 
   // tiles start on multiples of 16 keys; keys outside [tb, te) are masked
-  const int first = tb & ~(NT - 1);
   const int ntiles = (te - first + NT - 1) / NT;
   int page_next = 0;
 #pragma unroll

@@ -151,6 +151,12 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
 #pragma unroll
     for (int k = 0; k < KS; ++k) qf[k] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k + 8 * h);
   }
+  // The tile loads are inline assembly that the compiler's wait-count pass
+  // does not see; it would count only these query loads as outstanding and,
+  // at every use of a query register in the tile loop, wait until that few
+  // loads remain, i.e. for the tile loads still in flight.  Finishing the
+  // query loads here leaves it nothing to wait for in the loop.
+  wait_vmcnt<0>();
 
   // positions spanned by this wave's valid rows, for skipping masked tiles
   int pmin = row_valid ? pos : INT32_MAX, pmax = row_valid ? pos : -1;
