@@ -200,11 +200,34 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   auto lane_off = [&](int j) {
     return (lane_off0 ^ (uint32_t)(swz<PIECES>(KEYS_PER_LOAD * j) << 4)) + (uint32_t)(KEYS_PER_LOAD * j) * rs2;
   };
+  // Page numbers of this wave's key group in 64 consecutive tiles are one
+  // vector load (lane k holding tile win + k's, handed out with v_readlane),
+  // reloaded every 64 tiles: a scalar load per tile would make the first
+  // LDS-read wait after it (lgkmcnt(0)) also wait for that load's trip to
+  // memory.
+  const int t_base = tb & ~(NT - 1);
+  int win = 0, win_pages = 0;
+  auto load_window = [&](int w) {
+    return bt[min(t_base + (w + lane) * NT + KEYS_PER_WAVE * wq, te - 1) >> a.page_shift];
+  };
+  if constexpr (UNIFORM) {
+    win_pages = load_window(0);
+    wait_vmcnt<0>();
+  }
   auto page_of = [&](int t0) {
-    if constexpr (UNIFORM)
-      return load_uniform(bt, min(t0 + KEYS_PER_WAVE * wq, te - 1) >> a.page_shift);
-    else
+    if constexpr (UNIFORM) {
+      const int jt = (t0 - t_base) / NT;
+      if (jt - win >= kWave) {
+        win += kWave;
+        win_pages = load_window(win);
+        // wait here, once per 64 tiles: left pending, the load would make the
+        // compiler wait for all memory operations where the paths merge
+        wait_vmcnt<0>();
+      }
+      return __builtin_amdgcn_readlane(win_pages, jt - win);
+    } else {
       return 0;
+    }
   };
   auto issue_tile = [&](int t0, char* stage, int page) {
     char* dst = stage + (loads_v ? TILE : 0) + KEYS_PER_WAVE * wq * (D * 2);
