@@ -204,7 +204,8 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
  *                caller time the two kernels separately)
  *
  * The plan must be a GQA plan (mla == 0) made on the current device.
- * Q == 0 returns PA_OK without launching anything.
+ * Q == 0 returns PA_OK without launching anything; q and out (empty then)
+ * may be NULL.
  */
 int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool,
                      const void* v_pool, void* out, float* lse, int32_t head_dim,

@@ -668,7 +668,8 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
   if (plan->mla) return fail(PA_ERR_INVALID, "plan was made for MLA (use pa_mla_fwd)");
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
-  if (!q || !k_pool || !v_pool || !out) return fail(PA_ERR_INVALID, "q, k_pool, v_pool and out are required");
+  if (!k_pool || !v_pool) return fail(PA_ERR_INVALID, "k_pool and v_pool are required");
+  if (plan->Q > 0 && (!q || !out)) return fail(PA_ERR_INVALID, "q and out are required when there are queries");
   if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
     return fail(PA_ERR_SHAPE, "head sizes D=%d Dv=%d outside [1, 1024]", head_dim, v_head_dim);
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
@@ -729,8 +730,9 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
   if (!plan->mla) return fail(PA_ERR_INVALID, "plan was made for GQA (use pa_attention_fwd)");
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
-  if (!q_abs || !q_rope || !latent || !kpos || !out)
-    return fail(PA_ERR_INVALID, "q_abs, q_rope, latent, kpos and out are required");
+  if (!latent || !kpos) return fail(PA_ERR_INVALID, "latent and kpos are required");
+  if (plan->Q > 0 && (!q_abs || !q_rope || !out))
+    return fail(PA_ERR_INVALID, "q_abs, q_rope and out are required when there are queries");
   if (rank <= 0 || rank > 1024) return fail(PA_ERR_SHAPE, "latent rank %d outside [1, 1024]", rank);
   if (rope_dim <= 0 || rope_dim > 256)
     return fail(PA_ERR_SHAPE, "incompatible MLA positional dimensions: rope_dim %d outside [1, 256]", rope_dim);

@@ -131,3 +131,31 @@ def test_windowed_long_row_starts_mid_page():
     b = random_batch(42, dtype="bf16", hq=16, hkv=4, d=128, page_size=16, q_counts=(1, 2),
                      histories=[12345, 9999], window=7001)
     _parity(b)
+
+
+def test_sequences_without_queries():
+    """Sequences with no queries (one of them with no keys either) between
+    decode rows and a three-query chunk."""
+    b = random_batch(50, dtype="bf16", hq=8, hkv=2, d=128, page_size=16, q_counts=(0, 1, 0, 3),
+                     histories=[5, 300, 0, 40])
+    _parity(b)
+
+
+def test_batch_without_queries_launches_nothing():
+    import torch
+    b = random_batch(51, dtype="bf16", hq=8, hkv=2, d=128, page_size=16, q_counts=(0, 0), histories=[5, 0])
+    run = GqaRun(b)
+    assert run.info["launches"] == 0 and run.info["workgroups"] == 0
+    run()
+    torch.cuda.synchronize()
+    assert run.out.numel() == 0
+
+
+@pytest.mark.parametrize("hq,hkv,max_splits", [(8, 1, 64), (32, 2, 64), (32, 8, 1)])
+def test_128k_key_row(hq, hkv, max_splits):
+    """One decode row over 131072 keys (8192 pages): split up to the 64-piece
+    limit, or walked unsplit by one workgroup per head group."""
+    b = random_batch(52, dtype="bf16", hq=hq, hkv=hkv, d=128, page_size=16, q_counts=(1,), histories=[131071],
+                     max_splits=max_splits)
+    run = _parity(b)
+    assert (run.info["split_rows"] > 0) == (max_splits > 1)

@@ -82,3 +82,12 @@ def test_mla_page_permutation_bitwise_and_deterministic():
     r2()
     o2, l2 = r2.result()
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("max_splits", [64, 1])
+def test_mla_64k_key_row(max_splits):
+    """One MLA row over 65536 keys: split to the 64-piece limit, or unsplit
+    (one workgroup walks 4096 tiles, reloading its page-number window 64
+    times)."""
+    m = random_mla_batch(3100, page_size=64, q_counts=(1,), histories=[65535], max_splits=max_splits)
+    _parity(m)

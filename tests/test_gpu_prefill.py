@@ -56,6 +56,8 @@ PREFILL_CASES = [
     dict(hq=32, hkv=8, d=128, page_size=1, q_counts=(70,), max_len=200),
     dict(hq=32, hkv=8, d=128, page_size=16, q_counts=(513,), histories=[4096 - 513]),
     dict(hq=32, hkv=8, d=128, page_size=16, q_counts=(33, 1, 2, 3, 4, 5), max_len=300, causal=False, window=100),
+    # sequences without queries (one without keys) around a chunk and a decode row
+    dict(hq=32, hkv=8, d=128, page_size=16, q_counts=(0, 97, 0, 1, 0), histories=[40, 200, 0, 1000, 3]),
 ]
 
 

@@ -214,3 +214,19 @@ def test_host_plan_rejects_bad_cu_counts():
     for n in (0, -3, 1 << 20):
         with pytest.raises(pa.PaError):
             pa.pa_plan_create_host(num_cus=n, **s)
+
+
+def test_query_pointers_may_be_null_only_without_queries():
+    """q and out are required when the plan has queries (PA_ERR_INVALID, -1);
+    without queries NULL passes the argument checks and the host-only plan is
+    then refused for the device (PA_ERR_DEVICE, -9)."""
+    lib = pa.load_library()
+    s = schedule(**DECODE_SCHEDULES[2])
+    p = pa.pa_plan_create_host(num_cus=256, **s)
+    assert lib.pa_attention_fwd(p.handle, 1, None, 16, 16, None, None, 128, 128, 1.0, None, 0, None, None) == -1
+    pa.pa_plan_destroy(p)
+    s0 = schedule(9, q_counts=[0, 0], histories=[40, 0], page_size=16, hq=8, hkv=2)
+    p0 = pa.pa_plan_create_host(num_cus=256, **s0)
+    assert pa.pa_plan_get_info(p0)["launches"] == 0
+    assert lib.pa_attention_fwd(p0.handle, 1, None, 16, 16, None, None, 128, 128, 1.0, None, 0, None, None) == -9
+    pa.pa_plan_destroy(p0)
