@@ -17,8 +17,8 @@
 // The four waves of a workgroup share a four-stage LDS ring of 16-key tiles
 // (three in flight while one is used, one barrier per tile), loaded with
 // global_load_lds_dwordx4 (16-byte pieces of key row t stored at piece ^
-// swz(t)); block-table entries are wave-uniform scalar loads, so the
-// vector-memory counter counts tile loads only.  Every wave computes the
+// swz(t)); page numbers come from a per-lane window of 64 tiles loaded
+// once per 64 tiles, so the vector-memory counter counts tile loads only.  Every wave computes the
 // small score tile (so softmax statistics agree across waves without any
 // exchange) and owns R / 4 = 128 output dims; latent^T fragments come from
 // ds_read_b64_tr_b16.  Every lane owns one head's column, so softmax needs

@@ -106,10 +106,11 @@ __device__ __forceinline__ int tile_off(int key, int piece) {
   return key * (D * 2) + ((piece ^ swz<D / 8>(key)) << 4);
 }
 
-// UNIFORM: pages hold >= 16 keys, so a tile's page numbers are scalar loads
-// and the loop body issues no other vector-memory loads (a single per-lane
-// lookup would make the compiler drain the vector-memory counter before
-// every tile issue).
+// UNIFORM: pages hold >= 16 keys, so each wave's tile rows share one page,
+// whose number comes from a per-lane window of 64 tiles loaded once per 64
+// tiles; the loop body issues no other vector-memory loads (a per-tile
+// per-lane lookup would make the compiler drain the vector-memory counter
+// before every tile issue).
 template <int D, int G, bool UNIFORM>
 __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const WorkItem& it, char* smem) {
   constexpr int NT = kPrefillTileKeys;
@@ -179,8 +180,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // or the V tile (w >= 4) with LOADS_PER_WAVE loads of KEYS_PER_LOAD rows;
   // lane l carries stored piece l % PIECES of row l / PIECES of its load.
   // Sixteen aligned keys never straddle a page of >= 16 keys, so one page
-  // number per wave and tile is enough: it is a scalar load issued a tile
-  // ahead.  Keys past tok_end read the last key instead (every row in LDS is
+  // number per wave and tile is enough (see page_of).  Keys past tok_end read the last key instead (every row in LDS is
   // finite sequence data; such keys are masked); keys before tok_begin are
   // sequence keys and are masked as well.
   const int wq = wave % HALF;
@@ -396,8 +396,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // land two barriers after their loads are issued; the ring holds tile
   // j - 1 (V, read in M(j)), j (being read), j + 1 (in flight) and j + 2
   // (issued after the barrier of tile j into the stage of tile j - 2, whose
-  // last reader was M(j - 1)).  Page numbers run one tile ahead of the loads
-  // that use them.
+  // last reader was M(j - 1)).
   const int t_first = tb & ~(NT - 1);
   const int ntiles = (te - t_first + NT - 1) / NT;
   const bool lead = !kPrefillPingPong || wave < kPrefillWaves / 2;
