@@ -10,6 +10,7 @@ from the definition: boostr 0.2.0-beta.2 `standard_attention_fwd` /
 positions of ruDNN 0.1.107 `DevicePlan::attention` and `DevicePlan::mla`).
 This module only builds it with gcc and marshals numpy arrays into it.
 `brute.py` is an independent pure-Python brute force for tiny inputs.
+`append_kv` (the cache write before attention) is a plain numpy loop.
 """
 from __future__ import annotations
 
@@ -131,3 +132,20 @@ def mla(b, rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None
     if rows is None:
         return out.reshape(Q, b.heads, b.r), lse.reshape(Q, b.heads)
     return out, lse
+
+
+def append_kv(seq_lens, cu_q, q_pos, block_table, page_size: int, k_new: np.ndarray, v_new: np.ndarray,
+              k_pool: np.ndarray, v_pool: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Paged K/V append, following ruDNN 0.1.107 paged_attention
+    `DevicePlan::append`: query i of sequence s at absolute position p writes
+    its new rows into pool page block_table[s][p // page_size], slot
+    p % page_size.  Returns updated copies of the pools (any storage dtype:
+    rows are copied as they are).  A plain loop over the queries."""
+    k_out, v_out = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    for s in range(len(seq_lens)):
+        for i in range(int(cu_q[s]), int(cu_q[s + 1])):
+            p = int(q_pos[i])
+            page = int(block_table[s][p // page_size])
+            k_out[page, p % page_size] = k_new[i]
+            v_out[page, p % page_size] = v_new[i]
+    return k_out, v_out

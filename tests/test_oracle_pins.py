@@ -280,3 +280,52 @@ def test_bf16_rounding_is_round_to_nearest_even():
     # 1 + 3*2^-8 is a tie between 1+2^-7 and 1+2^-6: rounds to even (1+2^-6)
     assert list(bits[:3]) == [0x3F80, 0x3F80, 0x3F82]
     assert bits[3] == 0xC020 and bits[5] == 0x7F80 and bits[6] == 0x8000
+
+
+@pytest.mark.parametrize("dtype,page_size", [("bf16", 16), ("f32", 1), ("bf16", 64)])
+def test_append_places_rows_at_their_positions(dtype, page_size):
+    """Paged append (ruDNN paged_attention `DevicePlan::append`): read back in
+    logical order through the dense view (numpy indexing, not the oracle's
+    loop), position q_pos[i] of each sequence holds query i's new rows, every
+    other position and every unreferenced page is unchanged."""
+    b = random_batch(70, dtype=dtype, hq=8, hkv=2, d=64, page_size=page_size, q_counts=(1, 5, 0, 3),
+                     histories=[40, 0, 7, 129])
+    rng = np.random.default_rng(71)
+    store = np.float32 if dtype == "f32" else np.uint16
+    k_new = rng.integers(0, 1 << 15, size=(b.num_queries, b.hkv, b.d)).astype(store)
+    v_new = rng.integers(0, 1 << 15, size=(b.num_queries, b.hkv, b.dv)).astype(store)
+    k2, v2 = oracle.append_kv(b.seq_lens, b.cu_q, b.q_pos, b.block_table, b.page_size, k_new, v_new, b.k, b.v)
+    touched = np.zeros(b.k.shape[:2], bool)
+    for s in range(b.num_seqs):
+        L = int(b.seq_lens[s])
+        before_k = dense_sequence(b.k, b.block_table, s, L, b.page_size)
+        after_k = dense_sequence(k2, b.block_table, s, L, b.page_size)
+        after_v = dense_sequence(v2, b.block_table, s, L, b.page_size)
+        mine = np.zeros(L, bool)
+        for i in range(int(b.cu_q[s]), int(b.cu_q[s + 1])):
+            p = int(b.q_pos[i])
+            mine[p] = True
+            assert np.array_equal(after_k[p], k_new[i]) and np.array_equal(after_v[p], v_new[i])
+        same = ~mine
+        assert np.array_equal(after_k[same].view(np.uint8), before_k[same].view(np.uint8))
+        t = np.arange(L)[mine]
+        touched[b.block_table[s, t // b.page_size], t % b.page_size] = True
+    # nothing outside the written slots changed (NaN-poisoned rows compared bitwise)
+    assert np.array_equal(k2[~touched].view(np.uint8), b.k[~touched].view(np.uint8))
+    assert np.array_equal(v2[~touched].view(np.uint8), b.v[~touched].view(np.uint8))
+
+
+def test_append_then_window_one_attention_returns_the_new_values():
+    """After appending, attention with a one-key window reads each query's own
+    new V row through the C oracle's paged gather (an independent route from
+    page number and slot to row)."""
+    b = random_batch(72, dtype="bf16", hq=8, hkv=2, d=64, page_size=16, q_counts=(1, 4, 2), histories=[33, 0, 500],
+                     window=1)
+    rng = np.random.default_rng(73)
+    v_new = f32_to_bf16_bits(rng.standard_normal((b.num_queries, b.hkv, b.dv)).astype(np.float32))
+    k_new = f32_to_bf16_bits(rng.standard_normal((b.num_queries, b.hkv, b.d)).astype(np.float32))
+    k2, v2 = oracle.append_kv(b.seq_lens, b.cu_q, b.q_pos, b.block_table, b.page_size, k_new, v_new, b.k, b.v)
+    out, lse = oracle.attention(dataclasses.replace(b, k=k2, v=v2))
+    G = b.hq // b.hkv
+    want = widen(v_new, "bf16")[:, np.arange(b.hq) // G]
+    assert np.array_equal(out, want) and np.all(lse == lse)
