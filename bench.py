@@ -241,8 +241,54 @@ def summarize(name, r):
     return out
 
 
+def measure_append(name, steps, warmup):
+    """Paged K/V append of one new K and V row per (query, KV head) of
+    workload `name` into its pools (the cache write before attention), timed
+    with HIP events around `steps` back-to-back calls.  Bytes: each new row
+    read once and written once."""
+    import torch
+    import paged_kv_attention_gqa_amd as pa
+    from synth import CONFIGS
+    from tests.gpu_harness import GqaRun
+
+    b = CONFIGS[name]()
+    run_ = GqaRun(b, with_lse=False)
+    rng = np.random.default_rng(0)
+    k_new = torch.from_numpy(rng.standard_normal((b.num_queries, b.hkv, b.d), dtype=np.float32)).to(
+        "cuda", dtype=torch.bfloat16)
+    v_new = torch.from_numpy(rng.standard_normal((b.num_queries, b.hkv, b.dv), dtype=np.float32)).to(
+        "cuda", dtype=torch.bfloat16)
+    for _ in range(warmup):
+        pa.pa_append_kv(run_.plan, k_new, v_new, run_.k, run_.v)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    # one call as a caller makes it (the host's ~10 us per call included) ...
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pa.pa_append_kv(run_.plan, k_new, v_new, run_.k, run_.v)
+    torch.cuda.synchronize()
+    call_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # ... and the kernels back to back: the GPU first sleeps while the host
+    # queues every call, so the events bracket device time only
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e6 + steps * 5e4))
+    e0.record(stream)
+    for _ in range(steps):
+        pa.pa_append_kv(run_.plan, k_new, v_new, run_.k, run_.v)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = 2 * (k_new.numel() + v_new.numel()) * 2
+    del run_
+    torch.cuda.empty_cache()
+    return {"workload": f"append:{name}", "ms_per_call": round(call_ms, 5), "kernel_ms": round(ms, 5),
+            "bytes": nbytes, "bound": "hbm", "kernel_gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 PRIMARY = "bf16_decode_batch"
 SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode")
+APPEND = ("bf16_decode_batch", "bf16_chunked_prefill")  # cache writes of one decode step and of one chunk
 
 
 def run(args):
@@ -295,6 +341,8 @@ def run(args):
                 result["secondary"].append(summarize(n, measure(n, args.steps, args.warmup)))
             except pa.PaError as e:  # a workload this build cannot run is reported, not hidden
                 result["secondary"].append({"workload": n, "error": str(e)})
+        for n in APPEND:
+            result["secondary"].append(measure_append(n, args.steps, args.warmup))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, mla, bytes_alg if hbm else flops_alg, hbm)
     return result

@@ -240,6 +240,33 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
 /* Static name of a status code. */
 const char* pa_status_string(int status);
 
+/*
+ * Paged K/V append (ruDNN 0.1.107 paged_attention `DevicePlan::append`: the
+ * cache write that precedes attention in a decode or prefill step): for every
+ * packed query i of sequence s at position p = q_pos[i], the new rows go to
+ * pool page block_table[s][p / page_size], slot p % page_size:
+ *
+ *   k_pool[page, slot, h, :] = k_new[i, h, :]   v_pool[page, slot, h, :] = v_new[i, h, :]
+ *
+ *   dtype     PA_F32 or PA_BF16 (of all four tensors; rows are copied bit for bit)
+ *   k_new     [Q, heads, head_dim]       v_new [Q, heads, v_head_dim]
+ *   k_pool    [num_pages, page_size, heads, head_dim], written in place
+ *   v_pool    [num_pages, page_size, heads, v_head_dim], written in place
+ *   heads     the plan's num_kv_heads (1 for an MLA plan: k_new / k_pool are
+ *             the latent rows and pool, v_new / v_pool the rotary ones)
+ *
+ * Rows of the pools that no query's position names are left as they are.
+ * Copy-on-write of caches shared between sequences is the caller's (the
+ * library never allocates).  Errors: PA_ERR_PLAN when two queries of the plan
+ * name the same pool slot (their writes would race); PA_ERR_UNSUPPORTED for
+ * rows that are not whole 16-byte chunks; PA_ERR_OVERLAP when a new-row
+ * tensor overlaps a pool or the pools overlap; otherwise as pa_attention_fwd.
+ * Q == 0 returns PA_OK without launching anything (k_new and v_new may then
+ * be NULL).
+ */
+int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const void* v_new, void* k_pool,
+                 void* v_pool, int32_t head_dim, int32_t v_head_dim, void* stream);
+
 /* Detail message of the calling thread's last failure ("" if none). */
 const char* pa_last_error(void);
 

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_INVALID", -2: "PA_ERR_SHAPE", -3: "PA_ER
                 -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_OVERLAP", -7: "PA_ERR_RANGE", -8: "PA_ERR_HIP",
                 -9: "PA_ERR_DEVICE"}
 EXPORTED = ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
-            "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_status_string", "pa_last_error")
+            "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv", "pa_status_string",
+            "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -70,12 +71,13 @@ def load_library():
     lib.pa_plan_workspace_bytes.argtypes = [P, I, ctypes.POINTER(S)]
     lib.pa_attention_fwd.argtypes = [P, I, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_mla_fwd.argtypes = [P, I, P, P, P, P, P, P, I, I, F, P, S, P, P]
+    lib.pa_append_kv.argtypes = [P, I, P, P, P, P, I, I, P]
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     for n in ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
-              "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd"):
+              "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv"):
         getattr(lib, n).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -308,3 +310,24 @@ def pa_mla_fwd(plan: Plan, q_abs, q_rope, latent, kpos, out, lse=None, *, scale:
     wp, wn = _ws(workspace)
     _check(load_library().pa_mla_fwd(plan.handle, dt, pa_, pr, pl_, pk, po, plse, R, P, float(scale), wp, wn,
                                      _event(event_after_main), _stream_handle(stream)), "pa_mla_fwd")
+
+
+def pa_append_kv(plan: Plan, k_new, v_new, k_pool, v_pool, *, stream=None) -> None:
+    """Write the new K/V rows of every query into its pool slot (see
+    pa_append_kv in paged_attn.h)."""
+    d = plan.desc
+    dt = _dtype_code(k_pool)
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("v_pool", v_pool)):
+        if t.dtype != k_pool.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from k_pool dtype {k_pool.dtype}")
+    pk, pv = _dev(k_pool, "k_pool", 4), _dev(v_pool, "v_pool", 4)
+    Q, heads = d["num_queries"], d["num_kv_heads"]
+    D, Dv = int(k_pool.shape[3]), int(v_pool.shape[3])
+    pool = (d["num_pages"], d["page_size"], heads)
+    if tuple(k_pool.shape[:3]) != pool or tuple(v_pool.shape[:3]) != pool:
+        raise ValueError(f"pool shapes {tuple(k_pool.shape)}, {tuple(v_pool.shape)} do not match {pool} x (D, Dv)")
+    if tuple(k_new.shape) != (Q, heads, D) or tuple(v_new.shape) != (Q, heads, Dv):
+        raise ValueError(f"new-row shapes {tuple(k_new.shape)}, {tuple(v_new.shape)} != {(Q, heads, D)}, {(Q, heads, Dv)}")
+    pkn, pvn = _dev(k_new, "k_new", 3), _dev(v_new, "v_new", 3)
+    _check(load_library().pa_append_kv(plan.handle, dt, pkn, pvn, pk, pv, D, Dv, _stream_handle(stream)),
+           "pa_append_kv")

@@ -83,6 +83,10 @@ struct pa_plan {
   int32_t heads_shift = 0;        // decode items cover 2^heads_shift consecutive KV heads
   int32_t n_wg = 0;               // workgroups of the main launch
   int32_t n_cu = 0;               // compute units of the plan's device
+  // append: pool slot (page * page_size + slot) of every query's position,
+  // and the first query whose slot another query also writes (-1: none)
+  std::vector<int32_t> slot_of;
+  int32_t dup_query = -1;
   // device copy: one allocation
   std::vector<char> blob;
   char* dev = nullptr;
@@ -91,6 +95,7 @@ struct pa_plan {
   const int32_t* d_lens = nullptr;
   const WorkItem* d_items = nullptr;
   const int32_t* d_wg_first = nullptr;
+  const int32_t* d_slot_of = nullptr;
   const MergeItem* d_merges = nullptr;
 
   int group() const { return hq / hkv; }
@@ -486,6 +491,21 @@ pa_plan* new_plan(const pa_plan_desc* desc) {
   }
   p->Q = p->cu_q.back();
   if (p->Q > 0) p->q_pos.assign(desc->q_pos, desc->q_pos + p->Q);
+  // append slots (positions are validated: every one maps to a pool page)
+  p->slot_of.resize(p->Q);
+  for (int s = 0; s < p->S; ++s)
+    for (int i = p->cu_q[s]; i < p->cu_q[s + 1]; ++i) {
+      const int pos = p->q_pos[i];
+      p->slot_of[i] = p->bt[(size_t)s * p->W + pos / p->ps] * p->ps + pos % p->ps;
+    }
+  std::vector<std::pair<int32_t, int32_t>> order(p->Q);
+  for (int i = 0; i < p->Q; ++i) order[i] = {p->slot_of[i], i};
+  std::sort(order.begin(), order.end());
+  for (int i = 1; i < p->Q; ++i)
+    if (order[i].first == order[i - 1].first) {
+      p->dup_query = std::max(order[i].second, order[i - 1].second);
+      break;
+    }
   return p;
 }
 
@@ -508,14 +528,15 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   }
   build_work(p);
 
-  // one blob: block table | q_pos | seq_lens | items | workgroup ranges | merges
+  // one blob: block table | q_pos | seq_lens | items | workgroup ranges | merges | append slots
   size_t off_bt = 0;
   size_t off_qpos = align_up(off_bt + p->bt.size() * 4, kAlign);
   size_t off_lens = align_up(off_qpos + p->q_pos.size() * 4, kAlign);
   size_t off_items = align_up(off_lens + p->seq_lens.size() * 4, kAlign);
   size_t off_wg = align_up(off_items + p->items.size() * sizeof(WorkItem), kAlign);
   size_t off_merges = align_up(off_wg + p->wg_first.size() * 4, kAlign);
-  size_t total = align_up(off_merges + p->merges.size() * sizeof(MergeItem), kAlign);
+  size_t off_slots = align_up(off_merges + p->merges.size() * sizeof(MergeItem), kAlign);
+  size_t total = align_up(off_slots + p->slot_of.size() * 4, kAlign);
   total = std::max(total, kAlign);
   p->blob.assign(total, 0);
   if (!p->bt.empty()) memcpy(p->blob.data() + off_bt, p->bt.data(), p->bt.size() * 4);
@@ -525,6 +546,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   memcpy(p->blob.data() + off_wg, p->wg_first.data(), p->wg_first.size() * 4);
   if (!p->merges.empty())
     memcpy(p->blob.data() + off_merges, p->merges.data(), p->merges.size() * sizeof(MergeItem));
+  if (!p->slot_of.empty()) memcpy(p->blob.data() + off_slots, p->slot_of.data(), p->slot_of.size() * 4);
 
   e = hipMalloc(reinterpret_cast<void**>(&p->dev), total);
   if (e != hipSuccess) {
@@ -548,6 +570,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   p->d_items = reinterpret_cast<const WorkItem*>(p->dev + off_items);
   p->d_wg_first = reinterpret_cast<const int32_t*>(p->dev + off_wg);
   p->d_merges = reinterpret_cast<const MergeItem*>(p->dev + off_merges);
+  p->d_slot_of = reinterpret_cast<const int32_t*>(p->dev + off_slots);
   *out_plan = p;
   return ok();
 }
@@ -786,6 +809,41 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   a.causal = plan->causal;
   a.window = plan->window;
   return launch_common(c, true);
+}
+
+int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const void* v_new, void* k_pool,
+                 void* v_pool, int32_t head_dim, int32_t v_head_dim, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!k_pool || !v_pool) return fail(PA_ERR_INVALID, "k_pool and v_pool are required");
+  if (plan->Q > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID, "k_new and v_new are required when there are queries");
+  if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
+    return fail(PA_ERR_SHAPE, "row widths %d, %d outside [1, 1024]", head_dim, v_head_dim);
+  const size_t es = dtype == PA_F32 ? 4 : 2;
+  const int heads = plan->mla ? 1 : plan->hkv;
+  if ((head_dim * es) % 16 || (v_head_dim * es) % 16)
+    return fail(PA_ERR_UNSUPPORTED, "this build appends rows of whole 16-byte chunks (widths %d, %d)", head_dim,
+                v_head_dim);
+  if (plan->dup_query >= 0)
+    return fail(PA_ERR_PLAN, "query %d writes the pool slot of another query of the plan", plan->dup_query);
+  const size_t slots = (size_t)plan->num_pages * plan->ps * heads;
+  std::vector<Extent> outs = {{k_pool, slots * head_dim * es, "k_pool"}, {v_pool, slots * v_head_dim * es, "v_pool"}};
+  std::vector<Extent> ins = {{k_new, (size_t)plan->Q * heads * head_dim * es, "k_new"},
+                             {v_new, (size_t)plan->Q * heads * v_head_dim * es, "v_new"}};
+  int rc = check_disjoint(outs, ins);
+  if (rc != PA_OK) return rc;
+  rc = check_device(plan);
+  if (rc != PA_OK) return rc;
+  if (plan->Q == 0) return ok();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (st != plan->created_on) {
+    hipError_t e = hipStreamWaitEvent(st, plan->ready, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(plan)");
+  }
+  hipError_t e = pa::launch_append(k_new, v_new, k_pool, v_pool, plan->d_slot_of, plan->Q, heads,
+                                   (int)(head_dim * es), (int)(v_head_dim * es), std::max(plan->n_cu, 1), st);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
 }
 
 const char* pa_status_string(int status) {

@@ -32,5 +32,11 @@ hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream);
 hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream);
 
+// Paged K/V append: rows (i, h) of k_new [Q, heads, k_row_bytes] and v_new
+// [Q, heads, v_row_bytes] to pool rows (slot_of[i], h).  Row sizes are
+// multiples of 16 bytes; n_cu sizes the grid.
+hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* slot_of,
+                         int64_t queries, int heads, int k_row_bytes, int v_row_bytes, int n_cu, hipStream_t stream);
+
 
 }  // namespace pa

@@ -230,3 +230,21 @@ def test_query_pointers_may_be_null_only_without_queries():
     assert pa.pa_plan_get_info(p0)["launches"] == 0
     assert lib.pa_attention_fwd(p0.handle, 1, None, 16, 16, None, None, 128, 128, 1.0, None, 0, None, None) == -9
     pa.pa_plan_destroy(p0)
+
+
+def test_append_rejects_two_queries_writing_one_slot():
+    """pa_append_kv refuses a plan in which two queries name one pool slot
+    (PA_ERR_PLAN, -3) before any device check; a plan without such a pair
+    passes the argument checks and the host-only plan is then refused for the
+    device (PA_ERR_DEVICE, -9).  Tensor pointers are never dereferenced."""
+    lib = pa.load_library()
+    s = schedule(8, q_counts=[1, 3], histories=[20, 50], page_size=16, hq=8, hkv=2)
+    p = pa.pa_plan_create_host(num_cus=256, **s)
+    assert lib.pa_append_kv(p.handle, 1, 1 << 20, 2 << 20, 3 << 20, 1 << 30, 64, 64, None) == -9
+    pa.pa_plan_destroy(p)
+    s["q_pos"] = s["q_pos"].copy()
+    s["q_pos"][2] = s["q_pos"][1]
+    p = pa.pa_plan_create_host(num_cus=256, **s)
+    assert lib.pa_append_kv(p.handle, 1, 1 << 20, 2 << 20, 3 << 20, 1 << 30, 64, 64, None) == -3
+    assert "writes the pool slot" in pa.pa_last_error()
+    pa.pa_plan_destroy(p)
