@@ -45,7 +45,7 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int
-        for name, extra in (("po_attention", [P, P, P]), ("po_mla", [P, P, P, P])):
+        for name, extra in (("po_attention", [P, P, P]), ("po_mla", [P, P, P, P]), ("po_widen", [])):
             fn = getattr(lib, name)
             fn.restype = I
         _lib = lib
@@ -67,12 +67,24 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else ctypes.c_void_p(a.ctypes.data)
 
 
-_DT = {"f32": 0, "bf16": 1}
+_DT = {"f32": 0, "bf16": 1, "f16": 2}
 
 
 def _storage(a: np.ndarray, dtype: str) -> np.ndarray:
-    want = np.float32 if dtype == "f32" else np.uint16
+    want = np.float32 if dtype == "f32" else np.uint16  # bf16 and f16: raw 16-bit patterns
     return np.ascontiguousarray(a, dtype=want)
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored elements (f32 values, or bf16 / f16 bit patterns) -> float64,
+    exactly, through the oracle's own conversion."""
+    lib = _load()
+    x = _storage(a, dtype)
+    out = np.empty(x.size, dtype=np.float64)
+    rc = lib.po_widen(ctypes.c_int(_DT[dtype]), _ptr(x), ctypes.c_int64(x.size), _ptr(out))
+    if rc:
+        raise RuntimeError(f"oracle: {_ERR.get(rc, rc)}")
+    return out.reshape(x.shape)
 
 
 _ERR = {-1: "query outside every sequence", -2: "block-table entry outside the pool",

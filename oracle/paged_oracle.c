@@ -27,9 +27,10 @@
  *     value, rotated position cache [pages, page_size, 1, P]; the score adds
  *     the latent dot product and the position dot product before scaling.
  *
- * Keys that are not visible to a query row are never read.  Inputs are f32 or
- * bf16 (raw 16-bit patterns) and are widened exactly to double.  All
- * arithmetic is double precision with libm exp/log.
+ * Keys that are not visible to a query row are never read.  Inputs are f32,
+ * bf16 or IEEE binary16 (both as raw 16-bit patterns; ruDNN's tensor check
+ * admits all three types) and are widened exactly to double.  All arithmetic
+ * is double precision with libm exp/log.
  *
  * Rows run in parallel on POSIX threads; each (query, head) row is computed by
  * one thread in one fixed order, so results do not depend on the thread count.
@@ -40,17 +41,45 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { PO_F32 = 0, PO_BF16 = 1 };
+enum { PO_F32 = 0, PO_BF16 = 1, PO_F16 = 2 };
+
+/* IEEE 754 binary16 bits -> double (exact): 1 sign bit, 5 exponent bits
+ * (bias 15), 10 fraction bits; exponent 0 holds zero and the subnormals
+ * m * 2^-24, exponent 31 infinities and NaN. */
+static double po_half(uint16_t h)
+{
+    const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
 
 /* Exact widening of one stored element to double. */
 static double po_load(int dtype, const void *base, int64_t idx)
 {
     if (dtype == PO_F32)
         return (double)((const float *)base)[idx];
+    if (dtype == PO_F16)
+        return po_half(((const uint16_t *)base)[idx]);
     uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* The widening above, exported for tests: out[i] = element i of base. */
+int po_widen(int dtype, const void *base, int64_t n, double *out)
+{
+    if (dtype != PO_F32 && dtype != PO_BF16 && dtype != PO_F16)
+        return -4;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = po_load(dtype, base, i);
+    return 0;
 }
 
 typedef struct {
@@ -189,6 +218,7 @@ static void *po_worker(void *arg)
 static int po_run(po_job *j)
 {
     if (j->hq <= 0 || j->hkv <= 0 || j->hq % j->hkv != 0 || j->page_size <= 0) return -4;
+    if (j->dtype != PO_F32 && j->dtype != PO_BF16 && j->dtype != PO_F16) return -4;
     if (j->rows) {
         for (int64_t r = 0; r < j->num_rows; ++r)
             if (j->rows[r] < 0 || j->rows[r] >= (int64_t)j->num_queries * j->hq) return -4;

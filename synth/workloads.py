@@ -1,8 +1,9 @@
 """Seeded synthetic paged-KV workloads.
 
-Every array is plain numpy.  bf16 tensors are carried as their raw 16-bit
-patterns (uint16), produced from float32 draws by round-to-nearest-even; the
-same rounded bits feed both the HIP path and the oracle.
+Every array is plain numpy.  bf16 and f16 (IEEE binary16) tensors are carried
+as their raw 16-bit patterns (uint16), produced from float32 draws by
+round-to-nearest-even; the same rounded bits feed both the HIP path and the
+oracle.
 
 Layouts follow ruDNN 0.1.107 paged_attention/mod.rs (`DevicePlan::attention`,
 `DevicePlan::mla`): packed Q [queries, Hq, D]; K pool [pages, page_size, Hkv,
@@ -27,6 +28,7 @@ from typing import Callable, Dict, Optional
 import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
+F16_NAN = np.uint16(0x7E00)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -44,6 +46,13 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     if nan.any():
         out[nan] = BF16_NAN
     return out
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (numpy's conversion: round to
+    nearest even, overflow to infinity, NaN -> NaN)."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -84,25 +93,27 @@ def _chunked(rng: np.random.Generator, n: int, fill):
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     """N(0,1) float32 draws rounded to the storage type."""
     n = int(np.prod(shape))
+    if dtype not in ("f32", "bf16", "f16"):
+        raise ValueError(f"unknown storage type {dtype!r}")
     out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
 
     def fill(g, s, e):
         x = g.standard_normal(e - s, dtype=np.float32)
-        out[s:e] = x if dtype == "f32" else f32_to_bf16_bits(x)
+        out[s:e] = x if dtype == "f32" else (f32_to_bf16_bits(x) if dtype == "bf16" else f32_to_f16_bits(x))
 
     _chunked(rng, n, fill)
     return out.reshape(shape)
 
 
 def _nan_value(dtype: str):
-    return np.float32(np.nan) if dtype == "f32" else BF16_NAN
+    return {"f32": np.float32(np.nan), "bf16": BF16_NAN, "f16": F16_NAN}[dtype]
 
 
 @dataclasses.dataclass
 class PagedBatch:
     """One packed batch over a paged K/V pool (GQA/MHA)."""
     name: str
-    dtype: str                      # "f32" | "bf16"
+    dtype: str                      # "f32" | "bf16" | "f16"
     seq_lens: np.ndarray            # int32 [S]
     cu_q: np.ndarray                # int32 [S+1]
     q_pos: np.ndarray               # int32 [Q]
@@ -287,9 +298,10 @@ def config_bf16_mixed_batch(seed: int = 4) -> PagedBatch:
                       bt, ps, pool, hq, hkv, d, d, 1.0 / math.sqrt(128.0), True, 4096, q, k, v, seed, 16)
 
 
-def _unit_rms_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+def _unit_rms(rng: np.random.Generator, shape, dtype: str = "bf16") -> np.ndarray:
     """N(0,1) rows rescaled in float32 to unit RMS (no epsilon, no weight),
-    then rounded to bf16."""
+    then rounded to the 16-bit storage type."""
+    to_bits = f32_to_bf16_bits if dtype == "bf16" else f32_to_f16_bits
     width = shape[-1]
     rows = int(np.prod(shape[:-1]))
     out = np.empty(rows * width, dtype=np.uint16)
@@ -298,7 +310,7 @@ def _unit_rms_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     def fill(g, s, e):
         x = g.standard_normal(e - s, dtype=np.float32).reshape(-1, width)
         rms = np.sqrt(np.mean(x * x, axis=1, dtype=np.float32), dtype=np.float32)
-        out[s:e] = f32_to_bf16_bits(x / rms[:, None]).reshape(-1)
+        out[s:e] = to_bits(x / rms[:, None]).reshape(-1)
 
     _chunked(rng, rows * width, fill)
     return out.reshape(shape)
@@ -314,7 +326,7 @@ def config_bf16_mla_decode(seed: int = 5) -> MlaBatch:
     bt, pool, _ = _tables(rng, seq_lens, ps)
     q_abs = _normal(rng, (S, H, R), "bf16")
     q_rope = _normal(rng, (S, H, P), "bf16")
-    latent = _unit_rms_bf16(rng, (pool, ps, 1, R))
+    latent = _unit_rms(rng, (pool, ps, 1, R))
     kpos = _normal(rng, (pool, ps, 1, P), "bf16")
     return MlaBatch("bf16_mla_decode", "bf16", seq_lens, _packed([1] * S), seq_lens - 1, bt, ps, pool,
                     H, R, P, 1.0 / math.sqrt(576.0), True, 0, q_abs, q_rope, latent, kpos, seed, 16)
@@ -366,9 +378,11 @@ def random_batch(seed: int, *, dtype: str = "bf16", hq: int = 8, hkv: int = 2, d
 def random_mla_batch(seed: int, *, heads: int = 16, r: int = 512, p: int = 64, page_size: int = 64,
                      q_counts=(1, 1, 1), histories=None, max_len: int = 700, causal: bool = True,
                      window: int = 0, extra_pages: int = 2, poison: bool = True,
-                     max_splits: int = 16) -> MlaBatch:
-    """A small ragged absorbed-MLA batch (bf16), laid out like the MLA
+                     max_splits: int = 16, dtype: str = "bf16") -> MlaBatch:
+    """A small ragged absorbed-MLA batch (bf16 or f16), laid out like the MLA
     workload above, with NaN in unreferenced pages and tail slots."""
+    if dtype not in ("bf16", "f16"):
+        raise ValueError(f"MLA batches are 16-bit, not {dtype!r}")
     rng = np.random.default_rng(seed)
     S = len(q_counts)
     if histories is None:
@@ -379,13 +393,13 @@ def random_mla_batch(seed: int, *, heads: int = 16, r: int = 512, p: int = 64, p
     q_pos = np.concatenate([np.arange(L - c, L, dtype=np.int32) for L, c in zip(seq_lens, q_counts)]
                            + [np.zeros(0, np.int32)])
     Q = int(sum(q_counts))
-    q_abs = _normal(rng, (Q, heads, r), "bf16")
-    q_rope = _normal(rng, (Q, heads, p), "bf16")
-    latent = _unit_rms_bf16(rng, (pool, page_size, 1, r))
-    kpos = _normal(rng, (pool, page_size, 1, p), "bf16")
+    q_abs = _normal(rng, (Q, heads, r), dtype)
+    q_rope = _normal(rng, (Q, heads, p), dtype)
+    latent = _unit_rms(rng, (pool, page_size, 1, r), dtype)
+    kpos = _normal(rng, (pool, page_size, 1, p), dtype)
     if poison:
         for t in (latent, kpos):
-            _poison_unused(t, used, seq_lens, bt, page_size, "bf16", tails=True)
-    return MlaBatch(f"random_mla_{seed}", "bf16", seq_lens, _packed(list(q_counts)), q_pos.astype(np.int32), bt,
+            _poison_unused(t, used, seq_lens, bt, page_size, dtype, tails=True)
+    return MlaBatch(f"random_mla_{seed}", dtype, seq_lens, _packed(list(q_counts)), q_pos.astype(np.int32), bt,
                     page_size, pool, heads, r, p, 1.0 / math.sqrt(r + p), causal, window, q_abs, q_rope, latent,
                     kpos, seed, max_splits)

@@ -9,8 +9,12 @@ from synth import bf16_bits_to_f32
 
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Stored values -> float64 (exact)."""
-    return (a.astype(np.float64) if dtype == "f32" else bf16_bits_to_f32(a).astype(np.float64))
+    """Stored values -> float64 (exact); f16 through numpy's IEEE binary16."""
+    if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "f16":
+        return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
+    return bf16_bits_to_f32(a).astype(np.float64)
 
 
 def dense_sequence(pool: np.ndarray, block_table: np.ndarray, s: int, length: int, page_size: int) -> np.ndarray:

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from oracle import brute
-from synth import f32_to_bf16_bits, random_batch, random_mla_batch, PagedBatch
+from synth import f32_to_bf16_bits, f32_to_f16_bits, random_batch, random_mla_batch, PagedBatch
 from tests.dense_view import dense_sequence, scatter_into_pool, widen
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -50,6 +50,8 @@ CASES = [
     dict(dtype="bf16", hq=6, hkv=3, d=8, page_size=16, q_counts=(3, 1), causal=False, window=7),
     dict(dtype="f32", hq=8, hkv=2, d=12, page_size=5, q_counts=(1, 1, 1), causal=True, window=1),
     dict(dtype="bf16", hq=3, hkv=1, d=8, page_size=2, q_counts=(5,), causal=True, window=2, dv=4),
+    dict(dtype="f16", hq=4, hkv=2, d=16, page_size=4, q_counts=(1, 3, 2), causal=True, window=6),
+    dict(dtype="f16", hq=2, hkv=1, d=8, page_size=1, q_counts=(2, 1), causal=False, window=0, dv=4),
 ]
 
 
@@ -115,7 +117,7 @@ def test_p4_fixture_paged_matches_dense():
     assert rel.max() < fx["page_rel_tolerance"]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_window_one_returns_own_value_bitwise(dtype):
     """W = 1: each query sees only its own key, so the softmax has one weight
     e^0 = 1 and the output is that key's value row exactly."""
@@ -230,16 +232,17 @@ def test_logsumexp_combines_over_disjoint_key_ranges():
     np.testing.assert_allclose(comb, full_o, rtol=1e-12, atol=1e-13)
 
 
-def test_mla_equals_mqa_over_concatenated_key():
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mla_equals_mqa_over_concatenated_key(dtype):
     """ruDNN `DevicePlan::mla` passes the latent as key and value and adds a
     position term to the score: that is single-KV-head attention whose key is
     [latent | kpos] (width R+P), whose query is [q_abs | q_rope] and whose
     value is the latent (width R)."""
-    m = random_mla_batch(18, heads=4, r=32, p=8, page_size=8, q_counts=(1, 3, 1), max_len=60)
+    m = random_mla_batch(18, heads=4, r=32, p=8, page_size=8, q_counts=(1, 3, 1), max_len=60, dtype=dtype)
     out, lse = oracle.mla(m)
     k = np.concatenate([m.latent, m.kpos], axis=-1)
     q = np.concatenate([m.q_abs, m.q_rope], axis=-1)
-    b = PagedBatch("mqa", "bf16", m.seq_lens, m.cu_q, m.q_pos, m.block_table, m.page_size, m.num_pages,
+    b = PagedBatch("mqa", dtype, m.seq_lens, m.cu_q, m.q_pos, m.block_table, m.page_size, m.num_pages,
                    m.heads, 1, m.r + m.p, m.r, m.scale, m.causal, m.window, q, k, m.latent)
     out2, lse2 = oracle.attention(b)
     np.testing.assert_allclose(out, out2, rtol=1e-12, atol=1e-13)
@@ -282,7 +285,36 @@ def test_bf16_rounding_is_round_to_nearest_even():
     assert bits[3] == 0xC020 and bits[5] == 0x7F80 and bits[6] == 0x8000
 
 
-@pytest.mark.parametrize("dtype,page_size", [("bf16", 16), ("f32", 1), ("bf16", 64)])
+def test_f16_rounding_is_round_to_nearest_even():
+    """IEEE binary16: 10 fraction bits, so ulp(1) = 2^-10; the smallest
+    subnormal is 2^-24; values from 65520 up overflow to infinity."""
+    x = np.array([1.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -2.5, 65504.0, 65520.0, 2.0 ** -25, 3 * 2.0 ** -25,
+                  -0.0, np.inf], dtype=np.float32)
+    bits = f32_to_f16_bits(x)
+    assert [int(v) for v in bits] == [0x3C00, 0x3C00, 0x3C02, 0xC100, 0x7BFF, 0x7C00, 0x0000, 0x0002, 0x8000,
+                                      0x7C00]
+
+
+def test_oracle_f16_widening_is_ieee_binary16():
+    """The oracle's own binary16 decoding against the IEEE definition: hand
+    values (sign, exponent bias 15, subnormals m 2^-24, infinities, NaN), then
+    all 65536 patterns against numpy's float16 (a library routine)."""
+    table = {0x0000: 0.0, 0x8000: -0.0, 0x3C00: 1.0, 0xC000: -2.0, 0x3555: 0.333251953125, 0x7BFF: 65504.0,
+             0x0400: 2.0 ** -14, 0x03FF: 1023 * 2.0 ** -24, 0x0001: 2.0 ** -24, 0x8001: -(2.0 ** -24),
+             0x7C00: math.inf, 0xFC00: -math.inf, 0x3BFF: 1 - 2.0 ** -11, 0x4248: 3.140625}
+    got = oracle.widen(np.array(list(table), dtype=np.uint16), "f16")
+    for (bits, want), g in zip(table.items(), got):
+        assert g == want and math.copysign(1, g) == math.copysign(1, want), hex(bits)
+    assert np.isnan(oracle.widen(np.array([0x7E00, 0xFC01, 0x7C01], dtype=np.uint16), "f16")).all()
+    every = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(every, "f16")
+    ref = every.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan]) and np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("dtype,page_size", [("bf16", 16), ("f32", 1), ("bf16", 64), ("f16", 8)])
 def test_append_places_rows_at_their_positions(dtype, page_size):
     """Paged append (ruDNN paged_attention `DevicePlan::append`): read back in
     logical order through the dense view (numpy indexing, not the oracle's
