@@ -63,7 +63,8 @@ typedef enum pa_status {
 
 typedef enum pa_dtype {
   PA_F32 = 0, /* IEEE binary32 */
-  PA_BF16 = 1 /* bfloat16, raw 16-bit patterns; outputs rounded to nearest even */
+  PA_BF16 = 1, /* bfloat16, raw 16-bit patterns; outputs rounded to nearest even */
+  PA_F16 = 2   /* IEEE binary16; outputs rounded to nearest even */
 } pa_dtype;
 
 /*
@@ -187,7 +188,7 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
  * Paged GQA/MHA attention forward (ruDNN `DevicePlan::attention_into` /
  * `attention_into_split`).
  *
- *   dtype        PA_F32 or PA_BF16, the type of q, k_pool, v_pool and out
+ *   dtype        PA_F32, PA_BF16 or PA_F16, the type of q, k_pool, v_pool and out
  *   q            [Q, Hq, head_dim]
  *   k_pool       [num_pages, page_size, Hkv, head_dim]
  *   v_pool       [num_pages, page_size, Hkv, v_head_dim]
@@ -224,8 +225,8 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
  *   latent  [num_pages, page_size, 1, rank]
  *   kpos    [num_pages, page_size, 1, rope_dim]
  *   out     [Q, H, rank]        lse NULL or f32 [Q, H]
- *   rank    1..1024, rope_dim 1..256 (this build runs bf16 with H = 16,
- *           rank = 512, rope_dim = 64)
+ *   rank    1..1024, rope_dim 1..256 (this build runs bf16 and f16 with
+ *           H = 16, rank = 512, rope_dim = 64)
  *   scale   from the model's original query/key head size, not the latent
  *           rank (e.g. 1/sqrt(rank + rope_dim))
  *
@@ -248,7 +249,8 @@ const char* pa_status_string(int status);
  *
  *   k_pool[page, slot, h, :] = k_new[i, h, :]   v_pool[page, slot, h, :] = v_new[i, h, :]
  *
- *   dtype     PA_F32 or PA_BF16 (of all four tensors; rows are copied bit for bit)
+ *   dtype     PA_F32, PA_BF16 or PA_F16 (of all four tensors; rows are copied bit
+ *             for bit)
  *   k_new     [Q, heads, head_dim]       v_new [Q, heads, v_head_dim]
  *   k_pool    [num_pages, page_size, heads, head_dim], written in place
  *   v_pool    [num_pages, page_size, heads, v_head_dim], written in place

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
 PA_OK = 0
 PA_F32 = 0
 PA_BF16 = 1
+PA_F16 = 2
 STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_INVALID", -2: "PA_ERR_SHAPE", -3: "PA_ERR_PLAN", -4: "PA_ERR_UNSUPPORTED",
                 -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_OVERLAP", -7: "PA_ERR_RANGE", -8: "PA_ERR_HIP",
                 -9: "PA_ERR_DEVICE"}
@@ -224,6 +225,8 @@ def _dtype_code(t) -> int:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
+    if t.dtype == torch.float16:
+        return PA_F16
     raise ValueError(f"unsupported tensor dtype {t.dtype}")
 
 

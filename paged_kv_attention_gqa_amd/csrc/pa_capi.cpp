@@ -690,7 +690,7 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                      size_t workspace_bytes, void* event_after_main, void* stream) {
   if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
   if (plan->mla) return fail(PA_ERR_INVALID, "plan was made for MLA (use pa_mla_fwd)");
-  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
   if (!k_pool || !v_pool) return fail(PA_ERR_INVALID, "k_pool and v_pool are required");
   if (plan->Q > 0 && (!q || !out)) return fail(PA_ERR_INVALID, "q and out are required when there are queries");
   if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
@@ -752,7 +752,7 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
                void* workspace, size_t workspace_bytes, void* event_after_main, void* stream) {
   if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
   if (!plan->mla) return fail(PA_ERR_INVALID, "plan was made for GQA (use pa_attention_fwd)");
-  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
   if (!latent || !kpos) return fail(PA_ERR_INVALID, "latent and kpos are required");
   if (plan->Q > 0 && (!q_abs || !q_rope || !out))
     return fail(PA_ERR_INVALID, "q_abs, q_rope and out are required when there are queries");
@@ -814,7 +814,7 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
 int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const void* v_new, void* k_pool,
                  void* v_pool, int32_t head_dim, int32_t v_head_dim, void* stream) {
   if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
-  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
   if (!k_pool || !v_pool) return fail(PA_ERR_INVALID, "k_pool and v_pool are required");
   if (plan->Q > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID, "k_new and v_new are required when there are queries");
   if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)

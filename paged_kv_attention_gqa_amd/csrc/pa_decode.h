@@ -31,6 +31,10 @@ template <>
 struct Vec16<uint16_t> {
   static constexpr int kElems = 8;
 };
+template <>
+struct Vec16<_Float16> {
+  static constexpr int kElems = 8;
+};
 
 __device__ __forceinline__ uint4 load16(const void* base, uint64_t elem_off, int esize) {
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + elem_off * esize);
@@ -51,7 +55,7 @@ constexpr int kStreamLoad = 2;  // cache-policy operand of buffer loads: nt
 template <typename T>
 __device__ __forceinline__ void store_out(void* out, uint64_t idx, float v) {
   if constexpr (sizeof(T) == 2) {
-    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)(pack_bf16(v, 0.f) & 0xFFFFu);
+    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)(Pair16<T>::pack(v, 0.f) & 0xFFFFu);
   } else {
     reinterpret_cast<float*>(out)[idx] = v;
   }
@@ -70,10 +74,10 @@ __device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float acc = 0.f;
-      acc = dot2_bf16(qv[g].x, kv.x, acc);
-      acc = dot2_bf16(qv[g].y, kv.y, acc);
-      acc = dot2_bf16(qv[g].z, kv.z, acc);
-      acc = dot2_bf16(qv[g].w, kv.w, acc);
+      acc = Pair16<T>::dot2(qv[g].x, kv.x, acc);
+      acc = Pair16<T>::dot2(qv[g].y, kv.y, acc);
+      acc = Pair16<T>::dot2(qv[g].z, kv.z, acc);
+      acc = Pair16<T>::dot2(qv[g].w, kv.w, acc);
       s[g] = acc;
     }
   } else {
@@ -129,8 +133,8 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   for (int g = 0; g < G; ++g)
     qv[g] = load16(a.q, ((uint64_t)qi * a.hq + (uint64_t)kvh * G + g) * D + c * EPV, sizeof(T));
 
-  // l sums the weights as the P.V products used them (bf16-rounded for bf16
-  // data) and normalises the output; lx sums the unrounded weights for the
+  // l sums the weights as the P.V products used them (rounded to the storage
+  // type for 16-bit data) and normalises the output; lx sums the unrounded weights for the
   // logsumexp.
   float m[G], l[G], lx[G], o[G][EPV];
 #pragma unroll
@@ -216,11 +220,11 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const uint32_t pp = pack_bf16(s[u][g], s[u + 1][g]);
-          l[g] += bf16_lo(pp) + bf16_hi(pp);
+          const uint32_t pp = Pair16<T>::pack(s[u][g], s[u + 1][g]);
+          l[g] += Pair16<T>::lo(pp) + Pair16<T>::hi(pp);
           lx[g] += s[u][g] + s[u + 1][g];
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) o[g][e] = dot2_bf16(vp[e], pp, o[g][e]);
+          for (int e = 0; e < EPV; ++e) o[g][e] = Pair16<T>::dot2(vp[e], pp, o[g][e]);
         }
       }
     } else {

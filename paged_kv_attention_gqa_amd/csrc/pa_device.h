@@ -180,6 +180,41 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit storage types: bf16 travels as raw uint16_t patterns, IEEE binary16
+// (f16) as _Float16.  Pair16<T> works on two elements packed in one 32-bit
+// word, element 0 in the low half; conversions from float round to nearest
+// even.
+// ---------------------------------------------------------------------------
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+template <typename T>
+struct Pair16;
+
+template <>
+struct Pair16<uint16_t> {  // bf16
+  static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16(a, b); }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) { return dot2_bf16(a, b, c); }
+};
+
+template <>
+struct Pair16<_Float16> {  // f16
+  static __device__ __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
+  static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    float2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2_t));
+  }
+  // v_dot2_f32_f16: a.lo*b.lo + a.hi*b.hi + c with an fp32 accumulator
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+  }
+};
+
 // (lo16(a), lo16(b)) and (hi16(a), hi16(b)): the same dimension of two keys.
 __device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

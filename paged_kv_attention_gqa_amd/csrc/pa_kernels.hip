@@ -73,7 +73,7 @@ void mixed_kernel(KernelArgs a) {
   if (it.kind == kEmpty) return;
   if (it.kind == kPrefill) {
     if constexpr (MixedShape<T, D, G>::kMfma)
-      prefill_item<D, G>(a, it, smem);
+      prefill_item<T, D, G>(a, it, smem);
     else
       prefill_item_by_queries<T, D, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
   } else {
@@ -166,6 +166,7 @@ template <template <typename, int, int> class Sel>
 LaunchFn pick(int dtype, int d, int g) {
   if (dtype == 0) return pick_d<Sel, float>(d, g);
   if (dtype == 1) return pick_d<Sel, uint16_t>(d, g);
+  if (dtype == 2) return pick_d<Sel, _Float16>(d, g);
   return nullptr;
 }
 
@@ -226,13 +227,16 @@ int decode_waves(int g) {
 int mla_wgs_per_cu() { return 2; }
 
 bool mla_supported(int dtype, int h, int r, int p) {
-  return dtype == 1 && h == kMlaHeads && r == kMlaRank && p == kMlaRope;
+  return (dtype == 1 || dtype == 2) && h == kMlaHeads && r == kMlaRank && p == kMlaRope;
 }
 
 hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream) {
-  if (dtype != 1) return hipErrorInvalidValue;
+  if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
   if (a.n_wg > 0) {
-    hipLaunchKernelGGL((mla_kernel<uint16_t>), dim3(a.n_wg), dim3(kMlaWaves * kWave), 0, stream, a);
+    if (dtype == 1)
+      hipLaunchKernelGGL((mla_kernel<uint16_t>), dim3(a.n_wg), dim3(kMlaWaves * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((mla_kernel<_Float16>), dim3(a.n_wg), dim3(kMlaWaves * kWave), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -240,8 +244,9 @@ hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream) {
 
 hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream) {
-  if (dtype != 1) return hipErrorInvalidValue;
-  return launch_merge_t<uint16_t, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, stream);
+  if (dtype == 1) return launch_merge_t<uint16_t, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, stream);
+  if (dtype == 2) return launch_merge_t<_Float16, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, stream);
+  return hipErrorInvalidValue;
 }
 
 

@@ -8,7 +8,7 @@
 
 namespace pa {
 
-// dtype: 0 = f32, 1 = bf16.  d: head size.  g: query heads per KV head.
+// dtype: 0 = f32, 1 = bf16, 2 = f16.  d: head size.  g: query heads per KV head.
 bool gqa_supported(int dtype, int d, int g);
 bool prefill_supported(int dtype, int d, int g);
 // Main GQA launch over the a.n_items entries of a.items: decode-only, or one

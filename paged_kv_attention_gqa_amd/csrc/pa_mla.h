@@ -1,4 +1,4 @@
-// Absorbed-MLA decode body (bf16 MFMA): one query, all H = 16 heads, one
+// Absorbed-MLA decode body (16-bit MFMA, bf16 or f16): one query, all H = 16 heads, one
 // contiguous range of its visible keys.
 //
 // Definition followed: ruDNN 0.1.107 paged_attention/mod.rs `DevicePlan::mla`
@@ -8,7 +8,7 @@
 // softmax and masking of boostr 0.2.0-beta.2 `standard_attention_fwd` /
 // `build_attention_mask`.
 //
-// Per key the method reads R + P = 576 bf16 (1152 bytes) and does 16 x (576 +
+// Per key the method reads R + P = 576 16-bit elements (1152 bytes) and does 16 x (576 +
 // 512) multiply-adds: ~30 flops per byte, above what the fp32 vector units
 // sustain at HBM speed, so both products run on MFMA with the 16 heads as the
 // N dimension:
@@ -47,15 +47,25 @@ struct MlaSmem {
   static constexpr int kBytes = kMlaStages * kStage;             // 72 KB
 };
 
-__device__ __forceinline__ floatx4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b, const floatx4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+template <typename T>
+__device__ __forceinline__ floatx4_t mfma_16x16x32(const frag_t& a, const frag_t& b, const floatx4_t& c) {
+  if constexpr (__is_same(T, _Float16))
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+template <typename T>
 __device__ __forceinline__ floatx4_t mfma_16x16x16(const short4_t& a, const short4_t& b, const floatx4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  if constexpr (__is_same(T, _Float16))
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b), c,
+                                                 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Byte offset of 16-byte piece `piece` of key row `key` in a tile of WIDTH
-// bf16 per row.
+// 16-bit elements per row.
 template <int WIDTH>
 __device__ __forceinline__ int mla_off(int key, int piece) {
   return key * (WIDTH * 2) + ((piece ^ swz<WIDTH / 8>(key)) << 4);
@@ -84,14 +94,14 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   const uint16_t* kpos = reinterpret_cast<const uint16_t*>(a.kr);
 
   // q^T operands: lane (n, c) holds dims 32 ks + 8 c .. +7 of head n
-  bf16x8_t qa[KS_LAT], qp[KS_POS];
+  frag_t qa[KS_LAT], qp[KS_POS];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((uint64_t)qi * H + n) * R;
     const uint16_t* prow = reinterpret_cast<const uint16_t*>(a.qr) + ((uint64_t)qi * H + n) * P;
 #pragma unroll
-    for (int k = 0; k < KS_LAT; ++k) qa[k] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * k + 8 * c);
+    for (int k = 0; k < KS_LAT; ++k) qa[k] = *reinterpret_cast<const frag_t*>(qrow + 32 * k + 8 * c);
 #pragma unroll
-    for (int k = 0; k < KS_POS; ++k) qp[k] = *reinterpret_cast<const bf16x8_t*>(prow + 32 * k + 8 * c);
+    for (int k = 0; k < KS_POS; ++k) qp[k] = *reinterpret_cast<const frag_t*>(prow + 32 * k + 8 * c);
   }
   // The tile loads below are inline assembly that the compiler's wait-count
   // pass does not see; it would count only these query loads as outstanding
@@ -190,17 +200,17 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
 
     // S^T: lane (n, c) holds keys 4 c + r (r = 0..3) of head n; two
     // accumulator chains halve the dependent MFMA latency
-    bf16x8_t kf[KS_LAT + KS_POS];
+    frag_t kf[KS_LAT + KS_POS];
 #pragma unroll
-    for (int k = 0; k < KS_LAT; ++k) kf[k] = *reinterpret_cast<const bf16x8_t*>(ls + mla_off<R>(n, 4 * k + c));
+    for (int k = 0; k < KS_LAT; ++k) kf[k] = *reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * k + c));
 #pragma unroll
     for (int k = 0; k < KS_POS; ++k)
-      kf[KS_LAT + k] = *reinterpret_cast<const bf16x8_t*>(kps + mla_off<P>(n, 4 * k + c));
+      kf[KS_LAT + k] = *reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * k + c));
     floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int k = 0; k < KS_LAT; ++k) sc[k & 1] = mfma_16x16x32(kf[k], qa[k], sc[k & 1]);
+    for (int k = 0; k < KS_LAT; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[k], qa[k], sc[k & 1]);
 #pragma unroll
-    for (int k = 0; k < KS_POS; ++k) sc[k & 1] = mfma_16x16x32(kf[KS_LAT + k], qp[k], sc[k & 1]);
+    for (int k = 0; k < KS_POS; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[KS_LAT + k], qp[k], sc[k & 1]);
     floatx4_t s = sc[0] + sc[1];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -226,8 +236,8 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -sub));
-    const uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);
-    l += bf16_lo(w0) + bf16_hi(w0) + bf16_lo(w1) + bf16_hi(w1);
+    const uint32_t w0 = Pair16<T>::pack(p[0], p[1]), w1 = Pair16<T>::pack(p[2], p[3]);
+    l += Pair16<T>::lo(w0) + Pair16<T>::hi(w0) + Pair16<T>::lo(w1) + Pair16<T>::hi(w1);
     lx += (p[0] + p[1]) + (p[2] + p[3]);
     const short4_t pf = __builtin_bit_cast(short4_t, make_uint2(w0, w1));
 
@@ -242,7 +252,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       vf[b] = lds_read_tr16(ls + mla_off<R>(key, dim >> 3) + (dim & 7) * 2);
     }
 #pragma unroll
-    for (int b = 0; b < DB; ++b) o[b] = mfma_16x16x16(vf[b], pf, o[b]);
+    for (int b = 0; b < DB; ++b) o[b] = mfma_16x16x16<T>(vf[b], pf, o[b]);
   }
 
   // full row sums: the four k-groups of lanes hold different keys
@@ -256,8 +266,8 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       uint2 w;
-      w.x = pack_bf16(o[b][0] * inv, o[b][1] * inv);
-      w.y = pack_bf16(o[b][2] * inv, o[b][3] * inv);
+      w.x = Pair16<T>::pack(o[b][0] * inv, o[b][1] * inv);
+      w.y = Pair16<T>::pack(o[b][2] * inv, o[b][3] * inv);
       *reinterpret_cast<uint2*>(orow + 16 * b + 4 * c) = w;
     }
     if (a.lse && wave == 0 && c == 0) a.lse[(uint64_t)qi * H + n] = m * a.scale + logf(lx);

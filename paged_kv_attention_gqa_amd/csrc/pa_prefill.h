@@ -1,4 +1,4 @@
-// Chunked-prefill body (bf16 MFMA): up to 256 query rows -- 256/G consecutive
+// Chunked-prefill body (16-bit MFMA, bf16 or f16): up to 256 query rows -- 256/G consecutive
 // queries of one sequence times the G query heads of one KV head -- against
 // the keys the plan assigns to the tile, gathered page by page through the
 // block table.
@@ -8,7 +8,7 @@
 // `build_attention_mask`, softmax, weights times V, logsumexp) with queries at
 // absolute positions as ruDNN 0.1.107 `DevicePlan::attention` specifies for
 // prefill chunks.  Both products are dense contractions and run on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; softmax statistics are
+// v_mfma_f32_32x32x16_bf16 (_f16 for f16 data) with fp32 accumulation; softmax statistics are
 // fp32 and kept per query row in registers (online softmax across key tiles).
 //
 // Data flow per 64-key tile (three LDS stages, two tiles in flight, one
@@ -28,7 +28,9 @@
 
 namespace pa {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// Eight 16-bit elements of an MFMA operand.  The register type is the same
+// for bf16 and f16 data; mfma_* reinterpret it as the storage type T.
+typedef __bf16 frag_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
@@ -47,8 +49,13 @@ struct PrefillSmem {
   static constexpr int kBytes = kPrefillStages * kStage;
 };
 
-__device__ __forceinline__ floatx16_t mfma_32x32x16(const bf16x8_t& a, const bf16x8_t& b, const floatx16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+template <typename T>
+__device__ __forceinline__ floatx16_t mfma_32x32x16(const frag_t& a, const frag_t& b, const floatx16_t& c) {
+  if constexpr (__is_same(T, _Float16))
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -111,7 +118,7 @@ __device__ __forceinline__ int tile_off(int key, int piece) {
 // tiles; the loop body issues no other vector-memory loads (a per-tile
 // per-lane lookup would make the compiler drain the vector-memory counter
 // before every tile issue).
-template <int D, int G, bool UNIFORM>
+template <typename T, int D, int G, bool UNIFORM>
 __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const WorkItem& it, char* smem) {
   constexpr int NT = kPrefillTileKeys;
   constexpr int KS = D / 16;                         // MFMA k-steps of S^T (over head dims)
@@ -146,11 +153,11 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   const float c2 = a.scale_log2;
 
   // Q^T operand: lane (n, h) holds dims 16 ks + 8 h .. +7 of row n
-  bf16x8_t qf[KS];
+  frag_t qf[KS];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((uint64_t)qi * a.hq + head) * D;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qf[k] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k + 8 * h);
+    for (int k = 0; k < KS; ++k) qf[k] = *reinterpret_cast<const frag_t*>(qrow + 16 * k + 8 * h);
   }
   // The tile loads are inline assembly that the compiler's wait-count pass
   // does not see; it would count only these query loads as outstanding and,
@@ -294,17 +301,17 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     // K fragments run kAhead MFMAs ahead of their use (a small register ring)
     constexpr int kSteps = MB * KS, kAhead = 4;
     auto frag = [&](int i) {
-      return *reinterpret_cast<const bf16x8_t*>(ks + koff[i / MB] + (i % MB) * 32 * (D * 2));
+      return *reinterpret_cast<const frag_t*>(ks + koff[i / MB] + (i % MB) * 32 * (D * 2));
     };
-    bf16x8_t ring[kAhead];
+    frag_t ring[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) ring[i] = frag(i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
-      const bf16x8_t kf = ring[i % kAhead];
+      const frag_t kf = ring[i % kAhead];
       if (i + kAhead < kSteps) ring[i % kAhead] = frag(i + kAhead);
-      s[i % MB] = mfma_32x32x16(kf, qf[i / MB], s[i % MB]);
+      s[i % MB] = mfma_32x32x16<T>(kf, qf[i / MB], s[i % MB]);
       __builtin_amdgcn_sched_barrier(0);  // keep the read distance (the scheduler would shorten it)
     }
   };
@@ -347,10 +354,10 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     }
     return (m == -INFINITY ? 0.f : m) * c2;
   };
-  // P^T = 2^(S^T c - ref) rounded to bf16 (vector work only).  k-step kk
+  // P^T = 2^(S^T c - ref) rounded to the storage type (vector work only).  k-step kk
   // covers keys 16 kk .. +15; lane (n, h) feeds keys 16 kk + 8 (e/4) + 4 h +
   // e%4 (e = 0..7): elements 8 (kk % 2) + e of S^T block kk / 2.
-  auto weights = [&](const floatx16_t (&s)[MB], float sub, bf16x8_t (&pf)[NT / 16]) {
+  auto weights = [&](const floatx16_t (&s)[MB], float sub, frag_t (&pf)[NT / 16]) {
 #pragma unroll
     for (int kk = 0; kk < NT / 16; ++kk) {
       const int mb = kk >> 1, e0 = 8 * (kk & 1);
@@ -359,28 +366,28 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
       for (int j = 0; j < 4; ++j) {
         const float p0 = fast_exp2(__builtin_fmaf(s[mb][e0 + 2 * j], c2, -sub));
         const float p1 = fast_exp2(__builtin_fmaf(s[mb][e0 + 2 * j + 1], c2, -sub));
-        pw[j] = pack_bf16(p0, p1);
+        pw[j] = Pair16<T>::pack(p0, p1);
         l += p0 + p1;
       }
-      pf[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      pf[kk] = __builtin_bit_cast(frag_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     }
   };
   // O^T += V^T . P^T (matrix work only): the V^T rows of k-step kk's keys by
   // two transposed reads (4 keys each) of dims 32 b + 16 (lane/16 % 2) +
   // lane % 16 (offsets voff, plus 16 rows per k-step).
-  auto pv = [&](const char* vs, const bf16x8_t (&pf)[NT / 16]) {
+  auto pv = [&](const char* vs, const frag_t (&pf)[NT / 16]) {
 #pragma unroll
     for (int kk = 0; kk < NT / 16; ++kk) {
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
         const short4_t v0 = lds_read_tr16(vs + voff[b][0] + kk * 16 * (D * 2));
         const short4_t v1 = lds_read_tr16(vs + voff[b][1] + kk * 16 * (D * 2));
-        const bf16x8_t vf = __builtin_bit_cast(
-            bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
+        const frag_t vf = __builtin_bit_cast(
+            frag_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
-        o[b] = mfma_32x32x16(vf, pf[kk], o[b]);
+        o[b] = mfma_32x32x16<T>(vf, pf[kk], o[b]);
       }
     }
   };
@@ -411,7 +418,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   page_next = page_of(t_first + (NS - 2) * NT);
 
   floatx16_t s[MB];
-  bf16x8_t pf[NT / 16];
+  frag_t pf[NT / 16];
   auto sync = [&](int j) {
     wait_tiles(min(ntiles - 1 - j, 1));  // tile j has landed, j + 1 may be in flight
     __syncthreads();                     // ... for every wave; tile j - 2 is no longer read
@@ -448,19 +455,20 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     for (int k = 0; k < 4; ++k) {
       // dims 32 b + 8 k + 4 h + 0..3
       uint2 w;
-      w.x = pack_bf16(o[b][4 * k + 0] * inv, o[b][4 * k + 1] * inv);
-      w.y = pack_bf16(o[b][4 * k + 2] * inv, o[b][4 * k + 3] * inv);
+      w.x = Pair16<T>::pack(o[b][4 * k + 0] * inv, o[b][4 * k + 1] * inv);
+      w.y = Pair16<T>::pack(o[b][4 * k + 2] * inv, o[b][4 * k + 3] * inv);
       *reinterpret_cast<uint2*>(orow + 32 * b + 8 * k + 4 * h) = w;
     }
   if (a.lse && h == 0) a.lse[(uint64_t)qi * a.hq + head] = m * a.scale + logf(l);
 }
 
-template <int D, int G>
+template <typename T, int D, int G>
 __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem& it, char* smem) {
+  static_assert(sizeof(T) == 2, "the MFMA tile runs on 16-bit data");
   if (a.page_shift >= 4)
-    prefill_item_impl<D, G, true>(a, it, smem);
+    prefill_item_impl<T, D, G, true>(a, it, smem);
   else
-    prefill_item_impl<D, G, false>(a, it, smem);
+    prefill_item_impl<T, D, G, false>(a, it, smem);
 }
 
 // A prefill tile handled one query at a time by the decode body (f32 data and
