@@ -196,7 +196,8 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
  *   lse          NULL or f32 [Q, Hq]: natural-log logsumexp of the scaled,
  *                masked scores of each row
  *   head_dim     D, 1..1024; v_head_dim Dv, 1..1024 (this build runs
- *                D = Dv in {64, 128, 256}; others give PA_ERR_UNSUPPORTED)
+ *                D = Dv in {64, 128, 256} and D = 192 with Dv = 128; other
+ *                pairs give PA_ERR_UNSUPPORTED)
  *   scale        finite and > 0 (e.g. 1/sqrt(D))
  *   workspace    f32 scratch of >= pa_plan_workspace_bytes(plan, v_head_dim)
  *                bytes, 256-byte aligned; may be NULL when that size is 0

@@ -652,7 +652,7 @@ static int launch_common(FwdCall& c, bool is_mla) {
   if (is_mla) {
     e = pa::launch_mla_main(c.dtype, c.args, c.stream);
   } else {
-    e = pa::launch_gqa_main(c.dtype, c.d, p->group(), p->n_prefill > 0, c.args, c.stream);
+    e = pa::launch_gqa_main(c.dtype, c.d, c.dv, p->group(), p->n_prefill > 0, c.args, c.stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (c.event_after_main) {
@@ -661,7 +661,7 @@ static int launch_common(FwdCall& c, bool is_mla) {
   }
   if (!p->merges.empty()) {
     e = is_mla ? pa::launch_mla_merge(c.dtype, c.args, p->d_merges, (int)p->merges.size(), c.stream)
-               : pa::launch_gqa_merge(c.dtype, c.d, p->group(), c.args, p->d_merges, (int)p->merges.size(),
+               : pa::launch_gqa_merge(c.dtype, c.d, c.dv, p->group(), c.args, p->d_merges, (int)p->merges.size(),
                                       c.stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
@@ -703,11 +703,12 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   rc = check_workspace(plan, v_head_dim, workspace, workspace_bytes, &ws_o, &ws_ml, &need);
   if (rc != PA_OK) return rc;
   const int G = plan->group();
-  if (head_dim != v_head_dim) return fail(PA_ERR_UNSUPPORTED, "this build needs D == Dv (got %d, %d)", head_dim, v_head_dim);
-  if (plan->n_decode > 0 && !pa::gqa_supported(dtype, head_dim, G))
-    return fail(PA_ERR_UNSUPPORTED, "no decode kernel for dtype %d, D=%d, G=%d", dtype, head_dim, G);
-  if (plan->n_prefill > 0 && !pa::prefill_supported(dtype, head_dim, G))
-    return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, D=%d, G=%d", dtype, head_dim, G);
+  if (plan->n_decode > 0 && !pa::gqa_supported(dtype, head_dim, v_head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "no decode kernel for dtype %d, D=%d, Dv=%d, G=%d", dtype, head_dim, v_head_dim,
+                G);
+  if (plan->n_prefill > 0 && !pa::prefill_supported(dtype, head_dim, v_head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, D=%d, Dv=%d, G=%d", dtype, head_dim,
+                v_head_dim, G);
   const size_t es = dtype == PA_F32 ? 4 : 2;
   const size_t slots = (size_t)plan->num_pages * plan->ps * plan->hkv;
   std::vector<Extent> outs = {{out, (size_t)plan->Q * plan->hq * v_head_dim * es, "out"},

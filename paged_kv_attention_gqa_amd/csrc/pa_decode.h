@@ -21,36 +21,98 @@
 
 namespace pa {
 
-template <typename T>
-struct Vec16;  // one 16-byte load
-template <>
-struct Vec16<float> {
-  static constexpr int kElems = 4;
-};
-template <>
-struct Vec16<uint16_t> {
-  static constexpr int kElems = 8;
-};
-template <>
-struct Vec16<_Float16> {
-  static constexpr int kElems = 8;
+// Lane layout of a decode wave for K rows of D elements and V rows of DV
+// elements: a key row is spread over kLanes lanes (the smallest power of two
+// that keeps a lane's K share within one 16-byte load), each holding kKWords
+// 32-bit words of K and kVWords of V.  D = DV = 128 in bf16: 16 lanes x 16
+// bytes of K and of V; D = 192, DV = 128 in bf16: 32 lanes x 12 bytes of K and
+// 8 bytes of V.
+constexpr int decode_lanes(int row_bytes) {
+  int p = 1;
+  while (row_bytes > 16 * p) p *= 2;
+  return p;
+}
+template <typename T, int D, int DV>
+struct DecodeLayout {
+  static constexpr int kLanes = decode_lanes(D * (int)sizeof(T));
+  static constexpr int kKWords = D * (int)sizeof(T) / kLanes / 4;
+  static constexpr int kVWords = DV * (int)sizeof(T) / kLanes / 4;
+  static constexpr int kKElems = D / kLanes;
+  static constexpr int kVElems = DV / kLanes;
+  static_assert(kLanes <= kWave && D % kLanes == 0 && DV % kLanes == 0, "unsupported head sizes");
+  static_assert(kKWords * kLanes * 4 == D * (int)sizeof(T) && kVWords * kLanes * 4 == DV * (int)sizeof(T),
+                "a lane's share of a row must be whole 32-bit words");
+  static_assert(kKWords >= 1 && kVWords >= 1 && kVWords <= 8, "unsupported head sizes");
 };
 
-__device__ __forceinline__ uint4 load16(const void* base, uint64_t elem_off, int esize) {
-  return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + elem_off * esize);
+template <int N>
+struct Words {
+  uint32_t w[N];
+};
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// N words at p (4-byte aligned; 16-byte aligned when N is a multiple of 4,
+// 8-byte aligned when N == 2).  NT: non-temporal ("nt") loads.
+template <int N, bool NT>
+__device__ __forceinline__ Words<N> load_words(const char* p) {
+  Words<N> r;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p) + i;
+      const u32x4_t v = NT ? __builtin_nontemporal_load(q) : *q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.w[4 * i + j] = v[j];
+    }
+  } else if constexpr (N == 2) {
+    const u32x2_t* q = reinterpret_cast<const u32x2_t*>(p);
+    const u32x2_t v = NT ? __builtin_nontemporal_load(q) : *q;
+    r.w[0] = v[0];
+    r.w[1] = v[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(p) + i;
+      r.w[i] = NT ? __builtin_nontemporal_load(q) : *q;
+    }
+  }
+  return r;
 }
 
 // K/V rows a decode item reads once: non-temporal ("nt") loads.  Measured on
 // MI355X: streaming reads reach ~7.0 TB/s with nt against ~6.2 TB/s without,
 // and the decode kernel gained 11%.
 constexpr float kDecodeLazyLog2 = 8.f;  // weights may reach 2^8 before the reference max moves
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16_stream(const void* base, uint64_t elem_off, int esize) {
-  return __builtin_bit_cast(
-      uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) + elem_off * esize)));
-}
 constexpr int kStreamLoad = 2;  // cache-policy operand of buffer loads: nt
+
+// N words from a buffer resource at (voffset + soffset) bytes, nt.
+template <int N>
+__device__ __forceinline__ Words<N> buffer_words(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  Words<N> r;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16 * i, soff,
+                                                                                           kStreamLoad));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.w[4 * i + j] = v[j];
+    }
+  } else if constexpr (N == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(rsrc, voff, soff, kStreamLoad);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) r.w[j] = (uint32_t)v[j];
+  } else if constexpr (N == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, kStreamLoad);
+    r.w[0] = (uint32_t)v[0];
+    r.w[1] = (uint32_t)v[1];
+  } else {
+    static_assert(N == 1, "unsupported chunk");
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, soff, kStreamLoad);
+  }
+  return r;
+}
 
 template <typename T>
 __device__ __forceinline__ void store_out(void* out, uint64_t idx, float v) {
@@ -68,25 +130,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base) {
 }
 
 // Scores of G heads against one key chunk held by this lane.
-template <typename T, int G>
-__device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& kv, float (&s)[G]) {
+template <typename T, int G, int KW>
+__device__ __forceinline__ void chunk_scores(const Words<KW> (&qv)[G], const Words<KW>& kv, float (&s)[G]) {
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float acc = 0.f;
-      acc = Pair16<T>::dot2(qv[g].x, kv.x, acc);
-      acc = Pair16<T>::dot2(qv[g].y, kv.y, acc);
-      acc = Pair16<T>::dot2(qv[g].z, kv.z, acc);
-      acc = Pair16<T>::dot2(qv[g].w, kv.w, acc);
+#pragma unroll
+      for (int j = 0; j < KW; ++j) acc = Pair16<T>::dot2(qv[g].w[j], kv.w[j], acc);
       s[g] = acc;
     }
   } else {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float acc = __uint_as_float(qv[g].x) * __uint_as_float(kv.x);
-      acc = fmaf(__uint_as_float(qv[g].y), __uint_as_float(kv.y), acc);
-      acc = fmaf(__uint_as_float(qv[g].z), __uint_as_float(kv.z), acc);
-      acc = fmaf(__uint_as_float(qv[g].w), __uint_as_float(kv.w), acc);
+      float acc = __uint_as_float(qv[g].w[0]) * __uint_as_float(kv.w[0]);
+#pragma unroll
+      for (int j = 1; j < KW; ++j) acc = fmaf(__uint_as_float(qv[g].w[j]), __uint_as_float(kv.w[j]), acc);
       s[g] = acc;
     }
   }
@@ -98,18 +157,23 @@ __device__ __forceinline__ void chunk_scores(const uint4 (&qv)[G], const uint4& 
 // head are combined through LDS at the end.  With HW = NW every wave walks the
 // item's whole key range for its own head, and the waves together read whole
 // [Hkv, D] slot rows of each page at the same time.
-// smem must hold NW * G * (D + 3) floats.
+// K rows hold D elements, V rows DV (DecodeLayout gives the lane shares).
+// smem must hold NW * G * (DV + 3) floats.
 // tid: the thread index (threadIdx.x); callers that run several items in a
 // loop pass a copy the compiler cannot see through, so that per-lane values
 // are recomputed per item instead of being kept live across the loop.
-template <typename T, int D, int G, int NW, int U>
+template <typename T, int D, int DV, int G, int NW, int U>
 __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem& it, float* smem,
                                             int tid = threadIdx.x, int hw_shift = 0) {
-  constexpr int EPV = Vec16<T>::kElems;  // elements per 16-byte chunk
-  constexpr int LPT = D / EPV;           // lanes per key row
+  using Lay = DecodeLayout<T, D, DV>;
+  constexpr int LPT = Lay::kLanes;       // lanes per key row
+  constexpr int KW = Lay::kKWords;       // 32-bit words of K per lane and key
+  constexpr int VW = Lay::kVWords;       // 32-bit words of V per lane and key
+  constexpr int EK = Lay::kKElems;       // K elements per lane and key
+  constexpr int EV = Lay::kVElems;       // V elements (output dims) per lane
   constexpr int TPW = kWave / LPT;       // keys per wave-wide load
   constexpr int BLK = U * TPW;           // keys per wave per block
-  static_assert(D % EPV == 0 && LPT <= kWave && kWave % LPT == 0, "unsupported head size");
+  constexpr int SZ = (int)sizeof(T);
   static_assert(U % 2 == 0, "keys are processed in pairs");
   static_assert(NW > 1, "waves combine through LDS");
 
@@ -125,37 +189,45 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   const int tb = it.tok_begin, te = it.tok_end;
   const int ps = 1 << a.page_shift;
   const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
-  const uint64_t row_stride = (uint64_t)a.hkv * D;  // elements between consecutive slots
+  const uint64_t krow = (uint64_t)a.hkv * D;   // K elements between consecutive slots
+  const uint64_t vrow = (uint64_t)a.hkv * DV;  // V elements between consecutive slots
 
   // This lane's chunk of the G query rows of the group.
-  uint4 qv[G];
+  Words<KW> qv[G];
 #pragma unroll
   for (int g = 0; g < G; ++g)
-    qv[g] = load16(a.q, ((uint64_t)qi * a.hq + (uint64_t)kvh * G + g) * D + c * EPV, sizeof(T));
+    qv[g] = load_words<KW, false>(reinterpret_cast<const char*>(a.q) +
+                                  (((uint64_t)qi * a.hq + (uint64_t)kvh * G + g) * D + c * EK) * SZ);
 
   // l sums the weights as the P.V products used them (rounded to the storage
   // type for 16-bit data) and normalises the output; lx sums the unrounded weights for the
   // logsumexp.
-  float m[G], l[G], lx[G], o[G][EPV];
+  float m[G], l[G], lx[G], o[G][EV];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
     lx[g] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) o[g][e] = 0.f;
+    for (int e = 0; e < EV; ++e) o[g][e] = 0.f;
   }
 
   // Key slot u of a block starting at B: rows take consecutive key pairs.
   auto key_of = [&](int B, int u) { return B + 2 * ((u >> 1) * TPW + r) + (u & 1); };
-  auto slot_offset = [&](int page, int tc) -> uint64_t {
-    return ((uint64_t)page * ps + (tc & (ps - 1))) * row_stride + (uint64_t)kvh * D + c * EPV;
+  // byte addresses of this lane's K and V chunks of key tc in pool page `page`
+  auto k_addr = [&](int page, int tc) {
+    return reinterpret_cast<const char*>(a.k) +
+           (((uint64_t)page * ps + (tc & (ps - 1))) * krow + (uint64_t)kvh * D + c * EK) * SZ;
+  };
+  auto v_addr = [&](int page, int tc) {
+    return reinterpret_cast<const char*>(a.v) +
+           (((uint64_t)page * ps + (tc & (ps - 1))) * vrow + (uint64_t)kvh * DV + c * EV) * SZ;
   };
 
   // Scores, online softmax and P.V of one block held in kr / vr.  Keys
   // outside [tb, te) were loaded from a clamped in-range key (every load stays
   // inside the sequence's referenced pages, no branches) and are masked here.
-  auto compute_block = [&](int B, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+  auto compute_block = [&](int B, const Words<KW> (&kr)[U], const Words<VW> (&vr)[U]) {
     bool valid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -166,7 +238,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
     // independent DPP operations fill each other's hazard slots)
     float s[U][G];
 #pragma unroll
-    for (int u = 0; u < U; ++u) chunk_scores<T, G>(qv, kr[u], s[u]);
+    for (int u = 0; u < U; ++u) chunk_scores<T, G, KW>(qv, kr[u], s[u]);
     group_sum_all<LPT, U * G>(&s[0][0]);
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -196,7 +268,7 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
         l[g] *= alpha;
         lx[g] *= alpha;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) o[g][e] *= alpha;
+        for (int e = 0; e < EV; ++e) o[g][e] *= alpha;
       }
     }
 #pragma unroll
@@ -210,13 +282,11 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int u = 0; u < U; u += 2) {
-        const uint32_t v0[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
-        const uint32_t v1[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
-        uint32_t vp[EPV];
+        uint32_t vp[EV];  // (key u, key u + 1) pairs of each output dim
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vp[2 * j] = interleave_lo(v0[j], v1[j]);
-          vp[2 * j + 1] = interleave_hi(v0[j], v1[j]);
+        for (int j = 0; j < VW; ++j) {
+          vp[2 * j] = interleave_lo(vr[u].w[j], vr[u + 1].w[j]);
+          vp[2 * j + 1] = interleave_hi(vr[u].w[j], vr[u + 1].w[j]);
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -224,20 +294,18 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
           l[g] += Pair16<T>::lo(pp) + Pair16<T>::hi(pp);
           lx[g] += s[u][g] + s[u + 1][g];
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) o[g][e] = Pair16<T>::dot2(vp[e], pp, o[g][e]);
+          for (int e = 0; e < EV; ++e) o[g][e] = Pair16<T>::dot2(vp[e], pp, o[g][e]);
         }
       }
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float vf[4] = {__uint_as_float(vr[u].x), __uint_as_float(vr[u].y), __uint_as_float(vr[u].z),
-                             __uint_as_float(vr[u].w)};
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           l[g] += s[u][g];
           lx[g] += s[u][g];
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) o[g][e] = fmaf(s[u][g], vf[e], o[g][e]);
+          for (int e = 0; e < EV; ++e) o[g][e] = fmaf(s[u][g], __uint_as_float(vr[u].w[e]), o[g][e]);
         }
       }
     }
@@ -261,32 +329,37 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
     const int B0 = tstart + kpart * BLK;
     const int nb = B0 < te ? (te - 1 - B0) / step + 1 : 0;           // blocks with B < te
     const int nfull = B0 + BLK <= te ? (te - BLK - B0) / step + 1 : 0;  // blocks with B + BLK <= te
-    const uint32_t rs2 = (uint32_t)(row_stride * sizeof(T));  // bytes between consecutive slots
-    const char* kbase = reinterpret_cast<const char*>(a.k) + (uint64_t)kvh * D * sizeof(T);
-    const char* vbase = reinterpret_cast<const char*>(a.v) + (uint64_t)kvh * D * sizeof(T);
-    uint32_t lane_off[U];  // byte offset of this lane's chunk of key u, from the block's first slot
+    const uint32_t ks2 = (uint32_t)(krow * SZ), vs2 = (uint32_t)(vrow * SZ);  // bytes between consecutive slots
+    const char* kbase = reinterpret_cast<const char*>(a.k) + (uint64_t)kvh * D * SZ;
+    const char* vbase = reinterpret_cast<const char*>(a.v) + (uint64_t)kvh * DV * SZ;
+    // byte offsets of this lane's chunks of key u, from the block's first slot
+    uint32_t klane[U], vlane[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) lane_off[u] = (uint32_t)(key_of(0, u) * rs2 + c * 16);
+    for (int u = 0; u < U; ++u) {
+      klane[u] = (uint32_t)(key_of(0, u) * ks2 + c * KW * 4);
+      vlane[u] = (uint32_t)(key_of(0, u) * vs2 + c * VW * 4);
+    }
     const int last_page = (te - 1) >> a.page_shift;
     for (int w0 = 0; w0 < nb; w0 += kWave) {
       const int pv = bt[min((B0 + (w0 + lane) * step) >> a.page_shift, last_page)];
       // buffer loads: the page base in a scalar resource, the slot row as a
       // scalar offset, this lane's chunk as a fixed vector offset (no per-load
       // address arithmetic, no address registers next to in-flight loads)
-      auto load_full = [&](int k, uint4 (&kr)[U], uint4 (&vr)[U]) {
+      auto load_full = [&](int k, Words<KW> (&kr)[U], Words<VW> (&vr)[U]) {
         const int B = B0 + k * step;
-        const uint64_t pg = (uint64_t)__builtin_amdgcn_readlane(pv, k - w0) * ps * rs2;
-        const uint32_t soff = (uint32_t)(B & (ps - 1)) * rs2;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + pg), rv = make_rsrc(vbase + pg);
+        const uint64_t pg = (uint64_t)__builtin_amdgcn_readlane(pv, k - w0) * ps;
+        const uint32_t slot = (uint32_t)(B & (ps - 1));
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + pg * ks2), rv = make_rsrc(vbase + pg * vs2);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off[u], soff, kStreamLoad));
-          vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off[u], soff, kStreamLoad));
+          kr[u] = buffer_words<KW>(rk, klane[u], slot * ks2);
+          vr[u] = buffer_words<VW>(rv, vlane[u], slot * vs2);
         }
       };
       const int kend = min(nfull, w0 + kWave);  // full blocks of this window: w0 .. kend - 1
       if (w0 < kend) {
-        uint4 ka[U], va[U], kb[U], vb[U];
+        Words<KW> ka[U], kb[U];
+        Words<VW> va[U], vb[U];
         load_full(w0, ka, va);
         int k = w0;
         while (true) {
@@ -303,12 +376,13 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
       if (nfull < nb && nfull < w0 + kWave) {  // the wave's partial last block (k = nfull) is in this window
         const int B = B0 + nfull * step;
         const int page = __builtin_amdgcn_readlane(pv, nfull - w0);  // B and te - 1 share this page
-        uint4 kr[U], vr[U];
+        Words<KW> kr[U];
+        Words<VW> vr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const uint64_t off = slot_offset(page, min(key_of(B, u), te - 1));
-          kr[u] = load16_stream(a.k, off, sizeof(T));
-          vr[u] = load16_stream(a.v, off, sizeof(T));
+          const int tc = min(key_of(B, u), te - 1);
+          kr[u] = load_words<KW, true>(k_addr(page, tc));
+          vr[u] = load_words<VW, true>(v_addr(page, tc));
         }
         compute_block(B, kr, vr);
       }
@@ -318,12 +392,13 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
       int pg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) pg[u] = bt[min(max(key_of(B, u), tb), te - 1) >> a.page_shift];
-      uint4 kr[U], vr[U];
+      Words<KW> kr[U];
+      Words<VW> vr[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint64_t off = slot_offset(pg[u], min(max(key_of(B, u), tb), te - 1));
-        kr[u] = load16_stream(a.k, off, sizeof(T));
-        vr[u] = load16_stream(a.v, off, sizeof(T));
+        const int tc = min(max(key_of(B, u), tb), te - 1);
+        kr[u] = load_words<KW, true>(k_addr(pg[u], tc));
+        vr[u] = load_words<VW, true>(v_addr(pg[u], tc));
       }
       compute_block(B, kr, vr);
     }
@@ -339,17 +414,17 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
     l[g] = column_sum<LPT>(l[g] * f);
     lx[g] = column_sum<LPT>(lx[g] * f);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) o[g][e] = column_sum<LPT>(o[g][e] * f);
+    for (int e = 0; e < EV; ++e) o[g][e] = column_sum<LPT>(o[g][e] * f);
   }
 
-  // combine the NW waves through LDS: [wave][g][D] sums, then [wave][g] (m, l, lx)
+  // combine the NW waves through LDS: [wave][g][DV] sums, then [wave][g] (m, l, lx)
   float* so = smem;
-  float* sml = smem + NW * G * D;
+  float* sml = smem + NW * G * DV;
   if (r == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) so[(wave * G + g) * D + c * EPV + e] = o[g][e];
+      for (int e = 0; e < EV; ++e) so[(wave * G + g) * DV + c * EV + e] = o[g][e];
       if (c == 0) {
         sml[(wave * G + g) * 3 + 0] = m[g];
         sml[(wave * G + g) * 3 + 1] = l[g];
@@ -361,8 +436,8 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
 
   // thread x finalises outputs (head, g, d) = x, x + blockDim, ... of the
   // item's HW heads, combining the waves w = head + j * HW
-  for (int idx = tid; idx < (G * D << hw_shift); idx += NW * kWave) {
-    const int hs = idx / (G * D), g = idx / D % G, d = idx % D;
+  for (int idx = tid; idx < (G * DV << hw_shift); idx += NW * kWave) {
+    const int hs = idx / (G * DV), g = idx / DV % G, d = idx % DV;
     float M = -INFINITY;
     for (int w = hs; w < NW; w += 1 << hw_shift) M = fmaxf(M, sml[(w * G + g) * 3]);
     const float mu = (M == -INFINITY) ? 0.f : M;
@@ -371,15 +446,15 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
       const float f = fast_exp2((sml[(w * G + g) * 3] - mu) * a.scale_log2);
       L += sml[(w * G + g) * 3 + 1] * f;
       LX += sml[(w * G + g) * 3 + 2] * f;
-      O += so[(w * G + g) * D + d] * f;
+      O += so[(w * G + g) * DV + d] * f;
     }
     const int h = (it.kvh + hs) * G + g;
     if (it.slot < 0) {
-      store_out<T>(a.out, ((uint64_t)qi * a.hq + h) * D + d, O / L);
+      store_out<T>(a.out, ((uint64_t)qi * a.hq + h) * DV + d, O / L);
       if (a.lse && d == 0) a.lse[(uint64_t)qi * a.hq + h] = M * a.scale + logf(LX);
     } else {
       const uint64_t sl = (uint64_t)(it.slot + hs) * G + g;
-      a.ws_o[sl * D + d] = O;
+      a.ws_o[sl * DV + d] = O;
       if (d == 0) {
         a.ws_ml[sl * 3 + 0] = M * a.scale_log2;
         a.ws_ml[sl * 3 + 1] = L;
@@ -398,10 +473,10 @@ constexpr int kMergeUnroll = 16;
 
 // The (g, d) outputs of a row are spread over `chunks` workgroups; this one
 // takes outputs chunk, chunk + chunks, ... in units of blockDim.
-template <typename T, int D, int G>
+template <typename T, int DV, int G>
 __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& mi, int chunk, int chunks) {
-  for (int idx = chunk * blockDim.x + threadIdx.x; idx < G * D; idx += chunks * blockDim.x) {
-    const int g = idx / D, d = idx % D;
+  for (int idx = chunk * blockDim.x + threadIdx.x; idx < G * DV; idx += chunks * blockDim.x) {
+    const int g = idx / DV, d = idx % DV;
     float M = -INFINITY, L = 0.f, LX = 0.f, O = 0.f;
     for (int j0 = 0; j0 < mi.nsplit; j0 += kMergeUnroll) {
       float mj[kMergeUnroll], lj[kMergeUnroll], lxj[kMergeUnroll], oj[kMergeUnroll];
@@ -412,7 +487,7 @@ __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& 
         mj[u] = a.ws_ml[sl * 3];
         lj[u] = a.ws_ml[sl * 3 + 1];
         lxj[u] = a.ws_ml[sl * 3 + 2];
-        oj[u] = a.ws_o[sl * D + d];
+        oj[u] = a.ws_o[sl * DV + d];
         if (j >= mi.nsplit) mj[u] = -INFINITY;
       }
       float Mn = M;
@@ -432,7 +507,7 @@ __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& 
       M = Mn;
     }
     const int h = mi.kvh * G + g;
-    store_out<T>(a.out, ((uint64_t)mi.q * a.hq + h) * D + d, O / L);
+    store_out<T>(a.out, ((uint64_t)mi.q * a.hq + h) * DV + d, O / L);
     if (a.lse && d == 0) a.lse[(uint64_t)mi.q * a.hq + h] = (M + log2f(LX)) * 0.69314718055994530942f;
   }
 }

@@ -38,11 +38,11 @@ struct DecodeShape {
   static constexpr int kWgsPerCu = Occupancy<G>::kDecode * 4 / kWaves;
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 __global__ __launch_bounds__(DecodeShape<G>::kWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kDecode)))
 void decode_kernel(KernelArgs a) {
   constexpr int NW = DecodeShape<G>::kWaves;
-  __shared__ float smem[NW * G * (D + 3)];
+  __shared__ float smem[NW * G * (DV + 3)];
   const int first = a.wg_first[blockIdx.x], last = a.wg_first[blockIdx.x + 1];
   int tid = threadIdx.x;
   for (int i = first; i < last; ++i) {
@@ -50,34 +50,35 @@ void decode_kernel(KernelArgs a) {
     if (it.kind == kEmpty) continue;
     if (i > first) __syncthreads();  // the previous item's waves are done with the LDS
     asm volatile("" : "+v"(tid));    // per-lane values are recomputed per item, not kept live
-    decode_item<T, D, G, NW, DecodeUnroll<G>::kValue>(a, it, smem, tid, a.heads_shift);
+    decode_item<T, D, DV, G, NW, DecodeUnroll<G>::kValue>(a, it, smem, tid, a.heads_shift);
   }
 }
 
 // One launch for plans with prefill tiles: decode items and prefill tiles
 // share the grid (packed decode + chunked prefill in one dispatch).
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 struct MixedShape {
-  static constexpr bool kMfma = sizeof(T) == 2 && (D == 64 || D == 128) && G <= kPrefillRows;
-  static constexpr int kDecodeBytes = kPrefillWaves * G * (D + 3) * 4;
+  static constexpr bool kMfma = sizeof(T) == 2 && D == DV && (D == 64 || D == 128) && G <= kPrefillRows;
+  static constexpr int kDecodeBytes = kPrefillWaves * G * (DV + 3) * 4;
   static constexpr int kPrefillBytes = kMfma ? PrefillSmem<(D <= 128 ? D : 128)>::kBytes : 0;
   static constexpr int kBytes = kDecodeBytes > kPrefillBytes ? kDecodeBytes : kPrefillBytes;
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 __global__ __launch_bounds__(kPrefillWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kMixed)))
 void mixed_kernel(KernelArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[MixedShape<T, D, G>::kBytes];
+  __shared__ __attribute__((aligned(16))) char smem[MixedShape<T, D, DV, G>::kBytes];
   // plans with prefill tiles run one item per workgroup (wg_first[b] = b)
   const WorkItem it = a.items[blockIdx.x];
   if (it.kind == kEmpty) return;
   if (it.kind == kPrefill) {
-    if constexpr (MixedShape<T, D, G>::kMfma)
+    if constexpr (MixedShape<T, D, DV, G>::kMfma)
       prefill_item<T, D, G>(a, it, smem);
     else
-      prefill_item_by_queries<T, D, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
+      prefill_item_by_queries<T, D, DV, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it,
+                                                                                  reinterpret_cast<float*>(smem));
   } else {
-    decode_item<T, D, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
+    decode_item<T, D, DV, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it, reinterpret_cast<float*>(smem));
   }
 }
 
@@ -99,21 +100,21 @@ __global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_e
 
 // grid: (split rows, chunks of 256 outputs per row)
 constexpr int kMergeThreads = 256;
-template <typename T, int D, int G>
+template <typename T, int DV, int G>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelArgs a, const MergeItem* merges) {
   const MergeItem mi = merges[blockIdx.x];
-  merge_row<T, D, G>(a, mi, blockIdx.y, gridDim.y);
+  merge_row<T, DV, G>(a, mi, blockIdx.y, gridDim.y);
 }
 
 namespace {
 
 using LaunchFn = hipError_t (*)(const KernelArgs&, int, const MergeItem*, int, hipStream_t);
 
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 hipError_t launch_decode_t(const KernelArgs& a, int n_wg, const MergeItem* merges, int n_merges,
                            hipStream_t stream) {
   if (n_wg > 0) {
-    hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(n_wg), dim3(DecodeShape<G>::kWaves * kWave), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, DV, G>), dim3(n_wg), dim3(DecodeShape<G>::kWaves * kWave), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -121,83 +122,85 @@ hipError_t launch_decode_t(const KernelArgs& a, int n_wg, const MergeItem* merge
 }
 
 
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 hipError_t launch_mixed_t(const KernelArgs& a, int n_wg, const MergeItem*, int, hipStream_t stream) {
   if (n_wg > 0) {
-    hipLaunchKernelGGL((mixed_kernel<T, D, G>), dim3(n_wg), dim3(kPrefillWaves * kWave), 0, stream, a);
+    hipLaunchKernelGGL((mixed_kernel<T, D, DV, G>), dim3(n_wg), dim3(kPrefillWaves * kWave), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-template <typename T, int D, int G>
+template <typename T, int DV, int G>
 hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, hipStream_t stream) {
   if (n_merges > 0) {
-    const int chunks = (G * D + kMergeThreads - 1) / kMergeThreads;
-    hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3(n_merges, chunks), dim3(kMergeThreads), 0, stream, a, merges);
+    const int chunks = (G * DV + kMergeThreads - 1) / kMergeThreads;
+    hipLaunchKernelGGL((merge_kernel<T, DV, G>), dim3(n_merges, chunks), dim3(kMergeThreads), 0, stream, a, merges);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-template <template <typename, int, int> class Sel, typename T, int D>
+template <template <typename, int, int, int> class Sel, typename T, int D, int DV>
 LaunchFn pick_g(int g) {
   switch (g) {
-    case 1: return Sel<T, D, 1>::fn;
-    case 2: return Sel<T, D, 2>::fn;
-    case 4: return Sel<T, D, 4>::fn;
-    case 8: return Sel<T, D, 8>::fn;
-    case 16: return Sel<T, D, 16>::fn;
+    case 1: return Sel<T, D, DV, 1>::fn;
+    case 2: return Sel<T, D, DV, 2>::fn;
+    case 4: return Sel<T, D, DV, 4>::fn;
+    case 8: return Sel<T, D, DV, 8>::fn;
+    case 16: return Sel<T, D, DV, 16>::fn;
     default: return nullptr;
   }
 }
 
-template <template <typename, int, int> class Sel, typename T>
-LaunchFn pick_d(int d, int g) {
-  switch (d) {
-    case 64: return pick_g<Sel, T, 64>(g);
-    case 128: return pick_g<Sel, T, 128>(g);
-    case 256: return pick_g<Sel, T, 256>(g);
-    default: return nullptr;
-  }
-}
-
-template <template <typename, int, int> class Sel>
-LaunchFn pick(int dtype, int d, int g) {
-  if (dtype == 0) return pick_d<Sel, float>(d, g);
-  if (dtype == 1) return pick_d<Sel, uint16_t>(d, g);
-  if (dtype == 2) return pick_d<Sel, _Float16>(d, g);
+// (K, V) head sizes with kernels: equal sizes 64, 128, 256, and K 192 with
+// V 128 (a 128-wide no-position part plus a 64-wide rotary part in the key).
+template <template <typename, int, int, int> class Sel, typename T>
+LaunchFn pick_d(int d, int dv, int g) {
+  if (d == 64 && dv == 64) return pick_g<Sel, T, 64, 64>(g);
+  if (d == 128 && dv == 128) return pick_g<Sel, T, 128, 128>(g);
+  if (d == 256 && dv == 256) return pick_g<Sel, T, 256, 256>(g);
+  if (d == 192 && dv == 128) return pick_g<Sel, T, 192, 128>(g);
   return nullptr;
 }
 
-template <typename T, int D, int G>
+template <template <typename, int, int, int> class Sel>
+LaunchFn pick(int dtype, int d, int dv, int g) {
+  if (dtype == 0) return pick_d<Sel, float>(d, dv, g);
+  if (dtype == 1) return pick_d<Sel, uint16_t>(d, dv, g);
+  if (dtype == 2) return pick_d<Sel, _Float16>(d, dv, g);
+  return nullptr;
+}
+
+template <typename T, int D, int DV, int G>
 struct DecodeSel {
-  static constexpr LaunchFn fn = launch_decode_t<T, D, G>;
+  static constexpr LaunchFn fn = launch_decode_t<T, D, DV, G>;
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 struct MixedSel {
-  static constexpr LaunchFn fn = launch_mixed_t<T, D, G>;
+  static constexpr LaunchFn fn = launch_mixed_t<T, D, DV, G>;
 };
-template <typename T, int D, int G>
-struct MergeSel {
-  static constexpr LaunchFn fn = launch_merge_t<T, D, G>;
+template <typename T, int D, int DV, int G>
+struct MergeSel {  // depends on the output width only
+  static constexpr LaunchFn fn = launch_merge_t<T, DV, G>;
 };
 
 }  // namespace
 
-bool gqa_supported(int dtype, int d, int g) { return pick<DecodeSel>(dtype, d, g) != nullptr; }
+bool gqa_supported(int dtype, int d, int dv, int g) { return pick<DecodeSel>(dtype, d, dv, g) != nullptr; }
 
-bool prefill_supported(int dtype, int d, int g) { return pick<MixedSel>(dtype, d, g) != nullptr; }
+bool prefill_supported(int dtype, int d, int dv, int g) { return pick<MixedSel>(dtype, d, dv, g) != nullptr; }
 
-hipError_t launch_gqa_main(int dtype, int d, int g, bool has_prefill, const KernelArgs& a, hipStream_t stream) {
-  LaunchFn f = has_prefill ? pick<MixedSel>(dtype, d, g) : pick<DecodeSel>(dtype, d, g);
+hipError_t launch_gqa_main(int dtype, int d, int dv, int g, bool has_prefill, const KernelArgs& a,
+                           hipStream_t stream) {
+  LaunchFn f = has_prefill ? pick<MixedSel>(dtype, d, dv, g) : pick<DecodeSel>(dtype, d, dv, g);
   return f ? f(a, a.n_wg, nullptr, 0, stream) : hipErrorInvalidValue;
 }
 
-hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,
-                            hipStream_t stream) {
-  LaunchFn f = pick<MergeSel>(dtype, d, g);
+hipError_t launch_gqa_merge(int dtype, int d, int dv, int g, const KernelArgs& a, const MergeItem* merges,
+                            int n_merges, hipStream_t stream) {
+  LaunchFn f = pick<MergeSel>(dtype, d, dv, g);
   return f ? f(a, 0, merges, n_merges, stream) : hipErrorInvalidValue;
 }
 

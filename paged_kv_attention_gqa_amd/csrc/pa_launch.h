@@ -8,15 +8,17 @@
 
 namespace pa {
 
-// dtype: 0 = f32, 1 = bf16, 2 = f16.  d: head size.  g: query heads per KV head.
-bool gqa_supported(int dtype, int d, int g);
-bool prefill_supported(int dtype, int d, int g);
+// dtype: 0 = f32, 1 = bf16, 2 = f16.  d, dv: K and V head sizes.  g: query
+// heads per KV head.
+bool gqa_supported(int dtype, int d, int dv, int g);
+bool prefill_supported(int dtype, int d, int dv, int g);
 // Main GQA launch over the a.n_items entries of a.items: decode-only, or one
 // mixed launch when the list holds prefill tiles.
-hipError_t launch_gqa_main(int dtype, int d, int g, bool has_prefill, const KernelArgs& a, hipStream_t stream);
+hipError_t launch_gqa_main(int dtype, int d, int dv, int g, bool has_prefill, const KernelArgs& a,
+                           hipStream_t stream);
 // Log-sum-exp merge of split rows into the output.
-hipError_t launch_gqa_merge(int dtype, int d, int g, const KernelArgs& a, const MergeItem* merges, int n_merges,
-                            hipStream_t stream);
+hipError_t launch_gqa_merge(int dtype, int d, int dv, int g, const KernelArgs& a, const MergeItem* merges,
+                            int n_merges, hipStream_t stream);
 
 // Workgroups of the decode-only (group size g) and MLA kernels that one CU
 // holds at once; the planner balances decode work over CUs x this many.

@@ -471,10 +471,10 @@ __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem
     prefill_item_impl<T, D, G, false>(a, it, smem);
 }
 
-// A prefill tile handled one query at a time by the decode body (f32 data and
-// head sizes without an MFMA tile): each query's keys [lo, hi] are its own
-// visible range.
-template <typename T, int D, int G, int NW, int U>
+// A prefill tile handled one query at a time by the decode body (f32 data,
+// and head sizes without an MFMA tile: D = 256, or K and V rows of different
+// widths): each query's keys [lo, hi] are its own visible range.
+template <typename T, int D, int DV, int G, int NW, int U>
 __device__ __forceinline__ void prefill_item_by_queries(const KernelArgs& a, const WorkItem& it, float* smem) {
   const int L = a.seq_lens[it.seq];
   for (int j = 0; j < it.q_count; ++j) {
@@ -487,7 +487,7 @@ __device__ __forceinline__ void prefill_item_by_queries(const KernelArgs& a, con
     d.tok_end = (a.causal ? p : L - 1) + 1;
     d.tok_begin = a.window > 0 ? max(0, p - a.window + 1) : 0;
     d.slot = -1;
-    decode_item<T, D, G, NW, U>(a, d, smem);
+    decode_item<T, D, DV, G, NW, U>(a, d, smem);
     __syncthreads();
   }
 }

@@ -1,0 +1,90 @@
+"""GPU parity for K and V rows of different widths (ruDNN paged_attention:
+K [pages, page_size, Hkv, D], V [pages, page_size, Hkv, Dv], output
+[queries, Hq, Dv]): D = 192 with Dv = 128, the shape of a 128-wide
+no-position key part plus a 64-wide rotary part.  Decode items, split merges
+and prefill tiles (run query by query) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_attention_gqa_amd as pa
+from synth import random_batch
+from tests.gpu_harness import GqaRun, assert_close, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(b, **kw):
+    run = GqaRun(b, **kw)
+    run()
+    out, lse = run.result()
+    ref_o, ref_l = oracle.attention(b)
+    assert out.shape == ref_o.shape == (b.num_queries, b.hq, b.dv)
+    assert_close(out, ref_o, b.dtype)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-4 if b.dtype == "f32" else 1e-3)
+    return run
+
+
+CASES = [
+    dict(dtype="bf16", hq=32, hkv=8, page_size=16, q_counts=(1, 1, 1, 2, 1), max_len=3000),
+    dict(dtype="bf16", hq=128, hkv=128, page_size=64, q_counts=(1, 3), max_len=2000),
+    dict(dtype="bf16", hq=16, hkv=1, page_size=16, q_counts=(1, 1), max_len=2100, window=300),
+    dict(dtype="f16", hq=16, hkv=2, page_size=32, q_counts=(1, 2, 1), max_len=1500, causal=False),
+    dict(dtype="f16", hq=8, hkv=8, page_size=1, q_counts=(1, 1), max_len=300),
+    dict(dtype="f32", hq=8, hkv=2, page_size=16, q_counts=(1, 1, 1), max_len=1200),
+    dict(dtype="f32", hq=16, hkv=1, page_size=64, q_counts=(2,), max_len=700, window=65),
+]
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_d192_dv128_decode_parity(i, split_tokens):
+    b = random_batch(6000 + i, d=192, dv=128, **CASES[i])
+    _parity(b, split_tokens=split_tokens)
+
+
+@pytest.mark.parametrize("case", [
+    dict(dtype="bf16", hq=32, hkv=8, page_size=16, q_counts=(40, 1, 9), max_len=400),
+    dict(dtype="f16", hq=16, hkv=16, page_size=64, q_counts=(1, 70), max_len=500, window=33),
+    dict(dtype="f32", hq=8, hkv=2, page_size=16, q_counts=(12, 1), max_len=200, causal=False),
+])
+def test_d192_dv128_prefill_and_mixed_parity(case):
+    b = random_batch(6100, d=192, dv=128, **case)
+    run = _parity(b)
+    assert run.info["prefill_items"] > 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_d192_dv128_window_one_returns_own_value_bitwise(dtype):
+    b = random_batch(6200, dtype=dtype, hq=32, hkv=8, d=192, dv=128, page_size=16, q_counts=(1, 1, 5, 1),
+                     max_len=1500, window=1)
+    run = GqaRun(b)
+    run()
+    out, _ = run.result()
+    v = to_f64(run.v)
+    G = b.hq // b.hkv
+    for s in range(b.num_seqs):
+        for i in range(int(b.cu_q[s]), int(b.cu_q[s + 1])):
+            p = int(b.q_pos[i])
+            row = v[b.block_table[s, p // b.page_size], p % b.page_size]
+            for h in range(b.hq):
+                assert np.array_equal(out[i, h], row[h // G]), (i, h)
+
+
+def test_d192_dv128_long_rows_split_to_the_limit():
+    """Rows of 20-40k keys: every piece of every row merged (the merge reads
+    Dv-wide partials)."""
+    b = random_batch(6300, dtype="bf16", hq=16, hkv=2, d=192, dv=128, page_size=16, q_counts=(1, 1),
+                     histories=[20000, 40000])
+    run = _parity(b, max_splits=64)
+    assert run.info["split_rows"] > 0
+
+
+def test_head_size_pairs_without_kernels_are_refused():
+    import torch
+    b = random_batch(6400, dtype="bf16", hq=8, hkv=2, d=128, dv=64, page_size=16, q_counts=(1, 1), max_len=100)
+    run = GqaRun(b)
+    with pytest.raises(pa.PaError) as e:
+        run()
+    assert e.value.status == -4
+    torch.cuda.synchronize()
