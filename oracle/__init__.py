@@ -8,9 +8,12 @@ library and never imports it.
 from the definition: boostr 0.2.0-beta.2 `standard_attention_fwd` /
 `build_attention_mask` / `expand_kv`, with the paged layout and absolute
 positions of ruDNN 0.1.107 `DevicePlan::attention` and `DevicePlan::mla`).
-This module only builds it with gcc and marshals numpy arrays into it.
-`brute.py` is an independent pure-Python brute force for tiny inputs.
-`append_kv` (the cache write before attention) is a plain numpy loop.
+The backward (`attention_bwd`, `mla_bwd`: ruDNN `attention_backward` /
+`mla_backward`, written out from boostr `standard_attention_bwd`) lives in
+the same file.  This module only builds it with gcc and marshals numpy
+arrays into it.  `brute.py` is an independent pure-Python brute force for
+tiny inputs.  `append_kv` (the cache write before attention) is a plain
+numpy loop.
 """
 from __future__ import annotations
 
@@ -43,11 +46,9 @@ def _load():
         if not os.path.exists(_LIB_PATH):
             build()
         lib = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.c_void_p
         I = ctypes.c_int
-        for name, extra in (("po_attention", [P, P, P]), ("po_mla", [P, P, P, P]), ("po_widen", [])):
-            fn = getattr(lib, name)
-            fn.restype = I
+        for name in ("po_attention", "po_mla", "po_widen", "po_attention_bwd", "po_mla_bwd"):
+            getattr(lib, name).restype = I
         _lib = lib
     return _lib
 
@@ -144,6 +145,57 @@ def mla(b, rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None
     if rows is None:
         return out.reshape(Q, b.heads, b.r), lse.reshape(Q, b.heads)
     return out, lse
+
+
+def attention_bwd(b, dout: np.ndarray, nthreads: Optional[int] = None
+                  ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of `attention(b)` for the output gradient `dout` [Q, hq, dv]
+    (storage dtype of b), following ruDNN paged_attention
+    `attention_backward` with the formulas of boostr `standard_attention_bwd`.
+    Returns float64 (dq [Q, hq, d], dk [pages, ps, hkv, d], dv [pages, ps,
+    hkv, dv]); pool rows no visible key names are zero."""
+    lib = _load()
+    Q = int(b.cu_q[-1])
+    dq = np.empty((Q, b.hq, b.d), dtype=np.float64)
+    dk = np.empty((b.num_pages, b.page_size, b.hkv, b.d), dtype=np.float64)
+    dv = np.empty((b.num_pages, b.page_size, b.hkv, b.dv), dtype=np.float64)
+    q, k, v, g = (_storage(x, b.dtype) for x in (b.q, b.k, b.v, dout))
+    assert g.shape == (Q, b.hq, b.dv)
+    sl, cu, qp, bt = _i32(b.seq_lens), _i32(b.cu_q), _i32(b.q_pos), _i32(b.block_table)
+    rc = lib.po_attention_bwd(
+        ctypes.c_int(_DT[b.dtype]), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+        ctypes.c_int(len(sl)), _ptr(sl), _ptr(cu), _ptr(qp), _ptr(bt), ctypes.c_int(bt.shape[1]),
+        ctypes.c_int(b.page_size), ctypes.c_int(b.num_pages), ctypes.c_int(b.hq), ctypes.c_int(b.hkv),
+        ctypes.c_int(b.d), ctypes.c_int(b.dv), ctypes.c_double(b.scale), ctypes.c_int(int(b.causal)),
+        ctypes.c_int(int(b.window)), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.c_int(nthreads or default_threads()))
+    if rc:
+        raise RuntimeError(f"oracle: {_ERR.get(rc, rc)}")
+    return dq, dk, dv
+
+
+def mla_bwd(b, dout: np.ndarray, nthreads: Optional[int] = None
+            ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of `mla(b)` for `dout` [Q, heads, r] (ruDNN `mla_backward`):
+    float64 (dq_abs [Q, heads, r], dq_rope [Q, heads, p], dlatent [pages, ps,
+    1, r] with its key and value terms, dkpos [pages, ps, 1, p])."""
+    lib = _load()
+    Q = int(b.cu_q[-1])
+    dqa = np.empty((Q, b.heads, b.r), dtype=np.float64)
+    dqr = np.empty((Q, b.heads, b.p), dtype=np.float64)
+    dlat = np.empty((b.num_pages, b.page_size, 1, b.r), dtype=np.float64)
+    dkp = np.empty((b.num_pages, b.page_size, 1, b.p), dtype=np.float64)
+    qa, qr, lat, kp, g = (_storage(x, b.dtype) for x in (b.q_abs, b.q_rope, b.latent, b.kpos, dout))
+    assert g.shape == (Q, b.heads, b.r)
+    sl, cu, qp, bt = _i32(b.seq_lens), _i32(b.cu_q), _i32(b.q_pos), _i32(b.block_table)
+    rc = lib.po_mla_bwd(
+        ctypes.c_int(_DT[b.dtype]), _ptr(qa), _ptr(qr), _ptr(lat), _ptr(kp), _ptr(g),
+        ctypes.c_int(len(sl)), _ptr(sl), _ptr(cu), _ptr(qp), _ptr(bt), ctypes.c_int(bt.shape[1]),
+        ctypes.c_int(b.page_size), ctypes.c_int(b.num_pages), ctypes.c_int(b.heads), ctypes.c_int(b.r),
+        ctypes.c_int(b.p), ctypes.c_double(b.scale), ctypes.c_int(int(b.causal)), ctypes.c_int(int(b.window)),
+        _ptr(dqa), _ptr(dqr), _ptr(dlat), _ptr(dkp), ctypes.c_int(nthreads or default_threads()))
+    if rc:
+        raise RuntimeError(f"oracle: {_ERR.get(rc, rc)}")
+    return dqa, dqr, dlat, dkp
 
 
 def append_kv(seq_lens, cu_q, q_pos, block_table, page_size: int, k_new: np.ndarray, v_new: np.ndarray,

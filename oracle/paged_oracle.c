@@ -288,3 +288,203 @@ int po_mla(int dtype, const void *q_abs, const void *q_rope, const void *latent,
     j.rows = rows; j.num_rows = num_rows; j.out = out; j.lse = lse; j.nthreads = nthreads;
     return po_run(&j);
 }
+
+/* ------------------------------------------------------------------------
+ * Backward (ruDNN paged_attention `attention_backward`, `mla_backward`:
+ * first-order gradients of the forward above, recomputing the scores from
+ * Q and K), written out from the standard attention backward of boostr
+ * attention/flash_standard.rs (`standard_attention_bwd`): with P the softmax
+ * weights of a row and dO its output gradient,
+ *   dV_t += P_t dO,   dP_t = dO . V_t,   D = dO . O,   dS_t = P_t (dP_t - D),
+ *   dQ = scale sum_t dS_t K_t,   dK_t += scale dS_t Q,
+ * with the GQA head map summing the gradients of the G query heads that share
+ * a KV head (`sum_gqa_grads`).  MLA: the latent is key and value, so its
+ * gradient receives both the dK and the dV terms; the position query and
+ * cache receive the dQ / dK terms of the position dot product.
+ *
+ * Single pass per KV head (threads own disjoint KV heads, so the history
+ * gradients of one head are summed by one thread in a fixed order: sequences,
+ * queries, query heads, keys ascending); pool rows no visible key names keep
+ * gradient zero.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    po_job *job;
+    const void *dout;            /* [queries, hq, dv], storage dtype */
+    double *dq, *dqp;            /* [queries, hq, d] / [queries, hq, p] */
+    double *dk, *dv, *dkp;       /* pool shaped; MLA: dk == dv (latent), dkp [pages, ps, 1, p] */
+    int kvh0, kvh_step;
+    int status;
+} po_bwd_arg;
+
+static void *po_bwd_worker(void *arg)
+{
+    po_bwd_arg *a = (po_bwd_arg *)arg;
+    po_job *j = a->job;
+    const int group = j->hq / j->hkv;
+    int max_len = 1;
+    for (int s = 0; s < j->num_seqs; ++s)
+        if (j->seq_lens[s] > max_len) max_len = j->seq_lens[s];
+    double *pw = (double *)malloc(sizeof(double) * (size_t)max_len);  /* P_t */
+    double *ds = (double *)malloc(sizeof(double) * (size_t)max_len);  /* dS_t */
+    double *o = (double *)malloc(sizeof(double) * (size_t)j->dv);
+    if (!pw || !ds || !o) { free(pw); free(ds); free(o); a->status = -3; return NULL; }
+    for (int kvh = a->kvh0; kvh < j->hkv; kvh += a->kvh_step) {
+        for (int s = 0; s < j->num_seqs; ++s) {
+            const int len = j->seq_lens[s];
+            for (int i = j->cu_q[s]; i < j->cu_q[s + 1]; ++i) {
+                const int pos = j->q_pos[i];
+                for (int h = kvh * group; h < (kvh + 1) * group; ++h) {
+                    const int64_t row = (int64_t)i * j->hq + h;
+                    int bad = 0, count = 0;
+                    double m = -INFINITY;
+                    /* scores of the visible keys */
+                    for (int t = 0; t < len; ++t) {
+                        if (!po_visible(j, t, pos, len)) { pw[t] = -INFINITY; continue; }
+                        double dot = 0.0;
+                        for (int c = 0; c < j->d; ++c)
+                            dot += po_load(j->dtype, j->q, row * j->d + c) *
+                                   po_load(j->dtype, j->k, po_pool_offset(j, s, t, kvh, j->hkv, j->d, c, &bad));
+                        for (int c = 0; c < j->p; ++c)
+                            dot += po_load(j->dtype, j->qp, row * j->p + c) *
+                                   po_load(j->dtype, j->kp, po_pool_offset(j, s, t, 0, 1, j->p, c, &bad));
+                        if (bad) { a->status = -2; goto done; }
+                        pw[t] = j->scale * dot;
+                        if (pw[t] > m) m = pw[t];
+                        ++count;
+                    }
+                    if (count == 0) { a->status = -1; goto done; }
+                    /* softmax weights P_t and the row output O */
+                    double l = 0.0;
+                    for (int t = 0; t < len; ++t) {
+                        if (pw[t] == -INFINITY) continue;
+                        pw[t] = exp(pw[t] - m);
+                        l += pw[t];
+                    }
+                    for (int c = 0; c < j->dv; ++c) o[c] = 0.0;
+                    for (int t = 0; t < len; ++t) {
+                        if (pw[t] == -INFINITY) continue;
+                        pw[t] /= l;
+                        for (int c = 0; c < j->dv; ++c)
+                            o[c] += pw[t] * po_load(j->dtype, j->v, po_pool_offset(j, s, t, kvh, j->hkv, j->dv, c, &bad));
+                    }
+                    /* D = dO . O, then dP_t, dS_t and dV_t */
+                    double dd = 0.0;
+                    for (int c = 0; c < j->dv; ++c) dd += po_load(j->dtype, a->dout, row * j->dv + c) * o[c];
+                    for (int t = 0; t < len; ++t) {
+                        if (pw[t] == -INFINITY) { ds[t] = 0.0; continue; }
+                        double dp = 0.0;
+                        for (int c = 0; c < j->dv; ++c) {
+                            const double g = po_load(j->dtype, a->dout, row * j->dv + c);
+                            const int64_t off = po_pool_offset(j, s, t, kvh, j->hkv, j->dv, c, &bad);
+                            dp += g * po_load(j->dtype, j->v, off);
+                            a->dv[off] += pw[t] * g;
+                        }
+                        ds[t] = pw[t] * (dp - dd);
+                    }
+                    /* dQ (and the position query) from dS and K; dK_t from dS_t and Q */
+                    for (int c = 0; c < j->d; ++c) a->dq[row * j->d + c] = 0.0;
+                    for (int c = 0; c < j->p; ++c) a->dqp[row * j->p + c] = 0.0;
+                    for (int t = 0; t < len; ++t) {
+                        if (pw[t] == -INFINITY) continue;
+                        for (int c = 0; c < j->d; ++c) {
+                            const int64_t off = po_pool_offset(j, s, t, kvh, j->hkv, j->d, c, &bad);
+                            a->dq[row * j->d + c] += j->scale * ds[t] * po_load(j->dtype, j->k, off);
+                            a->dk[off] += j->scale * ds[t] * po_load(j->dtype, j->q, row * j->d + c);
+                        }
+                        for (int c = 0; c < j->p; ++c) {
+                            const int64_t off = po_pool_offset(j, s, t, 0, 1, j->p, c, &bad);
+                            a->dqp[row * j->p + c] += j->scale * ds[t] * po_load(j->dtype, j->kp, off);
+                            a->dkp[off] += j->scale * ds[t] * po_load(j->dtype, j->qp, row * j->p + c);
+                        }
+                    }
+                    if (bad) { a->status = -2; goto done; }
+                }
+            }
+        }
+    }
+done:
+    free(pw);
+    free(ds);
+    free(o);
+    return NULL;
+}
+
+static int po_bwd_run(po_job *j, const void *dout, double *dq, double *dqp, double *dk, double *dv, double *dkp,
+                      int64_t k_elems, int64_t v_elems, int64_t kp_elems)
+{
+    if (j->hq <= 0 || j->hkv <= 0 || j->hq % j->hkv != 0 || j->page_size <= 0) return -4;
+    if (j->dtype != PO_F32 && j->dtype != PO_BF16 && j->dtype != PO_F16) return -4;
+    /* history gradients start at zero (MLA: dk and dv are the same array) */
+    for (int64_t e = 0; e < k_elems; ++e) dk[e] = 0.0;
+    if (dv != dk)
+        for (int64_t e = 0; e < v_elems; ++e) dv[e] = 0.0;
+    for (int64_t e = 0; e < kp_elems; ++e) dkp[e] = 0.0;
+    int n = j->nthreads > 0 ? j->nthreads : 1;
+    if (n > j->hkv) n = j->hkv;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n);
+    po_bwd_arg *args = (po_bwd_arg *)malloc(sizeof(po_bwd_arg) * (size_t)n);
+    if (!th || !args) { free(th); free(args); return -3; }
+    for (int t = 0; t < n; ++t) {
+        po_bwd_arg init = {j, dout, dq, dqp, dk, dv, dkp, t, n, 0};
+        args[t] = init;
+        pthread_create(&th[t], NULL, po_bwd_worker, &args[t]);
+    }
+    int status = 0;
+    for (int t = 0; t < n; ++t) {
+        pthread_join(th[t], NULL);
+        if (args[t].status) status = args[t].status;
+    }
+    free(th);
+    free(args);
+    return status;
+}
+
+/*
+ * Paged GQA/MHA backward: dq [queries, hq, d]; dk, dv pool shaped ([pages,
+ * page_size, hkv, d] / [.., dv]), zero where no visible key lands.  dout has
+ * the storage dtype.  Return codes as po_attention.
+ */
+int po_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
+                     int num_seqs, const int32_t *seq_lens, const int32_t *cu_q, const int32_t *q_pos,
+                     const int32_t *block_table, int table_width, int page_size, int num_pages,
+                     int hq, int hkv, int d, int dv, double scale, int causal, int window,
+                     double *dq, double *dk, double *dvv, int nthreads)
+{
+    po_job j;
+    memset(&j, 0, sizeof j);
+    j.dtype = dtype;
+    j.num_seqs = num_seqs; j.table_width = table_width; j.page_size = page_size; j.num_pages = num_pages;
+    j.seq_lens = seq_lens; j.cu_q = cu_q; j.q_pos = q_pos; j.block_table = block_table;
+    j.num_queries = num_seqs > 0 ? cu_q[num_seqs] : 0;
+    j.hq = hq; j.hkv = hkv; j.d = d; j.dv = dv; j.p = 0;
+    j.scale = scale; j.causal = causal; j.window = window;
+    j.q = q; j.k = k; j.v = v;
+    j.nthreads = nthreads;
+    const int64_t slots = (int64_t)num_pages * page_size * hkv;
+    return po_bwd_run(&j, dout, dq, NULL, dk, dvv, NULL, slots * d, slots * dv, 0);
+}
+
+/*
+ * Absorbed-MLA backward: dq_abs [queries, heads, r], dq_rope [queries, heads,
+ * p], dlatent [pages, page_size, 1, r] (key and value terms), dkpos [pages,
+ * page_size, 1, p].  Return codes as po_attention.
+ */
+int po_mla_bwd(int dtype, const void *q_abs, const void *q_rope, const void *latent, const void *kpos,
+               const void *dout, int num_seqs, const int32_t *seq_lens, const int32_t *cu_q,
+               const int32_t *q_pos, const int32_t *block_table, int table_width, int page_size,
+               int num_pages, int heads, int r, int p, double scale, int causal, int window,
+               double *dq_abs, double *dq_rope, double *dlatent, double *dkpos, int nthreads)
+{
+    po_job j;
+    memset(&j, 0, sizeof j);
+    j.dtype = dtype;
+    j.num_seqs = num_seqs; j.table_width = table_width; j.page_size = page_size; j.num_pages = num_pages;
+    j.seq_lens = seq_lens; j.cu_q = cu_q; j.q_pos = q_pos; j.block_table = block_table;
+    j.num_queries = num_seqs > 0 ? cu_q[num_seqs] : 0;
+    j.hq = heads; j.hkv = 1; j.d = r; j.dv = r; j.p = p;
+    j.scale = scale; j.causal = causal; j.window = window;
+    j.q = q_abs; j.k = latent; j.v = latent; j.qp = q_rope; j.kp = kpos;
+    j.nthreads = nthreads;
+    const int64_t slots = (int64_t)num_pages * page_size;
+    return po_bwd_run(&j, dout, dq_abs, dq_rope, dlatent, dlatent, dkpos, slots * r, slots * r, slots * p);
+}
