@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (VALU), published
 METRIC = "decode KV GB/s (% HBM peak); chunked-prefill TFLOP/s (% bf16 MFMA peak)"
 
 
@@ -286,9 +287,58 @@ def measure_append(name, steps, warmup):
             "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def measure_backward(name, steps, warmup):
+    """Paged GQA backward of workload `name` (pa_attention_bwd: zero the
+    gradient pools, D = dO . O, dQ, dK/dV) after one forward call, timed with
+    HIP events around `steps` back-to-back calls.  Algorithmic flops per
+    visible (query row, key) pair: 2 (3 D + 2 Dv) (scores, dP, dQ, dK, dV)."""
+    import torch
+    import paged_kv_attention_gqa_amd as pa
+    from synth import CONFIGS
+    from tests.gpu_harness import GqaRun
+
+    b = CONFIGS[name]()
+    f = GqaRun(b)
+    f()
+    rng = np.random.default_rng(1)
+    dout = torch.from_numpy(rng.standard_normal((b.num_queries, b.hq, b.dv), dtype=np.float32)).to(
+        "cuda", dtype=torch.bfloat16)
+    dq = torch.empty_like(f.q)
+    dk, dv = torch.empty_like(f.k), torch.empty_like(f.v)
+    n = pa.pa_plan_bwd_workspace_bytes(f.plan)
+    ws = torch.empty(n // 4 + 64, dtype=torch.float32, device="cuda")
+
+    def call():
+        pa.pa_attention_bwd(f.plan, f.q, f.k, f.v, f.out, f.lse, dout, dq, dk, dv, scale=b.scale, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e6 + steps * 5e4))
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = int(visible_counts(b).sum()) * b.hq
+    flops = pairs * 2 * (3 * b.d + 2 * b.dv)
+    info = pa.pa_plan_get_info(f.plan)
+    del f, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"backward:{name}", "kernel_ms": round(ms, 5), "flops": flops, "bound": "mfma",
+            "tflops": round(tf, 2), "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "frac_of_fp32_vector_peak": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "items": {"dq": info["bwd_dq_items"], "dkv": info["bwd_kv_items"]}}
+
+
 PRIMARY = "bf16_decode_batch"
 SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode")
 APPEND = ("bf16_decode_batch", "bf16_chunked_prefill")  # cache writes of one decode step and of one chunk
+BACKWARD = ("bf16_chunked_prefill",)  # gradients of one chunk step
 
 
 def run(args):
@@ -343,6 +393,8 @@ def run(args):
                 result["secondary"].append({"workload": n, "error": str(e)})
         for n in APPEND:
             result["secondary"].append(measure_append(n, args.steps, args.warmup))
+        for n in BACKWARD:
+            result["secondary"].append(measure_backward(n, args.steps, args.warmup))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, mla, bytes_alg if hbm else flops_alg, hbm)
     return result
@@ -376,9 +428,16 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the backward of --workload (one JSON line)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(1, args.steps))
+        return
+    if args.backward_only:
+        import paged_kv_attention_gqa_amd as pa
+        pa.load_library()
+        print(json.dumps(measure_backward(args.workload, args.steps, args.warmup)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "

@@ -130,6 +130,8 @@ typedef struct pa_plan_info {
   int32_t launches;      /* kernels one forward call enqueues (0, 1 or 2) */
   int32_t workgroups;    /* workgroups of the main launch */
   int32_t heads_per_item; /* KV heads one decode item covers (decode-only plans: a power of two) */
+  int32_t bwd_dq_items;   /* backward: (query, KV head) workgroups of the dQ pass (GQA plans) */
+  int32_t bwd_kv_items;   /* backward: (64-key block, KV head) workgroups of the dK/dV pass */
 } pa_plan_info;
 
 /*
@@ -205,6 +207,9 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
  *                the main attention kernel and before the split merge (lets a
  *                caller time the two kernels separately)
  *
+ * Tensors other than lse and the workspace must be 16-byte aligned
+ * (PA_ERR_INVALID otherwise); the kernels move rows in 16-byte pieces.
+ *
  * The plan must be a GQA plan (mla == 0) made on the current device.
  * Q == 0 returns PA_OK without launching anything; q and out (empty then)
  * may be NULL.
@@ -269,6 +274,46 @@ const char* pa_status_string(int status);
  */
 int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const void* v_new, void* k_pool,
                  void* v_pool, int32_t head_dim, int32_t v_head_dim, void* stream);
+
+/*
+ * Bytes of f32 workspace pa_attention_bwd needs: one value per (query, head)
+ * row (D = dO . O), 256-byte aligned; 0 when the plan has no queries.
+ */
+int pa_plan_bwd_workspace_bytes(const pa_plan* plan, size_t* bytes);
+
+/*
+ * Paged GQA/MHA backward (ruDNN 0.1.107 paged_attention
+ * `attention_backward_into`: first-order gradients, scores recomputed from Q
+ * and K; formulas of boostr `standard_attention_bwd`).  With P the softmax
+ * weights of a row and dO its output gradient:
+ *
+ *   D = dO . O   dS_t = P_t (dO . V_t - D)   dQ = scale sum_t dS_t K_t
+ *   dK_t = scale sum_rows dS_t Q             dV_t = sum_rows P_t dO
+ *
+ * summed over the G query heads of each KV head.  Every pool row has a single
+ * writer (ruDNN's ordered, atomic-free variant), so results are reproducible.
+ *
+ *   dtype        of q, k_pool, v_pool, out, dout, dq, dk_pool, dv_pool
+ *   q, k_pool, v_pool  as for pa_attention_fwd with the same plan
+ *   out, lse     the forward's output [Q, Hq, Dv] and f32 logsumexp [Q, Hq]
+ *   dout         output gradient [Q, Hq, Dv]
+ *   dq           [Q, Hq, D], written
+ *   dk_pool, dv_pool  pool shaped like k_pool / v_pool, written in full: rows
+ *                no visible key of any query lands on are zero
+ *   workspace    >= pa_plan_bwd_workspace_bytes bytes, 256-byte aligned
+ *
+ * Head sizes as for pa_attention_fwd.  Errors: PA_ERR_UNSUPPORTED for MLA
+ * plans (no MLA backward in this build) and for missing kernels; PA_ERR_PLAN
+ * when a pool page holds key positions of two sequences (or two positions of
+ * one: the single-writer pass cannot own it); PA_ERR_WORKSPACE,
+ * PA_ERR_OVERLAP, PA_ERR_SHAPE, PA_ERR_DEVICE, PA_ERR_HIP as for
+ * pa_attention_fwd.  Q == 0 zeroes dk_pool and dv_pool and touches nothing
+ * else.
+ */
+int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool, const void* v_pool,
+                     const void* out, const float* lse, const void* dout, void* dq, void* dk_pool, void* dv_pool,
+                     int32_t head_dim, int32_t v_head_dim, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* Detail message of the calling thread's last failure ("" if none). */
 const char* pa_last_error(void);

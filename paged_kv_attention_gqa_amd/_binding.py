@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_INVALID", -2: "PA_ERR_SHAPE", -3: "PA_ER
                 -9: "PA_ERR_DEVICE"}
 EXPORTED = ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
             "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv", "pa_status_string",
-            "pa_last_error")
+            "pa_last_error", "pa_plan_bwd_workspace_bytes", "pa_attention_bwd")
 
 
 class PaError(RuntimeError):
@@ -48,7 +48,8 @@ class _PlanInfo(ctypes.Structure):
     _fields_ = [("num_queries", ctypes.c_int32), ("decode_items", ctypes.c_int32),
                 ("prefill_items", ctypes.c_int32), ("split_rows", ctypes.c_int32),
                 ("split_slots", ctypes.c_int32), ("launches", ctypes.c_int32), ("workgroups", ctypes.c_int32),
-                ("heads_per_item", ctypes.c_int32)]
+                ("heads_per_item", ctypes.c_int32), ("bwd_dq_items", ctypes.c_int32),
+                ("bwd_kv_items", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,12 +74,15 @@ def load_library():
     lib.pa_attention_fwd.argtypes = [P, I, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_mla_fwd.argtypes = [P, I, P, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_append_kv.argtypes = [P, I, P, P, P, P, I, I, P]
+    lib.pa_plan_bwd_workspace_bytes.argtypes = [P, ctypes.POINTER(S)]
+    lib.pa_attention_bwd.argtypes = [P, I, P, P, P, P, P, P, P, P, P, I, I, F, P, S, P]
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     for n in ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
-              "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv"):
+              "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv",
+              "pa_plan_bwd_workspace_bytes", "pa_attention_bwd"):
         getattr(lib, n).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -283,6 +287,40 @@ def pa_attention_fwd(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: flo
     wp, wn = _ws(workspace)
     _check(load_library().pa_attention_fwd(plan.handle, dt, pq, pk, pv, po, pl, D, Dv, float(scale), wp, wn,
                                            _event(event_after_main), _stream_handle(stream)), "pa_attention_fwd")
+
+
+def pa_plan_bwd_workspace_bytes(plan: Plan) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().pa_plan_bwd_workspace_bytes(plan.handle, ctypes.byref(n)), "pa_plan_bwd_workspace_bytes")
+    return int(n.value)
+
+
+def pa_attention_bwd(plan: Plan, q, k_pool, v_pool, out, lse, dout, dq, dk_pool, dv_pool, *, scale: float,
+                     workspace=None, stream=None) -> None:
+    """Paged GQA backward into dq, dk_pool, dv_pool (see pa_attention_bwd in
+    paged_attn.h); out and lse are the forward's."""
+    import torch
+    d = plan.desc
+    dt = _dtype_code(q)
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool), ("out", out), ("dout", dout), ("dq", dq),
+                    ("dk_pool", dk_pool), ("dv_pool", dv_pool)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    D, Dv = int(q.shape[2]), int(v_pool.shape[3])
+    Q, Hq = d["num_queries"], d["num_q_heads"]
+    pool = (d["num_pages"], d["page_size"], d["num_kv_heads"])
+    for name, t, shape in (("q", q, (Q, Hq, D)), ("out", out, (Q, Hq, Dv)), ("dout", dout, (Q, Hq, Dv)),
+                           ("dq", dq, (Q, Hq, D)), ("k_pool", k_pool, pool + (D,)), ("v_pool", v_pool, pool + (Dv,)),
+                           ("dk_pool", dk_pool, pool + (D,)), ("dv_pool", dv_pool, pool + (Dv,))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {shape}")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Q, Hq):
+        raise ValueError("lse must be float32 [Q, Hq]")
+    wp, wn = _ws(workspace)
+    _check(load_library().pa_attention_bwd(
+        plan.handle, dt, _dev(q, "q", 3), _dev(k_pool, "k_pool", 4), _dev(v_pool, "v_pool", 4), _dev(out, "out", 3),
+        _dev(lse, "lse", 2), _dev(dout, "dout", 3), _dev(dq, "dq", 3), _dev(dk_pool, "dk_pool", 4),
+        _dev(dv_pool, "dv_pool", 4), D, Dv, float(scale), wp, wn, _stream_handle(stream)), "pa_attention_bwd")
 
 
 def pa_mla_fwd(plan: Plan, q_abs, q_rope, latent, kpos, out, lse=None, *, scale: float, workspace=None,

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_attn.so")
-SOURCES = ["pa_capi.cpp", "pa_kernels.hip", "pa_append.hip"]
+SOURCES = ["pa_capi.cpp", "pa_kernels.hip", "pa_append.hip", "pa_backward.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

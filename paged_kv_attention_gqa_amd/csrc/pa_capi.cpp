@@ -87,6 +87,11 @@ struct pa_plan {
   // and the first query whose slot another query also writes (-1: none)
   std::vector<int32_t> slot_of;
   int32_t dup_query = -1;
+  // backward (GQA plans): dQ items, then dK/dV items; a page that two key
+  // positions share (-1: none) makes the single-writer dK/dV pass impossible
+  std::vector<pa::BwdItem> bwd_items;
+  int32_t n_bwd_dq = 0, n_bwd_kv = 0;
+  int32_t shared_page = -1;
   // device copy: one allocation
   std::vector<char> blob;
   char* dev = nullptr;
@@ -97,6 +102,7 @@ struct pa_plan {
   const int32_t* d_wg_first = nullptr;
   const int32_t* d_slot_of = nullptr;
   const MergeItem* d_merges = nullptr;
+  const pa::BwdItem* d_bwd = nullptr;
 
   int group() const { return hq / hkv; }
 };
@@ -407,6 +413,59 @@ void build_work(pa_plan* p) {
   p->n_wg = (int32_t)p->wg_first.size() - 1;
 }
 
+// Backward work (ruDNN `attention_backward`: scores recomputed from Q and K,
+// a second scan of the history).  dQ: one item per (query, KV head) over the
+// query's visible keys.  dK/dV: one item per (block of kBwdBlockKeys keys,
+// KV head) of every sequence with queries, skipping blocks no query sees;
+// every pool row then has a single writer, which needs each referenced page
+// to hold key positions of one sequence only.  Both lists run longest first.
+void build_bwd(pa_plan* p) {
+  if (p->mla) return;
+  std::vector<int32_t> owner(p->num_pages, -1);
+  for (int s = 0; s < p->S && p->shared_page < 0; ++s) {
+    const int pages = (p->seq_lens[s] + p->ps - 1) / p->ps;
+    for (int j = 0; j < pages; ++j) {
+      const int page = p->bt[(size_t)s * p->W + j];
+      if (owner[page] >= 0) {
+        p->shared_page = page;
+        break;
+      }
+      owner[page] = s;
+    }
+  }
+  std::vector<std::pair<int64_t, pa::BwdItem>> dq, kv;
+  for (int s = 0; s < p->S; ++s) {
+    const int q0 = p->cu_q[s], q1 = p->cu_q[s + 1], L = p->seq_lens[s];
+    if (q0 == q1) continue;
+    for (int i = q0; i < q1; ++i) {
+      int lo, hi;
+      visible_range(p->q_pos[i], L, p->causal, p->window, &lo, &hi);
+      for (int kvh = 0; kvh < p->hkv; ++kvh) dq.push_back({hi + 1 - lo, pa::BwdItem{s, kvh, i, i + 1, lo, hi + 1}});
+    }
+    for (int t0 = 0; t0 < L; t0 += pa::kBwdBlockKeys) {
+      const int t1 = std::min(L, t0 + pa::kBwdBlockKeys);
+      int64_t rows = 0;  // queries that see a key of the block
+      for (int i = q0; i < q1; ++i) {
+        int lo, hi;
+        visible_range(p->q_pos[i], L, p->causal, p->window, &lo, &hi);
+        rows += (lo < t1 && hi >= t0);
+      }
+      if (rows == 0) continue;
+      for (int kvh = 0; kvh < p->hkv; ++kvh) kv.push_back({rows, pa::BwdItem{s, kvh, q0, q1, t0, t1}});
+    }
+  }
+  auto longest_first = [](const std::pair<int64_t, pa::BwdItem>& a, const std::pair<int64_t, pa::BwdItem>& b) {
+    return a.first > b.first;
+  };
+  std::stable_sort(dq.begin(), dq.end(), longest_first);
+  std::stable_sort(kv.begin(), kv.end(), longest_first);
+  p->bwd_items.clear();
+  for (auto& x : dq) p->bwd_items.push_back(x.second);
+  for (auto& x : kv) p->bwd_items.push_back(x.second);
+  p->n_bwd_dq = (int32_t)dq.size();
+  p->n_bwd_kv = (int32_t)kv.size();
+}
+
 // Workspace: partial sums [slots, G, Dv] | (max, sum, unrounded sum) [slots, G, 3].
 size_t ws_o_bytes(const pa_plan* p, int dv) { return align_up((size_t)p->n_slots * p->group() * dv * 4, kAlign); }
 size_t ws_ml_bytes(const pa_plan* p) { return align_up((size_t)p->n_slots * p->group() * 3 * 4, kAlign); }
@@ -435,6 +494,14 @@ int check_disjoint(const std::vector<Extent>& outs, const std::vector<Extent>& i
     for (size_t j = i + 1; j < outs.size(); ++j)
       if (overlaps(outs[i], outs[j])) return fail(PA_ERR_OVERLAP, "%s overlaps %s", outs[i].name, outs[j].name);
   }
+  return PA_OK;
+}
+
+// The kernels move tensor rows in 16-byte pieces.
+int check_aligned(const std::vector<Extent>& ts) {
+  for (const Extent& t : ts)
+    if (t.p && t.n && reinterpret_cast<uintptr_t>(t.p) % 16)
+      return fail(PA_ERR_INVALID, "%s must be 16-byte aligned", t.name);
   return PA_OK;
 }
 
@@ -527,8 +594,9 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
     return hip_fail(e, "device query");
   }
   build_work(p);
+  build_bwd(p);
 
-  // one blob: block table | q_pos | seq_lens | items | workgroup ranges | merges | append slots
+  // one blob: block table | q_pos | seq_lens | items | workgroup ranges | merges | append slots | backward items
   size_t off_bt = 0;
   size_t off_qpos = align_up(off_bt + p->bt.size() * 4, kAlign);
   size_t off_lens = align_up(off_qpos + p->q_pos.size() * 4, kAlign);
@@ -536,7 +604,8 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   size_t off_wg = align_up(off_items + p->items.size() * sizeof(WorkItem), kAlign);
   size_t off_merges = align_up(off_wg + p->wg_first.size() * 4, kAlign);
   size_t off_slots = align_up(off_merges + p->merges.size() * sizeof(MergeItem), kAlign);
-  size_t total = align_up(off_slots + p->slot_of.size() * 4, kAlign);
+  size_t off_bwd = align_up(off_slots + p->slot_of.size() * 4, kAlign);
+  size_t total = align_up(off_bwd + p->bwd_items.size() * sizeof(pa::BwdItem), kAlign);
   total = std::max(total, kAlign);
   p->blob.assign(total, 0);
   if (!p->bt.empty()) memcpy(p->blob.data() + off_bt, p->bt.data(), p->bt.size() * 4);
@@ -547,6 +616,8 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   if (!p->merges.empty())
     memcpy(p->blob.data() + off_merges, p->merges.data(), p->merges.size() * sizeof(MergeItem));
   if (!p->slot_of.empty()) memcpy(p->blob.data() + off_slots, p->slot_of.data(), p->slot_of.size() * 4);
+  if (!p->bwd_items.empty())
+    memcpy(p->blob.data() + off_bwd, p->bwd_items.data(), p->bwd_items.size() * sizeof(pa::BwdItem));
 
   e = hipMalloc(reinterpret_cast<void**>(&p->dev), total);
   if (e != hipSuccess) {
@@ -571,6 +642,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   p->d_wg_first = reinterpret_cast<const int32_t*>(p->dev + off_wg);
   p->d_merges = reinterpret_cast<const MergeItem*>(p->dev + off_merges);
   p->d_slot_of = reinterpret_cast<const int32_t*>(p->dev + off_slots);
+  p->d_bwd = reinterpret_cast<const pa::BwdItem*>(p->dev + off_bwd);
   *out_plan = p;
   return ok();
 }
@@ -584,6 +656,7 @@ int pa_plan_create_host(const pa_plan_desc* desc, int32_t num_cus, pa_plan** out
   if (!p) return fail(PA_ERR_HIP, "host allocation failed");
   p->n_cu = num_cus;
   build_work(p);
+  build_bwd(p);
   *out_plan = p;
   return ok();
 }
@@ -631,6 +704,8 @@ int pa_plan_get_info(const pa_plan* plan, pa_plan_info* info) {
   info->launches = plan->items.empty() ? 0 : (plan->merges.empty() ? 1 : 2);
   info->workgroups = plan->n_wg;
   info->heads_per_item = 1 << plan->heads_shift;
+  info->bwd_dq_items = plan->n_bwd_dq;
+  info->bwd_kv_items = plan->n_bwd_kv;
   return ok();
 }
 
@@ -718,6 +793,7 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                              {k_pool, slots * head_dim * es, "k_pool"},
                              {v_pool, slots * v_head_dim * es, "v_pool"}};
   rc = check_disjoint(outs, ins);
+  if (rc == PA_OK) rc = check_aligned({outs[0], ins[0], ins[1], ins[2]});
   if (rc != PA_OK) return rc;
 
   FwdCall c{plan, dtype, head_dim, v_head_dim, {}, event_after_main, reinterpret_cast<hipStream_t>(stream)};
@@ -780,6 +856,7 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
                              {latent, slots * rank * es, "latent"},
                              {kpos, slots * rope_dim * es, "kpos"}};
   rc = check_disjoint(outs, ins);
+  if (rc == PA_OK) rc = check_aligned({outs[0], ins[0], ins[1], ins[2], ins[3]});
   if (rc != PA_OK) return rc;
 
   FwdCall c{plan, dtype, rank, rank, {}, event_after_main, reinterpret_cast<hipStream_t>(stream)};
@@ -832,6 +909,8 @@ int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const vo
   std::vector<Extent> ins = {{k_new, (size_t)plan->Q * heads * head_dim * es, "k_new"},
                              {v_new, (size_t)plan->Q * heads * v_head_dim * es, "v_new"}};
   int rc = check_disjoint(outs, ins);
+  if (rc == PA_OK) rc = check_aligned(outs);
+  if (rc == PA_OK) rc = check_aligned(ins);
   if (rc != PA_OK) return rc;
   rc = check_device(plan);
   if (rc != PA_OK) return rc;
@@ -844,6 +923,88 @@ int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const vo
   hipError_t e = pa::launch_append(k_new, v_new, k_pool, v_pool, plan->d_slot_of, plan->Q, heads,
                                    (int)(head_dim * es), (int)(v_head_dim * es), std::max(plan->n_cu, 1), st);
   if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+int pa_plan_bwd_workspace_bytes(const pa_plan* plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(PA_ERR_INVALID, "plan or bytes is NULL");
+  *bytes = plan->Q > 0 ? align_up((size_t)plan->Q * plan->hq * 4, kAlign) : 0;
+  return ok();
+}
+
+int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool, const void* v_pool,
+                     const void* out, const float* lse, const void* dout, void* dq, void* dk_pool, void* dv_pool,
+                     int32_t head_dim, int32_t v_head_dim, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
+  if (plan->mla) return fail(PA_ERR_UNSUPPORTED, "this build has no MLA backward");
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!k_pool || !v_pool || !dk_pool || !dv_pool)
+    return fail(PA_ERR_INVALID, "k_pool, v_pool, dk_pool and dv_pool are required");
+  if (plan->Q > 0 && (!q || !out || !lse || !dout || !dq))
+    return fail(PA_ERR_INVALID, "q, out, lse, dout and dq are required when there are queries");
+  if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
+    return fail(PA_ERR_SHAPE, "head sizes D=%d Dv=%d outside [1, 1024]", head_dim, v_head_dim);
+  if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
+  if (plan->shared_page >= 0)
+    return fail(PA_ERR_PLAN, "pool page %d holds key positions of two sequences (or two positions of one); "
+                "the single-writer backward needs pages owned by one position each", plan->shared_page);
+  const int G = plan->group();
+  if (!pa::bwd_supported(dtype, head_dim, v_head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "no backward kernel for dtype %d, D=%d, Dv=%d, G=%d", dtype, head_dim, v_head_dim,
+                G);
+  size_t need = 0;
+  pa_plan_bwd_workspace_bytes(plan, &need);
+  if (need > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "backward needs %zu bytes of workspace", need);
+    if (workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "backward workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const size_t es = dtype == PA_F32 ? 4 : 2;
+  const size_t slots = (size_t)plan->num_pages * plan->ps * plan->hkv;
+  const size_t rows = (size_t)plan->Q * plan->hq;
+  std::vector<Extent> outs = {{dq, rows * head_dim * es, "dq"},
+                              {dk_pool, slots * head_dim * es, "dk_pool"},
+                              {dv_pool, slots * v_head_dim * es, "dv_pool"},
+                              {workspace, need, "workspace"}};
+  std::vector<Extent> ins = {{q, rows * head_dim * es, "q"},
+                             {k_pool, slots * head_dim * es, "k_pool"},
+                             {v_pool, slots * v_head_dim * es, "v_pool"},
+                             {out, rows * v_head_dim * es, "out"},
+                             {lse, rows * 4, "lse"},
+                             {dout, rows * v_head_dim * es, "dout"}};
+  int rc = check_disjoint(outs, ins);
+  if (rc == PA_OK) rc = check_aligned({outs[0], outs[1], outs[2], ins[0], ins[1], ins[2], ins[3], ins[5]});
+  if (rc != PA_OK) return rc;
+  rc = check_device(plan);
+  if (rc != PA_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (st != plan->created_on) {
+    hipError_t e = hipStreamWaitEvent(st, plan->ready, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(plan)");
+  }
+  pa::KernelArgs a{};
+  a.q = q;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.out = const_cast<void*>(out);
+  a.lse = const_cast<float*>(lse);
+  a.block_table = plan->d_bt;
+  a.q_pos = plan->d_qpos;
+  a.seq_lens = plan->d_lens;
+  a.table_width = plan->W;
+  a.page_shift = plan->page_shift;
+  a.hq = plan->hq;
+  a.hkv = plan->hkv;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.causal = plan->causal;
+  a.window = plan->window;
+  hipError_t e = pa::launch_gqa_bwd(dtype, head_dim, v_head_dim, G, a, dout, dq, dk_pool, dv_pool,
+                                    reinterpret_cast<float*>(workspace), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv,
+                                    (int64_t)rows, (int64_t)slots, std::max(plan->n_cu, 1), st);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }
 

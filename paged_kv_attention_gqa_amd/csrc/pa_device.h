@@ -38,6 +38,17 @@ struct MergeItem {
   int32_t q, kvh, slot, nsplit, stride;
 };
 
+// One unit of backward work.  dQ items: one query (q_end = q_begin + 1) and
+// one KV head over that query's visible keys [tok_begin, tok_end).  dK/dV
+// items: one block of keys [tok_begin, tok_end) of one sequence and KV head
+// against the sequence's queries [q_begin, q_end).
+struct BwdItem {
+  int32_t seq, kvh;
+  int32_t q_begin, q_end;
+  int32_t tok_begin, tok_end;
+};
+constexpr int kBwdBlockKeys = 64;  // keys of one dK/dV item
+
 struct KernelArgs {
   const void* q;          // [Q, Hq, D]            (MLA: absorbed query [Q, H, R])
   const void* k;          // [pages, ps, Hkv, D]   (MLA: latent [pages, ps, 1, R])
