@@ -31,7 +31,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (VALU), published
 METRIC = "decode KV GB/s (% HBM peak); chunked-prefill TFLOP/s (% bf16 MFMA peak)"
 
 
@@ -331,7 +330,6 @@ def measure_backward(name, steps, warmup):
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": f"backward:{name}", "kernel_ms": round(ms, 5), "flops": flops, "bound": "mfma",
             "tflops": round(tf, 2), "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-            "frac_of_fp32_vector_peak": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
             "items": {"dq": info["bwd_dq_items"], "dkv": info["bwd_kv_items"]}}
 
 
@@ -435,8 +433,10 @@ def main():
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return
     if args.backward_only:
+        import torch
         import paged_kv_attention_gqa_amd as pa
         pa.load_library()
+        torch.cuda.set_device(0)
         print(json.dumps(measure_backward(args.workload, args.steps, args.warmup)), flush=True)
         return
     if args.gpus != 1:

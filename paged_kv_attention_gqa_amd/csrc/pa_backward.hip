@@ -13,14 +13,16 @@
 //
 // Four launches: zero the K/V gradient pools, D per row, dQ (one workgroup
 // per (query, KV head), keys strided over lanes as in the decode body), and
-// dK/dV (one workgroup per 64-key block and KV head, looping over the
-// sequence's query rows).  Each pool row has a single writer, so the result
+// dK/dV (one workgroup per 128-key block and KV head, looping over the
+// sequence's query rows: on 16-bit MFMA for bf16 / f16 with D = Dv in {64,
+// 128}, else on the vector units).  Each pool row has a single writer, so the result
 // does not depend on scheduling (ruDNN's ordered, atomic-free variant).
 #include <algorithm>
 
 #include "pa_decode.h"
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "pa_mla.h"
 
 namespace pa {
 
@@ -152,18 +154,25 @@ __global__ __launch_bounds__(kBwdDqWaves* kWave) void bwd_dq_kernel(BwdArgs b) {
   }
 }
 
-// dK and dV of one block of up to kBwdBlockKeys keys and one KV head.  Lane
-// (r, c) of wave w holds chunk c of keys tok_begin + (u NW + w) TPW + r,
-// u < U, and their gradient sums; the sequence's query rows stream past.
+// dK and dV of one block of up to kBwdBlockKeys keys and one KV head, in
+// sub-blocks of 64 keys.  Lane (r, c) of wave w holds chunk c of keys
+// sub + (u NW + w) TPW + r, u < U, and their gradient sums; the sequence's
+// query rows stream past.
+constexpr int kBwdSubKeys = 64;
 template <typename T, int D, int DV, int G>
 __global__ __launch_bounds__(kBwdKvWaves* kWave) void bwd_dkv_kernel(BwdArgs b, int first_item) {
   using Lay = DecodeLayout<T, D, DV>;
   constexpr int LPT = Lay::kLanes, KW = Lay::kKWords, VW = Lay::kVWords, EK = Lay::kKElems, EV = Lay::kVElems;
   constexpr int TPW = kWave / LPT, NW = kBwdKvWaves, SZ = (int)sizeof(T);
-  constexpr int U = kBwdBlockKeys / (NW * TPW);
-  static_assert(U >= 1 && U * NW * TPW == kBwdBlockKeys, "a block must split evenly over the lanes");
+  constexpr int U = kBwdSubKeys / (NW * TPW);
+  static_assert(U >= 1 && U * NW * TPW == kBwdSubKeys && kBwdBlockKeys % kBwdSubKeys == 0,
+                "a sub-block must split evenly over the lanes");
   const KernelArgs& a = b.a;
-  const BwdItem it = b.items[first_item + blockIdx.x];
+  const BwdItem item = b.items[first_item + blockIdx.x];
+  for (int sub = item.tok_begin; sub < item.tok_end; sub += kBwdSubKeys) {
+  BwdItem it = item;
+  it.tok_begin = sub;
+  it.tok_end = min(item.tok_end, sub + kBwdSubKeys);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r = lane / LPT, c = lane % LPT;
@@ -242,21 +251,344 @@ __global__ __launch_bounds__(kBwdKvWaves* kWave) void bwd_dkv_kernel(BwdArgs b, 
 #pragma unroll
     for (int e = 0; e < EV; ++e) store_out<T>(b.dv, slot[u] * vrow + (uint64_t)kvh * DV + c * EV + e, dv[u][e]);
   }
+  }
+}
+
+// dK and dV of one block of kBwdBlockKeys keys and one KV head on 16-bit
+// MFMA (v_mfma_f32_16x16x32): eight waves of 16 keys; the sequence's query
+// rows (query, head of the group) stream through LDS in tiles of 32 rows.
+// Per tile and wave, with the 16x16 accumulator layout (lane (n, g) holds
+// column n, rows 4 g .. 4 g + 3):
+//   S  = Q K^T,  dP = dO V^T          (rows x keys; K^T and V^T of the wave's
+//                                      keys stay in registers)
+//   P  = 2^(S c - lse2) masked,  dS = P (dP - D) scale
+//   dV += P^T dO,  dK += dS^T Q       (keys x dims; P^T / dS^T straight from
+//                                      the S / dP accumulators, with the
+//                                      row order of the two 16-row halves
+//                                      interleaved; dO and Q columns by
+//                                      transposed LDS reads in that order)
+constexpr int kBwdMfmaWaves = 8;
+constexpr int kBwdRowTile = 32;
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdArgs b, int first_item, int G) {
+  constexpr int KS = D / 32;        // 16x16x32 k-steps over the head dims
+  constexpr int DB = D / 16;        // 16-dim blocks of dK / dV
+  constexpr int PIECES = D / 8;     // 16-byte pieces per row
+  constexpr int TILE = kBwdRowTile * D * 2;
+  static_assert(kBwdMfmaWaves * 16 == kBwdBlockKeys, "eight waves of 16 keys");
+  __shared__ __attribute__((aligned(16))) char qs[TILE];
+  __shared__ __attribute__((aligned(16))) char gs[TILE];
+  __shared__ float lse2s[kBwdRowTile], dls[kBwdRowTile];
+  __shared__ int poss[kBwdRowTile];
+  const KernelArgs& a = b.a;
+  const BwdItem it = b.items[first_item + blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = lane & 15, g4 = lane >> 4;  // MFMA column and k-group
+  const int kvh = it.kvh;
+  const int ps = 1 << a.page_shift;
+  const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
+  const uint64_t row_stride = (uint64_t)a.hkv * D;
+  const int nrows = (it.q_end - it.q_begin) * G;
+  const float c2 = a.scale_log2;
+
+  // K^T and V^T operands of this wave's 16 keys (key column n, dims 32 k + 8 g4 ..)
+  const int my_key = it.tok_begin + wave * 16 + n;
+  const bool key_ok = my_key < it.tok_end;
+  frag_t kb[KS], vb[KS];
+  {
+    const int tc = key_ok ? my_key : it.tok_end - 1;
+    const uint64_t slot = (uint64_t)bt[tc >> a.page_shift] * ps + (tc & (ps - 1));
+    const uint16_t* kr = reinterpret_cast<const uint16_t*>(a.k) + slot * row_stride + (uint64_t)kvh * D;
+    const uint16_t* vr = reinterpret_cast<const uint16_t*>(a.v) + slot * row_stride + (uint64_t)kvh * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      kb[k] = *reinterpret_cast<const frag_t*>(kr + 32 * k + 8 * g4);
+      vb[k] = *reinterpret_cast<const frag_t*>(vr + 32 * k + 8 * g4);
+    }
+  }
+  floatx4_t dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dk[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    dv[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // keys of this lane's dK / dV accumulator rows: 4 g4 + e, e < 4
+  const int key_lo = it.tok_begin + wave * 16;
+
+  // Tile loads: thread t moves 16-byte piece t % PIECES of tile row
+  // t / PIECES of Q and dO (rows past the item's last are row 0 again,
+  // masked through lse2 = +inf); threads below 32 the row statistics.
+  const int lrow = tid / PIECES, lpiece = tid % PIECES;
+  const bool loader = tid < kBwdRowTile * PIECES;
+  auto row_addr = [&](int rho) -> uint64_t {  // element offset of tile row rho's query row
+    const int rg = rho < nrows ? rho : 0;
+    return ((uint64_t)(it.q_begin + rg / G) * a.hq + (uint64_t)kvh * G + rg % G);
+  };
+  u32x4_t pq = {0u, 0u, 0u, 0u}, pg = {0u, 0u, 0u, 0u};
+  float pl = 0.f, pd = 0.f;
+  int pp = 0;
+  auto fetch = [&](int r0) {
+    if (loader) {
+      const uint64_t row = row_addr(r0 + lrow);
+      pq = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + lpiece * 8);
+      pg = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * D + lpiece * 8);
+    }
+    if (tid < kBwdRowTile) {
+      const int rho = r0 + tid;
+      const uint64_t row = row_addr(rho);
+      const bool ok = rho < nrows;
+      pl = ok ? a.lse[row] * kLog2e : INFINITY;
+      pd = ok ? b.delta[row] : 0.f;
+      pp = a.q_pos[it.q_begin + (ok ? rho : 0) / G];
+    }
+  };
+  // transposed-read offsets: 16-lane group g4, lane 4 r + j -> tile row
+  // 4 g4 + r (+16 for the second read), dims 16 blk + 4 j
+  uint32_t troff[DB][2];
+#pragma unroll
+  for (int blk = 0; blk < DB; ++blk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 4 * g4 + (n >> 2) + 16 * h, dim = 16 * blk + 4 * (n & 3);
+      troff[blk][h] = (uint32_t)(tile_off<D>(row, dim >> 3) + (dim & 7) * 2);
+    }
+  auto tfrag = [&](const char* t, int blk) {
+    const short4_t v0 = lds_read_tr16(t + troff[blk][0]);
+    const short4_t v1 = lds_read_tr16(t + troff[blk][1]);
+    return __builtin_bit_cast(frag_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
+                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
+                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
+                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
+  };
+
+  if (nrows > 0) fetch(0);
+  for (int r0 = 0; r0 < nrows; r0 += kBwdRowTile) {
+    __syncthreads();  // every wave is done with the previous tile
+    if (loader) {
+      *reinterpret_cast<u32x4_t*>(qs + tile_off<D>(lrow, lpiece)) = pq;
+      *reinterpret_cast<u32x4_t*>(gs + tile_off<D>(lrow, lpiece)) = pg;
+    }
+    if (tid < kBwdRowTile) {
+      lse2s[tid] = pl;
+      dls[tid] = pd;
+      poss[tid] = pp;
+    }
+    __syncthreads();
+    if (r0 + kBwdRowTile < nrows) fetch(r0 + kBwdRowTile);
+
+    // S and dP of the two 16-row halves
+    floatx4_t s[2], dp[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      s[h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      dp[h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const frag_t qa = *reinterpret_cast<const frag_t*>(qs + tile_off<D>(16 * h + n, 4 * k + g4));
+        const frag_t ga = *reinterpret_cast<const frag_t*>(gs + tile_off<D>(16 * h + n, 4 * k + g4));
+        s[h] = mfma_16x16x32<T>(qa, kb[k], s[h]);
+        dp[h] = mfma_16x16x32<T>(ga, vb[k], dp[h]);
+      }
+    }
+    // P and dS; lane (n, g4) element e of half h is row 16 h + 4 g4 + e, key n
+    uint32_t pw[4], dw[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const floatx4_t l4 = *reinterpret_cast<const floatx4_t*>(lse2s + 16 * h + 4 * g4);
+      const floatx4_t d4 = *reinterpret_cast<const floatx4_t*>(dls + 16 * h + 4 * g4);
+      float p[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = poss[16 * h + 4 * g4 + e];
+        const bool vis = key_ok && (!a.causal || my_key <= pos) && (a.window == 0 || my_key > pos - a.window);
+        p[e] = vis ? fast_exp2(__builtin_fmaf(s[h][e], c2, -l4[e])) : 0.f;
+        ds[e] = p[e] * (dp[h][e] - d4[e]) * a.scale;
+      }
+      pw[2 * h] = Pair16<T>::pack(p[0], p[1]);
+      pw[2 * h + 1] = Pair16<T>::pack(p[2], p[3]);
+      dw[2 * h] = Pair16<T>::pack(ds[0], ds[1]);
+      dw[2 * h + 1] = Pair16<T>::pack(ds[2], ds[3]);
+    }
+    const frag_t pf = __builtin_bit_cast(frag_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    const frag_t df = __builtin_bit_cast(frag_t, make_uint4(dw[0], dw[1], dw[2], dw[3]));
+    // dV += P^T dO, dK += dS^T Q over the tile's 32 rows
+#pragma unroll
+    for (int blk = 0; blk < DB; ++blk) {
+      dv[blk] = mfma_16x16x32<T>(pf, tfrag(gs, blk), dv[blk]);
+      dk[blk] = mfma_16x16x32<T>(df, tfrag(qs, blk), dk[blk]);
+    }
+  }
+
+  // lane (n, g4) of block blk holds dims 16 blk + n of keys key_lo + 4 g4 + e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = key_lo + 4 * g4 + e;
+    if (t >= it.tok_end) continue;
+    const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+    const uint64_t base = slot * row_stride + (uint64_t)kvh * D + n;
+#pragma unroll
+    for (int blk = 0; blk < DB; ++blk) {
+      store_out<T>(b.dk, base + 16 * blk, dk[blk][e]);
+      store_out<T>(b.dv, base + 16 * blk, dv[blk][e]);
+    }
+  }
+}
+
+// dQ of one tile of up to kBwdQRows query rows (queries q_begin .. q_end of
+// one sequence times the G heads of one KV head) on 16-bit MFMA: eight waves
+// of 16 rows; the keys the tile sees stream through LDS 32 at a time.  The
+// mirror image of bwd_dkv_mfma_kernel: Q^T and dO^T of the wave's rows stay
+// in registers,
+//   S^T = K Q^T, dP^T = V dO^T          (keys x rows, per 16-key half)
+//   P^T, dS^T as there (row statistics are per lane: lane column = row)
+//   dQ += dS K                          (rows x dims; dS straight from the
+//                                        dS^T accumulators, K columns by
+//                                        transposed LDS reads)
+constexpr int kBwdKeyTile = 32;
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdArgs b, int first_item, int G) {
+  constexpr int KS = D / 32, DB = D / 16, PIECES = D / 8;
+  constexpr int TILE = kBwdKeyTile * D * 2;
+  static_assert(kBwdMfmaWaves * 16 == kBwdQRows, "eight waves of 16 rows");
+  __shared__ __attribute__((aligned(16))) char ks[TILE];
+  __shared__ __attribute__((aligned(16))) char vs[TILE];
+  const KernelArgs& a = b.a;
+  const BwdItem it = b.items[first_item + blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = lane & 15, g4 = lane >> 4;
+  const int kvh = it.kvh;
+  const int ps = 1 << a.page_shift;
+  const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
+  const uint64_t row_stride = (uint64_t)a.hkv * D;
+  const int nrows = (it.q_end - it.q_begin) * G;
+  const float c2 = a.scale_log2;
+
+  // this lane's row (MFMA column n): Q^T and dO^T operands, statistics, position
+  const int my_row = wave * 16 + n;
+  const bool row_ok = my_row < nrows;
+  const int rg = row_ok ? my_row : 0;
+  const uint64_t row = (uint64_t)(it.q_begin + rg / G) * a.hq + (uint64_t)kvh * G + rg % G;
+  frag_t qb[KS], gb[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    qb[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + 32 * k + 8 * g4);
+    gb[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * D + 32 * k + 8 * g4);
+  }
+  const float l2 = row_ok ? a.lse[row] * kLog2e : INFINITY;
+  const float dl = row_ok ? b.delta[row] : 0.f;
+  const int pos = a.q_pos[it.q_begin + rg / G];
+  floatx4_t dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dq[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // tile loads: thread t moves piece t % PIECES of key t / PIECES of K and V
+  const int lkey = tid / PIECES, lpiece = tid % PIECES;
+  const bool loader = tid < kBwdKeyTile * PIECES;
+  u32x4_t pk = {0u, 0u, 0u, 0u}, pv = {0u, 0u, 0u, 0u};
+  auto fetch = [&](int t0) {
+    if (loader) {
+      const int t = min(t0 + lkey, it.tok_end - 1);
+      const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+      const uint64_t off = slot * row_stride + (uint64_t)kvh * D + lpiece * 8;
+      pk = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.k) + off);
+      pv = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.v) + off);
+    }
+  };
+  uint32_t troff[DB][2];
+#pragma unroll
+  for (int blk = 0; blk < DB; ++blk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = 4 * g4 + (n >> 2) + 16 * h, dim = 16 * blk + 4 * (n & 3);
+      troff[blk][h] = (uint32_t)(tile_off<D>(key, dim >> 3) + (dim & 7) * 2);
+    }
+  auto tfrag = [&](const char* t, int blk) {
+    const short4_t v0 = lds_read_tr16(t + troff[blk][0]);
+    const short4_t v1 = lds_read_tr16(t + troff[blk][1]);
+    return __builtin_bit_cast(frag_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
+                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
+                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
+                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
+  };
+
+  fetch(it.tok_begin);
+  for (int t0 = it.tok_begin; t0 < it.tok_end; t0 += kBwdKeyTile) {
+    __syncthreads();  // every wave is done with the previous tile
+    if (loader) {
+      *reinterpret_cast<u32x4_t*>(ks + tile_off<D>(lkey, lpiece)) = pk;
+      *reinterpret_cast<u32x4_t*>(vs + tile_off<D>(lkey, lpiece)) = pv;
+    }
+    __syncthreads();
+    if (t0 + kBwdKeyTile < it.tok_end) fetch(t0 + kBwdKeyTile);
+
+    uint32_t dw[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      floatx4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const frag_t ka = *reinterpret_cast<const frag_t*>(ks + tile_off<D>(16 * h + n, 4 * k + g4));
+        const frag_t va = *reinterpret_cast<const frag_t*>(vs + tile_off<D>(16 * h + n, 4 * k + g4));
+        s = mfma_16x16x32<T>(ka, qb[k], s);
+        dp = mfma_16x16x32<T>(va, gb[k], dp);
+      }
+      // lane (n, g4) element e: key t0 + 16 h + 4 g4 + e, row my_row
+      float ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + 16 * h + 4 * g4 + e;
+        const bool vis = row_ok && t < it.tok_end && (!a.causal || t <= pos) && (a.window == 0 || t > pos - a.window);
+        const float p = vis ? fast_exp2(__builtin_fmaf(s[e], c2, -l2)) : 0.f;
+        ds[e] = p * (dp[e] - dl) * a.scale;
+      }
+      dw[2 * h] = Pair16<T>::pack(ds[0], ds[1]);
+      dw[2 * h + 1] = Pair16<T>::pack(ds[2], ds[3]);
+    }
+    const frag_t df = __builtin_bit_cast(frag_t, make_uint4(dw[0], dw[1], dw[2], dw[3]));
+#pragma unroll
+    for (int blk = 0; blk < DB; ++blk) dq[blk] = mfma_16x16x32<T>(df, tfrag(ks, blk), dq[blk]);
+  }
+
+  // lane (n, g4) of block blk holds dims 16 blk + n of rows wave 16 + 4 g4 + e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = wave * 16 + 4 * g4 + e;
+    if (r >= nrows) continue;
+    const uint64_t orow = (uint64_t)(it.q_begin + r / G) * a.hq + (uint64_t)kvh * G + r % G;
+#pragma unroll
+    for (int blk = 0; blk < DB; ++blk) store_out<T>(b.dq, orow * D + 16 * blk + n, dq[blk][e]);
+  }
 }
 
 namespace {
 
-using BwdFn = hipError_t (*)(const BwdArgs&, int, int, hipStream_t);
+using BwdFn = hipError_t (*)(const BwdArgs&, int, int, int, hipStream_t);
 
+// items: [0, n_dq) dQ per (query, KV head), [n_dq, n_dq + n_kv) dK/dV per
+// key block, then n_dqt dQ row tiles
 template <typename T, int D, int DV, int G>
-hipError_t launch_bwd_t(const BwdArgs& b, int n_dq, int n_kv, hipStream_t stream) {
-  if (n_dq > 0) {
+hipError_t launch_bwd_t(const BwdArgs& b, int n_dq, int n_kv, int n_dqt, hipStream_t stream) {
+  constexpr bool kMfma = sizeof(T) == 2 && D == DV && (D == 64 || D == 128);
+  if (kMfma && n_dqt > 0) {
+    if constexpr (kMfma)
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D>), dim3(n_dqt), dim3(kBwdMfmaWaves * kWave), 0, stream, b,
+                         n_dq + n_kv, G);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (n_dq > 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, DV, G>), dim3(n_dq), dim3(kBwdDqWaves * kWave), 0, stream, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (n_kv > 0) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, DV, G>), dim3(n_kv), dim3(kBwdKvWaves * kWave), 0, stream, b, n_dq);
+    if constexpr (kMfma)
+      hipLaunchKernelGGL((bwd_dkv_mfma_kernel<T, D>), dim3(n_kv), dim3(kBwdMfmaWaves * kWave), 0, stream, b, n_dq, G);
+    else
+      hipLaunchKernelGGL((bwd_dkv_kernel<T, D, DV, G>), dim3(n_kv), dim3(kBwdKvWaves * kWave), 0, stream, b, n_dq);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -295,7 +627,7 @@ BwdFn pick_bwd(int dtype, int d, int dv, int g) {
 bool bwd_supported(int dtype, int d, int dv, int g) { return pick_bwd(dtype, d, dv, g) != nullptr; }
 
 hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, const void* dout, void* dq, void* dk,
-                          void* dvp, float* delta, const BwdItem* items, int n_dq, int n_kv, int64_t rows,
+                          void* dvp, float* delta, const BwdItem* items, int n_dq, int n_kv, int n_dqt, int64_t rows,
                           int64_t pool_slots, int n_cu, hipStream_t stream) {
   BwdFn f = pick_bwd(dtype, d, dv, g);
   if (!f) return hipErrorInvalidValue;
@@ -322,7 +654,7 @@ hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return f(b, n_dq, n_kv, stream);
+  return f(b, n_dq, n_kv, n_dqt, stream);
 }
 
 }  // namespace pa

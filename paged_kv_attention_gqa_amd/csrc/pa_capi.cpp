@@ -90,7 +90,7 @@ struct pa_plan {
   // backward (GQA plans): dQ items, then dK/dV items; a page that two key
   // positions share (-1: none) makes the single-writer dK/dV pass impossible
   std::vector<pa::BwdItem> bwd_items;
-  int32_t n_bwd_dq = 0, n_bwd_kv = 0;
+  int32_t n_bwd_dq = 0, n_bwd_kv = 0, n_bwd_dqt = 0;
   int32_t shared_page = -1;
   // device copy: one allocation
   std::vector<char> blob;
@@ -415,7 +415,9 @@ void build_work(pa_plan* p) {
 
 // Backward work (ruDNN `attention_backward`: scores recomputed from Q and K,
 // a second scan of the history).  dQ: one item per (query, KV head) over the
-// query's visible keys.  dK/dV: one item per (block of kBwdBlockKeys keys,
+// query's visible keys (vector kernel), and one per tile of kBwdQRows query
+// rows and KV head over the union of their visible keys (MFMA kernel; the
+// launch picks one list by data type and head size).  dK/dV: one item per (block of kBwdBlockKeys keys,
 // KV head) of every sequence with queries, skipping blocks no query sees;
 // every pool row then has a single writer, which needs each referenced page
 // to hold key positions of one sequence only.  Both lists run longest first.
@@ -433,7 +435,8 @@ void build_bwd(pa_plan* p) {
       owner[page] = s;
     }
   }
-  std::vector<std::pair<int64_t, pa::BwdItem>> dq, kv;
+  std::vector<std::pair<int64_t, pa::BwdItem>> dq, kv, dqt;
+  const int tile_q = std::max(1, pa::kBwdQRows / p->group());
   for (int s = 0; s < p->S; ++s) {
     const int q0 = p->cu_q[s], q1 = p->cu_q[s + 1], L = p->seq_lens[s];
     if (q0 == q1) continue;
@@ -441,6 +444,18 @@ void build_bwd(pa_plan* p) {
       int lo, hi;
       visible_range(p->q_pos[i], L, p->causal, p->window, &lo, &hi);
       for (int kvh = 0; kvh < p->hkv; ++kvh) dq.push_back({hi + 1 - lo, pa::BwdItem{s, kvh, i, i + 1, lo, hi + 1}});
+    }
+    for (int a0 = q0; a0 < q1; a0 += tile_q) {
+      const int a1 = std::min(q1, a0 + tile_q);
+      int lo = INT32_MAX, hi = -1;
+      for (int i = a0; i < a1; ++i) {
+        int x, y;
+        visible_range(p->q_pos[i], L, p->causal, p->window, &x, &y);
+        lo = std::min(lo, x);
+        hi = std::max(hi, y);
+      }
+      for (int kvh = 0; kvh < p->hkv; ++kvh)
+        dqt.push_back({(int64_t)(hi + 1 - lo) * (a1 - a0), pa::BwdItem{s, kvh, a0, a1, lo, hi + 1}});
     }
     for (int t0 = 0; t0 < L; t0 += pa::kBwdBlockKeys) {
       const int t1 = std::min(L, t0 + pa::kBwdBlockKeys);
@@ -459,11 +474,14 @@ void build_bwd(pa_plan* p) {
   };
   std::stable_sort(dq.begin(), dq.end(), longest_first);
   std::stable_sort(kv.begin(), kv.end(), longest_first);
+  std::stable_sort(dqt.begin(), dqt.end(), longest_first);
   p->bwd_items.clear();
   for (auto& x : dq) p->bwd_items.push_back(x.second);
   for (auto& x : kv) p->bwd_items.push_back(x.second);
+  for (auto& x : dqt) p->bwd_items.push_back(x.second);
   p->n_bwd_dq = (int32_t)dq.size();
   p->n_bwd_kv = (int32_t)kv.size();
+  p->n_bwd_dqt = (int32_t)dqt.size();
 }
 
 // Workspace: partial sums [slots, G, Dv] | (max, sum, unrounded sum) [slots, G, 3].
@@ -1003,7 +1021,7 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   a.window = plan->window;
   hipError_t e = pa::launch_gqa_bwd(dtype, head_dim, v_head_dim, G, a, dout, dq, dk_pool, dv_pool,
                                     reinterpret_cast<float*>(workspace), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv,
-                                    (int64_t)rows, (int64_t)slots, std::max(plan->n_cu, 1), st);
+                                    plan->n_bwd_dqt, (int64_t)rows, (int64_t)slots, std::max(plan->n_cu, 1), st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }

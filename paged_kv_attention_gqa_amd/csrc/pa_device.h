@@ -39,15 +39,18 @@ struct MergeItem {
 };
 
 // One unit of backward work.  dQ items: one query (q_end = q_begin + 1) and
-// one KV head over that query's visible keys [tok_begin, tok_end).  dK/dV
-// items: one block of keys [tok_begin, tok_end) of one sequence and KV head
-// against the sequence's queries [q_begin, q_end).
+// one KV head over that query's visible keys [tok_begin, tok_end); dQ tile
+// items: up to kBwdQRows / G consecutive queries of one sequence and one KV
+// head over the union of their visible keys.  dK/dV items: one block of keys
+// [tok_begin, tok_end) of one sequence and KV head against the sequence's
+// queries [q_begin, q_end).
 struct BwdItem {
   int32_t seq, kvh;
   int32_t q_begin, q_end;
   int32_t tok_begin, tok_end;
 };
-constexpr int kBwdBlockKeys = 64;  // keys of one dK/dV item
+constexpr int kBwdBlockKeys = 128;  // keys of one dK/dV item
+constexpr int kBwdQRows = 128;      // query rows (query, head of the group) of one dQ tile item
 
 struct KernelArgs {
   const void* q;          // [Q, Hq, D]            (MLA: absorbed query [Q, H, R])

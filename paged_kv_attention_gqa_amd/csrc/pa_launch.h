@@ -41,11 +41,12 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, voi
                          int64_t queries, int heads, int k_row_bytes, int v_row_bytes, int n_cu, hipStream_t stream);
 
 // Paged GQA/MHA backward: zero dk / dv (pool shaped, pool_slots rows of each),
-// D = dO . O for the `rows` (query, head) rows into delta, then dQ over items
-// [0, n_dq) and dK / dV over items [n_dq, n_dq + n_kv).
+// D = dO . O for the `rows` (query, head) rows into delta, then dQ (per-query
+// items [0, n_dq), or on MFMA the row tiles [n_dq + n_kv, + n_dqt)) and
+// dK / dV over items [n_dq, n_dq + n_kv).
 bool bwd_supported(int dtype, int d, int dv, int g);
 hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, const void* dout, void* dq, void* dk,
-                          void* dvp, float* delta, const BwdItem* items, int n_dq, int n_kv, int64_t rows,
+                          void* dvp, float* delta, const BwdItem* items, int n_dq, int n_kv, int n_dqt, int64_t rows,
                           int64_t pool_slots, int n_cu, hipStream_t stream);
 
 
