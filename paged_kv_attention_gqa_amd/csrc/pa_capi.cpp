@@ -414,7 +414,8 @@ void build_work(pa_plan* p) {
 }
 
 // Backward work (ruDNN `attention_backward`: scores recomputed from Q and K,
-// a second scan of the history).  dQ: one item per (query, KV head) over the
+// a second scan of the history).  dK/dV items stream only the queries from
+// the first to the last that see their block.  dQ: one item per (query, KV head) over the
 // query's visible keys (vector kernel), and one per tile of kBwdQRows query
 // rows and KV head over the union of their visible keys (MFMA kernel; the
 // launch picks one list by data type and head size).  dK/dV: one item per (block of kBwdBlockKeys keys,
@@ -459,14 +460,19 @@ void build_bwd(pa_plan* p) {
     }
     for (int t0 = 0; t0 < L; t0 += pa::kBwdBlockKeys) {
       const int t1 = std::min(L, t0 + pa::kBwdBlockKeys);
-      int64_t rows = 0;  // queries that see a key of the block
+      int64_t rows = 0;  // queries that see a key of the block, and the first and last of them
+      int first = -1, last = -1;
       for (int i = q0; i < q1; ++i) {
         int lo, hi;
         visible_range(p->q_pos[i], L, p->causal, p->window, &lo, &hi);
-        rows += (lo < t1 && hi >= t0);
+        if (lo < t1 && hi >= t0) {
+          ++rows;
+          if (first < 0) first = i;
+          last = i;
+        }
       }
       if (rows == 0) continue;
-      for (int kvh = 0; kvh < p->hkv; ++kvh) kv.push_back({rows, pa::BwdItem{s, kvh, q0, q1, t0, t1}});
+      for (int kvh = 0; kvh < p->hkv; ++kvh) kv.push_back({rows, pa::BwdItem{s, kvh, first, last + 1, t0, t1}});
     }
   }
   auto longest_first = [](const std::pair<int64_t, pa::BwdItem>& a, const std::pair<int64_t, pa::BwdItem>& b) {
