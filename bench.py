@@ -127,18 +127,19 @@ def _is_mla(b):
 
 
 def split_work(b):
-    """Algorithmic work split by role: (decode K/V bytes, prefill flops) for
-    GQA batches, where decode queries are sequences with at most 4 queries."""
+    """Algorithmic work split by role: (decode K/V bytes, prefill flops), where
+    decode queries are sequences with at most 4 queries."""
     vis = visible_counts(b)
     counts = np.diff(b.cu_q)
     es = 4 if b.dtype == "f32" else 2
+    mla = _is_mla(b)
     dec_b, pre_f = 0, 0
     for s in range(b.num_seqs):
         v = int(vis[b.cu_q[s]:b.cu_q[s + 1]].sum())
         if counts[s] <= 4:
-            dec_b += v * b.hkv * (b.d + b.dv) * es
+            dec_b += v * ((b.r + b.p) * es if mla else b.hkv * (b.d + b.dv) * es)
         else:
-            pre_f += v * b.hq * 2 * (b.d + b.dv)
+            pre_f += v * (b.heads * (2 * (b.r + b.p) + 2 * b.r) if mla else b.hq * 2 * (b.d + b.dv))
     return dec_b, pre_f
 
 
@@ -221,7 +222,7 @@ def summarize(name, r):
     step_s = r["ms_per_step"] * 1e-3
     out = {"workload": name, "ms_per_step": round(r["ms_per_step"], 5), "main_kernel_ms": round(r["main_ms"], 5),
            "merge_kernel_ms": round(r["merge_ms"], 5), "kv_bytes": kv_bytes, "flops": flops}
-    if r["mla"] or r["info"]["prefill_items"] == 0:
+    if r["info"]["prefill_items"] == 0:
         out.update(bound="hbm", step_gbs=round(kv_bytes / step_s / 1e9, 2),
                    kernel_gbs=round(kv_bytes / main_s / 1e9, 2),
                    frac=round(kv_bytes / main_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -334,7 +335,7 @@ def measure_backward(name, steps, warmup):
 
 
 PRIMARY = "bf16_decode_batch"
-SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode")
+SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode", "bf16_mla_chunked_prefill")
 APPEND = ("bf16_decode_batch", "bf16_chunked_prefill")  # cache writes of one decode step and of one chunk
 BACKWARD = ("bf16_chunked_prefill",)  # gradients of one chunk step
 

@@ -367,7 +367,7 @@ void build_work(pa_plan* p) {
   std::vector<WorkItem> dec, pre;
   const int G = p->group();
   bool has_prefill = false;
-  for (int s = 0; s < p->S && !p->mla; ++s) has_prefill |= (p->cu_q[s + 1] - p->cu_q[s]) > kDecodeMaxQueries;
+  for (int s = 0; s < p->S; ++s) has_prefill |= (p->cu_q[s + 1] - p->cu_q[s]) > kDecodeMaxQueries;
   if (!has_prefill && p->split_tokens == 0 && p->max_splits > 1 && p->n_cu > 0) {
     int per_cu = pa::mla_wgs_per_cu();
     if (!p->mla) {
@@ -389,8 +389,22 @@ void build_work(pa_plan* p) {
     const int q0 = p->cu_q[s], q1 = p->cu_q[s + 1];
     const int nq = q1 - q0;
     if (nq == 0) continue;
-    if (p->mla || nq <= kDecodeMaxQueries) {
+    if (nq <= kDecodeMaxQueries) {
       for (int i = q0; i < q1; ++i) plan_decode_row(p, s, i, split_tokens, dec);
+    } else if (p->mla) {
+      // MLA chunks: items of kMlaPrefillQueries consecutive queries over the
+      // union of their visible keys, one query per wave
+      for (int t0 = q0; t0 < q1; t0 += pa::kMlaPrefillQueries) {
+        const int t1 = std::min(q1, t0 + pa::kMlaPrefillQueries);
+        int lo = INT32_MAX, hi = -1;
+        for (int i = t0; i < t1; ++i) {
+          int a, b;
+          visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &a, &b);
+          lo = std::min(lo, a);
+          hi = std::max(hi, b);
+        }
+        pre.push_back(WorkItem{pa::kPrefill, 0, s, t0, t1 - t0, lo, hi + 1, -1});
+      }
     } else {
       const int tile_q = std::max(1, kPrefillRows / G);
       for (int kvh = 0; kvh < p->hkv; ++kvh)
@@ -749,7 +763,7 @@ static int launch_common(FwdCall& c, bool is_mla) {
   }
   hipError_t e;
   if (is_mla) {
-    e = pa::launch_mla_main(c.dtype, c.args, c.stream);
+    e = pa::launch_mla_main(c.dtype, p->n_prefill > 0, c.args, c.stream);
   } else {
     e = pa::launch_gqa_main(c.dtype, c.d, c.dv, p->group(), p->n_prefill > 0, c.args, c.stream);
   }

@@ -50,6 +50,7 @@ struct BwdItem {
   int32_t tok_begin, tok_end;
 };
 constexpr int kBwdBlockKeys = 128;  // keys of one dK/dV item
+constexpr int kMlaPrefillQueries = 2;  // queries of one absorbed-MLA chunked-prefill item (two waves each)
 constexpr int kBwdQRows = 128;      // query rows (query, head of the group) of one dQ tile item
 
 struct KernelArgs {

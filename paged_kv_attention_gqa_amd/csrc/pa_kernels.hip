@@ -82,9 +82,12 @@ void mixed_kernel(KernelArgs a) {
   }
 }
 
-// Absorbed-MLA decode: one (query, key range) item per workgroup, a 72 KB
-// LDS tile ring, two workgroups per CU.
-template <typename T>
+// Absorbed MLA: decode items (one query, one key range) and, in plans that
+// have them (PREFILL), chunked-prefill items (two queries, two waves each);
+// a 72 KB LDS tile ring, two workgroups per CU.  Decode-only plans run the
+// instantiation without the prefill body, whose 128 output registers per
+// wave would otherwise set the register allocation of the decode body too.
+template <typename T, bool PREFILL>
 __global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_eu(2))) void mla_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[MlaSmem::kBytes];
   const int first = a.wg_first[blockIdx.x], last = a.wg_first[blockIdx.x + 1];
@@ -94,7 +97,10 @@ __global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_e
     if (it.kind == kEmpty) continue;
     if (i > first) __syncthreads();  // the previous item's waves are done with the LDS ring
     asm volatile("" : "+v"(tid));    // per-lane values are recomputed per item, not kept live
-    mla_item<T>(a, it, smem, tid);
+    if (PREFILL && it.kind == kPrefill)
+      mla_item<T, PREFILL>(a, it, smem, tid);
+    else
+      mla_item<T, false>(a, it, smem, tid);
   }
 }
 
@@ -233,13 +239,18 @@ bool mla_supported(int dtype, int h, int r, int p) {
   return (dtype == 1 || dtype == 2) && h == kMlaHeads && r == kMlaRank && p == kMlaRope;
 }
 
-hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream) {
+hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, hipStream_t stream) {
   if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
   if (a.n_wg > 0) {
-    if (dtype == 1)
-      hipLaunchKernelGGL((mla_kernel<uint16_t>), dim3(a.n_wg), dim3(kMlaWaves * kWave), 0, stream, a);
+    const dim3 grid(a.n_wg), block(kMlaWaves * kWave);
+    if (dtype == 1 && has_prefill)
+      hipLaunchKernelGGL((mla_kernel<uint16_t, true>), grid, block, 0, stream, a);
+    else if (dtype == 1)
+      hipLaunchKernelGGL((mla_kernel<uint16_t, false>), grid, block, 0, stream, a);
+    else if (has_prefill)
+      hipLaunchKernelGGL((mla_kernel<_Float16, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((mla_kernel<_Float16>), dim3(a.n_wg), dim3(kMlaWaves * kWave), 0, stream, a);
+      hipLaunchKernelGGL((mla_kernel<_Float16, false>), grid, block, 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;

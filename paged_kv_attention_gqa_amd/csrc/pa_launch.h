@@ -30,7 +30,8 @@ int mla_wgs_per_cu();
 
 // Absorbed MLA: h query heads, latent rank r, position width p.
 bool mla_supported(int dtype, int h, int r, int p);
-hipError_t launch_mla_main(int dtype, const KernelArgs& a, hipStream_t stream);
+// has_prefill: the item list holds chunked-prefill items.
+hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, hipStream_t stream);
 hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream);
 

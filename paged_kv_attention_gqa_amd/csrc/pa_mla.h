@@ -72,11 +72,20 @@ __device__ __forceinline__ int mla_off(int key, int piece) {
 }
 
 // tid: the thread index, as for decode_item.
-template <typename T>
+//
+// PREFILL: the item holds up to kMlaPrefillQueries consecutive queries of
+// one sequence (chunked prefill); waves 2 i and 2 i + 1 take query q_begin +
+// i, its 16 heads as the MFMA columns, each owning half of the R output dims
+// (both compute the query's scores), and mask the keys of the shared tiles
+// by that query's position.  The tiles are loaded once for the item's
+// queries.
+constexpr int kMlaWavesPerQuery = kMlaWaves / kMlaPrefillQueries;
+static_assert(kMlaWavesPerQuery == 2, "two waves per prefill query");
+template <typename T, bool PREFILL = false>
 __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it, char* smem, int tid = threadIdx.x) {
   constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = kMlaTileKeys;
   constexpr int KS_LAT = R / 32, KS_POS = P / 32;  // 16x16x32 k-steps
-  constexpr int DW = R / kMlaWaves;                 // output dims per wave
+  constexpr int DW = PREFILL ? R / kMlaWavesPerQuery : R / kMlaWaves;  // output dims per wave
   constexpr int DB = DW / 16;                       // 16-dim blocks of O^T per wave
   constexpr int ROWS_PER_WAVE = NT / kMlaWaves;     // latent rows each wave loads per tile
   constexpr int LOADS_PER_TILE = ROWS_PER_WAVE + 1; // + a quarter of the rotary tile
@@ -86,7 +95,11 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   // lookups in scalar registers and scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, c = lane >> 4;           // MFMA column (head / key row) and k-group
-  const int qi = it.q_begin;
+  const int wq = wave / kMlaWavesPerQuery;          // PREFILL: this wave's query of the item
+  const bool q_ok = !PREFILL || wq < it.q_count;
+  const int qi = it.q_begin + (PREFILL ? min(wq, it.q_count - 1) : 0);
+  const int qpos = PREFILL ? a.q_pos[qi] : 0;
+  const int dim0 = DW * (PREFILL ? wave % kMlaWavesPerQuery : wave);  // first output dim of this wave
   const int tb = it.tok_begin, te = it.tok_end;
   const int ps = 1 << a.page_shift;
   const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
@@ -200,22 +213,39 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
 
     // S^T: lane (n, c) holds keys 4 c + r (r = 0..3) of head n; two
     // accumulator chains halve the dependent MFMA latency
-    frag_t kf[KS_LAT + KS_POS];
+    floatx4_t s;
+    if constexpr (PREFILL) {
+      // fragments read as they are used (the output sums hold 128 registers)
+      floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int k = 0; k < KS_LAT; ++k) kf[k] = *reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * k + c));
+      for (int k = 0; k < KS_LAT; ++k)
+        sc[k & 1] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * k + c)), qa[k], sc[k & 1]);
 #pragma unroll
-    for (int k = 0; k < KS_POS; ++k)
-      kf[KS_LAT + k] = *reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * k + c));
-    floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      for (int k = 0; k < KS_POS; ++k)
+        sc[k & 1] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * k + c)), qp[k], sc[k & 1]);
+      s = sc[0] + sc[1];
+    } else {
+      frag_t kf[KS_LAT + KS_POS];
 #pragma unroll
-    for (int k = 0; k < KS_LAT; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[k], qa[k], sc[k & 1]);
+      for (int k = 0; k < KS_LAT; ++k) kf[k] = *reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * k + c));
 #pragma unroll
-    for (int k = 0; k < KS_POS; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[KS_LAT + k], qp[k], sc[k & 1]);
-    floatx4_t s = sc[0] + sc[1];
+      for (int k = 0; k < KS_POS; ++k)
+        kf[KS_LAT + k] = *reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * k + c));
+      floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int k = 0; k < KS_LAT; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[k], qa[k], sc[k & 1]);
+#pragma unroll
+      for (int k = 0; k < KS_POS; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[KS_LAT + k], qp[k], sc[k & 1]);
+      s = sc[0] + sc[1];
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 4 * c + r;
-      s[r] = (t >= tb && t < te) ? s[r] : -INFINITY;
+      if constexpr (PREFILL)
+        s[r] = (t >= tb && t < te && (!a.causal || t <= qpos) && (a.window == 0 || t > qpos - a.window)) ? s[r]
+                                                                                                     : -INFINITY;
+      else
+        s[r] = (t >= tb && t < te) ? s[r] : -INFINITY;
     }
 
     // Online softmax against a lazily raised reference max (weights stay
@@ -241,28 +271,44 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
     lx += (p[0] + p[1]) + (p[2] + p[3]);
     const short4_t pf = __builtin_bit_cast(short4_t, make_uint2(w0, w1));
 
-    // O^T block b (dims DW wave + 16 b ..): lane (i = lane % 16, c) needs
-    // latent[4 c + r][DW wave + 16 b + i]: one transposed read, lane 4 r + j
-    // giving the address of dims DW wave + 16 b + 4 j of key row 4 c + r.
+    // O^T block b (dims dim0 + 16 b ..): lane (i = lane % 16, c) needs
+    // latent[4 c + r][dim0 + 16 b + i]: one transposed read, lane 4 r + j
+    // giving the address of dims dim0 + 16 b + 4 j of key row 4 c + r.
     const int key = 4 * c + (n >> 2);
-    short4_t vf[DB];
+    if constexpr (PREFILL) {
+      constexpr int VB = 8;  // fragments read per group (the output sums hold 128 registers)
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const int dim = DW * wave + 16 * b + 4 * (n & 3);
-      vf[b] = lds_read_tr16(ls + mla_off<R>(key, dim >> 3) + (dim & 7) * 2);
+      for (int b0 = 0; b0 < DB; b0 += VB) {
+        short4_t vf[VB];
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          const int dim = dim0 + 16 * (b0 + b) + 4 * (n & 3);
+          vf[b] = lds_read_tr16(ls + mla_off<R>(key, dim >> 3) + (dim & 7) * 2);
+        }
+#pragma unroll
+        for (int b = 0; b < VB; ++b) o[b0 + b] = mfma_16x16x16<T>(vf[b], pf, o[b0 + b]);
+      }
+    } else {
+      short4_t vf[DB];
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const int dim = DW * wave + 16 * b + 4 * (n & 3);
+        vf[b] = lds_read_tr16(ls + mla_off<R>(key, dim >> 3) + (dim & 7) * 2);
+      }
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b] = mfma_16x16x16<T>(vf[b], pf, o[b]);
     }
-#pragma unroll
-    for (int b = 0; b < DB; ++b) o[b] = mfma_16x16x16<T>(vf[b], pf, o[b]);
   }
 
   // full row sums: the four k-groups of lanes hold different keys
   l = pair32_sum(pair16_sum(l));
   lx = pair32_sum(pair16_sum(lx));
 
-  // O^T lane (n, c) element r is dim DW wave + 16 b + 4 c + r of head n
-  if (it.slot < 0) {
+  // O^T lane (n, c) element r is dim dim0 + 16 b + 4 c + r of head n
+  if (PREFILL || it.slot < 0) {
+    if (PREFILL && !q_ok) return;
     const float inv = 1.f / l;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * H + n) * R + DW * wave;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * H + n) * R + (PREFILL ? dim0 : DW * wave);
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       uint2 w;
@@ -270,7 +316,8 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       w.y = Pair16<T>::pack(o[b][2] * inv, o[b][3] * inv);
       *reinterpret_cast<uint2*>(orow + 16 * b + 4 * c) = w;
     }
-    if (a.lse && wave == 0 && c == 0) a.lse[(uint64_t)qi * H + n] = m * a.scale + logf(lx);
+    if (a.lse && (PREFILL ? wave % kMlaWavesPerQuery : wave) == 0 && c == 0)
+      a.lse[(uint64_t)qi * H + n] = m * a.scale + logf(lx);
   } else {
     float* dst = a.ws_o + ((uint64_t)it.slot * H + n) * R + DW * wave;
 #pragma unroll

@@ -332,12 +332,32 @@ def config_bf16_mla_decode(seed: int = 5) -> MlaBatch:
                     H, R, P, 1.0 / math.sqrt(576.0), True, 0, q_abs, q_rope, latent, kpos, seed, 16)
 
 
+def config_bf16_mla_chunked_prefill(seed: int = 6) -> MlaBatch:
+    """bf16 absorbed-MLA chunked prefill (a workload of this library, beside
+    the MLA decode one): 8 sequences, each a 256-query chunk after a history
+    uniform in [0, 4096], H=16, R=512, P=64, page 64, unit-RMS latent rows,
+    scale 1/sqrt(576), causal."""
+    rng = np.random.default_rng(seed)
+    S, H, R, P, ps, C = 8, 16, 512, 64, 64, 256
+    hist = rng.integers(0, 4096 + 1, size=S)
+    seq_lens = (hist + C).astype(np.int32)
+    bt, pool, _ = _tables(rng, seq_lens, ps)
+    q_pos = np.concatenate([np.arange(h, h + C, dtype=np.int32) for h in hist])
+    q_abs = _normal(rng, (S * C, H, R), "bf16")
+    q_rope = _normal(rng, (S * C, H, P), "bf16")
+    latent = _unit_rms(rng, (pool, ps, 1, R))
+    kpos = _normal(rng, (pool, ps, 1, P), "bf16")
+    return MlaBatch("bf16_mla_chunked_prefill", "bf16", seq_lens, _packed([C] * S), q_pos, bt, ps, pool,
+                    H, R, P, 1.0 / math.sqrt(576.0), True, 0, q_abs, q_rope, latent, kpos, seed, 16)
+
+
 CONFIGS: Dict[str, Callable] = {
     "tiny_f32_decode": config_tiny_f32_decode,
     "bf16_decode_batch": config_bf16_decode_batch,
     "bf16_chunked_prefill": config_bf16_chunked_prefill,
     "bf16_mixed_batch": config_bf16_mixed_batch,
     "bf16_mla_decode": config_bf16_mla_decode,
+    "bf16_mla_chunked_prefill": config_bf16_mla_chunked_prefill,
 }
 
 

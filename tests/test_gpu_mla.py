@@ -91,3 +91,63 @@ def test_mla_64k_key_row(max_splits):
     times)."""
     m = random_mla_batch(3100, page_size=64, q_counts=(1,), histories=[65535], max_splits=max_splits)
     _parity(m)
+
+
+MLA_PREFILL_CASES = [
+    dict(page_size=64, q_counts=(64, 1, 17), max_len=1500),
+    dict(page_size=16, q_counts=(33,), histories=[0]),
+    dict(page_size=64, q_counts=(40, 5), max_len=2000, window=300),
+    dict(page_size=32, q_counts=(9, 1), max_len=900, causal=False),
+    dict(page_size=1, q_counts=(7,), max_len=100),
+    dict(page_size=64, q_counts=(0, 12, 0, 1, 3), histories=[50, 600, 0, 20, 90]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("i", range(len(MLA_PREFILL_CASES)))
+def test_mla_chunked_prefill_parity(i, dtype):
+    """Sequences with more than four queries run as chunked-prefill items (two
+    queries per workgroup sharing the latent tiles), next to decode items."""
+    m = random_mla_batch(3600 + i, dtype=dtype, **MLA_PREFILL_CASES[i])
+    run = MlaRun(m)
+    run()
+    out, lse = run.result()
+    ref_o, ref_l = oracle.mla(m)
+    assert_close(out, ref_o, dtype)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-3)
+    assert run.info["prefill_items"] > 0
+
+
+def test_mla_chunked_prefill_window_one_bitwise():
+    m = random_mla_batch(3700, page_size=64, q_counts=(30, 1, 9), max_len=1500, window=1)
+    run = MlaRun(m)
+    run()
+    out, _ = run.result()
+    lat = to_f64(run.latent)
+    for s in range(m.num_seqs):
+        for i in range(int(m.cu_q[s]), int(m.cu_q[s + 1])):
+            p = int(m.q_pos[i])
+            row = lat[m.block_table[s, p // m.page_size], p % m.page_size, 0]
+            for h in range(m.heads):
+                assert np.array_equal(out[i, h], row), (i, h)
+
+
+def test_mla_chunked_prefill_full_size_sampled():
+    """The MLA chunked-prefill workload (8 chunks of 256 queries after
+    histories of up to 4096 keys) on sampled rows plus every head of each
+    chunk's first and last query."""
+    from synth import config_bf16_mla_chunked_prefill
+    m = config_bf16_mla_chunked_prefill()
+    run = MlaRun(m)
+    run()
+    out, lse = run.result()
+    rng = np.random.default_rng(3800)
+    rows = set(rng.integers(0, m.num_queries * m.heads, size=1500).tolist())
+    for s in range(m.num_seqs):
+        for i in (int(m.cu_q[s]), int(m.cu_q[s + 1]) - 1):
+            rows.update(range(i * m.heads, (i + 1) * m.heads))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    ref_o, ref_l = oracle.mla(m, rows=rows)
+    assert_close(out.reshape(-1, m.r)[rows], ref_o, "bf16")
+    np.testing.assert_allclose(lse.reshape(-1)[rows], ref_l, rtol=0, atol=1e-3)
+    assert run.info["prefill_items"] > 0 and run.info["decode_items"] == 0
