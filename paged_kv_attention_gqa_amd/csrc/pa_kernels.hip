@@ -4,6 +4,7 @@
 #include "pa_launch.h"
 #include "pa_mla.h"
 #include "pa_prefill.h"
+#include "pa_prefill16.h"
 
 namespace pa {
 
@@ -59,8 +60,11 @@ void decode_kernel(KernelArgs a) {
 template <typename T, int D, int DV, int G>
 struct MixedShape {
   static constexpr bool kMfma = sizeof(T) == 2 && D == DV && (D == 64 || D == 128) && G <= kPrefillRows;
+  // K and V rows of different widths: the 16x16x32 MFMA tile
+  static constexpr bool kMfma16 = sizeof(T) == 2 && D != DV && D % 64 == 0 && DV % 64 == 0 && G <= kPrefillRows;
   static constexpr int kDecodeBytes = kPrefillWaves * G * (DV + 3) * 4;
-  static constexpr int kPrefillBytes = kMfma ? PrefillSmem<(D <= 128 ? D : 128)>::kBytes : 0;
+  static constexpr int kPrefillBytes =
+      kMfma ? PrefillSmem<(D <= 128 ? D : 128)>::kBytes : (kMfma16 ? Prefill16Smem<D, DV>::kBytes : 0);
   static constexpr int kBytes = kDecodeBytes > kPrefillBytes ? kDecodeBytes : kPrefillBytes;
 };
 
@@ -74,6 +78,8 @@ void mixed_kernel(KernelArgs a) {
   if (it.kind == kPrefill) {
     if constexpr (MixedShape<T, D, DV, G>::kMfma)
       prefill_item<T, D, G>(a, it, smem);
+    else if constexpr (MixedShape<T, D, DV, G>::kMfma16)
+      prefill16_item<T, D, DV, G>(a, it, smem);
     else
       prefill_item_by_queries<T, D, DV, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it,
                                                                                   reinterpret_cast<float*>(smem));

@@ -47,6 +47,14 @@ def test_d192_dv128_decode_parity(i, split_tokens):
     dict(dtype="bf16", hq=32, hkv=8, page_size=16, q_counts=(40, 1, 9), max_len=400),
     dict(dtype="f16", hq=16, hkv=16, page_size=64, q_counts=(1, 70), max_len=500, window=33),
     dict(dtype="f32", hq=8, hkv=2, page_size=16, q_counts=(12, 1), max_len=200, causal=False),
+    # 16-bit tiles on MFMA: MHA (G = 1) chunks over several 256-row tiles, G = 16, G = 8 with a
+    # window, page size 1, non-causal, history 0
+    dict(dtype="bf16", hq=16, hkv=16, page_size=16, q_counts=(600,), max_len=1000),
+    dict(dtype="bf16", hq=16, hkv=1, page_size=64, q_counts=(65, 2), max_len=700),
+    dict(dtype="f16", hq=64, hkv=8, page_size=16, q_counts=(100, 3), max_len=900, window=129),
+    dict(dtype="bf16", hq=32, hkv=8, page_size=1, q_counts=(70,), max_len=200),
+    dict(dtype="bf16", hq=8, hkv=2, page_size=32, q_counts=(150, 5), max_len=700, causal=False),
+    dict(dtype="f16", hq=32, hkv=8, page_size=16, q_counts=(200,), histories=[0]),
 ])
 def test_d192_dv128_prefill_and_mixed_parity(case):
     b = random_batch(6100, d=192, dv=128, **case)
@@ -78,6 +86,23 @@ def test_d192_dv128_long_rows_split_to_the_limit():
                      histories=[20000, 40000])
     run = _parity(b, max_splits=64)
     assert run.info["split_rows"] > 0
+
+
+def test_d192_dv128_prefill_window_one_bitwise():
+    """MFMA prefill tiles with a one-key window return each query's own V row."""
+    b = random_batch(6500, dtype="bf16", hq=32, hkv=8, d=192, dv=128, page_size=16, q_counts=(150, 1, 40),
+                     max_len=600, window=1)
+    run = GqaRun(b)
+    run()
+    out, _ = run.result()
+    v = to_f64(run.v)
+    G = b.hq // b.hkv
+    for s in range(b.num_seqs):
+        for i in range(int(b.cu_q[s]), int(b.cu_q[s + 1])):
+            p = int(b.q_pos[i])
+            row = v[b.block_table[s, p // b.page_size], p % b.page_size]
+            for h in range(b.hq):
+                assert np.array_equal(out[i, h], row[h // G]), (i, h)
 
 
 def test_head_size_pairs_without_kernels_are_refused():
