@@ -60,8 +60,9 @@ void decode_kernel(KernelArgs a) {
 template <typename T, int D, int DV, int G>
 struct MixedShape {
   static constexpr bool kMfma = sizeof(T) == 2 && D == DV && (D == 64 || D == 128) && G <= kPrefillRows;
-  // K and V rows of different widths: the 16x16x32 MFMA tile
-  static constexpr bool kMfma16 = sizeof(T) == 2 && D != DV && D % 64 == 0 && DV % 64 == 0 && G <= kPrefillRows;
+  // K and V rows of different widths, and D = Dv = 256: the 16x16x32 MFMA tile
+  static constexpr bool kMfma16 =
+      sizeof(T) == 2 && !kMfma && D % 64 == 0 && DV % 64 == 0 && (D != DV || D == 256) && G <= kPrefillRows;
   static constexpr int kDecodeBytes = kPrefillWaves * G * (DV + 3) * 4;
   static constexpr int kPrefillBytes =
       kMfma ? PrefillSmem<(D <= 128 ? D : 128)>::kBytes : (kMfma16 ? Prefill16Smem<D, DV>::kBytes : 0);

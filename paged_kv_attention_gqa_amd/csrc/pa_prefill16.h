@@ -1,5 +1,6 @@
-// Chunked-prefill body on 16x16x32 MFMA for K and V rows of different widths
-// (D = 192, Dv = 128 in bf16 / f16): the rows and keys of a prefill tile as in
+// Chunked-prefill body on 16x16x32 MFMA for head sizes the prefill_item tile
+// does not take (D = 192 with Dv = 128, and D = Dv = 256, in bf16 / f16): the
+// rows and keys of a prefill tile as in
 // prefill_item (up to 256 query rows -- 256 / G consecutive queries of one
 // sequence times the G heads of one KV head -- against the keys the plan
 // assigns to the tile), computed with the operand scheme of the backward's
@@ -21,7 +22,9 @@
 //                                      columns by transposed LDS reads in
 //                                      that order)
 // O's accumulator holds rows 4 g + e in lane (dim, g): its per-row rescale
-// and normalisation take the row's value from lane 4 g + e.
+// and normalisation take the row's value from lane 4 g + e.  Value rows wider
+// than 128 run in passes of 128 output dims over the whole key range (the
+// scores are recomputed per pass), so that the output sums fit the registers.
 #pragma once
 
 #include "pa_decode.h"
@@ -43,20 +46,23 @@ __device__ __forceinline__ int tile16_off(int row, int piece) {
 
 template <int D, int DV>
 struct Prefill16Smem {
+  static constexpr int kPasses = DV > 128 ? DV / 128 : 1;
+  static constexpr int kPassDims = DV / kPasses;  // output dims per pass
   static constexpr int kK = kPrefill16Keys * D * 2;
-  static constexpr int kV = kPrefill16Keys * DV * 2;
+  static constexpr int kV = kPrefill16Keys * kPassDims * 2;
   static constexpr int kBytes = kK + kV;
 };
 
 template <typename T, int D, int DV, int G>
 __device__ __forceinline__ void prefill16_item(const KernelArgs& a, const WorkItem& it, char* smem) {
   constexpr int NT = kPrefill16Keys;
-  constexpr int KS = D / 32, VB = DV / 16;      // k-steps of S^T; 16-dim blocks of O
-  constexpr int PK = D / 8, PV = DV / 8;        // 16-byte pieces per K / V row
+  constexpr int PASSES = Prefill16Smem<D, DV>::kPasses, DVP = Prefill16Smem<D, DV>::kPassDims;
+  constexpr int KS = D / 32, VB = DVP / 16;     // k-steps of S^T; 16-dim blocks of O per pass
+  constexpr int PK = D / 8, PV = DVP / 8;       // 16-byte pieces per K / V tile row
   constexpr int CHUNKS = NT * (PK + PV);        // 16-byte pieces per tile
   constexpr int THREADS = kPrefillWaves * kWave;
   constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
-  static_assert(D % 32 == 0 && DV % 16 == 0 && PK % 8 == 0 && PV % 8 == 0, "unsupported head sizes");
+  static_assert(D % 32 == 0 && DVP * PASSES == DV && PK % 8 == 0 && PV % 8 == 0, "unsupported head sizes");
   static_assert(kPrefillWaves * 32 == kPrefillRows, "eight waves of 32 rows");
   char* ks = smem;
   char* vs = smem + Prefill16Smem<D, DV>::kK;
@@ -77,8 +83,6 @@ __device__ __forceinline__ void prefill16_item(const KernelArgs& a, const WorkIt
   frag_t qb[2][KS];
   int pos[2];
   bool row_ok[2];
-  float m[2], l[2];
-  floatx4_t o[2][VB];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int rho = wave * 32 + blk * 16 + n;
@@ -89,6 +93,14 @@ __device__ __forceinline__ void prefill16_item(const KernelArgs& a, const WorkIt
     for (int k = 0; k < KS; ++k)
       qb[blk][k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + 32 * k + 8 * g4);
     pos[blk] = a.q_pos[it.q_begin + rg / G];
+  }
+
+  for (int pass = 0; pass < PASSES; ++pass) {
+  const int vd0 = pass * DVP;  // first output dim of this pass
+  float m[2], l[2];
+  floatx4_t o[2][VB];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
     m[blk] = -INFINITY;
     l[blk] = 0.f;
 #pragma unroll
@@ -108,7 +120,7 @@ __device__ __forceinline__ void prefill16_item(const KernelArgs& a, const WorkIt
         const int t = min(t0 + key, te - 1);
         const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
         const uint16_t* src = is_k ? reinterpret_cast<const uint16_t*>(a.k) + slot * krow + (uint64_t)kvh * D
-                                   : reinterpret_cast<const uint16_t*>(a.v) + slot * vrow + (uint64_t)kvh * DV;
+                                   : reinterpret_cast<const uint16_t*>(a.v) + slot * vrow + (uint64_t)kvh * DV + vd0;
         pre[j] = *reinterpret_cast<const u32x4_t*>(src + piece * 8);
       }
     }
@@ -120,7 +132,7 @@ __device__ __forceinline__ void prefill16_item(const KernelArgs& a, const WorkIt
       if (c < CHUNKS) {
         const bool is_k = c < NT * PK;
         const int cc = is_k ? c : c - NT * PK;
-        char* dst = is_k ? ks + tile16_off<D>(cc / PK, cc % PK) : vs + tile16_off<DV>(cc / PV, cc % PV);
+        char* dst = is_k ? ks + tile16_off<D>(cc / PK, cc % PK) : vs + tile16_off<DVP>(cc / PV, cc % PV);
         *reinterpret_cast<u32x4_t*>(dst) = pre[j];
       }
     }
@@ -133,7 +145,7 @@ __device__ __forceinline__ void prefill16_item(const KernelArgs& a, const WorkIt
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key = 4 * g4 + (n >> 2) + 16 * h, dim = 16 * b + 4 * (n & 3);
-      troff[b][h] = (uint32_t)(tile16_off<DV>(key, dim >> 3) + (dim & 7) * 2);
+      troff[b][h] = (uint32_t)(tile16_off<DVP>(key, dim >> 3) + (dim & 7) * 2);
     }
 
   const int t_first = tb & ~(NT - 1);
@@ -213,7 +225,7 @@ __device__ __forceinline__ void prefill16_item(const KernelArgs& a, const WorkIt
   for (int blk = 0; blk < 2; ++blk) {
     const float lt = pair32_sum(pair16_sum(l[blk]));
     const int rho_n = wave * 32 + blk * 16 + n;
-    if (a.lse && g4 == 0 && rho_n < nrows) {
+    if (a.lse && pass == 0 && g4 == 0 && rho_n < nrows) {
       const uint64_t row = (uint64_t)(it.q_begin + rho_n / G) * a.hq + (uint64_t)kvh * G + rho_n % G;
       a.lse[row] = m[blk] * a.scale + logf(lt);
     }
@@ -225,8 +237,9 @@ __device__ __forceinline__ void prefill16_item(const KernelArgs& a, const WorkIt
       if (rho >= nrows) continue;
       const uint64_t row = (uint64_t)(it.q_begin + rho / G) * a.hq + (uint64_t)kvh * G + rho % G;
 #pragma unroll
-      for (int b = 0; b < VB; ++b) store_out<T>(a.out, row * DV + 16 * b + n, o[blk][b][e] * ie);
+      for (int b = 0; b < VB; ++b) store_out<T>(a.out, row * DV + vd0 + 16 * b + n, o[blk][b][e] * ie);
     }
+  }
   }
 }
 
