@@ -14,8 +14,8 @@
 // Four launches: zero the K/V gradient pools, D per row, dQ (one workgroup
 // per (query, KV head), keys strided over lanes as in the decode body), and
 // dK/dV (one workgroup per 128-key block and KV head, looping over the
-// sequence's query rows: on 16-bit MFMA for bf16 / f16 with D = Dv in {64,
-// 128}, else on the vector units).  Each pool row has a single writer, so the result
+// sequence's query rows): on 16-bit MFMA for bf16 / f16, on the vector units
+// for f32.  Each pool row has a single writer, so the result
 // does not depend on scheduling (ruDNN's ordered, atomic-free variant).
 #include <algorithm>
 
@@ -269,15 +269,44 @@ __global__ __launch_bounds__(kBwdKvWaves* kWave) void bwd_dkv_kernel(BwdArgs b, 
 //                                      transposed LDS reads in that order)
 constexpr int kBwdMfmaWaves = 8;
 constexpr int kBwdRowTile = 32;
-template <typename T, int D>
+
+// Tile layout of the backward's LDS tiles: rows of WIDTH elements in 16-byte
+// pieces, stored at piece ^ (three low row bits), which stays inside the row
+// for any multiple of 8 pieces (D = 192 has 24).
+template <int WIDTH>
+__device__ __forceinline__ int bwd_off(int row, int piece) {
+  return row * (WIDTH * 2) + ((piece ^ (((row & 3) << 1) | ((row >> 2) & 1))) << 4);
+}
+
+// Eight 16-bit elements of column dims 16 blk + (lane % 16) from the rows
+// 4 g + 0..3 and 16 + 4 g + 0..3 of a tile (g = lane / 16): two transposed
+// reads, the order in which the 16x16 accumulators hold their rows.
+template <int WIDTH>
+__device__ __forceinline__ uint32_t bwd_troff(int blk, int h, int n, int g4) {
+  const int row = 4 * g4 + (n >> 2) + 16 * h, dim = 16 * blk + 4 * (n & 3);
+  return (uint32_t)(bwd_off<WIDTH>(row, dim >> 3) + (dim & 7) * 2);
+}
+__device__ __forceinline__ frag_t bwd_tfrag(const char* t, uint32_t off0, uint32_t off1) {
+  const short4_t v0 = lds_read_tr16(t + off0);
+  const short4_t v1 = lds_read_tr16(t + off1);
+  return __builtin_bit_cast(frag_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
+                                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
+                                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
+                                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
+}
+
+template <typename T, int D, int DV>
 __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdArgs b, int first_item, int G) {
-  constexpr int KS = D / 32;        // 16x16x32 k-steps over the head dims
-  constexpr int DB = D / 16;        // 16-dim blocks of dK / dV
-  constexpr int PIECES = D / 8;     // 16-byte pieces per row
-  constexpr int TILE = kBwdRowTile * D * 2;
+  constexpr int KSK = D / 32, KSV = DV / 32;  // 16x16x32 k-steps over the K / V dims
+  constexpr int DBK = D / 16, DBV = DV / 16;  // 16-dim blocks of dK / dV
+  constexpr int PK = D / 8, PV = DV / 8;      // 16-byte pieces per Q / dO row
+  constexpr int CHUNKS = kBwdRowTile * (PK + PV);
+  constexpr int THREADS = kBwdMfmaWaves * kWave;
+  constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
   static_assert(kBwdMfmaWaves * 16 == kBwdBlockKeys, "eight waves of 16 keys");
-  __shared__ __attribute__((aligned(16))) char qs[TILE];
-  __shared__ __attribute__((aligned(16))) char gs[TILE];
+  static_assert(D % 64 == 0 && DV % 64 == 0, "rows of whole 8-piece groups");
+  __shared__ __attribute__((aligned(16))) char qs[kBwdRowTile * D * 2];
+  __shared__ __attribute__((aligned(16))) char gs[kBwdRowTile * DV * 2];
   __shared__ float lse2s[kBwdRowTile], dls[kBwdRowTile];
   __shared__ int poss[kBwdRowTile];
   const KernelArgs& a = b.a;
@@ -289,51 +318,55 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
   const int kvh = it.kvh;
   const int ps = 1 << a.page_shift;
   const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
-  const uint64_t row_stride = (uint64_t)a.hkv * D;
+  const uint64_t krow = (uint64_t)a.hkv * D, vrow = (uint64_t)a.hkv * DV;
   const int nrows = (it.q_end - it.q_begin) * G;
   const float c2 = a.scale_log2;
 
   // K^T and V^T operands of this wave's 16 keys (key column n, dims 32 k + 8 g4 ..)
   const int my_key = it.tok_begin + wave * 16 + n;
   const bool key_ok = my_key < it.tok_end;
-  frag_t kb[KS], vb[KS];
+  frag_t kb[KSK], vb[KSV];
   {
     const int tc = key_ok ? my_key : it.tok_end - 1;
     const uint64_t slot = (uint64_t)bt[tc >> a.page_shift] * ps + (tc & (ps - 1));
-    const uint16_t* kr = reinterpret_cast<const uint16_t*>(a.k) + slot * row_stride + (uint64_t)kvh * D;
-    const uint16_t* vr = reinterpret_cast<const uint16_t*>(a.v) + slot * row_stride + (uint64_t)kvh * D;
+    const uint16_t* kr = reinterpret_cast<const uint16_t*>(a.k) + slot * krow + (uint64_t)kvh * D;
+    const uint16_t* vr = reinterpret_cast<const uint16_t*>(a.v) + slot * vrow + (uint64_t)kvh * DV;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      kb[k] = *reinterpret_cast<const frag_t*>(kr + 32 * k + 8 * g4);
-      vb[k] = *reinterpret_cast<const frag_t*>(vr + 32 * k + 8 * g4);
-    }
-  }
-  floatx4_t dk[DB], dv[DB];
+    for (int k = 0; k < KSK; ++k) kb[k] = *reinterpret_cast<const frag_t*>(kr + 32 * k + 8 * g4);
 #pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    dk[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    dv[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < KSV; ++k) vb[k] = *reinterpret_cast<const frag_t*>(vr + 32 * k + 8 * g4);
   }
+  floatx4_t dk[DBK], dv[DBV];
+#pragma unroll
+  for (int i = 0; i < DBK; ++i) dk[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < DBV; ++i) dv[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   // keys of this lane's dK / dV accumulator rows: 4 g4 + e, e < 4
   const int key_lo = it.tok_begin + wave * 16;
 
-  // Tile loads: thread t moves 16-byte piece t % PIECES of tile row
-  // t / PIECES of Q and dO (rows past the item's last are row 0 again,
-  // masked through lse2 = +inf); threads below 32 the row statistics.
-  const int lrow = tid / PIECES, lpiece = tid % PIECES;
-  const bool loader = tid < kBwdRowTile * PIECES;
-  auto row_addr = [&](int rho) -> uint64_t {  // element offset of tile row rho's query row
+  // Tile loads: piece c < 32 PK of Q (row c / PK), then of dO (rows past the
+  // item's last are row 0 again, masked through lse2 = +inf); threads below
+  // 32 the row statistics.
+  auto row_addr = [&](int rho) -> uint64_t {  // (query, head) row of tile row rho
     const int rg = rho < nrows ? rho : 0;
     return ((uint64_t)(it.q_begin + rg / G) * a.hq + (uint64_t)kvh * G + rg % G);
   };
-  u32x4_t pq = {0u, 0u, 0u, 0u}, pg = {0u, 0u, 0u, 0u};
+  u32x4_t pre[PER_THREAD];
   float pl = 0.f, pd = 0.f;
   int pp = 0;
   auto fetch = [&](int r0) {
-    if (loader) {
-      const uint64_t row = row_addr(r0 + lrow);
-      pq = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + lpiece * 8);
-      pg = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * D + lpiece * 8);
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int c = tid + j * THREADS;
+      if (c < CHUNKS) {
+        const bool is_q = c < kBwdRowTile * PK;
+        const int cc = is_q ? c : c - kBwdRowTile * PK;
+        const int r = is_q ? cc / PK : cc / PV, piece = is_q ? cc % PK : cc % PV;
+        const uint64_t row = row_addr(r0 + r);
+        pre[j] = is_q ? *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + piece * 8)
+                      : *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * DV +
+                                                          piece * 8);
+      }
     }
     if (tid < kBwdRowTile) {
       const int rho = r0 + tid;
@@ -344,37 +377,28 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
       pp = a.q_pos[it.q_begin + (ok ? rho : 0) / G];
     }
   };
-  // transposed-read offsets: 16-lane group g4, lane 4 r + j -> tile row
-  // 4 g4 + r (+16 for the second read), dims 16 blk + 4 j
-  uint32_t troff[DB][2];
+  auto store = [&]() {
 #pragma unroll
-  for (int blk = 0; blk < DB; ++blk)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 4 * g4 + (n >> 2) + 16 * h, dim = 16 * blk + 4 * (n & 3);
-      troff[blk][h] = (uint32_t)(tile_off<D>(row, dim >> 3) + (dim & 7) * 2);
-    }
-  auto tfrag = [&](const char* t, int blk) {
-    const short4_t v0 = lds_read_tr16(t + troff[blk][0]);
-    const short4_t v1 = lds_read_tr16(t + troff[blk][1]);
-    return __builtin_bit_cast(frag_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
-                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
-                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
-                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
-  };
-
-  if (nrows > 0) fetch(0);
-  for (int r0 = 0; r0 < nrows; r0 += kBwdRowTile) {
-    __syncthreads();  // every wave is done with the previous tile
-    if (loader) {
-      *reinterpret_cast<u32x4_t*>(qs + tile_off<D>(lrow, lpiece)) = pq;
-      *reinterpret_cast<u32x4_t*>(gs + tile_off<D>(lrow, lpiece)) = pg;
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int c = tid + j * THREADS;
+      if (c < CHUNKS) {
+        const bool is_q = c < kBwdRowTile * PK;
+        const int cc = is_q ? c : c - kBwdRowTile * PK;
+        char* dst = is_q ? qs + bwd_off<D>(cc / PK, cc % PK) : gs + bwd_off<DV>(cc / PV, cc % PV);
+        *reinterpret_cast<u32x4_t*>(dst) = pre[j];
+      }
     }
     if (tid < kBwdRowTile) {
       lse2s[tid] = pl;
       dls[tid] = pd;
       poss[tid] = pp;
     }
+  };
+
+  if (nrows > 0) fetch(0);
+  for (int r0 = 0; r0 < nrows; r0 += kBwdRowTile) {
+    __syncthreads();  // every wave is done with the previous tile
+    store();
     __syncthreads();
     if (r0 + kBwdRowTile < nrows) fetch(r0 + kBwdRowTile);
 
@@ -385,12 +409,12 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
       s[h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
       dp[h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const frag_t qa = *reinterpret_cast<const frag_t*>(qs + tile_off<D>(16 * h + n, 4 * k + g4));
-        const frag_t ga = *reinterpret_cast<const frag_t*>(gs + tile_off<D>(16 * h + n, 4 * k + g4));
-        s[h] = mfma_16x16x32<T>(qa, kb[k], s[h]);
-        dp[h] = mfma_16x16x32<T>(ga, vb[k], dp[h]);
-      }
+      for (int k = 0; k < KSK; ++k)
+        s[h] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(qs + bwd_off<D>(16 * h + n, 4 * k + g4)), kb[k], s[h]);
+#pragma unroll
+      for (int k = 0; k < KSV; ++k)
+        dp[h] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(gs + bwd_off<DV>(16 * h + n, 4 * k + g4)), vb[k],
+                                 dp[h]);
     }
     // P and dS; lane (n, g4) element e of half h is row 16 h + 4 g4 + e, key n
     uint32_t pw[4], dw[4];
@@ -415,10 +439,13 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
     const frag_t df = __builtin_bit_cast(frag_t, make_uint4(dw[0], dw[1], dw[2], dw[3]));
     // dV += P^T dO, dK += dS^T Q over the tile's 32 rows
 #pragma unroll
-    for (int blk = 0; blk < DB; ++blk) {
-      dv[blk] = mfma_16x16x32<T>(pf, tfrag(gs, blk), dv[blk]);
-      dk[blk] = mfma_16x16x32<T>(df, tfrag(qs, blk), dk[blk]);
-    }
+    for (int blk = 0; blk < DBV; ++blk)
+      dv[blk] = mfma_16x16x32<T>(pf, bwd_tfrag(gs, bwd_troff<DV>(blk, 0, n, g4), bwd_troff<DV>(blk, 1, n, g4)),
+                                 dv[blk]);
+#pragma unroll
+    for (int blk = 0; blk < DBK; ++blk)
+      dk[blk] = mfma_16x16x32<T>(df, bwd_tfrag(qs, bwd_troff<D>(blk, 0, n, g4), bwd_troff<D>(blk, 1, n, g4)),
+                                 dk[blk]);
   }
 
   // lane (n, g4) of block blk holds dims 16 blk + n of keys key_lo + 4 g4 + e
@@ -427,12 +454,10 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
     const int t = key_lo + 4 * g4 + e;
     if (t >= it.tok_end) continue;
     const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
-    const uint64_t base = slot * row_stride + (uint64_t)kvh * D + n;
 #pragma unroll
-    for (int blk = 0; blk < DB; ++blk) {
-      store_out<T>(b.dk, base + 16 * blk, dk[blk][e]);
-      store_out<T>(b.dv, base + 16 * blk, dv[blk][e]);
-    }
+    for (int blk = 0; blk < DBK; ++blk) store_out<T>(b.dk, slot * krow + (uint64_t)kvh * D + 16 * blk + n, dk[blk][e]);
+#pragma unroll
+    for (int blk = 0; blk < DBV; ++blk) store_out<T>(b.dv, slot * vrow + (uint64_t)kvh * DV + 16 * blk + n, dv[blk][e]);
   }
 }
 
@@ -447,13 +472,17 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
 //                                        dS^T accumulators, K columns by
 //                                        transposed LDS reads)
 constexpr int kBwdKeyTile = 32;
-template <typename T, int D>
+template <typename T, int D, int DV>
 __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdArgs b, int first_item, int G) {
-  constexpr int KS = D / 32, DB = D / 16, PIECES = D / 8;
-  constexpr int TILE = kBwdKeyTile * D * 2;
+  constexpr int KSK = D / 32, KSV = DV / 32, DBK = D / 16;
+  constexpr int PK = D / 8, PV = DV / 8;
+  constexpr int CHUNKS = kBwdKeyTile * (PK + PV);
+  constexpr int THREADS = kBwdMfmaWaves * kWave;
+  constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
   static_assert(kBwdMfmaWaves * 16 == kBwdQRows, "eight waves of 16 rows");
-  __shared__ __attribute__((aligned(16))) char ks[TILE];
-  __shared__ __attribute__((aligned(16))) char vs[TILE];
+  static_assert(D % 64 == 0 && DV % 64 == 0, "rows of whole 8-piece groups");
+  __shared__ __attribute__((aligned(16))) char ks[kBwdKeyTile * D * 2];
+  __shared__ __attribute__((aligned(16))) char vs[kBwdKeyTile * DV * 2];
   const KernelArgs& a = b.a;
   const BwdItem it = b.items[first_item + blockIdx.x];
   const int tid = threadIdx.x;
@@ -463,7 +492,7 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdAr
   const int kvh = it.kvh;
   const int ps = 1 << a.page_shift;
   const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
-  const uint64_t row_stride = (uint64_t)a.hkv * D;
+  const uint64_t krow = (uint64_t)a.hkv * D, vrow = (uint64_t)a.hkv * DV;
   const int nrows = (it.q_end - it.q_begin) * G;
   const float c2 = a.scale_log2;
 
@@ -472,56 +501,56 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdAr
   const bool row_ok = my_row < nrows;
   const int rg = row_ok ? my_row : 0;
   const uint64_t row = (uint64_t)(it.q_begin + rg / G) * a.hq + (uint64_t)kvh * G + rg % G;
-  frag_t qb[KS], gb[KS];
+  frag_t qb[KSK], gb[KSV];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) {
+  for (int k = 0; k < KSK; ++k)
     qb[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + 32 * k + 8 * g4);
-    gb[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * D + 32 * k + 8 * g4);
-  }
+#pragma unroll
+  for (int k = 0; k < KSV; ++k)
+    gb[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * DV + 32 * k + 8 * g4);
   const float l2 = row_ok ? a.lse[row] * kLog2e : INFINITY;
   const float dl = row_ok ? b.delta[row] : 0.f;
   const int pos = a.q_pos[it.q_begin + rg / G];
-  floatx4_t dq[DB];
+  floatx4_t dq[DBK];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) dq[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < DBK; ++i) dq[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // tile loads: thread t moves piece t % PIECES of key t / PIECES of K and V
-  const int lkey = tid / PIECES, lpiece = tid % PIECES;
-  const bool loader = tid < kBwdKeyTile * PIECES;
-  u32x4_t pk = {0u, 0u, 0u, 0u}, pv = {0u, 0u, 0u, 0u};
+  // tile loads: piece c < 32 PK of K (key c / PK), then of V
+  u32x4_t pre[PER_THREAD];
   auto fetch = [&](int t0) {
-    if (loader) {
-      const int t = min(t0 + lkey, it.tok_end - 1);
-      const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
-      const uint64_t off = slot * row_stride + (uint64_t)kvh * D + lpiece * 8;
-      pk = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.k) + off);
-      pv = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.v) + off);
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int c = tid + j * THREADS;
+      if (c < CHUNKS) {
+        const bool is_k = c < kBwdKeyTile * PK;
+        const int cc = is_k ? c : c - kBwdKeyTile * PK;
+        const int key = is_k ? cc / PK : cc / PV, piece = is_k ? cc % PK : cc % PV;
+        const int t = min(t0 + key, it.tok_end - 1);
+        const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+        pre[j] = is_k ? *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.k) + slot * krow +
+                                                          (uint64_t)kvh * D + piece * 8)
+                      : *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.v) + slot * vrow +
+                                                          (uint64_t)kvh * DV + piece * 8);
+      }
     }
   };
-  uint32_t troff[DB][2];
+  auto store = [&]() {
 #pragma unroll
-  for (int blk = 0; blk < DB; ++blk)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = 4 * g4 + (n >> 2) + 16 * h, dim = 16 * blk + 4 * (n & 3);
-      troff[blk][h] = (uint32_t)(tile_off<D>(key, dim >> 3) + (dim & 7) * 2);
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int c = tid + j * THREADS;
+      if (c < CHUNKS) {
+        const bool is_k = c < kBwdKeyTile * PK;
+        const int cc = is_k ? c : c - kBwdKeyTile * PK;
+        char* dst = is_k ? ks + bwd_off<D>(cc / PK, cc % PK) : vs + bwd_off<DV>(cc / PV, cc % PV);
+        *reinterpret_cast<u32x4_t*>(dst) = pre[j];
+      }
     }
-  auto tfrag = [&](const char* t, int blk) {
-    const short4_t v0 = lds_read_tr16(t + troff[blk][0]);
-    const short4_t v1 = lds_read_tr16(t + troff[blk][1]);
-    return __builtin_bit_cast(frag_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
-                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
-                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
-                                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
   };
 
   fetch(it.tok_begin);
   for (int t0 = it.tok_begin; t0 < it.tok_end; t0 += kBwdKeyTile) {
     __syncthreads();  // every wave is done with the previous tile
-    if (loader) {
-      *reinterpret_cast<u32x4_t*>(ks + tile_off<D>(lkey, lpiece)) = pk;
-      *reinterpret_cast<u32x4_t*>(vs + tile_off<D>(lkey, lpiece)) = pv;
-    }
+    store();
     __syncthreads();
     if (t0 + kBwdKeyTile < it.tok_end) fetch(t0 + kBwdKeyTile);
 
@@ -530,12 +559,11 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdAr
     for (int h = 0; h < 2; ++h) {
       floatx4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const frag_t ka = *reinterpret_cast<const frag_t*>(ks + tile_off<D>(16 * h + n, 4 * k + g4));
-        const frag_t va = *reinterpret_cast<const frag_t*>(vs + tile_off<D>(16 * h + n, 4 * k + g4));
-        s = mfma_16x16x32<T>(ka, qb[k], s);
-        dp = mfma_16x16x32<T>(va, gb[k], dp);
-      }
+      for (int k = 0; k < KSK; ++k)
+        s = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(ks + bwd_off<D>(16 * h + n, 4 * k + g4)), qb[k], s);
+#pragma unroll
+      for (int k = 0; k < KSV; ++k)
+        dp = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(vs + bwd_off<DV>(16 * h + n, 4 * k + g4)), gb[k], dp);
       // lane (n, g4) element e: key t0 + 16 h + 4 g4 + e, row my_row
       float ds[4];
 #pragma unroll
@@ -550,7 +578,8 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdAr
     }
     const frag_t df = __builtin_bit_cast(frag_t, make_uint4(dw[0], dw[1], dw[2], dw[3]));
 #pragma unroll
-    for (int blk = 0; blk < DB; ++blk) dq[blk] = mfma_16x16x32<T>(df, tfrag(ks, blk), dq[blk]);
+    for (int blk = 0; blk < DBK; ++blk)
+      dq[blk] = mfma_16x16x32<T>(df, bwd_tfrag(ks, bwd_troff<D>(blk, 0, n, g4), bwd_troff<D>(blk, 1, n, g4)), dq[blk]);
   }
 
   // lane (n, g4) of block blk holds dims 16 blk + n of rows wave 16 + 4 g4 + e
@@ -560,7 +589,7 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdAr
     if (r >= nrows) continue;
     const uint64_t orow = (uint64_t)(it.q_begin + r / G) * a.hq + (uint64_t)kvh * G + r % G;
 #pragma unroll
-    for (int blk = 0; blk < DB; ++blk) store_out<T>(b.dq, orow * D + 16 * blk + n, dq[blk][e]);
+    for (int blk = 0; blk < DBK; ++blk) store_out<T>(b.dq, orow * D + 16 * blk + n, dq[blk][e]);
   }
 }
 
@@ -572,10 +601,10 @@ using BwdFn = hipError_t (*)(const BwdArgs&, int, int, int, hipStream_t);
 // key block, then n_dqt dQ row tiles
 template <typename T, int D, int DV, int G>
 hipError_t launch_bwd_t(const BwdArgs& b, int n_dq, int n_kv, int n_dqt, hipStream_t stream) {
-  constexpr bool kMfma = sizeof(T) == 2 && D == DV && (D == 64 || D == 128);
+  constexpr bool kMfma = sizeof(T) == 2 && D % 64 == 0 && DV % 64 == 0;
   if (kMfma && n_dqt > 0) {
     if constexpr (kMfma)
-      hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D>), dim3(n_dqt), dim3(kBwdMfmaWaves * kWave), 0, stream, b,
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, DV>), dim3(n_dqt), dim3(kBwdMfmaWaves * kWave), 0, stream, b,
                          n_dq + n_kv, G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -586,7 +615,8 @@ hipError_t launch_bwd_t(const BwdArgs& b, int n_dq, int n_kv, int n_dqt, hipStre
   }
   if (n_kv > 0) {
     if constexpr (kMfma)
-      hipLaunchKernelGGL((bwd_dkv_mfma_kernel<T, D>), dim3(n_kv), dim3(kBwdMfmaWaves * kWave), 0, stream, b, n_dq, G);
+      hipLaunchKernelGGL((bwd_dkv_mfma_kernel<T, D, DV>), dim3(n_kv), dim3(kBwdMfmaWaves * kWave), 0, stream, b, n_dq,
+                         G);
     else
       hipLaunchKernelGGL((bwd_dkv_kernel<T, D, DV, G>), dim3(n_kv), dim3(kBwdKvWaves * kWave), 0, stream, b, n_dq);
     return hipGetLastError();

@@ -86,6 +86,10 @@ CASES = [
     dict(dtype="f32", hq=8, hkv=2, d=64, page_size=16, q_counts=(20, 1, 3), max_len=300),
     dict(dtype="f32", hq=16, hkv=4, d=128, page_size=64, q_counts=(9,), max_len=700, causal=False, window=100),
     dict(dtype="bf16", hq=8, hkv=2, d=128, page_size=16, q_counts=(0, 33, 0, 1), histories=[40, 100, 0, 5]),
+    # 16-bit MFMA backward for the other head sizes
+    dict(dtype="bf16", hq=16, hkv=16, d=192, dv=128, page_size=16, q_counts=(70, 1), max_len=400),
+    dict(dtype="bf16", hq=8, hkv=2, d=256, page_size=32, q_counts=(40, 3), max_len=300, window=50),
+    dict(dtype="f16", hq=16, hkv=2, d=64, page_size=1, q_counts=(33,), max_len=100, causal=False),
 ]
 
 
