@@ -335,7 +335,8 @@ def measure_backward(name, steps, warmup):
 
 
 PRIMARY = "bf16_decode_batch"
-SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode", "bf16_mla_chunked_prefill")
+SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode", "bf16_mla_chunked_prefill",
+             "bf16_chunked_prefill_d192")
 APPEND = ("bf16_decode_batch", "bf16_chunked_prefill")  # cache writes of one decode step and of one chunk
 BACKWARD = ("bf16_chunked_prefill",)  # gradients of one chunk step
 

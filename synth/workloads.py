@@ -332,6 +332,23 @@ def config_bf16_mla_decode(seed: int = 5) -> MlaBatch:
                     H, R, P, 1.0 / math.sqrt(576.0), True, 0, q_abs, q_rope, latent, kpos, seed, 16)
 
 
+def config_bf16_chunked_prefill_d192(seed: int = 7) -> PagedBatch:
+    """The chunked-prefill shape with K rows of 192 and V rows of 128 (a
+    workload of this library): 8 sequences, history uniform in [0, 4096] plus a
+    512-query chunk, causal, Hq=32, Hkv=8, page 16, scale 1/sqrt(192)."""
+    rng = np.random.default_rng(seed)
+    S, C, ps, hq, hkv, d, dv = 8, 512, 16, 32, 8, 192, 128
+    hist = rng.integers(0, 4096 + 1, size=S).astype(np.int32)
+    seq_lens = (hist + C).astype(np.int32)
+    bt, pool, _ = _tables(rng, seq_lens, ps)
+    q_pos = np.concatenate([np.arange(h, h + C, dtype=np.int32) for h in hist])
+    q = _normal(rng, (S * C, hq, d), "bf16")
+    k = _normal(rng, (pool, ps, hkv, d), "bf16")
+    v = _normal(rng, (pool, ps, hkv, dv), "bf16")
+    return PagedBatch("bf16_chunked_prefill_d192", "bf16", seq_lens, _packed([C] * S), q_pos, bt, ps, pool,
+                      hq, hkv, d, dv, 1.0 / math.sqrt(192.0), True, 0, q, k, v, seed, 16)
+
+
 def config_bf16_mla_chunked_prefill(seed: int = 6) -> MlaBatch:
     """bf16 absorbed-MLA chunked prefill (a workload of this library, beside
     the MLA decode one): 8 sequences, each a 256-query chunk after a history
@@ -358,6 +375,7 @@ CONFIGS: Dict[str, Callable] = {
     "bf16_mixed_batch": config_bf16_mixed_batch,
     "bf16_mla_decode": config_bf16_mla_decode,
     "bf16_mla_chunked_prefill": config_bf16_mla_chunked_prefill,
+    "bf16_chunked_prefill_d192": config_bf16_chunked_prefill_d192,
 }
 
 
