@@ -310,7 +310,7 @@ def measure_backward(name, steps, warmup):
         "cuda", dtype=torch.bfloat16)
     dq = torch.empty_like(f.q)
     dk, dv = torch.empty_like(f.k), torch.empty_like(f.v)
-    n = pa.pa_plan_bwd_workspace_bytes(f.plan)
+    n = pa.pa_plan_bwd_workspace_bytes(f.plan, b.dtype, b.d, b.dv)
     ws = torch.empty(n // 4 + 64, dtype=torch.float32, device="cuda")
 
     def call():

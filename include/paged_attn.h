@@ -131,7 +131,8 @@ typedef struct pa_plan_info {
   int32_t workgroups;    /* workgroups of the main launch */
   int32_t heads_per_item; /* KV heads one decode item covers (decode-only plans: a power of two) */
   int32_t bwd_dq_items;   /* backward: (query, KV head) workgroups of the dQ pass (GQA plans) */
-  int32_t bwd_kv_items;   /* backward: (64-key block, KV head) workgroups of the dK/dV pass */
+  int32_t bwd_kv_items;   /* backward: (128-key block, KV head) workgroups of the dK/dV pass */
+  int32_t bwd_shared_pages; /* backward: 1 when a referenced pool page holds two key positions (f32 atomic sums) */
 } pa_plan_info;
 
 /*
@@ -276,10 +277,18 @@ int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const vo
                  void* v_pool, int32_t head_dim, int32_t v_head_dim, void* stream);
 
 /*
- * Bytes of f32 workspace pa_attention_bwd needs: one value per (query, head)
- * row (D = dO . O), 256-byte aligned; 0 when the plan has no queries.
+ * Bytes of f32 workspace pa_attention_bwd needs for this plan, data type and
+ * head sizes: one value per (query, head) row (D = dO . O), 256-byte aligned;
+ * when the plan has queries and a pool page holding two key positions
+ * (pa_plan_info.bwd_shared_pages) and the data are 16-bit, also f32 sums of
+ * the whole dK and dV pools (num_pages * page_size * Hkv * (D + Dv) values;
+ * ruDNN's backward keeps low-precision history gradients in f32 scratch the
+ * same way).  0 when the plan has no queries.  Errors: PA_ERR_INVALID for a
+ * NULL argument or an unknown dtype, PA_ERR_SHAPE for head sizes outside
+ * [1, 1024].
  */
-int pa_plan_bwd_workspace_bytes(const pa_plan* plan, size_t* bytes);
+int pa_plan_bwd_workspace_bytes(const pa_plan* plan, int32_t dtype, int32_t head_dim, int32_t v_head_dim,
+                                size_t* bytes);
 
 /*
  * Paged GQA/MHA backward (ruDNN 0.1.107 paged_attention
@@ -290,8 +299,15 @@ int pa_plan_bwd_workspace_bytes(const pa_plan* plan, size_t* bytes);
  *   D = dO . O   dS_t = P_t (dO . V_t - D)   dQ = scale sum_t dS_t K_t
  *   dK_t = scale sum_rows dS_t Q             dV_t = sum_rows P_t dO
  *
- * summed over the G query heads of each KV head.  Every pool row has a single
- * writer (ruDNN's ordered, atomic-free variant), so results are reproducible.
+ * summed over the G query heads of each KV head.  When every referenced pool
+ * page holds key positions of one sequence, every pool row has a single
+ * writer (ruDNN's ordered, atomic-free variant) and results repeat bit for
+ * bit.  When a page is shared (prefix sharing between sequences, or one page
+ * at two positions of a sequence), the contributions to its rows are added
+ * up in f32 with atomic adds (ruDNN's atomic variant), in the pools for f32
+ * data and in workspace sums rounded into the pools once for 16-bit data;
+ * the order of the additions, and so the last bits of those rows, may then
+ * change from call to call.
  *
  *   dtype        of q, k_pool, v_pool, out, dout, dq, dk_pool, dv_pool
  *   q, k_pool, v_pool  as for pa_attention_fwd with the same plan
@@ -303,9 +319,8 @@ int pa_plan_bwd_workspace_bytes(const pa_plan* plan, size_t* bytes);
  *   workspace    >= pa_plan_bwd_workspace_bytes bytes, 256-byte aligned
  *
  * Head sizes as for pa_attention_fwd.  Errors: PA_ERR_UNSUPPORTED for MLA
- * plans (no MLA backward in this build) and for missing kernels; PA_ERR_PLAN
- * when a pool page holds key positions of two sequences (or two positions of
- * one: the single-writer pass cannot own it); PA_ERR_WORKSPACE,
+ * plans (no MLA backward in this build) and for missing kernels;
+ * PA_ERR_WORKSPACE,
  * PA_ERR_OVERLAP, PA_ERR_SHAPE, PA_ERR_DEVICE, PA_ERR_HIP as for
  * pa_attention_fwd.  Q == 0 zeroes dk_pool and dv_pool and touches nothing
  * else.

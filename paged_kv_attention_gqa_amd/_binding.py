@@ -49,7 +49,7 @@ class _PlanInfo(ctypes.Structure):
                 ("prefill_items", ctypes.c_int32), ("split_rows", ctypes.c_int32),
                 ("split_slots", ctypes.c_int32), ("launches", ctypes.c_int32), ("workgroups", ctypes.c_int32),
                 ("heads_per_item", ctypes.c_int32), ("bwd_dq_items", ctypes.c_int32),
-                ("bwd_kv_items", ctypes.c_int32)]
+                ("bwd_kv_items", ctypes.c_int32), ("bwd_shared_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -74,7 +74,7 @@ def load_library():
     lib.pa_attention_fwd.argtypes = [P, I, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_mla_fwd.argtypes = [P, I, P, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_append_kv.argtypes = [P, I, P, P, P, P, I, I, P]
-    lib.pa_plan_bwd_workspace_bytes.argtypes = [P, ctypes.POINTER(S)]
+    lib.pa_plan_bwd_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S)]
     lib.pa_attention_bwd.argtypes = [P, I, P, P, P, P, P, P, P, P, P, I, I, F, P, S, P]
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -234,6 +234,20 @@ def _dtype_code(t) -> int:
     raise ValueError(f"unsupported tensor dtype {t.dtype}")
 
 
+def _dtype_enum(dtype) -> int:
+    """Library dtype code of a torch dtype or of "f32" / "bf16" / "f16"."""
+    names = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16}
+    if isinstance(dtype, str):
+        if dtype not in names:
+            raise ValueError(f"unsupported dtype {dtype!r}")
+        return names[dtype]
+    import torch
+    codes = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.float16: PA_F16}
+    if dtype not in codes:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return codes[dtype]
+
+
 def _dev(t, name: str, ndim: int):
     if t is None:
         return None
@@ -289,9 +303,12 @@ def pa_attention_fwd(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: flo
                                            _event(event_after_main), _stream_handle(stream)), "pa_attention_fwd")
 
 
-def pa_plan_bwd_workspace_bytes(plan: Plan) -> int:
+def pa_plan_bwd_workspace_bytes(plan: Plan, dtype, head_dim: int, v_head_dim: int) -> int:
+    """Workspace bytes pa_attention_bwd needs; dtype is a torch dtype or
+    "f32" / "bf16" / "f16"."""
     n = ctypes.c_size_t()
-    _check(load_library().pa_plan_bwd_workspace_bytes(plan.handle, ctypes.byref(n)), "pa_plan_bwd_workspace_bytes")
+    _check(load_library().pa_plan_bwd_workspace_bytes(plan.handle, _dtype_enum(dtype), int(head_dim), int(v_head_dim),
+                                                      ctypes.byref(n)), "pa_plan_bwd_workspace_bytes")
     return int(n.value)
 
 

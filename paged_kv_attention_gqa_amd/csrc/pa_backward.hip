@@ -38,7 +38,20 @@ struct BwdArgs {
   void* dv;            // pool shaped [pages, ps, Hkv, Dv]
   float* delta;        // [Q, Hq]: D = dO . O
   const BwdItem* items;
+  float* acc_k;        // null: dK rows are stored (one writer each); else f32 sums shaped like dk
+  float* acc_v;        // likewise for dV
 };
+
+// One dK or dV element of a pool row: stored when every pool row has a
+// single writer, added to the f32 sums when pages are shared (several
+// sequences, or several positions of one, contribute to the row).
+template <typename T>
+__device__ __forceinline__ void put_grad(void* pool, float* acc, uint64_t idx, float v) {
+  if (acc)
+    unsafeAtomicAdd(acc + idx, v);
+  else
+    store_out<T>(pool, idx, v);
+}
 
 // Element e of a lane's chunk as float.
 template <typename T, int N>
@@ -64,6 +77,16 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(u32x4_t* p, int64_t n) {
   const u32x4_t z = {0u, 0u, 0u, 0u};
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = z;
+}
+
+// The f32 sums of shared-page gradients rounded into the 16-bit pool, four
+// elements per thread (grid-stride).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_cast_kernel(const float4* src, uint2* dst, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 x = src[i];
+    dst[i] = uint2{Pair16<T>::pack(x.x, x.y), Pair16<T>::pack(x.z, x.w)};
+  }
 }
 
 // D = dO . O per (query, head) row: one wave per row.
@@ -247,9 +270,9 @@ __global__ __launch_bounds__(kBwdKvWaves* kWave) void bwd_dkv_kernel(BwdArgs b, 
   for (int u = 0; u < U; ++u) {
     if (!valid[u]) continue;
 #pragma unroll
-    for (int e = 0; e < EK; ++e) store_out<T>(b.dk, slot[u] * krow + (uint64_t)kvh * D + c * EK + e, dk[u][e]);
+    for (int e = 0; e < EK; ++e) put_grad<T>(b.dk, b.acc_k, slot[u] * krow + (uint64_t)kvh * D + c * EK + e, dk[u][e]);
 #pragma unroll
-    for (int e = 0; e < EV; ++e) store_out<T>(b.dv, slot[u] * vrow + (uint64_t)kvh * DV + c * EV + e, dv[u][e]);
+    for (int e = 0; e < EV; ++e) put_grad<T>(b.dv, b.acc_v, slot[u] * vrow + (uint64_t)kvh * DV + c * EV + e, dv[u][e]);
   }
   }
 }
@@ -455,9 +478,11 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
     if (t >= it.tok_end) continue;
     const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
 #pragma unroll
-    for (int blk = 0; blk < DBK; ++blk) store_out<T>(b.dk, slot * krow + (uint64_t)kvh * D + 16 * blk + n, dk[blk][e]);
+    for (int blk = 0; blk < DBK; ++blk)
+      put_grad<T>(b.dk, b.acc_k, slot * krow + (uint64_t)kvh * D + 16 * blk + n, dk[blk][e]);
 #pragma unroll
-    for (int blk = 0; blk < DBV; ++blk) store_out<T>(b.dv, slot * vrow + (uint64_t)kvh * DV + 16 * blk + n, dv[blk][e]);
+    for (int blk = 0; blk < DBV; ++blk)
+      put_grad<T>(b.dv, b.acc_v, slot * vrow + (uint64_t)kvh * DV + 16 * blk + n, dv[blk][e]);
   }
 }
 
@@ -657,22 +682,31 @@ BwdFn pick_bwd(int dtype, int d, int dv, int g) {
 bool bwd_supported(int dtype, int d, int dv, int g) { return pick_bwd(dtype, d, dv, g) != nullptr; }
 
 hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, const void* dout, void* dq, void* dk,
-                          void* dvp, float* delta, const BwdItem* items, int n_dq, int n_kv, int n_dqt, int64_t rows,
-                          int64_t pool_slots, int n_cu, hipStream_t stream) {
+                          void* dvp, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
+                          int n_dqt, int64_t rows, int64_t pool_slots, int n_cu, hipStream_t stream) {
   BwdFn f = pick_bwd(dtype, d, dv, g);
   if (!f) return hipErrorInvalidValue;
   const int es = dtype == 0 ? 4 : 2;
-  // gradient pools start at zero: rows no query sees keep it
+  // Shared pages: f32 gradients are added into the pools themselves, 16-bit
+  // ones into f32 sums in the workspace that are rounded into the pools last.
+  float* acc_k = nullptr;
+  float* acc_v = nullptr;
+  if (shared) {
+    acc_k = dtype == 0 ? static_cast<float*>(dk) : acc;
+    acc_v = dtype == 0 ? static_cast<float*>(dvp) : acc + pool_slots * d;
+  }
+  // the gradient sums start at zero: rows no query sees keep it
   for (int pass = 0; pass < 2; ++pass) {
-    const int64_t chunks = pool_slots * (pass == 0 ? d : dv) * es / 16;
+    void* base = pass == 0 ? (acc_k ? static_cast<void*>(acc_k) : dk) : (acc_v ? static_cast<void*>(acc_v) : dvp);
+    const int64_t chunks = pool_slots * (pass == 0 ? d : dv) * (acc_k ? 4 : es) / 16;
     if (chunks == 0) continue;
     const int64_t grid = std::min<int64_t>((chunks + 255) / 256, (int64_t)std::max(n_cu, 1) * 16);
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       reinterpret_cast<u32x4_t*>(pass == 0 ? dk : dvp), chunks);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)grid), dim3(256), 0, stream, reinterpret_cast<u32x4_t*>(base),
+                       chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  BwdArgs b{a, dout, dq, dk, dvp, delta, items};
+  BwdArgs b{a, dout, dq, dk, dvp, delta, items, acc_k, acc_v};
   if (rows > 0) {
     const unsigned grid = (unsigned)((rows + 3) / 4);
     if (dtype == 0)
@@ -684,7 +718,22 @@ hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return f(b, n_dq, n_kv, n_dqt, stream);
+  hipError_t e = f(b, n_dq, n_kv, n_dqt, stream);
+  if (e != hipSuccess || !shared || dtype == 0) return e;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t n4 = pool_slots * (pass == 0 ? d : dv) / 4;
+    if (n4 == 0) continue;
+    const int64_t grid = std::min<int64_t>((n4 + 255) / 256, (int64_t)std::max(n_cu, 1) * 16);
+    const float4* src = reinterpret_cast<const float4*>(pass == 0 ? acc_k : acc_v);
+    uint2* dst = reinterpret_cast<uint2*>(pass == 0 ? dk : dvp);
+    if (dtype == 1)
+      hipLaunchKernelGGL(bwd_cast_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, src, dst, n4);
+    else
+      hipLaunchKernelGGL(bwd_cast_kernel<_Float16>, dim3((unsigned)grid), dim3(256), 0, stream, src, dst, n4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pa

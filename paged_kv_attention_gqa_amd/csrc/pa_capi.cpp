@@ -434,8 +434,9 @@ void build_work(pa_plan* p) {
 // rows and KV head over the union of their visible keys (MFMA kernel; the
 // launch picks one list by data type and head size).  dK/dV: one item per (block of kBwdBlockKeys keys,
 // KV head) of every sequence with queries, skipping blocks no query sees;
-// every pool row then has a single writer, which needs each referenced page
-// to hold key positions of one sequence only.  Both lists run longest first.
+// every pool row then has a single writer when each referenced page holds key
+// positions of one sequence only (else the launch adds the rows up in f32 and
+// shared_page names the first shared page).  The lists run longest first.
 void build_bwd(pa_plan* p) {
   if (p->mla) return;
   std::vector<int32_t> owner(p->num_pages, -1);
@@ -744,6 +745,7 @@ int pa_plan_get_info(const pa_plan* plan, pa_plan_info* info) {
   info->heads_per_item = 1 << plan->heads_shift;
   info->bwd_dq_items = plan->n_bwd_dq;
   info->bwd_kv_items = plan->n_bwd_kv;
+  info->bwd_shared_pages = plan->shared_page >= 0 ? 1 : 0;
   return ok();
 }
 
@@ -964,9 +966,24 @@ int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const vo
   return ok();
 }
 
-int pa_plan_bwd_workspace_bytes(const pa_plan* plan, size_t* bytes) {
+// f32 D = dO . O per (query, head) row at the start of the backward workspace.
+static size_t bwd_delta_bytes(const pa_plan* plan) {
+  return plan->Q > 0 ? align_up((size_t)plan->Q * plan->hq * 4, kAlign) : 0;
+}
+
+// Some pool row takes dK / dV from two key positions (only matters when
+// there are queries).
+static bool bwd_shared(const pa_plan* plan) { return plan->shared_page >= 0 && plan->Q > 0; }
+
+int pa_plan_bwd_workspace_bytes(const pa_plan* plan, int32_t dtype, int32_t head_dim, int32_t v_head_dim,
+                                size_t* bytes) {
   if (!plan || !bytes) return fail(PA_ERR_INVALID, "plan or bytes is NULL");
-  *bytes = plan->Q > 0 ? align_up((size_t)plan->Q * plan->hq * 4, kAlign) : 0;
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
+    return fail(PA_ERR_SHAPE, "head sizes D=%d Dv=%d outside [1, 1024]", head_dim, v_head_dim);
+  *bytes = bwd_delta_bytes(plan);
+  if (bwd_shared(plan) && dtype != PA_F32)
+    *bytes += align_up((size_t)plan->num_pages * plan->ps * plan->hkv * (head_dim + v_head_dim) * 4, kAlign);
   return ok();
 }
 
@@ -984,15 +1001,12 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
     return fail(PA_ERR_SHAPE, "head sizes D=%d Dv=%d outside [1, 1024]", head_dim, v_head_dim);
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
-  if (plan->shared_page >= 0)
-    return fail(PA_ERR_PLAN, "pool page %d holds key positions of two sequences (or two positions of one); "
-                "the single-writer backward needs pages owned by one position each", plan->shared_page);
   const int G = plan->group();
   if (!pa::bwd_supported(dtype, head_dim, v_head_dim, G))
     return fail(PA_ERR_UNSUPPORTED, "no backward kernel for dtype %d, D=%d, Dv=%d, G=%d", dtype, head_dim, v_head_dim,
                 G);
   size_t need = 0;
-  pa_plan_bwd_workspace_bytes(plan, &need);
+  pa_plan_bwd_workspace_bytes(plan, dtype, head_dim, v_head_dim, &need);
   if (need > 0) {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "backward needs %zu bytes of workspace", need);
     if (workspace_bytes < need)
@@ -1040,7 +1054,9 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   a.causal = plan->causal;
   a.window = plan->window;
   hipError_t e = pa::launch_gqa_bwd(dtype, head_dim, v_head_dim, G, a, dout, dq, dk_pool, dv_pool,
-                                    reinterpret_cast<float*>(workspace), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv,
+                                    reinterpret_cast<float*>(workspace),
+                                    reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(plan)),
+                                    bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv,
                                     plan->n_bwd_dqt, (int64_t)rows, (int64_t)slots, std::max(plan->n_cu, 1), st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();

@@ -44,11 +44,13 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, voi
 // Paged GQA/MHA backward: zero dk / dv (pool shaped, pool_slots rows of each),
 // D = dO . O for the `rows` (query, head) rows into delta, then dQ (per-query
 // items [0, n_dq), or on MFMA the row tiles [n_dq + n_kv, + n_dqt)) and
-// dK / dV over items [n_dq, n_dq + n_kv).
+// dK / dV over items [n_dq, n_dq + n_kv).  `shared` (a pool page holds two
+// key positions): dK / dV are added up in f32 -- in the pools for f32 data,
+// else in `acc` (pool_slots x (d + dv) floats) rounded into the pools last.
 bool bwd_supported(int dtype, int d, int dv, int g);
 hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, const void* dout, void* dq, void* dk,
-                          void* dvp, float* delta, const BwdItem* items, int n_dq, int n_kv, int n_dqt, int64_t rows,
-                          int64_t pool_slots, int n_cu, hipStream_t stream);
+                          void* dvp, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
+                          int n_dqt, int64_t rows, int64_t pool_slots, int n_cu, hipStream_t stream);
 
 
 }  // namespace pa

@@ -413,6 +413,23 @@ def random_batch(seed: int, *, dtype: str = "bf16", hq: int = 8, hkv: int = 2, d
                       page_size, pool, hq, hkv, d, dv, sc, causal, window, q, k, v, seed, max_splits)
 
 
+def with_shared_pages(b: PagedBatch, links) -> PagedBatch:
+    """A copy of `b` whose block table points page slot j_dst of sequence
+    s_dst at the pool page of slot j_src of sequence s_src, for each
+    (s_dst, j_dst, s_src, j_src) in `links` (prefix sharing between sequences,
+    or one page at two positions of a sequence).  The pools are unchanged; the
+    rows the new reader sees must be rows the source sequence holds (so no
+    poisoned tail slot becomes visible)."""
+    bt = b.block_table.copy()
+    ps = b.page_size
+    for s_dst, j_dst, s_src, j_src in links:
+        need = min(ps, int(b.seq_lens[s_dst]) - j_dst * ps)
+        have = min(ps, int(b.seq_lens[s_src]) - j_src * ps)
+        assert 0 < need <= have, (s_dst, j_dst, s_src, j_src)
+        bt[s_dst, j_dst] = b.block_table[s_src, j_src]
+    return dataclasses.replace(b, name=b.name + "+shared", block_table=bt)
+
+
 def random_mla_batch(seed: int, *, heads: int = 16, r: int = 512, p: int = 64, page_size: int = 64,
                      q_counts=(1, 1, 1), histories=None, max_len: int = 700, causal: bool = True,
                      window: int = 0, extra_pages: int = 2, poison: bool = True,

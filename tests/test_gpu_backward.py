@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import paged_kv_attention_gqa_amd as pa
-from synth import f32_to_bf16_bits, f32_to_f16_bits, random_batch
+from synth import f32_to_bf16_bits, f32_to_f16_bits, random_batch, with_shared_pages
 from tests.gpu_harness import GqaRun, make_plan, to_f64, to_torch, torch_dtype
 
 pytestmark = pytest.mark.gpu
@@ -36,7 +36,7 @@ class BwdRun:
         self.dq = torch.empty((b.num_queries, b.hq, b.d), dtype=dt, device="cuda")
         self.dk = torch.full_like(self.fwd.k, float("nan"))  # every element must be written
         self.dv = torch.full_like(self.fwd.v, float("nan"))
-        n = pa.pa_plan_bwd_workspace_bytes(self.fwd.plan)
+        n = pa.pa_plan_bwd_workspace_bytes(self.fwd.plan, b.dtype, b.d, b.dv)
         self.ws = torch.empty(max(n, 4) // 4 + 64, dtype=torch.float32, device="cuda") if n else None
 
     def __call__(self):
@@ -137,20 +137,30 @@ def test_backward_without_queries_zeroes_the_pools():
     assert not dk.float().abs().sum().item() and not dv.float().abs().sum().item()
 
 
-def test_backward_refuses_shared_pages_and_mla_plans():
-    import torch
-    b = random_batch(7500, dtype="bf16", hq=8, hkv=2, d=64, page_size=16, q_counts=(1, 1), histories=[20, 20])
-    bt = b.block_table.copy()
-    bt[1, 0] = bt[0, 0]  # both sequences read one page
-    plan = pa.pa_plan_create(b.seq_lens, b.cu_q, b.q_pos, bt, page_size=b.page_size, num_pages=b.num_pages,
-                             num_q_heads=b.hq, num_kv_heads=b.hkv, causal=True, window=0, max_splits=1)
-    q, k, v = to_torch(b.q, "bf16"), to_torch(b.k, "bf16"), to_torch(b.v, "bf16")
-    out = torch.empty((b.num_queries, b.hq, b.dv), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((b.num_queries, b.hq), dtype=torch.float32, device="cuda")
-    pa.pa_attention_fwd(plan, q, k, v, out, lse, scale=b.scale)
-    ws = torch.empty(pa.pa_plan_bwd_workspace_bytes(plan) // 4 + 64, dtype=torch.float32, device="cuda")
-    with pytest.raises(pa.PaError) as e:
-        pa.pa_attention_bwd(plan, q, k, v, out, lse, out.clone(), torch.empty_like(q), torch.empty_like(k),
-                            torch.empty_like(v), scale=b.scale, workspace=ws)
-    assert e.value.status == -3
-    torch.cuda.synchronize()
+SHARED_CASES = [
+    # two sequences continue a 128-key prefix held by sequence 0's pages
+    (dict(dtype="bf16", hq=32, hkv=8, d=128, page_size=16, q_counts=(40, 30, 1), histories=[200, 180, 300]),
+     [(s, j, 0, j) for s in (1, 2) for j in range(8)]),
+    (dict(dtype="f16", hq=32, hkv=8, d=192, dv=128, page_size=16, q_counts=(20, 9), histories=[100, 90]),
+     [(1, j, 0, j) for j in range(5)]),
+    # f32 (vector kernels add into the pools), one page read at two positions of a sequence too
+    (dict(dtype="f32", hq=8, hkv=2, d=64, page_size=16, q_counts=(12, 5), histories=[70, 80]),
+     [(1, 0, 0, 0), (1, 1, 0, 1), (1, 4, 1, 2)]),
+    (dict(dtype="bf16", hq=16, hkv=4, d=64, page_size=1, q_counts=(17, 2), histories=[30, 25], window=20),
+     [(1, j, 0, j) for j in range(20)]),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SHARED_CASES)))
+def test_backward_shared_pages_parity(i):
+    """Pages read by two sequences (prefix sharing) or at two positions of one:
+    their rows' gradients are f32 sums of every reader's contribution."""
+    kw, links = SHARED_CASES[i]
+    b = with_shared_pages(random_batch(7500 + i, **kw), links)
+    run, _, _ = _parity(b, 7550 + i)
+    info = pa.pa_plan_get_info(run.fwd.plan)
+    assert info["bwd_shared_pages"] == 1
+    es = 4 if b.dtype == "f32" else 2
+    extra = 0 if es == 4 else b.num_pages * b.page_size * b.hkv * (b.d + b.dv) * 4
+    base = pa.pa_plan_bwd_workspace_bytes(make_plan(random_batch(7500 + i, **kw)), b.dtype, b.d, b.dv)
+    assert pa.pa_plan_bwd_workspace_bytes(run.fwd.plan, b.dtype, b.d, b.dv) >= base + extra

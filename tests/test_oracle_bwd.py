@@ -85,6 +85,29 @@ def test_backward_matches_torch_autograd_float64(i):
     np.testing.assert_allclose(dv, rv, rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_with_shared_pages_matches_torch_autograd_float64(dtype):
+    """Prefix sharing (sequence 1 reads sequence 0's first two pages) and one
+    page at two positions of sequence 2: a pool row's key and value gradients
+    are the sums over every position that reads it (np.add.at over the dense
+    views in the reference)."""
+    from synth import with_shared_pages
+    b = random_batch(350, dtype=dtype, hq=4, hkv=2, d=8, page_size=4, q_counts=(3, 2, 4),
+                     histories=[10, 12, 14], poison=True)
+    s = with_shared_pages(b, [(1, 0, 0, 0), (1, 1, 0, 1), (2, 3, 2, 1)])
+    dout = _dout(s, 351)
+    dq, dk, dv = oracle.attention_bwd(s, dout)
+    rq, rk, rv = _torch_grads(s, dout)
+    np.testing.assert_allclose(dq, rq, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, rk, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, rv, rtol=1e-11, atol=1e-12)
+    # the shared rows really take two contributions: differ from the
+    # unshared tables' gradients there
+    _, uk, _ = oracle.attention_bwd(b, dout)
+    p0 = b.block_table[0, 0]
+    assert not np.allclose(dk[p0], uk[p0])
+
+
 def test_backward_matches_central_differences_of_the_forward():
     """d/dx of sum(dout * out) by (f(x + h) - f(x - h)) / 2h on f32 inputs,
     h = 2^-12 (exact in f32 for these values), for elements of q, k and v."""

@@ -248,3 +248,35 @@ def test_append_rejects_two_queries_writing_one_slot():
     assert lib.pa_append_kv(p.handle, 1, 1 << 20, 2 << 20, 3 << 20, 1 << 30, 64, 64, None) == -3
     assert "writes the pool slot" in pa.pa_last_error()
     pa.pa_plan_destroy(p)
+
+
+def test_backward_workspace_and_shared_page_detection():
+    """The backward workspace holds one f32 D = dO . O per (query, head) row
+    (256-byte aligned); a table that points two positions at one pool page
+    sets bwd_shared_pages and, for 16-bit data, adds f32 sums of the whole dK
+    and dV pools; f32 data need none (the sums are the pools).  Bad dtype or
+    head sizes are refused."""
+    s = schedule(10, q_counts=[3, 2], histories=[40, 30], page_size=16, hq=8, hkv=2)
+    p = pa.pa_plan_create_host(num_cus=256, **s)
+    assert pa.pa_plan_get_info(p)["bwd_shared_pages"] == 0
+    assert pa.pa_plan_bwd_workspace_bytes(p, "bf16", 64, 64) == 256
+    assert pa.pa_plan_bwd_workspace_bytes(p, "f32", 64, 64) == 256
+    with pytest.raises(ValueError):
+        pa.pa_plan_bwd_workspace_bytes(p, "f64", 64, 64)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan_bwd_workspace_bytes(p, "bf16", 0, 64)
+    assert e.value.status == -2
+    pa.pa_plan_destroy(p)
+    s["block_table"] = s["block_table"].copy()
+    s["block_table"][1, 0] = s["block_table"][0, 0]  # prefix sharing of the first page
+    p = pa.pa_plan_create_host(num_cus=256, **s)
+    assert pa.pa_plan_get_info(p)["bwd_shared_pages"] == 1
+    slots = s["num_pages"] * 16 * 2
+    assert pa.pa_plan_bwd_workspace_bytes(p, "bf16", 64, 32) == 256 + -(-slots * 96 * 4 // 256) * 256
+    assert pa.pa_plan_bwd_workspace_bytes(p, "f32", 64, 32) == 256
+    pa.pa_plan_destroy(p)
+    s0 = schedule(11, q_counts=[0, 0], histories=[40, 30], page_size=16, hq=8, hkv=2)
+    s0["block_table"][1, 0] = s0["block_table"][0, 0]
+    p = pa.pa_plan_create_host(num_cus=256, **s0)
+    assert pa.pa_plan_bwd_workspace_bytes(p, "bf16", 64, 64) == 0  # no queries: nothing to add up
+    pa.pa_plan_destroy(p)
