@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_e
     if (PREFILL && it.kind == kPrefill)
       mla_item<T, PREFILL>(a, it, smem, tid);
     else
-      mla_item<T, false>(a, it, smem, tid);
+      mla_item<T, false, !PREFILL>(a, it, smem, tid);
   }
 }
 

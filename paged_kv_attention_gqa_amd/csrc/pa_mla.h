@@ -18,11 +18,13 @@
 // (three in flight while one is used, one barrier per tile), loaded with
 // global_load_lds_dwordx4 (16-byte pieces of key row t stored at piece ^
 // swz(t)); page numbers come from a per-lane window of 64 tiles loaded
-// once per 64 tiles, so the vector-memory counter counts tile loads only.  Every wave computes the
-// small score tile (so softmax statistics agree across waves without any
-// exchange) and owns R / 4 = 128 output dims; latent^T fragments come from
-// ds_read_b64_tr_b16.  Every lane owns one head's column, so softmax needs
-// two cross-lane steps per tile.
+// once per 64 tiles, so the vector-memory counter counts tile loads only.  Each
+// wave computes the score tile over a quarter of the 576 dims; the four
+// partial tiles meet in LDS and every wave sums them in one fixed order, so
+// all waves hold the same scores and softmax statistics.  Each wave owns
+// R / 4 = 128 output dims; latent^T fragments come from ds_read_b64_tr_b16.
+// Every lane owns one head's column, so softmax needs two cross-lane steps
+// per tile.
 #pragma once
 
 #include "pa_decode.h"
@@ -44,7 +46,8 @@ struct MlaSmem {
   static constexpr int kLatTile = kMlaTileKeys * kMlaRank * 2;   // 16 KB
   static constexpr int kPosTile = kMlaTileKeys * kMlaRope * 2;   // 2 KB
   static constexpr int kStage = kLatTile + kPosTile;
-  static constexpr int kBytes = kMlaStages * kStage;             // 72 KB
+  static constexpr int kXchgOff = kMlaStages * kStage;           // 72 KB
+  static constexpr int kBytes = kXchgOff + kMlaWaves * 64 * 16;  // + partial scores of the four waves
 };
 
 template <typename T>
@@ -79,9 +82,15 @@ __device__ __forceinline__ int mla_off(int key, int piece) {
 // (both compute the query's scores), and mask the keys of the shared tiles
 // by that query's position.  The tiles are loaded once for the item's
 // queries.
+//
+// SPLIT (decode items): the score tile is split over the waves as above.
+// The prefill instantiation runs its decode items with SPLIT = false, every
+// wave computing the whole score tile: hipcc for gfx950 fails to generate
+// code ("operand has incorrect register class") for the split tile next to
+// the prefill body in one kernel.
 constexpr int kMlaWavesPerQuery = kMlaWaves / kMlaPrefillQueries;
 static_assert(kMlaWavesPerQuery == 2, "two waves per prefill query");
-template <typename T, bool PREFILL = false>
+template <typename T, bool PREFILL = false, bool SPLIT = true>
 __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it, char* smem, int tid = threadIdx.x) {
   constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = kMlaTileKeys;
   constexpr int KS_LAT = R / 32, KS_POS = P / 32;  // 16x16x32 k-steps
@@ -106,15 +115,25 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.k);
   const uint16_t* kpos = reinterpret_cast<const uint16_t*>(a.kr);
 
-  // q^T operands: lane (n, c) holds dims 32 ks + 8 c .. +7 of head n
-  frag_t qa[KS_LAT], qp[KS_POS];
+  // q^T operands: lane (n, c) holds dims 32 ks + 8 c .. +7 of head n.
+  // Decode: each wave computes the scores over its own quarter of the
+  // latent k-steps (4 wave .. 4 wave + 3, 16x16x32) and of the rotary dims
+  // (16 wave .. 16 wave + 15, one 16x16x16 step: lane (n, c) holds dims
+  // 16 wave + 4 c .. +3); the four partial tiles are summed through LDS.
+  constexpr bool SPLIT_S = !PREFILL && SPLIT;
+  constexpr int QA = SPLIT_S ? KS_LAT / kMlaWaves : KS_LAT, QP = SPLIT_S ? 0 : KS_POS;
+  static_assert(P == 16 * kMlaWaves, "one 16-dim rotary step per wave");
+  const int ks0 = SPLIT_S ? QA * wave : 0;
+  frag_t qa[QA], qp[QP > 0 ? QP : 1];
+  short4_t qp16 = {};
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((uint64_t)qi * H + n) * R;
     const uint16_t* prow = reinterpret_cast<const uint16_t*>(a.qr) + ((uint64_t)qi * H + n) * P;
 #pragma unroll
-    for (int k = 0; k < KS_LAT; ++k) qa[k] = *reinterpret_cast<const frag_t*>(qrow + 32 * k + 8 * c);
+    for (int k = 0; k < QA; ++k) qa[k] = *reinterpret_cast<const frag_t*>(qrow + 32 * (ks0 + k) + 8 * c);
 #pragma unroll
-    for (int k = 0; k < KS_POS; ++k) qp[k] = *reinterpret_cast<const frag_t*>(prow + 32 * k + 8 * c);
+    for (int k = 0; k < QP; ++k) qp[k] = *reinterpret_cast<const frag_t*>(prow + 32 * k + 8 * c);
+    if constexpr (SPLIT_S) qp16 = *reinterpret_cast<const short4_t*>(prow + 16 * wave + 4 * c);
   }
   // The tile loads below are inline assembly that the compiler's wait-count
   // pass does not see; it would count only these query loads as outstanding
@@ -224,7 +243,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       for (int k = 0; k < KS_POS; ++k)
         sc[k & 1] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * k + c)), qp[k], sc[k & 1]);
       s = sc[0] + sc[1];
-    } else {
+    } else if constexpr (!SPLIT_S) {
       frag_t kf[KS_LAT + KS_POS];
 #pragma unroll
       for (int k = 0; k < KS_LAT; ++k) kf[k] = *reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * k + c));
@@ -237,6 +256,26 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
 #pragma unroll
       for (int k = 0; k < KS_POS; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[KS_LAT + k], qp[k], sc[k & 1]);
       s = sc[0] + sc[1];
+    } else {
+      frag_t kf[QA];
+      // pieces 16 wave + 4 k + c: the swizzle (< 16) leaves the 16-piece block in place
+      const char* lsw = ls + 256 * wave;
+#pragma unroll
+      for (int k = 0; k < QA; ++k) kf[k] = *reinterpret_cast<const frag_t*>(lsw + mla_off<R>(n, 4 * k + c));
+      const short4_t kp16 = *reinterpret_cast<const short4_t*>(kps + mla_off<P>(n, 2 * wave + (c >> 1)) + (c & 1) * 8);
+      floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int k = 0; k < QA; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[k], qa[k], sc[k & 1]);
+      sc[0] = mfma_16x16x16<T>(kp16, qp16, sc[0]);
+      // the partial tiles of the four waves, summed in one fixed order so
+      // that every wave holds the same scores (the previous tile's reads
+      // were done before this tile's barrier)
+      typedef __attribute__((address_space(3))) floatx4_t lds_f4_t;
+      lds_f4_t* xs = (lds_f4_t*)(size_t)__builtin_amdgcn_readfirstlane(
+          (uint32_t)(size_t)(lds_void_t*)(smem + MlaSmem::kXchgOff));
+      xs[wave * 64 + lane] = sc[0] + sc[1];
+      __syncthreads();
+      s = ((xs[lane] + xs[64 + lane]) + xs[128 + lane]) + xs[192 + lane];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
