@@ -475,11 +475,15 @@ constexpr int kMergeUnroll = 16;
 // takes outputs chunk, chunk + chunks, ... in units of blockDim.
 template <typename T, int DV, int G>
 __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& mi, int chunk, int chunks) {
-  for (int idx = chunk * blockDim.x + threadIdx.x; idx < G * DV; idx += chunks * blockDim.x) {
-    const int g = idx / DV, d = idx % DV;
-    float M = -INFINITY, L = 0.f, LX = 0.f, O = 0.f;
+  // four consecutive output dims per thread (16-byte partial loads)
+  static_assert(DV % 4 == 0, "merge reads four dims at a time");
+  for (int idx = chunk * blockDim.x + threadIdx.x; idx < G * DV / 4; idx += chunks * blockDim.x) {
+    const int g = (4 * idx) / DV, d = (4 * idx) % DV;
+    float M = -INFINITY, L = 0.f, LX = 0.f;
+    floatx4_t O = {0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < mi.nsplit; j0 += kMergeUnroll) {
-      float mj[kMergeUnroll], lj[kMergeUnroll], lxj[kMergeUnroll], oj[kMergeUnroll];
+      float mj[kMergeUnroll], lj[kMergeUnroll], lxj[kMergeUnroll];
+      floatx4_t oj[kMergeUnroll];
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
         const int j = j0 + u;
@@ -487,7 +491,7 @@ __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& 
         mj[u] = a.ws_ml[sl * 3];
         lj[u] = a.ws_ml[sl * 3 + 1];
         lxj[u] = a.ws_ml[sl * 3 + 2];
-        oj[u] = a.ws_o[sl * DV + d];
+        oj[u] = *reinterpret_cast<const floatx4_t*>(a.ws_o + sl * DV + d);
         if (j >= mi.nsplit) mj[u] = -INFINITY;
       }
       float Mn = M;
@@ -507,7 +511,9 @@ __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& 
       M = Mn;
     }
     const int h = mi.kvh * G + g;
-    store_out<T>(a.out, ((uint64_t)mi.q * a.hq + h) * DV + d, O / L);
+    const uint64_t o0 = ((uint64_t)mi.q * a.hq + h) * DV + d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out<T>(a.out, o0 + e, O[e] / L);
     if (a.lse && d == 0) a.lse[(uint64_t)mi.q * a.hq + h] = (M + log2f(LX)) * 0.69314718055994530942f;
   }
 }

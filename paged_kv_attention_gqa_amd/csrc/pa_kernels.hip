@@ -147,7 +147,7 @@ hipError_t launch_mixed_t(const KernelArgs& a, int n_wg, const MergeItem*, int, 
 template <typename T, int DV, int G>
 hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, hipStream_t stream) {
   if (n_merges > 0) {
-    const int chunks = (G * DV + kMergeThreads - 1) / kMergeThreads;
+    const int chunks = (G * DV / 4 + kMergeThreads - 1) / kMergeThreads;
     hipLaunchKernelGGL((merge_kernel<T, DV, G>), dim3(n_merges, chunks), dim3(kMergeThreads), 0, stream, a, merges);
     return hipGetLastError();
   }
