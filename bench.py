@@ -208,11 +208,28 @@ def measure(name, steps, warmup, split_tokens=0):
         step(j, mids[j])
         ends[j].record(stream)
     torch.cuda.synchronize()
+    mains = [x.elapsed_time(y) for x, y in zip(starts, mids)]
+
+    # Plan creation (validation, host planning and the one upload of tables
+    # and work items), timed apart from the steps it serves.
+    import paged_kv_attention_gqa_amd as pa
+    from tests.gpu_harness import make_plan
+    plan_ms = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        p = make_plan(b, mla=mla, split_tokens=split_tokens)
+        torch.cuda.synchronize()
+        plan_ms.append((time.perf_counter() - t) * 1e3)
+        pa.pa_plan_destroy(p)
     res = {
         "b": b, "mla": mla, "info": run_.info, "copies": len(pools),
         "ms_per_step": max(wall * 1e3, gpu_ms) / steps,
-        "main_ms": float(np.mean([x.elapsed_time(y) for x, y in zip(starts, mids)])),
+        "main_ms": float(np.mean(mains)),
+        "main_ms_median": float(np.median(mains)),
+        "main_ms_min": float(np.min(mains)),
         "merge_ms": float(np.mean([x.elapsed_time(y) for x, y in zip(mids, ends)])),
+        "plan_ms": float(np.median(plan_ms)),
     }
     del pools, run_
     torch.cuda.empty_cache()
@@ -226,7 +243,9 @@ def summarize(name, r):
     main_s = r["main_ms"] * 1e-3
     step_s = r["ms_per_step"] * 1e-3
     out = {"workload": name, "ms_per_step": round(r["ms_per_step"], 5), "main_kernel_ms": round(r["main_ms"], 5),
-           "merge_kernel_ms": round(r["merge_ms"], 5), "kv_bytes": kv_bytes, "flops": flops}
+           "main_kernel_ms_median": round(r["main_ms_median"], 5), "main_kernel_ms_min": round(r["main_ms_min"], 5),
+           "merge_kernel_ms": round(r["merge_ms"], 5), "plan_ms": round(r["plan_ms"], 3),
+           "queries_per_s": round(b.num_queries / step_s, 1), "kv_bytes": kv_bytes, "flops": flops}
     if r["info"]["prefill_items"] == 0:
         out.update(bound="hbm", step_gbs=round(kv_bytes / step_s / 1e9, 2),
                    kernel_gbs=round(kv_bytes / main_s / 1e9, 2),
@@ -387,7 +406,10 @@ def run(args):
                    "pool_copies_rotated": r["copies"]},
         "roofline": {"bound": "hbm" if hbm else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": _traffic(f"{name}:main")},
-        "kernels": {"main_ms": round(r["main_ms"], 5), "merge_ms": round(r["merge_ms"], 5), "plan": r["info"]},
+        "kernels": {"main_ms": round(r["main_ms"], 5), "main_ms_median": round(r["main_ms_median"], 5),
+                    "main_ms_min": round(r["main_ms_min"], 5), "merge_ms": round(r["merge_ms"], 5),
+                    "plan_create_ms": round(r["plan_ms"], 3),
+                    "queries_per_s": round(r["b"].num_queries / (r["ms_per_step"] * 1e-3), 1), "plan": r["info"]},
     }
     if not args.no_secondary and name == PRIMARY:
         result["secondary"] = []
