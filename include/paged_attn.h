@@ -30,11 +30,16 @@
  *   - Device pointers are HIP device addresses on the plan's device; tensors
  *     are dense row-major with the shapes stated.  The caller owns every
  *     tensor, the workspace included; the library owns only the plan.
- *   - `stream` is a hipStream_t (NULL = the null stream).  The forward calls
- *     only enqueue kernels: no host synchronisation, no device-to-host
- *     readback (ruDNN `attention_into_split`).
- *   - Calls that share an output or a workspace must be ordered by the
- *     caller (same stream, or events); concurrent calls on them race.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  A plan belongs to
+ *     the device and the stream it was made on, and so does any workspace
+ *     used with it (ruDNN: metadata and split workspaces belong to one device
+ *     queue): every call with a plan must pass that stream, else
+ *     PA_ERR_DEVICE.  The forward calls only enqueue kernels: no host
+ *     synchronisation, no device-to-host readback (ruDNN
+ *     `attention_into_split`).
+ *   - Calls with different plans that share an output or a workspace must be
+ *     ordered by the caller (same stream, or events); concurrent calls on
+ *     them race.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -46,19 +51,20 @@
 extern "C" {
 #endif
 
-/* Status codes.  The error strings of ruDNN's `PagedAttentionError` map onto
- * these classes; pa_status_string() names them. */
+/* Status codes.  Each error case of ruDNN's `PagedAttentionError` falls in
+ * one of these classes; pa_status_string() describes a class. */
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID = -1,     /* null pointer, unknown dtype, flag out of range */
-  PA_ERR_SHAPE = -2,       /* incompatible head/cache/output shape or scale */
+  PA_ERR_SHAPE = -2,       /* tensor sizes, head counts or scale that do not fit together */
   PA_ERR_PLAN = -3,        /* malformed schedule: offsets, positions, block table */
   PA_ERR_UNSUPPORTED = -4, /* valid request with no kernel specialisation in this build */
   PA_ERR_WORKSPACE = -5,   /* split workspace missing or too small */
   PA_ERR_OVERLAP = -6,     /* an output overlaps an input or another output */
   PA_ERR_RANGE = -7,       /* a size exceeds the 32-bit index range */
   PA_ERR_HIP = -8,         /* HIP runtime failure (allocation, copy or launch) */
-  PA_ERR_DEVICE = -9       /* plan used on a device other than the one it was made on, or built on the host only */
+  PA_ERR_DEVICE = -9       /* plan used on a device or stream other than the one it was made on, or built on
+                              the host only */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -137,14 +143,18 @@ typedef struct pa_plan_info {
 
 /*
  * Validate a schedule, build the work list on the host and upload it with one
- * asynchronous host-to-device copy on `stream` (on the current HIP device).
- * The plan keeps its host copy and is bound to that device.  Errors:
+ * asynchronous host-to-device copy on `stream` (on the current HIP device),
+ * into device memory allocated in stream order on that stream.  The plan
+ * keeps its host copy and is bound to that device and stream.  Errors:
  * PA_ERR_INVALID, PA_ERR_PLAN, PA_ERR_UNSUPPORTED (e.g. page_size not a power of
  * two), PA_ERR_RANGE, PA_ERR_HIP.  *out_plan is set only on success.
  */
 int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan);
 
-/* Free a plan (NULL is allowed).  Waits for the device to finish using it. */
+/* Free a plan (NULL is allowed).  The device buffer is released in stream
+ * order on the plan's stream, after every call already enqueued there; the
+ * host does not wait for the device (only, if still pending, for the upload
+ * copy).  Destroy a plan before destroying its stream. */
 int pa_plan_destroy(pa_plan* plan);
 
 /* Fill *info with the plan's work counts. */
@@ -204,9 +214,10 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
  *   scale        finite and > 0 (e.g. 1/sqrt(D))
  *   workspace    f32 scratch of >= pa_plan_workspace_bytes(plan, v_head_dim)
  *                bytes, 256-byte aligned; may be NULL when that size is 0
- *   event_after_main  NULL, or a hipEvent_t recorded on `stream` right after
- *                the main attention kernel and before the split merge (lets a
- *                caller time the two kernels separately)
+ *   main_events  NULL, or an array of two hipEvent_t (timing enabled) that
+ *                receive the start and the end of the main attention
+ *                kernel's own execution (hipExtLaunchKernel), so a caller can
+ *                time that kernel apart from the split merge
  *
  * Tensors other than lse and the workspace must be 16-byte aligned
  * (PA_ERR_INVALID otherwise); the kernels move rows in 16-byte pieces.
@@ -218,7 +229,7 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
 int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool,
                      const void* v_pool, void* out, float* lse, int32_t head_dim,
                      int32_t v_head_dim, float scale, void* workspace, size_t workspace_bytes,
-                     void* event_after_main, void* stream);
+                     void* const* main_events, void* stream);
 
 /*
  * Absorbed multi-head latent attention forward (ruDNN `DevicePlan::mla`): one
@@ -243,7 +254,7 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
 int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void* q_rope,
                const void* latent, const void* kpos, void* out, float* lse, int32_t rank,
                int32_t rope_dim, float scale, void* workspace, size_t workspace_bytes,
-               void* event_after_main, void* stream);
+               void* const* main_events, void* stream);
 
 /* Static name of a status code. */
 const char* pa_status_string(int status);

@@ -268,15 +268,25 @@ def _ws(workspace):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
-def _event(ev):
-    if ev is None:
-        return None
+def _event(ev) -> int:
     return ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
 
 
+def _events(main_events):
+    """(start, end) torch events or raw hipEvent_t handles -> a C array of two
+    handles (kept alive by the caller's reference), or None."""
+    if main_events is None:
+        return None
+    start, end = main_events
+    return (ctypes.c_void_p * 2)(_event(start), _event(end))
+
+
 def pa_attention_fwd(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: float, workspace=None,
-                     event_after_main=None, stream=None) -> None:
-    """Paged GQA forward into `out` (see pa_attention_fwd in paged_attn.h)."""
+                     main_events=None, stream=None) -> None:
+    """Paged GQA forward into `out` (see pa_attention_fwd in paged_attn.h).
+    main_events: None or (start, end) timing events (torch.cuda.Event that
+    have been recorded once, or hipEvent_t handles) that receive the main
+    kernel's own start and end."""
     d = plan.desc
     dt = _dtype_code(q)
     for name, t in (("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
@@ -299,8 +309,9 @@ def pa_attention_fwd(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: flo
             raise ValueError("lse must be float32 [Q, Hq]")
         pl = _dev(lse, "lse", 2)
     wp, wn = _ws(workspace)
+    ev = _events(main_events)
     _check(load_library().pa_attention_fwd(plan.handle, dt, pq, pk, pv, po, pl, D, Dv, float(scale), wp, wn,
-                                           _event(event_after_main), _stream_handle(stream)), "pa_attention_fwd")
+                                           ev, _stream_handle(stream)), "pa_attention_fwd")
 
 
 def pa_plan_bwd_workspace_bytes(plan: Plan, dtype, head_dim: int, v_head_dim: int) -> int:
@@ -341,8 +352,9 @@ def pa_attention_bwd(plan: Plan, q, k_pool, v_pool, out, lse, dout, dq, dk_pool,
 
 
 def pa_mla_fwd(plan: Plan, q_abs, q_rope, latent, kpos, out, lse=None, *, scale: float, workspace=None,
-               event_after_main=None, stream=None) -> None:
-    """Absorbed-MLA forward into `out` (see pa_mla_fwd in paged_attn.h)."""
+               main_events=None, stream=None) -> None:
+    """Absorbed-MLA forward into `out` (see pa_mla_fwd in paged_attn.h);
+    main_events as for pa_attention_fwd."""
     d = plan.desc
     dt = _dtype_code(q_abs)
     for name, t in (("q_rope", q_rope), ("latent", latent), ("kpos", kpos), ("out", out)):
@@ -366,8 +378,9 @@ def pa_mla_fwd(plan: Plan, q_abs, q_rope, latent, kpos, out, lse=None, *, scale:
             raise ValueError("lse must be float32 [Q, H]")
         plse = _dev(lse, "lse", 2)
     wp, wn = _ws(workspace)
+    ev = _events(main_events)
     _check(load_library().pa_mla_fwd(plan.handle, dt, pa_, pr, pl_, pk, po, plse, R, P, float(scale), wp, wn,
-                                     _event(event_after_main), _stream_handle(stream)), "pa_mla_fwd")
+                                     ev, _stream_handle(stream)), "pa_mla_fwd")
 
 
 def pa_append_kv(plan: Plan, k_new, v_new, k_pool, v_pool, *, stream=None) -> None:

@@ -69,8 +69,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct pa_plan {
   int device = -1;
+  // every device-side use of the plan (upload, forward, append, backward and
+  // the final free) is ordered on this stream
   hipStream_t created_on = nullptr;
-  hipEvent_t ready = nullptr;
+  hipEvent_t uploaded = nullptr;  // the upload copy (reads the host blob) has finished
   // schedule, host copy
   int32_t S = 0, Q = 0, W = 0, ps = 1, page_shift = 0, num_pages = 0;
   int32_t hq = 0, hkv = 0, causal = 0, window = 0, max_splits = 1, mla = 0, split_tokens = 0;
@@ -544,12 +546,23 @@ int check_aligned(const std::vector<Extent>& ts) {
   return PA_OK;
 }
 
-int check_device(const pa_plan* p) {
+// A plan (and the workspace used with it) lives on the device and the
+// stream it was made on (ruDNN: metadata and split workspaces belong to one
+// device queue).
+int check_device(const pa_plan* p, void* stream) {
   if (!p->dev) return fail(PA_ERR_DEVICE, "plan was built on the host only (pa_plan_create_host)");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
-  if (dev != p->device) return fail(PA_ERR_DEVICE, "metadata belongs to device %d, current device is %d", p->device, dev);
+  if (dev != p->device) return fail(PA_ERR_DEVICE, "plan was made on device %d; the current device is %d", p->device, dev);
+  if (reinterpret_cast<hipStream_t>(stream) != p->created_on)
+    return fail(PA_ERR_DEVICE, "plan was made on stream %p and is used on that stream only (call on %p)",
+                (void*)p->created_on, stream);
   return PA_OK;
+}
+
+pa::MainEvents main_events_of(void* const* ev) {
+  if (!ev) return {};
+  return {reinterpret_cast<hipEvent_t>(ev[0]), reinterpret_cast<hipEvent_t>(ev[1])};
 }
 
 int hip_fail(hipError_t e, const char* what) {
@@ -561,7 +574,7 @@ struct FwdCall {
   const pa_plan* plan;
   int dtype, d, dv;
   pa::KernelArgs args;
-  void* event_after_main;
+  pa::MainEvents events;
   hipStream_t stream;
 };
 
@@ -658,19 +671,22 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   if (!p->bwd_items.empty())
     memcpy(p->blob.data() + off_bwd, p->bwd_items.data(), p->bwd_items.size() * sizeof(pa::BwdItem));
 
-  e = hipMalloc(reinterpret_cast<void**>(&p->dev), total);
-  if (e != hipSuccess) {
-    delete p;
-    return hip_fail(e, "hipMalloc(plan)");
-  }
+  // stream-ordered allocation, upload and (in pa_plan_destroy) free: no call
+  // of the plan's life waits for the device
   p->created_on = reinterpret_cast<hipStream_t>(stream);
+  e = hipMallocAsync(reinterpret_cast<void**>(&p->dev), total, p->created_on);
+  if (e != hipSuccess) {
+    p->dev = nullptr;
+    delete p;
+    return hip_fail(e, "hipMallocAsync(plan)");
+  }
   e = hipMemcpyAsync(p->dev, p->blob.data(), total, hipMemcpyHostToDevice, p->created_on);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ready, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventRecord(p->ready, p->created_on);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(p->uploaded, p->created_on);
   if (e != hipSuccess) {
     (void)hipStreamSynchronize(p->created_on);
-    (void)hipFree(p->dev);
-    if (p->ready) (void)hipEventDestroy(p->ready);
+    (void)hipFreeAsync(p->dev, p->created_on);
+    if (p->uploaded) (void)hipEventDestroy(p->uploaded);
     delete p;
     return hip_fail(e, "plan upload");
   }
@@ -720,16 +736,19 @@ int pa_plan_destroy(pa_plan* plan) {
     delete plan;
     return ok();
   }
+  // Every kernel that reads the plan was enqueued on its stream, so a free
+  // ordered after them on that stream needs no wait for them.  The host
+  // blob is the source of the upload copy, enqueued when the plan was made:
+  // wait for that copy alone before the blob goes.
   int prev = -1;
   (void)hipGetDevice(&prev);
   if (prev != plan->device) (void)hipSetDevice(plan->device);
-  if (plan->ready) (void)hipEventSynchronize(plan->ready);
-  // kernels that read the plan may still be queued on other streams
-  (void)hipDeviceSynchronize();
-  if (plan->dev) (void)hipFree(plan->dev);
-  if (plan->ready) (void)hipEventDestroy(plan->ready);
+  if (plan->uploaded) (void)hipEventSynchronize(plan->uploaded);
+  hipError_t e = hipFreeAsync(plan->dev, plan->created_on);
+  if (plan->uploaded) (void)hipEventDestroy(plan->uploaded);
   if (prev >= 0 && prev != plan->device) (void)hipSetDevice(prev);
   delete plan;
+  if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(plan)");
   return ok();
 }
 
@@ -759,21 +778,13 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
 static int launch_common(FwdCall& c, bool is_mla) {
   const pa_plan* p = c.plan;
   if (p->Q == 0 || p->items.empty()) return ok();
-  if (c.stream != p->created_on) {
-    hipError_t e = hipStreamWaitEvent(c.stream, p->ready, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(plan)");
-  }
   hipError_t e;
   if (is_mla) {
-    e = pa::launch_mla_main(c.dtype, p->n_prefill > 0, c.args, c.stream);
+    e = pa::launch_mla_main(c.dtype, p->n_prefill > 0, c.args, c.events, c.stream);
   } else {
-    e = pa::launch_gqa_main(c.dtype, c.d, c.dv, p->group(), p->n_prefill > 0, c.args, c.stream);
+    e = pa::launch_gqa_main(c.dtype, c.d, c.dv, p->group(), p->n_prefill > 0, c.args, c.events, c.stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (c.event_after_main) {
-    e = hipEventRecord(reinterpret_cast<hipEvent_t>(c.event_after_main), c.stream);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(event_after_main)");
-  }
   if (!p->merges.empty()) {
     e = is_mla ? pa::launch_mla_merge(c.dtype, c.args, p->d_merges, (int)p->merges.size(), c.stream)
                : pa::launch_gqa_merge(c.dtype, c.d, c.dv, p->group(), c.args, p->d_merges, (int)p->merges.size(),
@@ -802,7 +813,7 @@ static int check_workspace(const pa_plan* p, int dv, void* workspace, size_t wor
 
 int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool, const void* v_pool,
                      void* out, float* lse, int32_t head_dim, int32_t v_head_dim, float scale, void* workspace,
-                     size_t workspace_bytes, void* event_after_main, void* stream) {
+                     size_t workspace_bytes, void* const* main_events, void* stream) {
   if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
   if (plan->mla) return fail(PA_ERR_INVALID, "plan was made for MLA (use pa_mla_fwd)");
   if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
@@ -811,7 +822,7 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
     return fail(PA_ERR_SHAPE, "head sizes D=%d Dv=%d outside [1, 1024]", head_dim, v_head_dim);
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
-  int rc = check_device(plan);
+  int rc = check_device(plan, stream);
   if (rc != PA_OK) return rc;
   float *ws_o, *ws_ml;
   size_t need;
@@ -836,7 +847,7 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   if (rc == PA_OK) rc = check_aligned({outs[0], ins[0], ins[1], ins[2]});
   if (rc != PA_OK) return rc;
 
-  FwdCall c{plan, dtype, head_dim, v_head_dim, {}, event_after_main, reinterpret_cast<hipStream_t>(stream)};
+  FwdCall c{plan, dtype, head_dim, v_head_dim, {}, main_events_of(main_events), reinterpret_cast<hipStream_t>(stream)};
   pa::KernelArgs& a = c.args;
   a.q = q;
   a.k = k_pool;
@@ -866,7 +877,7 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
 
 int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void* q_rope, const void* latent,
                const void* kpos, void* out, float* lse, int32_t rank, int32_t rope_dim, float scale,
-               void* workspace, size_t workspace_bytes, void* event_after_main, void* stream) {
+               void* workspace, size_t workspace_bytes, void* const* main_events, void* stream) {
   if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
   if (!plan->mla) return fail(PA_ERR_INVALID, "plan was made for GQA (use pa_attention_fwd)");
   if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
@@ -875,9 +886,9 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
     return fail(PA_ERR_INVALID, "q_abs, q_rope and out are required when there are queries");
   if (rank <= 0 || rank > 1024) return fail(PA_ERR_SHAPE, "latent rank %d outside [1, 1024]", rank);
   if (rope_dim <= 0 || rope_dim > 256)
-    return fail(PA_ERR_SHAPE, "incompatible MLA positional dimensions: rope_dim %d outside [1, 256]", rope_dim);
+    return fail(PA_ERR_SHAPE, "rotary width rope_dim %d outside [1, 256]", rope_dim);
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
-  int rc = check_device(plan);
+  int rc = check_device(plan, stream);
   if (rc != PA_OK) return rc;
   float *ws_o, *ws_ml;
   size_t need;
@@ -899,7 +910,7 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   if (rc == PA_OK) rc = check_aligned({outs[0], ins[0], ins[1], ins[2], ins[3]});
   if (rc != PA_OK) return rc;
 
-  FwdCall c{plan, dtype, rank, rank, {}, event_after_main, reinterpret_cast<hipStream_t>(stream)};
+  FwdCall c{plan, dtype, rank, rank, {}, main_events_of(main_events), reinterpret_cast<hipStream_t>(stream)};
   pa::KernelArgs& a = c.args;
   a.q = q_abs;
   a.k = latent;
@@ -952,14 +963,10 @@ int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const vo
   if (rc == PA_OK) rc = check_aligned(outs);
   if (rc == PA_OK) rc = check_aligned(ins);
   if (rc != PA_OK) return rc;
-  rc = check_device(plan);
+  rc = check_device(plan, stream);
   if (rc != PA_OK) return rc;
   if (plan->Q == 0) return ok();
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (st != plan->created_on) {
-    hipError_t e = hipStreamWaitEvent(st, plan->ready, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(plan)");
-  }
   hipError_t e = pa::launch_append(k_new, v_new, k_pool, v_pool, plan->d_slot_of, plan->Q, heads,
                                    (int)(head_dim * es), (int)(v_head_dim * es), std::max(plan->n_cu, 1), st);
   if (e != hipSuccess) return hip_fail(e, "append launch");
@@ -1029,13 +1036,9 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   int rc = check_disjoint(outs, ins);
   if (rc == PA_OK) rc = check_aligned({outs[0], outs[1], outs[2], ins[0], ins[1], ins[2], ins[3], ins[5]});
   if (rc != PA_OK) return rc;
-  rc = check_device(plan);
+  rc = check_device(plan, stream);
   if (rc != PA_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (st != plan->created_on) {
-    hipError_t e = hipStreamWaitEvent(st, plan->ready, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(plan)");
-  }
   pa::KernelArgs a{};
   a.q = q;
   a.k = k_pool;
@@ -1064,16 +1067,16 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
 
 const char* pa_status_string(int status) {
   switch (status) {
-    case PA_OK: return "ok";
-    case PA_ERR_INVALID: return "invalid argument";
-    case PA_ERR_SHAPE: return "incompatible paged head/cache/output shape or scale";
-    case PA_ERR_PLAN: return "malformed schedule metadata";
-    case PA_ERR_UNSUPPORTED: return "no kernel specialisation for this request";
-    case PA_ERR_WORKSPACE: return "split workspace shape mismatch";
-    case PA_ERR_OVERLAP: return "output overlaps an input";
-    case PA_ERR_RANGE: return "paged dimension exceeds 32-bit indexing";
-    case PA_ERR_HIP: return "HIP runtime failure";
-    case PA_ERR_DEVICE: return "metadata belongs to another device";
+    case PA_OK: return "success";
+    case PA_ERR_INVALID: return "bad argument: null pointer, unknown data type or flag out of range";
+    case PA_ERR_SHAPE: return "tensor sizes, head counts or softmax scale do not fit together";
+    case PA_ERR_PLAN: return "schedule is inconsistent (offsets, positions or block table)";
+    case PA_ERR_UNSUPPORTED: return "valid request that no kernel of this build handles";
+    case PA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case PA_ERR_OVERLAP: return "an output shares memory with an input or another output";
+    case PA_ERR_RANGE: return "a size does not fit 32-bit element indexing";
+    case PA_ERR_HIP: return "the HIP runtime reported a failure";
+    case PA_ERR_DEVICE: return "plan used away from the device or stream it was made for";
     default: return "unknown status";
   }
 }

@@ -1,5 +1,7 @@
 // Kernel entry points and their launchers.  Host code reaches the kernels
 // only through the launch_* functions declared in pa_launch.h.
+#include <hip/hip_ext.h>
+
 #include "pa_decode.h"
 #include "pa_launch.h"
 #include "pa_mla.h"
@@ -121,31 +123,36 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelArgs a, cons
 
 namespace {
 
-using LaunchFn = hipError_t (*)(const KernelArgs&, int, const MergeItem*, int, hipStream_t);
-
-template <typename T, int D, int DV, int G>
-hipError_t launch_decode_t(const KernelArgs& a, int n_wg, const MergeItem* merges, int n_merges,
-                           hipStream_t stream) {
-  if (n_wg > 0) {
-    hipLaunchKernelGGL((decode_kernel<T, D, DV, G>), dim3(n_wg), dim3(DecodeShape<G>::kWaves * kWave), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+// One main-kernel launch; with timing events, through hipExtLaunchKernel so
+// that the events carry the kernel's own start and end.
+template <typename K>
+hipError_t launch_main(K kernel, int n_wg, int threads, const KernelArgs& a, const MainEvents& ev,
+                       hipStream_t stream) {
+  if (n_wg <= 0) return hipSuccess;
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, dim3(n_wg), dim3(threads), 0, stream, ev.start, ev.stop, 0, a);
+  else
+    hipLaunchKernelGGL(kernel, dim3(n_wg), dim3(threads), 0, stream, a);
+  return hipGetLastError();
 }
 
+using LaunchFn = hipError_t (*)(const KernelArgs&, int, const MergeItem*, int, const MainEvents&, hipStream_t);
 
 template <typename T, int D, int DV, int G>
-hipError_t launch_mixed_t(const KernelArgs& a, int n_wg, const MergeItem*, int, hipStream_t stream) {
-  if (n_wg > 0) {
-    hipLaunchKernelGGL((mixed_kernel<T, D, DV, G>), dim3(n_wg), dim3(kPrefillWaves * kWave), 0, stream, a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+hipError_t launch_decode_t(const KernelArgs& a, int n_wg, const MergeItem*, int, const MainEvents& ev,
+                           hipStream_t stream) {
+  return launch_main(decode_kernel<T, D, DV, G>, n_wg, DecodeShape<G>::kWaves * kWave, a, ev, stream);
+}
+
+template <typename T, int D, int DV, int G>
+hipError_t launch_mixed_t(const KernelArgs& a, int n_wg, const MergeItem*, int, const MainEvents& ev,
+                          hipStream_t stream) {
+  return launch_main(mixed_kernel<T, D, DV, G>, n_wg, kPrefillWaves * kWave, a, ev, stream);
 }
 
 template <typename T, int DV, int G>
-hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, hipStream_t stream) {
+hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, const MainEvents&,
+                          hipStream_t stream) {
   if (n_merges > 0) {
     const int chunks = (G * DV / 4 + kMergeThreads - 1) / kMergeThreads;
     hipLaunchKernelGGL((merge_kernel<T, DV, G>), dim3(n_merges, chunks), dim3(kMergeThreads), 0, stream, a, merges);
@@ -206,15 +213,15 @@ bool gqa_supported(int dtype, int d, int dv, int g) { return pick<DecodeSel>(dty
 bool prefill_supported(int dtype, int d, int dv, int g) { return pick<MixedSel>(dtype, d, dv, g) != nullptr; }
 
 hipError_t launch_gqa_main(int dtype, int d, int dv, int g, bool has_prefill, const KernelArgs& a,
-                           hipStream_t stream) {
+                           const MainEvents& ev, hipStream_t stream) {
   LaunchFn f = has_prefill ? pick<MixedSel>(dtype, d, dv, g) : pick<DecodeSel>(dtype, d, dv, g);
-  return f ? f(a, a.n_wg, nullptr, 0, stream) : hipErrorInvalidValue;
+  return f ? f(a, a.n_wg, nullptr, 0, ev, stream) : hipErrorInvalidValue;
 }
 
 hipError_t launch_gqa_merge(int dtype, int d, int dv, int g, const KernelArgs& a, const MergeItem* merges,
                             int n_merges, hipStream_t stream) {
   LaunchFn f = pick<MergeSel>(dtype, d, dv, g);
-  return f ? f(a, 0, merges, n_merges, stream) : hipErrorInvalidValue;
+  return f ? f(a, 0, merges, n_merges, MainEvents{}, stream) : hipErrorInvalidValue;
 }
 
 int decode_wgs_per_cu(int g) {
@@ -246,27 +253,20 @@ bool mla_supported(int dtype, int h, int r, int p) {
   return (dtype == 1 || dtype == 2) && h == kMlaHeads && r == kMlaRank && p == kMlaRope;
 }
 
-hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, hipStream_t stream) {
-  if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
-  if (a.n_wg > 0) {
-    const dim3 grid(a.n_wg), block(kMlaWaves * kWave);
-    if (dtype == 1 && has_prefill)
-      hipLaunchKernelGGL((mla_kernel<uint16_t, true>), grid, block, 0, stream, a);
-    else if (dtype == 1)
-      hipLaunchKernelGGL((mla_kernel<uint16_t, false>), grid, block, 0, stream, a);
-    else if (has_prefill)
-      hipLaunchKernelGGL((mla_kernel<_Float16, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mla_kernel<_Float16, false>), grid, block, 0, stream, a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, const MainEvents& ev,
+                           hipStream_t stream) {
+  constexpr int threads = kMlaWaves * kWave;
+  if (dtype == 1 && has_prefill) return launch_main(mla_kernel<uint16_t, true>, a.n_wg, threads, a, ev, stream);
+  if (dtype == 1) return launch_main(mla_kernel<uint16_t, false>, a.n_wg, threads, a, ev, stream);
+  if (dtype == 2 && has_prefill) return launch_main(mla_kernel<_Float16, true>, a.n_wg, threads, a, ev, stream);
+  if (dtype == 2) return launch_main(mla_kernel<_Float16, false>, a.n_wg, threads, a, ev, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream) {
-  if (dtype == 1) return launch_merge_t<uint16_t, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, stream);
-  if (dtype == 2) return launch_merge_t<_Float16, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, stream);
+  if (dtype == 1) return launch_merge_t<uint16_t, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, MainEvents{}, stream);
+  if (dtype == 2) return launch_merge_t<_Float16, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, MainEvents{}, stream);
   return hipErrorInvalidValue;
 }
 

@@ -8,6 +8,13 @@
 
 namespace pa {
 
+// Optional timing events of a main attention launch: when set, the launch
+// records the start and end of the kernel's own execution into them
+// (hipExtLaunchKernel).
+struct MainEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // dtype: 0 = f32, 1 = bf16, 2 = f16.  d, dv: K and V head sizes.  g: query
 // heads per KV head.
 bool gqa_supported(int dtype, int d, int dv, int g);
@@ -15,7 +22,7 @@ bool prefill_supported(int dtype, int d, int dv, int g);
 // Main GQA launch over the a.n_items entries of a.items: decode-only, or one
 // mixed launch when the list holds prefill tiles.
 hipError_t launch_gqa_main(int dtype, int d, int dv, int g, bool has_prefill, const KernelArgs& a,
-                           hipStream_t stream);
+                           const MainEvents& ev, hipStream_t stream);
 // Log-sum-exp merge of split rows into the output.
 hipError_t launch_gqa_merge(int dtype, int d, int dv, int g, const KernelArgs& a, const MergeItem* merges,
                             int n_merges, hipStream_t stream);
@@ -31,7 +38,8 @@ int mla_wgs_per_cu();
 // Absorbed MLA: h query heads, latent rank r, position width p.
 bool mla_supported(int dtype, int h, int r, int p);
 // has_prefill: the item list holds chunked-prefill items.
-hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, hipStream_t stream);
+hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, const MainEvents& ev,
+                           hipStream_t stream);
 hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream);
 

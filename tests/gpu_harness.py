@@ -57,9 +57,9 @@ class GqaRun:
         self.workspace = torch.zeros(max(nbytes, 1) // 4 + 64, dtype=torch.float32, device="cuda") if nbytes else None
         self.info = pa.pa_plan_get_info(self.plan)
 
-    def __call__(self, event_after_main=None):
+    def __call__(self, main_events=None):
         pa.pa_attention_fwd(self.plan, self.q, self.k, self.v, self.out, self.lse, scale=self.b.scale,
-                            workspace=self.workspace, event_after_main=event_after_main)
+                            workspace=self.workspace, main_events=main_events)
         return self.out
 
     def result(self):
@@ -85,9 +85,9 @@ class MlaRun:
         self.workspace = torch.zeros(max(nbytes, 1) // 4 + 64, dtype=torch.float32, device="cuda") if nbytes else None
         self.info = pa.pa_plan_get_info(self.plan)
 
-    def __call__(self, event_after_main=None):
+    def __call__(self, main_events=None):
         pa.pa_mla_fwd(self.plan, self.q_abs, self.q_rope, self.latent, self.kpos, self.out, self.lse,
-                      scale=self.m.scale, workspace=self.workspace, event_after_main=event_after_main)
+                      scale=self.m.scale, workspace=self.workspace, main_events=main_events)
         return self.out
 
     def result(self):

@@ -159,3 +159,54 @@ def test_128k_key_row(hq, hkv, max_splits):
                      max_splits=max_splits)
     run = _parity(b)
     assert (run.info["split_rows"] > 0) == (max_splits > 1)
+
+
+def test_plan_is_bound_to_its_stream_and_freed_in_stream_order():
+    """A plan works on the stream it was made on and is refused on another
+    (PA_ERR_DEVICE, before any launch); destroying it right after a call on
+    its stream leaves that call's result intact (the free is ordered after
+    the kernels that read the plan)."""
+    import torch
+    import paged_kv_attention_gqa_amd as pa
+    from tests.gpu_harness import make_plan
+    b = random_batch(1900, dtype="bf16", hq=32, hkv=8, d=128, page_size=16, q_counts=(1, 1, 1), max_len=3000)
+    run = GqaRun(b, split_tokens=256)
+    torch.cuda.synchronize()  # inputs were copied on the default stream
+    side = torch.cuda.Stream()
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_attention_fwd(run.plan, run.q, run.k, run.v, run.out, run.lse, scale=b.scale,
+                            workspace=run.workspace, stream=side)
+    assert e.value.name == "PA_ERR_DEVICE"
+    # a plan made on the side stream runs there; it is destroyed before the
+    # stream has finished the call
+    with torch.cuda.stream(side):
+        plan = make_plan(b, split_tokens=256, stream=side)
+        pa.pa_attention_fwd(plan, run.q, run.k, run.v, run.out, run.lse, scale=b.scale, workspace=run.workspace,
+                            stream=side)
+        pa.pa_plan_destroy(plan)
+    side.synchronize()
+    out, lse = to_f64(run.out), run.lse.cpu().numpy().astype(np.float64)
+    ref_o, ref_l = oracle.attention(b)
+    assert_close(out, ref_o, "bf16")
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-3)
+
+
+def test_main_kernel_timing_events():
+    """main_events receive the main kernel's own start and end: the interval
+    is positive and no longer than the whole call measured around it."""
+    import torch
+    b = config_bf16_decode_batch()
+    run = GqaRun(b)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    outer0, outer1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for ev in (start, end):
+        ev.record()
+    torch.cuda.synchronize()
+    outer0.record()
+    run(main_events=(start, end))
+    outer1.record()
+    torch.cuda.synchronize()
+    k_ms, call_ms = start.elapsed_time(end), outer0.elapsed_time(outer1)
+    assert 0 < k_ms <= call_ms, (k_ms, call_ms)
+    out, _ = run.result()
+    assert_close(out, oracle.attention(b)[0], "bf16")

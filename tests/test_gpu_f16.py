@@ -79,21 +79,18 @@ def test_f16_prefill_and_mixed_parity(i):
     assert run.info["prefill_items"] > 0
 
 
-def test_f16_chunked_prefill_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_f16_chunked_prefill_full_size_every_row():
     """The chunked-prefill shape (8 sequences, 512-query chunks after 0..4096
-    cached keys, Hq 32, Hkv 8, D 128) in f16; sampled rows plus every head of
-    each chunk's first and last query."""
+    cached keys, Hq 32, Hkv 8, D 128) in f16: every output element and every
+    lse against the oracle."""
     rng = np.random.default_rng(5300)
     hist = rng.integers(0, 4096 + 1, size=8)
     b = random_batch(5301, dtype="f16", hq=32, hkv=8, d=128, page_size=16, q_counts=(512,) * 8, histories=hist)
     run = GqaRun(b)
     run()
-    rows = set(rng.integers(0, b.num_queries * b.hq, size=2000).tolist())
-    for s in range(b.num_seqs):
-        for i in (int(b.cu_q[s]), int(b.cu_q[s + 1]) - 1):
-            rows.update(range(i * b.hq, (i + 1) * b.hq))
-    rows = np.array(sorted(rows), dtype=np.int64)
-    _check(run, *oracle.attention(b, rows=rows), rows=rows)
+    _check(run, *oracle.attention(b))
+    assert run.info["prefill_items"] > 0
 
 
 @pytest.mark.parametrize("q_counts,page_size", [((1, 1, 2, 1), 16), ((150, 1, 40), 16), ((3, 90), 64)])
