@@ -231,6 +231,32 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                      int32_t v_head_dim, float scale, void* workspace, size_t workspace_bytes,
                      void* const* main_events, void* stream);
 
+/* Bytes of the fixed device array that pa_attention_fwd_noalloc keeps the
+ * split partials in (per GPU, held until the process ends). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * pa_attention_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It runs the same kernels as
+ * pa_attention_fwd; the split partials live in one file-scope device array
+ * of PA_NOALLOC_SCRATCH_BYTES bytes per GPU instead of a caller workspace.
+ * The call allocates nothing (no hipMalloc, no host heap in its checks).
+ *
+ * Every call on one GPU shares that array, which keeps the last call's
+ * contents (nothing in it needs clearing: each partial the merge reads is
+ * written earlier in the same call).  Calls that overlap in time on one GPU
+ * -- on different streams, or from plans whose calls are not ordered --
+ * race on it; order them.
+ *
+ * Arguments, layouts and errors as for pa_attention_fwd (no main_events),
+ * plus PA_ERR_WORKSPACE when pa_plan_workspace_bytes(plan, v_head_dim)
+ * exceeds PA_NOALLOC_SCRATCH_BYTES (checked before anything is launched).
+ */
+int pa_attention_fwd_noalloc(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool,
+                             const void* v_pool, void* out, float* lse, int32_t head_dim,
+                             int32_t v_head_dim, float scale, void* stream);
+
 /*
  * Absorbed multi-head latent attention forward (ruDNN `DevicePlan::mla`): one
  * shared latent head serves as both key and value; a rotated position cache

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_INVALID", -2: "PA_ERR_SHAPE", -3: "PA_ER
                 -9: "PA_ERR_DEVICE"}
 EXPORTED = ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
             "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv", "pa_status_string",
-            "pa_last_error", "pa_plan_bwd_workspace_bytes", "pa_attention_bwd")
+            "pa_last_error", "pa_plan_bwd_workspace_bytes", "pa_attention_bwd", "pa_attention_fwd_noalloc")
 
 
 class PaError(RuntimeError):
@@ -72,6 +72,7 @@ def load_library():
     lib.pa_plan_get_info.argtypes = [P, ctypes.POINTER(_PlanInfo)]
     lib.pa_plan_workspace_bytes.argtypes = [P, I, ctypes.POINTER(S)]
     lib.pa_attention_fwd.argtypes = [P, I, P, P, P, P, P, I, I, F, P, S, P, P]
+    lib.pa_attention_fwd_noalloc.argtypes = [P, I, P, P, P, P, P, I, I, F, P]
     lib.pa_mla_fwd.argtypes = [P, I, P, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_append_kv.argtypes = [P, I, P, P, P, P, I, I, P]
     lib.pa_plan_bwd_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S)]
@@ -82,7 +83,7 @@ def load_library():
     lib.pa_last_error.restype = ctypes.c_char_p
     for n in ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
               "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv",
-              "pa_plan_bwd_workspace_bytes", "pa_attention_bwd"):
+              "pa_plan_bwd_workspace_bytes", "pa_attention_bwd", "pa_attention_fwd_noalloc"):
         getattr(lib, n).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -281,12 +282,8 @@ def _events(main_events):
     return (ctypes.c_void_p * 2)(_event(start), _event(end))
 
 
-def pa_attention_fwd(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: float, workspace=None,
-                     main_events=None, stream=None) -> None:
-    """Paged GQA forward into `out` (see pa_attention_fwd in paged_attn.h).
-    main_events: None or (start, end) timing events (torch.cuda.Event that
-    have been recorded once, or hipEvent_t handles) that receive the main
-    kernel's own start and end."""
+def _fwd_args(plan: Plan, q, k_pool, v_pool, out, lse):
+    """Checked device pointers and sizes of a GQA forward call."""
     d = plan.desc
     dt = _dtype_code(q)
     for name, t in (("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
@@ -308,10 +305,29 @@ def pa_attention_fwd(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: flo
         if lse.dtype != torch.float32 or tuple(lse.shape) != (Q, Hq):
             raise ValueError("lse must be float32 [Q, Hq]")
         pl = _dev(lse, "lse", 2)
+    return dt, pq, pk, pv, po, pl, D, Dv
+
+
+def pa_attention_fwd(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: float, workspace=None,
+                     main_events=None, stream=None) -> None:
+    """Paged GQA forward into `out` (see pa_attention_fwd in paged_attn.h).
+    main_events: None or (start, end) timing events (torch.cuda.Event that
+    have been recorded once, or hipEvent_t handles) that receive the main
+    kernel's own start and end."""
+    dt, pq, pk, pv, po, pl, D, Dv = _fwd_args(plan, q, k_pool, v_pool, out, lse)
     wp, wn = _ws(workspace)
     ev = _events(main_events)
     _check(load_library().pa_attention_fwd(plan.handle, dt, pq, pk, pv, po, pl, D, Dv, float(scale), wp, wn,
                                            ev, _stream_handle(stream)), "pa_attention_fwd")
+
+
+def pa_attention_fwd_noalloc(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: float, stream=None) -> None:
+    """Paged GQA forward that allocates nothing: split partials in the
+    library's fixed per-GPU array (see pa_attention_fwd_noalloc in
+    paged_attn.h)."""
+    dt, pq, pk, pv, po, pl, D, Dv = _fwd_args(plan, q, k_pool, v_pool, out, lse)
+    _check(load_library().pa_attention_fwd_noalloc(plan.handle, dt, pq, pk, pv, po, pl, D, Dv, float(scale),
+                                                   _stream_handle(stream)), "pa_attention_fwd_noalloc")
 
 
 def pa_plan_bwd_workspace_bytes(plan: Plan, dtype, head_dim: int, v_head_dim: int) -> int:

@@ -10,11 +10,13 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <string>
 #include <vector>
 
 #include "paged_attn.h"
+#include "pa_host.h"
 #include "pa_launch.h"
 #include "pa_prefill.h"
 
@@ -66,6 +68,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
+
+int pa::host_fail(int status, const char* msg) { return fail(status, "%s", msg); }
 
 struct pa_plan {
   int device = -1;
@@ -528,18 +532,19 @@ bool overlaps(const Extent& a, const Extent& b) {
   return x < y + b.n && y < x + a.n;
 }
 
-int check_disjoint(const std::vector<Extent>& outs, const std::vector<Extent>& ins) {
-  for (size_t i = 0; i < outs.size(); ++i) {
+// (initializer lists: argument checks make no heap allocation)
+int check_disjoint(std::initializer_list<Extent> outs, std::initializer_list<Extent> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
     for (const Extent& in : ins)
-      if (overlaps(outs[i], in)) return fail(PA_ERR_OVERLAP, "%s overlaps %s", outs[i].name, in.name);
-    for (size_t j = i + 1; j < outs.size(); ++j)
-      if (overlaps(outs[i], outs[j])) return fail(PA_ERR_OVERLAP, "%s overlaps %s", outs[i].name, outs[j].name);
+      if (overlaps(*o, in)) return fail(PA_ERR_OVERLAP, "%s overlaps %s", o->name, in.name);
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlaps(*o, *o2)) return fail(PA_ERR_OVERLAP, "%s overlaps %s", o->name, o2->name);
   }
   return PA_OK;
 }
 
 // The kernels move tensor rows in 16-byte pieces.
-int check_aligned(const std::vector<Extent>& ts) {
+int check_aligned(std::initializer_list<Extent> ts) {
   for (const Extent& t : ts)
     if (t.p && t.n && reinterpret_cast<uintptr_t>(t.p) % 16)
       return fail(PA_ERR_INVALID, "%s must be 16-byte aligned", t.name);
@@ -837,14 +842,14 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                 v_head_dim, G);
   const size_t es = dtype == PA_F32 ? 4 : 2;
   const size_t slots = (size_t)plan->num_pages * plan->ps * plan->hkv;
-  std::vector<Extent> outs = {{out, (size_t)plan->Q * plan->hq * v_head_dim * es, "out"},
-                              {lse, lse ? (size_t)plan->Q * plan->hq * 4 : 0, "lse"},
-                              {workspace, need, "workspace"}};
-  std::vector<Extent> ins = {{q, (size_t)plan->Q * plan->hq * head_dim * es, "q"},
-                             {k_pool, slots * head_dim * es, "k_pool"},
-                             {v_pool, slots * v_head_dim * es, "v_pool"}};
-  rc = check_disjoint(outs, ins);
-  if (rc == PA_OK) rc = check_aligned({outs[0], ins[0], ins[1], ins[2]});
+  const Extent e_out{out, (size_t)plan->Q * plan->hq * v_head_dim * es, "out"};
+  const Extent e_lse{lse, lse ? (size_t)plan->Q * plan->hq * 4 : 0, "lse"};
+  const Extent e_ws{workspace, need, "workspace"};
+  const Extent e_q{q, (size_t)plan->Q * plan->hq * head_dim * es, "q"};
+  const Extent e_k{k_pool, slots * head_dim * es, "k_pool"};
+  const Extent e_v{v_pool, slots * v_head_dim * es, "v_pool"};
+  rc = check_disjoint({e_out, e_lse, e_ws}, {e_q, e_k, e_v});
+  if (rc == PA_OK) rc = check_aligned({e_out, e_q, e_k, e_v});
   if (rc != PA_OK) return rc;
 
   FwdCall c{plan, dtype, head_dim, v_head_dim, {}, main_events_of(main_events), reinterpret_cast<hipStream_t>(stream)};
@@ -899,15 +904,15 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
                 rope_dim);
   const size_t es = dtype == PA_F32 ? 4 : 2;
   const size_t slots = (size_t)plan->num_pages * plan->ps;
-  std::vector<Extent> outs = {{out, (size_t)plan->Q * plan->hq * rank * es, "out"},
-                              {lse, lse ? (size_t)plan->Q * plan->hq * 4 : 0, "lse"},
-                              {workspace, need, "workspace"}};
-  std::vector<Extent> ins = {{q_abs, (size_t)plan->Q * plan->hq * rank * es, "q_abs"},
-                             {q_rope, (size_t)plan->Q * plan->hq * rope_dim * es, "q_rope"},
-                             {latent, slots * rank * es, "latent"},
-                             {kpos, slots * rope_dim * es, "kpos"}};
-  rc = check_disjoint(outs, ins);
-  if (rc == PA_OK) rc = check_aligned({outs[0], ins[0], ins[1], ins[2], ins[3]});
+  const Extent e_out{out, (size_t)plan->Q * plan->hq * rank * es, "out"};
+  const Extent e_lse{lse, lse ? (size_t)plan->Q * plan->hq * 4 : 0, "lse"};
+  const Extent e_ws{workspace, need, "workspace"};
+  const Extent e_qa{q_abs, (size_t)plan->Q * plan->hq * rank * es, "q_abs"};
+  const Extent e_qr{q_rope, (size_t)plan->Q * plan->hq * rope_dim * es, "q_rope"};
+  const Extent e_lat{latent, slots * rank * es, "latent"};
+  const Extent e_kp{kpos, slots * rope_dim * es, "kpos"};
+  rc = check_disjoint({e_out, e_lse, e_ws}, {e_qa, e_qr, e_lat, e_kp});
+  if (rc == PA_OK) rc = check_aligned({e_out, e_qa, e_qr, e_lat, e_kp});
   if (rc != PA_OK) return rc;
 
   FwdCall c{plan, dtype, rank, rank, {}, main_events_of(main_events), reinterpret_cast<hipStream_t>(stream)};
@@ -956,12 +961,11 @@ int pa_append_kv(const pa_plan* plan, int32_t dtype, const void* k_new, const vo
   if (plan->dup_query >= 0)
     return fail(PA_ERR_PLAN, "query %d writes the pool slot of another query of the plan", plan->dup_query);
   const size_t slots = (size_t)plan->num_pages * plan->ps * heads;
-  std::vector<Extent> outs = {{k_pool, slots * head_dim * es, "k_pool"}, {v_pool, slots * v_head_dim * es, "v_pool"}};
-  std::vector<Extent> ins = {{k_new, (size_t)plan->Q * heads * head_dim * es, "k_new"},
-                             {v_new, (size_t)plan->Q * heads * v_head_dim * es, "v_new"}};
-  int rc = check_disjoint(outs, ins);
-  if (rc == PA_OK) rc = check_aligned(outs);
-  if (rc == PA_OK) rc = check_aligned(ins);
+  const Extent e_kp{k_pool, slots * head_dim * es, "k_pool"}, e_vp{v_pool, slots * v_head_dim * es, "v_pool"};
+  const Extent e_kn{k_new, (size_t)plan->Q * heads * head_dim * es, "k_new"};
+  const Extent e_vn{v_new, (size_t)plan->Q * heads * v_head_dim * es, "v_new"};
+  int rc = check_disjoint({e_kp, e_vp}, {e_kn, e_vn});
+  if (rc == PA_OK) rc = check_aligned({e_kp, e_vp, e_kn, e_vn});
   if (rc != PA_OK) return rc;
   rc = check_device(plan, stream);
   if (rc != PA_OK) return rc;
@@ -1023,18 +1027,13 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   const size_t es = dtype == PA_F32 ? 4 : 2;
   const size_t slots = (size_t)plan->num_pages * plan->ps * plan->hkv;
   const size_t rows = (size_t)plan->Q * plan->hq;
-  std::vector<Extent> outs = {{dq, rows * head_dim * es, "dq"},
-                              {dk_pool, slots * head_dim * es, "dk_pool"},
-                              {dv_pool, slots * v_head_dim * es, "dv_pool"},
-                              {workspace, need, "workspace"}};
-  std::vector<Extent> ins = {{q, rows * head_dim * es, "q"},
-                             {k_pool, slots * head_dim * es, "k_pool"},
-                             {v_pool, slots * v_head_dim * es, "v_pool"},
-                             {out, rows * v_head_dim * es, "out"},
-                             {lse, rows * 4, "lse"},
-                             {dout, rows * v_head_dim * es, "dout"}};
-  int rc = check_disjoint(outs, ins);
-  if (rc == PA_OK) rc = check_aligned({outs[0], outs[1], outs[2], ins[0], ins[1], ins[2], ins[3], ins[5]});
+  const Extent e_dq{dq, rows * head_dim * es, "dq"}, e_dk{dk_pool, slots * head_dim * es, "dk_pool"};
+  const Extent e_dv{dv_pool, slots * v_head_dim * es, "dv_pool"}, e_ws{workspace, need, "workspace"};
+  const Extent e_q{q, rows * head_dim * es, "q"}, e_k{k_pool, slots * head_dim * es, "k_pool"};
+  const Extent e_v{v_pool, slots * v_head_dim * es, "v_pool"}, e_o{out, rows * v_head_dim * es, "out"};
+  const Extent e_l{lse, rows * 4, "lse"}, e_do{dout, rows * v_head_dim * es, "dout"};
+  int rc = check_disjoint({e_dq, e_dk, e_dv, e_ws}, {e_q, e_k, e_v, e_o, e_l, e_do});
+  if (rc == PA_OK) rc = check_aligned({e_dq, e_dk, e_dv, e_q, e_k, e_v, e_o, e_do});
   if (rc != PA_OK) return rc;
   rc = check_device(plan, stream);
   if (rc != PA_OK) return rc;
