@@ -209,8 +209,9 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
  *   lse          NULL or f32 [Q, Hq]: natural-log logsumexp of the scaled,
  *                masked scores of each row
  *   head_dim     D, 1..1024; v_head_dim Dv, 1..1024 (this build runs
- *                D = Dv in {64, 128, 256} and D = 192 with Dv = 128; other
- *                pairs give PA_ERR_UNSUPPORTED)
+ *                D = Dv in {64, 128, 256} and D = 192 with Dv = 128, with
+ *                group sizes Hq / Hkv in {1, 2, 3, 4, 5, 6, 7, 8, 12, 16};
+ *                other pairs and group sizes give PA_ERR_UNSUPPORTED)
  *   scale        finite and > 0 (e.g. 1/sqrt(D))
  *   workspace    f32 scratch of >= pa_plan_workspace_bytes(plan, v_head_dim)
  *                bytes, 256-byte aligned; may be NULL when that size is 0
@@ -366,6 +367,51 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                      const void* out, const float* lse, const void* dout, void* dq, void* dk_pool, void* dv_pool,
                      int32_t head_dim, int32_t v_head_dim, float scale, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * Block-sparse top-k attention (alice-llm 2.0.0, sparse_attention/
+ * llama3_bridge.rs, `llama3_sparse_attention`), on a GQA plan.  Key
+ * positions are grouped in blocks of `block_size` (a multiple of the plan's
+ * page size: block r holds positions [r * block_size, (r + 1) *
+ * block_size)).  For each query and KV head:
+ *
+ *   1. candidates: the blocks that hold a key the query sees (mask as for
+ *      pa_attention_fwd);
+ *   2. proxy score of a candidate: the largest dot product between the
+ *      group's FIRST query head (h = kvh * G) and a visible key of the block,
+ *      an f32 sum over dimensions in increasing order, one fused
+ *      multiply-add per dimension (`compute_proxy_block_max_scores`);
+ *   3. kept blocks: all candidates when topk == 0 or topk >= their number
+ *      (the page's dense fallback), else the topk best scores, a tie going
+ *      to the lower block index (`sparse_topk_select_batch`);
+ *   4. every query head of the group attends to the visible keys of the kept
+ *      blocks only: one partial per block, merged by log-sum-exp weights
+ *      (`kvouter_forward`, `lse_combine`).
+ *
+ *   block_size  > 0, a multiple of the plan's page size; a query row may
+ *               span at most 8192 blocks
+ *   topk        >= 0 (0 = keep every block)
+ *   selection   NULL, or int32 [Q, Hkv, width] receiving each row's kept
+ *               blocks in increasing order, -1 padded (width from
+ *               pa_sparse_workspace_bytes)
+ *   workspace   >= pa_sparse_workspace_bytes bytes, 256-byte aligned
+ *
+ * Other arguments, layouts and errors as for pa_attention_fwd (the plan's
+ * own split settings are not used: each kept block is one split piece);
+ * PA_ERR_SHAPE for a block size that is not a positive multiple of the page
+ * size; PA_ERR_UNSUPPORTED for K rows that are not whole 16-byte pieces or
+ * rows of more than 8192 blocks.  Three launches: selection, block
+ * attention, merge.
+ */
+int pa_sparse_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool,
+                            const void* v_pool, void* out, float* lse, int32_t head_dim,
+                            int32_t v_head_dim, float scale, int32_t block_size, int32_t topk,
+                            int32_t* selection, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes and selection width (topk, or for topk == 0 the largest
+ * candidate count of any row) of pa_sparse_attention_fwd for this plan. */
+int pa_sparse_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, int32_t block_size, int32_t topk,
+                              size_t* bytes, int32_t* width);
 
 /* Detail message of the calling thread's last failure ("" if none). */
 const char* pa_last_error(void);

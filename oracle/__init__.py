@@ -13,7 +13,10 @@ The backward (`attention_bwd`, `mla_bwd`: ruDNN `attention_backward` /
 the same file.  This module only builds it with gcc and marshals numpy
 arrays into it.  `brute.py` is an independent pure-Python brute force for
 tiny inputs.  `append_kv` (the cache write before attention) is a plain
-numpy loop.
+numpy loop.  `sparse_proxy_scores`, `sparse_select` and `sparse_attention`
+are the block-sparse top-k path of alice-llm 2.0.0
+sparse_attention/llama3_bridge.rs (proxy block-max scores and attention
+over the kept blocks in the C file, the top-k choice here).
 """
 from __future__ import annotations
 
@@ -47,7 +50,8 @@ def _load():
             build()
         lib = ctypes.CDLL(_LIB_PATH)
         I = ctypes.c_int
-        for name in ("po_attention", "po_mla", "po_widen", "po_attention_bwd", "po_mla_bwd"):
+        for name in ("po_attention", "po_mla", "po_widen", "po_attention_bwd", "po_mla_bwd", "po_sparse_proxy",
+                     "po_sparse_attention"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -213,3 +217,89 @@ def append_kv(seq_lens, cu_q, q_pos, block_table, page_size: int, k_new: np.ndar
             k_out[page, p % page_size] = k_new[i]
             v_out[page, p % page_size] = v_new[i]
     return k_out, v_out
+
+
+def visible_range(b, i: int, s: int) -> Tuple[int, int]:
+    """Keys [lo, hi] query i of sequence s sees (causal, window, t < L)."""
+    p, L = int(b.q_pos[i]), int(b.seq_lens[s])
+    hi = p if b.causal else L - 1
+    lo = max(0, p - b.window + 1) if b.window > 0 else 0
+    return lo, hi
+
+
+def sparse_proxy_scores(b, block_size: int, nthreads: Optional[int] = None) -> np.ndarray:
+    """Proxy block scores float32 [Q, hkv, nblk] (nblk = ceil(max L /
+    block_size)): the largest f32 dot product of the group's first query
+    head with a visible key of the block, summed in increasing dimension
+    order; -inf for blocks without a visible key (alice-llm
+    `compute_proxy_block_max_scores` with the first query head of each KV
+    head as proxy)."""
+    lib = _load()
+    Q = int(b.cu_q[-1])
+    nblk = max(1, -(-int(max(b.seq_lens, default=0)) // block_size))
+    scores = np.empty((Q, b.hkv, nblk), dtype=np.float32)
+    q, k = (_storage(x, b.dtype) for x in (b.q, b.k))
+    sl, cu, qp, bt = _i32(b.seq_lens), _i32(b.cu_q), _i32(b.q_pos), _i32(b.block_table)
+    rc = lib.po_sparse_proxy(
+        ctypes.c_int(_DT[b.dtype]), _ptr(q), _ptr(k), ctypes.c_int(len(sl)), _ptr(sl), _ptr(cu), _ptr(qp), _ptr(bt),
+        ctypes.c_int(bt.shape[1]), ctypes.c_int(b.page_size), ctypes.c_int(b.num_pages), ctypes.c_int(b.hq),
+        ctypes.c_int(b.hkv), ctypes.c_int(b.d), ctypes.c_int(int(b.causal)), ctypes.c_int(int(b.window)),
+        ctypes.c_int(block_size), _ptr(scores), ctypes.c_int(nblk), ctypes.c_int(nthreads or default_threads()))
+    if rc:
+        raise RuntimeError(f"oracle: {_ERR.get(rc, rc)}")
+    return scores
+
+
+def sparse_select(b, block_size: int, topk: int, scores: Optional[np.ndarray] = None) -> np.ndarray:
+    """Kept blocks int32 [Q, hkv, topk] in increasing order, -1 padded
+    (alice-llm `sparse_topk_select_batch`).  The candidates of a row are the
+    blocks holding a visible key; topk == 0 or topk >= their number keeps
+    them all (the dense fallback), else the topk largest proxy scores, a tie
+    going to the lower block index.  With topk == 0 the width is the largest
+    candidate count of any row."""
+    if scores is None:
+        scores = sparse_proxy_scores(b, block_size)
+    Q = int(b.cu_q[-1])
+    rows = []
+    for s in range(b.num_seqs):
+        for i in range(int(b.cu_q[s]), int(b.cu_q[s + 1])):
+            lo, hi = visible_range(b, i, s)
+            cand = list(range(lo // block_size, hi // block_size + 1))
+            for h in range(b.hkv):
+                if topk == 0 or topk >= len(cand):
+                    keep = cand
+                else:
+                    keep = sorted(sorted(cand, key=lambda r: (-float(scores[i, h, r]), r))[:topk])
+                rows.append((i, h, keep))
+    width = topk if topk > 0 else max([len(k) for _, _, k in rows], default=1)
+    sel = np.full((Q, b.hkv, max(width, 1)), -1, dtype=np.int32)
+    for i, h, keep in rows:
+        sel[i, h, :len(keep)] = keep
+    return sel
+
+
+def sparse_attention(b, sel: np.ndarray, block_size: int, nthreads: Optional[int] = None
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of batch `b` over the visible keys of the kept blocks `sel`
+    [Q, hkv, k] (-1 = none), all query heads of a KV head sharing its
+    blocks (alice-llm `kvouter_forward` + `lse_combine`, written as one
+    softmax over the union of the kept keys).  Returns (out [Q, hq, dv],
+    lse [Q, hq])."""
+    lib = _load()
+    Q = int(b.cu_q[-1])
+    out = np.empty((Q * b.hq, b.dv), dtype=np.float64)
+    lse = np.empty(Q * b.hq, dtype=np.float64)
+    q, k, v = (_storage(x, b.dtype) for x in (b.q, b.k, b.v))
+    sl, cu, qp, bt = _i32(b.seq_lens), _i32(b.cu_q), _i32(b.q_pos), _i32(b.block_table)
+    sel = _i32(sel)
+    assert sel.shape[:2] == (Q, b.hkv)
+    rc = lib.po_sparse_attention(
+        ctypes.c_int(_DT[b.dtype]), _ptr(q), _ptr(k), _ptr(v),
+        ctypes.c_int(len(sl)), _ptr(sl), _ptr(cu), _ptr(qp), _ptr(bt), ctypes.c_int(bt.shape[1]),
+        ctypes.c_int(b.page_size), ctypes.c_int(b.num_pages), ctypes.c_int(b.hq), ctypes.c_int(b.hkv),
+        ctypes.c_int(b.d), ctypes.c_int(b.dv), ctypes.c_double(b.scale), ctypes.c_int(int(b.causal)),
+        ctypes.c_int(int(b.window)), _ptr(sel), ctypes.c_int(sel.shape[2]), ctypes.c_int(block_size),
+        _ptr(out), _ptr(lse), ctypes.c_int(nthreads or default_threads()))
+    if rc:
+        raise RuntimeError(f"oracle: {_ERR.get(rc, rc)}")
+    return out.reshape(Q, b.hq, b.dv), lse.reshape(Q, b.hq)

@@ -95,6 +95,11 @@ typedef struct {
     /* tensors */
     const void *q, *k, *v;       /* MLA: k = v = latent */
     const void *qp, *kp;         /* MLA only */
+    /* block-sparse attention only: keys of block t / block_size count for
+     * (query i, KV head h) iff that block is among sel[(i * hkv + h) * sel_k
+     * .. + sel_k) (-1 entries unused); NULL = every visible key */
+    const int32_t *sel;
+    int sel_k, block_size;
     /* rows to evaluate: NULL = every (query, head) in order */
     const int64_t *rows;
     int64_t num_rows;
@@ -125,6 +130,18 @@ static int po_visible(const po_job *j, int t, int pos, int len)
     return 1;
 }
 
+/* Key t of a visible row counts: every visible key, or for block-sparse
+ * attention the visible keys of the selected blocks. */
+static int po_used(const po_job *j, int i, int kvh, int t, int pos, int len)
+{
+    if (!po_visible(j, t, pos, len)) return 0;
+    if (!j->sel) return 1;
+    const int32_t *row = j->sel + ((int64_t)i * j->hkv + kvh) * j->sel_k;
+    for (int e = 0; e < j->sel_k; ++e)
+        if (row[e] >= 0 && row[e] == t / j->block_size) return 1;
+    return 0;
+}
+
 /* Element offset of (key t, kv head kvh, component c) in a pool whose rows are
  * `width` wide and that has `heads` heads per slot. */
 static int64_t po_pool_offset(const po_job *j, int s, int t, int kvh, int heads, int width, int c,
@@ -151,7 +168,7 @@ static int po_row(const po_job *j, int i, int h, double *sc, double *out_row, do
     double m = -INFINITY;
     int count = 0;
     for (int t = 0; t < len; ++t) {
-        if (!po_visible(j, t, pos, len)) { sc[t] = -INFINITY; continue; }
+        if (!po_used(j, i, kvh, t, pos, len)) { sc[t] = -INFINITY; continue; }
         double dot = 0.0;
         for (int c = 0; c < j->d; ++c) {
             double qv = po_load(j->dtype, j->q, ((int64_t)i * j->hq + h) * j->d + c);
@@ -185,7 +202,7 @@ static int po_row(const po_job *j, int i, int h, double *sc, double *out_row, do
     /* weighted sum of the visible value rows, keys in increasing order */
     for (int c = 0; c < j->dv; ++c) out_row[c] = 0.0;
     for (int t = 0; t < len; ++t) {
-        if (!po_visible(j, t, pos, len)) continue;
+        if (!po_used(j, i, kvh, t, pos, len)) continue;
         for (int c = 0; c < j->dv; ++c)
             out_row[c] += sc[t] * po_load(j->dtype, j->v, po_pool_offset(j, s, t, kvh, j->hkv, j->dv, c, &bad));
     }
@@ -487,4 +504,135 @@ int po_mla_bwd(int dtype, const void *q_abs, const void *q_rope, const void *lat
     j.nthreads = nthreads;
     const int64_t slots = (int64_t)num_pages * page_size;
     return po_bwd_run(&j, dout, dq_abs, dq_rope, dlatent, dlatent, dkpos, slots * r, slots * r, slots * p);
+}
+
+/* ------------------------------------------------------------------------
+ * Block-sparse top-k attention (alice-llm 2.0.0, sparse_attention/
+ * llama3_bridge.rs, `llama3_sparse_attention`): keys are grouped in blocks
+ * of block_size consecutive positions; for each (query, KV head) a proxy
+ * scores every block by the largest dot product between the first query
+ * head of the group and the block's keys (`compute_proxy_block_max_scores`,
+ * the cheap proxy "first Q lane of each KV head"), the top-k blocks are kept
+ * (`sparse_topk_select_batch`) and attention runs over the keys of the kept
+ * blocks only, its per-block partials merged by log-sum-exp
+ * (`kvouter_forward`, `lse_combine`) -- the same value as one softmax over
+ * the union of those keys, which is what po_sparse_attention computes.
+ *
+ * The page runs the proxy in f32 on the CPU.  The proxy here is the f32
+ * product sum taken in increasing dimension order, each step one fused
+ * multiply-add (for 16-bit inputs the products are exact in f32, so a plain
+ * multiply then add gives the same bits); a block's score is the largest
+ * score of its visible keys, -inf for a block with none.
+ * ---------------------------------------------------------------------- */
+
+/* Exact widening of one stored element to float (f32 data as is). */
+static float po_loadf(int dtype, const void *base, int64_t idx)
+{
+    if (dtype == PO_F32)
+        return ((const float *)base)[idx];
+    return (float)po_load(dtype, base, idx);
+}
+
+typedef struct {
+    const po_job *job;
+    float *scores;      /* [queries, hkv, nblk] */
+    int nblk, tid, nthreads, status;
+} po_proxy_arg;
+
+static void *po_proxy_worker(void *arg)
+{
+    po_proxy_arg *a = (po_proxy_arg *)arg;
+    const po_job *j = a->job;
+    const int64_t rows = (int64_t)j->num_queries * j->hkv;
+    const int group = j->hq / j->hkv;
+    for (int64_t row = a->tid; row < rows; row += a->nthreads) {
+        const int i = (int)(row / j->hkv), kvh = (int)(row % j->hkv);
+        float *out = a->scores + row * a->nblk;
+        for (int r = 0; r < a->nblk; ++r) out[r] = -INFINITY;
+        const int s = po_seq_of(j, i);
+        if (s < 0) { a->status = -1; continue; }
+        const int len = j->seq_lens[s], pos = j->q_pos[i];
+        const int64_t qbase = ((int64_t)i * j->hq + (int64_t)kvh * group) * j->d; /* first head of the group */
+        for (int t = 0; t < len; ++t) {
+            if (!po_visible(j, t, pos, len)) continue;
+            int bad = 0;
+            float acc = 0.f;
+            for (int c = 0; c < j->d; ++c) {
+                const float qv = po_loadf(j->dtype, j->q, qbase + c);
+                const float kv = po_loadf(j->dtype, j->k, po_pool_offset(j, s, t, kvh, j->hkv, j->d, c, &bad));
+                acc = j->dtype == PO_F32 ? fmaf(qv, kv, acc) : acc + qv * kv;
+            }
+            if (bad) { a->status = -2; break; }
+            const int r = t / j->block_size;
+            if (r < a->nblk && acc > out[r]) out[r] = acc;
+        }
+    }
+    return NULL;
+}
+
+/*
+ * Proxy block scores of every (query, KV head) row: scores [queries, hkv,
+ * nblk] float, block r covering key positions [r * block_size, (r + 1) *
+ * block_size).  Return codes as po_attention.
+ */
+int po_sparse_proxy(int dtype, const void *q, const void *k, int num_seqs, const int32_t *seq_lens,
+                    const int32_t *cu_q, const int32_t *q_pos, const int32_t *block_table, int table_width,
+                    int page_size, int num_pages, int hq, int hkv, int d, int causal, int window, int block_size,
+                    float *scores, int nblk, int nthreads)
+{
+    po_job j;
+    memset(&j, 0, sizeof j);
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || page_size <= 0 || block_size <= 0 || nblk < 0) return -4;
+    if (dtype != PO_F32 && dtype != PO_BF16 && dtype != PO_F16) return -4;
+    j.dtype = dtype;
+    j.num_seqs = num_seqs; j.table_width = table_width; j.page_size = page_size; j.num_pages = num_pages;
+    j.seq_lens = seq_lens; j.cu_q = cu_q; j.q_pos = q_pos; j.block_table = block_table;
+    j.num_queries = num_seqs > 0 ? cu_q[num_seqs] : 0;
+    j.hq = hq; j.hkv = hkv; j.d = d; j.dv = d;
+    j.causal = causal; j.window = window; j.block_size = block_size;
+    j.q = q; j.k = k;
+    int n = nthreads > 0 ? nthreads : 1;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n);
+    po_proxy_arg *args = (po_proxy_arg *)malloc(sizeof(po_proxy_arg) * (size_t)n);
+    if (!th || !args) { free(th); free(args); return -3; }
+    for (int t = 0; t < n; ++t) {
+        po_proxy_arg init = {&j, scores, nblk, t, n, 0};
+        args[t] = init;
+        pthread_create(&th[t], NULL, po_proxy_worker, &args[t]);
+    }
+    int status = 0;
+    for (int t = 0; t < n; ++t) {
+        pthread_join(th[t], NULL);
+        if (args[t].status) status = args[t].status;
+    }
+    free(th);
+    free(args);
+    return status;
+}
+
+/*
+ * Attention over the visible keys of the selected blocks: sel [queries, hkv,
+ * sel_k] block indices (-1 = none); otherwise as po_attention.  With every
+ * block of a row selected the row is exactly po_attention's.
+ */
+int po_sparse_attention(int dtype, const void *q, const void *k, const void *v,
+                        int num_seqs, const int32_t *seq_lens, const int32_t *cu_q, const int32_t *q_pos,
+                        const int32_t *block_table, int table_width, int page_size, int num_pages,
+                        int hq, int hkv, int d, int dv, double scale, int causal, int window,
+                        const int32_t *sel, int sel_k, int block_size,
+                        double *out, double *lse, int nthreads)
+{
+    po_job j;
+    memset(&j, 0, sizeof j);
+    if (!sel || sel_k <= 0 || block_size <= 0) return -4;
+    j.dtype = dtype;
+    j.num_seqs = num_seqs; j.table_width = table_width; j.page_size = page_size; j.num_pages = num_pages;
+    j.seq_lens = seq_lens; j.cu_q = cu_q; j.q_pos = q_pos; j.block_table = block_table;
+    j.num_queries = num_seqs > 0 ? cu_q[num_seqs] : 0;
+    j.hq = hq; j.hkv = hkv; j.d = d; j.dv = dv; j.p = 0;
+    j.scale = scale; j.causal = causal; j.window = window;
+    j.q = q; j.k = k; j.v = v;
+    j.sel = sel; j.sel_k = sel_k; j.block_size = block_size;
+    j.out = out; j.lse = lse; j.nthreads = nthreads;
+    return po_run(&j);
 }

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_INVALID", -2: "PA_ERR_SHAPE", -3: "PA_ER
                 -9: "PA_ERR_DEVICE"}
 EXPORTED = ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
             "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv", "pa_status_string",
-            "pa_last_error", "pa_plan_bwd_workspace_bytes", "pa_attention_bwd", "pa_attention_fwd_noalloc")
+            "pa_last_error", "pa_plan_bwd_workspace_bytes", "pa_attention_bwd", "pa_attention_fwd_noalloc",
+            "pa_sparse_attention_fwd", "pa_sparse_workspace_bytes")
 
 
 class PaError(RuntimeError):
@@ -73,6 +74,8 @@ def load_library():
     lib.pa_plan_workspace_bytes.argtypes = [P, I, ctypes.POINTER(S)]
     lib.pa_attention_fwd.argtypes = [P, I, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_attention_fwd_noalloc.argtypes = [P, I, P, P, P, P, P, I, I, F, P]
+    lib.pa_sparse_attention_fwd.argtypes = [P, I, P, P, P, P, P, I, I, F, I, I, P, P, S, P]
+    lib.pa_sparse_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S), ctypes.POINTER(I)]
     lib.pa_mla_fwd.argtypes = [P, I, P, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_append_kv.argtypes = [P, I, P, P, P, P, I, I, P]
     lib.pa_plan_bwd_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S)]
@@ -83,7 +86,8 @@ def load_library():
     lib.pa_last_error.restype = ctypes.c_char_p
     for n in ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
               "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv",
-              "pa_plan_bwd_workspace_bytes", "pa_attention_bwd", "pa_attention_fwd_noalloc"):
+              "pa_plan_bwd_workspace_bytes", "pa_attention_bwd", "pa_attention_fwd_noalloc",
+            "pa_sparse_attention_fwd", "pa_sparse_workspace_bytes"):
         getattr(lib, n).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -328,6 +332,31 @@ def pa_attention_fwd_noalloc(plan: Plan, q, k_pool, v_pool, out, lse=None, *, sc
     dt, pq, pk, pv, po, pl, D, Dv = _fwd_args(plan, q, k_pool, v_pool, out, lse)
     _check(load_library().pa_attention_fwd_noalloc(plan.handle, dt, pq, pk, pv, po, pl, D, Dv, float(scale),
                                                    _stream_handle(stream)), "pa_attention_fwd_noalloc")
+
+
+def pa_sparse_workspace_bytes(plan: Plan, v_head_dim: int, block_size: int, topk: int):
+    """(workspace bytes, selection width) of pa_sparse_attention_fwd."""
+    n, w = ctypes.c_size_t(), ctypes.c_int32()
+    _check(load_library().pa_sparse_workspace_bytes(plan.handle, int(v_head_dim), int(block_size), int(topk),
+                                                    ctypes.byref(n), ctypes.byref(w)), "pa_sparse_workspace_bytes")
+    return int(n.value), int(w.value)
+
+
+def pa_sparse_attention_fwd(plan: Plan, q, k_pool, v_pool, out, lse=None, *, scale: float, block_size: int,
+                            topk: int, selection=None, workspace=None, stream=None) -> None:
+    """Block-sparse top-k forward into `out` (see pa_sparse_attention_fwd in
+    paged_attn.h); selection: None or an int32 device tensor [Q, Hkv, width]."""
+    import torch
+    dt, pq, pk, pv, po, pl, D, Dv = _fwd_args(plan, q, k_pool, v_pool, out, lse)
+    psel = None
+    if selection is not None:
+        if selection.dtype != torch.int32 or selection.dim() != 3:
+            raise ValueError("selection must be an int32 [Q, Hkv, width] tensor")
+        psel = _dev(selection, "selection", 3)
+    wp, wn = _ws(workspace)
+    _check(load_library().pa_sparse_attention_fwd(plan.handle, dt, pq, pk, pv, po, pl, D, Dv, float(scale),
+                                                  int(block_size), int(topk), psel, wp, wn, _stream_handle(stream)),
+           "pa_sparse_attention_fwd")
 
 
 def pa_plan_bwd_workspace_bytes(plan: Plan, dtype, head_dim: int, v_head_dim: int) -> int:

@@ -93,6 +93,7 @@ struct pa_plan {
   // and the first query whose slot another query also writes (-1: none)
   std::vector<int32_t> slot_of;
   int32_t dup_query = -1;
+  std::vector<int32_t> seq_of;    // sequence of each packed query (block-sparse selection)
   // backward (GQA plans): dQ items, then dK/dV items; a page that two key
   // positions share (-1: none) makes the single-writer dK/dV pass impossible
   std::vector<pa::BwdItem> bwd_items;
@@ -107,6 +108,7 @@ struct pa_plan {
   const WorkItem* d_items = nullptr;
   const int32_t* d_wg_first = nullptr;
   const int32_t* d_slot_of = nullptr;
+  const int32_t* d_seq_of = nullptr;
   const MergeItem* d_merges = nullptr;
   const pa::BwdItem* d_bwd = nullptr;
 
@@ -617,8 +619,10 @@ pa_plan* new_plan(const pa_plan_desc* desc) {
   if (p->Q > 0) p->q_pos.assign(desc->q_pos, desc->q_pos + p->Q);
   // append slots (positions are validated: every one maps to a pool page)
   p->slot_of.resize(p->Q);
+  p->seq_of.resize(p->Q);
   for (int s = 0; s < p->S; ++s)
     for (int i = p->cu_q[s]; i < p->cu_q[s + 1]; ++i) {
+      p->seq_of[i] = s;
       const int pos = p->q_pos[i];
       p->slot_of[i] = p->bt[(size_t)s * p->W + pos / p->ps] * p->ps + pos % p->ps;
     }
@@ -662,7 +666,8 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   size_t off_merges = align_up(off_wg + p->wg_first.size() * 4, kAlign);
   size_t off_slots = align_up(off_merges + p->merges.size() * sizeof(MergeItem), kAlign);
   size_t off_bwd = align_up(off_slots + p->slot_of.size() * 4, kAlign);
-  size_t total = align_up(off_bwd + p->bwd_items.size() * sizeof(pa::BwdItem), kAlign);
+  size_t off_seq = align_up(off_bwd + p->bwd_items.size() * sizeof(pa::BwdItem), kAlign);
+  size_t total = align_up(off_seq + p->seq_of.size() * 4, kAlign);
   total = std::max(total, kAlign);
   p->blob.assign(total, 0);
   if (!p->bt.empty()) memcpy(p->blob.data() + off_bt, p->bt.data(), p->bt.size() * 4);
@@ -675,6 +680,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   if (!p->slot_of.empty()) memcpy(p->blob.data() + off_slots, p->slot_of.data(), p->slot_of.size() * 4);
   if (!p->bwd_items.empty())
     memcpy(p->blob.data() + off_bwd, p->bwd_items.data(), p->bwd_items.size() * sizeof(pa::BwdItem));
+  if (!p->seq_of.empty()) memcpy(p->blob.data() + off_seq, p->seq_of.data(), p->seq_of.size() * 4);
 
   // stream-ordered allocation, upload and (in pa_plan_destroy) free: no call
   // of the plan's life waits for the device
@@ -703,6 +709,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   p->d_merges = reinterpret_cast<const MergeItem*>(p->dev + off_merges);
   p->d_slot_of = reinterpret_cast<const int32_t*>(p->dev + off_slots);
   p->d_bwd = reinterpret_cast<const pa::BwdItem*>(p->dev + off_bwd);
+  p->d_seq_of = reinterpret_cast<const int32_t*>(p->dev + off_seq);
   *out_plan = p;
   return ok();
 }
@@ -1061,6 +1068,166 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                                     bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv,
                                     plan->n_bwd_dqt, (int64_t)rows, (int64_t)slots, std::max(plan->n_cu, 1), st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Block-sparse top-k attention (alice-llm 2.0.0, sparse_attention/
+// llama3_bridge.rs, `llama3_sparse_attention`).  Workspace: decode items and
+// identity workgroup map [rows * width], merge records [rows], then split
+// partials of rows * width slots (rows = Q * Hkv, one slot per kept block).
+// ---------------------------------------------------------------------------
+namespace {
+
+struct SparseLayout {
+  int32_t width = 0;
+  size_t off_items = 0, off_wg = 0, off_merges = 0, off_o = 0, off_ml = 0, total = 0;
+};
+
+int sparse_layout(const pa_plan* p, int dv, int block_size, int topk, SparseLayout* out) {
+  if (p->mla) return fail(PA_ERR_INVALID, "block-sparse attention runs on GQA plans (mla == 0)");
+  if (block_size <= 0 || block_size % p->ps != 0)
+    return fail(PA_ERR_SHAPE, "block_size %d must be a positive multiple of page_size %d", block_size, p->ps);
+  if (topk < 0) return fail(PA_ERR_INVALID, "topk %d < 0", topk);
+  if (dv <= 0 || dv > 1024) return fail(PA_ERR_SHAPE, "v_head_dim %d outside [1, 1024]", dv);
+  int32_t most = 0;  // candidate blocks of the widest row
+  for (int s = 0; s < p->S; ++s)
+    for (int i = p->cu_q[s]; i < p->cu_q[s + 1]; ++i) {
+      int lo, hi;
+      visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &lo, &hi);
+      most = std::max(most, hi / block_size - lo / block_size + 1);
+    }
+  if (most > pa::kSparseMaxBlocks)
+    return fail(PA_ERR_UNSUPPORTED, "a row spans %d blocks of %d keys; the selection holds at most %d", most,
+                block_size, pa::kSparseMaxBlocks);
+  SparseLayout L;
+  L.width = topk > 0 ? topk : std::max(most, 1);
+  const size_t rows = (size_t)p->Q * p->hkv, slots = rows * L.width;
+  if (slots > (size_t)INT32_MAX) return fail(PA_ERR_RANGE, "rows x kept blocks exceed 32-bit indexing");
+  L.off_items = 0;
+  L.off_wg = align_up(slots * sizeof(WorkItem), kAlign);
+  L.off_merges = align_up(L.off_wg + (slots + 1) * 4, kAlign);
+  L.off_o = align_up(L.off_merges + rows * sizeof(MergeItem), kAlign);
+  L.off_ml = align_up(L.off_o + slots * p->group() * dv * 4, kAlign);
+  L.total = p->Q > 0 ? align_up(L.off_ml + slots * p->group() * 3 * 4, kAlign) : 0;
+  *out = L;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_sparse_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, int32_t block_size, int32_t topk,
+                              size_t* bytes, int32_t* width) {
+  if (!plan || !bytes || !width) return fail(PA_ERR_INVALID, "plan, bytes and width are required");
+  SparseLayout L;
+  const int rc = sparse_layout(plan, v_head_dim, block_size, topk, &L);
+  if (rc != PA_OK) return rc;
+  *bytes = L.total;
+  *width = L.width;
+  return ok();
+}
+
+int pa_sparse_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool,
+                            const void* v_pool, void* out, float* lse, int32_t head_dim, int32_t v_head_dim,
+                            float scale, int32_t block_size, int32_t topk, int32_t* selection, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!k_pool || !v_pool) return fail(PA_ERR_INVALID, "k_pool and v_pool are required");
+  if (plan->Q > 0 && (!q || !out)) return fail(PA_ERR_INVALID, "q and out are required when there are queries");
+  if (head_dim <= 0 || head_dim > pa::kSparseMaxDim || v_head_dim <= 0 || v_head_dim > 1024)
+    return fail(PA_ERR_SHAPE, "head sizes D=%d Dv=%d outside [1, 1024]", head_dim, v_head_dim);
+  const size_t es = dtype == PA_F32 ? 4 : 2;
+  if ((head_dim * es) % 16) return fail(PA_ERR_UNSUPPORTED, "K rows of %d elements are not whole 16-byte pieces", head_dim);
+  if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
+  SparseLayout L;
+  int rc = sparse_layout(plan, v_head_dim, block_size, topk, &L);
+  if (rc != PA_OK) return rc;
+  rc = check_device(plan, stream);
+  if (rc != PA_OK) return rc;
+  const int G = plan->group();
+  if (!pa::gqa_supported(dtype, head_dim, v_head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "no decode kernel for dtype %d, D=%d, Dv=%d, G=%d", dtype, head_dim, v_head_dim,
+                G);
+  if (L.total > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "block-sparse attention needs %zu bytes of workspace", L.total);
+    if (workspace_bytes < L.total)
+      return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, block-sparse attention needs %zu", workspace_bytes,
+                  L.total);
+    if ((uintptr_t)workspace % kAlign) return fail(PA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  }
+  const size_t rows = (size_t)plan->Q * plan->hkv;
+  const size_t slots = (size_t)plan->num_pages * plan->ps * plan->hkv;
+  const Extent e_out{out, (size_t)plan->Q * plan->hq * v_head_dim * es, "out"};
+  const Extent e_lse{lse, lse ? (size_t)plan->Q * plan->hq * 4 : 0, "lse"};
+  const Extent e_ws{workspace, L.total, "workspace"};
+  const Extent e_sel{selection, selection ? rows * L.width * 4 : 0, "selection"};
+  const Extent e_q{q, (size_t)plan->Q * plan->hq * head_dim * es, "q"};
+  const Extent e_k{k_pool, slots * head_dim * es, "k_pool"};
+  const Extent e_v{v_pool, slots * v_head_dim * es, "v_pool"};
+  rc = check_disjoint({e_out, e_lse, e_ws, e_sel}, {e_q, e_k, e_v});
+  if (rc == PA_OK) rc = check_aligned({e_out, e_q, e_k, e_v});
+  if (rc != PA_OK) return rc;
+  if (plan->Q == 0) return ok();
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  pa::SparseArgs sa{};
+  sa.q = q;
+  sa.k = k_pool;
+  sa.block_table = plan->d_bt;
+  sa.q_pos = plan->d_qpos;
+  sa.seq_lens = plan->d_lens;
+  sa.seq_of = plan->d_seq_of;
+  sa.table_width = plan->W;
+  sa.page_shift = plan->page_shift;
+  sa.hq = plan->hq;
+  sa.hkv = plan->hkv;
+  sa.d = head_dim;
+  sa.causal = plan->causal;
+  sa.window = plan->window;
+  sa.block_size = block_size;
+  sa.topk = topk;
+  sa.width = L.width;
+  sa.selection = selection;
+  sa.items = reinterpret_cast<WorkItem*>(ws + L.off_items);
+  sa.wg_first = reinterpret_cast<int32_t*>(ws + L.off_wg);
+  sa.merges = reinterpret_cast<MergeItem*>(ws + L.off_merges);
+  hipError_t e = pa::launch_sparse_select(dtype, sa, (int)rows, st);
+  if (e != hipSuccess) return hip_fail(e, "block selection launch");
+
+  pa::KernelArgs a{};
+  a.q = q;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = reinterpret_cast<float*>(ws + L.off_o);
+  a.ws_ml = reinterpret_cast<float*>(ws + L.off_ml);
+  a.block_table = plan->d_bt;
+  a.q_pos = plan->d_qpos;
+  a.seq_lens = plan->d_lens;
+  a.items = sa.items;
+  a.n_items = (int32_t)(rows * L.width);
+  a.wg_first = sa.wg_first;
+  a.n_wg = (int32_t)(rows * L.width);
+  a.heads_shift = 0;
+  a.table_width = plan->W;
+  a.page_shift = plan->page_shift;
+  a.hq = plan->hq;
+  a.hkv = plan->hkv;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.causal = plan->causal;
+  a.window = plan->window;
+  e = pa::launch_gqa_main(dtype, head_dim, v_head_dim, G, false, a, pa::MainEvents{}, st);
+  if (e != hipSuccess) return hip_fail(e, "block attention launch");
+  e = pa::launch_gqa_merge(dtype, head_dim, v_head_dim, G, a, sa.merges, (int)rows, st);
+  if (e != hipSuccess) return hip_fail(e, "block merge launch");
   return ok();
 }
 

@@ -17,6 +17,22 @@ struct MainEvents {
 
 // dtype: 0 = f32, 1 = bf16, 2 = f16.  d, dv: K and V head sizes.  g: query
 // heads per KV head.
+
+// Launcher of one GQA kernel (decode, mixed or merge) for one data type, head
+// size pair and group size.
+using LaunchFn = hipError_t (*)(const KernelArgs&, int n_wg, const MergeItem* merges, int n_merges,
+                                const MainEvents& ev, hipStream_t stream);
+// The kernels of one group size (a launcher is null when no kernel exists
+// for that data type and head size pair) and the decode launch shape.
+struct GqaFamily {
+  LaunchFn decode = nullptr, mixed = nullptr, merge = nullptr;
+  int waves = 1, wgs_per_cu = 1;
+};
+// Lookups of the two translation units that instantiate the group sizes
+// (false when g is not among theirs).
+bool gqa_family_pow2(int dtype, int d, int dv, int g, GqaFamily* out);
+bool gqa_family_other(int dtype, int d, int dv, int g, GqaFamily* out);
+
 bool gqa_supported(int dtype, int d, int dv, int g);
 bool prefill_supported(int dtype, int d, int dv, int g);
 // Main GQA launch over the a.n_items entries of a.items: decode-only, or one
@@ -48,6 +64,29 @@ hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* mer
 // multiples of 16 bytes; n_cu sizes the grid.
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* slot_of,
                          int64_t queries, int heads, int k_row_bytes, int v_row_bytes, int n_cu, hipStream_t stream);
+
+// Block-sparse top-k selection: one workgroup per (query, KV head) row
+// scores the row's candidate blocks, keeps `topk` of them (all when topk is
+// 0 or covers every candidate) and writes, at [row * width, + width), one
+// decode item per kept block (increasing block order, kEmpty padding), the
+// identity workgroup map and the row's merge record.
+constexpr int kSparseMaxBlocks = 8192;  // candidate blocks of one row (LDS scores)
+constexpr int kSparseMaxDim = 1024;     // K head size (LDS proxy query)
+struct SparseArgs {
+  const void* q;  // [Q, Hq, D]
+  const void* k;  // [pages, ps, Hkv, D]
+  const int32_t* block_table;
+  const int32_t* q_pos;
+  const int32_t* seq_lens;
+  const int32_t* seq_of;  // sequence of each packed query
+  int32_t table_width, page_shift, hq, hkv, d, causal, window;
+  int32_t block_size, topk, width;
+  int32_t* selection;  // [Q, Hkv, width] kept blocks, -1 padded, or null
+  WorkItem* items;     // [Q * Hkv * width]
+  int32_t* wg_first;   // [Q * Hkv * width + 1]
+  MergeItem* merges;   // [Q * Hkv]
+};
+hipError_t launch_sparse_select(int dtype, const SparseArgs& a, int rows, hipStream_t stream);
 
 // Paged GQA/MHA backward: zero dk / dv (pool shaped, pool_slots rows of each),
 // D = dO . O for the `rows` (query, head) rows into delta, then dQ (per-query

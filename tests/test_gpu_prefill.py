@@ -128,3 +128,56 @@ def test_prefill_sequence_order_does_not_change_rows():
     r2()
     o2, _ = r2.result()
     assert np.array_equal(o1[qidx], o2)
+
+
+GROUP_CASES = [  # group sizes that are not powers of two (Hq / Hkv)
+    dict(hq=24, hkv=8, d=128, page_size=16, q_counts=(1, 90, 1, 3), max_len=1500),          # G = 3
+    dict(hq=40, hkv=8, d=128, page_size=64, q_counts=(2, 1, 70), max_len=2500, window=300),  # G = 5
+    dict(hq=12, hkv=2, d=64, page_size=16, q_counts=(1, 1, 130), max_len=900),              # G = 6
+    dict(hq=28, hkv=4, d=128, page_size=32, q_counts=(1, 60, 1), max_len=3000),            # G = 7
+    dict(hq=48, hkv=4, d=128, page_size=16, q_counts=(1, 1, 40), max_len=2000, causal=False),  # G = 12
+    dict(hq=14, hkv=2, d=128, page_size=16, q_counts=(1, 1), max_len=5000),                # G = 7, decode only
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("i", range(len(GROUP_CASES)))
+def test_group_sizes_beyond_powers_of_two(i, dtype):
+    """Hq / Hkv of 3, 5, 6, 7 and 12: decode rows (split and whole) and MFMA
+    prefill tiles whose 256 rows hold floor(256 / G) queries."""
+    b = random_batch(2500 + i, dtype=dtype, **GROUP_CASES[i])
+    for split_tokens in (0, 128):
+        run = GqaRun(b, split_tokens=split_tokens)
+        run()
+        out, lse = run.result()
+        ref_o, ref_l = oracle.attention(b)
+        assert_close(out, ref_o, dtype)
+        np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-3)
+
+
+def test_group_size_seven_f32_and_window_one_bitwise():
+    """f32 tiles (query by query) at G = 7, and one visible key returning its
+    own value row bit for bit at G = 5 in a mixed launch."""
+    b = random_batch(2600, dtype="f32", hq=28, hkv=4, d=64, page_size=16, q_counts=(1, 20, 2), max_len=700)
+    _all_rows(b)
+    b = random_batch(2601, dtype="bf16", hq=40, hkv=8, d=128, page_size=16, q_counts=(1, 50, 1), max_len=900,
+                     window=1)
+    run = GqaRun(b)
+    run()
+    out, _ = run.result()
+    v = to_f64(run.v)
+    for s in range(b.num_seqs):
+        for i in range(int(b.cu_q[s]), int(b.cu_q[s + 1])):
+            p = int(b.q_pos[i])
+            row = v[b.block_table[s, p // b.page_size], p % b.page_size]
+            for h in range(b.hq):
+                assert np.array_equal(out[i, h], row[h // 5]), (i, h)
+
+
+def test_unsupported_group_size_is_refused():
+    """G = 32 has no kernel in this build: refused before any launch."""
+    import paged_kv_attention_gqa_amd as pa
+    b = random_batch(2700, dtype="bf16", hq=32, hkv=1, d=128, page_size=16, q_counts=(1,), max_len=100)
+    with pytest.raises(pa.PaError) as e:
+        GqaRun(b)()
+    assert e.value.name == "PA_ERR_UNSUPPORTED"
