@@ -356,8 +356,9 @@ int pa_plan_bwd_workspace_bytes(const pa_plan* plan, int32_t dtype, int32_t head
  *                no visible key of any query lands on are zero
  *   workspace    >= pa_plan_bwd_workspace_bytes bytes, 256-byte aligned
  *
- * Head sizes as for pa_attention_fwd.  Errors: PA_ERR_UNSUPPORTED for MLA
- * plans (no MLA backward in this build) and for missing kernels;
+ * Head sizes as for pa_attention_fwd (group sizes 1, 2, 4, 8, 16).  Errors:
+ * PA_ERR_INVALID for MLA plans (pa_mla_bwd), PA_ERR_UNSUPPORTED for missing
+ * kernels;
  * PA_ERR_WORKSPACE,
  * PA_ERR_OVERLAP, PA_ERR_SHAPE, PA_ERR_DEVICE, PA_ERR_HIP as for
  * pa_attention_fwd.  Q == 0 zeroes dk_pool and dv_pool and touches nothing
@@ -412,6 +413,36 @@ int pa_sparse_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, c
  * candidate count of any row) of pa_sparse_attention_fwd for this plan. */
 int pa_sparse_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, int32_t block_size, int32_t topk,
                               size_t* bytes, int32_t* width);
+
+/*
+ * Absorbed-MLA backward (ruDNN 0.1.107 paged_attention `mla_backward` /
+ * `mla_backward_into`): first-order gradients of pa_mla_fwd, scores
+ * recomputed from the queries and the caches.  The latent serves as key and
+ * value, so its gradient holds both terms.  With s_t = scale (q_abs . lat_t
+ * + q_rope . kpos_t), P the softmax weights of a row (from the forward's
+ * lse), dP_t = dO . lat_t, D = dO . O and dS_t = P_t (dP_t - D):
+ *
+ *   dq_abs = scale sum_t dS_t lat_t        dq_rope = scale sum_t dS_t kpos_t
+ *   dlat_t = sum_rows (scale dS_t q_abs + P_t dO)
+ *   dkpos_t = sum_rows scale dS_t q_rope
+ *
+ *   dtype        PA_BF16 or PA_F16 (this build: H = 16, rank 512, rope_dim 64)
+ *   q_abs, q_rope, latent, kpos, out, lse  as for pa_mla_fwd with the same
+ *                plan (out and lse: the forward's results)
+ *   dout         [Q, H, rank] output gradient
+ *   dq_abs       [Q, H, rank], dq_rope [Q, H, rope_dim], written
+ *   dlatent, dkpos  pools shaped like latent / kpos, written in full (rows no
+ *                visible key lands on are zero)
+ *   workspace    >= pa_plan_bwd_workspace_bytes(plan, dtype, rank, rope_dim)
+ *
+ * Pool rows have a single writer unless a page is shared (then f32 sums in
+ * the workspace, as pa_attention_bwd).  Errors as pa_attention_bwd; a GQA
+ * plan gives PA_ERR_INVALID.
+ */
+int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void* q_rope, const void* latent,
+               const void* kpos, const void* out, const float* lse, const void* dout, void* dq_abs, void* dq_rope,
+               void* dlatent, void* dkpos, int32_t rank, int32_t rope_dim, float scale, void* workspace,
+               size_t workspace_bytes, void* stream);
 
 /* Detail message of the calling thread's last failure ("" if none). */
 const char* pa_last_error(void);

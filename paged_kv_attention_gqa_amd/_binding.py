@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_INVALID", -2: "PA_ERR_SHAPE", -3: "PA_ER
 EXPORTED = ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
             "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv", "pa_status_string",
             "pa_last_error", "pa_plan_bwd_workspace_bytes", "pa_attention_bwd", "pa_attention_fwd_noalloc",
-            "pa_sparse_attention_fwd", "pa_sparse_workspace_bytes")
+            "pa_sparse_attention_fwd", "pa_sparse_workspace_bytes", "pa_mla_bwd")
 
 
 class PaError(RuntimeError):
@@ -76,6 +76,7 @@ def load_library():
     lib.pa_attention_fwd_noalloc.argtypes = [P, I, P, P, P, P, P, I, I, F, P]
     lib.pa_sparse_attention_fwd.argtypes = [P, I, P, P, P, P, P, I, I, F, I, I, P, P, S, P]
     lib.pa_sparse_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S), ctypes.POINTER(I)]
+    lib.pa_mla_bwd.argtypes = [P, I, P, P, P, P, P, P, P, P, P, P, P, I, I, F, P, S, P]
     lib.pa_mla_fwd.argtypes = [P, I, P, P, P, P, P, P, I, I, F, P, S, P, P]
     lib.pa_append_kv.argtypes = [P, I, P, P, P, P, I, I, P]
     lib.pa_plan_bwd_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S)]
@@ -87,7 +88,7 @@ def load_library():
     for n in ("pa_plan_create", "pa_plan_create_host", "pa_plan_get_work", "pa_plan_destroy", "pa_plan_get_info",
               "pa_plan_workspace_bytes", "pa_attention_fwd", "pa_mla_fwd", "pa_append_kv",
               "pa_plan_bwd_workspace_bytes", "pa_attention_bwd", "pa_attention_fwd_noalloc",
-            "pa_sparse_attention_fwd", "pa_sparse_workspace_bytes"):
+            "pa_sparse_attention_fwd", "pa_sparse_workspace_bytes", "pa_mla_bwd"):
         getattr(lib, n).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -394,6 +395,34 @@ def pa_attention_bwd(plan: Plan, q, k_pool, v_pool, out, lse, dout, dq, dk_pool,
         plan.handle, dt, _dev(q, "q", 3), _dev(k_pool, "k_pool", 4), _dev(v_pool, "v_pool", 4), _dev(out, "out", 3),
         _dev(lse, "lse", 2), _dev(dout, "dout", 3), _dev(dq, "dq", 3), _dev(dk_pool, "dk_pool", 4),
         _dev(dv_pool, "dv_pool", 4), D, Dv, float(scale), wp, wn, _stream_handle(stream)), "pa_attention_bwd")
+
+
+def pa_mla_bwd(plan: Plan, q_abs, q_rope, latent, kpos, out, lse, dout, dq_abs, dq_rope, dlatent, dkpos, *,
+               scale: float, workspace=None, stream=None) -> None:
+    """Absorbed-MLA backward into dq_abs, dq_rope, dlatent, dkpos (see
+    pa_mla_bwd in paged_attn.h); out and lse are the forward's."""
+    import torch
+    d = plan.desc
+    dt = _dtype_code(q_abs)
+    R, P = int(q_abs.shape[2]), int(q_rope.shape[2])
+    Q, H = d["num_queries"], d["num_q_heads"]
+    pool = (d["num_pages"], d["page_size"], 1)
+    for name, t, shape in (("q_abs", q_abs, (Q, H, R)), ("q_rope", q_rope, (Q, H, P)), ("out", out, (Q, H, R)),
+                           ("dout", dout, (Q, H, R)), ("dq_abs", dq_abs, (Q, H, R)), ("dq_rope", dq_rope, (Q, H, P)),
+                           ("latent", latent, pool + (R,)), ("kpos", kpos, pool + (P,)),
+                           ("dlatent", dlatent, pool + (R,)), ("dkpos", dkpos, pool + (P,))):
+        if t.dtype != q_abs.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q_abs dtype {q_abs.dtype}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {shape}")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Q, H):
+        raise ValueError("lse must be float32 [Q, H]")
+    wp, wn = _ws(workspace)
+    _check(load_library().pa_mla_bwd(
+        plan.handle, dt, _dev(q_abs, "q_abs", 3), _dev(q_rope, "q_rope", 3), _dev(latent, "latent", 4),
+        _dev(kpos, "kpos", 4), _dev(out, "out", 3), _dev(lse, "lse", 2), _dev(dout, "dout", 3),
+        _dev(dq_abs, "dq_abs", 3), _dev(dq_rope, "dq_rope", 3), _dev(dlatent, "dlatent", 4), _dev(dkpos, "dkpos", 4),
+        R, P, float(scale), wp, wn, _stream_handle(stream)), "pa_mla_bwd")
 
 
 def pa_mla_fwd(plan: Plan, q_abs, q_rope, latent, kpos, out, lse=None, *, scale: float, workspace=None,

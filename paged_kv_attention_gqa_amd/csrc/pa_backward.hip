@@ -40,6 +40,7 @@ struct BwdArgs {
   const BwdItem* items;
   float* acc_k;        // null: dK rows are stored (one writer each); else f32 sums shaped like dk
   float* acc_v;        // likewise for dV
+  void* dq2;           // MLA: dq_rope [Q, H, P] (dq is dq_abs, dk the latent pool, dv the rotary pool)
 };
 
 // One dK or dV element of a pool row: stored when every pool row has a
@@ -618,6 +619,254 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdAr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Absorbed-MLA backward (ruDNN 0.1.107 paged_attention `mla_backward` /
+// `mla_backward_into`), on 16-bit MFMA.  The latent is both key and value,
+// so its gradient receives the key term and the value term; the rotated
+// position cache and the position query receive the terms of their own dot
+// product.  With s = scale (q_abs . lat_t + q_rope . kpos_t), P = exp(s -
+// lse), dP_t = dO . lat_t, D = dO . O and dS = P (dP - D):
+//   dq_abs = scale sum_t dS_t lat_t     dq_rope = scale sum_t dS_t kpos_t
+//   dlat_t = sum_rows (scale dS_t q_abs + P_t dO)   dkpos_t = sum_rows scale dS_t q_rope
+// Four waves per workgroup split the 512 latent dims (128 each) and the 64
+// rotary dims (16 each) of every product; the partial score and dP tiles
+// of the waves meet in LDS and are summed in one fixed order, as in the
+// forward's split score tile.  LDS rows are padded by 16 bytes so that the
+// 16 rows one operand read touches fall in distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kMlaBwdWaves = 4;
+constexpr int kMlaLatRow = kMlaRank * 2 + 16;  // padded LDS bytes of a 512-wide row
+constexpr int kMlaPosRow = kMlaRope * 2 + 16;  // padded LDS bytes of a 64-wide row
+
+// Copy rows [0, 16) of a [16, WIDTH] 16-bit tile into LDS (padded rows of
+// ROW bytes); row r comes from src(r).
+template <int WIDTH, int ROW, typename Src>
+__device__ __forceinline__ void mla_tile_to_lds(char* dst, Src src) {
+  constexpr int PIECES = WIDTH / 8;  // 16-byte pieces per row
+  for (int idx = threadIdx.x; idx < 16 * PIECES; idx += kMlaBwdWaves * kWave) {
+    const int r = idx / PIECES, piece = idx % PIECES;
+    *reinterpret_cast<u32x4_t*>(dst + r * ROW + piece * 16) =
+        *reinterpret_cast<const u32x4_t*>(src(r) + piece * 8);
+  }
+}
+
+// dq_abs and dq_rope of one query (all 16 heads) over its visible keys
+// [tok_begin, tok_end), 16 keys per tile:
+//   S^T, dP^T [16 keys x 16 heads]    (partial over each wave's dims, summed)
+//   dq_abs^T [dims x heads] += lat^T . dS^T,  dq_rope^T += kpos^T . dS^T
+template <typename T>
+__global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dq_kernel(BwdArgs b, int first_item) {
+  constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = 16;
+  __shared__ __attribute__((aligned(16))) char lat_s[NT * kMlaLatRow];
+  __shared__ __attribute__((aligned(16))) char kp_s[NT * kMlaPosRow];
+  __shared__ floatx4_t xs[2][kMlaBwdWaves][kWave];
+  const KernelArgs& a = b.a;
+  const BwdItem it = b.items[first_item + blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = lane & 15, c = lane >> 4;
+  const int qi = it.q_begin, tb = it.tok_begin, te = it.tok_end;
+  const int ps = 1 << a.page_shift;
+  const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
+  const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.k);
+  const uint16_t* kpos = reinterpret_cast<const uint16_t*>(a.kr);
+
+  // this wave's operands: q_abs^T and dO^T over latent dims 128 wave .. +127
+  // (lane (n, c): head n, dims 32 k + 8 c), q_rope^T over rotary dims 16 wave ..
+  const uint64_t row = (uint64_t)qi * H + n;
+  frag_t qa[4], go[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d0 = 32 * (4 * wave + k) + 8 * c;
+    qa[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * R + d0);
+    go[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * R + d0);
+  }
+  const short4_t qr = *reinterpret_cast<const short4_t*>(reinterpret_cast<const uint16_t*>(a.qr) + row * P +
+                                                         16 * wave + 4 * c);
+  const float l2 = a.lse[row] * kLog2e, dl = b.delta[row];
+  const float c2 = a.scale_log2;
+
+  floatx4_t dqa[8], dqr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dqa[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = tb & ~(NT - 1); t0 < te; t0 += NT) {
+    auto slot_of = [&](int r) {
+      const int t = min(max(t0 + r, tb), te - 1);  // clamped keys are masked below
+      return (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+    };
+    mla_tile_to_lds<R, kMlaLatRow>(lat_s, [&](int r) { return lat + slot_of(r) * R; });
+    mla_tile_to_lds<P, kMlaPosRow>(kp_s, [&](int r) { return kpos + slot_of(r) * P; });
+    __syncthreads();
+    floatx4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const frag_t lf = *reinterpret_cast<const frag_t*>(lat_s + n * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2);
+      sc = mfma_16x16x32<T>(lf, qa[k], sc);
+      dp = mfma_16x16x32<T>(lf, go[k], dp);
+    }
+    sc = mfma_16x16x16<T>(*reinterpret_cast<const short4_t*>(kp_s + n * kMlaPosRow + (16 * wave + 4 * c) * 2), qr,
+                          sc);
+    xs[0][wave][lane] = sc;
+    xs[1][wave][lane] = dp;
+    __syncthreads();
+    sc = ((xs[0][0][lane] + xs[0][1][lane]) + xs[0][2][lane]) + xs[0][3][lane];
+    dp = ((xs[1][0][lane] + xs[1][1][lane]) + xs[1][2][lane]) + xs[1][3][lane];
+    // lane (n, c): keys t0 + 4 c + r of head n
+    float ds[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 4 * c + r;
+      const float p = (t >= tb && t < te) ? fast_exp2(__builtin_fmaf(sc[r], c2, -l2)) : 0.f;
+      ds[r] = p * (dp[r] - dl);
+    }
+    const short4_t dsf =
+        __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(ds[0], ds[1]), Pair16<T>::pack(ds[2], ds[3])));
+    // A = lat^T [16 dims x 16 keys] by transposed reads: lane 4 r + j of a
+    // 16-lane group gives dims .. + 4 j of key row 4 c + r
+    const int key = 4 * c + (n >> 2);
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const int dim = 128 * wave + 16 * blk + 4 * (n & 3);
+      dqa[blk] = mfma_16x16x16<T>(lds_read_tr16(lat_s + key * kMlaLatRow + dim * 2), dsf, dqa[blk]);
+    }
+    dqr = mfma_16x16x16<T>(lds_read_tr16(kp_s + key * kMlaPosRow + (16 * wave + 4 * (n & 3)) * 2), dsf, dqr);
+    __syncthreads();  // the tiles and the exchange are rewritten next
+  }
+
+  // lane (n, c) element e: dim (block base) + 4 c + e of head n
+  uint16_t* oa = reinterpret_cast<uint16_t*>(b.dq) + row * R + 128 * wave + 4 * c;
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) {
+    uint2 w;
+    w.x = Pair16<T>::pack(dqa[blk][0] * a.scale, dqa[blk][1] * a.scale);
+    w.y = Pair16<T>::pack(dqa[blk][2] * a.scale, dqa[blk][3] * a.scale);
+    *reinterpret_cast<uint2*>(oa + 16 * blk) = w;
+  }
+  uint2 w;
+  w.x = Pair16<T>::pack(dqr[0] * a.scale, dqr[1] * a.scale);
+  w.y = Pair16<T>::pack(dqr[2] * a.scale, dqr[3] * a.scale);
+  *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(b.dq2) + row * P + 16 * wave + 4 * c) = w;
+}
+
+// dlatent and dkpos of one block of up to kBwdBlockKeys keys, 16 keys at a
+// time, against the queries [q_begin, q_end) that see the block (each query
+// is one 16-row tile: its 16 heads):
+//   S, dP [16 heads x 16 keys]       (partial over each wave's dims, summed)
+//   dlat^T [dims x keys] += dO^T . P + scale q_abs^T . dS
+//   dkpos^T [dims x keys] += scale q_rope^T . dS
+template <typename T>
+__global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dkv_kernel(BwdArgs b, int first_item) {
+  constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = 16;
+  __shared__ __attribute__((aligned(16))) char lat_s[NT * kMlaLatRow];
+  __shared__ __attribute__((aligned(16))) char kp_s[NT * kMlaPosRow];
+  __shared__ __attribute__((aligned(16))) char qa_s[H * kMlaLatRow];
+  __shared__ __attribute__((aligned(16))) char go_s[H * kMlaLatRow];
+  __shared__ __attribute__((aligned(16))) char qr_s[H * kMlaPosRow];
+  __shared__ floatx4_t xs[2][kMlaBwdWaves][kWave];
+  __shared__ float l2s[H], dls[H];
+  const KernelArgs& a = b.a;
+  const BwdItem it = b.items[first_item + blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = lane & 15, c = lane >> 4;
+  const int ps = 1 << a.page_shift;
+  const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
+  const int L = a.seq_lens[it.seq];
+  const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.k);
+  const uint16_t* kpos = reinterpret_cast<const uint16_t*>(a.kr);
+  const float c2 = a.scale_log2;
+
+  for (int sub = it.tok_begin; sub < it.tok_end; sub += NT) {
+    const int te = min(it.tok_end, sub + NT);
+    auto slot_of = [&](int r) {
+      const int t = min(sub + r, te - 1);
+      return (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+    };
+    mla_tile_to_lds<R, kMlaLatRow>(lat_s, [&](int r) { return lat + slot_of(r) * R; });
+    mla_tile_to_lds<P, kMlaPosRow>(kp_s, [&](int r) { return kpos + slot_of(r) * P; });
+    __syncthreads();
+    // B operands of S = q_abs lat^T (+ q_rope kpos^T) and dP = dO lat^T:
+    // lane (n, c) holds key n's dims 32 k + 8 c (this wave's k-steps)
+    frag_t lb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      lb[k] = *reinterpret_cast<const frag_t*>(lat_s + n * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2);
+    const short4_t kb = *reinterpret_cast<const short4_t*>(kp_s + n * kMlaPosRow + (16 * wave + 4 * c) * 2);
+    const int t = sub + n;  // the key of this lane's accumulator column
+    floatx4_t dla[8], dkp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dla[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int qi = it.q_begin; qi < it.q_end; ++qi) {
+      const int pos = a.q_pos[qi];
+      const int hi = a.causal ? pos : L - 1;
+      const int lo = a.window > 0 ? max(0, pos - a.window + 1) : 0;
+      if (hi < sub || lo >= te) continue;  // this query sees no key of the 16
+      const uint64_t row0 = (uint64_t)qi * H;
+      __syncthreads();  // the previous query's tiles are no longer read
+      mla_tile_to_lds<R, kMlaLatRow>(qa_s, [&](int r) { return reinterpret_cast<const uint16_t*>(a.q) + (row0 + r) * R; });
+      mla_tile_to_lds<R, kMlaLatRow>(go_s,
+                                     [&](int r) { return reinterpret_cast<const uint16_t*>(b.dout) + (row0 + r) * R; });
+      mla_tile_to_lds<P, kMlaPosRow>(qr_s, [&](int r) { return reinterpret_cast<const uint16_t*>(a.qr) + (row0 + r) * P; });
+      if (tid < H) {
+        l2s[tid] = a.lse[row0 + tid] * kLog2e;
+        dls[tid] = b.delta[row0 + tid];
+      }
+      __syncthreads();
+      floatx4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int off = n * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2;
+        sc = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(qa_s + off), lb[k], sc);
+        dp = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(go_s + off), lb[k], dp);
+      }
+      sc = mfma_16x16x16<T>(*reinterpret_cast<const short4_t*>(qr_s + n * kMlaPosRow + (16 * wave + 4 * c) * 2), kb,
+                            sc);
+      xs[0][wave][lane] = sc;
+      xs[1][wave][lane] = dp;
+      __syncthreads();
+      sc = ((xs[0][0][lane] + xs[0][1][lane]) + xs[0][2][lane]) + xs[0][3][lane];
+      dp = ((xs[1][0][lane] + xs[1][1][lane]) + xs[1][2][lane]) + xs[1][3][lane];
+      // lane (n, c): heads 4 c + r of key t
+      const bool vis = t < te && t >= lo && t <= hi;
+      float pv[4], ds[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * c + r;
+        pv[r] = vis ? fast_exp2(__builtin_fmaf(sc[r], c2, -l2s[h])) : 0.f;
+        ds[r] = pv[r] * (dp[r] - dls[h]) * a.scale;
+      }
+      const short4_t pf =
+          __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(pv[0], pv[1]), Pair16<T>::pack(pv[2], pv[3])));
+      const short4_t dsf =
+          __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(ds[0], ds[1]), Pair16<T>::pack(ds[2], ds[3])));
+      // A = dO^T / q_abs^T [16 dims x 16 heads] by transposed reads: lane
+      // 4 r + j of a 16-lane group gives dims .. + 4 j of head row 4 c + r
+      const int head = 4 * c + (n >> 2);
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int off = head * kMlaLatRow + (128 * wave + 16 * blk + 4 * (n & 3)) * 2;
+        dla[blk] = mfma_16x16x16<T>(lds_read_tr16(go_s + off), pf, dla[blk]);
+        dla[blk] = mfma_16x16x16<T>(lds_read_tr16(qa_s + off), dsf, dla[blk]);
+      }
+      dkp = mfma_16x16x16<T>(lds_read_tr16(qr_s + head * kMlaPosRow + (16 * wave + 4 * (n & 3)) * 2), dsf, dkp);
+    }
+    // lane (n, c) element e: dim (block base) + 4 c + e of key sub + n
+    if (t < te) {
+      const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          put_grad<T>(b.dk, b.acc_k, slot * R + 128 * wave + 16 * blk + 4 * c + e, dla[blk][e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) put_grad<T>(b.dv, b.acc_v, slot * P + 16 * wave + 4 * c + e, dkp[e]);
+    }
+    __syncthreads();  // the key tiles are rewritten by the next 16 keys
+  }
+}
+
 namespace {
 
 using BwdFn = hipError_t (*)(const BwdArgs&, int, int, int, hipStream_t);
@@ -706,7 +955,7 @@ hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  BwdArgs b{a, dout, dq, dk, dvp, delta, items, acc_k, acc_v};
+  BwdArgs b{a, dout, dq, dk, dvp, delta, items, acc_k, acc_v, nullptr};
   if (rows > 0) {
     const unsigned grid = (unsigned)((rows + 3) / 4);
     if (dtype == 0)
@@ -731,6 +980,67 @@ hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, 
     else
       hipLaunchKernelGGL(bwd_cast_kernel<_Float16>, dim3((unsigned)grid), dim3(256), 0, stream, src, dst, n4);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+
+hipError_t launch_mla_bwd(int dtype, const KernelArgs& a, const void* dout, void* dq_abs, void* dq_rope, void* dlat,
+                          void* dkpos, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
+                          int64_t rows, int64_t pool_slots, int n_cu, hipStream_t stream) {
+  if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
+  constexpr int R = kMlaRank, P = kMlaRope;
+  float* acc_k = shared ? acc : nullptr;
+  float* acc_v = shared ? acc + pool_slots * R : nullptr;
+  // the gradient sums start at zero: rows no query sees keep it
+  for (int pass = 0; pass < 2; ++pass) {
+    void* base = pass == 0 ? (acc_k ? static_cast<void*>(acc_k) : dlat) : (acc_v ? static_cast<void*>(acc_v) : dkpos);
+    const int64_t chunks = pool_slots * (pass == 0 ? R : P) * (shared ? 4 : 2) / 16;
+    if (chunks == 0) continue;
+    const int64_t grid = std::min<int64_t>((chunks + 255) / 256, (int64_t)std::max(n_cu, 1) * 16);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)grid), dim3(256), 0, stream, reinterpret_cast<u32x4_t*>(base),
+                       chunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdArgs b{a, dout, dq_abs, dlat, dkpos, delta, items, acc_k, acc_v, dq_rope};
+  if (rows > 0) {
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+    if (dtype == 1)
+      hipLaunchKernelGGL(bwd_delta_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, b, rows, R);
+    else
+      hipLaunchKernelGGL(bwd_delta_kernel<_Float16>, dim3(grid), dim3(256), 0, stream, b, rows, R);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n_dq > 0) {
+    if (dtype == 1)
+      hipLaunchKernelGGL(mla_bwd_dq_kernel<uint16_t>, dim3(n_dq), dim3(kMlaBwdWaves * kWave), 0, stream, b, 0);
+    else
+      hipLaunchKernelGGL(mla_bwd_dq_kernel<_Float16>, dim3(n_dq), dim3(kMlaBwdWaves * kWave), 0, stream, b, 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n_kv > 0) {
+    if (dtype == 1)
+      hipLaunchKernelGGL(mla_bwd_dkv_kernel<uint16_t>, dim3(n_kv), dim3(kMlaBwdWaves * kWave), 0, stream, b, n_dq);
+    else
+      hipLaunchKernelGGL(mla_bwd_dkv_kernel<_Float16>, dim3(n_kv), dim3(kMlaBwdWaves * kWave), 0, stream, b, n_dq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!shared) return hipSuccess;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t n4 = pool_slots * (pass == 0 ? R : P) / 4;
+    const int64_t grid = std::min<int64_t>((n4 + 255) / 256, (int64_t)std::max(n_cu, 1) * 16);
+    const float4* src = reinterpret_cast<const float4*>(pass == 0 ? acc_k : acc_v);
+    uint2* dst = reinterpret_cast<uint2*>(pass == 0 ? dlat : dkpos);
+    if (dtype == 1)
+      hipLaunchKernelGGL(bwd_cast_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, src, dst, n4);
+    else
+      hipLaunchKernelGGL(bwd_cast_kernel<_Float16>, dim3((unsigned)grid), dim3(256), 0, stream, src, dst, n4);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

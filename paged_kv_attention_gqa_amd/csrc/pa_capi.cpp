@@ -446,7 +446,6 @@ void build_work(pa_plan* p) {
 // positions of one sequence only (else the launch adds the rows up in f32 and
 // shared_page names the first shared page).  The lists run longest first.
 void build_bwd(pa_plan* p) {
-  if (p->mla) return;
   std::vector<int32_t> owner(p->num_pages, -1);
   for (int s = 0; s < p->S && p->shared_page < 0; ++s) {
     const int pages = (p->seq_lens[s] + p->ps - 1) / p->ps;
@@ -469,7 +468,7 @@ void build_bwd(pa_plan* p) {
       visible_range(p->q_pos[i], L, p->causal, p->window, &lo, &hi);
       for (int kvh = 0; kvh < p->hkv; ++kvh) dq.push_back({hi + 1 - lo, pa::BwdItem{s, kvh, i, i + 1, lo, hi + 1}});
     }
-    for (int a0 = q0; a0 < q1; a0 += tile_q) {
+    for (int a0 = q0; a0 < q1 && !p->mla; a0 += tile_q) {  // MLA: per-query dQ items only
       const int a1 = std::min(q1, a0 + tile_q);
       int lo = INT32_MAX, hi = -1;
       for (int i = a0; i < a1; ++i) {
@@ -1010,7 +1009,7 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                      int32_t head_dim, int32_t v_head_dim, float scale, void* workspace, size_t workspace_bytes,
                      void* stream) {
   if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
-  if (plan->mla) return fail(PA_ERR_UNSUPPORTED, "this build has no MLA backward");
+  if (plan->mla) return fail(PA_ERR_INVALID, "plan was made for MLA (use pa_mla_bwd)");
   if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
   if (!k_pool || !v_pool || !dk_pool || !dv_pool)
     return fail(PA_ERR_INVALID, "k_pool, v_pool, dk_pool and dv_pool are required");
@@ -1068,6 +1067,74 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                                     bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv,
                                     plan->n_bwd_dqt, (int64_t)rows, (int64_t)slots, std::max(plan->n_cu, 1), st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
+int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void* q_rope, const void* latent,
+               const void* kpos, const void* out, const float* lse, const void* dout, void* dq_abs, void* dq_rope,
+               void* dlatent, void* dkpos, int32_t rank, int32_t rope_dim, float scale, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(PA_ERR_INVALID, "plan is NULL");
+  if (!plan->mla) return fail(PA_ERR_INVALID, "plan was made for GQA (use pa_attention_bwd)");
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16) return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!latent || !kpos || !dlatent || !dkpos)
+    return fail(PA_ERR_INVALID, "latent, kpos, dlatent and dkpos are required");
+  if (plan->Q > 0 && (!q_abs || !q_rope || !out || !lse || !dout || !dq_abs || !dq_rope))
+    return fail(PA_ERR_INVALID, "q_abs, q_rope, out, lse, dout, dq_abs and dq_rope are required when there are queries");
+  if (rank <= 0 || rank > 1024) return fail(PA_ERR_SHAPE, "latent rank %d outside [1, 1024]", rank);
+  if (rope_dim <= 0 || rope_dim > 256) return fail(PA_ERR_SHAPE, "rotary width rope_dim %d outside [1, 256]", rope_dim);
+  if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
+  if (!pa::mla_supported(dtype, plan->hq, rank, rope_dim))
+    return fail(PA_ERR_UNSUPPORTED, "no MLA backward kernel for dtype %d, H=%d, rank=%d, rope_dim=%d", dtype, plan->hq,
+                rank, rope_dim);
+  size_t need = 0;
+  pa_plan_bwd_workspace_bytes(plan, dtype, rank, rope_dim, &need);
+  if (need > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "MLA backward needs %zu bytes of workspace", need);
+    if (workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "MLA backward workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+      return fail(PA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  }
+  const size_t es = 2;
+  const size_t slots = (size_t)plan->num_pages * plan->ps;
+  const size_t rows = (size_t)plan->Q * plan->hq;
+  const Extent e_dqa{dq_abs, rows * rank * es, "dq_abs"}, e_dqr{dq_rope, rows * rope_dim * es, "dq_rope"};
+  const Extent e_dl{dlatent, slots * rank * es, "dlatent"}, e_dk{dkpos, slots * rope_dim * es, "dkpos"};
+  const Extent e_ws{workspace, need, "workspace"};
+  const Extent e_qa{q_abs, rows * rank * es, "q_abs"}, e_qr{q_rope, rows * rope_dim * es, "q_rope"};
+  const Extent e_l{latent, slots * rank * es, "latent"}, e_k{kpos, slots * rope_dim * es, "kpos"};
+  const Extent e_o{out, rows * rank * es, "out"}, e_lse{lse, rows * 4, "lse"}, e_do{dout, rows * rank * es, "dout"};
+  int rc = check_disjoint({e_dqa, e_dqr, e_dl, e_dk, e_ws}, {e_qa, e_qr, e_l, e_k, e_o, e_lse, e_do});
+  if (rc == PA_OK) rc = check_aligned({e_dqa, e_dqr, e_dl, e_dk, e_qa, e_qr, e_l, e_k, e_o, e_do});
+  if (rc != PA_OK) return rc;
+  rc = check_device(plan, stream);
+  if (rc != PA_OK) return rc;
+  pa::KernelArgs a{};
+  a.q = q_abs;
+  a.qr = q_rope;
+  a.k = latent;
+  a.v = latent;
+  a.kr = kpos;
+  a.out = const_cast<void*>(out);
+  a.lse = const_cast<float*>(lse);
+  a.block_table = plan->d_bt;
+  a.q_pos = plan->d_qpos;
+  a.seq_lens = plan->d_lens;
+  a.table_width = plan->W;
+  a.page_shift = plan->page_shift;
+  a.hq = plan->hq;
+  a.hkv = 1;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.causal = plan->causal;
+  a.window = plan->window;
+  hipError_t e = pa::launch_mla_bwd(dtype, a, dout, dq_abs, dq_rope, dlatent, dkpos,
+                                    reinterpret_cast<float*>(workspace),
+                                    reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(plan)),
+                                    bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv, (int64_t)rows,
+                                    (int64_t)slots, std::max(plan->n_cu, 1), reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "MLA backward launch");
   return ok();
 }
 

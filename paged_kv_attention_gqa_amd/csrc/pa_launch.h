@@ -65,6 +65,15 @@ hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* mer
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* slot_of,
                          int64_t queries, int heads, int k_row_bytes, int v_row_bytes, int n_cu, hipStream_t stream);
 
+// Absorbed-MLA backward (16-bit data, H = 16, R = 512, P = 64): zero the
+// latent / rotary gradient pools (or their f32 sums `acc`, pool_slots x (R +
+// P) floats, when pages are shared), D = dO . O, dq_abs / dq_rope over items
+// [0, n_dq) (one per query), dlatent / dkpos over [n_dq, n_dq + n_kv) (one
+// per block of keys), then the sums rounded into the pools.
+hipError_t launch_mla_bwd(int dtype, const KernelArgs& a, const void* dout, void* dq_abs, void* dq_rope, void* dlat,
+                          void* dkpos, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
+                          int64_t rows, int64_t pool_slots, int n_cu, hipStream_t stream);
+
 // Block-sparse top-k selection: one workgroup per (query, KV head) row
 // scores the row's candidate blocks, keeps `topk` of them (all when topk is
 // 0 or covers every candidate) and writes, at [row * width, + width), one
