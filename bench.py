@@ -365,11 +365,116 @@ def measure_backward(name, steps, warmup):
             "items": {"dq": info["bwd_dq_items"], "dkv": info["bwd_kv_items"]}}
 
 
+def measure_mla_backward(name, steps, warmup):
+    """Absorbed-MLA backward of workload `name` (pa_mla_bwd) after one
+    forward call, timed with HIP events around `steps` back-to-back calls.
+    Algorithmic flops per visible (query row, key) pair: 2 (R + P) scores,
+    2 R dP, 2 (R + P) dq, 2 R + 2 R for the latent's key and value terms and
+    2 P for the rotary cache: 10 R + 6 P."""
+    import torch
+    import paged_kv_attention_gqa_amd as pa
+    from synth import CONFIGS
+    from tests.gpu_harness import MlaRun
+
+    m = CONFIGS[name]()
+    f = MlaRun(m)
+    f()
+    rng = np.random.default_rng(1)
+    dout = torch.from_numpy(rng.standard_normal((m.num_queries, m.heads, m.r), dtype=np.float32)).to(
+        "cuda", dtype=torch.bfloat16)
+    dqa, dqr = torch.empty_like(f.q_abs), torch.empty_like(f.q_rope)
+    dlat, dkp = torch.empty_like(f.latent), torch.empty_like(f.kpos)
+    n = pa.pa_plan_bwd_workspace_bytes(f.plan, m.dtype, m.r, m.p)
+    ws = torch.empty(n // 4 + 64, dtype=torch.float32, device="cuda")
+
+    def call():
+        pa.pa_mla_bwd(f.plan, f.q_abs, f.q_rope, f.latent, f.kpos, f.out, f.lse, dout, dqa, dqr, dlat, dkp,
+                      scale=m.scale, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e6 + steps * 5e4))
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = int(visible_counts(m).sum()) * m.heads
+    flops = pairs * (10 * m.r + 6 * m.p)
+    del f, dqa, dqr, dlat, dkp, ws
+    torch.cuda.empty_cache()
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"mla_backward:{name}", "kernel_ms": round(ms, 5), "flops": flops, "bound": "mfma",
+            "tflops": round(tf, 2), "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+
+
+def measure_sparse(name, steps, warmup, block_size=64, topk=16):
+    """Block-sparse top-k attention of workload `name` (pa_sparse_attention_fwd:
+    selection, block attention, merge), timed with HIP events around `steps`
+    back-to-back calls.  Bytes: the proxy pass reads every visible K row once
+    per (query, KV head), the attention reads the K and V rows of the kept
+    blocks."""
+    import torch
+    import paged_kv_attention_gqa_amd as pa
+    from synth import CONFIGS
+    from tests.gpu_harness import GqaRun
+
+    b = CONFIGS[name]()
+    f = GqaRun(b, with_lse=False)
+    nbytes, width = pa.pa_sparse_workspace_bytes(f.plan, b.dv, block_size, topk)
+    ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
+    sel = torch.empty((b.num_queries, b.hkv, width), dtype=torch.int32, device="cuda")
+
+    def call():
+        pa.pa_sparse_attention_fwd(f.plan, f.q, f.k, f.v, f.out, None, scale=b.scale, block_size=block_size,
+                                   topk=topk, selection=sel, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e6 + steps * 5e4))
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    es = 2 if b.dtype != "f32" else 4
+    vis = visible_counts(b)
+    proxy_bytes = int(vis.sum()) * b.hkv * b.d * es
+    s = sel.cpu().numpy()
+    kept_keys = 0
+    for si in range(b.num_seqs):
+        for i in range(int(b.cu_q[si]), int(b.cu_q[si + 1])):
+            hi = int(b.q_pos[i]) if b.causal else int(b.seq_lens[si]) - 1
+            lo = max(0, int(b.q_pos[i]) - b.window + 1) if b.window > 0 else 0
+            for h in range(b.hkv):
+                for r in s[i, h]:
+                    if r >= 0:
+                        kept_keys += min(hi + 1, (int(r) + 1) * block_size) - max(lo, int(r) * block_size)
+    attn_bytes = kept_keys * (b.d + b.dv) * es
+    total = proxy_bytes + attn_bytes
+    del f, ws, sel
+    torch.cuda.empty_cache()
+    gbs = total / (ms * 1e-3) / 1e9
+    return {"workload": f"sparse_top{topk}_of_{block_size}:{name}", "ms_per_call": round(ms, 5),
+            "bytes": total, "proxy_bytes": proxy_bytes, "kept_kv_bytes": attn_bytes, "bound": "hbm",
+            "gbs": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 PRIMARY = "bf16_decode_batch"
 SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode", "bf16_mla_chunked_prefill",
              "bf16_chunked_prefill_d192")
 APPEND = ("bf16_decode_batch", "bf16_chunked_prefill")  # cache writes of one decode step and of one chunk
 BACKWARD = ("bf16_chunked_prefill",)  # gradients of one chunk step
+MLA_BACKWARD = ("bf16_mla_chunked_prefill",)
+SPARSE = ("bf16_decode_batch",)  # top-16 of 64-key blocks per decode row
 
 
 def run(args):
@@ -426,6 +531,10 @@ def run(args):
             result["secondary"].append(measure_append(n, args.steps, args.warmup))
         for n in BACKWARD:
             result["secondary"].append(measure_backward(n, args.steps, args.warmup))
+        for n in MLA_BACKWARD:
+            result["secondary"].append(measure_mla_backward(n, args.steps, args.warmup))
+        for n in SPARSE:
+            result["secondary"].append(measure_sparse(n, args.steps, args.warmup))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, mla, bytes_alg if hbm else flops_alg, hbm)
     return result

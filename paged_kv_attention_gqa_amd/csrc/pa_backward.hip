@@ -80,6 +80,20 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(u32x4_t* p, int64_t n) {
     p[i] = z;
 }
 
+// Zero the pool rows of the slot runs (first, count) no dK/dV item writes:
+// one workgroup per run, rows of k_row / v_row bytes (multiples of 16) in
+// the two gradient pools.
+__global__ __launch_bounds__(256) void bwd_zero_runs_kernel(char* dk, char* dv, const int32_t* runs, int k_row,
+                                                            int v_row) {
+  const int64_t first = runs[2 * blockIdx.x], count = runs[2 * blockIdx.x + 1];
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  const int64_t nk = count * k_row / 16, nv = count * v_row / 16;
+  u32x4_t* pk = reinterpret_cast<u32x4_t*>(dk + first * k_row);
+  u32x4_t* pv = reinterpret_cast<u32x4_t*>(dv + first * v_row);
+  for (int64_t i = threadIdx.x; i < nk; i += blockDim.x) pk[i] = z;
+  for (int64_t i = threadIdx.x; i < nv; i += blockDim.x) pv[i] = z;
+}
+
 // The f32 sums of shared-page gradients rounded into the 16-bit pool, four
 // elements per thread (grid-stride).
 template <typename T>
@@ -932,7 +946,8 @@ bool bwd_supported(int dtype, int d, int dv, int g) { return pick_bwd(dtype, d, 
 
 hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, const void* dout, void* dq, void* dk,
                           void* dvp, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
-                          int n_dqt, int64_t rows, int64_t pool_slots, int n_cu, hipStream_t stream) {
+                          int n_dqt, const int32_t* zero_runs, int n_zero_runs, int64_t rows, int64_t pool_slots,
+                          int n_cu, hipStream_t stream) {
   BwdFn f = pick_bwd(dtype, d, dv, g);
   if (!f) return hipErrorInvalidValue;
   const int es = dtype == 0 ? 4 : 2;
@@ -944,14 +959,23 @@ hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, 
     acc_k = dtype == 0 ? static_cast<float*>(dk) : acc;
     acc_v = dtype == 0 ? static_cast<float*>(dvp) : acc + pool_slots * d;
   }
-  // the gradient sums start at zero: rows no query sees keep it
-  for (int pass = 0; pass < 2; ++pass) {
-    void* base = pass == 0 ? (acc_k ? static_cast<void*>(acc_k) : dk) : (acc_v ? static_cast<void*>(acc_v) : dvp);
-    const int64_t chunks = pool_slots * (pass == 0 ? d : dv) * (acc_k ? 4 : es) / 16;
-    if (chunks == 0) continue;
-    const int64_t grid = std::min<int64_t>((chunks + 255) / 256, (int64_t)std::max(n_cu, 1) * 16);
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)grid), dim3(256), 0, stream, reinterpret_cast<u32x4_t*>(base),
-                       chunks);
+  if (shared) {
+    // the sums start at zero everywhere: several items add into a row
+    for (int pass = 0; pass < 2; ++pass) {
+      void* base = pass == 0 ? static_cast<void*>(acc_k) : static_cast<void*>(acc_v);
+      const int64_t chunks = pool_slots * (pass == 0 ? d : dv) * 4 / 16;
+      if (chunks == 0) continue;
+      const int64_t grid = std::min<int64_t>((chunks + 255) / 256, (int64_t)std::max(n_cu, 1) * 16);
+      hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                         reinterpret_cast<u32x4_t*>(base), chunks);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else if (n_zero_runs > 0) {
+    // single writer per row: only the rows no item writes are zeroed
+    const int hkv = a.hkv;
+    hipLaunchKernelGGL(bwd_zero_runs_kernel, dim3(n_zero_runs), dim3(256), 0, stream, static_cast<char*>(dk),
+                       static_cast<char*>(dvp), zero_runs, hkv * d * es, hkv * dv * es);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -988,19 +1012,28 @@ hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, 
 
 hipError_t launch_mla_bwd(int dtype, const KernelArgs& a, const void* dout, void* dq_abs, void* dq_rope, void* dlat,
                           void* dkpos, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
-                          int64_t rows, int64_t pool_slots, int n_cu, hipStream_t stream) {
+                          const int32_t* zero_runs, int n_zero_runs, int64_t rows, int64_t pool_slots, int n_cu,
+                          hipStream_t stream) {
   if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
   constexpr int R = kMlaRank, P = kMlaRope;
   float* acc_k = shared ? acc : nullptr;
   float* acc_v = shared ? acc + pool_slots * R : nullptr;
-  // the gradient sums start at zero: rows no query sees keep it
-  for (int pass = 0; pass < 2; ++pass) {
-    void* base = pass == 0 ? (acc_k ? static_cast<void*>(acc_k) : dlat) : (acc_v ? static_cast<void*>(acc_v) : dkpos);
-    const int64_t chunks = pool_slots * (pass == 0 ? R : P) * (shared ? 4 : 2) / 16;
-    if (chunks == 0) continue;
-    const int64_t grid = std::min<int64_t>((chunks + 255) / 256, (int64_t)std::max(n_cu, 1) * 16);
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)grid), dim3(256), 0, stream, reinterpret_cast<u32x4_t*>(base),
-                       chunks);
+  if (shared) {
+    // the f32 sums start at zero everywhere: several items add into a row
+    for (int pass = 0; pass < 2; ++pass) {
+      void* base = pass == 0 ? static_cast<void*>(acc_k) : static_cast<void*>(acc_v);
+      const int64_t chunks = pool_slots * (pass == 0 ? R : P) * 4 / 16;
+      if (chunks == 0) continue;
+      const int64_t grid = std::min<int64_t>((chunks + 255) / 256, (int64_t)std::max(n_cu, 1) * 16);
+      hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                         reinterpret_cast<u32x4_t*>(base), chunks);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else if (n_zero_runs > 0) {
+    // single writer per row: only the rows no item writes are zeroed
+    hipLaunchKernelGGL(bwd_zero_runs_kernel, dim3(n_zero_runs), dim3(256), 0, stream, static_cast<char*>(dlat),
+                       static_cast<char*>(dkpos), zero_runs, R * 2, P * 2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -98,6 +98,9 @@ struct pa_plan {
   // positions share (-1: none) makes the single-writer dK/dV pass impossible
   std::vector<pa::BwdItem> bwd_items;
   int32_t n_bwd_dq = 0, n_bwd_kv = 0, n_bwd_dqt = 0;
+  // backward, single-writer mode: runs (first pool slot, count) of the slots
+  // no dK/dV item writes, which are zeroed instead
+  std::vector<int32_t> zero_runs;
   int32_t shared_page = -1;
   // device copy: one allocation
   std::vector<char> blob;
@@ -111,6 +114,7 @@ struct pa_plan {
   const int32_t* d_seq_of = nullptr;
   const MergeItem* d_merges = nullptr;
   const pa::BwdItem* d_bwd = nullptr;
+  const int32_t* d_zero_runs = nullptr;
 
   int group() const { return hq / hkv; }
 };
@@ -510,6 +514,30 @@ void build_bwd(pa_plan* p) {
   p->n_bwd_dq = (int32_t)dq.size();
   p->n_bwd_kv = (int32_t)kv.size();
   p->n_bwd_dqt = (int32_t)dqt.size();
+  // Each dK/dV item writes every slot of its block (zero where no query sees
+  // the key); the other slots of the pools are zeroed by runs of at most
+  // kZeroRunSlots slots.
+  constexpr int kZeroRunSlots = 64;
+  const int64_t pool_slots = (int64_t)p->num_pages * p->ps;
+  std::vector<char> owned((size_t)pool_slots, 0);
+  for (const auto& x : kv) {
+    const pa::BwdItem& b = x.second;
+    if (b.kvh != 0) continue;  // the items of all KV heads cover the same slots
+    for (int t = b.tok_begin; t < b.tok_end; ++t)
+      owned[(size_t)p->bt[(size_t)b.seq * p->W + t / p->ps] * p->ps + t % p->ps] = 1;
+  }
+  p->zero_runs.clear();
+  for (int64_t i = 0; i < pool_slots;) {
+    if (owned[(size_t)i]) {
+      ++i;
+      continue;
+    }
+    int64_t j = i;
+    while (j < pool_slots && !owned[(size_t)j] && j - i < kZeroRunSlots) ++j;
+    p->zero_runs.push_back((int32_t)i);
+    p->zero_runs.push_back((int32_t)(j - i));
+    i = j;
+  }
 }
 
 // Workspace: partial sums [slots, G, Dv] | (max, sum, unrounded sum) [slots, G, 3].
@@ -666,7 +694,8 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   size_t off_slots = align_up(off_merges + p->merges.size() * sizeof(MergeItem), kAlign);
   size_t off_bwd = align_up(off_slots + p->slot_of.size() * 4, kAlign);
   size_t off_seq = align_up(off_bwd + p->bwd_items.size() * sizeof(pa::BwdItem), kAlign);
-  size_t total = align_up(off_seq + p->seq_of.size() * 4, kAlign);
+  size_t off_zr = align_up(off_seq + p->seq_of.size() * 4, kAlign);
+  size_t total = align_up(off_zr + p->zero_runs.size() * 4, kAlign);
   total = std::max(total, kAlign);
   p->blob.assign(total, 0);
   if (!p->bt.empty()) memcpy(p->blob.data() + off_bt, p->bt.data(), p->bt.size() * 4);
@@ -680,6 +709,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   if (!p->bwd_items.empty())
     memcpy(p->blob.data() + off_bwd, p->bwd_items.data(), p->bwd_items.size() * sizeof(pa::BwdItem));
   if (!p->seq_of.empty()) memcpy(p->blob.data() + off_seq, p->seq_of.data(), p->seq_of.size() * 4);
+  if (!p->zero_runs.empty()) memcpy(p->blob.data() + off_zr, p->zero_runs.data(), p->zero_runs.size() * 4);
 
   // stream-ordered allocation, upload and (in pa_plan_destroy) free: no call
   // of the plan's life waits for the device
@@ -709,6 +739,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   p->d_slot_of = reinterpret_cast<const int32_t*>(p->dev + off_slots);
   p->d_bwd = reinterpret_cast<const pa::BwdItem*>(p->dev + off_bwd);
   p->d_seq_of = reinterpret_cast<const int32_t*>(p->dev + off_seq);
+  p->d_zero_runs = reinterpret_cast<const int32_t*>(p->dev + off_zr);
   *out_plan = p;
   return ok();
 }
@@ -1065,7 +1096,8 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
                                     reinterpret_cast<float*>(workspace),
                                     reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(plan)),
                                     bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv,
-                                    plan->n_bwd_dqt, (int64_t)rows, (int64_t)slots, std::max(plan->n_cu, 1), st);
+                                    plan->n_bwd_dqt, plan->d_zero_runs, (int)(plan->zero_runs.size() / 2), (int64_t)rows,
+                                    (int64_t)slots, std::max(plan->n_cu, 1), st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }
@@ -1132,7 +1164,8 @@ int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   hipError_t e = pa::launch_mla_bwd(dtype, a, dout, dq_abs, dq_rope, dlatent, dkpos,
                                     reinterpret_cast<float*>(workspace),
                                     reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(plan)),
-                                    bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv, (int64_t)rows,
+                                    bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv, plan->d_zero_runs,
+                                    (int)(plan->zero_runs.size() / 2), (int64_t)rows,
                                     (int64_t)slots, std::max(plan->n_cu, 1), reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "MLA backward launch");
   return ok();

@@ -254,4 +254,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Workgroup barrier that leaves this wave's vector-memory operations in
+// flight.  __syncthreads() opens with a workgroup release fence, which on
+// gfx950 waits for every outstanding vector-memory operation (s_waitcnt
+// vmcnt(0)) -- the LDS-DMA loads of the tiles being prefetched included --
+// so a tile ring behind it keeps nothing in flight across the barrier.
+// Here only LDS operations are waited for (ds_write before the barrier is
+// visible after it); callers that publish LDS-DMA data wait for their own
+// loads with wait_vmcnt first.  The "memory" clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace pa

@@ -72,7 +72,8 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, voi
 // per block of keys), then the sums rounded into the pools.
 hipError_t launch_mla_bwd(int dtype, const KernelArgs& a, const void* dout, void* dq_abs, void* dq_rope, void* dlat,
                           void* dkpos, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
-                          int64_t rows, int64_t pool_slots, int n_cu, hipStream_t stream);
+                          const int32_t* zero_runs, int n_zero_runs, int64_t rows, int64_t pool_slots, int n_cu,
+                          hipStream_t stream);
 
 // Block-sparse top-k selection: one workgroup per (query, KV head) row
 // scores the row's candidate blocks, keeps `topk` of them (all when topk is
@@ -97,7 +98,9 @@ struct SparseArgs {
 };
 hipError_t launch_sparse_select(int dtype, const SparseArgs& a, int rows, hipStream_t stream);
 
-// Paged GQA/MHA backward: zero dk / dv (pool shaped, pool_slots rows of each),
+// Paged GQA/MHA backward: zero the dk / dv rows (pool shaped, pool_slots rows
+// of each) that no dK/dV item writes (zero_runs: n_zero_runs pairs (first
+// slot, count); with shared pages the whole f32 sums instead),
 // D = dO . O for the `rows` (query, head) rows into delta, then dQ (per-query
 // items [0, n_dq), or on MFMA the row tiles [n_dq + n_kv, + n_dqt)) and
 // dK / dV over items [n_dq, n_dq + n_kv).  `shared` (a pool page holds two
@@ -106,7 +109,8 @@ hipError_t launch_sparse_select(int dtype, const SparseArgs& a, int rows, hipStr
 bool bwd_supported(int dtype, int d, int dv, int g);
 hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, const void* dout, void* dq, void* dk,
                           void* dvp, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
-                          int n_dqt, int64_t rows, int64_t pool_slots, int n_cu, hipStream_t stream);
+                          int n_dqt, const int32_t* zero_runs, int n_zero_runs, int64_t rows, int64_t pool_slots,
+                          int n_cu, hipStream_t stream);
 
 
 }  // namespace pa

@@ -220,7 +220,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       wait_vmcnt<LOADS_PER_TILE>();
     else
       wait_vmcnt<0>();
-    __syncthreads();  // ... every wave's share has; tile j-1's stage is free for reuse
+    barrier_keep_loads();  // ... every wave's share has; tile j-1's stage is free for reuse
     if (j + kMlaStages - 1 < ntiles) {
       issue_tile(first + (j + kMlaStages - 1) * NT, smem + ((j + kMlaStages - 1) % kMlaStages) * MlaSmem::kStage,
                  page_next);
@@ -274,7 +274,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       lds_f4_t* xs = (lds_f4_t*)(size_t)__builtin_amdgcn_readfirstlane(
           (uint32_t)(size_t)(lds_void_t*)(smem + MlaSmem::kXchgOff));
       xs[wave * 64 + lane] = sc[0] + sc[1];
-      __syncthreads();
+      barrier_keep_loads();  // the exchange is written (the tiles in flight stay in flight)
       s = ((xs[lane] + xs[64 + lane]) + xs[128 + lane]) + xs[192 + lane];
     }
 #pragma unroll

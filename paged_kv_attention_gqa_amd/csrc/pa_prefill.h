@@ -421,7 +421,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   frag_t pf[NT / 16];
   auto sync = [&](int j) {
     wait_tiles(min(ntiles - 1 - j, 1));  // tile j has landed, j + 1 may be in flight
-    __syncthreads();                     // ... for every wave; tile j - 2 is no longer read
+    barrier_keep_loads();                // ... for every wave; tile j - 2 is no longer read
     if (j + NS - 2 < ntiles) {
       issue_tile(t_first + (j + NS - 2) * NT, smem + ((j + NS - 2) % NS) * STAGE, page_next);
       page_next = page_of(t_first + (j + NS - 1) * NT);
