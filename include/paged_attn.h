@@ -401,8 +401,8 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
  * own split settings are not used: each kept block is one split piece);
  * PA_ERR_SHAPE for a block size that is not a positive multiple of the page
  * size; PA_ERR_UNSUPPORTED for K rows that are not whole 16-byte pieces or
- * rows of more than 8192 blocks.  Three launches: selection, block
- * attention, merge.
+ * rows of more than 8192 blocks.  Four launches when topk > 0 (block
+ * scores, selection, block attention, merge), three when topk == 0.
  */
 int pa_sparse_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const void* k_pool,
                             const void* v_pool, void* out, float* lse, int32_t head_dim,

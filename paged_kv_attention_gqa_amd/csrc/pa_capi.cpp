@@ -13,6 +13,7 @@
 #include <initializer_list>
 #include <new>
 #include <string>
+#include <mutex>
 #include <vector>
 
 #include "paged_attn.h"
@@ -102,6 +103,14 @@ struct pa_plan {
   // no dK/dV item writes, which are zeroed instead
   std::vector<int32_t> zero_runs;
   int32_t shared_page = -1;
+  // The backward lists are built on first need (a backward call, its
+  // workspace size or pa_plan_get_info), so that forward-only plans do not
+  // pay for them; the device copy is uploaded by the first backward call.
+  std::mutex bwd_mu;
+  bool bwd_built = false;
+  std::vector<char> bwd_blob;
+  char* bwd_dev = nullptr;
+  hipEvent_t bwd_uploaded = nullptr;
   // device copy: one allocation
   std::vector<char> blob;
   char* dev = nullptr;
@@ -540,6 +549,51 @@ void build_bwd(pa_plan* p) {
   }
 }
 
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The backward lists of a plan, built once on the host (thread-safe: the
+// plan's lock).  The plan is logically const; the lists are a cache.
+void ensure_bwd_host(const pa_plan* cp) {
+  pa_plan* p = const_cast<pa_plan*>(cp);
+  std::lock_guard<std::mutex> lock(p->bwd_mu);
+  if (p->bwd_built) return;
+  build_bwd(p);
+  p->bwd_built = true;
+}
+
+// ... and their device copy, uploaded on the plan's stream by the first
+// backward call (ordered before that call's kernels; freed with the plan).
+int ensure_bwd_device(const pa_plan* cp) {
+  ensure_bwd_host(cp);
+  pa_plan* p = const_cast<pa_plan*>(cp);
+  std::lock_guard<std::mutex> lock(p->bwd_mu);
+  if (p->bwd_dev) return PA_OK;
+  const size_t off_zr = align_up(p->bwd_items.size() * sizeof(pa::BwdItem), kAlign);
+  const size_t total = std::max(align_up(off_zr + p->zero_runs.size() * 4, kAlign), kAlign);
+  p->bwd_blob.assign(total, 0);
+  if (!p->bwd_items.empty()) memcpy(p->bwd_blob.data(), p->bwd_items.data(), p->bwd_items.size() * sizeof(pa::BwdItem));
+  if (!p->zero_runs.empty()) memcpy(p->bwd_blob.data() + off_zr, p->zero_runs.data(), p->zero_runs.size() * 4);
+  char* dev = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&dev), total, p->created_on);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(backward lists)");
+  e = hipMemcpyAsync(dev, p->bwd_blob.data(), total, hipMemcpyHostToDevice, p->created_on);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->bwd_uploaded, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(p->bwd_uploaded, p->created_on);
+  if (e != hipSuccess) {
+    (void)hipStreamSynchronize(p->created_on);
+    (void)hipFreeAsync(dev, p->created_on);
+    if (p->bwd_uploaded) (void)hipEventDestroy(p->bwd_uploaded);
+    p->bwd_uploaded = nullptr;
+    return hip_fail(e, "backward list upload");
+  }
+  p->bwd_dev = dev;
+  p->d_bwd = reinterpret_cast<const pa::BwdItem*>(dev);
+  p->d_zero_runs = reinterpret_cast<const int32_t*>(dev + off_zr);
+  return PA_OK;
+}
+
 // Workspace: partial sums [slots, G, Dv] | (max, sum, unrounded sum) [slots, G, 3].
 size_t ws_o_bytes(const pa_plan* p, int dv) { return align_up((size_t)p->n_slots * p->group() * dv * 4, kAlign); }
 size_t ws_ml_bytes(const pa_plan* p) { return align_up((size_t)p->n_slots * p->group() * 3 * 4, kAlign); }
@@ -597,10 +651,6 @@ int check_device(const pa_plan* p, void* stream) {
 pa::MainEvents main_events_of(void* const* ev) {
   if (!ev) return {};
   return {reinterpret_cast<hipEvent_t>(ev[0]), reinterpret_cast<hipEvent_t>(ev[1])};
-}
-
-int hip_fail(hipError_t e, const char* what) {
-  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 // Common forward path once the kernel family is chosen.
@@ -682,9 +732,8 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
     return hip_fail(e, "device query");
   }
   build_work(p);
-  build_bwd(p);
 
-  // one blob: block table | q_pos | seq_lens | items | workgroup ranges | merges | append slots | backward items
+  // one blob: block table | q_pos | seq_lens | items | workgroup ranges | merges | append slots | query sequences
   size_t off_bt = 0;
   size_t off_qpos = align_up(off_bt + p->bt.size() * 4, kAlign);
   size_t off_lens = align_up(off_qpos + p->q_pos.size() * 4, kAlign);
@@ -692,10 +741,8 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   size_t off_wg = align_up(off_items + p->items.size() * sizeof(WorkItem), kAlign);
   size_t off_merges = align_up(off_wg + p->wg_first.size() * 4, kAlign);
   size_t off_slots = align_up(off_merges + p->merges.size() * sizeof(MergeItem), kAlign);
-  size_t off_bwd = align_up(off_slots + p->slot_of.size() * 4, kAlign);
-  size_t off_seq = align_up(off_bwd + p->bwd_items.size() * sizeof(pa::BwdItem), kAlign);
-  size_t off_zr = align_up(off_seq + p->seq_of.size() * 4, kAlign);
-  size_t total = align_up(off_zr + p->zero_runs.size() * 4, kAlign);
+  size_t off_seq = align_up(off_slots + p->slot_of.size() * 4, kAlign);
+  size_t total = align_up(off_seq + p->seq_of.size() * 4, kAlign);
   total = std::max(total, kAlign);
   p->blob.assign(total, 0);
   if (!p->bt.empty()) memcpy(p->blob.data() + off_bt, p->bt.data(), p->bt.size() * 4);
@@ -706,10 +753,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   if (!p->merges.empty())
     memcpy(p->blob.data() + off_merges, p->merges.data(), p->merges.size() * sizeof(MergeItem));
   if (!p->slot_of.empty()) memcpy(p->blob.data() + off_slots, p->slot_of.data(), p->slot_of.size() * 4);
-  if (!p->bwd_items.empty())
-    memcpy(p->blob.data() + off_bwd, p->bwd_items.data(), p->bwd_items.size() * sizeof(pa::BwdItem));
   if (!p->seq_of.empty()) memcpy(p->blob.data() + off_seq, p->seq_of.data(), p->seq_of.size() * 4);
-  if (!p->zero_runs.empty()) memcpy(p->blob.data() + off_zr, p->zero_runs.data(), p->zero_runs.size() * 4);
 
   // stream-ordered allocation, upload and (in pa_plan_destroy) free: no call
   // of the plan's life waits for the device
@@ -737,9 +781,7 @@ int pa_plan_create(const pa_plan_desc* desc, void* stream, pa_plan** out_plan) {
   p->d_wg_first = reinterpret_cast<const int32_t*>(p->dev + off_wg);
   p->d_merges = reinterpret_cast<const MergeItem*>(p->dev + off_merges);
   p->d_slot_of = reinterpret_cast<const int32_t*>(p->dev + off_slots);
-  p->d_bwd = reinterpret_cast<const pa::BwdItem*>(p->dev + off_bwd);
   p->d_seq_of = reinterpret_cast<const int32_t*>(p->dev + off_seq);
-  p->d_zero_runs = reinterpret_cast<const int32_t*>(p->dev + off_zr);
   *out_plan = p;
   return ok();
 }
@@ -753,7 +795,6 @@ int pa_plan_create_host(const pa_plan_desc* desc, int32_t num_cus, pa_plan** out
   if (!p) return fail(PA_ERR_HIP, "host allocation failed");
   p->n_cu = num_cus;
   build_work(p);
-  build_bwd(p);
   *out_plan = p;
   return ok();
 }
@@ -786,8 +827,14 @@ int pa_plan_destroy(pa_plan* plan) {
   (void)hipGetDevice(&prev);
   if (prev != plan->device) (void)hipSetDevice(plan->device);
   if (plan->uploaded) (void)hipEventSynchronize(plan->uploaded);
+  if (plan->bwd_uploaded) (void)hipEventSynchronize(plan->bwd_uploaded);
   hipError_t e = hipFreeAsync(plan->dev, plan->created_on);
+  if (plan->bwd_dev) {
+    const hipError_t e2 = hipFreeAsync(plan->bwd_dev, plan->created_on);
+    if (e == hipSuccess) e = e2;
+  }
   if (plan->uploaded) (void)hipEventDestroy(plan->uploaded);
+  if (plan->bwd_uploaded) (void)hipEventDestroy(plan->bwd_uploaded);
   if (prev >= 0 && prev != plan->device) (void)hipSetDevice(prev);
   delete plan;
   if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(plan)");
@@ -804,6 +851,7 @@ int pa_plan_get_info(const pa_plan* plan, pa_plan_info* info) {
   info->launches = plan->items.empty() ? 0 : (plan->merges.empty() ? 1 : 2);
   info->workgroups = plan->n_wg;
   info->heads_per_item = 1 << plan->heads_shift;
+  ensure_bwd_host(plan);
   info->bwd_dq_items = plan->n_bwd_dq;
   info->bwd_kv_items = plan->n_bwd_kv;
   info->bwd_shared_pages = plan->shared_page >= 0 ? 1 : 0;
@@ -1021,7 +1069,10 @@ static size_t bwd_delta_bytes(const pa_plan* plan) {
 
 // Some pool row takes dK / dV from two key positions (only matters when
 // there are queries).
-static bool bwd_shared(const pa_plan* plan) { return plan->shared_page >= 0 && plan->Q > 0; }
+static bool bwd_shared(const pa_plan* plan) {
+  ensure_bwd_host(plan);
+  return plan->shared_page >= 0 && plan->Q > 0;
+}
 
 int pa_plan_bwd_workspace_bytes(const pa_plan* plan, int32_t dtype, int32_t head_dim, int32_t v_head_dim,
                                 size_t* bytes) {
@@ -1073,6 +1124,8 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   if (rc == PA_OK) rc = check_aligned({e_dq, e_dk, e_dv, e_q, e_k, e_v, e_o, e_do});
   if (rc != PA_OK) return rc;
   rc = check_device(plan, stream);
+  if (rc != PA_OK) return rc;
+  rc = ensure_bwd_device(plan);
   if (rc != PA_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   pa::KernelArgs a{};
@@ -1142,6 +1195,8 @@ int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   if (rc != PA_OK) return rc;
   rc = check_device(plan, stream);
   if (rc != PA_OK) return rc;
+  rc = ensure_bwd_device(plan);
+  if (rc != PA_OK) return rc;
   pa::KernelArgs a{};
   a.q = q_abs;
   a.qr = q_rope;
@@ -1176,14 +1231,15 @@ int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
 // ---------------------------------------------------------------------------
 // Block-sparse top-k attention (alice-llm 2.0.0, sparse_attention/
 // llama3_bridge.rs, `llama3_sparse_attention`).  Workspace: decode items and
-// identity workgroup map [rows * width], merge records [rows], then split
-// partials of rows * width slots (rows = Q * Hkv, one slot per kept block).
+// identity workgroup map [rows * width], merge records [rows], split partials
+// of rows * width slots (rows = Q * Hkv, one slot per kept block), then (when
+// topk > 0) the candidate block scores [rows, widest row's candidates].
 // ---------------------------------------------------------------------------
 namespace {
 
 struct SparseLayout {
-  int32_t width = 0;
-  size_t off_items = 0, off_wg = 0, off_merges = 0, off_o = 0, off_ml = 0, total = 0;
+  int32_t width = 0, cand = 0, span = 0, spans = 0;
+  size_t off_items = 0, off_wg = 0, off_merges = 0, off_o = 0, off_ml = 0, off_scores = 0, total = 0;
 };
 
 int sparse_layout(const pa_plan* p, int dv, int block_size, int topk, SparseLayout* out) {
@@ -1192,26 +1248,35 @@ int sparse_layout(const pa_plan* p, int dv, int block_size, int topk, SparseLayo
     return fail(PA_ERR_SHAPE, "block_size %d must be a positive multiple of page_size %d", block_size, p->ps);
   if (topk < 0) return fail(PA_ERR_INVALID, "topk %d < 0", topk);
   if (dv <= 0 || dv > 1024) return fail(PA_ERR_SHAPE, "v_head_dim %d outside [1, 1024]", dv);
-  int32_t most = 0;  // candidate blocks of the widest row
+  const int span = pa::sparse_span(block_size);
+  int32_t most = 0, spans = 0;  // candidate blocks and scoring spans of the widest row
   for (int s = 0; s < p->S; ++s)
     for (int i = p->cu_q[s]; i < p->cu_q[s + 1]; ++i) {
       int lo, hi;
       visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &lo, &hi);
       most = std::max(most, hi / block_size - lo / block_size + 1);
+      spans = std::max(spans, hi / span - lo / span + 1);
     }
   if (most > pa::kSparseMaxBlocks)
     return fail(PA_ERR_UNSUPPORTED, "a row spans %d blocks of %d keys; the selection holds at most %d", most,
                 block_size, pa::kSparseMaxBlocks);
   SparseLayout L;
   L.width = topk > 0 ? topk : std::max(most, 1);
+  L.cand = std::max(most, 1);
+  L.span = span;
+  L.spans = std::max(spans, 1);
   const size_t rows = (size_t)p->Q * p->hkv, slots = rows * L.width;
   if (slots > (size_t)INT32_MAX) return fail(PA_ERR_RANGE, "rows x kept blocks exceed 32-bit indexing");
+  if (L.spans > 65535) return fail(PA_ERR_UNSUPPORTED, "a row spans %d scoring spans of %d keys", L.spans, span);
   L.off_items = 0;
   L.off_wg = align_up(slots * sizeof(WorkItem), kAlign);
   L.off_merges = align_up(L.off_wg + (slots + 1) * 4, kAlign);
   L.off_o = align_up(L.off_merges + rows * sizeof(MergeItem), kAlign);
   L.off_ml = align_up(L.off_o + slots * p->group() * dv * 4, kAlign);
-  L.total = p->Q > 0 ? align_up(L.off_ml + slots * p->group() * 3 * 4, kAlign) : 0;
+  // block scores only when some blocks are dropped
+  L.off_scores = align_up(L.off_ml + slots * p->group() * 3 * 4, kAlign);
+  const size_t score_bytes = topk > 0 ? rows * L.cand * 4 : 0;
+  L.total = p->Q > 0 ? align_up(L.off_scores + score_bytes, kAlign) : 0;
   *out = L;
   return PA_OK;
 }
@@ -1297,6 +1362,10 @@ int pa_sparse_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, c
   sa.items = reinterpret_cast<WorkItem*>(ws + L.off_items);
   sa.wg_first = reinterpret_cast<int32_t*>(ws + L.off_wg);
   sa.merges = reinterpret_cast<MergeItem*>(ws + L.off_merges);
+  sa.scores = reinterpret_cast<uint32_t*>(ws + L.off_scores);
+  sa.cand_width = L.cand;
+  sa.span = L.span;
+  sa.spans = L.spans;
   hipError_t e = pa::launch_sparse_select(dtype, sa, (int)rows, st);
   if (e != hipSuccess) return hip_fail(e, "block selection launch");
 

@@ -95,7 +95,13 @@ struct SparseArgs {
   WorkItem* items;     // [Q * Hkv * width]
   int32_t* wg_first;   // [Q * Hkv * width + 1]
   MergeItem* merges;   // [Q * Hkv]
+  uint32_t* scores;    // [Q * Hkv, cand_width] order-mapped block scores of the candidates
+  int32_t cand_width;  // candidate blocks of the widest row
+  int32_t span;        // keys per scoring workgroup: a multiple of block_size, aligned to itself
+  int32_t spans;       // scoring workgroups per row (the widest row's span count)
 };
+// Keys one scoring workgroup covers for blocks of `block_size` keys.
+inline int sparse_span(int block_size) { return block_size * (block_size >= 1024 ? 1 : 1024 / block_size); }
 hipError_t launch_sparse_select(int dtype, const SparseArgs& a, int rows, hipStream_t stream);
 
 // Paged GQA/MHA backward: zero the dk / dv rows (pool shaped, pool_slots rows

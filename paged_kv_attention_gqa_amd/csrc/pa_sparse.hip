@@ -11,8 +11,17 @@
 // The proxy score of a key is the f32 product sum in increasing dimension
 // order, one fused multiply-add per dimension (for 16-bit data the products
 // are exact in f32), so that the choice is reproducible bit for bit; a tie
-// goes to the lower block index.  The selection runs once per row and reads
-// only K; it is not on the dense path.
+// goes to the lower block index.
+//
+// Two kernels.  sparse_scores_kernel streams K: one workgroup per row and
+// span of keys (a whole number of blocks), each wave 64 keys at a time.  The
+// wave reads the keys' rows in 16-byte pieces with consecutive lanes on
+// consecutive pieces of a row (coalesced), parks them in LDS with one spare
+// piece per key row, and then each lane runs its own key's product sum over
+// its row in LDS (the spare piece puts 16 consecutive keys' pieces in 16
+// different bank groups).  Block maxima go through LDS to the row's score
+// buffer.  sparse_topk_kernel then picks the kept blocks of each row and
+// writes the work list.
 #include <hip/hip_runtime.h>
 
 #include "pa_launch.h"
@@ -57,10 +66,126 @@ __device__ __forceinline__ uint64_t wg_max(uint64_t v, uint64_t* red) {
   return m;
 }
 
+constexpr int kPieces = 8;  // 16-byte pieces of a key row per pass (a longer row takes several passes)
+
 template <typename T>
-__global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseArgs a) {
-  __shared__ uint32_t score[kSparseMaxBlocks];
+__global__ __launch_bounds__(kSelThreads) void sparse_scores_kernel(SparseArgs a) {
+  __shared__ uint4 stage[kSelThreads / kWave][kWave * (kPieces + 1)];
   __shared__ float qp[kSparseMaxDim];
+  __shared__ uint32_t bmax[1024];
+
+  const int row = blockIdx.x;  // query * hkv + KV head
+  const int i = row / a.hkv, h = row % a.hkv;
+  const int s = a.seq_of[i];
+  const int L = a.seq_lens[s], p = a.q_pos[i];
+  const int hi = a.causal ? p : L - 1;
+  const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+  const int B = a.block_size;
+  const int r0 = lo / B, ncand = hi / B - r0 + 1;
+  if (a.topk == 0 || a.topk >= ncand) return;  // every block kept: nothing to score
+  const int SPAN = a.span;
+  const int ks0 = (lo / SPAN + (int)blockIdx.y) * SPAN;  // this workgroup's keys [ks0, ks0 + SPAN)
+  if (ks0 > hi) return;
+  const int ks_lo = max(ks0, lo), ks_hi = min(ks0 + SPAN - 1, hi);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nb = SPAN / B;
+
+  const T* q = reinterpret_cast<const T*>(a.q) + ((uint64_t)i * a.hq + (uint64_t)h * (a.hq / a.hkv)) * a.d;
+  for (int c = tid; c < a.d; c += kSelThreads) qp[c] = widen(q, c);
+  for (int j = tid; j < nb; j += kSelThreads) bmax[j] = 0u;
+  __syncthreads();
+
+  constexpr int EPP = 16 / (int)sizeof(T);  // elements per piece
+  const int P = a.d / EPP;                  // pieces per key row
+  const uint64_t row_bytes = (uint64_t)a.d * sizeof(T);
+  const char* kbase = reinterpret_cast<const char*>(a.k) + (uint64_t)h * row_bytes;
+  const int32_t* bt = a.block_table + (size_t)s * a.table_width;
+  const int ps = 1 << a.page_shift;
+  uint4* st = stage[wave];
+  for (int base = ks0 + kWave * wave; base <= ks_hi; base += kSelThreads) {
+    if (base + kWave - 1 < ks_lo) continue;
+    const int t = base + lane;
+    const bool valid = t >= ks_lo && t <= ks_hi;
+    const int tc = min(max(t, ks_lo), ks_hi);  // out-of-range lanes read an in-range key
+    const uint64_t slot = (uint64_t)bt[tc >> a.page_shift] * ps + (tc & (ps - 1));
+    const uint64_t my_off = slot * a.hkv * row_bytes;  // this lane's key row (KV head offset in kbase)
+    float acc = 0.f;
+    // one pass: np pieces of the 64 key rows from piece c0 on; the loads are
+    // coalesced (piece j * 64 + lane of the 64 x np block is piece (.. % np)
+    // of key (.. / np)), parked in LDS, then each lane runs its own key's
+    // pieces in dimension order
+    // LDS index and source of piece j * 64 + lane of a pass
+    auto piece_dst = [&](int j, int np) {
+      const int qi = j * kWave + lane, key = qi / np;
+      return key * (kPieces + 1) + (qi - key * np);
+    };
+    auto piece_src = [&](int j, int np, int c0) {
+      const int qi = j * kWave + lane, key = qi / np;
+      const uint32_t lo32 = __shfl((uint32_t)my_off, key), hi32 = __shfl((uint32_t)(my_off >> 32), key);
+      return *reinterpret_cast<const uint4*>(kbase + (((uint64_t)hi32 << 32) | lo32) +
+                                             (uint64_t)(c0 + qi - key * np) * 16);
+    };
+    auto dot = [&](int np, int c0) {
+      // other lanes' pieces: keep the reads after the writes (a wave's LDS
+      // accesses complete in order) and the next pass's writes after them
+      asm volatile("" ::: "memory");
+      for (int pc = 0; pc < np; ++pc) {
+        const uint4 w = st[lane * (kPieces + 1) + pc];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        const float* qq = qp + (c0 + pc) * EPP;
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(qq[e], __uint_as_float(ws[e]), acc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc = __builtin_fmaf(qq[2 * e], Pair16<T>::lo(ws[e]), acc);
+            acc = __builtin_fmaf(qq[2 * e + 1], Pair16<T>::hi(ws[e]), acc);
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+    };
+    int c0 = 0;
+    for (; c0 + kPieces <= P; c0 += kPieces) {  // full passes: all loads in flight together
+      uint4 v[kPieces];
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) v[j] = piece_src(j, kPieces, c0);
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) st[piece_dst(j, kPieces)] = v[j];
+      dot(kPieces, c0);
+    }
+    if (c0 < P) {  // the row's last pieces
+      const int np = P - c0;
+      for (int j = 0; j < np; ++j) {
+        const uint4 v = piece_src(j, np, c0);
+        st[piece_dst(j, np)] = v;
+      }
+      dot(np, c0);
+    }
+    const uint32_t key = valid ? ordered(acc) : 0u;
+    if (B % kWave == 0) {
+      // the 64 keys (aligned to 64) lie in one block: one wave maximum
+      uint32_t m = key;
+#pragma unroll
+      for (int sh = 1; sh < kWave; sh <<= 1) m = max(m, (uint32_t)__shfl_xor(m, sh));
+      if (lane == 0) atomicMax(&bmax[(base - ks0) / B], m);
+    } else if (valid) {
+      atomicMax(&bmax[(t - ks0) / B], key);
+    }
+  }
+  __syncthreads();
+  // the span's candidate blocks (each has a visible key, so a score above 0)
+  uint32_t* out = a.scores + (size_t)row * a.cand_width;
+  for (int j = tid; j < nb; j += kSelThreads) {
+    const int gb = ks0 / B + j;
+    if (gb >= r0 && gb < r0 + ncand) out[gb - r0] = bmax[j];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSelThreads) void sparse_topk_kernel(SparseArgs a) {
+  __shared__ uint32_t score[kSparseMaxBlocks];
   __shared__ uint64_t red[kSelThreads / kWave];
   __shared__ int32_t wave_count[kSelThreads / kWave];
 
@@ -77,35 +202,8 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseArgs a
   const int tid = threadIdx.x;
 
   if (!all) {
-    // proxy query: the first query head of the group, widened to f32
-    const T* q = reinterpret_cast<const T*>(a.q) + ((uint64_t)i * a.hq + (uint64_t)h * (a.hq / a.hkv)) * a.d;
-    for (int c = tid; c < a.d; c += kSelThreads) qp[c] = widen(q, c);
-    for (int r = tid; r < ncand; r += kSelThreads) score[r] = ordered(-INFINITY);
-    __syncthreads();
-    // one thread per visible key: the sequential f32 product sum, then the
-    // block maximum by an order-preserving atomic max
-    const int32_t* bt = a.block_table + (size_t)s * a.table_width;
-    const int ps = 1 << a.page_shift;
-    for (int t = lo + tid; t <= hi; t += kSelThreads) {
-      const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
-      const T* krow = reinterpret_cast<const T*>(a.k) + (slot * a.hkv + h) * a.d;
-      float acc = 0.f;
-      for (int c0 = 0; c0 < a.d; c0 += 16 / (int)sizeof(T)) {
-        const uint4 w = *reinterpret_cast<const uint4*>(krow + c0);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        if constexpr (sizeof(T) == 4) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(qp[c0 + e], __uint_as_float(ws[e]), acc);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc = __builtin_fmaf(qp[c0 + 2 * e], Pair16<T>::lo(ws[e]), acc);
-            acc = __builtin_fmaf(qp[c0 + 2 * e + 1], Pair16<T>::hi(ws[e]), acc);
-          }
-        }
-      }
-      atomicMax(&score[t / B - r0], ordered(acc));
-    }
+    const uint32_t* sc = a.scores + (size_t)row * a.cand_width;
+    for (int r = tid; r < ncand; r += kSelThreads) score[r] = sc[r];
     __syncthreads();
     // keep rounds: the best untaken block (a tie to the lower index) is
     // marked taken (0)
@@ -158,17 +256,24 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseArgs a
 
 }  // namespace
 
+template <typename T>
+hipError_t launch_select_t(const SparseArgs& a, int rows, hipStream_t stream) {
+  if (a.topk > 0) {
+    hipLaunchKernelGGL(sparse_scores_kernel<T>, dim3(rows, a.spans), dim3(kSelThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(sparse_topk_kernel<T>, dim3(rows), dim3(kSelThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_select(int dtype, const SparseArgs& a, int rows, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (dtype == 0)
-    hipLaunchKernelGGL(sparse_select_kernel<float>, dim3(rows), dim3(kSelThreads), 0, stream, a);
-  else if (dtype == 1)
-    hipLaunchKernelGGL(sparse_select_kernel<uint16_t>, dim3(rows), dim3(kSelThreads), 0, stream, a);
-  else if (dtype == 2)
-    hipLaunchKernelGGL(sparse_select_kernel<_Float16>, dim3(rows), dim3(kSelThreads), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (a.span > 1024 * a.block_size || a.span / a.block_size > 1024) return hipErrorInvalidValue;
+  if (dtype == 0) return launch_select_t<float>(a, rows, stream);
+  if (dtype == 1) return launch_select_t<uint16_t>(a, rows, stream);
+  if (dtype == 2) return launch_select_t<_Float16>(a, rows, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa
