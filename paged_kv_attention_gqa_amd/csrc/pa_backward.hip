@@ -652,12 +652,12 @@ constexpr int kMlaBwdWaves = 4;
 constexpr int kMlaLatRow = kMlaRank * 2 + 16;  // padded LDS bytes of a 512-wide row
 constexpr int kMlaPosRow = kMlaRope * 2 + 16;  // padded LDS bytes of a 64-wide row
 
-// Copy rows [0, 16) of a [16, WIDTH] 16-bit tile into LDS (padded rows of
-// ROW bytes); row r comes from src(r).
-template <int WIDTH, int ROW, typename Src>
+// Copy rows [0, ROWS) of a [ROWS, WIDTH] 16-bit tile into LDS (padded rows
+// of ROW bytes); row r comes from src(r).
+template <int WIDTH, int ROW, int ROWS = 16, typename Src>
 __device__ __forceinline__ void mla_tile_to_lds(char* dst, Src src) {
   constexpr int PIECES = WIDTH / 8;  // 16-byte pieces per row
-  for (int idx = threadIdx.x; idx < 16 * PIECES; idx += kMlaBwdWaves * kWave) {
+  for (int idx = threadIdx.x; idx < ROWS * PIECES; idx += kMlaBwdWaves * kWave) {
     const int r = idx / PIECES, piece = idx % PIECES;
     *reinterpret_cast<u32x4_t*>(dst + r * ROW + piece * 16) =
         *reinterpret_cast<const u32x4_t*>(src(r) + piece * 8);
@@ -763,21 +763,23 @@ __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dq_kernel(BwdArgs
   *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(b.dq2) + row * P + 16 * wave + 4 * c) = w;
 }
 
-// dlatent and dkpos of one block of up to kBwdBlockKeys keys, 16 keys at a
-// time, against the queries [q_begin, q_end) that see the block (each query
-// is one 16-row tile: its 16 heads):
-//   S, dP [16 heads x 16 keys]       (partial over each wave's dims, summed)
+// dlatent and dkpos of one block of up to kBwdBlockKeys keys, 64 keys (four
+// 16-key tiles) at a time, against the queries [q_begin, q_end) that see
+// them (each query is one 16-row tile: its 16 heads); a query's operand
+// tiles are loaded once for the 64 keys:
+//   S, dP [16 heads x 16 keys] per key tile (partial over each wave's dims,
+//   summed)
 //   dlat^T [dims x keys] += dO^T . P + scale q_abs^T . dS
 //   dkpos^T [dims x keys] += scale q_rope^T . dS
 template <typename T>
 __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dkv_kernel(BwdArgs b, int first_item) {
-  constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = 16;
-  __shared__ __attribute__((aligned(16))) char lat_s[NT * kMlaLatRow];
-  __shared__ __attribute__((aligned(16))) char kp_s[NT * kMlaPosRow];
+  constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = 16, KT = 4;
+  __shared__ __attribute__((aligned(16))) char lat_s[KT * NT * kMlaLatRow];
+  __shared__ __attribute__((aligned(16))) char kp_s[KT * NT * kMlaPosRow];
   __shared__ __attribute__((aligned(16))) char qa_s[H * kMlaLatRow];
   __shared__ __attribute__((aligned(16))) char go_s[H * kMlaLatRow];
   __shared__ __attribute__((aligned(16))) char qr_s[H * kMlaPosRow];
-  __shared__ floatx4_t xs[2][kMlaBwdWaves][kWave];
+  __shared__ floatx4_t xs[2][KT][kMlaBwdWaves][kWave];
   __shared__ float l2s[H], dls[H];
   const KernelArgs& a = b.a;
   const BwdItem it = b.items[first_item + blockIdx.x];
@@ -791,34 +793,41 @@ __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dkv_kernel(BwdArg
   const uint16_t* kpos = reinterpret_cast<const uint16_t*>(a.kr);
   const float c2 = a.scale_log2;
 
-  for (int sub = it.tok_begin; sub < it.tok_end; sub += NT) {
-    const int te = min(it.tok_end, sub + NT);
+  for (int sub = it.tok_begin; sub < it.tok_end; sub += KT * NT) {
+    const int te = min(it.tok_end, sub + KT * NT);
     auto slot_of = [&](int r) {
       const int t = min(sub + r, te - 1);
       return (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
     };
-    mla_tile_to_lds<R, kMlaLatRow>(lat_s, [&](int r) { return lat + slot_of(r) * R; });
-    mla_tile_to_lds<P, kMlaPosRow>(kp_s, [&](int r) { return kpos + slot_of(r) * P; });
+    mla_tile_to_lds<R, kMlaLatRow, KT * NT>(lat_s, [&](int r) { return lat + slot_of(r) * R; });
+    mla_tile_to_lds<P, kMlaPosRow, KT * NT>(kp_s, [&](int r) { return kpos + slot_of(r) * P; });
     __syncthreads();
     // B operands of S = q_abs lat^T (+ q_rope kpos^T) and dP = dO lat^T:
-    // lane (n, c) holds key n's dims 32 k + 8 c (this wave's k-steps)
-    frag_t lb[4];
+    // lane (n, c) holds key 16 kt + n's dims 32 k + 8 c (this wave's k-steps)
+    frag_t lb[KT][4];
+    short4_t kb[KT];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      lb[k] = *reinterpret_cast<const frag_t*>(lat_s + n * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2);
-    const short4_t kb = *reinterpret_cast<const short4_t*>(kp_s + n * kMlaPosRow + (16 * wave + 4 * c) * 2);
-    const int t = sub + n;  // the key of this lane's accumulator column
-    floatx4_t dla[8], dkp = {0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dla[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < 4; ++k)
+        lb[kt][k] = *reinterpret_cast<const frag_t*>(lat_s + (NT * kt + n) * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2);
+      kb[kt] = *reinterpret_cast<const short4_t*>(kp_s + (NT * kt + n) * kMlaPosRow + (16 * wave + 4 * c) * 2);
+    }
+    floatx4_t dla[KT][8], dkp[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      dkp[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dla[kt][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     for (int qi = it.q_begin; qi < it.q_end; ++qi) {
       const int pos = a.q_pos[qi];
       const int hi = a.causal ? pos : L - 1;
       const int lo = a.window > 0 ? max(0, pos - a.window + 1) : 0;
-      if (hi < sub || lo >= te) continue;  // this query sees no key of the 16
+      if (hi < sub || lo >= te) continue;  // this query sees none of the keys
       const uint64_t row0 = (uint64_t)qi * H;
-      __syncthreads();  // the previous query's tiles are no longer read
+      __syncthreads();  // the previous query's tiles and partials are no longer read
       mla_tile_to_lds<R, kMlaLatRow>(qa_s, [&](int r) { return reinterpret_cast<const uint16_t*>(a.q) + (row0 + r) * R; });
       mla_tile_to_lds<R, kMlaLatRow>(go_s,
                                      [&](int r) { return reinterpret_cast<const uint16_t*>(b.dout) + (row0 + r) * R; });
@@ -828,56 +837,69 @@ __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dkv_kernel(BwdArg
         dls[tid] = b.delta[row0 + tid];
       }
       __syncthreads();
-      floatx4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      // this wave's partial S and dP of every key tile
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int off = n * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2;
-        sc = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(qa_s + off), lb[k], sc);
-        dp = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(go_s + off), lb[k], dp);
+      for (int kt = 0; kt < KT; ++kt) {
+        floatx4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int off = n * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2;
+          sc = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(qa_s + off), lb[kt][k], sc);
+          dp = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(go_s + off), lb[kt][k], dp);
+        }
+        sc = mfma_16x16x16<T>(*reinterpret_cast<const short4_t*>(qr_s + n * kMlaPosRow + (16 * wave + 4 * c) * 2),
+                              kb[kt], sc);
+        xs[0][kt][wave][lane] = sc;
+        xs[1][kt][wave][lane] = dp;
       }
-      sc = mfma_16x16x16<T>(*reinterpret_cast<const short4_t*>(qr_s + n * kMlaPosRow + (16 * wave + 4 * c) * 2), kb,
-                            sc);
-      xs[0][wave][lane] = sc;
-      xs[1][wave][lane] = dp;
       __syncthreads();
-      sc = ((xs[0][0][lane] + xs[0][1][lane]) + xs[0][2][lane]) + xs[0][3][lane];
-      dp = ((xs[1][0][lane] + xs[1][1][lane]) + xs[1][2][lane]) + xs[1][3][lane];
-      // lane (n, c): heads 4 c + r of key t
-      const bool vis = t < te && t >= lo && t <= hi;
-      float pv[4], ds[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * c + r;
-        pv[r] = vis ? fast_exp2(__builtin_fmaf(sc[r], c2, -l2s[h])) : 0.f;
-        ds[r] = pv[r] * (dp[r] - dls[h]) * a.scale;
-      }
-      const short4_t pf =
-          __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(pv[0], pv[1]), Pair16<T>::pack(pv[2], pv[3])));
-      const short4_t dsf =
-          __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(ds[0], ds[1]), Pair16<T>::pack(ds[2], ds[3])));
       // A = dO^T / q_abs^T [16 dims x 16 heads] by transposed reads: lane
       // 4 r + j of a 16-lane group gives dims .. + 4 j of head row 4 c + r
       const int head = 4 * c + (n >> 2);
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        const int off = head * kMlaLatRow + (128 * wave + 16 * blk + 4 * (n & 3)) * 2;
-        dla[blk] = mfma_16x16x16<T>(lds_read_tr16(go_s + off), pf, dla[blk]);
-        dla[blk] = mfma_16x16x16<T>(lds_read_tr16(qa_s + off), dsf, dla[blk]);
+      for (int kt = 0; kt < KT; ++kt) {
+        const floatx4_t sc = ((xs[0][kt][0][lane] + xs[0][kt][1][lane]) + xs[0][kt][2][lane]) + xs[0][kt][3][lane];
+        const floatx4_t dp = ((xs[1][kt][0][lane] + xs[1][kt][1][lane]) + xs[1][kt][2][lane]) + xs[1][kt][3][lane];
+        // lane (n, c): heads 4 c + r of key t
+        const int t = sub + NT * kt + n;
+        const bool vis = t < te && t >= lo && t <= hi;
+        float pv[4], ds[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * c + r;
+          pv[r] = vis ? fast_exp2(__builtin_fmaf(sc[r], c2, -l2s[h])) : 0.f;
+          ds[r] = pv[r] * (dp[r] - dls[h]) * a.scale;
+        }
+        const short4_t pf =
+            __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(pv[0], pv[1]), Pair16<T>::pack(pv[2], pv[3])));
+        const short4_t dsf =
+            __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(ds[0], ds[1]), Pair16<T>::pack(ds[2], ds[3])));
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+          const int off = head * kMlaLatRow + (128 * wave + 16 * blk + 4 * (n & 3)) * 2;
+          dla[kt][blk] = mfma_16x16x16<T>(lds_read_tr16(go_s + off), pf, dla[kt][blk]);
+          dla[kt][blk] = mfma_16x16x16<T>(lds_read_tr16(qa_s + off), dsf, dla[kt][blk]);
+        }
+        dkp[kt] = mfma_16x16x16<T>(lds_read_tr16(qr_s + head * kMlaPosRow + (16 * wave + 4 * (n & 3)) * 2), dsf,
+                                   dkp[kt]);
       }
-      dkp = mfma_16x16x16<T>(lds_read_tr16(qr_s + head * kMlaPosRow + (16 * wave + 4 * (n & 3)) * 2), dsf, dkp);
     }
-    // lane (n, c) element e: dim (block base) + 4 c + e of key sub + n
-    if (t < te) {
-      const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+    // lane (n, c) element e: dim (block base) + 4 c + e of key sub + 16 kt + n
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk)
+    for (int kt = 0; kt < KT; ++kt) {
+      const int t = sub + NT * kt + n;
+      if (t < te) {
+        const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          put_grad<T>(b.dk, b.acc_k, slot * R + 128 * wave + 16 * blk + 4 * c + e, dla[blk][e]);
+        for (int blk = 0; blk < 8; ++blk)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) put_grad<T>(b.dv, b.acc_v, slot * P + 16 * wave + 4 * c + e, dkp[e]);
+          for (int e = 0; e < 4; ++e)
+            put_grad<T>(b.dk, b.acc_k, slot * R + 128 * wave + 16 * blk + 4 * c + e, dla[kt][blk][e]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put_grad<T>(b.dv, b.acc_v, slot * P + 16 * wave + 4 * c + e, dkp[kt][e]);
+      }
     }
-    __syncthreads();  // the key tiles are rewritten by the next 16 keys
+    __syncthreads();  // the key tiles are rewritten by the next 64 keys
   }
 }
 

@@ -1366,6 +1366,7 @@ int pa_sparse_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, c
   sa.cand_width = L.cand;
   sa.span = L.span;
   sa.spans = L.spans;
+  sa.items_per_wg = pa::kSparseItemsPerWg;
   hipError_t e = pa::launch_sparse_select(dtype, sa, (int)rows, st);
   if (e != hipSuccess) return hip_fail(e, "block selection launch");
 
@@ -1383,7 +1384,7 @@ int pa_sparse_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, c
   a.items = sa.items;
   a.n_items = (int32_t)(rows * L.width);
   a.wg_first = sa.wg_first;
-  a.n_wg = (int32_t)(rows * L.width);
+  a.n_wg = (int32_t)((rows * L.width + pa::kSparseItemsPerWg - 1) / pa::kSparseItemsPerWg);
   a.heads_shift = 0;
   a.table_width = plan->W;
   a.page_shift = plan->page_shift;

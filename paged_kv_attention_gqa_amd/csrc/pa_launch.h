@@ -99,7 +99,10 @@ struct SparseArgs {
   int32_t cand_width;  // candidate blocks of the widest row
   int32_t span;        // keys per scoring workgroup: a multiple of block_size, aligned to itself
   int32_t spans;       // scoring workgroups per row (the widest row's span count)
+  int32_t items_per_wg;  // kept blocks per attention workgroup
 };
+// Kept blocks one attention workgroup runs (one after another).
+constexpr int kSparseItemsPerWg = 1;
 // Keys one scoring workgroup covers for blocks of `block_size` keys.
 inline int sparse_span(int block_size) { return block_size * (block_size >= 1024 ? 1 : 1024 / block_size); }
 hipError_t launch_sparse_select(int dtype, const SparseArgs& a, int rows, hipStream_t stream);

@@ -249,8 +249,13 @@ __global__ __launch_bounds__(kSelThreads) void sparse_topk_kernel(SparseArgs a) 
     if (a.selection) a.selection[base + j] = -1;
     a.items[base + j] = WorkItem{kEmpty, 0, 0, 0, 0, 0, 0, -1};
   }
-  for (int j = tid; j < width; j += kSelThreads) a.wg_first[base + j] = (int32_t)(base + j);
-  if (row == 0 && tid == 0) a.wg_first[(uint64_t)gridDim.x * width] = (int32_t)((uint64_t)gridDim.x * width);
+  // workgroup w runs items [w * ipw, (w + 1) * ipw) of the row-major list;
+  // this row writes the starts that fall in its items
+  const int ipw = a.items_per_wg;
+  const uint64_t total = (uint64_t)gridDim.x * width;
+  for (uint64_t w = (base + ipw - 1) / ipw + tid; w * ipw < base + width; w += kSelThreads)
+    a.wg_first[w] = (int32_t)(w * ipw);
+  if (row == 0 && tid == 0) a.wg_first[(total + ipw - 1) / ipw] = (int32_t)total;
   if (tid == 0) a.merges[row] = MergeItem{i, h, (int32_t)base, keep, 1};
 }
 
