@@ -66,12 +66,13 @@ def algorithmic_work(b, mla=False):
 
 def _source_hash():
     """Hash of the sources the forward kernels and their planner are built
-    from (the backward's own translation unit is left out: no forward launch
-    runs its code)."""
+    from (the translation units of the backward, the append, the block-sparse
+    selection and the no-allocation entry point are left out: no forward
+    launch of the benchmark runs their code)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc")
     for n in sorted(os.listdir(csrc)):
-        if n == "pa_backward.hip":
+        if n in ("pa_backward.hip", "pa_append.hip", "pa_sparse.hip", "pa_noalloc.hip"):
             continue
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode())
@@ -569,17 +570,23 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     ap.add_argument("--backward-only", action="store_true",
-                    help="only time the backward of --workload (one JSON line)")
+                    help="only time the backward of --workload (one JSON line; as --part backward)")
+    ap.add_argument("--part", choices=("backward", "mla-backward", "sparse", "append"),
+                    help="only run one of the secondary measurements on --workload (one JSON line)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return
     if args.backward_only:
+        args.part = "backward"
+    if args.part:
         import torch
         import paged_kv_attention_gqa_amd as pa
         pa.load_library()
         torch.cuda.set_device(0)
-        print(json.dumps(measure_backward(args.workload, args.steps, args.warmup)), flush=True)
+        fn = {"backward": measure_backward, "mla-backward": measure_mla_backward, "sparse": measure_sparse,
+              "append": measure_append}[args.part]
+        print(json.dumps(fn(args.workload, args.steps, args.warmup)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
