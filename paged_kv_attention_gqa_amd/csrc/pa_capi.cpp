@@ -1394,7 +1394,7 @@ int pa_sparse_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, c
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.causal = plan->causal;
   a.window = plan->window;
-  e = pa::launch_gqa_main(dtype, head_dim, v_head_dim, G, false, a, pa::MainEvents{}, st);
+  e = pa::launch_gqa_short(dtype, head_dim, v_head_dim, G, a, st);
   if (e != hipSuccess) return hip_fail(e, "block attention launch");
   e = pa::launch_gqa_merge(dtype, head_dim, v_head_dim, G, a, sa.merges, (int)rows, st);
   if (e != hipSuccess) return hip_fail(e, "block merge launch");

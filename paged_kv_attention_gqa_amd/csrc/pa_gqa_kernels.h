@@ -63,6 +63,27 @@ void decode_kernel(KernelArgs a) {
   }
 }
 
+// The decode body with kShortItemWaves waves per workgroup, for lists of short
+// items (block-sparse attention: one kept block, tens of keys, per item).  Few
+// waves give each wave several key blocks to pipeline and leave room for
+// many workgroups per CU; the eight-wave shape would hand each wave a single
+// block and then spend most of the item on its eight-wave combine.
+template <typename T, int D, int DV, int G>
+__global__ __launch_bounds__(kShortItemWaves* kWave) __attribute__((amdgpu_waves_per_eu(Occupancy<G>::kDecode)))
+void decode_short_kernel(KernelArgs a) {
+  constexpr int NW = kShortItemWaves;
+  __shared__ float smem[NW * G * (DV + 3)];
+  const int first = a.wg_first[blockIdx.x], last = a.wg_first[blockIdx.x + 1];
+  int tid = threadIdx.x;
+  for (int i = first; i < last; ++i) {
+    const WorkItem it = a.items[i];
+    if (it.kind == kEmpty) continue;
+    if (i > first) __syncthreads();  // the previous item's waves are done with the LDS
+    asm volatile("" : "+v"(tid));    // per-lane values are recomputed per item, not kept live
+    decode_item<T, D, DV, G, NW, DecodeUnroll<G>::kValue>(a, it, smem, tid, a.heads_shift);
+  }
+}
+
 // One launch for plans with prefill tiles: decode items and prefill tiles
 // share the grid (packed decode + chunked prefill in one dispatch).
 template <typename T, int D, int DV, int G>
@@ -127,6 +148,12 @@ hipError_t launch_decode_t(const KernelArgs& a, int n_wg, const MergeItem*, int,
 }
 
 template <typename T, int D, int DV, int G>
+hipError_t launch_short_t(const KernelArgs& a, int n_wg, const MergeItem*, int, const MainEvents& ev,
+                          hipStream_t stream) {
+  return launch_main(decode_short_kernel<T, D, DV, G>, n_wg, kShortItemWaves * kWave, a, ev, stream);
+}
+
+template <typename T, int D, int DV, int G>
 hipError_t launch_mixed_t(const KernelArgs& a, int n_wg, const MergeItem*, int, const MainEvents& ev,
                           hipStream_t stream) {
   return launch_main(mixed_kernel<T, D, DV, G>, n_wg, kPrefillWaves * kWave, a, ev, stream);
@@ -176,6 +203,11 @@ struct DecodeSel {
 };
 
 template <typename T, int D, int DV, int G>
+struct ShortSel {
+  static constexpr LaunchFn fn = launch_short_t<T, D, DV, G>;
+};
+
+template <typename T, int D, int DV, int G>
 struct MixedSel {
   static constexpr LaunchFn fn = launch_mixed_t<T, D, DV, G>;
 };
@@ -190,6 +222,7 @@ template <int... Gs>
 bool gqa_family_lookup(int dtype, int d, int dv, int g, GqaFamily* out) {
   if (!((g == Gs) || ...)) return false;
   out->decode = pick<DecodeSel, Gs...>(dtype, d, dv, g);
+  out->decode_short = pick<ShortSel, Gs...>(dtype, d, dv, g);
   out->mixed = pick<MixedSel, Gs...>(dtype, d, dv, g);
   out->merge = pick<MergeSel, Gs...>(dtype, d, dv, g);
   ((g == Gs ? (out->waves = DecodeShape<Gs>::kWaves, out->wgs_per_cu = DecodeShape<Gs>::kWgsPerCu, 0) : 0), ...);

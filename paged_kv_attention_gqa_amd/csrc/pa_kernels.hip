@@ -60,6 +60,12 @@ hipError_t launch_gqa_main(int dtype, int d, int dv, int g, bool has_prefill, co
   return fn ? fn(a, a.n_wg, nullptr, 0, ev, stream) : hipErrorInvalidValue;
 }
 
+hipError_t launch_gqa_short(int dtype, int d, int dv, int g, const KernelArgs& a, hipStream_t stream) {
+  GqaFamily f;
+  if (!gqa_family(dtype, d, dv, g, &f) || !f.decode_short) return hipErrorInvalidValue;
+  return f.decode_short(a, a.n_wg, nullptr, 0, MainEvents{}, stream);
+}
+
 hipError_t launch_gqa_merge(int dtype, int d, int dv, int g, const KernelArgs& a, const MergeItem* merges,
                             int n_merges, hipStream_t stream) {
   GqaFamily f;

@@ -25,7 +25,7 @@ using LaunchFn = hipError_t (*)(const KernelArgs&, int n_wg, const MergeItem* me
 // The kernels of one group size (a launcher is null when no kernel exists
 // for that data type and head size pair) and the decode launch shape.
 struct GqaFamily {
-  LaunchFn decode = nullptr, mixed = nullptr, merge = nullptr;
+  LaunchFn decode = nullptr, decode_short = nullptr, mixed = nullptr, merge = nullptr;
   int waves = 1, wgs_per_cu = 1;
 };
 // Lookups of the two translation units that instantiate the group sizes
@@ -39,6 +39,11 @@ bool prefill_supported(int dtype, int d, int dv, int g);
 // mixed launch when the list holds prefill tiles.
 hipError_t launch_gqa_main(int dtype, int d, int dv, int g, bool has_prefill, const KernelArgs& a,
                            const MainEvents& ev, hipStream_t stream);
+// Waves per workgroup of the decode launch for short items.
+constexpr int kShortItemWaves = 2;
+// Decode launch over a list of short items (a few key blocks each): fewer
+// waves per workgroup than the main decode launch.
+hipError_t launch_gqa_short(int dtype, int d, int dv, int g, const KernelArgs& a, hipStream_t stream);
 // Log-sum-exp merge of split rows into the output.
 hipError_t launch_gqa_merge(int dtype, int d, int dv, int g, const KernelArgs& a, const MergeItem* merges,
                             int n_merges, hipStream_t stream);

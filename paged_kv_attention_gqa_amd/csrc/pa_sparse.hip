@@ -49,21 +49,15 @@ __device__ __forceinline__ float widen(const T* p, int i) {
   }
 }
 
-// Largest 64-bit key of the workgroup (every thread receives it).
-__device__ __forceinline__ uint64_t wg_max(uint64_t v, uint64_t* red) {
+// Largest 64-bit key of the wave (every lane receives it).
+__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
 #pragma unroll
   for (int s = 1; s < kWave; s <<= 1) {
     const uint32_t lo = __shfl_xor((uint32_t)v, s), hi = __shfl_xor((uint32_t)(v >> 32), s);
     const uint64_t o = ((uint64_t)hi << 32) | lo;
     v = o > v ? o : v;
   }
-  const int wave = threadIdx.x / kWave;
-  __syncthreads();  // the previous round's readers are done with red
-  if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = v;
-  __syncthreads();
-  uint64_t m = red[0];
-  for (int w = 1; w < kSelThreads / kWave; ++w) m = red[w] > m ? red[w] : m;
-  return m;
+  return v;
 }
 
 constexpr int kPieces = 8;  // 16-byte pieces of a key row per pass (a longer row takes several passes)
@@ -186,7 +180,6 @@ __global__ __launch_bounds__(kSelThreads) void sparse_scores_kernel(SparseArgs a
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void sparse_topk_kernel(SparseArgs a) {
   __shared__ uint32_t score[kSparseMaxBlocks];
-  __shared__ uint64_t red[kSelThreads / kWave];
   __shared__ int32_t wave_count[kSelThreads / kWave];
 
   const int row = blockIdx.x;  // query * hkv + KV head
@@ -205,18 +198,23 @@ __global__ __launch_bounds__(kSelThreads) void sparse_topk_kernel(SparseArgs a) 
     const uint32_t* sc = a.scores + (size_t)row * a.cand_width;
     for (int r = tid; r < ncand; r += kSelThreads) score[r] = sc[r];
     __syncthreads();
-    // keep rounds: the best untaken block (a tie to the lower index) is
-    // marked taken (0)
-    for (int k = 0; k < keep; ++k) {
-      uint64_t best = 0;
-      for (int r = tid; r < ncand; r += kSelThreads) {
-        const uint64_t key = ((uint64_t)score[r] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)r);
-        best = key > best ? key : best;
+    // keep rounds, in the first wave alone (no workgroup barrier per round):
+    // the best untaken block (a tie to the lower index) is marked taken (0)
+    if (tid < kWave) {
+      for (int k = 0; k < keep; ++k) {
+        uint64_t best = 0;
+        for (int r = tid; r < ncand; r += kWave) {
+          const uint64_t key = ((uint64_t)score[r] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)r);
+          best = key > best ? key : best;
+        }
+        best = wave_max(best);
+        if (tid == 0 && (best >> 32) != 0) score[0xFFFFFFFFu - (uint32_t)best] = 0u;
+        // the mark is read by every lane next round (a wave's LDS accesses
+        // complete in order)
+        asm volatile("" ::: "memory");
       }
-      best = wg_max(best, red);
-      if (tid == 0 && (best >> 32) != 0) score[0xFFFFFFFFu - (uint32_t)best] = 0u;
-      __syncthreads();
     }
+    __syncthreads();
   }
 
   // kept blocks in increasing order: a prefix count over the candidates
