@@ -343,10 +343,11 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
   constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
   static_assert(kBwdMfmaWaves * 16 == kBwdBlockKeys, "eight waves of 16 keys");
   static_assert(D % 64 == 0 && DV % 64 == 0, "rows of whole 8-piece groups");
-  __shared__ __attribute__((aligned(16))) char qs[kBwdRowTile * D * 2];
-  __shared__ __attribute__((aligned(16))) char gs[kBwdRowTile * DV * 2];
-  __shared__ float lse2s[kBwdRowTile], dls[kBwdRowTile];
-  __shared__ int poss[kBwdRowTile];
+  // two LDS buffers: tile i in buffer i % 2
+  __shared__ __attribute__((aligned(16))) char qs2[2][kBwdRowTile * D * 2];
+  __shared__ __attribute__((aligned(16))) char gs2[2][kBwdRowTile * DV * 2];
+  __shared__ float lse2s2[2][kBwdRowTile], dls2[2][kBwdRowTile];
+  __shared__ int poss2[2][kBwdRowTile];
   const KernelArgs& a = b.a;
   const BwdItem it = b.items[first_item + blockIdx.x];
   const int tid = threadIdx.x;
@@ -389,10 +390,14 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
     const int rg = rho < nrows ? rho : 0;
     return ((uint64_t)(it.q_begin + rg / G) * a.hq + (uint64_t)kvh * G + rg % G);
   };
-  u32x4_t pre[PER_THREAD];
-  float pl = 0.f, pd = 0.f;
-  int pp = 0;
-  auto fetch = [&](int r0) {
+  // Tiles of query rows: registers two tiles ahead (fetched while the two
+  // tiles before them are computed), then one LDS buffer per tile parity.
+  struct Staged {
+    u32x4_t v[PER_THREAD];
+    float pl, pd;
+    int pp;
+  };
+  auto fetch = [&](Staged& st, int r0) {
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       const int c = tid + j * THREADS;
@@ -401,45 +406,43 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
         const int cc = is_q ? c : c - kBwdRowTile * PK;
         const int r = is_q ? cc / PK : cc / PV, piece = is_q ? cc % PK : cc % PV;
         const uint64_t row = row_addr(r0 + r);
-        pre[j] = is_q ? *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + piece * 8)
-                      : *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * DV +
-                                                          piece * 8);
+        st.v[j] = is_q ? *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + piece * 8)
+                       : *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * DV +
+                                                           piece * 8);
       }
     }
     if (tid < kBwdRowTile) {
       const int rho = r0 + tid;
       const uint64_t row = row_addr(rho);
       const bool ok = rho < nrows;
-      pl = ok ? a.lse[row] * kLog2e : INFINITY;
-      pd = ok ? b.delta[row] : 0.f;
-      pp = a.q_pos[it.q_begin + (ok ? rho : 0) / G];
+      st.pl = ok ? a.lse[row] * kLog2e : INFINITY;
+      st.pd = ok ? b.delta[row] : 0.f;
+      st.pp = a.q_pos[it.q_begin + (ok ? rho : 0) / G];
     }
   };
-  auto store = [&]() {
+  auto store = [&](const Staged& st, int buf) {
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       const int c = tid + j * THREADS;
       if (c < CHUNKS) {
         const bool is_q = c < kBwdRowTile * PK;
         const int cc = is_q ? c : c - kBwdRowTile * PK;
-        char* dst = is_q ? qs + bwd_off<D>(cc / PK, cc % PK) : gs + bwd_off<DV>(cc / PV, cc % PV);
-        *reinterpret_cast<u32x4_t*>(dst) = pre[j];
+        char* dst = is_q ? qs2[buf] + bwd_off<D>(cc / PK, cc % PK) : gs2[buf] + bwd_off<DV>(cc / PV, cc % PV);
+        *reinterpret_cast<u32x4_t*>(dst) = st.v[j];
       }
     }
     if (tid < kBwdRowTile) {
-      lse2s[tid] = pl;
-      dls[tid] = pd;
-      poss[tid] = pp;
+      lse2s2[buf][tid] = st.pl;
+      dls2[buf][tid] = st.pd;
+      poss2[buf][tid] = st.pp;
     }
   };
-
-  if (nrows > 0) fetch(0);
-  for (int r0 = 0; r0 < nrows; r0 += kBwdRowTile) {
-    __syncthreads();  // every wave is done with the previous tile
-    store();
-    __syncthreads();
-    if (r0 + kBwdRowTile < nrows) fetch(r0 + kBwdRowTile);
-
+  auto compute = [&](int buf) {
+    const char* qs = qs2[buf];
+    const char* gs = gs2[buf];
+    const float* lse2s = lse2s2[buf];
+    const float* dls = dls2[buf];
+    const int* poss = poss2[buf];
     // S and dP of the two 16-row halves
     floatx4_t s[2], dp[2];
 #pragma unroll
@@ -484,6 +487,38 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dkv_mfma_kernel(BwdA
     for (int blk = 0; blk < DBK; ++blk)
       dk[blk] = mfma_16x16x32<T>(df, bwd_tfrag(qs, bwd_troff<D>(blk, 0, n, g4), bwd_troff<D>(blk, 1, n, g4)),
                                  dk[blk]);
+  };
+
+  // tile i: stored into buffer i % 2 after the barrier that follows the
+  // compute of tile i - 2 (its last readers), made visible by the next
+  // barrier, which also lets the fetch of tile i + 2 reuse its registers;
+  // the barriers leave the row fetches in flight
+  const int ntile = (nrows + kBwdRowTile - 1) / kBwdRowTile;
+  if constexpr (D + DV <= 256) {
+    Staged sa{}, sb{};
+    if (ntile > 0) fetch(sa, 0);
+    if (ntile > 1) fetch(sb, kBwdRowTile);
+    for (int i = 0; i < ntile; i += 2) {
+      store(sa, 0);
+      barrier_keep_loads();
+      if (i + 2 < ntile) fetch(sa, (i + 2) * kBwdRowTile);
+      compute(0);
+      if (i + 1 >= ntile) break;
+      store(sb, 1);
+      barrier_keep_loads();
+      if (i + 3 < ntile) fetch(sb, (i + 3) * kBwdRowTile);
+      compute(1);
+    }
+  } else {
+    // wider rows: one tile ahead in registers (two would spill)
+    Staged sa{};
+    if (ntile > 0) fetch(sa, 0);
+    for (int i = 0; i < ntile; ++i) {
+      store(sa, i & 1);
+      barrier_keep_loads();
+      if (i + 1 < ntile) fetch(sa, (i + 1) * kBwdRowTile);
+      compute(i & 1);
+    }
   }
 
   // lane (n, g4) of block blk holds dims 16 blk + n of keys key_lo + 4 g4 + e

@@ -50,6 +50,20 @@ struct MlaSmem {
   static constexpr int kBytes = kXchgOff + kMlaWaves * 64 * 16;  // + partial scores of the four waves
 };
 
+// Wait until at most `ahead` (<= MAXA) tiles of PER loads each are still in
+// flight for this wave.
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  if constexpr (MAXA == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= MAXA)
+      wait_vmcnt<PER * MAXA>();
+    else
+      wait_tiles_ahead<PER, MAXA - 1>(ahead);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ floatx4_t mfma_16x16x32(const frag_t& a, const frag_t& b, const floatx4_t& c) {
   if constexpr (__is_same(T, _Float16))
@@ -213,13 +227,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   page_next = tile_page(first + (kMlaStages - 1) * NT);
   for (int j = 0; j < ntiles; ++j) {
     // tiles j+1 .. j+2 may stay in flight; this wave's share of tile j has landed
-    const int ahead = min(ntiles - 1 - j, kMlaStages - 2);
-    if (ahead >= 2)
-      wait_vmcnt<2 * LOADS_PER_TILE>();
-    else if (ahead == 1)
-      wait_vmcnt<LOADS_PER_TILE>();
-    else
-      wait_vmcnt<0>();
+    wait_tiles_ahead<LOADS_PER_TILE, kMlaStages - 2>(min(ntiles - 1 - j, kMlaStages - 2));
     barrier_keep_loads();  // ... every wave's share has; tile j-1's stage is free for reuse
     if (j + kMlaStages - 1 < ntiles) {
       issue_tile(first + (j + kMlaStages - 1) * NT, smem + ((j + kMlaStages - 1) % kMlaStages) * MlaSmem::kStage,
