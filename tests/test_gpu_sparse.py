@@ -53,7 +53,9 @@ CASES = [
 
 
 @pytest.mark.parametrize("i", range(len(CASES)))
-@pytest.mark.parametrize("block,topk", [(64, 4), (16, 1), (128, 3)])
+# 48: a block size that is no power of two (per-key block maxima); 2048:
+# blocks wider than one scoring span of 1024 keys (the span is the block)
+@pytest.mark.parametrize("block,topk", [(64, 4), (16, 1), (128, 3), (48, 5), (2048, 1)])
 def test_sparse_selection_bit_exact_and_output_parity(i, block, topk):
     b = random_batch(9300 + i, **CASES[i])
     if block % b.page_size:
