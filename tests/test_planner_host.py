@@ -280,3 +280,77 @@ def test_backward_workspace_and_shared_page_detection():
     p = pa.pa_plan_create_host(num_cus=256, **s0)
     assert pa.pa_plan_bwd_workspace_bytes(p, "bf16", 64, 64) == 0  # no queries: nothing to add up
     pa.pa_plan_destroy(p)
+
+
+def test_backward_lists_on_first_use_match_the_visibility_rule():
+    """The backward work lists are built when first asked for (here by
+    pa_plan_get_info): one dQ item per (query, KV head), one dK/dV item per
+    (128-key block of a sequence that some query sees, KV head); asking twice
+    gives the same counts, and a plan with prefill chunks and decode rows
+    counts both."""
+    s = schedule(12, q_counts=[1, 37, 0, 2], histories=[300, 129, 50, 0], page_size=16, hq=12, hkv=3,
+                 window=90)
+    p = pa.pa_plan_create_host(num_cus=64, **s)
+    first = pa.pa_plan_get_info(p)
+    again = pa.pa_plan_get_info(p)
+    pa.pa_plan_destroy(p)
+    nq = int(s["cu_q"][-1])
+    assert first["bwd_dq_items"] == again["bwd_dq_items"] == nq * s["num_kv_heads"]
+    blocks = set()
+    for i in range(nq):
+        seq, lo, hi = visible(s, i)
+        for blk in range(lo // 128, (hi - 1) // 128 + 1):
+            blocks.add((seq, blk))
+    assert first["bwd_kv_items"] == again["bwd_kv_items"] == len(blocks) * s["num_kv_heads"]
+
+
+def sparse_candidates(s, block):
+    """Candidate blocks per query (those holding a key it sees)."""
+    out = []
+    for i in range(int(s["cu_q"][-1])):
+        _, lo, hi = visible(s, i)
+        out.append((hi - 1) // block - lo // block + 1)
+    return out
+
+
+@pytest.mark.parametrize("block", [16, 48, 2048])
+def test_sparse_workspace_and_width(block):
+    """pa_sparse_workspace_bytes: the selection width is topk, or the largest
+    candidate count of any row for topk = 0; the workspace is 256-byte
+    aligned, grows with topk, and with topk > 0 holds the candidate block
+    scores of every (query, KV head) row as well."""
+    s = schedule(13, q_counts=[1, 20, 3], histories=[5000, 700, 33], page_size=16, hq=8, hkv=2, window=0)
+    p = pa.pa_plan_create_host(num_cus=256, **s)
+    most = max(sparse_candidates(s, block))
+    n0, w0 = pa.pa_sparse_workspace_bytes(p, 64, block, 0)
+    n1, w1 = pa.pa_sparse_workspace_bytes(p, 64, block, 1)
+    n3, w3 = pa.pa_sparse_workspace_bytes(p, 64, block, 3)
+    pa.pa_plan_destroy(p)
+    assert (w0, w1, w3) == (most, 1, 3)
+    assert all(n % 256 == 0 and n > 0 for n in (n0, n1, n3))
+    rows = int(s["cu_q"][-1]) * s["num_kv_heads"]
+    assert n3 > n1
+    assert n1 >= rows * most * 4  # the score buffer alone
+
+
+def test_sparse_layout_errors():
+    """Block sizes that are not positive multiples of the page size, a
+    negative topk, rows of more than 8192 blocks and MLA plans are refused
+    before any device work."""
+    s = schedule(14, q_counts=[1, 2], histories=[9000, 100], page_size=1, hq=4, hkv=1)
+    p = pa.pa_plan_create_host(num_cus=256, **s)
+    for block, topk, status in [(0, 1, -2), (3, -1, -1)]:
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_sparse_workspace_bytes(p, 64, block, topk)
+        assert e.value.status == status
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_sparse_workspace_bytes(p, 64, 1, 4)  # 9001 one-key blocks in a row
+    assert e.value.status == -4
+    assert pa.pa_sparse_workspace_bytes(p, 64, 2, 4)[1] == 4  # 4501 blocks: accepted
+    pa.pa_plan_destroy(p)
+    s = schedule(15, q_counts=[1], histories=[100], page_size=16, hq=16, hkv=1, mla=True)
+    p = pa.pa_plan_create_host(num_cus=256, **s)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_sparse_workspace_bytes(p, 512, 64, 4)
+    assert e.value.status == -1
+    pa.pa_plan_destroy(p)
