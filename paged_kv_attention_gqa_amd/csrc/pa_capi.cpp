@@ -49,8 +49,10 @@ constexpr int kDecodeMaxQueries = 4;
 constexpr int kPrefillRows = pa::kPrefillRows;
 constexpr int kDefaultSplitTokens = 512;
 // In a launch that also runs prefill tiles, a decode item is worked by the
-// prefill workgroup's eight waves: give it proportionally more keys.
-constexpr int kMixedSplitTokens = 2048;
+// prefill workgroup's eight waves: give it proportionally more keys (on the
+// mixed batch with its 4096-key window, rows cut at 4096 keys -- whole rows --
+// ran 2% faster than rows cut at 2048, 3% faster than at 1024).
+constexpr int kMixedSplitTokens = 4096;
 constexpr int kDefaultMlaSplitTokens = 1024;
 constexpr int kSplitAlign = 64;
 // Shortest piece of a split decode row in a balanced plan: a piece's partial
