@@ -271,7 +271,8 @@ int pa_attention_fwd_noalloc(const pa_plan* plan, int32_t dtype, const void* q, 
  *   kpos    [num_pages, page_size, 1, rope_dim]
  *   out     [Q, H, rank]        lse NULL or f32 [Q, H]
  *   rank    1..1024, rope_dim 1..256 (this build runs bf16 and f16 with
- *           H = 16, rank = 512, rope_dim = 64)
+ *           rank = 512, rope_dim = 64 and any H >= 1; the kernels take the
+ *           heads in groups of 16, so H = 16 n uses every MFMA column)
  *   scale   from the model's original query/key head size, not the latent
  *           rank (e.g. 1/sqrt(rank + rope_dim))
  *
@@ -426,7 +427,7 @@ int pa_sparse_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, int32_t b
  *   dlat_t = sum_rows (scale dS_t q_abs + P_t dO)
  *   dkpos_t = sum_rows scale dS_t q_rope
  *
- *   dtype        PA_BF16 or PA_F16 (this build: H = 16, rank 512, rope_dim 64)
+ *   dtype        PA_BF16 or PA_F16 (this build: rank 512, rope_dim 64, any H)
  *   q_abs, q_rope, latent, kpos, out, lse  as for pa_mla_fwd with the same
  *                plan (out and lse: the forward's results)
  *   dout         [Q, H, rank] output gradient

@@ -699,7 +699,8 @@ __device__ __forceinline__ void mla_tile_to_lds(char* dst, Src src) {
   }
 }
 
-// dq_abs and dq_rope of one query (all 16 heads) over its visible keys
+// dq_abs and dq_rope of one query and group of 16 heads (item kvh = g: heads
+// 16 g .. 16 g + 15, the last group possibly partial) over its visible keys
 // [tok_begin, tok_end), 16 keys per tile:
 //   S^T, dP^T [16 keys x 16 heads]    (partial over each wave's dims, summed)
 //   dq_abs^T [dims x heads] += lat^T . dS^T,  dq_rope^T += kpos^T . dS^T
@@ -721,8 +722,11 @@ __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dq_kernel(BwdArgs
   const uint16_t* kpos = reinterpret_cast<const uint16_t*>(a.kr);
 
   // this wave's operands: q_abs^T and dO^T over latent dims 128 wave .. +127
-  // (lane (n, c): head n, dims 32 k + 8 c), q_rope^T over rotary dims 16 wave ..
-  const uint64_t row = (uint64_t)qi * H + n;
+  // (lane (n, c): head 16 g + n, dims 32 k + 8 c), q_rope^T over rotary dims
+  // 16 wave ..; columns past the last head repeat it and are not stored
+  const int head = H * it.kvh + n;
+  const bool head_ok = head < a.hq;
+  const uint64_t row = (uint64_t)qi * a.hq + min(head, a.hq - 1);
   frag_t qa[4], go[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -783,7 +787,8 @@ __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dq_kernel(BwdArgs
     __syncthreads();  // the tiles and the exchange are rewritten next
   }
 
-  // lane (n, c) element e: dim (block base) + 4 c + e of head n
+  // lane (n, c) element e: dim (block base) + 4 c + e of head 16 g + n
+  if (!head_ok) return;
   uint16_t* oa = reinterpret_cast<uint16_t*>(b.dq) + row * R + 128 * wave + 4 * c;
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
@@ -800,8 +805,9 @@ __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dq_kernel(BwdArgs
 
 // dlatent and dkpos of one block of up to kBwdBlockKeys keys, 64 keys (four
 // 16-key tiles) at a time, against the queries [q_begin, q_end) that see
-// them (each query is one 16-row tile: its 16 heads); a query's operand
-// tiles are loaded once for the 64 keys:
+// them, each query one 16-row tile per group of 16 heads (a partial last
+// group repeats its last head in the missing rows, weighted zero); a
+// (query, head group)'s operand tiles are loaded once for the 64 keys:
 //   S, dP [16 heads x 16 keys] per key tile (partial over each wave's dims,
 //   summed)
 //   dlat^T [dims x keys] += dO^T . P + scale q_abs^T . dS
@@ -861,62 +867,66 @@ __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dkv_kernel(BwdArg
       const int hi = a.causal ? pos : L - 1;
       const int lo = a.window > 0 ? max(0, pos - a.window + 1) : 0;
       if (hi < sub || lo >= te) continue;  // this query sees none of the keys
-      const uint64_t row0 = (uint64_t)qi * H;
-      __syncthreads();  // the previous query's tiles and partials are no longer read
-      mla_tile_to_lds<R, kMlaLatRow>(qa_s, [&](int r) { return reinterpret_cast<const uint16_t*>(a.q) + (row0 + r) * R; });
-      mla_tile_to_lds<R, kMlaLatRow>(go_s,
-                                     [&](int r) { return reinterpret_cast<const uint16_t*>(b.dout) + (row0 + r) * R; });
-      mla_tile_to_lds<P, kMlaPosRow>(qr_s, [&](int r) { return reinterpret_cast<const uint16_t*>(a.qr) + (row0 + r) * P; });
-      if (tid < H) {
-        l2s[tid] = a.lse[row0 + tid] * kLog2e;
-        dls[tid] = b.delta[row0 + tid];
-      }
-      __syncthreads();
-      // this wave's partial S and dP of every key tile
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        floatx4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int off = n * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2;
-          sc = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(qa_s + off), lb[kt][k], sc);
-          dp = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(go_s + off), lb[kt][k], dp);
+      for (int g0 = 0; g0 < a.hq; g0 += H) {
+        const int nh = min(H, a.hq - g0);  // heads of this group
+        const uint64_t row0 = (uint64_t)qi * a.hq + g0;
+        auto hrow = [&](int r) { return row0 + min(r, nh - 1); };
+        __syncthreads();  // the previous (query, head group)'s tiles and partials are no longer read
+        mla_tile_to_lds<R, kMlaLatRow>(qa_s, [&](int r) { return reinterpret_cast<const uint16_t*>(a.q) + hrow(r) * R; });
+        mla_tile_to_lds<R, kMlaLatRow>(go_s,
+                                       [&](int r) { return reinterpret_cast<const uint16_t*>(b.dout) + hrow(r) * R; });
+        mla_tile_to_lds<P, kMlaPosRow>(qr_s, [&](int r) { return reinterpret_cast<const uint16_t*>(a.qr) + hrow(r) * P; });
+        if (tid < H) {
+          l2s[tid] = a.lse[hrow(tid)] * kLog2e;
+          dls[tid] = b.delta[hrow(tid)];
         }
-        sc = mfma_16x16x16<T>(*reinterpret_cast<const short4_t*>(qr_s + n * kMlaPosRow + (16 * wave + 4 * c) * 2),
-                              kb[kt], sc);
-        xs[0][kt][wave][lane] = sc;
-        xs[1][kt][wave][lane] = dp;
-      }
-      __syncthreads();
-      // A = dO^T / q_abs^T [16 dims x 16 heads] by transposed reads: lane
-      // 4 r + j of a 16-lane group gives dims .. + 4 j of head row 4 c + r
-      const int head = 4 * c + (n >> 2);
+        __syncthreads();
+        // this wave's partial S and dP of every key tile
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const floatx4_t sc = ((xs[0][kt][0][lane] + xs[0][kt][1][lane]) + xs[0][kt][2][lane]) + xs[0][kt][3][lane];
-        const floatx4_t dp = ((xs[1][kt][0][lane] + xs[1][kt][1][lane]) + xs[1][kt][2][lane]) + xs[1][kt][3][lane];
-        // lane (n, c): heads 4 c + r of key t
-        const int t = sub + NT * kt + n;
-        const bool vis = t < te && t >= lo && t <= hi;
-        float pv[4], ds[4];
+        for (int kt = 0; kt < KT; ++kt) {
+          floatx4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = 4 * c + r;
-          pv[r] = vis ? fast_exp2(__builtin_fmaf(sc[r], c2, -l2s[h])) : 0.f;
-          ds[r] = pv[r] * (dp[r] - dls[h]) * a.scale;
+          for (int k = 0; k < 4; ++k) {
+            const int off = n * kMlaLatRow + (32 * (4 * wave + k) + 8 * c) * 2;
+            sc = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(qa_s + off), lb[kt][k], sc);
+            dp = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(go_s + off), lb[kt][k], dp);
+          }
+          sc = mfma_16x16x16<T>(*reinterpret_cast<const short4_t*>(qr_s + n * kMlaPosRow + (16 * wave + 4 * c) * 2),
+                                kb[kt], sc);
+          xs[0][kt][wave][lane] = sc;
+          xs[1][kt][wave][lane] = dp;
         }
-        const short4_t pf =
-            __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(pv[0], pv[1]), Pair16<T>::pack(pv[2], pv[3])));
-        const short4_t dsf =
-            __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(ds[0], ds[1]), Pair16<T>::pack(ds[2], ds[3])));
+        __syncthreads();
+        // A = dO^T / q_abs^T [16 dims x 16 heads] by transposed reads: lane
+        // 4 r + j of a 16-lane group gives dims .. + 4 j of head row 4 c + r
+        const int head = 4 * c + (n >> 2);
 #pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-          const int off = head * kMlaLatRow + (128 * wave + 16 * blk + 4 * (n & 3)) * 2;
-          dla[kt][blk] = mfma_16x16x16<T>(lds_read_tr16(go_s + off), pf, dla[kt][blk]);
-          dla[kt][blk] = mfma_16x16x16<T>(lds_read_tr16(qa_s + off), dsf, dla[kt][blk]);
+        for (int kt = 0; kt < KT; ++kt) {
+          const floatx4_t sc = ((xs[0][kt][0][lane] + xs[0][kt][1][lane]) + xs[0][kt][2][lane]) + xs[0][kt][3][lane];
+          const floatx4_t dp = ((xs[1][kt][0][lane] + xs[1][kt][1][lane]) + xs[1][kt][2][lane]) + xs[1][kt][3][lane];
+          // lane (n, c): heads 4 c + r of key t
+          const int t = sub + NT * kt + n;
+          const bool vis = t < te && t >= lo && t <= hi;
+          float pv[4], ds[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int h = 4 * c + r;
+            pv[r] = vis && h < nh ? fast_exp2(__builtin_fmaf(sc[r], c2, -l2s[h])) : 0.f;
+            ds[r] = pv[r] * (dp[r] - dls[h]) * a.scale;
+          }
+          const short4_t pf =
+              __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(pv[0], pv[1]), Pair16<T>::pack(pv[2], pv[3])));
+          const short4_t dsf =
+              __builtin_bit_cast(short4_t, make_uint2(Pair16<T>::pack(ds[0], ds[1]), Pair16<T>::pack(ds[2], ds[3])));
+#pragma unroll
+          for (int blk = 0; blk < 8; ++blk) {
+            const int off = head * kMlaLatRow + (128 * wave + 16 * blk + 4 * (n & 3)) * 2;
+            dla[kt][blk] = mfma_16x16x16<T>(lds_read_tr16(go_s + off), pf, dla[kt][blk]);
+            dla[kt][blk] = mfma_16x16x16<T>(lds_read_tr16(qa_s + off), dsf, dla[kt][blk]);
+          }
+          dkp[kt] = mfma_16x16x16<T>(lds_read_tr16(qr_s + head * kMlaPosRow + (16 * wave + 4 * (n & 3)) * 2), dsf,
+                                     dkp[kt]);
         }
-        dkp[kt] = mfma_16x16x16<T>(lds_read_tr16(qr_s + head * kMlaPosRow + (16 * wave + 4 * (n & 3)) * 2), dsf,
-                                   dkp[kt]);
       }
     }
     // lane (n, c) element e: dim (block base) + 4 c + e of key sub + 16 kt + n

@@ -128,6 +128,11 @@ struct pa_plan {
   const int32_t* d_zero_runs = nullptr;
 
   int group() const { return hq / hkv; }
+  // Work units of one query row: its KV heads (GQA), or its query heads in
+  // groups of kMlaGroupHeads (MLA: one shared latent head; the last group
+  // may be partial), and the query heads of one unit.
+  int units() const { return mla ? (hq + pa::kMlaGroupHeads - 1) / pa::kMlaGroupHeads : hkv; }
+  int unit_heads() const { return mla ? pa::kMlaGroupHeads : hq / hkv; }
 };
 
 namespace {
@@ -195,7 +200,7 @@ int validate_desc(const pa_plan_desc* d) {
 // [Hkv, D] slot rows of each page.  Partial slots of a split row are laid out
 // [range][KV head]; an item's slot is its first head's.
 void plan_decode_row(pa_plan* p, int s, int i, int split_tokens, std::vector<WorkItem>& out) {
-  const int hw = 1 << p->heads_shift;
+  const int hw = 1 << p->heads_shift, U = p->units();
   int lo, hi;
   visible_range(p->q_pos[i], p->seq_lens[s], p->causal, p->window, &lo, &hi);
   const int n = hi - lo + 1;
@@ -208,17 +213,17 @@ void plan_decode_row(pa_plan* p, int s, int i, int split_tokens, std::vector<Wor
     nsplit = (n + chunk - 1) / chunk;
   }
   if (nsplit == 1) {
-    for (int kvh = 0; kvh < p->hkv; kvh += hw) out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, lo, hi + 1, -1});
+    for (int kvh = 0; kvh < U; kvh += hw) out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, lo, hi + 1, -1});
     return;
   }
   const int base = p->n_slots;
   for (int j = 0; j < nsplit; ++j) {
     const int b = lo + j * chunk, e = std::min(hi + 1, b + chunk);
-    for (int kvh = 0; kvh < p->hkv; kvh += hw)
-      out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, b, e, base + j * p->hkv + kvh});
+    for (int kvh = 0; kvh < U; kvh += hw)
+      out.push_back(WorkItem{pa::kDecode, kvh, s, i, 1, b, e, base + j * U + kvh});
   }
-  for (int kvh = 0; kvh < p->hkv; ++kvh) p->merges.push_back(MergeItem{i, kvh, base + kvh, nsplit, p->hkv});
-  p->n_slots += nsplit * p->hkv;
+  for (int kvh = 0; kvh < U; ++kvh) p->merges.push_back(MergeItem{i, kvh, base + kvh, nsplit, U});
+  p->n_slots += nsplit * U;
 }
 
 // Estimated run time of an item, in units of one decode key: a decode item
@@ -241,26 +246,33 @@ int64_t item_cost(const WorkItem& w) {
 // built per XCD and interleaved.  Units of work are dealt, largest first, to
 // the XCD with the least estimated work so far; a unit is one decode item or
 // all prefill tiles of one (sequence, KV head), which read the same keys and
-// so share one L2.  Each XCD then runs its items longest first; XCDs with
+// so share one L2 (MLA: all prefill tiles of one sequence, and the decode
+// items of all head groups of one key range).  Each XCD then runs its items longest first; XCDs with
 // fewer items are padded with empty items.
 constexpr int kXcds = 8;
 void order_items(pa_plan* p, const std::vector<WorkItem>& pre, const std::vector<WorkItem>& dec) {
   std::vector<std::vector<WorkItem>> units;
   std::vector<int64_t> unit_cost;
   std::map<std::pair<int, int>, size_t> group_of;
-  for (const WorkItem& w : pre) {
-    auto g = group_of.find({w.seq, w.kvh});
+  auto add = [&](std::pair<int, int> key, const WorkItem& w) {
+    auto g = group_of.find(key);
     if (g == group_of.end()) {
-      g = group_of.emplace(std::make_pair(w.seq, w.kvh), units.size()).first;
+      g = group_of.emplace(key, units.size()).first;
       units.emplace_back();
       unit_cost.push_back(0);
     }
     units[g->second].push_back(w);
     unit_cost[g->second] += item_cost(w);
-  }
+  };
+  for (const WorkItem& w : pre) add({w.seq, p->mla ? 0 : w.kvh}, w);
   for (const WorkItem& w : dec) {
-    units.push_back({w});
-    unit_cost.push_back(item_cost(w));
+    if (p->mla) {
+      // the head groups of one MLA key range read the same latent rows
+      add({-1 - w.q_begin, w.tok_begin}, w);
+    } else {
+      units.push_back({w});
+      unit_cost.push_back(item_cost(w));
+    }
   }
   std::vector<size_t> order(units.size());
   for (size_t u = 0; u < order.size(); ++u) order[u] = u;
@@ -314,8 +326,8 @@ void plan_balanced(pa_plan* p, int slots, int min_piece) {
       rows.push_back(Row{s, i, lo, hi + 1});
       left += hi + 1 - lo;
     }
-  const int hw = 1 << p->heads_shift;
-  const int groups = std::max(1, slots / (p->hkv / hw));
+  const int hw = 1 << p->heads_shift, U = p->units();
+  const int groups = std::max(1, slots / (U / hw));
   auto align_up = [](int64_t x) { return (x + kSplitAlign - 1) / kSplitAlign * kSplitAlign; };
   auto align_down = [](int64_t x) { return x / kSplitAlign * kSplitAlign; };
   struct Piece {
@@ -362,26 +374,37 @@ void plan_balanced(pa_plan* p, int slots, int min_piece) {
     }
   }
   while (!grp.empty() && grp.back().empty()) grp.pop_back();
-  // partial slots: row r, piece j, KV head h -> first[r] + j * Hkv + h
+  // partial slots: row r, piece j, unit h -> first[r] + j * U + h
   std::vector<int> first(rows.size(), -1);
   for (size_t ri = 0; ri < rows.size(); ++ri) {
     if (nparts[ri] < 2) continue;
     first[ri] = p->n_slots;
-    for (int h = 0; h < p->hkv; ++h)
-      p->merges.push_back(MergeItem{rows[ri].q, h, p->n_slots + h, nparts[ri], p->hkv});
-    p->n_slots += p->hkv * nparts[ri];
+    for (int h = 0; h < U; ++h) p->merges.push_back(MergeItem{rows[ri].q, h, p->n_slots + h, nparts[ri], U});
+    p->n_slots += U * nparts[ri];
   }
   p->items.clear();
   p->wg_first.assign(1, 0);
-  for (const auto& g : grp)
-    for (int h = 0; h < p->hkv; h += hw) {
-      for (const Piece& pc : g) {
+  auto emit = [&](const std::vector<Piece>* g, int h) {
+    if (g)
+      for (const Piece& pc : *g) {
         const Row& r = rows[pc.row];
-        const int slot = first[pc.row] < 0 ? -1 : first[pc.row] + pc.part * p->hkv + h;
+        const int slot = first[pc.row] < 0 ? -1 : first[pc.row] + pc.part * U + h;
         p->items.push_back(WorkItem{pa::kDecode, h, r.s, r.q, 1, pc.b, pc.e, slot});
       }
-      p->wg_first.push_back((int32_t)p->items.size());
-    }
+    p->wg_first.push_back((int32_t)p->items.size());
+  };
+  if (p->mla && U > 1) {
+    // the head groups of one group of pieces read the same latent rows: put
+    // their workgroups kXcds apart (one XCD, one L2), the groups of a block
+    // of kXcds side by side; missing groups of the last block leave empty
+    // workgroups
+    for (size_t b0 = 0; b0 < grp.size(); b0 += kXcds)
+      for (int h = 0; h < U; ++h)
+        for (size_t j = b0; j < b0 + kXcds; ++j) emit(j < grp.size() ? &grp[j] : nullptr, h);
+  } else {
+    for (const auto& g : grp)
+      for (int h = 0; h < U; h += hw) emit(&g, h);
+  }
   p->n_decode = (int32_t)p->items.size();
   p->n_prefill = 0;
 }
@@ -415,8 +438,8 @@ void build_work(pa_plan* p) {
     if (nq <= kDecodeMaxQueries) {
       for (int i = q0; i < q1; ++i) plan_decode_row(p, s, i, split_tokens, dec);
     } else if (p->mla) {
-      // MLA chunks: items of kMlaPrefillQueries consecutive queries over the
-      // union of their visible keys, one query per wave
+      // MLA chunks: items of kMlaPrefillQueries consecutive queries and one
+      // head group over the union of their visible keys, one query per two waves
       for (int t0 = q0; t0 < q1; t0 += pa::kMlaPrefillQueries) {
         const int t1 = std::min(q1, t0 + pa::kMlaPrefillQueries);
         int lo = INT32_MAX, hi = -1;
@@ -426,7 +449,7 @@ void build_work(pa_plan* p) {
           lo = std::min(lo, a);
           hi = std::max(hi, b);
         }
-        pre.push_back(WorkItem{pa::kPrefill, 0, s, t0, t1 - t0, lo, hi + 1, -1});
+        for (int h = 0; h < p->units(); ++h) pre.push_back(WorkItem{pa::kPrefill, h, s, t0, t1 - t0, lo, hi + 1, -1});
       }
     } else {
       const int tile_q = std::max(1, kPrefillRows / G);
@@ -481,7 +504,7 @@ void build_bwd(pa_plan* p) {
     for (int i = q0; i < q1; ++i) {
       int lo, hi;
       visible_range(p->q_pos[i], L, p->causal, p->window, &lo, &hi);
-      for (int kvh = 0; kvh < p->hkv; ++kvh) dq.push_back({hi + 1 - lo, pa::BwdItem{s, kvh, i, i + 1, lo, hi + 1}});
+      for (int kvh = 0; kvh < p->units(); ++kvh) dq.push_back({hi + 1 - lo, pa::BwdItem{s, kvh, i, i + 1, lo, hi + 1}});
     }
     for (int a0 = q0; a0 < q1 && !p->mla; a0 += tile_q) {  // MLA: per-query dQ items only
       const int a1 = std::min(q1, a0 + tile_q);
@@ -509,6 +532,7 @@ void build_bwd(pa_plan* p) {
         }
       }
       if (rows == 0) continue;
+      // (MLA: one item per block, which takes every head group of its queries)
       for (int kvh = 0; kvh < p->hkv; ++kvh) kv.push_back({rows, pa::BwdItem{s, kvh, first, last + 1, t0, t1}});
     }
   }
@@ -597,8 +621,8 @@ int ensure_bwd_device(const pa_plan* cp) {
 }
 
 // Workspace: partial sums [slots, G, Dv] | (max, sum, unrounded sum) [slots, G, 3].
-size_t ws_o_bytes(const pa_plan* p, int dv) { return align_up((size_t)p->n_slots * p->group() * dv * 4, kAlign); }
-size_t ws_ml_bytes(const pa_plan* p) { return align_up((size_t)p->n_slots * p->group() * 3 * 4, kAlign); }
+size_t ws_o_bytes(const pa_plan* p, int dv) { return align_up((size_t)p->n_slots * p->unit_heads() * dv * 4, kAlign); }
+size_t ws_ml_bytes(const pa_plan* p) { return align_up((size_t)p->n_slots * p->unit_heads() * 3 * 4, kAlign); }
 
 size_t workspace_bytes_for(const pa_plan* p, int dv) {
   if (p->n_slots == 0) return 0;

@@ -473,12 +473,15 @@ constexpr int kMergeUnroll = 16;
 
 // The (g, d) outputs of a row are spread over `chunks` workgroups; this one
 // takes outputs chunk, chunk + chunks, ... in units of blockDim.
-template <typename T, int DV, int G>
+// PARTIAL: the row's last group of G heads may reach past head hq - 1 (MLA
+// head groups), whose dims are skipped.
+template <typename T, int DV, int G, bool PARTIAL = false>
 __device__ __forceinline__ void merge_row(const KernelArgs& a, const MergeItem& mi, int chunk, int chunks) {
   // four consecutive output dims per thread (16-byte partial loads)
   static_assert(DV % 4 == 0, "merge reads four dims at a time");
   for (int idx = chunk * blockDim.x + threadIdx.x; idx < G * DV / 4; idx += chunks * blockDim.x) {
     const int g = (4 * idx) / DV, d = (4 * idx) % DV;
+    if (PARTIAL && mi.kvh * G + g >= a.hq) break;  // past the last head
     float M = -INFINITY, L = 0.f, LX = 0.f;
     floatx4_t O = {0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < mi.nsplit; j0 += kMergeUnroll) {

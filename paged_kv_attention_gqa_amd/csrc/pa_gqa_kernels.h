@@ -120,10 +120,10 @@ void mixed_kernel(KernelArgs a) {
 
 // grid: (split rows, chunks of 256 outputs per row)
 constexpr int kMergeThreads = 256;
-template <typename T, int DV, int G>
+template <typename T, int DV, int G, bool PARTIAL = false>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelArgs a, const MergeItem* merges) {
   const MergeItem mi = merges[blockIdx.x];
-  merge_row<T, DV, G>(a, mi, blockIdx.y, gridDim.y);
+  merge_row<T, DV, G, PARTIAL>(a, mi, blockIdx.y, gridDim.y);
 }
 
 namespace {
@@ -159,12 +159,13 @@ hipError_t launch_mixed_t(const KernelArgs& a, int n_wg, const MergeItem*, int, 
   return launch_main(mixed_kernel<T, D, DV, G>, n_wg, kPrefillWaves * kWave, a, ev, stream);
 }
 
-template <typename T, int DV, int G>
+template <typename T, int DV, int G, bool PARTIAL = false>
 hipError_t launch_merge_t(const KernelArgs& a, int, const MergeItem* merges, int n_merges, const MainEvents&,
                           hipStream_t stream) {
   if (n_merges > 0) {
     const int chunks = (G * DV / 4 + kMergeThreads - 1) / kMergeThreads;
-    hipLaunchKernelGGL((merge_kernel<T, DV, G>), dim3(n_merges, chunks), dim3(kMergeThreads), 0, stream, a, merges);
+    hipLaunchKernelGGL((merge_kernel<T, DV, G, PARTIAL>), dim3(n_merges, chunks), dim3(kMergeThreads), 0, stream, a,
+                       merges);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -6,12 +6,15 @@
 
 namespace pa {
 
+static_assert(kMlaHeads == kMlaGroupHeads, "an MLA work item covers one head group");
+
 bool gqa_family_pow2(int dtype, int d, int dv, int g, GqaFamily* out) {
   return gqa_family_lookup<1, 2, 4, 8, 16>(dtype, d, dv, g, out);
 }
 
-// Absorbed MLA: decode items (one query, one key range) and, in plans that
-// have them (PREFILL), chunked-prefill items (two queries, two waves each);
+// Absorbed MLA: decode items (one query and head group, one key range) and,
+// in plans that have them (PREFILL), chunked-prefill items (two queries of
+// one head group, two waves each);
 // a 72 KB LDS tile ring, two workgroups per CU.  Decode-only plans run the
 // instantiation without the prefill body, whose 128 output registers per
 // wave would otherwise set the register allocation of the decode body too.
@@ -87,7 +90,7 @@ int decode_waves(int g) {
 int mla_wgs_per_cu() { return 2; }
 
 bool mla_supported(int dtype, int h, int r, int p) {
-  return (dtype == 1 || dtype == 2) && h == kMlaHeads && r == kMlaRank && p == kMlaRope;
+  return (dtype == 1 || dtype == 2) && h >= 1 && r == kMlaRank && p == kMlaRope;
 }
 
 hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, const MainEvents& ev,
@@ -102,8 +105,10 @@ hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, con
 
 hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream) {
-  if (dtype == 1) return launch_merge_t<uint16_t, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, MainEvents{}, stream);
-  if (dtype == 2) return launch_merge_t<_Float16, kMlaRank, kMlaHeads>(a, 0, merges, n_merges, MainEvents{}, stream);
+  if (dtype == 1)
+    return launch_merge_t<uint16_t, kMlaRank, kMlaHeads, true>(a, 0, merges, n_merges, MainEvents{}, stream);
+  if (dtype == 2)
+    return launch_merge_t<_Float16, kMlaRank, kMlaHeads, true>(a, 0, merges, n_merges, MainEvents{}, stream);
   return hipErrorInvalidValue;
 }
 

@@ -56,7 +56,11 @@ int decode_wgs_per_cu(int g);
 int decode_waves(int g);
 int mla_wgs_per_cu();
 
-// Absorbed MLA: h query heads, latent rank r, position width p.
+// Absorbed MLA: h query heads, latent rank r, position width p.  The kernels
+// take the heads in groups of kMlaGroupHeads (the MFMA columns): a work item
+// or dQ item covers one group (the last one may be partial), and split
+// partials hold kMlaGroupHeads heads per slot.
+constexpr int kMlaGroupHeads = 16;
 bool mla_supported(int dtype, int h, int r, int p);
 // has_prefill: the item list holds chunked-prefill items.
 hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, const MainEvents& ev,

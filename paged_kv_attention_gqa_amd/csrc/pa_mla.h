@@ -1,5 +1,6 @@
-// Absorbed-MLA decode body (16-bit MFMA, bf16 or f16): one query, all H = 16 heads, one
-// contiguous range of its visible keys.
+// Absorbed-MLA decode body (16-bit MFMA, bf16 or f16): one query, one group of H = 16 of
+// its heads (heads 16 g .. 16 g + 15 of item kvh = g; the last group of a head count
+// that is no multiple of 16 is partial), one contiguous range of its visible keys.
 //
 // Definition followed: ruDNN 0.1.107 paged_attention/mod.rs `DevicePlan::mla`
 // -- one shared latent head [pages, page_size, 1, R] serves as key and value,
@@ -122,6 +123,9 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   const bool q_ok = !PREFILL || wq < it.q_count;
   const int qi = it.q_begin + (PREFILL ? min(wq, it.q_count - 1) : 0);
   const int qpos = PREFILL ? a.q_pos[qi] : 0;
+  const int head = H * it.kvh + n;  // this lane's query head (its MFMA column)
+  const bool head_ok = head < a.hq;  // columns past the last head compute a copy of it, unstored
+  const uint64_t hrow = (uint64_t)qi * a.hq + min(head, a.hq - 1);
   const int dim0 = DW * (PREFILL ? wave % kMlaWavesPerQuery : wave);  // first output dim of this wave
   const int tb = it.tok_begin, te = it.tok_end;
   const int ps = 1 << a.page_shift;
@@ -141,8 +145,8 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   frag_t qa[QA], qp[QP > 0 ? QP : 1];
   short4_t qp16 = {};
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((uint64_t)qi * H + n) * R;
-    const uint16_t* prow = reinterpret_cast<const uint16_t*>(a.qr) + ((uint64_t)qi * H + n) * P;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + hrow * R;
+    const uint16_t* prow = reinterpret_cast<const uint16_t*>(a.qr) + hrow * P;
 #pragma unroll
     for (int k = 0; k < QA; ++k) qa[k] = *reinterpret_cast<const frag_t*>(qrow + 32 * (ks0 + k) + 8 * c);
 #pragma unroll
@@ -353,9 +357,9 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
 
   // O^T lane (n, c) element r is dim dim0 + 16 b + 4 c + r of head n
   if (PREFILL || it.slot < 0) {
-    if (PREFILL && !q_ok) return;
+    if ((PREFILL && !q_ok) || !head_ok) return;
     const float inv = 1.f / l;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * H + n) * R + (PREFILL ? dim0 : DW * wave);
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + hrow * R + (PREFILL ? dim0 : DW * wave);
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       uint2 w;
@@ -363,8 +367,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       w.y = Pair16<T>::pack(o[b][2] * inv, o[b][3] * inv);
       *reinterpret_cast<uint2*>(orow + 16 * b + 4 * c) = w;
     }
-    if (a.lse && (PREFILL ? wave % kMlaWavesPerQuery : wave) == 0 && c == 0)
-      a.lse[(uint64_t)qi * H + n] = m * a.scale + logf(lx);
+    if (a.lse && (PREFILL ? wave % kMlaWavesPerQuery : wave) == 0 && c == 0) a.lse[hrow] = m * a.scale + logf(lx);
   } else {
     float* dst = a.ws_o + ((uint64_t)it.slot * H + n) * R + DW * wave;
 #pragma unroll

@@ -61,6 +61,12 @@ __device__ __forceinline__ floatx16_t mfma_32x32x16(const frag_t& a, const frag_
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
+// LDS address of a generic pointer into LDS: its low 32 bits (the LDS
+// aperture of the flat address space starts on a 4 GB boundary).  Taken by
+// truncation rather than an address-space cast, whose null check hipcc for
+// gfx950 can emit as a compare that fails instruction verification.
+__device__ __forceinline__ uint32_t lds_address(const void* p) { return (uint32_t)(size_t)p; }
+
 // 16 bytes from global memory to LDS at (wave-uniform base) + 16 * lane
 // (global_load_lds_dwordx4; M0 holds the LDS base).
 //
@@ -71,20 +77,20 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 // the DMA is ordered by the callers' own s_waitcnt vmcnt + barrier pairs.  The
 // instruction writes no VGPR, so there is no in-flight register to track.
 __device__ __forceinline__ void load_to_lds(const void* src, char* lds_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds_base);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_address(lds_base));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
 }
 // The same with the non-temporal hint, for data read once (MLA latent and
 // rotary rows); prefill tiles are shared by the query tiles of a sequence
 // through L2 and keep the default policy (nt measured 1-6% slower there).
 __device__ __forceinline__ void load_to_lds_stream(const void* src, char* lds_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds_base);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_address(lds_base));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(lds) : "m0");
 }
 // The same load from (wave-uniform base) + 32-bit per-lane byte offset
 // (global_load_lds_dwordx4 with a scalar base address).
 __device__ __forceinline__ void load_to_lds_sv(const char* base, uint32_t off, char* lds_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_t*)lds_base);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_address(lds_base));
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds) : "m0");
 }
 

@@ -332,6 +332,23 @@ def config_bf16_mla_decode(seed: int = 5) -> MlaBatch:
                     H, R, P, 1.0 / math.sqrt(576.0), True, 0, q_abs, q_rope, latent, kpos, seed, 16)
 
 
+def config_bf16_mla_decode_h128(seed: int = 5) -> MlaBatch:
+    """The MLA decode shape with all 128 query heads of a DeepSeek-V3-sized
+    model on one GPU (a workload of this library): 64 sequences, one query
+    each at L-1, H=128, R=512, P=64, contexts uniform in [1024, 16384], page
+    64, unit-RMS latent rows, scale 1/sqrt(576), causal."""
+    rng = np.random.default_rng(seed)
+    S, H, R, P, ps = 64, 128, 512, 64, 64
+    seq_lens = rng.integers(1024, 16384 + 1, size=S).astype(np.int32)
+    bt, pool, _ = _tables(rng, seq_lens, ps)
+    q_abs = _normal(rng, (S, H, R), "bf16")
+    q_rope = _normal(rng, (S, H, P), "bf16")
+    latent = _unit_rms(rng, (pool, ps, 1, R))
+    kpos = _normal(rng, (pool, ps, 1, P), "bf16")
+    return MlaBatch("bf16_mla_decode_h128", "bf16", seq_lens, _packed([1] * S), seq_lens - 1, bt, ps, pool,
+                    H, R, P, 1.0 / math.sqrt(576.0), True, 0, q_abs, q_rope, latent, kpos, seed, 16)
+
+
 def config_bf16_chunked_prefill_d192(seed: int = 7) -> PagedBatch:
     """The chunked-prefill shape with K rows of 192 and V rows of 128 (a
     workload of this library): 8 sequences, history uniform in [0, 4096] plus a
@@ -374,6 +391,7 @@ CONFIGS: Dict[str, Callable] = {
     "bf16_chunked_prefill": config_bf16_chunked_prefill,
     "bf16_mixed_batch": config_bf16_mixed_batch,
     "bf16_mla_decode": config_bf16_mla_decode,
+    "bf16_mla_decode_h128": config_bf16_mla_decode_h128,
     "bf16_mla_chunked_prefill": config_bf16_mla_chunked_prefill,
     "bf16_chunked_prefill_d192": config_bf16_chunked_prefill_d192,
 }

@@ -39,10 +39,49 @@ def test_random_mla_parity(i, split_tokens):
     _parity(m, split_tokens=split_tokens)
 
 
+MLA_HEAD_CASES = [
+    (128, dict(page_size=64, q_counts=(1, 1, 1), max_len=3000)),               # a full head count on one GPU
+    (32, dict(page_size=16, q_counts=(1, 1), max_len=900)),
+    (20, dict(page_size=64, q_counts=(1, 9, 1), max_len=1500)),                # partial last group, a chunk
+    (8, dict(page_size=64, q_counts=(1, 6), max_len=1500, window=300)),
+    (1, dict(page_size=32, q_counts=(3, 1), max_len=700, causal=False)),
+    (48, dict(page_size=64, q_counts=(0, 12, 1), histories=[50, 600, 90])),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("split_tokens", [0, 64])
+@pytest.mark.parametrize("i", range(len(MLA_HEAD_CASES)))
+def test_mla_head_counts_parity(i, split_tokens, dtype):
+    """Head counts other than 16: the heads run in groups of 16 (the MFMA
+    columns), the last group partial; every output element is written (the
+    output starts as NaN) and matches the oracle."""
+    heads, kw = MLA_HEAD_CASES[i]
+    m = random_mla_batch(3200 + i, heads=heads, dtype=dtype, **kw)
+    run = MlaRun(m, split_tokens=split_tokens)
+    run.out.fill_(float("nan"))
+    run.lse.fill_(float("nan"))
+    run()
+    out, lse = run.result()
+    ref_o, ref_l = oracle.mla(m)
+    assert_close(out, ref_o, dtype)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-3)
+
+
 def test_mla_decode_full_size_all_rows():
     m = config_bf16_mla_decode()
     run = _parity(m)
     assert run.info["decode_items"] >= 64 and run.info["split_rows"] > 0
+
+
+@pytest.mark.timeout(600)
+def test_mla_decode_h128_full_size_all_rows():
+    """The MLA decode shape with 128 query heads (eight head groups reading
+    the same latent rows): every output element and lse against the oracle."""
+    from synth import config_bf16_mla_decode_h128
+    m = config_bf16_mla_decode_h128()
+    run = _parity(m)
+    assert run.info["decode_items"] >= 64 * 8 and run.info["split_rows"] > 0
 
 
 def test_mla_window_one_returns_own_latent_bitwise():

@@ -90,6 +90,18 @@ def test_mla_backward_parity(i, dtype):
         assert np.array_equal(g, h, equal_nan=True)
 
 
+@pytest.mark.parametrize("heads,kw", [
+    (32, dict(page_size=64, q_counts=(1, 20, 1), max_len=600)),
+    (20, dict(page_size=16, q_counts=(9, 1), max_len=500, window=100)),
+    (1, dict(page_size=64, q_counts=(1, 3), max_len=300)),
+])
+def test_mla_backward_head_counts(heads, kw):
+    """Head counts other than 16: dQ items per group of 16 heads, and every
+    dK/dV block item summing all head groups of its queries."""
+    m = random_mla_batch(9900 + heads, heads=heads, dtype="bf16", **kw)
+    _parity(m, 9950 + heads)
+
+
 def test_mla_backward_unreferenced_rows_are_zero():
     """Pool rows that no visible key of any query lands on (extra pages, tail
     slots, keys before a window) get gradient exactly zero."""

@@ -63,7 +63,8 @@ def plan_of(s, num_cus):
 
 
 def check_plan(s, items, wg, merges, info, min_piece):
-    hkv = s["num_kv_heads"]
+    # work units of a row: KV heads, or for MLA groups of 16 query heads
+    hkv = -(-s["num_q_heads"] // 16) if s["mla"] else s["num_kv_heads"]
     Q = int(s["cu_q"][-1])
     hpi = info["heads_per_item"]
     assert hpi >= 1 and hkv % hpi == 0 and (hpi & (hpi - 1)) == 0
@@ -354,3 +355,38 @@ def test_sparse_layout_errors():
         pa.pa_sparse_workspace_bytes(p, 512, 64, 4)
     assert e.value.status == -1
     pa.pa_plan_destroy(p)
+
+
+@pytest.mark.parametrize("hq", [128, 20, 8])
+@pytest.mark.parametrize("num_cus", [256, 7])
+def test_mla_head_groups(hq, num_cus):
+    """MLA with other head counts: one unit per group of 16 query heads (the
+    last one partial), covering every (query, group) once; in balanced plans
+    the groups of one key range sit kXcds = 8 workgroups apart (one XCD), and
+    in mixed plans every item of a sequence lands on one XCD."""
+    rng = np.random.default_rng(6)
+    units = -(-hq // 16)
+    s = schedule(6, q_counts=[1] * 40, histories=list(rng.integers(1023, 16384, 40)), page_size=64, hq=hq, hkv=1,
+                 mla=True)
+    items, wg, merges, info = plan_of(s, num_cus)
+    check_plan(s, items, wg, merges, info, min_piece=256)
+    assert set(items[:, 1].tolist()) == set(range(units))
+    xcd_of = {}
+    for b in range(len(wg) - 1):
+        for i in range(wg[b], wg[b + 1]):
+            key = (int(items[i, 3]), int(items[i, 5]), int(items[i, 6]))
+            xcd_of.setdefault(key, set()).add(b % 8)
+    if units > 1:
+        assert all(len(x) == 1 for x in xcd_of.values())
+    assert all(m[1] < units and m[4] == units for m in merges.tolist())
+
+    s = schedule(7, q_counts=[40, 1, 9, 1], histories=[100, 5000, 700, 20], page_size=16, hq=hq, hkv=1, mla=True)
+    items, wg, merges, info = plan_of(s, num_cus)
+    check_plan(s, items, wg, merges, info, min_piece=1)
+    assert info["prefill_items"] == units * (20 + 5)
+    assert np.array_equal(wg, np.arange(len(items) + 1))
+    seq_xcd = {}
+    for i, it in enumerate(items.tolist()):
+        if it[0] == KIND_PREFILL:
+            seq_xcd.setdefault(it[2], set()).add(i % 8)
+    assert all(len(x) == 1 for x in seq_xcd.values())
