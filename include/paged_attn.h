@@ -270,9 +270,10 @@ int pa_attention_fwd_noalloc(const pa_plan* plan, int32_t dtype, const void* q, 
  *   latent  [num_pages, page_size, 1, rank]
  *   kpos    [num_pages, page_size, 1, rope_dim]
  *   out     [Q, H, rank]        lse NULL or f32 [Q, H]
- *   rank    1..1024, rope_dim 1..256 (this build runs bf16 and f16 with
- *           rank = 512, rope_dim = 64 and any H >= 1; the kernels take the
- *           heads in groups of 16, so H = 16 n uses every MFMA column)
+ *   rank    1..1024, rope_dim 1..256, any H >= 1, dtype PA_F32, PA_BF16 or
+ *           PA_F16.  16-bit data with rank 512 and rope_dim 64 runs on MFMA
+ *           (the heads in groups of 16, so H = 16 n uses every MFMA column);
+ *           every other shape and f32 run on a vector-ALU kernel (fp32)
  *   scale   from the model's original query/key head size, not the latent
  *           rank (e.g. 1/sqrt(rank + rope_dim))
  *

@@ -682,7 +682,7 @@ pa::MainEvents main_events_of(void* const* ev) {
 // Common forward path once the kernel family is chosen.
 struct FwdCall {
   const pa_plan* plan;
-  int dtype, d, dv;
+  int dtype, d, dv;  // MLA: d = latent rank, dv = rotary width
   pa::KernelArgs args;
   pa::MainEvents events;
   hipStream_t stream;
@@ -896,13 +896,13 @@ static int launch_common(FwdCall& c, bool is_mla) {
   if (p->Q == 0 || p->items.empty()) return ok();
   hipError_t e;
   if (is_mla) {
-    e = pa::launch_mla_main(c.dtype, p->n_prefill > 0, c.args, c.events, c.stream);
+    e = pa::launch_mla_main(c.dtype, c.d, c.dv, p->n_prefill > 0, c.args, c.events, c.stream);
   } else {
     e = pa::launch_gqa_main(c.dtype, c.d, c.dv, p->group(), p->n_prefill > 0, c.args, c.events, c.stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (!p->merges.empty()) {
-    e = is_mla ? pa::launch_mla_merge(c.dtype, c.args, p->d_merges, (int)p->merges.size(), c.stream)
+    e = is_mla ? pa::launch_mla_merge(c.dtype, c.d, c.dv, c.args, p->d_merges, (int)p->merges.size(), c.stream)
                : pa::launch_gqa_merge(c.dtype, c.d, c.dv, p->group(), c.args, p->d_merges, (int)p->merges.size(),
                                       c.stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
@@ -1026,7 +1026,7 @@ int pa_mla_fwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   if (rc == PA_OK) rc = check_aligned({e_out, e_qa, e_qr, e_lat, e_kp});
   if (rc != PA_OK) return rc;
 
-  FwdCall c{plan, dtype, rank, rank, {}, main_events_of(main_events), reinterpret_cast<hipStream_t>(stream)};
+  FwdCall c{plan, dtype, rank, rope_dim, {}, main_events_of(main_events), reinterpret_cast<hipStream_t>(stream)};
   pa::KernelArgs& a = c.args;
   a.q = q_abs;
   a.k = latent;
@@ -1195,7 +1195,7 @@ int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   if (rank <= 0 || rank > 1024) return fail(PA_ERR_SHAPE, "latent rank %d outside [1, 1024]", rank);
   if (rope_dim <= 0 || rope_dim > 256) return fail(PA_ERR_SHAPE, "rotary width rope_dim %d outside [1, 256]", rope_dim);
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
-  if (!pa::mla_supported(dtype, plan->hq, rank, rope_dim))
+  if (!pa::mla_bwd_supported(dtype, plan->hq, rank, rope_dim))
     return fail(PA_ERR_UNSUPPORTED, "no MLA backward kernel for dtype %d, H=%d, rank=%d, rope_dim=%d", dtype, plan->hq,
                 rank, rope_dim);
   size_t need = 0;

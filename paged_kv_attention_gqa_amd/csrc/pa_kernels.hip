@@ -89,12 +89,19 @@ int decode_waves(int g) {
 // two 4-wave workgroups per CU (72 KB of LDS each, waves_per_eu(2))
 int mla_wgs_per_cu() { return 2; }
 
+namespace {
+bool mla_mfma_shape(int dtype, int r, int p) { return (dtype == 1 || dtype == 2) && r == kMlaRank && p == kMlaRope; }
+}  // namespace
+
 bool mla_supported(int dtype, int h, int r, int p) {
-  return (dtype == 1 || dtype == 2) && h >= 1 && r == kMlaRank && p == kMlaRope;
+  return dtype >= 0 && dtype <= 2 && h >= 1 && r >= 1 && r <= kMlaMaxRank && p >= 1 && p <= kMlaMaxRope;
 }
 
-hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, const MainEvents& ev,
+bool mla_bwd_supported(int dtype, int h, int r, int p) { return h >= 1 && mla_mfma_shape(dtype, r, p); }
+
+hipError_t launch_mla_main(int dtype, int r, int p, bool has_prefill, const KernelArgs& a, const MainEvents& ev,
                            hipStream_t stream) {
+  if (!mla_mfma_shape(dtype, r, p)) return launch_mla_generic(dtype, r, p, a, ev, stream);
   constexpr int threads = kMlaWaves * kWave;
   if (dtype == 1 && has_prefill) return launch_main(mla_kernel<uint16_t, true>, a.n_wg, threads, a, ev, stream);
   if (dtype == 1) return launch_main(mla_kernel<uint16_t, false>, a.n_wg, threads, a, ev, stream);
@@ -103,8 +110,9 @@ hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, con
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
+hipError_t launch_mla_merge(int dtype, int r, int p, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream) {
+  if (!mla_mfma_shape(dtype, r, p)) return launch_mla_generic_merge(dtype, r, a, merges, n_merges, stream);
   if (dtype == 1)
     return launch_merge_t<uint16_t, kMlaRank, kMlaHeads, true>(a, 0, merges, n_merges, MainEvents{}, stream);
   if (dtype == 2)

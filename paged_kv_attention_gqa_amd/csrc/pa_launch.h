@@ -61,12 +61,22 @@ int mla_wgs_per_cu();
 // or dQ item covers one group (the last one may be partial), and split
 // partials hold kMlaGroupHeads heads per slot.
 constexpr int kMlaGroupHeads = 16;
+constexpr int kMlaMaxRank = 1024, kMlaMaxRope = 256;
+// Forward: any dtype, 1 <= r <= kMlaMaxRank, 1 <= p <= kMlaMaxRope, h >= 1
+// (16-bit data with r = 512, p = 64 on MFMA, the rest on the vector kernel).
 bool mla_supported(int dtype, int h, int r, int p);
+// Backward: 16-bit data, r = 512, p = 64, h >= 1.
+bool mla_bwd_supported(int dtype, int h, int r, int p);
 // has_prefill: the item list holds chunked-prefill items.
-hipError_t launch_mla_main(int dtype, bool has_prefill, const KernelArgs& a, const MainEvents& ev,
+hipError_t launch_mla_main(int dtype, int r, int p, bool has_prefill, const KernelArgs& a, const MainEvents& ev,
                            hipStream_t stream);
-hipError_t launch_mla_merge(int dtype, const KernelArgs& a, const MergeItem* merges, int n_merges,
+hipError_t launch_mla_merge(int dtype, int r, int p, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream);
+// The vector-ALU MLA forward and its merge (pa_mla_generic.hip).
+hipError_t launch_mla_generic(int dtype, int r, int p, const KernelArgs& a, const MainEvents& ev,
+                              hipStream_t stream);
+hipError_t launch_mla_generic_merge(int dtype, int r, const KernelArgs& a, const MergeItem* merges, int n_merges,
+                                    hipStream_t stream);
 
 // Paged K/V append: rows (i, h) of k_new [Q, heads, k_row_bytes] and v_new
 // [Q, heads, v_row_bytes] to pool rows (slot_of[i], h).  Row sizes are

@@ -71,16 +71,17 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
-def _chunked(rng: np.random.Generator, n: int, fill):
-    """Run fill(child_generator, start, end) over fixed 4M-element chunks.
-    Each chunk draws from its own child stream spawned from one seed taken
-    from `rng`, so the values do not depend on the thread count."""
+def _chunked(rng: np.random.Generator, n: int, fill, chunk: int = _CHUNK):
+    """Run fill(child_generator, start, end) over fixed chunks of `chunk`
+    (4M) elements.  Each chunk draws from its own child stream spawned from
+    one seed taken from `rng`, so the values do not depend on the thread
+    count."""
     seed = int(rng.integers(0, 2 ** 63 - 1))
-    starts = list(range(0, n, _CHUNK))
+    starts = list(range(0, n, chunk))
     children = np.random.SeedSequence(seed).spawn(len(starts))
 
     def work(k):
-        fill(np.random.default_rng(children[k]), starts[k], min(n, starts[k] + _CHUNK))
+        fill(np.random.default_rng(children[k]), starts[k], min(n, starts[k] + chunk))
 
     if len(starts) <= 1:
         for k in range(len(starts)):
@@ -300,19 +301,19 @@ def config_bf16_mixed_batch(seed: int = 4) -> PagedBatch:
 
 def _unit_rms(rng: np.random.Generator, shape, dtype: str = "bf16") -> np.ndarray:
     """N(0,1) rows rescaled in float32 to unit RMS (no epsilon, no weight),
-    then rounded to the 16-bit storage type."""
-    to_bits = f32_to_bf16_bits if dtype == "bf16" else f32_to_f16_bits
+    then rounded to the storage type (kept as is for f32)."""
+    to_bits = {"bf16": f32_to_bf16_bits, "f16": f32_to_f16_bits, "f32": lambda x: x}[dtype]
     width = shape[-1]
     rows = int(np.prod(shape[:-1]))
-    out = np.empty(rows * width, dtype=np.uint16)
-    assert _CHUNK % width == 0
+    out = np.empty(rows * width, dtype=np.float32 if dtype == "f32" else np.uint16)
 
     def fill(g, s, e):
         x = g.standard_normal(e - s, dtype=np.float32).reshape(-1, width)
         rms = np.sqrt(np.mean(x * x, axis=1, dtype=np.float32), dtype=np.float32)
         out[s:e] = to_bits(x / rms[:, None]).reshape(-1)
 
-    _chunked(rng, rows * width, fill)
+    # whole rows per chunk (the chunk size stays 4M elements for widths dividing it)
+    _chunked(rng, rows * width, fill, _CHUNK if _CHUNK % width == 0 else _CHUNK // width * width)
     return out.reshape(shape)
 
 
@@ -452,10 +453,10 @@ def random_mla_batch(seed: int, *, heads: int = 16, r: int = 512, p: int = 64, p
                      q_counts=(1, 1, 1), histories=None, max_len: int = 700, causal: bool = True,
                      window: int = 0, extra_pages: int = 2, poison: bool = True,
                      max_splits: int = 16, dtype: str = "bf16") -> MlaBatch:
-    """A small ragged absorbed-MLA batch (bf16 or f16), laid out like the MLA
-    workload above, with NaN in unreferenced pages and tail slots."""
-    if dtype not in ("bf16", "f16"):
-        raise ValueError(f"MLA batches are 16-bit, not {dtype!r}")
+    """A small ragged absorbed-MLA batch (f32, bf16 or f16), laid out like the
+    MLA workload above, with NaN in unreferenced pages and tail slots."""
+    if dtype not in ("f32", "bf16", "f16"):
+        raise ValueError(f"unknown storage type {dtype!r}")
     rng = np.random.default_rng(seed)
     S = len(q_counts)
     if histories is None:

@@ -74,6 +74,49 @@ def test_mla_decode_full_size_all_rows():
     assert run.info["decode_items"] >= 64 and run.info["split_rows"] > 0
 
 
+MLA_SHAPE_CASES = [
+    ("f32", 16, 512, 64, dict(page_size=64, q_counts=(1, 1, 7), max_len=1200)),
+    ("f32", 128, 512, 64, dict(page_size=16, q_counts=(1, 3), max_len=600)),
+    ("bf16", 16, 256, 32, dict(page_size=64, q_counts=(1, 9, 1), max_len=1500)),      # a smaller latent
+    ("f16", 40, 128, 32, dict(page_size=32, q_counts=(2, 1), max_len=900, window=200)),
+    ("bf16", 5, 100, 7, dict(page_size=1, q_counts=(1, 4), max_len=150, causal=False)),  # odd widths
+    ("f32", 20, 1024, 256, dict(page_size=64, q_counts=(1, 1, 6), max_len=700)),       # the widest rows
+]
+
+
+@pytest.mark.parametrize("split_tokens", [0, 64])
+@pytest.mark.parametrize("i", range(len(MLA_SHAPE_CASES)))
+def test_mla_other_shapes_and_f32(i, split_tokens):
+    """f32 data and latent / rotary widths other than 512 / 64 (the vector
+    kernel), decode rows and chunks, split and unsplit: every element and
+    lse against the oracle, output and lse starting as NaN."""
+    dtype, heads, r, p, kw = MLA_SHAPE_CASES[i]
+    m = random_mla_batch(3300 + i, heads=heads, r=r, p=p, dtype=dtype, **kw)
+    run = MlaRun(m, split_tokens=split_tokens)
+    run.out.fill_(float("nan"))
+    run.lse.fill_(float("nan"))
+    run()
+    out, lse = run.result()
+    ref_o, ref_l = oracle.mla(m)
+    assert_close(out, ref_o, dtype)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-4 if dtype == "f32" else 1e-3)
+
+
+def test_mla_backward_refuses_shapes_without_kernel():
+    """The backward runs 16-bit data with rank 512 and rotary width 64 only:
+    other shapes get PA_ERR_UNSUPPORTED before anything is launched."""
+    import torch
+    import paged_kv_attention_gqa_amd as pa
+    m = random_mla_batch(3400, r=256, p=32, q_counts=(1, 2), max_len=200)
+    run = MlaRun(m)
+    run()
+    z = torch.zeros_like(run.out)
+    with pytest.raises(pa.PaError, match="PA_ERR_UNSUPPORTED"):
+        pa.pa_mla_bwd(run.plan, run.q_abs, run.q_rope, run.latent, run.kpos, run.out, run.lse, z, z.clone(),
+                      torch.zeros_like(run.q_rope), torch.zeros_like(run.latent), torch.zeros_like(run.kpos),
+                      scale=m.scale, workspace=None)
+
+
 @pytest.mark.timeout(600)
 def test_mla_decode_h128_full_size_all_rows():
     """The MLA decode shape with 128 query heads (eight head groups reading

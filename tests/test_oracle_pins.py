@@ -232,7 +232,7 @@ def test_logsumexp_combines_over_disjoint_key_ranges():
     np.testing.assert_allclose(comb, full_o, rtol=1e-12, atol=1e-13)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_mla_equals_mqa_over_concatenated_key(dtype):
     """ruDNN `DevicePlan::mla` passes the latent as key and value and adds a
     position term to the score: that is single-KV-head attention whose key is
