@@ -208,10 +208,12 @@ int pa_plan_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, size_t* byt
  *   out          [Q, Hq, v_head_dim], written (must not overlap any input)
  *   lse          NULL or f32 [Q, Hq]: natural-log logsumexp of the scaled,
  *                masked scores of each row
- *   head_dim     D, 1..1024; v_head_dim Dv, 1..1024 (this build runs
- *                D = Dv in {64, 128, 256} and D = 192 with Dv = 128, with
- *                group sizes Hq / Hkv in {1, 2, 3, 4, 5, 6, 7, 8, 12, 16};
- *                other pairs and group sizes give PA_ERR_UNSUPPORTED)
+ *   head_dim     D, 1..1024; v_head_dim Dv, 1..1024, any group size
+ *                Hq / Hkv.  D = Dv in {64, 128, 256} and D = 192 with
+ *                Dv = 128 at group sizes {1, 2, 3, 4, 5, 6, 7, 8, 12, 16}
+ *                run on the specialised decode and MFMA kernels; every
+ *                other shape runs on a vector-ALU kernel (fp32), which takes
+ *                the query heads of a KV head in groups of 16
  *   scale        finite and > 0 (e.g. 1/sqrt(D))
  *   workspace    f32 scratch of >= pa_plan_workspace_bytes(plan, v_head_dim)
  *                bytes, 256-byte aligned; may be NULL when that size is 0
@@ -358,7 +360,8 @@ int pa_plan_bwd_workspace_bytes(const pa_plan* plan, int32_t dtype, int32_t head
  *                no visible key of any query lands on are zero
  *   workspace    >= pa_plan_bwd_workspace_bytes bytes, 256-byte aligned
  *
- * Head sizes as for pa_attention_fwd (group sizes 1, 2, 4, 8, 16).  Errors:
+ * Head sizes D = Dv in {64, 128, 256} and 192 / 128, group sizes 1, 2, 4, 8,
+ * 16 (other shapes give PA_ERR_UNSUPPORTED).  Errors:
  * PA_ERR_INVALID for MLA plans (pa_mla_bwd), PA_ERR_UNSUPPORTED for missing
  * kernels;
  * PA_ERR_WORKSPACE,

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <map>
+#include <tuple>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -128,11 +129,16 @@ struct pa_plan {
   const int32_t* d_zero_runs = nullptr;
 
   int group() const { return hq / hkv; }
-  // Work units of one query row: its KV heads (GQA), or its query heads in
-  // groups of kMlaGroupHeads (MLA: one shared latent head; the last group
-  // may be partial), and the query heads of one unit.
-  int units() const { return mla ? (hq + pa::kMlaGroupHeads - 1) / pa::kMlaGroupHeads : hkv; }
-  int unit_heads() const { return mla ? pa::kMlaGroupHeads : hq / hkv; }
+  // Work units of one query row.  GQA with G <= kGenericUnitHeads: its KV
+  // heads (a unit: one KV head and its G query heads).  MLA (one shared
+  // latent head) and GQA with a larger G: the query heads of each KV head
+  // in groups of kGenericUnitHeads (= kMlaGroupHeads), nsub groups per KV
+  // head, the last one possibly partial.  unit_heads: query heads per unit
+  // (and per split-partial slot).
+  bool grouped() const { return mla || hq / hkv > pa::kGenericUnitHeads; }
+  int nsub() const { return grouped() ? (group() + pa::kGenericUnitHeads - 1) / pa::kGenericUnitHeads : 1; }
+  int units() const { return hkv * nsub(); }
+  int unit_heads() const { return grouped() ? pa::kGenericUnitHeads : group(); }
 };
 
 namespace {
@@ -246,15 +252,16 @@ int64_t item_cost(const WorkItem& w) {
 // built per XCD and interleaved.  Units of work are dealt, largest first, to
 // the XCD with the least estimated work so far; a unit is one decode item or
 // all prefill tiles of one (sequence, KV head), which read the same keys and
-// so share one L2 (MLA: all prefill tiles of one sequence, and the decode
-// items of all head groups of one key range).  Each XCD then runs its items longest first; XCDs with
+// so share one L2 (with head groups, as in MLA: all prefill tiles of one
+// sequence and KV head, and the decode items of all head groups of one KV
+// head and key range).  Each XCD then runs its items longest first; XCDs with
 // fewer items are padded with empty items.
 constexpr int kXcds = 8;
 void order_items(pa_plan* p, const std::vector<WorkItem>& pre, const std::vector<WorkItem>& dec) {
   std::vector<std::vector<WorkItem>> units;
   std::vector<int64_t> unit_cost;
-  std::map<std::pair<int, int>, size_t> group_of;
-  auto add = [&](std::pair<int, int> key, const WorkItem& w) {
+  std::map<std::tuple<int, int, int>, size_t> group_of;
+  auto add = [&](std::tuple<int, int, int> key, const WorkItem& w) {
     auto g = group_of.find(key);
     if (g == group_of.end()) {
       g = group_of.emplace(key, units.size()).first;
@@ -264,11 +271,12 @@ void order_items(pa_plan* p, const std::vector<WorkItem>& pre, const std::vector
     units[g->second].push_back(w);
     unit_cost[g->second] += item_cost(w);
   };
-  for (const WorkItem& w : pre) add({w.seq, p->mla ? 0 : w.kvh}, w);
+  const int nsub = p->nsub();
+  for (const WorkItem& w : pre) add({w.seq, w.kvh / nsub, 0}, w);
   for (const WorkItem& w : dec) {
-    if (p->mla) {
-      // the head groups of one MLA key range read the same latent rows
-      add({-1 - w.q_begin, w.tok_begin}, w);
+    if (nsub > 1) {
+      // the head groups of one KV head and key range read the same K/V rows
+      add({-1 - w.q_begin, w.tok_begin, w.kvh / nsub}, w);
     } else {
       units.push_back({w});
       unit_cost.push_back(item_cost(w));
@@ -393,8 +401,8 @@ void plan_balanced(pa_plan* p, int slots, int min_piece) {
       }
     p->wg_first.push_back((int32_t)p->items.size());
   };
-  if (p->mla && U > 1) {
-    // the head groups of one group of pieces read the same latent rows: put
+  if (p->nsub() > 1) {
+    // the head groups of one group of pieces read the same K/V rows: put
     // their workgroups kXcds apart (one XCD, one L2), the groups of a block
     // of kXcds side by side; missing groups of the last block leave empty
     // workgroups
@@ -453,7 +461,7 @@ void build_work(pa_plan* p) {
       }
     } else {
       const int tile_q = std::max(1, kPrefillRows / G);
-      for (int kvh = 0; kvh < p->hkv; ++kvh)
+      for (int kvh = 0; kvh < p->units(); ++kvh)
         for (int t0 = q0; t0 < q1; t0 += tile_q) {
           const int t1 = std::min(q1, t0 + tile_q);
           int lo = INT32_MAX, hi = -1;
@@ -686,6 +694,8 @@ struct FwdCall {
   pa::KernelArgs args;
   pa::MainEvents events;
   hipStream_t stream;
+  bool generic = false;  // GQA on the vector kernel (pa_generic.hip), with this shape
+  pa::GenericShape shape{};
 };
 
 }  // namespace
@@ -895,16 +905,19 @@ static int launch_common(FwdCall& c, bool is_mla) {
   const pa_plan* p = c.plan;
   if (p->Q == 0 || p->items.empty()) return ok();
   hipError_t e;
-  if (is_mla) {
+  if (c.generic) {
+    e = pa::launch_generic(c.dtype, c.shape, c.args, c.events, c.stream);
+  } else if (is_mla) {
     e = pa::launch_mla_main(c.dtype, c.d, c.dv, p->n_prefill > 0, c.args, c.events, c.stream);
   } else {
     e = pa::launch_gqa_main(c.dtype, c.d, c.dv, p->group(), p->n_prefill > 0, c.args, c.events, c.stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (!p->merges.empty()) {
-    e = is_mla ? pa::launch_mla_merge(c.dtype, c.d, c.dv, c.args, p->d_merges, (int)p->merges.size(), c.stream)
-               : pa::launch_gqa_merge(c.dtype, c.d, c.dv, p->group(), c.args, p->d_merges, (int)p->merges.size(),
-                                      c.stream);
+    const int nm = (int)p->merges.size();
+    e = c.generic ? pa::launch_generic_merge(c.dtype, c.shape, c.args, p->d_merges, nm, c.stream)
+        : is_mla  ? pa::launch_mla_merge(c.dtype, c.d, c.dv, c.args, p->d_merges, nm, c.stream)
+                  : pa::launch_gqa_merge(c.dtype, c.d, c.dv, p->group(), c.args, p->d_merges, nm, c.stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return ok();
@@ -944,13 +957,11 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   size_t need;
   rc = check_workspace(plan, v_head_dim, workspace, workspace_bytes, &ws_o, &ws_ml, &need);
   if (rc != PA_OK) return rc;
+  // the specialised kernels when they cover the plan's items, else the
+  // vector kernel (any group size and head sizes up to 1024)
   const int G = plan->group();
-  if (plan->n_decode > 0 && !pa::gqa_supported(dtype, head_dim, v_head_dim, G))
-    return fail(PA_ERR_UNSUPPORTED, "no decode kernel for dtype %d, D=%d, Dv=%d, G=%d", dtype, head_dim, v_head_dim,
-                G);
-  if (plan->n_prefill > 0 && !pa::prefill_supported(dtype, head_dim, v_head_dim, G))
-    return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, D=%d, Dv=%d, G=%d", dtype, head_dim,
-                v_head_dim, G);
+  const bool generic = plan->grouped() || (plan->n_decode > 0 && !pa::gqa_supported(dtype, head_dim, v_head_dim, G)) ||
+                       (plan->n_prefill > 0 && !pa::prefill_supported(dtype, head_dim, v_head_dim, G));
   const size_t es = dtype == PA_F32 ? 4 : 2;
   const size_t slots = (size_t)plan->num_pages * plan->ps * plan->hkv;
   const Extent e_out{out, (size_t)plan->Q * plan->hq * v_head_dim * es, "out"};
@@ -964,6 +975,8 @@ int pa_attention_fwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   if (rc != PA_OK) return rc;
 
   FwdCall c{plan, dtype, head_dim, v_head_dim, {}, main_events_of(main_events), reinterpret_cast<hipStream_t>(stream)};
+  c.generic = generic;
+  c.shape = pa::GenericShape{head_dim, 0, v_head_dim, G, plan->nsub(), plan->unit_heads(), 1 << plan->heads_shift, 0};
   pa::KernelArgs& a = c.args;
   a.q = q;
   a.k = k_pool;

@@ -7,6 +7,7 @@
 namespace pa {
 
 static_assert(kMlaHeads == kMlaGroupHeads, "an MLA work item covers one head group");
+static_assert(kGenericUnitHeads == kMlaGroupHeads, "MLA plans serve both MLA kernels");
 
 bool gqa_family_pow2(int dtype, int d, int dv, int g, GqaFamily* out) {
   return gqa_family_lookup<1, 2, 4, 8, 16>(dtype, d, dv, g, out);
@@ -91,6 +92,11 @@ int mla_wgs_per_cu() { return 2; }
 
 namespace {
 bool mla_mfma_shape(int dtype, int r, int p) { return (dtype == 1 || dtype == 2) && r == kMlaRank && p == kMlaRope; }
+// MLA on the vector kernel: one KV head (the latent), its H query heads in
+// units of 16, the value the latent itself
+GenericShape mla_generic_shape(const KernelArgs& a, int r, int p) {
+  return GenericShape{r, p, r, a.hq, (a.hq + kMlaGroupHeads - 1) / kMlaGroupHeads, kMlaGroupHeads, 1, 1};
+}
 }  // namespace
 
 bool mla_supported(int dtype, int h, int r, int p) {
@@ -101,7 +107,7 @@ bool mla_bwd_supported(int dtype, int h, int r, int p) { return h >= 1 && mla_mf
 
 hipError_t launch_mla_main(int dtype, int r, int p, bool has_prefill, const KernelArgs& a, const MainEvents& ev,
                            hipStream_t stream) {
-  if (!mla_mfma_shape(dtype, r, p)) return launch_mla_generic(dtype, r, p, a, ev, stream);
+  if (!mla_mfma_shape(dtype, r, p)) return launch_generic(dtype, mla_generic_shape(a, r, p), a, ev, stream);
   constexpr int threads = kMlaWaves * kWave;
   if (dtype == 1 && has_prefill) return launch_main(mla_kernel<uint16_t, true>, a.n_wg, threads, a, ev, stream);
   if (dtype == 1) return launch_main(mla_kernel<uint16_t, false>, a.n_wg, threads, a, ev, stream);
@@ -112,7 +118,7 @@ hipError_t launch_mla_main(int dtype, int r, int p, bool has_prefill, const Kern
 
 hipError_t launch_mla_merge(int dtype, int r, int p, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream) {
-  if (!mla_mfma_shape(dtype, r, p)) return launch_mla_generic_merge(dtype, r, a, merges, n_merges, stream);
+  if (!mla_mfma_shape(dtype, r, p)) return launch_generic_merge(dtype, mla_generic_shape(a, r, p), a, merges, n_merges, stream);
   if (dtype == 1)
     return launch_merge_t<uint16_t, kMlaRank, kMlaHeads, true>(a, 0, merges, n_merges, MainEvents{}, stream);
   if (dtype == 2)

@@ -72,11 +72,25 @@ hipError_t launch_mla_main(int dtype, int r, int p, bool has_prefill, const Kern
                            hipStream_t stream);
 hipError_t launch_mla_merge(int dtype, int r, int p, const KernelArgs& a, const MergeItem* merges, int n_merges,
                             hipStream_t stream);
-// The vector-ALU MLA forward and its merge (pa_mla_generic.hip).
-hipError_t launch_mla_generic(int dtype, int r, int p, const KernelArgs& a, const MainEvents& ev,
-                              hipStream_t stream);
-hipError_t launch_mla_generic_merge(int dtype, int r, const KernelArgs& a, const MergeItem* merges, int n_merges,
-                                    hipStream_t stream);
+
+// The vector-ALU forward for every shape the specialised kernels do not take
+// (pa_generic.hip).  Key rows are [k1 | k2] (d1 + d2 wide; GQA: d2 = 0, MLA:
+// latent | kpos), query rows [q1 | q2], value rows dv wide (v_is_k: the
+// first dv dims of k1, as the MLA latent).  Work unit u of a plan covers
+// query heads (u / nsub) g + (u % nsub) unit_heads .. + unit_heads - 1 (at
+// most g - (u % nsub) unit_heads of them) of KV head u / nsub; a decode
+// item covers hw consecutive units (nsub = 1).  Split partials hold
+// unit_heads heads per slot.
+constexpr int kGenericUnitHeads = 16;
+constexpr int kGenericMaxKeyWidth = kMlaMaxRank + kMlaMaxRope, kGenericMaxValueWidth = 1024;
+struct GenericShape {
+  int32_t d1, d2, dv, g, nsub, unit_heads, hw, v_is_k;
+};
+bool generic_shape_ok(const GenericShape& s);
+hipError_t launch_generic(int dtype, const GenericShape& s, const KernelArgs& a, const MainEvents& ev,
+                          hipStream_t stream);
+hipError_t launch_generic_merge(int dtype, const GenericShape& s, const KernelArgs& a, const MergeItem* merges,
+                                int n_merges, hipStream_t stream);
 
 // Paged K/V append: rows (i, h) of k_new [Q, heads, k_row_bytes] and v_new
 // [Q, heads, v_row_bytes] to pool rows (slot_of[i], h).  Row sizes are

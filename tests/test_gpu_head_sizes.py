@@ -105,11 +105,20 @@ def test_d192_dv128_prefill_window_one_bitwise():
                 assert np.array_equal(out[i, h], row[h // G]), (i, h)
 
 
-def test_head_size_pairs_without_kernels_are_refused():
+def test_head_size_pairs_without_kernels_run_on_the_vector_kernel():
+    """(D, Dv) = (128, 64) has no specialised kernel: the vector kernel runs
+    it, decode rows and a chunk, against the oracle."""
+    b = random_batch(6400, dtype="bf16", hq=8, hkv=2, d=128, dv=64, page_size=16, q_counts=(1, 1, 12), max_len=400)
+    _parity(b)
+
+
+def test_head_sizes_past_1024_are_refused():
     import torch
-    b = random_batch(6400, dtype="bf16", hq=8, hkv=2, d=128, dv=64, page_size=16, q_counts=(1, 1), max_len=100)
+    b = random_batch(6401, dtype="bf16", hq=2, hkv=1, d=64, page_size=16, q_counts=(1,), max_len=50)
     run = GqaRun(b)
+    q = torch.zeros((b.num_queries, b.hq, 1032), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(tuple(run.k.shape[:3]) + (1032,), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(pa.PaError) as e:
-        run()
-    assert e.value.status == -4
+        pa.pa_attention_fwd(run.plan, q, k, run.v, run.out, run.lse, scale=b.scale, workspace=run.workspace)
+    assert e.value.name == "PA_ERR_SHAPE"
     torch.cuda.synchronize()

@@ -173,11 +173,3 @@ def test_group_size_seven_f32_and_window_one_bitwise():
             for h in range(b.hq):
                 assert np.array_equal(out[i, h], row[h // 5]), (i, h)
 
-
-def test_unsupported_group_size_is_refused():
-    """G = 32 has no kernel in this build: refused before any launch."""
-    import paged_kv_attention_gqa_amd as pa
-    b = random_batch(2700, dtype="bf16", hq=32, hkv=1, d=128, page_size=16, q_counts=(1,), max_len=100)
-    with pytest.raises(pa.PaError) as e:
-        GqaRun(b)()
-    assert e.value.name == "PA_ERR_UNSUPPORTED"

@@ -63,8 +63,10 @@ def plan_of(s, num_cus):
 
 
 def check_plan(s, items, wg, merges, info, min_piece):
-    # work units of a row: KV heads, or for MLA groups of 16 query heads
-    hkv = -(-s["num_q_heads"] // 16) if s["mla"] else s["num_kv_heads"]
+    # work units of a row: KV heads, or (MLA, and groups of more than 16
+    # query heads) each KV head's query heads in groups of 16
+    G = s["num_q_heads"] // s["num_kv_heads"]
+    hkv = s["num_kv_heads"] * (-(-G // 16) if s["mla"] or G > 16 else 1)
     Q = int(s["cu_q"][-1])
     hpi = info["heads_per_item"]
     assert hpi >= 1 and hkv % hpi == 0 and (hpi & (hpi - 1)) == 0
@@ -390,3 +392,29 @@ def test_mla_head_groups(hq, num_cus):
         if it[0] == KIND_PREFILL:
             seq_xcd.setdefault(it[2], set()).add(i % 8)
     assert all(len(x) == 1 for x in seq_xcd.values())
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (72, 8), (71, 1)])
+@pytest.mark.parametrize("num_cus", [256, 7])
+def test_large_group_sizes_use_head_groups(hq, hkv, num_cus):
+    """G > 16: one work unit per group of 16 query heads of each KV head (the
+    last one partial), in balanced decode plans (the groups of one KV head
+    and piece on one XCD) and in mixed plans."""
+    G = hq // hkv
+    units = hkv * -(-G // 16)
+    rng = np.random.default_rng(8)
+    s = schedule(8, q_counts=[1] * 30, histories=list(rng.integers(100, 9000, 30)), page_size=16, hq=hq, hkv=hkv)
+    items, wg, merges, info = plan_of(s, num_cus)
+    check_plan(s, items, wg, merges, info, min_piece=128)
+    assert set(items[items[:, 0] == KIND_DECODE][:, 1].tolist()) == set(range(units))
+    nsub = units // hkv
+    xcd_of = {}
+    for b in range(len(wg) - 1):
+        for i in range(wg[b], wg[b + 1]):
+            xcd_of.setdefault((int(items[i, 3]), int(items[i, 5]), int(items[i, 1]) // nsub), set()).add(b % 8)
+    assert all(len(x) == 1 for x in xcd_of.values())
+
+    s = schedule(9, q_counts=[40, 1, 9, 1], histories=[100, 5000, 700, 20], page_size=16, hq=hq, hkv=hkv)
+    items, wg, merges, info = plan_of(s, num_cus)
+    check_plan(s, items, wg, merges, info, min_piece=1)
+    assert info["prefill_items"] > 0 and set(items[items[:, 0] == KIND_PREFILL][:, 1].tolist()) == set(range(units))
