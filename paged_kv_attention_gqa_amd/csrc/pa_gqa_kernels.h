@@ -88,13 +88,17 @@ void decode_short_kernel(KernelArgs a) {
 // share the grid (packed decode + chunked prefill in one dispatch).
 template <typename T, int D, int DV, int G>
 struct MixedShape {
-  static constexpr bool kMfma = sizeof(T) == 2 && D == DV && (D == 64 || D == 128) && G <= kPrefillRows;
-  // K and V rows of different widths, and D = Dv = 256: the 16x16x32 MFMA tile
+  // the 32x32x16 MFMA tile with its LDS DMA ring: D = Dv = 64 or 128, and
+  // D = 192 with Dv = 128 (four 40 KB stages fill the 160 KB of LDS)
+  static constexpr bool kMfma = sizeof(T) == 2 && G <= kPrefillRows &&
+                                ((D == DV && (D == 64 || D == 128)) || (D == 192 && DV == 128));
+  // other K and V widths, and D = Dv = 256: the 16x16x32 MFMA tile
   static constexpr bool kMfma16 =
       sizeof(T) == 2 && !kMfma && D % 64 == 0 && DV % 64 == 0 && (D != DV || D == 256) && G <= kPrefillRows;
   static constexpr int kDecodeBytes = kPrefillWaves * G * (DV + 3) * 4;
   static constexpr int kPrefillBytes =
-      kMfma ? PrefillSmem<(D <= 128 ? D : 128)>::kBytes : (kMfma16 ? Prefill16Smem<D, DV>::kBytes : 0);
+      kMfma ? PrefillSmem<(kMfma ? D : 64), (kMfma ? DV : 64)>::kBytes
+            : (kMfma16 ? Prefill16Smem<D, DV>::kBytes : 0);
   static constexpr int kBytes = kDecodeBytes > kPrefillBytes ? kDecodeBytes : kPrefillBytes;
 };
 
@@ -107,7 +111,7 @@ void mixed_kernel(KernelArgs a) {
   if (it.kind == kEmpty) return;
   if (it.kind == kPrefill) {
     if constexpr (MixedShape<T, D, DV, G>::kMfma)
-      prefill_item<T, D, G>(a, it, smem);
+      prefill_item<T, D, DV, G>(a, it, smem);
     else if constexpr (MixedShape<T, D, DV, G>::kMfma16)
       prefill16_item<T, D, DV, G>(a, it, smem);
     else

@@ -14,10 +14,10 @@
 // Data flow per 64-key tile (three LDS stages, two tiles in flight, one
 // barrier per tile):
 //   HBM --global_load_lds_dwordx4 (page-gathered, no registers)--> LDS
-//     K, V row-major [64 keys][D], the 16-byte pieces of key row t stored at
+//     K [64 keys][D], V [64 keys][Dv] row-major, the 16-byte pieces of key row t stored at
 //     piece ^ swz(t) so that column reads hit distinct bank groups
 //   each wave (32 rows):  S^T[64 x 32] = K . Q^T      (Q^T held in registers)
-//                         O^T[D x 32] += V^T . P^T    (V^T read with
+//                         O^T[Dv x 32] += V^T . P^T   (V^T read with
 //                         ds_read_b64_tr_b16, P^T straight from S^T)
 // In the S^T / O^T accumulator layout every lane owns one query row, so the
 // row max, the rescale and the row sum need at most one cross-lane step.
@@ -42,10 +42,11 @@ constexpr int kPrefillStages = 4;  // K/V tiles in the LDS ring
 constexpr bool kPrefillPingPong = true;  // two wave groups in opposite phase (see prefill_item_impl)
 constexpr float kLazyRescaleLog2 = 8.f;  // weights may reach 2^8 before the reference max moves
 
-template <int D>
+template <int D, int DV = D>
 struct PrefillSmem {
-  static constexpr int kTile = kPrefillTileKeys * D * 2;  // bytes of one K or V tile
-  static constexpr int kStage = 2 * kTile;
+  static constexpr int kTileK = kPrefillTileKeys * D * 2;   // bytes of one K tile
+  static constexpr int kTileV = kPrefillTileKeys * DV * 2;  // bytes of one V tile
+  static constexpr int kStage = kTileK + kTileV;
   static constexpr int kBytes = kPrefillStages * kStage;
 };
 
@@ -105,13 +106,31 @@ __device__ __forceinline__ short4_t lds_read_tr16(const char* p) {
 // bit-rotated copy of the low key bits.  Sixteen consecutive keys reading the
 // same piece (16-byte operand reads) and four consecutive keys reading four
 // neighbouring pieces (transpose reads) then hit distinct 16-byte bank groups.
+// Rows of a multiple of 16 pieces use four key bits, other rows (8 or 24
+// pieces) three, so that the XOR stays inside the row.
 template <int PIECES>
 __device__ __forceinline__ int swz(int key) {
-  if constexpr (PIECES >= 16)
+  if constexpr (PIECES % 16 == 0)
     return ((key & 3) << 2) | ((key >> 2) & 3);
   else
     return ((key & 3) << 1) | ((key >> 2) & 1);
 }
+
+// Load piece idx (16 bytes) of a block of key rows W 16-bit elements wide,
+// stored with the tile swizzle: it is stored piece idx % (W / 8) of row
+// idx / (W / 8) and carries that row's logical piece (stored ^ swz(row)).
+// Returns the row and the source byte offset within it.
+template <int W>
+__device__ __forceinline__ uint32_t piece_src(int idx, int* row) {
+  constexpr int P = W / 8;
+  const int r = idx / P, p = idx - r * P;
+  *row = r;
+  return (uint32_t)((p ^ swz<P>(r)) << 4);
+}
+template <int W>
+struct RowWidth {
+  static constexpr int value = W;
+};
 
 // Byte offset of 16-byte piece `piece` of key row `key` inside a tile.
 template <int D>
@@ -124,24 +143,20 @@ __device__ __forceinline__ int tile_off(int key, int piece) {
 // tiles; the loop body issues no other vector-memory loads (a per-tile
 // per-lane lookup would make the compiler drain the vector-memory counter
 // before every tile issue).
-template <typename T, int D, int G, bool UNIFORM>
+template <typename T, int D, int DV, int G, bool UNIFORM>
 __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const WorkItem& it, char* smem) {
   constexpr int NT = kPrefillTileKeys;
   constexpr int KS = D / 16;                         // MFMA k-steps of S^T (over head dims)
-  constexpr int DB = D / 32;                         // 32-dim blocks of O^T
-  constexpr int PIECES = D / 8;                      // 16-byte pieces per key row
-  constexpr int TILE = PrefillSmem<D>::kTile;
-  constexpr int STAGE = PrefillSmem<D>::kStage;
+  constexpr int DB = DV / 32;                        // 32-dim blocks of O^T
+  constexpr int TILE_K = PrefillSmem<D, DV>::kTileK;
+  constexpr int STAGE = PrefillSmem<D, DV>::kStage;
   constexpr int NS = kPrefillStages;
-  constexpr int KEYS_PER_LOAD = kWave / PIECES;      // key rows one wave-wide load covers
-  constexpr int LOADS_PER_TILE = NT / KEYS_PER_LOAD; // per K (or V) tile
-  constexpr int LOADS_PER_WAVE = 2 * LOADS_PER_TILE / kPrefillWaves;
-  constexpr int KEYS_PER_WAVE = KEYS_PER_LOAD * LOADS_PER_WAVE;
-  static_assert(PIECES >= 8 && kWave % PIECES == 0, "head size must be a multiple of 64");
   constexpr int MB = NT / 32;                        // 32-key MFMA blocks per tile
   constexpr int HALF = kPrefillWaves / 2;            // waves loading K (the others load V)
-  static_assert(KEYS_PER_WAVE == 16 && LOADS_PER_TILE == HALF * LOADS_PER_WAVE && NT % 32 == 0,
-                "each wave loads 16 consecutive key rows of K (first half of the waves) or V");
+  constexpr int KEYS_PER_WAVE = NT / HALF;           // consecutive key rows one wave loads per tile
+  constexpr int LOADS_K = KEYS_PER_WAVE * D * 2 / 1024, LOADS_V = KEYS_PER_WAVE * DV * 2 / 1024;
+  static_assert(KEYS_PER_WAVE == 16 && NT % 32 == 0 && D % 32 == 0 && DV % 32 == 0,
+                "each wave loads 16 consecutive key rows of K (first half of the waves) or V in whole 1 KB loads");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,29 +205,19 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   float m = -INFINITY, l = 0.f;
 
   // Tile loads.  Wave w fills key rows 16 (w % 4) .. +15 of the K tile (w < 4)
-  // or the V tile (w >= 4) with LOADS_PER_WAVE loads of KEYS_PER_LOAD rows;
-  // lane l carries stored piece l % PIECES of row l / PIECES of its load.
-  // Sixteen aligned keys never straddle a page of >= 16 keys, so one page
-  // number per wave and tile is enough (see page_of).  Keys past tok_end read the last key instead (every row in LDS is
-  // finite sequence data; such keys are masked); keys before tok_begin are
-  // sequence keys and are masked as well.
+  // or the V tile (w >= 4) with LOADS_K (LOADS_V) loads of 1 KB; lane l of
+  // load j carries 16-byte piece 64 j + l of the 16 rows' stored layout (see
+  // piece_src; the swizzle takes the low key bits, which 16 (w % 4) leaves
+  // alone).  Sixteen aligned keys never straddle a page of >= 16 keys, so one
+  // page number per wave and tile is enough (see page_of).  Keys past tok_end
+  // read the last key instead (every row in LDS is finite sequence data; such
+  // keys are masked); keys before tok_begin are sequence keys and are masked
+  // as well.
   const int wq = wave % HALF;
   const bool loads_v = wave >= HALF;
-  const uint32_t rs2 = (uint32_t)a.hkv * D * 2;  // bytes between consecutive key rows
-  const char* pool_kvh = reinterpret_cast<const char*>(loads_v ? a.v : a.k) + (uint64_t)it.kvh * D * 2;
-  // Byte offset of this lane's source for load j: (KEYS_PER_LOAD j + my_key)
-  // rows plus its stored piece.  swz permutes the low key bits, so for row
-  // 16 (w % 4) + KEYS_PER_LOAD j + my_key it equals swz(my_key) ^
-  // swz(KEYS_PER_LOAD j); rows are >= 128 bytes apart, so the XOR stays in
-  // the piece bits: lane_off(j) = (lane_off0 ^ (swz(KEYS_PER_LOAD j) << 4)) +
-  // KEYS_PER_LOAD j rows.
-  const int my_key = lane / PIECES;
-  const uint32_t lane_piece0 = (uint32_t)(((lane % PIECES) ^ swz<PIECES>(my_key)) << 4);
-  const uint32_t lane_off0 = (uint32_t)my_key * rs2 + lane_piece0;
-  auto lane_piece = [&](int j) { return lane_piece0 ^ (uint32_t)(swz<PIECES>(KEYS_PER_LOAD * j) << 4); };
-  auto lane_off = [&](int j) {
-    return (lane_off0 ^ (uint32_t)(swz<PIECES>(KEYS_PER_LOAD * j) << 4)) + (uint32_t)(KEYS_PER_LOAD * j) * rs2;
-  };
+  const uint32_t rs_k = (uint32_t)a.hkv * D * 2, rs_v = (uint32_t)a.hkv * DV * 2;  // bytes between key rows
+  const char* pool_k = reinterpret_cast<const char*>(a.k) + (uint64_t)it.kvh * D * 2;
+  const char* pool_v = reinterpret_cast<const char*>(a.v) + (uint64_t)it.kvh * DV * 2;
   // Page numbers of this wave's key group in 64 consecutive tiles are one
   // vector load (lane k holding tile win + k's, handed out with v_readlane),
   // reloaded every 64 tiles: a scalar load per tile would make the first
@@ -242,27 +247,70 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
       return 0;
     }
   };
-  auto issue_tile = [&](int t0, char* stage, int page) {
-    char* dst = stage + (loads_v ? TILE : 0) + KEYS_PER_WAVE * wq * (D * 2);
-    const int k0 = t0 + KEYS_PER_WAVE * wq;  // first key of this wave's rows
+  // Equal K and V widths of 8 or 16 pieces: a load covers whole rows
+  // (KPL of them), lane l carries stored piece l % PIECES of row l / PIECES;
+  // swz permutes the low key bits, so for row KPL j + my_key the stored
+  // piece's offset is lane_piece0 ^ (swz(KPL j) << 4) (rows are >= 128 bytes
+  // apart, the XOR stays in the piece bits), computed from one per-lane value.
+  constexpr int PIECES = D / 8;
+  constexpr bool WHOLE_ROWS = D == DV && kWave % PIECES == 0;
+  constexpr int KPL = WHOLE_ROWS ? kWave / PIECES : 1;
+  const int my_key = lane / PIECES;
+  const uint32_t lane_piece0 = (uint32_t)(((lane % PIECES) ^ swz<PIECES>(my_key)) << 4);
+  const uint32_t lane_off0 = (uint32_t)my_key * rs_k + lane_piece0;
+  // row and stored-piece offset of load j for this lane (rows W elements wide)
+  auto load_piece = [&](auto width, int j, int* r) {
+    constexpr int W = decltype(width)::value;
+    if constexpr (WHOLE_ROWS) {
+      *r = KPL * j + my_key;
+      return lane_piece0 ^ (uint32_t)(swz<PIECES>(KPL * j) << 4);
+    } else {
+      return piece_src<W>(kWave * j + lane, r);
+    }
+  };
+  // this wave's 16 rows of one tile (rows W elements wide, rs bytes apart in the pool)
+  auto issue_rows = [&](auto width, const char* pool, uint32_t rs, char* dst, int k0, int page) {
+    constexpr int W = decltype(width)::value;
+    constexpr int LOADS = KEYS_PER_WAVE * W * 2 / 1024;
     if (UNIFORM && k0 + KEYS_PER_WAVE <= te) {
       // whole group in range: one scalar base, fixed lane offsets
-      const char* base = pool_kvh + ((uint64_t)page * ps + (k0 & (ps - 1))) * rs2;
+      const char* base = pool + ((uint64_t)page * ps + (k0 & (ps - 1))) * rs;
 #pragma unroll
-      for (int j = 0; j < LOADS_PER_WAVE; ++j)
-        load_to_lds_sv(base, lane_off(j), dst + j * 1024);
+      for (int j = 0; j < LOADS; ++j) {
+        if constexpr (WHOLE_ROWS) {
+          const uint32_t off = (lane_off0 ^ (uint32_t)(swz<PIECES>(KPL * j) << 4)) + (uint32_t)(KPL * j) * rs;
+          load_to_lds_sv(base, off, dst + j * 1024);
+        } else {
+          int r;
+          const uint32_t piece = load_piece(width, j, &r);
+          load_to_lds_sv(base, (uint32_t)r * rs + piece, dst + j * 1024);
+        }
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < LOADS_PER_WAVE; ++j) {
-        const int t = min(k0 + KEYS_PER_LOAD * j + my_key, te - 1);
-        const uint32_t off = (uint32_t)(t & (ps - 1)) * rs2 + lane_piece(j);
+      for (int j = 0; j < LOADS; ++j) {
+        int r;
+        const uint32_t piece = load_piece(width, j, &r);
+        const int t = min(k0 + r, te - 1);
+        const uint32_t off = (uint32_t)(t & (ps - 1)) * rs + piece;
         if constexpr (UNIFORM) {
-          load_to_lds_sv(pool_kvh + (uint64_t)page * ps * rs2, off, dst + j * 1024);
+          load_to_lds_sv(pool + (uint64_t)page * ps * rs, off, dst + j * 1024);
         } else {
-          const char* src = pool_kvh + (uint64_t)bt[t >> a.page_shift] * ps * rs2 + off;  // per-lane page
+          const char* src = pool + (uint64_t)bt[t >> a.page_shift] * ps * rs + off;  // per-lane page
           load_to_lds(src, dst + j * 1024);
         }
       }
+    }
+  };
+  auto issue_tile = [&](int t0, char* stage, int page) {
+    const int k0 = t0 + KEYS_PER_WAVE * wq;  // first key of this wave's rows
+    if constexpr (D == DV) {  // one code path for both halves of the waves
+      issue_rows(RowWidth<D>{}, loads_v ? pool_v : pool_k, rs_k,
+                 stage + (loads_v ? TILE_K : 0) + KEYS_PER_WAVE * wq * (D * 2), k0, page);
+    } else if (loads_v) {
+      issue_rows(RowWidth<DV>{}, pool_v, rs_v, stage + TILE_K + KEYS_PER_WAVE * wq * (DV * 2), k0, page);
+    } else {
+      issue_rows(RowWidth<D>{}, pool_k, rs_k, stage + KEYS_PER_WAVE * wq * (D * 2), k0, page);
     }
   };
   // wait until at most `ahead` tiles of this wave's loads are still in flight
@@ -270,9 +318,9 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     if (!UNIFORM || ahead <= 0)
       wait_vmcnt<0>();
     else if (ahead == 1)
-      wait_vmcnt<LOADS_PER_WAVE>();
+      loads_v ? wait_vmcnt<LOADS_V>() : wait_vmcnt<LOADS_K>();
     else
-      wait_vmcnt<2 * LOADS_PER_WAVE>();
+      loads_v ? wait_vmcnt<2 * LOADS_V>() : wait_vmcnt<2 * LOADS_K>();
   };
 
   // tile entirely hidden from every row of this wave?
@@ -295,7 +343,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int dim = 32 * b + dim0;
-        voff[b][r] = (uint32_t)(tile_off<D>(key0 + 8 * r, dim >> 3) + (dim & 7) * 2);
+        voff[b][r] = (uint32_t)(tile_off<DV>(key0 + 8 * r, dim >> 3) + (dim & 7) * 2);
       }
   }
   // S^T = K . Q^T : two 32-key blocks; lane (n, h) reads dims 16 k + 8 h of key row n
@@ -386,8 +434,8 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     for (int kk = 0; kk < NT / 16; ++kk) {
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        const short4_t v0 = lds_read_tr16(vs + voff[b][0] + kk * 16 * (D * 2));
-        const short4_t v1 = lds_read_tr16(vs + voff[b][1] + kk * 16 * (D * 2));
+        const short4_t v0 = lds_read_tr16(vs + voff[b][0] + kk * 16 * (DV * 2));
+        const short4_t v1 = lds_read_tr16(vs + voff[b][1] + kk * 16 * (DV * 2));
         const frag_t vf = __builtin_bit_cast(
             frag_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
@@ -437,7 +485,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
     if (jj >= 0 && jj < ntiles && !hidden(t_first + jj * NT)) weights(s, row_max(t_first + jj * NT, s), pf);
   };
   auto matrix_phase = [&](int jj) {  // P.V of tile jj - 1, scores of tile jj
-    if (jj > 0 && !hidden(t_first + (jj - 1) * NT)) pv(smem + ((jj - 1) % NS) * STAGE + TILE, pf);
+    if (jj > 0 && !hidden(t_first + (jj - 1) * NT)) pv(smem + ((jj - 1) % NS) * STAGE + TILE_K, pf);
     if (jj < ntiles && !hidden(t_first + jj * NT)) scores(smem + (jj % NS) * STAGE, s);
   };
   // One loop body for both groups, V(j - 1) then M(j); only the barrier
@@ -454,7 +502,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   l = pair32_sum(l);
   if (!row_valid) return;
   const float inv = 1.f / l;
-  uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * a.hq + head) * D;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * a.hq + head) * DV;
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -468,13 +516,13 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   if (a.lse && h == 0) a.lse[(uint64_t)qi * a.hq + head] = m * a.scale + logf(l);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem& it, char* smem) {
   static_assert(sizeof(T) == 2, "the MFMA tile runs on 16-bit data");
   if (a.page_shift >= 4)
-    prefill_item_impl<T, D, G, true>(a, it, smem);
+    prefill_item_impl<T, D, DV, G, true>(a, it, smem);
   else
-    prefill_item_impl<T, D, G, false>(a, it, smem);
+    prefill_item_impl<T, D, DV, G, false>(a, it, smem);
 }
 
 // A prefill tile handled one query at a time by the decode body (f32 data,

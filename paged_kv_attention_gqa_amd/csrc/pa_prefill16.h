@@ -1,5 +1,6 @@
 // Chunked-prefill body on 16x16x32 MFMA for head sizes the prefill_item tile
-// does not take (D = 192 with Dv = 128, and D = Dv = 256, in bf16 / f16): the
+// does not take (D = Dv = 256, and pairs of multiples of 64 other than
+// 192 / 128, in bf16 / f16): the
 // rows and keys of a prefill tile as in
 // prefill_item (up to 256 query rows -- 256 / G consecutive queries of one
 // sequence times the G heads of one KV head -- against the keys the plan
