@@ -90,7 +90,7 @@ struct pa_plan {
   std::vector<int32_t> wg_first;  // workgroup b runs items wg_first[b] .. wg_first[b + 1] - 1
   std::vector<MergeItem> merges;
   int32_t n_decode = 0, n_prefill = 0, n_slots = 0;
-  int32_t heads_shift = 0;        // decode items cover 2^heads_shift consecutive KV heads
+  int32_t heads_shift = 0;        // decode items cover 2^heads_shift consecutive units (KV heads, MLA head groups)
   int32_t n_wg = 0;               // workgroups of the main launch
   int32_t n_cu = 0;               // compute units of the plan's device
   // append: pool slot (page * page_size + slot) of every query's position,
@@ -335,7 +335,7 @@ void plan_balanced(pa_plan* p, int slots, int min_piece) {
       left += hi + 1 - lo;
     }
   const int hw = 1 << p->heads_shift, U = p->units();
-  const int groups = std::max(1, slots / (U / hw));
+  const int groups = std::max(1, slots / ((U + hw - 1) / hw));
   auto align_up = [](int64_t x) { return (x + kSplitAlign - 1) / kSplitAlign * kSplitAlign; };
   auto align_down = [](int64_t x) { return x / kSplitAlign * kSplitAlign; };
   struct Piece {
@@ -407,7 +407,7 @@ void plan_balanced(pa_plan* p, int slots, int min_piece) {
     // of kXcds side by side; missing groups of the last block leave empty
     // workgroups
     for (size_t b0 = 0; b0 < grp.size(); b0 += kXcds)
-      for (int h = 0; h < U; ++h)
+      for (int h = 0; h < U; h += hw)
         for (size_t j = b0; j < b0 + kXcds; ++j) emit(j < grp.size() ? &grp[j] : nullptr, h);
   } else {
     for (const auto& g : grp)
@@ -422,6 +422,9 @@ void build_work(pa_plan* p) {
   const int G = p->group();
   bool has_prefill = false;
   for (int s = 0; s < p->S; ++s) has_prefill |= (p->cu_q[s + 1] - p->cu_q[s]) > kDecodeMaxQueries;
+  // MLA decode-only plans of several head groups: items of two groups, which
+  // share each latent tile (the MFMA kernel's head-group pairs)
+  if (p->mla && !has_prefill && p->units() > 1) p->heads_shift = 1;
   if (!has_prefill && p->split_tokens == 0 && p->max_splits > 1 && p->n_cu > 0) {
     int per_cu = pa::mla_wgs_per_cu();
     if (!p->mla) {

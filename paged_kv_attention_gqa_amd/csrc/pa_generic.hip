@@ -18,7 +18,7 @@
 // The plans and work lists are the specialised kernels': an item is one
 // work unit (a KV head with its G <= 16 query heads, or a group of up to 16
 // of them when G > 16 or for MLA) of one query or a chunk of queries over
-// one key range; decode items may cover hw consecutive KV heads.  Split rows
+// one key range; decode items may cover hw consecutive units.  Split rows
 // leave the same partials (unit_heads heads per slot, max in log2 units,
 // sums) for the merge below.
 //
@@ -89,8 +89,9 @@ __global__ __launch_bounds__(kGenThreads) void generic_kernel(KernelArgs a, Gene
     const WorkItem it = a.items[i];
     if (it.kind == kEmpty) continue;
     const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
-    for (int j = 0; j < s.hw; ++j) {  // KV heads of a decode item (hw = 1 otherwise)
+    for (int j = 0; j < s.hw; ++j) {  // units of a decode item (hw = 1 otherwise)
       const int u = it.kvh + j;
+      if (u >= a.hkv * s.nsub) break;  // a unit past the last (an odd number of MLA head groups)
       const int kv = u / s.nsub;
       int h0, nh;
       unit_heads_of(s, u, &h0, &nh);

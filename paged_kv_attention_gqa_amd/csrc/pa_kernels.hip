@@ -19,9 +19,13 @@ bool gqa_family_pow2(int dtype, int d, int dv, int g, GqaFamily* out) {
 // a 72 KB LDS tile ring, two workgroups per CU.  Decode-only plans run the
 // instantiation without the prefill body, whose 128 output registers per
 // wave would otherwise set the register allocation of the decode body too.
-template <typename T, bool PREFILL>
+//
+// NG = 2 (decode-only plans of more than one head group): each decode item
+// takes two head groups of 16 heads, sharing the tile reads (80 KB of LDS).
+template <typename T, bool PREFILL, int NG = 1>
 __global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_eu(2))) void mla_kernel(KernelArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[MlaSmem::kBytes];
+  static_assert(NG == 1 || !PREFILL, "head-group pairs on decode-only plans");
+  __shared__ __attribute__((aligned(16))) char smem[MlaSmem<NG>::kBytes];
   const int first = a.wg_first[blockIdx.x], last = a.wg_first[blockIdx.x + 1];
   int tid = threadIdx.x;
   for (int i = first; i < last; ++i) {
@@ -32,7 +36,7 @@ __global__ __launch_bounds__(kMlaWaves* kWave) __attribute__((amdgpu_waves_per_e
     if (PREFILL && it.kind == kPrefill)
       mla_item<T, PREFILL>(a, it, smem, tid);
     else
-      mla_item<T, false, !PREFILL>(a, it, smem, tid);
+      mla_item<T, false, !PREFILL, NG>(a, it, smem, tid);
   }
 }
 
@@ -95,7 +99,8 @@ bool mla_mfma_shape(int dtype, int r, int p) { return (dtype == 1 || dtype == 2)
 // MLA on the vector kernel: one KV head (the latent), its H query heads in
 // units of 16, the value the latent itself
 GenericShape mla_generic_shape(const KernelArgs& a, int r, int p) {
-  return GenericShape{r, p, r, a.hq, (a.hq + kMlaGroupHeads - 1) / kMlaGroupHeads, kMlaGroupHeads, 1, 1};
+  return GenericShape{r, p, r, a.hq, (a.hq + kMlaGroupHeads - 1) / kMlaGroupHeads, kMlaGroupHeads,
+                      1 << a.heads_shift, 1};
 }
 }  // namespace
 
@@ -109,9 +114,13 @@ hipError_t launch_mla_main(int dtype, int r, int p, bool has_prefill, const Kern
                            hipStream_t stream) {
   if (!mla_mfma_shape(dtype, r, p)) return launch_generic(dtype, mla_generic_shape(a, r, p), a, ev, stream);
   constexpr int threads = kMlaWaves * kWave;
+  // decode-only plans of several head groups pair them (heads_shift 1)
+  const bool pairs = !has_prefill && a.heads_shift == 1;
   if (dtype == 1 && has_prefill) return launch_main(mla_kernel<uint16_t, true>, a.n_wg, threads, a, ev, stream);
+  if (dtype == 1 && pairs) return launch_main(mla_kernel<uint16_t, false, 2>, a.n_wg, threads, a, ev, stream);
   if (dtype == 1) return launch_main(mla_kernel<uint16_t, false>, a.n_wg, threads, a, ev, stream);
   if (dtype == 2 && has_prefill) return launch_main(mla_kernel<_Float16, true>, a.n_wg, threads, a, ev, stream);
+  if (dtype == 2 && pairs) return launch_main(mla_kernel<_Float16, false, 2>, a.n_wg, threads, a, ev, stream);
   if (dtype == 2) return launch_main(mla_kernel<_Float16, false>, a.n_wg, threads, a, ev, stream);
   return hipErrorInvalidValue;
 }

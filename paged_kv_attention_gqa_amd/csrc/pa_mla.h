@@ -43,12 +43,15 @@ constexpr int kMlaTileKeys = 16;
 constexpr int kMlaWaves = 4;
 constexpr int kMlaStages = 4;  // tiles in the ring: three in flight while one is used
 
+// NG: head groups per decode item (their partial score tiles share the
+// exchange area).
+template <int NG = 1>
 struct MlaSmem {
   static constexpr int kLatTile = kMlaTileKeys * kMlaRank * 2;   // 16 KB
   static constexpr int kPosTile = kMlaTileKeys * kMlaRope * 2;   // 2 KB
   static constexpr int kStage = kLatTile + kPosTile;
   static constexpr int kXchgOff = kMlaStages * kStage;           // 72 KB
-  static constexpr int kBytes = kXchgOff + kMlaWaves * 64 * 16;  // + partial scores of the four waves
+  static constexpr int kBytes = kXchgOff + NG * kMlaWaves * 64 * 16;  // + partial scores of the four waves
 };
 
 // Wait until at most `ahead` (<= MAXA) tiles of PER loads each are still in
@@ -103,9 +106,16 @@ __device__ __forceinline__ int mla_off(int key, int piece) {
 // wave computing the whole score tile: hipcc for gfx950 fails to generate
 // code ("operand has incorrect register class") for the split tile next to
 // the prefill body in one kernel.
+//
+// NG (split decode items only): the item covers head groups kvh .. kvh +
+// NG - 1, which share each tile's LDS reads (latent and rotary fragments,
+// transposed latent reads), the barriers and the exchange; each group has
+// its own query operands, scores, softmax state and output sums.  A group
+// past the last head (an odd number of groups) computes copies and stores
+// nothing; group g's split partials go to slot + g.
 constexpr int kMlaWavesPerQuery = kMlaWaves / kMlaPrefillQueries;
 static_assert(kMlaWavesPerQuery == 2, "two waves per prefill query");
-template <typename T, bool PREFILL = false, bool SPLIT = true>
+template <typename T, bool PREFILL = false, bool SPLIT = true, int NG = 1>
 __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it, char* smem, int tid = threadIdx.x) {
   constexpr int H = kMlaHeads, R = kMlaRank, P = kMlaRope, NT = kMlaTileKeys;
   constexpr int KS_LAT = R / 32, KS_POS = P / 32;  // 16x16x32 k-steps
@@ -123,9 +133,9 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   const bool q_ok = !PREFILL || wq < it.q_count;
   const int qi = it.q_begin + (PREFILL ? min(wq, it.q_count - 1) : 0);
   const int qpos = PREFILL ? a.q_pos[qi] : 0;
-  const int head = H * it.kvh + n;  // this lane's query head (its MFMA column)
-  const bool head_ok = head < a.hq;  // columns past the last head compute a copy of it, unstored
-  const uint64_t hrow = (uint64_t)qi * a.hq + min(head, a.hq - 1);
+  // row of this lane's query head (its MFMA column) in group g; columns past
+  // the last head compute a copy of it and store nothing
+  auto head_row = [&](int g) { return (uint64_t)qi * a.hq + min(H * (it.kvh + g) + n, a.hq - 1); };
   const int dim0 = DW * (PREFILL ? wave % kMlaWavesPerQuery : wave);  // first output dim of this wave
   const int tb = it.tok_begin, te = it.tok_end;
   const int ps = 1 << a.page_shift;
@@ -139,19 +149,22 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   // (16 wave .. 16 wave + 15, one 16x16x16 step: lane (n, c) holds dims
   // 16 wave + 4 c .. +3); the four partial tiles are summed through LDS.
   constexpr bool SPLIT_S = !PREFILL && SPLIT;
+  static_assert(NG == 1 || SPLIT_S, "several head groups per item only on split decode items");
   constexpr int QA = SPLIT_S ? KS_LAT / kMlaWaves : KS_LAT, QP = SPLIT_S ? 0 : KS_POS;
   static_assert(P == 16 * kMlaWaves, "one 16-dim rotary step per wave");
   const int ks0 = SPLIT_S ? QA * wave : 0;
-  frag_t qa[QA], qp[QP > 0 ? QP : 1];
-  short4_t qp16 = {};
-  {
+  frag_t qa[NG][QA], qp[QP > 0 ? QP : 1];
+  short4_t qp16[NG] = {};
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint64_t hrow = head_row(g);
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + hrow * R;
     const uint16_t* prow = reinterpret_cast<const uint16_t*>(a.qr) + hrow * P;
 #pragma unroll
-    for (int k = 0; k < QA; ++k) qa[k] = *reinterpret_cast<const frag_t*>(qrow + 32 * (ks0 + k) + 8 * c);
+    for (int k = 0; k < QA; ++k) qa[g][k] = *reinterpret_cast<const frag_t*>(qrow + 32 * (ks0 + k) + 8 * c);
 #pragma unroll
     for (int k = 0; k < QP; ++k) qp[k] = *reinterpret_cast<const frag_t*>(prow + 32 * k + 8 * c);
-    if constexpr (SPLIT_S) qp16 = *reinterpret_cast<const short4_t*>(prow + 16 * wave + 4 * c);
+    if constexpr (SPLIT_S) qp16[g] = *reinterpret_cast<const short4_t*>(prow + 16 * wave + 4 * c);
   }
   // The tile loads below are inline assembly that the compiler's wait-count
   // pass does not see; it would count only these query loads as outstanding
@@ -159,10 +172,16 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   // few loads remain, i.e. for the tile loads still in flight.  Finishing the
   // query loads here leaves it nothing to wait for in the loop.
 
-  floatx4_t o[DB];
+  floatx4_t o[NG][DB];
+  float m[NG], l[NG], lx[NG];
 #pragma unroll
-  for (int b = 0; b < DB; ++b) o[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f, lx = 0.f;
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[g][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+    lx[g] = 0.f;
+  }
 
   auto clamp_key = [&](int t) { return min(max(t, tb), te - 1); };
   // This wave's share of a tile: latent rows ROWS_PER_WAVE * wave + r (one
@@ -215,7 +234,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
       const int row = ROWS_PER_WAVE * wave + rl;
       const int t = clamp_key(t0 + row);
       const uint16_t* src = kpos + ((uint64_t)page * ps + (t & (ps - 1))) * P + (((lane & 7) ^ swz<P / 8>(row)) * 8);
-      load_to_lds_stream(src, stage + MlaSmem::kLatTile + wave * 512);
+      load_to_lds_stream(src, stage + MlaSmem<NG>::kLatTile + wave * 512);
     }
   };
 
@@ -226,7 +245,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   for (int j = 0; j < kMlaStages - 1; ++j)
     if (j < ntiles) {
       page_next = tile_page(first + j * NT);
-      issue_tile(first + j * NT, smem + j * MlaSmem::kStage, page_next);
+      issue_tile(first + j * NT, smem + j * MlaSmem<NG>::kStage, page_next);
     }
   page_next = tile_page(first + (kMlaStages - 1) * NT);
   for (int j = 0; j < ntiles; ++j) {
@@ -234,27 +253,28 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
     wait_tiles_ahead<LOADS_PER_TILE, kMlaStages - 2>(min(ntiles - 1 - j, kMlaStages - 2));
     barrier_keep_loads();  // ... every wave's share has; tile j-1's stage is free for reuse
     if (j + kMlaStages - 1 < ntiles) {
-      issue_tile(first + (j + kMlaStages - 1) * NT, smem + ((j + kMlaStages - 1) % kMlaStages) * MlaSmem::kStage,
+      issue_tile(first + (j + kMlaStages - 1) * NT, smem + ((j + kMlaStages - 1) % kMlaStages) * MlaSmem<NG>::kStage,
                  page_next);
       page_next = tile_page(first + (j + kMlaStages) * NT);
     }
     const int t0 = first + j * NT;
-    const char* ls = smem + (j % kMlaStages) * MlaSmem::kStage;
-    const char* kps = ls + MlaSmem::kLatTile;
+    const char* ls = smem + (j % kMlaStages) * MlaSmem<NG>::kStage;
+    const char* kps = ls + MlaSmem<NG>::kLatTile;
 
     // S^T: lane (n, c) holds keys 4 c + r (r = 0..3) of head n; two
     // accumulator chains halve the dependent MFMA latency
-    floatx4_t s;
+    floatx4_t s[NG];
     if constexpr (PREFILL) {
       // fragments read as they are used (the output sums hold 128 registers)
       floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int k = 0; k < KS_LAT; ++k)
-        sc[k & 1] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * k + c)), qa[k], sc[k & 1]);
+        sc[k & 1] =
+            mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * k + c)), qa[0][k], sc[k & 1]);
 #pragma unroll
       for (int k = 0; k < KS_POS; ++k)
         sc[k & 1] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * k + c)), qp[k], sc[k & 1]);
-      s = sc[0] + sc[1];
+      s[0] = sc[0] + sc[1];
     } else if constexpr (!SPLIT_S) {
       frag_t kf[KS_LAT + KS_POS];
 #pragma unroll
@@ -264,10 +284,10 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
         kf[KS_LAT + k] = *reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * k + c));
       floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int k = 0; k < KS_LAT; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[k], qa[k], sc[k & 1]);
+      for (int k = 0; k < KS_LAT; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[k], qa[0][k], sc[k & 1]);
 #pragma unroll
       for (int k = 0; k < KS_POS; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[KS_LAT + k], qp[k], sc[k & 1]);
-      s = sc[0] + sc[1];
+      s[0] = sc[0] + sc[1];
     } else {
       frag_t kf[QA];
       // pieces 16 wave + 4 k + c: the swizzle (< 16) leaves the 16-piece block in place
@@ -275,52 +295,63 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
 #pragma unroll
       for (int k = 0; k < QA; ++k) kf[k] = *reinterpret_cast<const frag_t*>(lsw + mla_off<R>(n, 4 * k + c));
       const short4_t kp16 = *reinterpret_cast<const short4_t*>(kps + mla_off<P>(n, 2 * wave + (c >> 1)) + (c & 1) * 8);
-      floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int k = 0; k < QA; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[k], qa[k], sc[k & 1]);
-      sc[0] = mfma_16x16x16<T>(kp16, qp16, sc[0]);
       // the partial tiles of the four waves, summed in one fixed order so
       // that every wave holds the same scores (the previous tile's reads
       // were done before this tile's barrier)
       typedef __attribute__((address_space(3))) floatx4_t lds_f4_t;
-      lds_f4_t* xs = (lds_f4_t*)(size_t)__builtin_amdgcn_readfirstlane(
-          (uint32_t)(size_t)(lds_void_t*)(smem + MlaSmem::kXchgOff));
-      xs[wave * 64 + lane] = sc[0] + sc[1];
+      lds_f4_t* xs = (lds_f4_t*)(size_t)__builtin_amdgcn_readfirstlane(lds_address(smem + MlaSmem<NG>::kXchgOff));
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int k = 0; k < QA; ++k) sc[k & 1] = mfma_16x16x32<T>(kf[k], qa[g][k], sc[k & 1]);
+        sc[0] = mfma_16x16x16<T>(kp16, qp16[g], sc[0]);
+        xs[(g * kMlaWaves + wave) * 64 + lane] = sc[0] + sc[1];
+      }
       barrier_keep_loads();  // the exchange is written (the tiles in flight stay in flight)
-      s = ((xs[lane] + xs[64 + lane]) + xs[128 + lane]) + xs[192 + lane];
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + 4 * c + r;
-      if constexpr (PREFILL)
-        s[r] = (t >= tb && t < te && (!a.causal || t <= qpos) && (a.window == 0 || t > qpos - a.window)) ? s[r]
-                                                                                                     : -INFINITY;
-      else
-        s[r] = (t >= tb && t < te) ? s[r] : -INFINITY;
+      for (int g = 0; g < NG; ++g) {
+        const lds_f4_t* xg = xs + g * kMlaWaves * 64;
+        s[g] = ((xg[lane] + xg[64 + lane]) + xg[128 + lane]) + xg[192 + lane];
+      }
     }
+    short4_t pf[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * c + r;
+        if constexpr (PREFILL)
+          s[g][r] = (t >= tb && t < te && (!a.causal || t <= qpos) && (a.window == 0 || t > qpos - a.window))
+                        ? s[g][r]
+                        : -INFINITY;
+        else
+          s[g][r] = (t >= tb && t < te) ? s[g][r] : -INFINITY;
+      }
 
-    // Online softmax against a lazily raised reference max (weights stay
-    // <= 2^kLazyRescaleLog2; the accumulators are rescaled only when a tile
-    // raises some head's max past that).
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = pair32_max(pair16_max(mx));  // over the four k-groups of lanes
-    if (__any(mx * a.scale_log2 > m * a.scale_log2 + kLazyRescaleLog2)) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2((m - (mn == -INFINITY ? 0.f : mn)) * a.scale_log2);
-      m = mn;
-      l *= alpha;
-      lx *= alpha;
+      // Online softmax against a lazily raised reference max (weights stay
+      // <= 2^kLazyRescaleLog2; the accumulators are rescaled only when a tile
+      // raises some head's max past that).
+      float mx = fmaxf(fmaxf(s[g][0], s[g][1]), fmaxf(s[g][2], s[g][3]));
+      mx = pair32_max(pair16_max(mx));  // over the four k-groups of lanes
+      if (__any(mx * a.scale_log2 > m[g] * a.scale_log2 + kLazyRescaleLog2)) {
+        const float mn = fmaxf(m[g], mx);
+        const float alpha = fast_exp2((m[g] - (mn == -INFINITY ? 0.f : mn)) * a.scale_log2);
+        m[g] = mn;
+        l[g] *= alpha;
+        lx[g] *= alpha;
 #pragma unroll
-      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+        for (int b = 0; b < DB; ++b) o[g][b] *= alpha;
+      }
+      const float sub = (m[g] == -INFINITY ? 0.f : m[g]) * a.scale_log2;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(s[g][r], a.scale_log2, -sub));
+      const uint32_t w0 = Pair16<T>::pack(p[0], p[1]), w1 = Pair16<T>::pack(p[2], p[3]);
+      l[g] += Pair16<T>::lo(w0) + Pair16<T>::hi(w0) + Pair16<T>::lo(w1) + Pair16<T>::hi(w1);
+      lx[g] += (p[0] + p[1]) + (p[2] + p[3]);
+      pf[g] = __builtin_bit_cast(short4_t, make_uint2(w0, w1));
     }
-    const float sub = (m == -INFINITY ? 0.f : m) * a.scale_log2;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -sub));
-    const uint32_t w0 = Pair16<T>::pack(p[0], p[1]), w1 = Pair16<T>::pack(p[2], p[3]);
-    l += Pair16<T>::lo(w0) + Pair16<T>::hi(w0) + Pair16<T>::lo(w1) + Pair16<T>::hi(w1);
-    lx += (p[0] + p[1]) + (p[2] + p[3]);
-    const short4_t pf = __builtin_bit_cast(short4_t, make_uint2(w0, w1));
 
     // O^T block b (dims dim0 + 16 b ..): lane (i = lane % 16, c) needs
     // latent[4 c + r][dim0 + 16 b + i]: one transposed read, lane 4 r + j
@@ -337,7 +368,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
           vf[b] = lds_read_tr16(ls + mla_off<R>(key, dim >> 3) + (dim & 7) * 2);
         }
 #pragma unroll
-        for (int b = 0; b < VB; ++b) o[b0 + b] = mfma_16x16x16<T>(vf[b], pf, o[b0 + b]);
+        for (int b = 0; b < VB; ++b) o[0][b0 + b] = mfma_16x16x16<T>(vf[b], pf[0], o[0][b0 + b]);
       }
     } else {
       short4_t vf[DB];
@@ -347,35 +378,45 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
         vf[b] = lds_read_tr16(ls + mla_off<R>(key, dim >> 3) + (dim & 7) * 2);
       }
 #pragma unroll
-      for (int b = 0; b < DB; ++b) o[b] = mfma_16x16x16<T>(vf[b], pf, o[b]);
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[g][b] = mfma_16x16x16<T>(vf[b], pf[g], o[g][b]);
     }
   }
 
-  // full row sums: the four k-groups of lanes hold different keys
-  l = pair32_sum(pair16_sum(l));
-  lx = pair32_sum(pair16_sum(lx));
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (H * (it.kvh + g) >= a.hq) break;  // a group past the last head (wave-uniform)
+    // full row sums: the four k-groups of lanes hold different keys
+    const float lg = pair32_sum(pair16_sum(l[g]));
+    const float lxg = pair32_sum(pair16_sum(lx[g]));
+    const bool head_ok = H * (it.kvh + g) + n < a.hq;
 
-  // O^T lane (n, c) element r is dim dim0 + 16 b + 4 c + r of head n
-  if (PREFILL || it.slot < 0) {
-    if ((PREFILL && !q_ok) || !head_ok) return;
-    const float inv = 1.f / l;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + hrow * R + (PREFILL ? dim0 : DW * wave);
+    // O^T lane (n, c) element r is dim dim0 + 16 b + 4 c + r of head n
+    if (PREFILL || it.slot < 0) {
+      if ((PREFILL && !q_ok) || !head_ok) continue;
+      const uint64_t hrow = head_row(g);
+      const float inv = 1.f / lg;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + hrow * R + (PREFILL ? dim0 : DW * wave);
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      uint2 w;
-      w.x = Pair16<T>::pack(o[b][0] * inv, o[b][1] * inv);
-      w.y = Pair16<T>::pack(o[b][2] * inv, o[b][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * b + 4 * c) = w;
-    }
-    if (a.lse && (PREFILL ? wave % kMlaWavesPerQuery : wave) == 0 && c == 0) a.lse[hrow] = m * a.scale + logf(lx);
-  } else {
-    float* dst = a.ws_o + ((uint64_t)it.slot * H + n) * R + DW * wave;
+      for (int b = 0; b < DB; ++b) {
+        uint2 w;
+        w.x = Pair16<T>::pack(o[g][b][0] * inv, o[g][b][1] * inv);
+        w.y = Pair16<T>::pack(o[g][b][2] * inv, o[g][b][3] * inv);
+        *reinterpret_cast<uint2*>(orow + 16 * b + 4 * c) = w;
+      }
+      if (a.lse && (PREFILL ? wave % kMlaWavesPerQuery : wave) == 0 && c == 0)
+        a.lse[hrow] = m[g] * a.scale + logf(lxg);
+    } else {
+      const uint64_t srow = (uint64_t)(it.slot + g) * H + n;
+      float* dst = a.ws_o + srow * R + DW * wave;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) *reinterpret_cast<floatx4_t*>(dst + 16 * b + 4 * c) = o[b];
-    if (wave == 0 && c == 0) {
-      a.ws_ml[((uint64_t)it.slot * H + n) * 3 + 0] = m * a.scale_log2;
-      a.ws_ml[((uint64_t)it.slot * H + n) * 3 + 1] = l;
-      a.ws_ml[((uint64_t)it.slot * H + n) * 3 + 2] = lx;
+      for (int b = 0; b < DB; ++b) *reinterpret_cast<floatx4_t*>(dst + 16 * b + 4 * c) = o[g][b];
+      if (wave == 0 && c == 0) {
+        a.ws_ml[srow * 3 + 0] = m[g] * a.scale_log2;
+        a.ws_ml[srow * 3 + 1] = lg;
+        a.ws_ml[srow * 3 + 2] = lxg;
+      }
     }
   }
 }

@@ -46,6 +46,8 @@ MLA_HEAD_CASES = [
     (8, dict(page_size=64, q_counts=(1, 6), max_len=1500, window=300)),
     (1, dict(page_size=32, q_counts=(3, 1), max_len=700, causal=False)),
     (48, dict(page_size=64, q_counts=(0, 12, 1), histories=[50, 600, 90])),
+    (48, dict(page_size=64, q_counts=(1, 1, 1), max_len=2500)),                # decode only: groups in pairs, odd count
+    (40, dict(page_size=16, q_counts=(1, 2), max_len=1800, window=700)),
 ]
 
 
@@ -54,8 +56,10 @@ MLA_HEAD_CASES = [
 @pytest.mark.parametrize("i", range(len(MLA_HEAD_CASES)))
 def test_mla_head_counts_parity(i, split_tokens, dtype):
     """Head counts other than 16: the heads run in groups of 16 (the MFMA
-    columns), the last group partial; every output element is written (the
-    output starts as NaN) and matches the oracle."""
+    columns), the last group partial, and decode-only plans pair the groups
+    (an odd count leaves the last item's second group past the end); every
+    output element is written (the output starts as NaN) and matches the
+    oracle."""
     heads, kw = MLA_HEAD_CASES[i]
     m = random_mla_batch(3200 + i, heads=heads, dtype=dtype, **kw)
     run = MlaRun(m, split_tokens=split_tokens)

@@ -69,7 +69,8 @@ def check_plan(s, items, wg, merges, info, min_piece):
     hkv = s["num_kv_heads"] * (-(-G // 16) if s["mla"] or G > 16 else 1)
     Q = int(s["cu_q"][-1])
     hpi = info["heads_per_item"]
-    assert hpi >= 1 and hkv % hpi == 0 and (hpi & (hpi - 1)) == 0
+    # MLA pairs head groups: with an odd number of groups the last item's second is past the end
+    assert hpi >= 1 and (hkv % hpi == 0 or s["mla"]) and (hpi & (hpi - 1)) == 0
     # workgroup ranges partition the item list
     assert wg[0] == 0 and wg[-1] == len(items) and np.all(np.diff(wg) >= 0)
     assert info["workgroups"] == len(wg) - 1
@@ -83,10 +84,10 @@ def check_plan(s, items, wg, merges, info, min_piece):
         if kind == KIND_EMPTY:
             continue
         if kind == KIND_DECODE:
-            assert qn == 1 and 0 <= kvh and kvh + hpi <= hkv and kvh % hpi == 0
+            assert qn == 1 and 0 <= kvh < hkv and kvh % hpi == 0
             vs, lo, hi = visible(s, q0)
             assert vs == seq and lo <= b < e <= hi, (q0, b, e, lo, hi)
-            for h in range(kvh, kvh + hpi):
+            for h in range(kvh, min(kvh + hpi, hkv)):
                 pieces.setdefault((q0, h), []).append((b, e, slot + (h - kvh) if slot >= 0 else -1))
         else:
             assert hpi == 1 and 0 <= kvh < hkv and qn >= 1
@@ -359,7 +360,7 @@ def test_sparse_layout_errors():
     pa.pa_plan_destroy(p)
 
 
-@pytest.mark.parametrize("hq", [128, 20, 8])
+@pytest.mark.parametrize("hq", [128, 48, 20, 8])
 @pytest.mark.parametrize("num_cus", [256, 7])
 def test_mla_head_groups(hq, num_cus):
     """MLA with other head counts: one unit per group of 16 query heads (the
@@ -372,7 +373,9 @@ def test_mla_head_groups(hq, num_cus):
                  mla=True)
     items, wg, merges, info = plan_of(s, num_cus)
     check_plan(s, items, wg, merges, info, min_piece=256)
-    assert set(items[:, 1].tolist()) == set(range(units))
+    # decode-only plans pair the head groups (two per item)
+    assert info["heads_per_item"] == (2 if units > 1 else 1)
+    assert set(items[:, 1].tolist()) == set(range(0, units, info["heads_per_item"]))
     xcd_of = {}
     for b in range(len(wg) - 1):
         for i in range(wg[b], wg[b + 1]):
