@@ -360,8 +360,10 @@ int pa_plan_bwd_workspace_bytes(const pa_plan* plan, int32_t dtype, int32_t head
  *                no visible key of any query lands on are zero
  *   workspace    >= pa_plan_bwd_workspace_bytes bytes, 256-byte aligned
  *
- * Head sizes D = Dv in {64, 128, 256} and 192 / 128, group sizes 1, 2, 4, 8,
- * 16 (other shapes give PA_ERR_UNSUPPORTED).  Errors:
+ * Head sizes and group sizes as for pa_attention_fwd: D = Dv in {64, 128, 256}
+ * and 192 / 128 at group sizes 1, 2, 4, 8, 16 run on the specialised kernels
+ * (16-bit MFMA, f32 vector), every other shape on vector-ALU kernels (fp32).
+ * Errors:
  * PA_ERR_INVALID for MLA plans (pa_mla_bwd), PA_ERR_UNSUPPORTED for missing
  * kernels;
  * PA_ERR_WORKSPACE,
@@ -431,7 +433,9 @@ int pa_sparse_workspace_bytes(const pa_plan* plan, int32_t v_head_dim, int32_t b
  *   dlat_t = sum_rows (scale dS_t q_abs + P_t dO)
  *   dkpos_t = sum_rows scale dS_t q_rope
  *
- *   dtype        PA_BF16 or PA_F16 (this build: rank 512, rope_dim 64, any H)
+ *   dtype        PA_F32, PA_BF16 or PA_F16; rank and rope_dim as for
+ *                pa_mla_fwd, any H (16-bit rank 512 / rope_dim 64 on MFMA,
+ *                the rest on vector-ALU kernels)
  *   q_abs, q_rope, latent, kpos, out, lse  as for pa_mla_fwd with the same
  *                plan (out and lse: the forward's results)
  *   dout         [Q, H, rank] output gradient

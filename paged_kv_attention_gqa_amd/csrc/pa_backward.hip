@@ -948,6 +948,296 @@ __global__ __launch_bounds__(kMlaBwdWaves* kWave) void mla_bwd_dkv_kernel(BwdArg
   }
 }
 
+// ---------------------------------------------------------------------------
+// Vector-ALU backward for every shape the kernels above do not take (any
+// group size, head sizes up to 1024, MLA with f32 data or other widths), in
+// the forward vector kernel's description (GenericShape: key rows [k1 | k2],
+// value rows V or, for MLA, k1 itself), fp32 throughout:
+//   dQ: one workgroup per dQ item (one query, one work unit of up to 16
+//       heads, its visible keys); the unit's heads in passes of 8, keys in
+//       tiles of 8: S and dP of the 64 (key, head) pairs (four threads per
+//       pair over a quarter of the dims each), dS = P (dP - D), then
+//       dq += dS k (d1 + d2 dims);
+//   dK/dV: one workgroup per dK/dV item (a block of keys of one KV head),
+//       8 keys at a time, their sums in registers while every (query, head)
+//       pair that sees them streams past 8 heads at a time:
+//       dk += scale dS q, dv += P dO; MLA adds dv to the latent's dk part.
+// Same items, zeroing, f32 sums for shared pages and D = dO . O pass as the
+// specialised kernels.
+// ---------------------------------------------------------------------------
+constexpr int kGbThreads = 256;
+constexpr int kGbHeads = 8;                                  // query heads per pass
+constexpr int kGbKeys = 8;                                   // keys per tile
+constexpr int kGbMaxW = kGenericMaxKeyWidth;                 // key row (d1 + d2) <= 1280
+constexpr int kGbMaxV = kGenericMaxValueWidth;               // value row <= 1024
+constexpr int kGbPhases = kGbThreads / kGbKeys;              // 32 threads per key / head of a pass
+constexpr int kGbW = kGbMaxW / kGbPhases, kGbV = kGbMaxV / kGbPhases;  // dims per thread: 40, 32
+static_assert(kGbThreads == 4 * kGbKeys * kGbHeads && kGbKeys == kGbHeads, "four threads per (key, head) pair");
+
+// First query head and head count of work unit u (as the forward kernel).
+__device__ __forceinline__ void gb_unit_heads(const GenericShape& s, int u, int* h0, int* nh) {
+  const int kv = u / s.nsub, sub = u - kv * s.nsub;
+  *h0 = kv * s.g + sub * s.unit_heads;
+  *nh = min(s.unit_heads, s.g - sub * s.unit_heads);
+}
+
+// The query rows (q1 | q2 -> qs, W wide) and output-gradient rows (-> gs,
+// DV wide) of heads h0 .. h0 + 7 of query qi (rows past n repeat the last),
+// their lse in log2 units and D = dO . O, as f32 in LDS.
+template <typename T>
+__device__ __forceinline__ void gb_load_rows(const BwdArgs& b, const GenericShape& s, int qi, int h0, int n, float* qs,
+                                             float* gs, float* st) {
+  const KernelArgs& a = b.a;
+  const int W = s.d1 + s.d2, DV = s.dv;
+  for (int idx = threadIdx.x; idx < kGbHeads * W; idx += kGbThreads) {
+    const int h = idx / W, d = idx - h * W;
+    const uint64_t row = (uint64_t)qi * a.hq + h0 + min(h, n - 1);
+    qs[idx] = d < s.d1 ? load_elem<T>(a.q, row * s.d1 + d) : load_elem<T>(a.qr, row * s.d2 + (d - s.d1));
+  }
+  for (int idx = threadIdx.x; idx < kGbHeads * DV; idx += kGbThreads) {
+    const int h = idx / DV, d = idx - h * DV;
+    gs[idx] = load_elem<T>(b.dout, ((uint64_t)qi * a.hq + h0 + min(h, n - 1)) * DV + d);
+  }
+  if (threadIdx.x < kGbHeads) {
+    const uint64_t row = (uint64_t)qi * a.hq + h0 + min((int)threadIdx.x, n - 1);
+    st[threadIdx.x] = a.lse[row] * kLog2e;
+    st[kGbHeads + threadIdx.x] = b.delta[row];
+  }
+}
+
+// Key rows (k1 | k2 -> ks, W wide) and value rows (-> vs, DV wide, unless V
+// is k1) of keys t0 .. t0 + 7 of KV head kv (keys from `last` on repeat it).
+template <typename T>
+__device__ __forceinline__ void gb_load_keys(const KernelArgs& a, const GenericShape& s, const int32_t* bt, int kv,
+                                             int t0, int last, float* ks, float* vs) {
+  const int W = s.d1 + s.d2, DV = s.dv, ps = 1 << a.page_shift;
+  for (int idx = threadIdx.x; idx < kGbKeys * W; idx += kGbThreads) {
+    const int k = idx / W, d = idx - k * W;
+    const int t = min(t0 + k, last);
+    const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+    ks[idx] = d < s.d1 ? load_elem<T>(a.k, (slot * a.hkv + kv) * s.d1 + d)
+                       : load_elem<T>(a.kr, slot * s.d2 + (d - s.d1));
+  }
+  if (!s.v_is_k) {
+    for (int idx = threadIdx.x; idx < kGbKeys * DV; idx += kGbThreads) {
+      const int k = idx / DV, d = idx - k * DV;
+      const int t = min(t0 + k, last);
+      const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+      vs[idx] = load_elem<T>(a.v, (slot * a.hkv + kv) * DV + d);
+    }
+  }
+}
+
+// S (log2 units) and dP of this thread's (key, head) pair: four threads per
+// pair, each over a quarter of the dims, summed by lane exchange.
+__device__ __forceinline__ void gb_pair_dots(const GenericShape& s, const float* qs, const float* gs, const float* ks,
+                                             const float* vt, int vstride, float scale_log2, int* sk, int* sh,
+                                             float* sc, float* dp) {
+  const int W = s.d1 + s.d2, DV = s.dv;
+  const int pair = threadIdx.x >> 2, part = threadIdx.x & 3;
+  *sk = pair / kGbHeads;
+  *sh = pair % kGbHeads;
+  const float* q = qs + *sh * W;
+  const float* k = ks + *sk * W;
+  const float* g = gs + *sh * DV;
+  const float* v = vt + *sk * vstride;
+  float a0 = 0.f, a1 = 0.f;
+  for (int d = part; d < W; d += 4) a0 = __builtin_fmaf(q[d], k[d], a0);
+  for (int d = part; d < DV; d += 4) a1 = __builtin_fmaf(g[d], v[d], a1);
+  a0 += __shfl_xor(a0, 1);
+  a1 += __shfl_xor(a1, 1);
+  a0 += __shfl_xor(a0, 2);
+  a1 += __shfl_xor(a1, 2);
+  *sc = a0 * scale_log2;
+  *dp = a1;
+}
+
+// Pool rows of any width: zero the runs of slots no dK/dV item writes, zero
+// f32 sums, round f32 sums into a 16-bit pool -- element by element (2-byte
+// units for the runs), since rows need not be whole 16-byte pieces here.
+__global__ __launch_bounds__(256) void gbwd_zero_runs_kernel(char* dk, char* dv, const int32_t* runs, int k_row,
+                                                             int v_row) {
+  const int64_t first = runs[2 * blockIdx.x], count = runs[2 * blockIdx.x + 1];
+  uint16_t* pk = reinterpret_cast<uint16_t*>(dk + first * k_row);
+  uint16_t* pv = reinterpret_cast<uint16_t*>(dv + first * v_row);
+  for (int64_t i = threadIdx.x; i < count * k_row / 2; i += blockDim.x) pk[i] = 0;
+  for (int64_t i = threadIdx.x; i < count * v_row / 2; i += blockDim.x) pv[i] = 0;
+}
+__global__ __launch_bounds__(256) void gbwd_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0.f;
+}
+template <typename T>
+__global__ __launch_bounds__(256) void gbwd_cast_kernel(const float* src, void* dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    store_out<T>(dst, i, src[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGbThreads) void gbwd_dq_kernel(BwdArgs b, GenericShape s) {
+  __shared__ float q_s[kGbHeads * kGbMaxW];
+  __shared__ float g_s[kGbHeads * kGbMaxV];
+  __shared__ float k_s[kGbKeys * kGbMaxW];
+  __shared__ float v_s[kGbKeys * kGbMaxV];
+  __shared__ float st_s[2 * kGbHeads];
+  __shared__ float ds_s[kGbKeys * kGbHeads];
+  const KernelArgs& a = b.a;
+  const BwdItem it = b.items[blockIdx.x];
+  const int W = s.d1 + s.d2;
+  const float* vt = s.v_is_k ? k_s : v_s;
+  const int vstride = s.v_is_k ? W : s.dv;
+  const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
+  const int qi = it.q_begin, pos = a.q_pos[qi];
+  const int kv = it.kvh / s.nsub;
+  int h0, nh;
+  gb_unit_heads(s, it.kvh, &h0, &nh);
+  const int oh = threadIdx.x / kGbPhases, od = threadIdx.x % kGbPhases;  // output head of the pass, dim phase
+  for (int p0 = 0; p0 < nh; p0 += kGbHeads) {
+    const int np = min(kGbHeads, nh - p0);
+    __syncthreads();  // the previous pass's rows are no longer read
+    gb_load_rows<T>(b, s, qi, h0 + p0, np, q_s, g_s, st_s);
+    float acc[kGbW];
+#pragma unroll
+    for (int j = 0; j < kGbW; ++j) acc[j] = 0.f;
+    for (int t0 = it.tok_begin; t0 < it.tok_end; t0 += kGbKeys) {
+      __syncthreads();  // the previous tile is consumed (and the rows are written)
+      gb_load_keys<T>(a, s, bt, kv, t0, it.tok_end - 1, k_s, v_s);
+      __syncthreads();
+      int sk, sh;
+      float sc, dp;
+      gb_pair_dots(s, q_s, g_s, k_s, vt, vstride, a.scale_log2, &sk, &sh, &sc, &dp);
+      if ((threadIdx.x & 3) == 0) {
+        const int t = t0 + sk;
+        const bool vis = t < it.tok_end && (!a.causal || t <= pos) && (a.window == 0 || t > pos - a.window);
+        const float p = vis ? fast_exp2(sc - st_s[sh]) : 0.f;
+        ds_s[sk * kGbHeads + sh] = p * (dp - st_s[kGbHeads + sh]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kGbW; ++j) {
+        const int d = od + kGbPhases * j;
+        if (d < W) {
+          float x = acc[j];
+#pragma unroll
+          for (int k = 0; k < kGbKeys; ++k) x = __builtin_fmaf(ds_s[k * kGbHeads + oh], k_s[k * W + d], x);
+          acc[j] = x;
+        }
+      }
+    }
+    if (oh < np) {
+      const uint64_t row = (uint64_t)qi * a.hq + h0 + p0 + oh;
+#pragma unroll
+      for (int j = 0; j < kGbW; ++j) {
+        const int d = od + kGbPhases * j;
+        if (d < s.d1)
+          store_out<T>(b.dq, row * s.d1 + d, acc[j] * a.scale);
+        else if (d < W)
+          store_out<T>(b.dq2, row * s.d2 + (d - s.d1), acc[j] * a.scale);
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGbThreads) void gbwd_dkv_kernel(BwdArgs b, GenericShape s, int first_item) {
+  __shared__ float q_s[kGbHeads * kGbMaxW];
+  __shared__ float g_s[kGbHeads * kGbMaxV];
+  __shared__ float k_s[kGbKeys * kGbMaxW];
+  __shared__ float v_s[kGbKeys * kGbMaxV];
+  __shared__ float st_s[2 * kGbHeads];
+  __shared__ float p_s[kGbKeys * kGbHeads], ds_s[kGbKeys * kGbHeads];
+  const KernelArgs& a = b.a;
+  const BwdItem it = b.items[first_item + blockIdx.x];
+  const int W = s.d1 + s.d2, DV = s.dv;
+  const float* vt = s.v_is_k ? k_s : v_s;
+  const int vstride = s.v_is_k ? W : DV;
+  const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
+  const int L = a.seq_lens[it.seq], ps = 1 << a.page_shift;
+  const int kv = it.kvh;
+  const int ok = threadIdx.x / kGbPhases, od = threadIdx.x % kGbPhases;  // key of the tile, dim phase
+  for (int sub = it.tok_begin; sub < it.tok_end; sub += kGbKeys) {
+    const int te = min(it.tok_end, sub + kGbKeys);
+    __syncthreads();  // the previous keys are no longer read
+    gb_load_keys<T>(a, s, bt, kv, sub, te - 1, k_s, v_s);
+    float dk[kGbW], dv[kGbV];
+#pragma unroll
+    for (int j = 0; j < kGbW; ++j) dk[j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kGbV; ++j) dv[j] = 0.f;
+    for (int qi = it.q_begin; qi < it.q_end; ++qi) {
+      const int pos = a.q_pos[qi];
+      const int hi = a.causal ? pos : L - 1;
+      const int lo = a.window > 0 ? max(0, pos - a.window + 1) : 0;
+      if (hi < sub || lo >= te) continue;  // this query sees none of the keys
+      for (int p0 = 0; p0 < s.g; p0 += kGbHeads) {
+        const int np = min(kGbHeads, s.g - p0);
+        __syncthreads();  // the previous rows and weights are no longer read (and the keys are written)
+        gb_load_rows<T>(b, s, qi, kv * s.g + p0, np, q_s, g_s, st_s);
+        __syncthreads();
+        int sk, sh;
+        float sc, dp;
+        gb_pair_dots(s, q_s, g_s, k_s, vt, vstride, a.scale_log2, &sk, &sh, &sc, &dp);
+        if ((threadIdx.x & 3) == 0) {
+          const int t = sub + sk;
+          const bool vis = sh < np && t < te && t >= lo && t <= hi;
+          const float p = vis ? fast_exp2(sc - st_s[sh]) : 0.f;
+          p_s[sk * kGbHeads + sh] = p;
+          ds_s[sk * kGbHeads + sh] = p * (dp - st_s[kGbHeads + sh]) * a.scale;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kGbW; ++j) {
+          const int d = od + kGbPhases * j;
+          if (d < W) {
+            float x = dk[j];
+#pragma unroll
+            for (int h = 0; h < kGbHeads; ++h) x = __builtin_fmaf(ds_s[ok * kGbHeads + h], q_s[h * W + d], x);
+            dk[j] = x;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kGbV; ++j) {
+          const int d = od + kGbPhases * j;
+          if (d < DV) {
+            float x = dv[j];
+#pragma unroll
+            for (int h = 0; h < kGbHeads; ++h) x = __builtin_fmaf(p_s[ok * kGbHeads + h], g_s[h * DV + d], x);
+            dv[j] = x;
+          }
+        }
+      }
+    }
+    // key sub + ok: GQA writes dk (d1 wide) and dv (DV wide) rows of KV head
+    // kv; MLA the latent row (dk's first d1 dims plus dv) and the rotary row
+    const int t = sub + ok;
+    if (t < te) {
+      const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+      const uint64_t ra = (slot * a.hkv + kv) * s.d1;
+      if (s.v_is_k) {
+#pragma unroll
+        for (int j = 0; j < kGbW; ++j) {
+          const int d = od + kGbPhases * j;
+          if (d < s.d1)
+            put_grad<T>(b.dk, b.acc_k, ra + d, dk[j] + (j < kGbV ? dv[j] : 0.f));
+          else if (d < W)
+            put_grad<T>(b.dv, b.acc_v, slot * s.d2 + (d - s.d1), dk[j]);
+        }
+      } else {
+        const uint64_t rb = (slot * a.hkv + kv) * DV;
+#pragma unroll
+        for (int j = 0; j < kGbW; ++j) {
+          const int d = od + kGbPhases * j;
+          if (d < s.d1) put_grad<T>(b.dk, b.acc_k, ra + d, dk[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kGbV; ++j) {
+          const int d = od + kGbPhases * j;
+          if (d < DV) put_grad<T>(b.dv, b.acc_v, rb + d, dv[j]);
+        }
+      }
+    }
+  }
+}
+
 namespace {
 
 using BwdFn = hipError_t (*)(const BwdArgs&, int, int, int, hipStream_t);
@@ -1144,6 +1434,71 @@ hipError_t launch_mla_bwd(int dtype, const KernelArgs& a, const void* dout, void
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+
+hipError_t launch_generic_bwd(int dtype, const GenericShape& s, const KernelArgs& a, const void* dout, void* dq,
+                              void* dq2, void* dk, void* dvp, float* delta, float* acc, bool shared,
+                              const BwdItem* items, int n_dq, int n_kv, const int32_t* zero_runs, int n_zero_runs,
+                              int64_t rows, int64_t pool_rows, int n_cu, hipStream_t stream) {
+  if (!generic_shape_ok(s) || dtype < 0 || dtype > 2) return hipErrorInvalidValue;
+  const int es = dtype == 0 ? 4 : 2;
+  const int wa = s.d1, wb = s.v_is_k ? s.d2 : s.dv;  // widths of the two gradient pools' rows
+  const int64_t grid_cap = (int64_t)std::max(n_cu, 1) * 16;
+  float* acc_k = nullptr;
+  float* acc_v = nullptr;
+  if (shared) {
+    // f32 gradients are added into the pools themselves, 16-bit ones into f32
+    // sums in the workspace; either way they start at zero everywhere
+    acc_k = dtype == 0 ? static_cast<float*>(dk) : acc;
+    acc_v = dtype == 0 ? static_cast<float*>(dvp) : acc + pool_rows * wa;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int64_t n = pool_rows * (pass == 0 ? wa : wb);
+      if (n == 0) continue;
+      hipLaunchKernelGGL(gbwd_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, grid_cap)), dim3(256), 0,
+                         stream, pass == 0 ? acc_k : acc_v, n);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else if (n_zero_runs > 0) {
+    hipLaunchKernelGGL(gbwd_zero_runs_kernel, dim3(n_zero_runs), dim3(256), 0, stream, static_cast<char*>(dk),
+                       static_cast<char*>(dvp), zero_runs, a.hkv * wa * es, a.hkv * wb * es);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdArgs b{a, dout, dq, dk, dvp, delta, items, acc_k, acc_v, dq2};
+  auto run = [&](auto tag) -> hipError_t {
+    using T = decltype(tag);
+    if (rows > 0) {
+      hipLaunchKernelGGL(bwd_delta_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, b, rows, s.dv);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (n_dq > 0) {
+      hipLaunchKernelGGL(gbwd_dq_kernel<T>, dim3(n_dq), dim3(kGbThreads), 0, stream, b, s);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (n_kv > 0) {
+      hipLaunchKernelGGL(gbwd_dkv_kernel<T>, dim3(n_kv), dim3(kGbThreads), 0, stream, b, s, n_dq);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (shared && dtype != 0) {
+      for (int pass = 0; pass < 2; ++pass) {
+        const int64_t n = pool_rows * (pass == 0 ? wa : wb);
+        if (n == 0) continue;
+        hipLaunchKernelGGL(gbwd_cast_kernel<T>, dim3((unsigned)std::min<int64_t>((n + 255) / 256, grid_cap)),
+                           dim3(256), 0, stream, pass == 0 ? acc_k : acc_v, pass == 0 ? dk : dvp, n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
+    return hipSuccess;
+  };
+  if (dtype == 0) return run(float{});
+  if (dtype == 1) return run(uint16_t{});
+  return run(_Float16{});
 }
 
 }  // namespace pa

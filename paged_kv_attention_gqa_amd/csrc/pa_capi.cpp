@@ -1142,10 +1142,10 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   if (head_dim <= 0 || v_head_dim <= 0 || head_dim > 1024 || v_head_dim > 1024)
     return fail(PA_ERR_SHAPE, "head sizes D=%d Dv=%d outside [1, 1024]", head_dim, v_head_dim);
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
+  // the specialised kernels where they exist, else the vector kernels (any
+  // group size and head sizes up to 1024)
   const int G = plan->group();
-  if (!pa::bwd_supported(dtype, head_dim, v_head_dim, G))
-    return fail(PA_ERR_UNSUPPORTED, "no backward kernel for dtype %d, D=%d, Dv=%d, G=%d", dtype, head_dim, v_head_dim,
-                G);
+  const bool generic = plan->grouped() || !pa::bwd_supported(dtype, head_dim, v_head_dim, G);
   size_t need = 0;
   pa_plan_bwd_workspace_bytes(plan, dtype, head_dim, v_head_dim, &need);
   if (need > 0) {
@@ -1187,12 +1187,20 @@ int pa_attention_bwd(const pa_plan* plan, int32_t dtype, const void* q, const vo
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.causal = plan->causal;
   a.window = plan->window;
-  hipError_t e = pa::launch_gqa_bwd(dtype, head_dim, v_head_dim, G, a, dout, dq, dk_pool, dv_pool,
-                                    reinterpret_cast<float*>(workspace),
-                                    reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(plan)),
-                                    bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv,
-                                    plan->n_bwd_dqt, plan->d_zero_runs, (int)(plan->zero_runs.size() / 2), (int64_t)rows,
-                                    (int64_t)slots, std::max(plan->n_cu, 1), st);
+  float* delta = reinterpret_cast<float*>(workspace);
+  float* acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(plan));
+  const int n_runs = (int)(plan->zero_runs.size() / 2);
+  hipError_t e;
+  if (generic) {
+    const pa::GenericShape shape{head_dim, 0, v_head_dim, G, plan->nsub(), plan->unit_heads(), 1, 0};
+    e = pa::launch_generic_bwd(dtype, shape, a, dout, dq, nullptr, dk_pool, dv_pool, delta, acc, bwd_shared(plan),
+                               plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv, plan->d_zero_runs, n_runs, (int64_t)rows,
+                               (int64_t)slots, std::max(plan->n_cu, 1), st);
+  } else {
+    e = pa::launch_gqa_bwd(dtype, head_dim, v_head_dim, G, a, dout, dq, dk_pool, dv_pool, delta, acc,
+                           bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv, plan->n_bwd_dqt,
+                           plan->d_zero_runs, n_runs, (int64_t)rows, (int64_t)slots, std::max(plan->n_cu, 1), st);
+  }
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }
@@ -1211,9 +1219,8 @@ int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   if (rank <= 0 || rank > 1024) return fail(PA_ERR_SHAPE, "latent rank %d outside [1, 1024]", rank);
   if (rope_dim <= 0 || rope_dim > 256) return fail(PA_ERR_SHAPE, "rotary width rope_dim %d outside [1, 256]", rope_dim);
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PA_ERR_SHAPE, "scale %g must be finite and > 0", scale);
-  if (!pa::mla_bwd_supported(dtype, plan->hq, rank, rope_dim))
-    return fail(PA_ERR_UNSUPPORTED, "no MLA backward kernel for dtype %d, H=%d, rank=%d, rope_dim=%d", dtype, plan->hq,
-                rank, rope_dim);
+  // the MFMA kernels for 16-bit rank 512 / width 64, else the vector kernels
+  const bool generic = !pa::mla_bwd_supported(dtype, plan->hq, rank, rope_dim);
   size_t need = 0;
   pa_plan_bwd_workspace_bytes(plan, dtype, rank, rope_dim, &need);
   if (need > 0) {
@@ -1223,7 +1230,7 @@ int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
       return fail(PA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
   }
-  const size_t es = 2;
+  const size_t es = dtype == PA_F32 ? 4 : 2;
   const size_t slots = (size_t)plan->num_pages * plan->ps;
   const size_t rows = (size_t)plan->Q * plan->hq;
   const Extent e_dqa{dq_abs, rows * rank * es, "dq_abs"}, e_dqr{dq_rope, rows * rope_dim * es, "dq_rope"};
@@ -1258,12 +1265,21 @@ int pa_mla_bwd(const pa_plan* plan, int32_t dtype, const void* q_abs, const void
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.causal = plan->causal;
   a.window = plan->window;
-  hipError_t e = pa::launch_mla_bwd(dtype, a, dout, dq_abs, dq_rope, dlatent, dkpos,
-                                    reinterpret_cast<float*>(workspace),
-                                    reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(plan)),
-                                    bwd_shared(plan), plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv, plan->d_zero_runs,
-                                    (int)(plan->zero_runs.size() / 2), (int64_t)rows,
-                                    (int64_t)slots, std::max(plan->n_cu, 1), reinterpret_cast<hipStream_t>(stream));
+  float* delta = reinterpret_cast<float*>(workspace);
+  float* acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(plan));
+  const int n_runs = (int)(plan->zero_runs.size() / 2);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (generic) {
+    const pa::GenericShape shape{rank, rope_dim, rank, plan->hq, plan->nsub(), plan->unit_heads(), 1, 1};
+    e = pa::launch_generic_bwd(dtype, shape, a, dout, dq_abs, dq_rope, dlatent, dkpos, delta, acc, bwd_shared(plan),
+                               plan->d_bwd, plan->n_bwd_dq, plan->n_bwd_kv, plan->d_zero_runs, n_runs, (int64_t)rows,
+                               (int64_t)slots, std::max(plan->n_cu, 1), st);
+  } else {
+    e = pa::launch_mla_bwd(dtype, a, dout, dq_abs, dq_rope, dlatent, dkpos, delta, acc, bwd_shared(plan), plan->d_bwd,
+                           plan->n_bwd_dq, plan->n_bwd_kv, plan->d_zero_runs, n_runs, (int64_t)rows, (int64_t)slots,
+                           std::max(plan->n_cu, 1), st);
+  }
   if (e != hipSuccess) return hip_fail(e, "MLA backward launch");
   return ok();
 }

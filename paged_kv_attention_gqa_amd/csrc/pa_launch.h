@@ -149,6 +149,17 @@ hipError_t launch_sparse_select(int dtype, const SparseArgs& a, int rows, hipStr
 // key positions): dK / dV are added up in f32 -- in the pools for f32 data,
 // else in `acc` (pool_slots x (d + dv) floats) rounded into the pools last.
 bool bwd_supported(int dtype, int d, int dv, int g);
+// The vector-ALU backward of every other shape (GQA or MLA in the forward
+// vector kernel's description): the same items (dQ per (query, work unit),
+// dK/dV per (key block, KV head)), zeroing, f32 sums for shared pages and
+// D pass as the specialised launches.  dq / dq2: gradients of the q1 / q2
+// query parts; dk / dvp: pools of rows s.d1 wide and (GQA) s.dv or (MLA)
+// s.d2 wide, pool_rows rows each (MLA: dk is the latent pool, receiving
+// the key and value terms).  acc: f32 sums of pool_rows x (both widths).
+hipError_t launch_generic_bwd(int dtype, const GenericShape& s, const KernelArgs& a, const void* dout, void* dq,
+                              void* dq2, void* dk, void* dvp, float* delta, float* acc, bool shared,
+                              const BwdItem* items, int n_dq, int n_kv, const int32_t* zero_runs, int n_zero_runs,
+                              int64_t rows, int64_t pool_rows, int n_cu, hipStream_t stream);
 hipError_t launch_gqa_bwd(int dtype, int d, int dv, int g, const KernelArgs& a, const void* dout, void* dq, void* dk,
                           void* dvp, float* delta, float* acc, bool shared, const BwdItem* items, int n_dq, int n_kv,
                           int n_dqt, const int32_t* zero_runs, int n_zero_runs, int64_t rows, int64_t pool_slots,

@@ -106,21 +106,6 @@ def test_mla_other_shapes_and_f32(i, split_tokens):
     np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-4 if dtype == "f32" else 1e-3)
 
 
-def test_mla_backward_refuses_shapes_without_kernel():
-    """The backward runs 16-bit data with rank 512 and rotary width 64 only:
-    other shapes get PA_ERR_UNSUPPORTED before anything is launched."""
-    import torch
-    import paged_kv_attention_gqa_amd as pa
-    m = random_mla_batch(3400, r=256, p=32, q_counts=(1, 2), max_len=200)
-    run = MlaRun(m)
-    run()
-    z = torch.zeros_like(run.out)
-    with pytest.raises(pa.PaError, match="PA_ERR_UNSUPPORTED"):
-        pa.pa_mla_bwd(run.plan, run.q_abs, run.q_rope, run.latent, run.kpos, run.out, run.lse, z, z.clone(),
-                      torch.zeros_like(run.q_rope), torch.zeros_like(run.latent), torch.zeros_like(run.kpos),
-                      scale=m.scale, workspace=None)
-
-
 @pytest.mark.timeout(600)
 def test_mla_decode_h128_full_size_all_rows():
     """The MLA decode shape with 128 query heads (eight head groups reading
