@@ -364,8 +364,7 @@ int pa_plan_bwd_workspace_bytes(const pa_plan* plan, int32_t dtype, int32_t head
  * and 192 / 128 at group sizes 1, 2, 4, 8, 16 run on the specialised kernels
  * (16-bit MFMA, f32 vector), every other shape on vector-ALU kernels (fp32).
  * Errors:
- * PA_ERR_INVALID for MLA plans (pa_mla_bwd), PA_ERR_UNSUPPORTED for missing
- * kernels;
+ * PA_ERR_INVALID for MLA plans (pa_mla_bwd);
  * PA_ERR_WORKSPACE,
  * PA_ERR_OVERLAP, PA_ERR_SHAPE, PA_ERR_DEVICE, PA_ERR_HIP as for
  * pa_attention_fwd.  Q == 0 zeroes dk_pool and dv_pool and touches nothing
