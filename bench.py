@@ -471,7 +471,7 @@ def measure_sparse(name, steps, warmup, block_size=64, topk=16):
 
 PRIMARY = "bf16_decode_batch"
 SECONDARY = ("bf16_chunked_prefill", "bf16_mixed_batch", "bf16_mla_decode", "bf16_mla_decode_h128",
-             "bf16_mla_chunked_prefill", "bf16_chunked_prefill_d192")
+             "bf16_mla_chunked_prefill", "bf16_chunked_prefill_d192", "bf16_chunked_prefill_d256")
 APPEND = ("bf16_decode_batch", "bf16_chunked_prefill")  # cache writes of one decode step and of one chunk
 BACKWARD = ("bf16_chunked_prefill",)  # gradients of one chunk step
 MLA_BACKWARD = ("bf16_mla_chunked_prefill",)

@@ -11,7 +11,6 @@
 #include "pa_decode.h"
 #include "pa_launch.h"
 #include "pa_prefill.h"
-#include "pa_prefill16.h"
 
 namespace pa {
 
@@ -88,17 +87,14 @@ void decode_short_kernel(KernelArgs a) {
 // share the grid (packed decode + chunked prefill in one dispatch).
 template <typename T, int D, int DV, int G>
 struct MixedShape {
-  // the 32x32x16 MFMA tile with its LDS DMA ring: D = Dv = 64 or 128, and
-  // D = 192 with Dv = 128 (four 40 KB stages fill the 160 KB of LDS)
+  // the 32x32x16 MFMA tile with its LDS DMA ring: D = Dv = 64 or 128,
+  // D = 192 with Dv = 128 (four 40 KB stages fill the 160 KB of LDS), and
+  // D = Dv = 256 in two passes of 128 output dims (three 48 KB stages)
   static constexpr bool kMfma = sizeof(T) == 2 && G <= kPrefillRows &&
-                                ((D == DV && (D == 64 || D == 128)) || (D == 192 && DV == 128));
-  // other K and V widths, and D = Dv = 256: the 16x16x32 MFMA tile
-  static constexpr bool kMfma16 =
-      sizeof(T) == 2 && !kMfma && D % 64 == 0 && DV % 64 == 0 && (D != DV || D == 256) && G <= kPrefillRows;
+                                ((D == DV && (D == 64 || D == 128 || D == 256)) || (D == 192 && DV == 128));
   static constexpr int kDecodeBytes = kPrefillWaves * G * (DV + 3) * 4;
   static constexpr int kPrefillBytes =
-      kMfma ? PrefillSmem<(kMfma ? D : 64), (kMfma ? DV : 64)>::kBytes
-            : (kMfma16 ? Prefill16Smem<D, DV>::kBytes : 0);
+      kMfma ? PrefillSmem<(kMfma ? D : 64), (kMfma ? PrefillPass<D, DV>::kDims : 64)>::kBytes : 0;
   static constexpr int kBytes = kDecodeBytes > kPrefillBytes ? kDecodeBytes : kPrefillBytes;
 };
 
@@ -112,8 +108,6 @@ void mixed_kernel(KernelArgs a) {
   if (it.kind == kPrefill) {
     if constexpr (MixedShape<T, D, DV, G>::kMfma)
       prefill_item<T, D, DV, G>(a, it, smem);
-    else if constexpr (MixedShape<T, D, DV, G>::kMfma16)
-      prefill16_item<T, D, DV, G>(a, it, smem);
     else
       prefill_item_by_queries<T, D, DV, G, kPrefillWaves, DecodeUnroll<G>::kValue>(a, it,
                                                                                   reinterpret_cast<float*>(smem));

@@ -38,7 +38,7 @@ constexpr int kPrefillTileKeys = 64;
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillRows = kPrefillWaves * kPrefillRowsPerWave;
-constexpr int kPrefillStages = 4;  // K/V tiles in the LDS ring
+constexpr int kLdsBytes = 160 * 1024;
 constexpr bool kPrefillPingPong = true;  // two wave groups in opposite phase (see prefill_item_impl)
 constexpr float kLazyRescaleLog2 = 8.f;  // weights may reach 2^8 before the reference max moves
 
@@ -47,7 +47,10 @@ struct PrefillSmem {
   static constexpr int kTileK = kPrefillTileKeys * D * 2;   // bytes of one K tile
   static constexpr int kTileV = kPrefillTileKeys * DV * 2;  // bytes of one V tile
   static constexpr int kStage = kTileK + kTileV;
-  static constexpr int kBytes = kPrefillStages * kStage;
+  // K/V tiles in the LDS ring: four (two in flight), or three (one in
+  // flight) where four stages do not fit the 160 KB of LDS
+  static constexpr int kStages = 4 * kStage <= kLdsBytes ? 4 : 3;
+  static constexpr int kBytes = kStages * kStage;
 };
 
 template <typename T>
@@ -143,14 +146,19 @@ __device__ __forceinline__ int tile_off(int key, int piece) {
 // tiles; the loop body issues no other vector-memory loads (a per-tile
 // per-lane lookup would make the compiler drain the vector-memory counter
 // before every tile issue).
-template <typename T, int D, int DV, int G, bool UNIFORM>
-__device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const WorkItem& it, char* smem) {
+//
+// DVM: the width of the V and output rows in memory; a tile computes output
+// dims dv0 .. dv0 + DV - 1 of them (DV < DVM: one pass of several, each
+// recomputing the scores).
+template <typename T, int D, int DV, int G, bool UNIFORM, int DVM = DV>
+__device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const WorkItem& it, char* smem, int dv0 = 0) {
   constexpr int NT = kPrefillTileKeys;
   constexpr int KS = D / 16;                         // MFMA k-steps of S^T (over head dims)
   constexpr int DB = DV / 32;                        // 32-dim blocks of O^T
   constexpr int TILE_K = PrefillSmem<D, DV>::kTileK;
   constexpr int STAGE = PrefillSmem<D, DV>::kStage;
-  constexpr int NS = kPrefillStages;
+  constexpr int NS = PrefillSmem<D, DV>::kStages;
+  static_assert(NS >= 3, "the ring holds the V tile read, the K tile scored and one in flight");
   constexpr int MB = NT / 32;                        // 32-key MFMA blocks per tile
   constexpr int HALF = kPrefillWaves / 2;            // waves loading K (the others load V)
   constexpr int KEYS_PER_WAVE = NT / HALF;           // consecutive key rows one wave loads per tile
@@ -215,9 +223,9 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   // as well.
   const int wq = wave % HALF;
   const bool loads_v = wave >= HALF;
-  const uint32_t rs_k = (uint32_t)a.hkv * D * 2, rs_v = (uint32_t)a.hkv * DV * 2;  // bytes between key rows
+  const uint32_t rs_k = (uint32_t)a.hkv * D * 2, rs_v = (uint32_t)a.hkv * DVM * 2;  // bytes between key rows
   const char* pool_k = reinterpret_cast<const char*>(a.k) + (uint64_t)it.kvh * D * 2;
-  const char* pool_v = reinterpret_cast<const char*>(a.v) + (uint64_t)it.kvh * DV * 2;
+  const char* pool_v = reinterpret_cast<const char*>(a.v) + ((uint64_t)it.kvh * DVM + dv0) * 2;
   // Page numbers of this wave's key group in 64 consecutive tiles are one
   // vector load (lane k holding tile win + k's, handed out with v_readlane),
   // reloaded every 64 tiles: a scalar load per tile would make the first
@@ -304,7 +312,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   };
   auto issue_tile = [&](int t0, char* stage, int page) {
     const int k0 = t0 + KEYS_PER_WAVE * wq;  // first key of this wave's rows
-    if constexpr (D == DV) {  // one code path for both halves of the waves
+    if constexpr (D == DV && DV == DVM) {  // one code path for both halves of the waves
       issue_rows(RowWidth<D>{}, loads_v ? pool_v : pool_k, rs_k,
                  stage + (loads_v ? TILE_K : 0) + KEYS_PER_WAVE * wq * (D * 2), k0, page);
     } else if (loads_v) {
@@ -474,7 +482,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   floatx16_t s[MB];
   frag_t pf[NT / 16];
   auto sync = [&](int j) {
-    wait_tiles(min(ntiles - 1 - j, 1));  // tile j has landed, j + 1 may be in flight
+    wait_tiles(min(ntiles - 1 - j, NS - 3));  // tile j has landed, j + 1 may be in flight (four stages)
     barrier_keep_loads();                // ... for every wave; tile j - 2 is no longer read
     if (j + NS - 2 < ntiles) {
       issue_tile(t_first + (j + NS - 2) * NT, smem + ((j + NS - 2) % NS) * STAGE, page_next);
@@ -502,7 +510,7 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   l = pair32_sum(l);
   if (!row_valid) return;
   const float inv = 1.f / l;
-  uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * a.hq + head) * DV;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((uint64_t)qi * a.hq + head) * DVM + dv0;
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -513,21 +521,33 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
       w.y = Pair16<T>::pack(o[b][4 * k + 2] * inv, o[b][4 * k + 3] * inv);
       *reinterpret_cast<uint2*>(orow + 32 * b + 8 * k + 4 * h) = w;
     }
-  if (a.lse && h == 0) a.lse[(uint64_t)qi * a.hq + head] = m * a.scale + logf(l);
+  if (a.lse && h == 0 && dv0 == 0) a.lse[(uint64_t)qi * a.hq + head] = m * a.scale + logf(l);
 }
+
+// D = Dv = 256 runs in two passes of 128 output dims (the output sums of 256
+// dims and the 256-dim query operand would not fit one wave's registers).
+template <int D, int DV>
+struct PrefillPass {
+  static constexpr int kDims = (D == 256 && DV == 256) ? 128 : DV;
+};
 
 template <typename T, int D, int DV, int G>
 __device__ __forceinline__ void prefill_item(const KernelArgs& a, const WorkItem& it, char* smem) {
   static_assert(sizeof(T) == 2, "the MFMA tile runs on 16-bit data");
-  if (a.page_shift >= 4)
-    prefill_item_impl<T, D, DV, G, true>(a, it, smem);
-  else
-    prefill_item_impl<T, D, DV, G, false>(a, it, smem);
+  constexpr int DP = PrefillPass<D, DV>::kDims;
+#pragma unroll 1
+  for (int dv0 = 0; dv0 < DV; dv0 += DP) {
+    if (dv0 > 0) __syncthreads();  // every wave is done with the previous pass's ring
+    if (a.page_shift >= 4)
+      prefill_item_impl<T, D, DP, G, true, DV>(a, it, smem, dv0);
+    else
+      prefill_item_impl<T, D, DP, G, false, DV>(a, it, smem, dv0);
+  }
 }
 
 // A prefill tile handled one query at a time by the decode body (f32 data,
-// and head sizes without an MFMA tile: D = 256, or K and V rows of different
-// widths): each query's keys [lo, hi] are its own visible range.
+// which has no MFMA tile): each query's keys [lo, hi] are its own visible
+// range.
 template <typename T, int D, int DV, int G, int NW, int U>
 __device__ __forceinline__ void prefill_item_by_queries(const KernelArgs& a, const WorkItem& it, float* smem) {
   const int L = a.seq_lens[it.seq];

@@ -367,6 +367,23 @@ def config_bf16_chunked_prefill_d192(seed: int = 7) -> PagedBatch:
                       hq, hkv, d, dv, 1.0 / math.sqrt(192.0), True, 0, q, k, v, seed, 16)
 
 
+def config_bf16_chunked_prefill_d256(seed: int = 8) -> PagedBatch:
+    """The chunked-prefill shape with K and V rows of 256 (a workload of this
+    library): 8 sequences, history uniform in [0, 4096] plus a 512-query
+    chunk, causal, Hq=32, Hkv=8, page 16, scale 1/sqrt(256)."""
+    rng = np.random.default_rng(seed)
+    S, C, ps, hq, hkv, d = 8, 512, 16, 32, 8, 256
+    hist = rng.integers(0, 4096 + 1, size=S).astype(np.int32)
+    seq_lens = (hist + C).astype(np.int32)
+    bt, pool, _ = _tables(rng, seq_lens, ps)
+    q_pos = np.concatenate([np.arange(h, h + C, dtype=np.int32) for h in hist])
+    q = _normal(rng, (S * C, hq, d), "bf16")
+    k = _normal(rng, (pool, ps, hkv, d), "bf16")
+    v = _normal(rng, (pool, ps, hkv, d), "bf16")
+    return PagedBatch("bf16_chunked_prefill_d256", "bf16", seq_lens, _packed([C] * S), q_pos, bt, ps, pool,
+                      hq, hkv, d, d, 1.0 / math.sqrt(256.0), True, 0, q, k, v, seed, 16)
+
+
 def config_bf16_mla_chunked_prefill(seed: int = 6) -> MlaBatch:
     """bf16 absorbed-MLA chunked prefill (a workload of this library, beside
     the MLA decode one): 8 sequences, each a 256-query chunk after a history
@@ -395,6 +412,7 @@ CONFIGS: Dict[str, Callable] = {
     "bf16_mla_decode_h128": config_bf16_mla_decode_h128,
     "bf16_mla_chunked_prefill": config_bf16_mla_chunked_prefill,
     "bf16_chunked_prefill_d192": config_bf16_chunked_prefill_d192,
+    "bf16_chunked_prefill_d256": config_bf16_chunked_prefill_d256,
 }
 
 

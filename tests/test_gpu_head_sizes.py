@@ -1,8 +1,8 @@
 """GPU parity for K and V rows of different widths (ruDNN paged_attention:
 K [pages, page_size, Hkv, D], V [pages, page_size, Hkv, Dv], output
 [queries, Hq, Dv]): D = 192 with Dv = 128, the shape of a 128-wide
-no-position key part plus a 64-wide rotary part.  Decode items, split merges
-and prefill tiles (run query by query) against the fp64 oracle."""
+no-position key part plus a 64-wide rotary part, and D = Dv = 256.  Decode
+items, split merges and prefill tiles against the fp64 oracle."""
 import numpy as np
 import pytest
 
@@ -91,6 +91,42 @@ def test_d192_dv128_long_rows_split_to_the_limit():
 def test_d192_dv128_prefill_window_one_bitwise():
     """MFMA prefill tiles with a one-key window return each query's own V row."""
     b = random_batch(6500, dtype="bf16", hq=32, hkv=8, d=192, dv=128, page_size=16, q_counts=(150, 1, 40),
+                     max_len=600, window=1)
+    run = GqaRun(b)
+    run()
+    out, _ = run.result()
+    v = to_f64(run.v)
+    G = b.hq // b.hkv
+    for s in range(b.num_seqs):
+        for i in range(int(b.cu_q[s]), int(b.cu_q[s + 1])):
+            p = int(b.q_pos[i])
+            row = v[b.block_table[s, p // b.page_size], p % b.page_size]
+            for h in range(b.hq):
+                assert np.array_equal(out[i, h], row[h // G]), (i, h)
+
+
+@pytest.mark.parametrize("case", [
+    # D = Dv = 256 on the 32x32x16 tile in two passes of 128 output dims:
+    # several tiles and a ragged tail, MHA with a window, G = 8 and 16, page
+    # size 1 (per-lane page lookups), non-causal, history 0, f16
+    dict(dtype="bf16", hq=32, hkv=8, page_size=16, q_counts=(300, 1, 9), max_len=900),
+    dict(dtype="f16", hq=16, hkv=16, page_size=64, q_counts=(1, 270), max_len=700, window=33),
+    dict(dtype="bf16", hq=64, hkv=8, page_size=16, q_counts=(100, 3), max_len=800, window=129),
+    dict(dtype="bf16", hq=16, hkv=1, page_size=32, q_counts=(65, 2), max_len=500),
+    dict(dtype="bf16", hq=32, hkv=8, page_size=1, q_counts=(70,), max_len=200),
+    dict(dtype="bf16", hq=8, hkv=2, page_size=32, q_counts=(150, 5), max_len=700, causal=False),
+    dict(dtype="f16", hq=32, hkv=8, page_size=16, q_counts=(200,), histories=[0]),
+])
+def test_d256_prefill_and_mixed_parity(case):
+    b = random_batch(6600, d=256, **case)
+    run = _parity(b)
+    assert run.info["prefill_items"] > 0
+
+
+def test_d256_prefill_window_one_bitwise():
+    """Both 128-dim passes of the D = 256 tiles return each query's own V
+    row under a one-key window."""
+    b = random_batch(6700, dtype="bf16", hq=32, hkv=8, d=256, page_size=16, q_counts=(150, 1, 40),
                      max_len=600, window=1)
     run = GqaRun(b)
     run()
