@@ -492,9 +492,15 @@ __device__ __forceinline__ void prefill_item_impl(const KernelArgs& a, const Wor
   auto vector_phase = [&](int jj) {  // tile jj's scores -> weights
     if (jj >= 0 && jj < ntiles && !hidden(t_first + jj * NT)) weights(s, row_max(t_first + jj * NT, s), pf);
   };
+  // The matrix phase runs at wave priority 1, so that where both waves of a
+  // SIMD have an instruction ready the MFMA chain and its operand reads
+  // issue first (chunked prefill +2%, mixed batch +1.6%; the vector phase
+  // raised instead: -1.5%).
   auto matrix_phase = [&](int jj) {  // P.V of tile jj - 1, scores of tile jj
+    __builtin_amdgcn_s_setprio(1);
     if (jj > 0 && !hidden(t_first + (jj - 1) * NT)) pv(smem + ((jj - 1) % NS) * STAGE + TILE_K, pf);
     if (jj < ntiles && !hidden(t_first + jj * NT)) scores(smem + (jj % NS) * STAGE, s);
+    __builtin_amdgcn_s_setprio(0);
   };
   // One loop body for both groups, V(j - 1) then M(j); only the barrier
   // (and the loads issued after it) sits before V(j - 1) in the trailing
