@@ -150,9 +150,17 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
   // 16 wave + 4 c .. +3); the four partial tiles are summed through LDS.
   constexpr bool SPLIT_S = !PREFILL && SPLIT;
   static_assert(NG == 1 || SPLIT_S, "several head groups per item only on split decode items");
-  constexpr int QA = SPLIT_S ? KS_LAT / kMlaWaves : KS_LAT, QP = SPLIT_S ? 0 : KS_POS;
+  // Prefill: the two waves of a query split its score tile the same way,
+  // wave 2 i + h taking latent k-steps 8 h .. 8 h + 7 and rotary k-step h
+  // (16x16x32), their partial tiles summed through LDS.
+  constexpr bool SPLIT_P = PREFILL;
+  static_assert(!SPLIT_P || (KS_LAT % kMlaWavesPerQuery == 0 && KS_POS == kMlaWavesPerQuery),
+                "prefill score tile split over a query's two waves");
+  constexpr int QA = SPLIT_S ? KS_LAT / kMlaWaves : (SPLIT_P ? KS_LAT / kMlaWavesPerQuery : KS_LAT);
+  constexpr int QP = SPLIT_S ? 0 : (SPLIT_P ? 1 : KS_POS);
   static_assert(P == 16 * kMlaWaves, "one 16-dim rotary step per wave");
-  const int ks0 = SPLIT_S ? QA * wave : 0;
+  const int half = wave % kMlaWavesPerQuery;  // prefill: this wave's half of the score k-steps
+  const int ks0 = SPLIT_S ? QA * wave : (SPLIT_P ? QA * half : 0);
   frag_t qa[NG][QA], qp[QP > 0 ? QP : 1];
   short4_t qp16[NG] = {};
 #pragma unroll
@@ -163,7 +171,7 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
 #pragma unroll
     for (int k = 0; k < QA; ++k) qa[g][k] = *reinterpret_cast<const frag_t*>(qrow + 32 * (ks0 + k) + 8 * c);
 #pragma unroll
-    for (int k = 0; k < QP; ++k) qp[k] = *reinterpret_cast<const frag_t*>(prow + 32 * k + 8 * c);
+    for (int k = 0; k < QP; ++k) qp[k] = *reinterpret_cast<const frag_t*>(prow + 32 * ((SPLIT_P ? half : 0) + k) + 8 * c);
     if constexpr (SPLIT_S) qp16[g] = *reinterpret_cast<const short4_t*>(prow + 16 * wave + 4 * c);
   }
   // The tile loads below are inline assembly that the compiler's wait-count
@@ -265,16 +273,21 @@ __device__ __forceinline__ void mla_item(const KernelArgs& a, const WorkItem& it
     // accumulator chains halve the dependent MFMA latency
     floatx4_t s[NG];
     if constexpr (PREFILL) {
-      // fragments read as they are used (the output sums hold 128 registers)
+      // this wave's half of the k-steps, fragments read as they are used (the
+      // output sums hold 128 registers); the pair's two partial tiles meet in
+      // LDS and both waves add them in one order, so they hold the same scores
       floatx4_t sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int k = 0; k < KS_LAT; ++k)
-        sc[k & 1] =
-            mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * k + c)), qa[0][k], sc[k & 1]);
-#pragma unroll
-      for (int k = 0; k < KS_POS; ++k)
-        sc[k & 1] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * k + c)), qp[k], sc[k & 1]);
-      s[0] = sc[0] + sc[1];
+      for (int k = 0; k < QA; ++k)
+        sc[k & 1] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(ls + mla_off<R>(n, 4 * (ks0 + k) + c)),
+                                     qa[0][k], sc[k & 1]);
+      sc[0] = mfma_16x16x32<T>(*reinterpret_cast<const frag_t*>(kps + mla_off<P>(n, 4 * half + c)), qp[0], sc[0]);
+      typedef __attribute__((address_space(3))) floatx4_t lds_f4_t;
+      lds_f4_t* xs = (lds_f4_t*)(size_t)__builtin_amdgcn_readfirstlane(lds_address(smem + MlaSmem<NG>::kXchgOff));
+      xs[wave * 64 + lane] = sc[0] + sc[1];
+      barrier_keep_loads();  // the exchange is written (the tiles in flight stay in flight)
+      const int w0 = wave - half;
+      s[0] = xs[w0 * 64 + lane] + xs[(w0 + 1) * 64 + lane];
     } else if constexpr (!SPLIT_S) {
       frag_t kf[KS_LAT + KS_POS];
 #pragma unroll
