@@ -668,6 +668,180 @@ __global__ __launch_bounds__(kBwdMfmaWaves* kWave) void bwd_dq_mfma_kernel(BwdAr
   }
 }
 
+// dQ per 128-row tile on the 32x32x16 MFMA (K = V head sizes 64 and 128):
+// four waves of 32 rows, so that each K and V fragment read from LDS feeds a
+// 32-row product (twice the rows of the 16x16x32 kernel above, half the LDS
+// bytes per flop).  The tile of 32 keys is held as in the forward's prefill
+// tile (pieces of key row t at piece ^ swz(t)):
+//   S^T[32 keys x 32 rows]  = K . Q^T       dP^T = V . dO^T
+//   dQ^T[D x 32 rows]      += K^T . dS^T    (K^T by transposed reads, dS^T
+//                                             straight from the accumulators)
+// Every lane owns one row (its accumulator column); dS is rounded to the
+// storage type for the product, as in the kernel above.
+constexpr int kBwdDq32Waves = 4;
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(kBwdDq32Waves* kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_mfma32_kernel(BwdArgs b, int first_item, int G) {
+  constexpr int NT = kBwdKeyTile;
+  constexpr int KSK = D / 16, KSV = DV / 16, DB = D / 32;
+  constexpr int PK = D / 8, PV = DV / 8;
+  constexpr int CHUNKS = NT * (PK + PV);
+  constexpr int THREADS = kBwdDq32Waves * kWave;
+  constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
+  static_assert(kBwdDq32Waves * 32 == kBwdQRows, "four waves of 32 rows");
+  static_assert(NT == 32 && D % 32 == 0 && DV % 16 == 0, "one 32-key block per tile");
+  __shared__ __attribute__((aligned(16))) char ks[NT * D * 2];
+  __shared__ __attribute__((aligned(16))) char vs[NT * DV * 2];
+  const KernelArgs& a = b.a;
+  const BwdItem it = b.items[first_item + blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = lane & 31, h = lane >> 5;
+  const int kvh = it.kvh;
+  const int ps = 1 << a.page_shift;
+  const int32_t* bt = a.block_table + (size_t)it.seq * a.table_width;
+  const uint64_t krow = (uint64_t)a.hkv * D, vrow = (uint64_t)a.hkv * DV;
+  const int nrows = (it.q_end - it.q_begin) * G;
+  const float c2 = a.scale_log2;
+
+  // this lane's row (accumulator column n): Q^T and dO^T operands (dims
+  // 16 k + 8 h .. +7), statistics, position
+  const int my_row = wave * 32 + n;
+  const bool row_ok = my_row < nrows;
+  const int rg = row_ok ? my_row : 0;
+  const uint64_t row = (uint64_t)(it.q_begin + rg / G) * a.hq + (uint64_t)kvh * G + rg % G;
+  frag_t qb[KSK], gb[KSV];
+#pragma unroll
+  for (int k = 0; k < KSK; ++k)
+    qb[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(a.q) + row * D + 16 * k + 8 * h);
+#pragma unroll
+  for (int k = 0; k < KSV; ++k)
+    gb[k] = *reinterpret_cast<const frag_t*>(reinterpret_cast<const uint16_t*>(b.dout) + row * DV + 16 * k + 8 * h);
+  const float l2 = row_ok ? a.lse[row] * kLog2e : INFINITY;
+  const float dl = row_ok ? b.delta[row] : 0.f;
+  const int pos = a.q_pos[it.q_begin + rg / G];
+  floatx16_t dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[i][e] = 0.f;
+
+  // K^T fragments of dim block blk and k-step kk: two transposed reads (4
+  // keys each) at toff[blk][r] + kk * 16 rows, the forward's V^T pattern
+  uint32_t toff[DB][2];
+  {
+    const int grp16 = lane >> 4, gi = lane & 15;
+    const int key0 = 4 * (grp16 >> 1) + (gi >> 2);
+    const int d0 = 16 * (grp16 & 1) + 4 * (gi & 3);
+#pragma unroll
+    for (int blk = 0; blk < DB; ++blk)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int dim = 32 * blk + d0;
+        toff[blk][r] = (uint32_t)(tile_off<D>(key0 + 8 * r, dim >> 3) + (dim & 7) * 2);
+      }
+  }
+
+  // tile loads: piece c < NT PK of K (key c / PK), then of V
+  u32x4_t pre[PER_THREAD];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int c = tid + j * THREADS;
+      if (c < CHUNKS) {
+        const bool is_k = c < NT * PK;
+        const int cc = is_k ? c : c - NT * PK;
+        const int key = is_k ? cc / PK : cc / PV, piece = is_k ? cc % PK : cc % PV;
+        const int t = min(t0 + key, it.tok_end - 1);
+        const uint64_t slot = (uint64_t)bt[t >> a.page_shift] * ps + (t & (ps - 1));
+        pre[j] = is_k ? *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.k) + slot * krow +
+                                                          (uint64_t)kvh * D + piece * 8)
+                      : *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.v) + slot * vrow +
+                                                          (uint64_t)kvh * DV + piece * 8);
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int c = tid + j * THREADS;
+      if (c < CHUNKS) {
+        const bool is_k = c < NT * PK;
+        const int cc = is_k ? c : c - NT * PK;
+        char* dst = is_k ? ks + tile_off<D>(cc / PK, cc % PK) : vs + tile_off<DV>(cc / PV, cc % PV);
+        *reinterpret_cast<u32x4_t*>(dst) = pre[j];
+      }
+    }
+  };
+
+  fetch(it.tok_begin);
+  for (int t0 = it.tok_begin; t0 < it.tok_end; t0 += NT) {
+    __syncthreads();  // every wave is done with the previous tile
+    store();
+    __syncthreads();
+    if (t0 + NT < it.tok_end) fetch(t0 + NT);
+
+    floatx16_t s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KSK; ++k)
+      s = mfma_32x32x16<T>(*reinterpret_cast<const frag_t*>(ks + tile_off<D>(n, 2 * k + h)), qb[k], s);
+#pragma unroll
+    for (int k = 0; k < KSV; ++k)
+      dp = mfma_32x32x16<T>(*reinterpret_cast<const frag_t*>(vs + tile_off<DV>(n, 2 * k + h)), gb[k], dp);
+    // element e: key t0 + 8 (e / 4) + 4 h + e % 4 of row my_row; k-step kk
+    // of dQ^T takes elements 8 kk .. 8 kk + 7 (keys 16 kk .. 16 kk + 15)
+    frag_t df[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float ds[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int e = 8 * kk + 2 * j + i;
+          const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
+          const bool vis =
+              row_ok && t < it.tok_end && (!a.causal || t <= pos) && (a.window == 0 || t > pos - a.window);
+          const float p = vis ? fast_exp2(__builtin_fmaf(s[e], c2, -l2)) : 0.f;
+          ds[i] = p * (dp[e] - dl) * a.scale;
+        }
+        w[j] = Pair16<T>::pack(ds[0], ds[1]);
+      }
+      df[kk] = __builtin_bit_cast(frag_t, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int blk = 0; blk < DB; ++blk) {
+        const short4_t v0 = lds_read_tr16(ks + toff[blk][0] + kk * 16 * (D * 2));
+        const short4_t v1 = lds_read_tr16(ks + toff[blk][1] + kk * 16 * (D * 2));
+        const frag_t kf = __builtin_bit_cast(
+            frag_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
+                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
+                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
+                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))));
+        dq[blk] = mfma_32x32x16<T>(kf, df[kk], dq[blk]);
+      }
+  }
+
+  // dQ^T block blk: lane (n, h) element 4 k + i is dim 32 blk + 8 k + 4 h + i of row my_row
+  if (!row_ok) return;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(b.dq) + row * D;
+#pragma unroll
+  for (int blk = 0; blk < DB; ++blk)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint2 w;
+      w.x = Pair16<T>::pack(dq[blk][4 * k + 0], dq[blk][4 * k + 1]);
+      w.y = Pair16<T>::pack(dq[blk][4 * k + 2], dq[blk][4 * k + 3]);
+      *reinterpret_cast<uint2*>(orow + 32 * blk + 8 * k + 4 * h) = w;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Absorbed-MLA backward (ruDNN 0.1.107 paged_attention `mla_backward` /
 // `mla_backward_into`), on 16-bit MFMA.  The latent is both key and value,
@@ -1247,8 +1421,12 @@ using BwdFn = hipError_t (*)(const BwdArgs&, int, int, int, hipStream_t);
 template <typename T, int D, int DV, int G>
 hipError_t launch_bwd_t(const BwdArgs& b, int n_dq, int n_kv, int n_dqt, hipStream_t stream) {
   constexpr bool kMfma = sizeof(T) == 2 && D % 64 == 0 && DV % 64 == 0;
+  constexpr bool kMfma32 = kMfma && D == DV && D <= 128;  // the 32x32x16 dQ kernel's registers
   if (kMfma && n_dqt > 0) {
-    if constexpr (kMfma)
+    if constexpr (kMfma32)
+      hipLaunchKernelGGL((bwd_dq_mfma32_kernel<T, D, DV>), dim3(n_dqt), dim3(kBwdDq32Waves * kWave), 0, stream, b,
+                         n_dq + n_kv, G);
+    else if constexpr (kMfma)
       hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, DV>), dim3(n_dqt), dim3(kBwdMfmaWaves * kWave), 0, stream, b,
                          n_dq + n_kv, G);
     hipError_t e = hipGetLastError();
