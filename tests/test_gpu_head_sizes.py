@@ -123,6 +123,17 @@ def test_d256_prefill_and_mixed_parity(case):
     assert run.info["prefill_items"] > 0
 
 
+@pytest.mark.timeout(900)
+def test_d256_chunked_prefill_full_size_every_row():
+    """The D = Dv = 256 chunked-prefill workload (8 sequences, 512-query
+    chunks after 0..4096 cached keys, Hq 32, Hkv 8, page 16): every output
+    element and every lse against the oracle."""
+    from synth import config_bf16_chunked_prefill_d256
+    b = config_bf16_chunked_prefill_d256()
+    run = _parity(b)
+    assert run.info["prefill_items"] > 0 and run.info["decode_items"] == 0
+
+
 def test_d256_prefill_window_one_bitwise():
     """Both 128-dim passes of the D = 256 tiles return each query's own V
     row under a one-key window."""

@@ -48,8 +48,9 @@ def test_random_prefill_and_mixed_parity(i):
     dict(dtype="f32", hq=8, hkv=2, d=64, page_size=16, q_counts=(20, 1), max_len=300),
     dict(dtype="bf16", hq=4, hkv=1, d=256, page_size=16, q_counts=(12,), max_len=200, window=20),
 ])
-def test_prefill_without_mfma_tile(case):
-    """f32 data and head size 256 run prefill tiles query by query."""
+def test_prefill_f32_and_d256_short_chunks(case):
+    """f32 data runs prefill tiles query by query (no MFMA tile); head size
+    256 runs the two-pass MFMA tile on a chunk shorter than one tile."""
     b = random_batch(2100, **case)
     _all_rows(b)
 
